@@ -1,0 +1,301 @@
+"""Pins of the fp64 CPU oracle against things other than itself.
+
+The pages print no numeric example of the scan, so every pin here is
+mathematical: an independent dense formulation (materialised semiseparable
+matrices + autograd), closed forms, a textbook filter routine, symmetries,
+causality, cache consistency and finite differences.  Each is chosen so that a
+plausible slip in ssd_oracle.c (wrong decay index, dropped diagonal, swapped
+direction, wrong group, sign error in a gradient) fails at least one of them.
+"""
+import math
+
+import numpy as np
+import pytest
+import scipy.signal
+
+from oracle import dense
+from oracle import oracle as O
+
+KEYS = ("x", "dt_f", "A_f", "B_f", "C_f", "dt_r", "A_r", "B_r", "C_r", "D")
+
+
+def rand_inputs(Z, L, H, P, N, G, seed=0, dt_lo=0.01, dt_hi=0.3):
+    r = np.random.default_rng(seed)
+    inp = {"x": r.standard_normal((Z, L, H, P)), "D": r.standard_normal(H)}
+    for d in ("f", "r"):
+        inp[f"dt_{d}"] = r.uniform(dt_lo, dt_hi, (Z, L, H))
+        inp[f"A_{d}"] = -np.exp(r.uniform(0, math.log(16), H))
+        inp[f"B_{d}"] = r.standard_normal((Z, L, G, N)) / math.sqrt(N)
+        inp[f"C_{d}"] = r.standard_normal((Z, L, G, N)) / math.sqrt(N)
+    return inp
+
+
+def rel(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    m = np.max(np.abs(b))
+    return float(np.max(np.abs(a - b)) / (m if m > 0 else 1.0))
+
+
+# ----------------------------------------------------------------- P1 dense
+
+@pytest.mark.parametrize("shape", [(2, 37, 3, 5, 4, 1), (1, 130, 4, 8, 6, 2),
+                                   (1, 64, 6, 3, 5, 3)])
+def test_recurrence_matches_dense_semiseparable(shape):
+    inp = rand_inputs(*shape, seed=1)
+    o = O.forward(inp, parts=True)
+    d = dense.forward(inp)
+    assert rel(o["y_f"], d["y_f"]) < 1e-12
+    assert rel(o["y_r"], d["y_r"]) < 1e-12
+    assert rel(o["y"], d["y"]) < 1e-12
+
+
+def test_recurrence_matches_dense_with_start_state():
+    Z, L, H, P, N, G = 2, 50, 3, 4, 5, 1
+    inp = rand_inputs(Z, L, H, P, N, G, seed=2)
+    S0 = np.random.default_rng(3).standard_normal((Z, H, P, N))
+    o = O.forward(inp, init_state=S0, parts=True, final_state=True)
+    d = dense.forward(inp, init_state=S0)
+    assert rel(o["y_f"], d["y_f"]) < 1e-12
+    assert rel(o["y"], d["y"]) < 1e-12
+
+
+# ----------------------------------------------------------- P2 closed form
+
+@pytest.mark.parametrize("L", [1, 7, 130])
+def test_closed_form_prefix_sums(L):
+    """A = 0, B = C = e_0, dt = 1: the forward scan is a running sum, the
+    reverse scan a running sum from the right, both exact in fp64."""
+    Z, H, P, N, G = 2, 3, 4, 5, 1
+    r = np.random.default_rng(L)
+    inp = {"x": r.integers(-1, 2, (Z, L, H, P)).astype(np.float64),
+           "D": np.array([0.0, 1.0, -2.0])}
+    e0 = np.zeros((Z, L, G, N))
+    e0[..., 0] = 1.0
+    for d in ("f", "r"):
+        inp[f"dt_{d}"] = np.ones((Z, L, H))
+        inp[f"A_{d}"] = np.zeros(H)
+        inp[f"B_{d}"] = e0
+        inp[f"C_{d}"] = e0
+    o = O.forward(inp, parts=True)
+    x = inp["x"]
+    cs = np.cumsum(x, axis=1)
+    rcs = np.cumsum(x[:, ::-1], axis=1)[:, ::-1]
+    assert np.array_equal(o["y_f"], cs)
+    assert np.array_equal(o["y_r"], rcs)
+    expect = x.sum(axis=1, keepdims=True) + x + inp["D"][None, None, :, None] * x
+    assert np.array_equal(o["y"], expect)
+
+
+# ------------------------------------------------------ P3 zero-decay limit
+
+def test_every_decay_zero_leaves_the_diagonal_in_both_directions():
+    Z, L, H, P, N, G = 2, 33, 3, 4, 6, 1
+    inp = rand_inputs(Z, L, H, P, N, G, seed=4)
+    inp["A_f"] = np.full(H, -1e30)
+    inp["A_r"] = np.full(H, -1e30)
+    o = O.forward(inp)
+    cbf = np.einsum("zlgn,zlgn->zlg", inp["B_f"], inp["C_f"])[..., 0]
+    cbr = np.einsum("zlgn,zlgn->zlg", inp["B_r"], inp["C_r"])[..., 0]
+    coef = inp["dt_f"] * cbf[..., None] + inp["dt_r"] * cbr[..., None] + inp["D"]
+    assert rel(o, coef[..., None] * inp["x"]) < 1e-14
+
+
+# --------------------------------------------------------- P4 scipy filter
+
+def test_scalar_case_is_a_first_order_iir_filter():
+    L = 300
+    r = np.random.default_rng(5)
+    x = r.standard_normal(L)
+    dtf, Af, dtr, Ar = 0.07, -2.5, 0.2, -0.9
+    inp = {"x": x.reshape(1, L, 1, 1), "D": np.zeros(1),
+           "dt_f": np.full((1, L, 1), dtf), "A_f": np.array([Af]),
+           "dt_r": np.full((1, L, 1), dtr), "A_r": np.array([Ar]),
+           "B_f": np.ones((1, L, 1, 1)), "C_f": np.ones((1, L, 1, 1)),
+           "B_r": np.ones((1, L, 1, 1)), "C_r": np.ones((1, L, 1, 1))}
+    o = O.forward(inp, parts=True)
+    yf = scipy.signal.lfilter([dtf], [1.0, -math.exp(dtf * Af)], x)
+    yr = scipy.signal.lfilter([dtr], [1.0, -math.exp(dtr * Ar)], x[::-1])[::-1]
+    assert rel(o["y_f"].ravel(), yf) < 1e-13
+    assert rel(o["y_r"].ravel(), yr) < 1e-13
+
+
+# --------------------------------------------------------- P5 flip symmetry
+
+def test_flip_swaps_the_two_directions():
+    Z, L, H, P, N, G = 2, 45, 4, 3, 5, 2
+    inp = rand_inputs(Z, L, H, P, N, G, seed=6)
+    o = O.forward(inp, parts=True)
+    fl = lambda a: a[:, ::-1].copy()  # noqa: E731
+    sw = {"x": fl(inp["x"]), "D": inp["D"],
+          "dt_f": fl(inp["dt_r"]), "A_f": inp["A_r"], "B_f": fl(inp["B_r"]), "C_f": fl(inp["C_r"]),
+          "dt_r": fl(inp["dt_f"]), "A_r": inp["A_f"], "B_r": fl(inp["B_f"]), "C_r": fl(inp["C_f"])}
+    s = O.forward(sw, parts=True)
+    assert rel(s["y_f"], fl(o["y_r"])) < 1e-14
+    assert rel(s["y_r"], fl(o["y_f"])) < 1e-14
+    assert rel(s["y"], fl(o["y"])) < 1e-14
+
+
+# ------------------------------------------------------------ P6 linearity
+
+def test_linear_in_x():
+    Z, L, H, P, N, G = 1, 40, 2, 3, 4, 1
+    a = rand_inputs(Z, L, H, P, N, G, seed=7)
+    b = dict(a)
+    b["x"] = np.random.default_rng(8).standard_normal(a["x"].shape)
+    c = dict(a)
+    c["x"] = 0.75 * a["x"] - 1.5 * b["x"]
+    ya, yb, yc = O.forward(a), O.forward(b), O.forward(c)
+    assert rel(yc, 0.75 * ya - 1.5 * yb) < 1e-13
+
+
+# ------------------------------------------------------------- P7 causality
+
+@pytest.mark.parametrize("s", [0, 17, 63])
+def test_impulse_respects_direction(s):
+    Z, L, H, P, N, G = 1, 64, 2, 3, 4, 1
+    inp = rand_inputs(Z, L, H, P, N, G, seed=9)
+    inp["x"] = np.zeros_like(inp["x"])
+    inp["x"][:, s] = 1.0
+    o = O.forward(inp, parts=True)
+    assert np.all(o["y_f"][:, :s] == 0.0)
+    assert np.all(o["y_r"][:, s + 1:] == 0.0)
+    assert np.all(o["y_f"][:, s:] != 0.0)
+    assert np.all(o["y_r"][:, : s + 1] != 0.0)
+
+
+# ----------------------------------------------------- P8 cache consistency
+
+def test_block_update_reuses_the_prefix_state_exactly():
+    """Scanning [prefix | block] forward equals continuing from the prefix's
+    final state; the block's reverse scan sees the block only."""
+    Z, Lp, Lb, H, P, N, G = 2, 70, 24, 3, 4, 5, 1
+    full = rand_inputs(Z, Lp + Lb, H, P, N, G, seed=10)
+    pre = {k: (v[:, :Lp] if v.ndim > 1 else v) for k, v in full.items()}
+    blk = {k: (v[:, Lp:] if v.ndim > 1 else v) for k, v in full.items()}
+    op = O.forward(pre, final_state=True)
+    of = O.forward(full, parts=True, final_state=True)
+    y, so = O.block_update(blk, op["final_state"])
+    ob = O.forward(blk, parts=True)   # block-only scans (reverse part used)
+    expect = of["y_f"][:, Lp:] + ob["y_r"] + blk["D"][None, None, :, None] * blk["x"]
+    assert np.array_equal(y, expect)
+    assert np.array_equal(so, of["final_state"])
+
+
+def test_block_update_state_out_may_alias_state_in():
+    Z, L, H, P, N, G = 1, 16, 2, 3, 4, 1
+    inp = rand_inputs(Z, L, H, P, N, G, seed=11)
+    S0 = np.random.default_rng(12).standard_normal((Z, H, P, N))
+    y1, so1 = O.block_update(inp, S0.copy())
+    d = dense.forward(inp, init_state=S0)
+    assert rel(y1, d["y"]) < 1e-12
+
+
+# ----------------------------------------------------- P10 backward pins
+
+def _loss(inp, dy, S0=None):
+    return float(np.sum(O.forward(inp, init_state=S0) * dy))
+
+
+@pytest.mark.parametrize("shape", [(1, 20, 2, 3, 4, 1), (2, 33, 4, 3, 2, 2)])
+def test_backward_matches_autograd_of_dense_form(shape):
+    inp = rand_inputs(*shape, seed=13)
+    dy = np.random.default_rng(14).standard_normal(inp["x"].shape)
+    g = O.backward(inp, dy)
+    ref = dense.gradients(inp, dy)
+    for k in KEYS:
+        assert rel(g["d" + k], ref["d" + k]) < 1e-11, k
+
+
+def test_backward_with_start_state_matches_autograd():
+    Z, L, H, P, N, G = 1, 150, 2, 3, 4, 1   # > 2 checkpoint segments
+    inp = rand_inputs(Z, L, H, P, N, G, seed=15)
+    S0 = np.random.default_rng(16).standard_normal((Z, H, P, N))
+    dy = np.random.default_rng(17).standard_normal(inp["x"].shape)
+    g = O.backward(inp, dy, init_state=S0)
+    ref = dense.gradients(inp, dy, init_state=S0)
+    for k in KEYS:
+        assert rel(g["d" + k], ref["d" + k]) < 1e-11, k
+
+
+def test_backward_finite_differences_tiny_fp32_shapes():
+    """Central differences in fp64 on the tiny correctness shapes
+    (L=128, 4 heads, P=64, N=64): a directional derivative per tensor."""
+    Z, L, H, P, N, G = 1, 128, 4, 64, 64, 1
+    inp = rand_inputs(Z, L, H, P, N, G, seed=18, dt_lo=1e-3, dt_hi=0.1)
+    r = np.random.default_rng(19)
+    dy = r.standard_normal(inp["x"].shape)
+    g = O.backward(inp, dy)
+    eps = 1e-6
+    for k in KEYS:
+        v = r.standard_normal(inp[k].shape)
+        plus = dict(inp)
+        minus = dict(inp)
+        plus[k] = inp[k] + eps * v
+        minus[k] = inp[k] - eps * v
+        fd = (_loss(plus, dy) - _loss(minus, dy)) / (2 * eps)
+        an = float(np.sum(g["d" + k] * v))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (k, fd, an)
+
+
+def test_backward_every_A_and_D_entry_by_finite_differences():
+    Z, L, H, P, N, G = 2, 40, 3, 4, 5, 1
+    inp = rand_inputs(Z, L, H, P, N, G, seed=20)
+    dy = np.random.default_rng(21).standard_normal(inp["x"].shape)
+    g = O.backward(inp, dy)
+    eps = 1e-6
+    for k in ("A_f", "A_r", "D"):
+        for h in range(H):
+            plus, minus = dict(inp), dict(inp)
+            plus[k] = inp[k].copy()
+            minus[k] = inp[k].copy()
+            plus[k][h] += eps
+            minus[k][h] -= eps
+            fd = (_loss(plus, dy) - _loss(minus, dy)) / (2 * eps)
+            assert abs(fd - g["d" + k][h]) <= 1e-7 * max(1.0, abs(fd)), (k, h)
+
+
+def test_backward_dx_is_the_adjoint_of_the_dense_operator():
+    Z, L, H, P, N, G = 2, 30, 3, 4, 5, 1
+    inp = rand_inputs(Z, L, H, P, N, G, seed=22)
+    dy = np.random.default_rng(23).standard_normal(inp["x"].shape)
+    g = O.backward(inp, dy)
+    for b in range(Z):
+        for h in range(H):
+            Mf, Mr = dense.matrices(inp, b, h)
+            M = Mf + Mr + inp["D"][h] * np.eye(L)
+            assert rel(g["dx"][b, :, h], M.T @ dy[b, :, h]) < 1e-12
+
+
+# --------------------------------------------------- P11 permutations
+
+def test_permuting_batch_rows_and_heads_permutes_outputs():
+    Z, L, H, P, N, G = 3, 25, 4, 3, 4, 1
+    inp = rand_inputs(Z, L, H, P, N, G, seed=24)
+    y = O.forward(inp)
+    pb = np.array([2, 0, 1])
+    ph = np.array([3, 1, 0, 2])
+    q = {}
+    for k, v in inp.items():
+        if k in ("A_f", "A_r", "D"):
+            q[k] = v[ph]
+        elif k.startswith(("B", "C")):
+            q[k] = v[pb]
+        elif k.startswith("dt"):
+            q[k] = v[pb][:, :, ph]
+        else:
+            q[k] = v[pb][:, :, ph]
+    yq = O.forward(q)
+    assert np.array_equal(yq, y[pb][:, :, ph])
+
+
+def test_thread_count_does_not_change_results():
+    inp = rand_inputs(2, 50, 3, 4, 5, 1, seed=25)
+    a = O.forward(inp, nthreads=1)
+    b = O.forward(inp, nthreads=5)
+    assert np.array_equal(a, b)
+    dy = np.random.default_rng(26).standard_normal(inp["x"].shape)
+    ga = O.backward(inp, dy, nthreads=1)
+    gb = O.backward(inp, dy, nthreads=4)
+    for k in ga:
+        assert np.array_equal(ga[k], gb[k]), k
