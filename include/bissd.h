@@ -1,0 +1,175 @@
+/*
+ * bissd.h -- C ABI of the bidirectional SSD (Mamba-2) scan library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  A bidirectional Mamba-2 mixer runs one selective scan over
+ * the sequence and one over the flipped sequence and adds the two ("DiffMamba
+ * Checkpoints" model card, Model details: forward plus flipped-reverse
+ * Mamba-2; "DiffuMamba: High-Throughput Diffusion LMs with Mamba Backbone",
+ * Technical Summary, Methodology / Core Architecture: two Mamba-2 layers, one
+ * per direction, fused additively).  Per batch row b and head h, with state
+ * S in R^{P x N} and group g = floor(h * G / H):
+ *
+ *   forward  (t = 0 .. L-1):  S <- exp(dt_f[t] A_f[h]) S + dt_f[t] x[t] (outer) B_f[t]
+ *                             yf[t] = S C_f[t]
+ *   reverse  (t = L-1 .. 0):  S' <- exp(dt_r[t] A_r[h]) S' + dt_r[t] x[t] (outer) B_r[t]
+ *                             yr[t] = S' C_r[t]
+ *   y[t] = yf[t] + yr[t] + D[h] x[t]
+ *
+ * Token t is counted by both directions.  The forward state starts from
+ * init_state (or zero); the reverse state always starts from zero after the
+ * last token.
+ *
+ * Block update ("Training Hybrid Block Diffusion Language Models with Partial
+ * Bidirectionality", Methodology and Technical Contribution): during
+ * block-wise denoising the forward state after the prefix is a cache that is
+ * reused exactly, while the reverse scan is confined to the active block.
+ * bissd_block_update is the forward above on the block alone, with the
+ * forward scan continuing from the cached prefix state and the reverse scan
+ * starting from zero at the block end.
+ *
+ * Layouts (row-major, contiguous, natural token order for both directions):
+ *   x, y, dy        [batch][seqlen][nheads][headdim]        dtype
+ *   dx              [batch][seqlen][nheads][headdim]        fp32
+ *   dt_f, dt_r      [batch][seqlen][nheads]                 dtype
+ *   B_*, C_*        [batch][seqlen][ngroups][dstate]        dtype
+ *   A_f, A_r, D     [nheads]                                fp32
+ *   states          [batch][nheads][headdim][dstate]        fp32
+ *   gradients       same layout as their input, fp32
+ *
+ * Pointers.  Every tensor pointer is a device pointer (from hipMalloc or any
+ * device allocator) aligned to 16 bytes; the caller owns every buffer.  The
+ * library allocates no device memory and keeps no state between calls: the
+ * only scratch memory is the caller's workspace, sized by
+ * bissd_workspace_size().  Calls are asynchronous on `stream` (a hipStream_t;
+ * NULL = the null stream): inputs must stay live and unmodified until the
+ * stream reaches the call.  Results are bitwise reproducible for identical
+ * inputs and shapes on the same device.
+ *
+ * Errors.  Every entry point returns a status code.  On any validation
+ * failure nothing is launched and no output is touched.  Values are not
+ * inspected: NaN/Inf inputs propagate.  No exception, abort or exit crosses
+ * the ABI.
+ *
+ * Support.  headdim == 64; dstate in {64, 128}; chunk in {64, 128, 256};
+ * nheads % ngroups == 0; any seqlen >= 1; dtype BISSD_F32 or BISSD_BF16.
+ * All arithmetic accumulates in fp32; bf16 operands feed the matrix cores.
+ */
+#ifndef BISSD_H
+#define BISSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* dtype of x, dt, B, C, y and dy. */
+enum { BISSD_F32 = 0, BISSD_BF16 = 1 };
+
+/* status codes */
+enum {
+  BISSD_OK = 0,
+  BISSD_ERR_NULL = -1,        /* a required pointer is NULL */
+  BISSD_ERR_SHAPE = -2,       /* a dim <= 0, nheads % ngroups != 0, or block longer than chunk */
+  BISSD_ERR_UNSUPPORTED = -3, /* headdim, dstate, chunk or dtype outside the supported set */
+  BISSD_ERR_ALIGN = -4,       /* a pointer not aligned to 16 bytes */
+  BISSD_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than bissd_workspace_size() */
+  BISSD_ERR_HIP = -6,         /* a HIP launch failed; see bissd_last_hip_error() */
+  BISSD_ERR_ALIAS = -7        /* an output overlaps an input it may not alias */
+};
+
+/* operation selector for bissd_workspace_size() */
+enum { BISSD_OP_FORWARD = 0, BISSD_OP_BACKWARD = 1, BISSD_OP_BLOCK = 2 };
+
+typedef struct {
+  int64_t batch;    /* Z */
+  int64_t seqlen;   /* L (the block length for bissd_block_update) */
+  int64_t nheads;   /* H */
+  int64_t headdim;  /* P */
+  int64_t dstate;   /* N */
+  int64_t ngroups;  /* G: B and C are shared by nheads/ngroups consecutive heads */
+  int64_t chunk;    /* chunk length of the chunked evaluation (a tiling choice;
+                       the result does not depend on it beyond rounding) */
+  int32_t dtype;    /* BISSD_F32 or BISSD_BF16 */
+  int32_t reserved; /* must be 0 */
+} bissd_shape_t;
+
+/* One scan direction's parameters.  dt is already positive (no softplus,
+ * bias or clamp is applied by the library). */
+typedef struct {
+  const void *dt;  /* [Z][L][H] dtype */
+  const float *A;  /* [H] fp32, the per-head scalar decay rate (A <= 0) */
+  const void *B;   /* [Z][L][G][N] dtype */
+  const void *C;   /* [Z][L][G][N] dtype */
+} bissd_dir_t;
+
+/* One direction's parameter gradients (all fp32, overwritten). */
+typedef struct {
+  float *ddt;  /* [Z][L][H] */
+  float *dA;   /* [H], summed over batch and time */
+  float *dB;   /* [Z][L][G][N], summed over the heads of each group */
+  float *dC;   /* [Z][L][G][N], summed over the heads of each group */
+} bissd_grad_t;
+
+/*
+ * Bytes of device workspace that `op` needs for `shape` (0 on a bad shape).
+ * The workspace holds the per-chunk carry states (fp32) and is overwritten
+ * by every call; its contents between calls mean nothing.
+ */
+size_t bissd_workspace_size(const bissd_shape_t *shape, int op);
+
+/*
+ * Full-sequence bidirectional scan: y = yf + yr + D x.
+ *   init_state  [Z][H][P][N] fp32 or NULL (zero): forward start state.
+ *   final_state [Z][H][P][N] fp32 or NULL: receives the forward state after
+ *               token L-1 (the cache a following block update continues from).
+ *               May equal init_state.
+ *   fwd.* and rev.* may point to the same buffers (weight-tied directions).
+ *   y must not overlap any input.
+ */
+int bissd_forward(const bissd_shape_t *shape, const void *x, bissd_dir_t fwd,
+                  bissd_dir_t rev, const float *D, const float *init_state, void *y,
+                  float *final_state, void *workspace, size_t workspace_bytes,
+                  void *stream);
+
+/*
+ * Gradients of Loss = sum(dy * y) for y = bissd_forward(...) with the same
+ * inputs (init_state optional and treated as a constant):
+ *   dx [Z][L][H][P] fp32; gfwd / grev: per-direction ddt, dA, dB, dC (fp32);
+ *   dD [H] fp32.  All outputs are overwritten; dA, dB, dC and dD are
+ *   reduced deterministically (no floating-point atomics).
+ */
+int bissd_backward(const bissd_shape_t *shape, const void *x, bissd_dir_t fwd,
+                   bissd_dir_t rev, const float *D, const float *init_state,
+                   const void *dy, float *dx, bissd_grad_t gfwd, bissd_grad_t grev,
+                   float *dD, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Block update with partial bidirectionality on an active block of
+ * shape->seqlen tokens (seqlen <= chunk):
+ *   y_blk = yf(from state_in) + yr(block only) + D x_blk
+ *   state_in  [Z][H][P][N] fp32: forward state after the last prefix token.
+ *   state_out [Z][H][P][N] fp32 or NULL: forward state after the last block
+ *             token (the next block's cache).  May equal state_in.
+ */
+int bissd_block_update(const bissd_shape_t *shape, const float *state_in,
+                       const void *x_blk, bissd_dir_t fwd, bissd_dir_t rev,
+                       const float *D, void *y_blk, float *state_out, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
+/* Text of a status code (static storage). */
+const char *bissd_status_string(int status);
+
+/* The hipError_t of the last BISSD_ERR_HIP on the calling thread (0 if none). */
+int bissd_last_hip_error(void);
+
+/* ABI version: 1. */
+int bissd_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BISSD_H */

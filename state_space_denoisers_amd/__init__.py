@@ -1,0 +1,156 @@
+"""Bidirectional SSD (Mamba-2) scan for AMD Instinct MI355X.
+
+Thin Python binding over the C ABI of libbissd.so (include/bissd.h).  The
+functions carry the ABI's names and only marshal arguments: torch provides
+device memory and the current stream, and every step of the scan runs in the
+library's HIP kernels.  There is no CPU or PyTorch fallback.
+
+    y = bissd_forward(x, fwd, rev, D, chunk=256)
+    y, state_out = bissd_block_update(state_in, x_blk, fwd, rev, D)
+    grads = bissd_backward(x, fwd, rev, D, dy)
+
+``fwd`` / ``rev`` are (dt, A, B, C) tuples: dt [Z,L,H], A [H] fp32,
+B and C [Z,L,G,N]; x [Z,L,H,P]; D [H] fp32.  x, dt, B, C (and dy) share one
+dtype, torch.float32 or torch.bfloat16.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from typing import NamedTuple, Optional
+
+import torch
+
+from . import _abi
+
+__all__ = ["Dir", "bissd_forward", "bissd_block_update", "bissd_backward",
+           "bissd_workspace_size", "shape_of", "library_path", "BissdError"]
+
+BissdError = _abi.BissdError
+
+
+class Dir(NamedTuple):
+    dt: torch.Tensor
+    A: torch.Tensor
+    B: torch.Tensor
+    C: torch.Tensor
+
+
+def library_path() -> str:
+    return _abi.LIB_PATH
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return _abi.BISSD_BF16
+    if t.dtype == torch.float32:
+        return _abi.BISSD_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def shape_of(x: torch.Tensor, B: torch.Tensor, chunk: int) -> _abi.Shape:
+    Z, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    return _abi.Shape(Z, L, H, P, N, G, int(chunk), _dtype_code(x), 0)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libbissd must be contiguous")
+    return C.c_void_p(t.data_ptr())
+
+
+def _dir(d) -> _abi.Dir:
+    d = Dir(*d)
+    for name, t, want in (("dt", d.dt, None), ("A", d.A, torch.float32),
+                          ("B", d.B, None), ("C", d.C, None)):
+        if want is not None and t.dtype != want:
+            raise TypeError(f"{name} must be {want}, got {t.dtype}")
+    return _abi.Dir(_ptr(d.dt), _ptr(d.A), _ptr(d.B), _ptr(d.C))
+
+
+def _stream(device: torch.device, stream) -> C.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return C.c_void_p(s.cuda_stream)
+
+
+def bissd_workspace_size(shape: _abi.Shape, op: int) -> int:
+    return int(_abi.load().bissd_workspace_size(C.byref(shape), int(op)))
+
+
+def _workspace(shape, op, device, workspace):
+    n = bissd_workspace_size(shape, op)
+    if workspace is not None:
+        return workspace, workspace.numel() * workspace.element_size()
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+    return ws, ws.numel()
+
+
+def bissd_forward(x: torch.Tensor, fwd, rev, D: torch.Tensor, *, chunk: int = 256,
+                  init_state: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
+                  final_state: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """y = yf + yr + D x (see include/bissd.h, bissd_forward)."""
+    lib = _abi.load()
+    fwd, rev = Dir(*fwd), Dir(*rev)
+    shape = shape_of(x, fwd.B, chunk)
+    if y is None:
+        y = torch.empty_like(x)
+    ws, nws = _workspace(shape, _abi.OP_FORWARD, x.device, workspace)
+    st = lib.bissd_forward(C.byref(shape), _ptr(x), _dir(fwd), _dir(rev), _ptr(D),
+                           _ptr(init_state), _ptr(y), _ptr(final_state), _ptr(ws),
+                           C.c_size_t(nws), _stream(x.device, stream))
+    _abi.check("bissd_forward", st)
+    return y
+
+
+def bissd_block_update(state_in: torch.Tensor, x_blk: torch.Tensor, fwd, rev,
+                       D: torch.Tensor, *, chunk: Optional[int] = None,
+                       y_blk: Optional[torch.Tensor] = None,
+                       state_out: Optional[torch.Tensor] = None, commit: bool = True,
+                       workspace: Optional[torch.Tensor] = None, stream=None):
+    """Block update with a cached forward prefix state (include/bissd.h,
+    bissd_block_update).  Returns (y_blk, state_out); state_out is None when
+    ``commit`` is false and none was given."""
+    lib = _abi.load()
+    fwd, rev = Dir(*fwd), Dir(*rev)
+    L = x_blk.shape[1]
+    if chunk is None:
+        chunk = 64 if L <= 64 else (128 if L <= 128 else 256)
+    shape = shape_of(x_blk, fwd.B, chunk)
+    if y_blk is None:
+        y_blk = torch.empty_like(x_blk)
+    if state_out is None and commit:
+        state_out = torch.empty_like(state_in)
+    ws, nws = _workspace(shape, _abi.OP_BLOCK, x_blk.device, workspace)
+    st = lib.bissd_block_update(C.byref(shape), _ptr(state_in), _ptr(x_blk), _dir(fwd),
+                                _dir(rev), _ptr(D), _ptr(y_blk), _ptr(state_out), _ptr(ws),
+                                C.c_size_t(nws), _stream(x_blk.device, stream))
+    _abi.check("bissd_block_update", st)
+    return y_blk, state_out
+
+
+def bissd_backward(x: torch.Tensor, fwd, rev, D: torch.Tensor, dy: torch.Tensor, *,
+                   chunk: int = 256, init_state: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """Gradients of sum(dy * y) (include/bissd.h, bissd_backward).  Returns a
+    dict with dx, ddt_f, dA_f, dB_f, dC_f, ddt_r, dA_r, dB_r, dC_r, dD (fp32)."""
+    lib = _abi.load()
+    fwd, rev = Dir(*fwd), Dir(*rev)
+    shape = shape_of(x, fwd.B, chunk)
+    f32 = dict(dtype=torch.float32, device=x.device)
+    g = {"dx": torch.empty(x.shape, **f32), "dD": torch.empty(D.shape, **f32)}
+    for d, p in (("f", fwd), ("r", rev)):
+        g[f"ddt_{d}"] = torch.empty(p.dt.shape, **f32)
+        g[f"dA_{d}"] = torch.empty(p.A.shape, **f32)
+        g[f"dB_{d}"] = torch.empty(p.B.shape, **f32)
+        g[f"dC_{d}"] = torch.empty(p.C.shape, **f32)
+    gf = _abi.Grad(_ptr(g["ddt_f"]), _ptr(g["dA_f"]), _ptr(g["dB_f"]), _ptr(g["dC_f"]))
+    gr = _abi.Grad(_ptr(g["ddt_r"]), _ptr(g["dA_r"]), _ptr(g["dB_r"]), _ptr(g["dC_r"]))
+    ws, nws = _workspace(shape, _abi.OP_BACKWARD, x.device, workspace)
+    st = lib.bissd_backward(C.byref(shape), _ptr(x), _dir(fwd), _dir(rev), _ptr(D),
+                            _ptr(init_state), _ptr(dy), _ptr(g["dx"]), gf, gr, _ptr(g["dD"]),
+                            _ptr(ws), C.c_size_t(nws), _stream(x.device, stream))
+    _abi.check("bissd_backward", st)
+    return g

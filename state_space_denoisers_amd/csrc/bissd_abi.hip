@@ -1,0 +1,279 @@
+// bissd_abi.hip -- the C ABI of the bidirectional SSD scan (include/bissd.h):
+// argument validation, workspace carving and launch sequencing.  Every check
+// runs on the host before anything is enqueued, so a rejected call launches
+// nothing and touches no output.
+#include <stdint.h>
+#include <string.h>
+
+#include "bissd.h"
+#include "bissd_internal.hpp"
+
+using bissd::ScanArgs;
+
+namespace {
+
+thread_local int g_last_hip = 0;
+
+constexpr int64_t kMaxElems = (int64_t)1 << 40;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_shape(const bissd_shape_t *s, int op) {
+  if (!s) return BISSD_ERR_NULL;
+  if (s->batch <= 0 || s->seqlen <= 0 || s->nheads <= 0 || s->headdim <= 0 || s->dstate <= 0 ||
+      s->ngroups <= 0 || s->chunk <= 0)
+    return BISSD_ERR_SHAPE;
+  if (s->nheads % s->ngroups != 0) return BISSD_ERR_SHAPE;
+  if (s->reserved != 0) return BISSD_ERR_SHAPE;
+  if (op != BISSD_OP_FORWARD && op != BISSD_OP_BACKWARD && op != BISSD_OP_BLOCK)
+    return BISSD_ERR_UNSUPPORTED;
+  if (s->headdim != 64) return BISSD_ERR_UNSUPPORTED;
+  if (s->dstate != 64 && s->dstate != 128) return BISSD_ERR_UNSUPPORTED;
+  if (s->chunk != 64 && s->chunk != 128 && s->chunk != 256) return BISSD_ERR_UNSUPPORTED;
+  if (s->dtype != BISSD_F32 && s->dtype != BISSD_BF16) return BISSD_ERR_UNSUPPORTED;
+  if (op == BISSD_OP_BLOCK && s->seqlen > s->chunk) return BISSD_ERR_SHAPE;
+  // grid and index limits
+  if (s->batch > (1 << 20) || s->nheads > 4096 || s->seqlen > ((int64_t)1 << 31))
+    return BISSD_ERR_UNSUPPORTED;
+  const int64_t nc = ceil_div(s->seqlen, s->chunk);
+  if (s->batch * nc * (s->chunk / 64) * 2 >= ((int64_t)1 << 31)) return BISSD_ERR_UNSUPPORTED;
+  if (s->batch * s->seqlen * s->nheads * s->headdim > kMaxElems) return BISSD_ERR_UNSUPPORTED;
+  return BISSD_OK;
+}
+
+struct WsLayout {
+  size_t states = 0, cdecay = 0, total = 0;
+};
+
+WsLayout ws_layout(const bissd_shape_t *s, int op) {
+  WsLayout w;
+  const int64_t nc = op == BISSD_OP_BLOCK ? 1 : ceil_div(s->seqlen, s->chunk);
+  const int64_t ndir = op == BISSD_OP_BLOCK ? 1 : 2;
+  const size_t st = (size_t)(ndir * s->batch * nc * s->nheads * s->headdim * s->dstate) * 4;
+  const size_t cd = (size_t)(ndir * s->batch * nc * s->nheads) * 4;
+  w.states = 0;
+  w.cdecay = align256(st);
+  w.total = w.cdecay + align256(cd);
+  return w;
+}
+
+size_t esize(const bissd_shape_t *s) { return s->dtype == BISSD_BF16 ? 2 : 4; }
+
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+  if (!a || !b || !na || !nb) return false;
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+struct Sizes {
+  size_t x, dt, bc, vec, state;
+};
+
+Sizes sizes(const bissd_shape_t *s) {
+  Sizes z;
+  const size_t e = esize(s);
+  z.x = (size_t)(s->batch * s->seqlen * s->nheads * s->headdim) * e;
+  z.dt = (size_t)(s->batch * s->seqlen * s->nheads) * e;
+  z.bc = (size_t)(s->batch * s->seqlen * s->ngroups * s->dstate) * e;
+  z.vec = (size_t)s->nheads * 4;
+  z.state = (size_t)(s->batch * s->nheads * s->headdim * s->dstate) * 4;
+  return z;
+}
+
+int check_dir(const bissd_dir_t &d) {
+  if (!d.dt || !d.A || !d.B || !d.C) return BISSD_ERR_NULL;
+  if (!aligned16(d.dt) || !aligned16(d.A) || !aligned16(d.B) || !aligned16(d.C))
+    return BISSD_ERR_ALIGN;
+  return BISSD_OK;
+}
+
+// true if `out` (n bytes) overlaps any input of the scan
+bool hits_inputs(const void *out, size_t n, const Sizes &z, const void *x, const bissd_dir_t &f,
+                 const bissd_dir_t &r, const float *D) {
+  const void *bufs[] = {x, f.dt, f.A, f.B, f.C, r.dt, r.A, r.B, r.C, D};
+  const size_t lens[] = {z.x, z.dt, z.vec, z.bc, z.bc, z.dt, z.vec, z.bc, z.bc, z.vec};
+  for (int i = 0; i < 10; ++i)
+    if (overlap(out, n, bufs[i], lens[i])) return true;
+  return false;
+}
+
+ScanArgs base_args(const bissd_shape_t *s, const void *x, const bissd_dir_t &f,
+                   const bissd_dir_t &r, const float *D) {
+  ScanArgs a;
+  memset(&a, 0, sizeof(a));
+  a.x = x;
+  a.dt[0] = f.dt;
+  a.dt[1] = r.dt;
+  a.A[0] = f.A;
+  a.A[1] = r.A;
+  a.B[0] = f.B;
+  a.B[1] = r.B;
+  a.C[0] = f.C;
+  a.C[1] = r.C;
+  a.D = D;
+  a.L = s->seqlen;
+  a.Z = (int)s->batch;
+  a.H = (int)s->nheads;
+  a.G = (int)s->ngroups;
+  a.N = (int)s->dstate;
+  a.chunk = (int)s->chunk;
+  a.dtype = s->dtype;
+  return a;
+}
+
+int finish(hipError_t e) {
+  if (e != hipSuccess) {
+    g_last_hip = (int)e;
+    return BISSD_ERR_HIP;
+  }
+  return BISSD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bissd_version(void) { return 1; }
+
+int bissd_last_hip_error(void) { return g_last_hip; }
+
+const char *bissd_status_string(int status) {
+  switch (status) {
+    case BISSD_OK: return "ok";
+    case BISSD_ERR_NULL: return "a required pointer is NULL";
+    case BISSD_ERR_SHAPE: return "bad shape";
+    case BISSD_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case BISSD_ERR_ALIGN: return "pointer not aligned to 16 bytes";
+    case BISSD_ERR_WORKSPACE: return "workspace missing or too small";
+    case BISSD_ERR_HIP: return "HIP launch failed";
+    case BISSD_ERR_ALIAS: return "an output overlaps an input";
+    default: return "unknown status";
+  }
+}
+
+size_t bissd_workspace_size(const bissd_shape_t *s, int op) {
+  if (check_shape(s, op) != BISSD_OK) return 0;
+  return ws_layout(s, op).total;
+}
+
+int bissd_forward(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, bissd_dir_t rev,
+                  const float *D, const float *init_state, void *y, float *final_state,
+                  void *workspace, size_t workspace_bytes, void *stream) {
+  int rc = check_shape(s, BISSD_OP_FORWARD);
+  if (rc) return rc;
+  if (!x || !D || !y) return BISSD_ERR_NULL;
+  if ((rc = check_dir(fwd)) || (rc = check_dir(rev))) return rc;
+  if (!aligned16(x) || !aligned16(D) || !aligned16(y) ||
+      (init_state && !aligned16(init_state)) || (final_state && !aligned16(final_state)))
+    return BISSD_ERR_ALIGN;
+  const WsLayout wl = ws_layout(s, BISSD_OP_FORWARD);
+  if (!workspace || workspace_bytes < wl.total) return BISSD_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return BISSD_ERR_ALIGN;
+  const Sizes z = sizes(s);
+  if (hits_inputs(y, z.x, z, x, fwd, rev, D) || overlap(y, z.x, init_state, z.state) ||
+      overlap(y, z.x, final_state, z.state) || overlap(y, z.x, workspace, wl.total))
+    return BISSD_ERR_ALIAS;
+  if (final_state && (hits_inputs(final_state, z.state, z, x, fwd, rev, D) ||
+                      overlap(final_state, z.state, workspace, wl.total)))
+    return BISSD_ERR_ALIAS;
+  if (hits_inputs(workspace, wl.total, z, x, fwd, rev, D) ||
+      overlap(workspace, wl.total, init_state, z.state))
+    return BISSD_ERR_ALIAS;
+
+  hipStream_t st = (hipStream_t)stream;
+  ScanArgs a = base_args(s, x, fwd, rev, D);
+  char *ws = (char *)workspace;
+  a.states = (float *)(ws + wl.states);
+  a.cdecay = (float *)(ws + wl.cdecay);
+  a.nchunks = (int)ceil_div(s->seqlen, s->chunk);
+  a.y = y;
+  a.dir0 = 0;
+  a.ndir = 2;
+  a.init_state = init_state;
+  a.final_state = final_state;
+  const int64_t PN = s->headdim * s->dstate;
+  for (int d = 0; d < 2; ++d) {
+    a.sin[d] = a.states + (int64_t)d * a.Z * a.nchunks * a.H * PN;
+    a.sin_bstride[d] = (int64_t)a.nchunks * a.H * PN;
+    a.sin_cstride[d] = (int64_t)a.H * PN;
+  }
+  hipError_t e = bissd::launch_scan_phase(a, bissd::PHASE_CHUNK_STATE, st);
+  if (e == hipSuccess) e = bissd::launch_scan_phase(a, bissd::PHASE_STATE_PASS, st);
+  if (e == hipSuccess) e = bissd::launch_scan_phase(a, bissd::PHASE_CHUNK_OUT, st);
+  return finish(e);
+}
+
+int bissd_block_update(const bissd_shape_t *s, const float *state_in, const void *x_blk,
+                       bissd_dir_t fwd, bissd_dir_t rev, const float *D, void *y_blk,
+                       float *state_out, void *workspace, size_t workspace_bytes,
+                       void *stream) {
+  int rc = check_shape(s, BISSD_OP_BLOCK);
+  if (rc) return rc;
+  if (!state_in || !x_blk || !D || !y_blk) return BISSD_ERR_NULL;
+  if ((rc = check_dir(fwd)) || (rc = check_dir(rev))) return rc;
+  if (!aligned16(state_in) || !aligned16(x_blk) || !aligned16(D) || !aligned16(y_blk) ||
+      (state_out && !aligned16(state_out)))
+    return BISSD_ERR_ALIGN;
+  const WsLayout wl = ws_layout(s, BISSD_OP_BLOCK);
+  if (!workspace || workspace_bytes < wl.total) return BISSD_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return BISSD_ERR_ALIGN;
+  const Sizes z = sizes(s);
+  if (hits_inputs(y_blk, z.x, z, x_blk, fwd, rev, D) || overlap(y_blk, z.x, state_in, z.state) ||
+      overlap(y_blk, z.x, state_out, z.state) || overlap(y_blk, z.x, workspace, wl.total))
+    return BISSD_ERR_ALIAS;
+  if (state_out && (hits_inputs(state_out, z.state, z, x_blk, fwd, rev, D) ||
+                    overlap(state_out, z.state, workspace, wl.total)))
+    return BISSD_ERR_ALIAS;
+  // state_out may equal state_in, but may not partially overlap it
+  if (state_out && state_out != state_in && overlap(state_out, z.state, state_in, z.state))
+    return BISSD_ERR_ALIAS;
+  if (hits_inputs(workspace, wl.total, z, x_blk, fwd, rev, D) ||
+      overlap(workspace, wl.total, state_in, z.state))
+    return BISSD_ERR_ALIAS;
+
+  hipStream_t st = (hipStream_t)stream;
+  ScanArgs a = base_args(s, x_blk, fwd, rev, D);
+  char *ws = (char *)workspace;
+  a.states = (float *)(ws + wl.states);
+  a.cdecay = (float *)(ws + wl.cdecay);
+  a.nchunks = 1;
+  a.y = y_blk;
+  a.dir0 = 0;
+  a.ndir = 1;  // the reverse carries nothing in or out of the block
+  a.init_state = state_in;
+  a.final_state = state_out;
+  const int64_t PN = s->headdim * s->dstate;
+  a.sin[0] = state_in;
+  a.sin_bstride[0] = (int64_t)a.H * PN;
+  a.sin_cstride[0] = 0;
+  a.sin[1] = nullptr;
+  // order matters when state_out == state_in: the output phase reads
+  // state_in before the state pass overwrites it
+  hipError_t e = hipSuccess;
+  if (state_out) e = bissd::launch_scan_phase(a, bissd::PHASE_CHUNK_STATE, st);
+  if (e == hipSuccess) e = bissd::launch_scan_phase(a, bissd::PHASE_CHUNK_OUT, st);
+  if (e == hipSuccess && state_out) e = bissd::launch_scan_phase(a, bissd::PHASE_STATE_PASS, st);
+  return finish(e);
+}
+
+int bissd_backward(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, bissd_dir_t rev,
+                   const float *D, const float *init_state, const void *dy, float *dx,
+                   bissd_grad_t gfwd, bissd_grad_t grev, float *dD, void *workspace,
+                   size_t workspace_bytes, void *stream) {
+  (void)init_state;
+  (void)workspace;
+  (void)workspace_bytes;
+  (void)stream;
+  int rc = check_shape(s, BISSD_OP_BACKWARD);
+  if (rc) return rc;
+  if (!x || !D || !dy || !dx || !dD) return BISSD_ERR_NULL;
+  if ((rc = check_dir(fwd)) || (rc = check_dir(rev))) return rc;
+  if (!gfwd.ddt || !gfwd.dA || !gfwd.dB || !gfwd.dC || !grev.ddt || !grev.dA || !grev.dB ||
+      !grev.dC)
+    return BISSD_ERR_NULL;
+  return BISSD_ERR_UNSUPPORTED;
+}
+
+}  // extern "C"

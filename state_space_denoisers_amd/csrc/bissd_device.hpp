@@ -1,0 +1,319 @@
+// bissd_device.hpp -- device building blocks of the bidirectional SSD scan
+// for CDNA4 (gfx950): MFMA fragments, LDS staging and wavefront scans.
+//
+// Matrix-core convention used throughout.  A 16x16 output tile D = A * B is
+// accumulated in 4 fp32 registers per lane: lane l holds D[4*(l/16)+i][l%16]
+// for i = 0..3.  A K-step contracts 32 values of k: lane l supplies A[l%16][k]
+// and B[k][l%16] for the 8 k values of its lane group l/16.  Which 8 k values
+// a group owns only has to agree between A and B, so two mappings are used:
+//   natural:  k = 8*(l/16) + e                       (8 contiguous values)
+//   paired :  k = 4*(l/16) + e        for e < 4,
+//             k = 16 + 4*(l/16) + e-4 for e >= 4     (two runs of 4)
+// The paired mapping lets a pair of 16x16 output tiles (two runs of 4 rows per
+// lane) be fed straight back in as the A operand of the next product.
+// bf16 operands use v_mfma_f32_16x16x32_bf16 (one instruction per K-step);
+// fp32 operands use eight v_mfma_f32_16x16x4_f32, element e of every lane in
+// instruction e, which covers the same 32 k values.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bissd {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kP = 64;        // head dim
+constexpr int kRB = 64;       // tokens per row-block (and per staged slab)
+constexpr int kThreads = 256; // 4 wavefronts of 64
+constexpr int kQmax = 256;    // largest chunk
+constexpr float kLog2e = 1.4426950408889634f;
+
+// 2^v on the transcendental unit.  Every decay in the scan is written as
+// exp(z) = 2^(z * log2 e); arguments are never positive except where a
+// bounded (< 2^40) rescale factor is intended.
+__device__ __forceinline__ float exp2_fast(float v) { return __builtin_amdgcn_exp2f(v); }
+
+__device__ __forceinline__ float to_f(float v) { return v; }
+__device__ __forceinline__ float to_f(bf16 v) { return (float)v; }
+
+template <typename T> __device__ __forceinline__ T from_f(float v);
+template <> __device__ __forceinline__ float from_f<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16 from_f<bf16>(float v) { return (bf16)v; }
+
+// ------------------------------------------------------------ global I/O
+
+__device__ __forceinline__ void gload8(float (&o)[8], const bf16 *p) {
+  const bf16x8 v = *reinterpret_cast<const bf16x8 *>(p);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = (float)v[e];
+}
+__device__ __forceinline__ void gload8(float (&o)[8], const float *p) {
+  const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
+  const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    o[e] = a[e];
+    o[4 + e] = b[e];
+  }
+}
+__device__ __forceinline__ void gstore8(bf16 *p, const float (&o)[8]) {
+  bf16x8 v;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = (bf16)o[e];
+  *reinterpret_cast<bf16x8 *>(p) = v;
+}
+__device__ __forceinline__ void gstore8(float *p, const float (&o)[8]) {
+  f32x4 a, b;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    a[e] = o[e];
+    b[e] = o[4 + e];
+  }
+  *reinterpret_cast<f32x4 *>(p) = a;
+  *reinterpret_cast<f32x4 *>(p + 4) = b;
+}
+
+// ------------------------------------------------------------- fragments
+
+template <typename T> struct Frag;
+template <> struct Frag<bf16> { bf16x8 v; };
+template <> struct Frag<float> { float v[8]; };
+
+__device__ __forceinline__ void frag_zero(Frag<bf16> &f) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f.v[e] = (bf16)0.0f;
+}
+__device__ __forceinline__ void frag_zero(Frag<float> &f) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f.v[e] = 0.0f;
+}
+__device__ __forceinline__ void frag_from(Frag<bf16> &f, const float (&x)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f.v[e] = (bf16)x[e];
+}
+__device__ __forceinline__ void frag_from(Frag<float> &f, const float (&x)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f.v[e] = x[e];
+}
+// natural mapping: 8 contiguous elements (16-byte aligned)
+__device__ __forceinline__ void frag_ld8(Frag<bf16> &f, const bf16 *p) {
+  f.v = *reinterpret_cast<const bf16x8 *>(p);
+}
+__device__ __forceinline__ void frag_ld8(Frag<float> &f, const float *p) {
+  const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
+  const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f.v[e] = a[e];
+    f.v[4 + e] = b[e];
+  }
+}
+// paired mapping: elements 0..3 from p0, 4..7 from p1
+__device__ __forceinline__ void frag_ld4x2(Frag<bf16> &f, const bf16 *p0, const bf16 *p1) {
+  const bf16x4 a = *reinterpret_cast<const bf16x4 *>(p0);
+  const bf16x4 b = *reinterpret_cast<const bf16x4 *>(p1);
+  f.v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ void frag_ld4x2(Frag<float> &f, const float *p0, const float *p1) {
+  const f32x4 a = *reinterpret_cast<const f32x4 *>(p0);
+  const f32x4 b = *reinterpret_cast<const f32x4 *>(p1);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f.v[e] = a[e];
+    f.v[4 + e] = b[e];
+  }
+}
+
+__device__ __forceinline__ void mma(f32x4 &c, const Frag<bf16> &a, const Frag<bf16> &b) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x4 &c, const Frag<float> &a, const Frag<float> &b) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[e], b.v[e], c, 0, 0, 0);
+}
+
+__device__ __forceinline__ void zero4(f32x4 &c) { c = f32x4{0.0f, 0.0f, 0.0f, 0.0f}; }
+
+// LDS row pitches (elements).  Rows of W contiguous elements read 16 bytes
+// per lane (natural mapping) get 16 extra bytes; token rows read as runs of
+// 4 (paired mapping) get 4 extra elements.  Both keep a 16-lane read phase
+// on distinct banks.
+template <typename T, int W> struct RowPitch {
+  static constexpr int value = W + 16 / (int)sizeof(T);
+};
+template <typename T> struct TokPitch {
+  static constexpr int value = kRB + 4;
+};
+
+// --------------------------------------------------------- LDS staging
+
+// Copy a slab of 64 token rows x W columns (row stride `rs` elements) into
+// LDS row-major [token][col] with pitch RowPitch<T,W>.  Rows >= nvalid read
+// as zero.
+template <typename T, int W>
+__device__ __forceinline__ void stage_rows(T *lds, const T *g, int64_t rs, int nvalid) {
+  constexpr int CG = W / 8;
+  constexpr int PT = RowPitch<T, W>::value;
+  for (int it = threadIdx.x; it < kRB * CG; it += kThreads) {
+    const int s = it / CG, c0 = (it % CG) * 8;
+    float v[8];
+    if (s < nvalid) {
+      gload8(v, g + (int64_t)s * rs + c0);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = 0.0f;
+    }
+    if constexpr (sizeof(T) == 2) {
+      bf16x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = (bf16)v[e];
+      *reinterpret_cast<bf16x8 *>(lds + s * PT + c0) = o;
+    } else {
+      gstore8(reinterpret_cast<float *>(lds) + s * PT + c0, v);
+    }
+  }
+}
+
+// Copy a slab of 64 token rows x W columns into LDS transposed, [col][token]
+// with pitch TokPitch, multiplying token row s by scale[s] (LDS, or nullptr
+// for 1) before the single rounding to T.  Rows >= nvalid read as zero.
+template <typename T, int W>
+__device__ __forceinline__ void stage_cols(T *lds, const T *g, int64_t rs, int nvalid,
+                                           const float *scale) {
+  constexpr int CG = W / 8;
+  constexpr int PT = TokPitch<T>::value;
+  if constexpr (sizeof(T) == 2) {
+    // two tokens per item so each LDS write is one 4-byte word
+    for (int it = threadIdx.x; it < (kRB / 2) * CG; it += kThreads) {
+      const int s = (it / CG) * 2, c0 = (it % CG) * 8;
+      float v0[8], v1[8];
+      if (s < nvalid) {
+        gload8(v0, g + (int64_t)s * rs + c0);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v0[e] = 0.0f;
+      }
+      if (s + 1 < nvalid) {
+        gload8(v1, g + (int64_t)(s + 1) * rs + c0);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v1[e] = 0.0f;
+      }
+      const float s0 = scale ? scale[s] : 1.0f;
+      const float s1 = scale ? scale[s + 1] : 1.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        bf16x2 pr;
+        pr[0] = (bf16)(v0[e] * s0);
+        pr[1] = (bf16)(v1[e] * s1);
+        *reinterpret_cast<bf16x2 *>(lds + (c0 + e) * PT + s) = pr;
+      }
+    }
+  } else {
+    for (int it = threadIdx.x; it < kRB * CG; it += kThreads) {
+      const int s = it / CG, c0 = (it % CG) * 8;
+      float v[8];
+      if (s < nvalid) {
+        gload8(v, g + (int64_t)s * rs + c0);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = 0.0f;
+      }
+      const float sc = scale ? scale[s] : 1.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) reinterpret_cast<float *>(lds)[(c0 + e) * PT + s] = v[e] * sc;
+    }
+  }
+}
+
+// ------------------------------------------------------ wavefront scans
+
+__device__ __forceinline__ float wave_scan_up(float v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float t = __shfl_up(v, o, 64);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+__device__ __forceinline__ float wave_scan_down(float v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float t = __shfl_down(v, o, 64);
+    if (lane + o < 64) v += t;
+  }
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Log2-decay cumulative sums of one chunk for one (direction, head), run by
+// one wavefront.  a_s = dt_s * A * log2(e) for the chunk's Q tokens (tokens
+// at or beyond qlen count as dt = 0).  Forward: lam[s] = sum_{k<=s} a_k.
+// Reverse: lam[s] = sum_{k>=s} a_k.  dtv[s] receives dt_s.  Returns the
+// largest |a_s| of the chunk (in every lane).
+template <typename T>
+__device__ __forceinline__ float chunk_decay_scan(const T *dt, int64_t stride, int qlen, int Q,
+                                                  float A2, bool reverse, float *lam,
+                                                  float *dtv) {
+  const int lane = threadIdx.x & 63;
+  const int K = Q / 64;  // 1, 2 or 4 tokens per lane
+  float a[4], d[4], amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int s = lane * K + i;
+    d[i] = (i < K && s < qlen) ? to_f(dt[(int64_t)s * stride]) : 0.0f;
+    a[i] = d[i] * A2;
+    amax = fmaxf(amax, fabsf(a[i]));
+  }
+  amax = wave_max(amax);
+  if (!reverse) {
+    float run = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      run += a[i];
+      a[i] = run;
+    }
+    const float incl = wave_scan_up(run);
+    float excl = __shfl_up(incl, 1, 64);
+    if (lane == 0) excl = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (i < K) {
+        lam[lane * K + i] = excl + a[i];
+        dtv[lane * K + i] = d[i];
+      }
+  } else {
+    float run = 0.0f;
+#pragma unroll
+    for (int i = 3; i >= 0; --i) {
+      if (i < K) {
+        run += a[i];
+        a[i] = run;
+      }
+    }
+    const float incl = wave_scan_down(run);
+    float excl = __shfl_down(incl, 1, 64);
+    if (lane == 63) excl = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (i < K) {
+        lam[lane * K + i] = excl + a[i];
+        dtv[lane * K + i] = d[i];
+      }
+  }
+  return amax;
+}
+
+}  // namespace bissd

@@ -1,0 +1,34 @@
+// bissd_internal.hpp -- launch arguments shared by the ABI layer and the
+// kernel launchers (not part of the public interface).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bissd {
+
+struct ScanArgs {
+  const void *x;
+  const void *dt[2];  // [0] forward, [1] reverse
+  const float *A[2];
+  const void *B[2];
+  const void *C[2];
+  const float *D;
+  void *y;
+  float *states;  // [ndir][Z][nchunks][H][P][N] chunk states (workspace)
+  float *cdecay;  // [ndir][Z][nchunks][H] chunk total log2-decay (workspace)
+  const float *sin[2];  // carry-in state of each chunk, per direction (nullptr = none)
+  int64_t sin_bstride[2], sin_cstride[2];
+  const float *init_state;  // forward start state for the state pass
+  float *final_state;       // forward end state written by the state pass
+  int64_t L;
+  int Z, H, G, N, chunk, nchunks;
+  int dir0, ndir;  // directions handled by the chunk-state / state-pass phases
+  int dtype;       // 0 fp32, 1 bf16
+};
+
+enum { PHASE_CHUNK_STATE = 0, PHASE_STATE_PASS = 1, PHASE_CHUNK_OUT = 2 };
+
+hipError_t launch_scan_phase(const ScanArgs &a, int phase, hipStream_t st);
+
+}  // namespace bissd

@@ -1,0 +1,136 @@
+"""The C ABI on the host: the library loads, exports every symbol the header
+declares, and rejects bad arguments before anything reaches a device.
+
+Pointers here are fake host addresses: validation only compares and
+alignment-checks them, it never dereferences them.
+"""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from state_space_denoisers_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_abi.LIB_PATH):
+        from state_space_denoisers_amd import build
+        build.build()
+    return _abi.load()
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "bissd.h")).read()
+    return sorted(set(re.findall(r"^\w[\w\s\*]*?\b(bissd_\w+)\s*\(", text, re.M)))
+
+
+def test_header_and_binding_agree():
+    assert sorted(_abi.EXPORTS) == header_functions()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    assert lib.bissd_version() == 1
+    assert lib.bissd_last_hip_error() == 0
+
+
+def test_no_torch_types_in_the_header():
+    text = open(os.path.join(ROOT, "include", "bissd.h")).read()
+    for banned in ("torch", "at::", "Tensor", "c10"):
+        assert banned not in text, banned
+    assert 'extern "C"' in text
+
+
+def shape(**kw):
+    d = dict(batch=2, seqlen=300, nheads=8, headdim=64, dstate=128, ngroups=1, chunk=256,
+             dtype=_abi.BISSD_BF16, reserved=0)
+    d.update(kw)
+    return _abi.Shape(**d)
+
+
+A = 1 << 20  # fake, 16-byte aligned addresses far apart
+
+
+def addr(i):
+    return C.c_void_p(A * (i + 1))
+
+
+def dirs(base):
+    return _abi.Dir(addr(base), addr(base + 1), addr(base + 2), addr(base + 3))
+
+
+def call_forward(lib, s, **over):
+    args = dict(x=addr(0), fwd=dirs(1), rev=dirs(5), D=addr(9), init=None, y=addr(10),
+                final=None, ws=addr(12), nws=1 << 40, stream=None)
+    args.update(over)
+    return lib.bissd_forward(C.byref(s) if s is not None else None, args["x"], args["fwd"],
+                             args["rev"], args["D"], args["init"], args["y"], args["final"],
+                             args["ws"], C.c_size_t(args["nws"]), args["stream"])
+
+
+def test_workspace_size(lib):
+    s = shape()
+    n = lib.bissd_workspace_size(C.byref(s), _abi.OP_FORWARD)
+    nc = (300 + 255) // 256
+    assert n >= 2 * 2 * nc * 8 * 64 * 128 * 4
+    assert lib.bissd_workspace_size(C.byref(shape(headdim=32)), 0) == 0
+    assert lib.bissd_workspace_size(None, 0) == 0
+    # linear in L (constant-size state per chunk)
+    n1 = lib.bissd_workspace_size(C.byref(shape(seqlen=256 * 8)), 0)
+    n2 = lib.bissd_workspace_size(C.byref(shape(seqlen=256 * 16)), 0)
+    assert 1.9 < n2 / n1 < 2.1
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(batch=0), -2), (dict(seqlen=0), -2), (dict(nheads=6, ngroups=4), -2),
+    (dict(headdim=32), -3), (dict(dstate=96), -3), (dict(chunk=100), -3),
+    (dict(dtype=7), -3), (dict(reserved=1), -2),
+])
+def test_bad_shapes(lib, over, code):
+    assert call_forward(lib, shape(**over)) == code
+
+
+def test_null_and_alignment(lib):
+    s = shape()
+    assert call_forward(lib, None) == -1
+    assert call_forward(lib, s, x=None) == -1
+    assert call_forward(lib, s, y=None) == -1
+    bad = _abi.Dir(addr(1), None, addr(3), addr(4))
+    assert call_forward(lib, s, fwd=bad) == -1
+    assert call_forward(lib, s, x=C.c_void_p(A + 8)) == -4
+    assert call_forward(lib, s, ws=None) == -5
+    assert call_forward(lib, s, nws=16) == -5
+
+
+def test_aliasing_is_rejected(lib):
+    s = shape()
+    assert call_forward(lib, s, y=addr(0)) == -7          # y over x
+    assert call_forward(lib, s, ws=addr(10)) == -7        # workspace over y
+    assert call_forward(lib, s, final=addr(9)) == -7      # final_state over D
+
+
+def test_block_update_validation(lib):
+    s = shape(seqlen=300, chunk=256)
+    rc = lib.bissd_block_update(C.byref(s), addr(20), addr(0), dirs(1), dirs(5), addr(9),
+                                addr(10), None, addr(12), C.c_size_t(1 << 40), None)
+    assert rc == -2  # block longer than chunk
+    s = shape(seqlen=64, chunk=64)
+    rc = lib.bissd_block_update(C.byref(s), None, addr(0), dirs(1), dirs(5), addr(9),
+                                addr(10), None, addr(12), C.c_size_t(1 << 40), None)
+    assert rc == -1
+    # state_out partially overlapping state_in
+    rc = lib.bissd_block_update(C.byref(s), addr(20), addr(0), dirs(1), dirs(5), addr(9),
+                                addr(10), C.c_void_p(A * 21 + 4096), addr(12),
+                                C.c_size_t(1 << 40), None)
+    assert rc == -7
+
+
+def test_status_strings(lib):
+    for code in _abi.STATUS:
+        assert lib.bissd_status_string(code)
+    assert b"unknown" in lib.bissd_status_string(99)

@@ -1,0 +1,128 @@
+"""GPU parity of the block update with partial bidirectionality
+(bissd_block_update) against the fp64 oracle, plus cache consistency
+between the block update and the full-sequence scan."""
+import numpy as np
+import pytest
+import torch
+
+import state_space_denoisers_amd as ssd
+from oracle import oracle as O
+from synth import gen
+from tests.gpu_util import TOL, dirs, f32_dev, host, maxrel, to_dev
+
+pytestmark = pytest.mark.gpu
+
+W = gen.WORKLOADS
+
+
+def prefix_state(w, blk_inp, length):
+    """Oracle forward state after a seeded synthetic prefix of `length`
+    tokens (the block's own A_f), rounded to fp32 as the cache holds it."""
+    pre = gen.make_prefix(w, length)
+    Z, H = w.Z, w.H
+    full = dict(pre)
+    full["A_f"] = blk_inp["A_f"]
+    full["dt_r"] = pre["dt_f"]
+    full["A_r"] = blk_inp["A_r"]
+    full["B_r"] = np.zeros_like(pre["B_f"])
+    full["C_r"] = np.zeros_like(pre["C_f"])
+    full["D"] = np.zeros(H)
+    return gen.round_fp32(O.forward(full, final_state=True)["final_state"])
+
+
+def gpu_block(inp, dtype, state_in, chunk=None, alias=False, commit=True):
+    T = to_dev(inp, dtype)
+    fwd, rev = dirs(T)
+    s_in = f32_dev(state_in)
+    kw = {}
+    if alias:
+        kw["state_out"] = s_in
+    y, so = ssd.bissd_block_update(s_in, T["x"], fwd, rev, T["D"], chunk=chunk, commit=commit, **kw)
+    torch.cuda.synchronize()
+    return host(y), (host(so) if so is not None else None)
+
+
+@pytest.mark.parametrize("mode", ("full", "fwd", "rev"))
+def test_block_update_workload(mode):
+    """Z=4, 64-token active block with 16 mask-token positions per row, 24
+    heads, N=128, bf16, cached fp32 prefix state from a 2048-token prefix."""
+    w = W["block_update"]
+    inp = gen.make_inputs(w, mode=mode)
+    S0 = prefix_state(w, inp, 2048)
+    print("block_update", mode, flush=True)
+    y, so = gpu_block(inp, "bf16", S0)
+    ry, rso = O.block_update(inp, S0)
+    assert maxrel(y, ry) <= TOL["bf16"]
+    assert maxrel(so, rso) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dtype", ("fp32", "bf16"))
+@pytest.mark.parametrize("Lb,chunk", [(1, 64), (17, 64), (64, 64), (100, 128), (256, 256), (5, 256)])
+def test_block_lengths(dtype, Lb, chunk):
+    w = W["block_update"].replace(Z=2, L=Lb, H=4, chunk=chunk, dtype=dtype, mask_count=0, seed=Lb)
+    for mode in ("fwd", "rev", "full"):
+        inp = gen.make_inputs(w, mode=mode)
+        S0 = gen.round_fp32(np.random.default_rng(Lb).standard_normal((2, 4, 64, 128)) * 0.05)
+        y, so = gpu_block(inp, dtype, S0, chunk=chunk)
+        ry, rso = O.block_update(inp, S0)
+        assert maxrel(y, ry) <= TOL[dtype], mode
+        assert maxrel(so, rso) <= TOL[dtype], mode
+
+
+def test_state_out_may_alias_state_in():
+    w = W["block_update"].replace(Z=2, H=8, mask_count=4, seed=9)
+    inp = gen.make_inputs(w)
+    S0 = gen.round_fp32(np.random.default_rng(1).standard_normal((2, 8, 64, 128)) * 0.05)
+    y, so = gpu_block(inp, "bf16", S0, alias=True)
+    ry, rso = O.block_update(inp, S0)
+    assert maxrel(y, ry) <= TOL["bf16"]
+    assert maxrel(so, rso) <= TOL["bf16"]
+
+
+def test_no_commit_leaves_only_y():
+    w = W["block_update"].replace(Z=1, H=4, mask_count=4, seed=12)
+    inp = gen.make_inputs(w, mode="fwd")
+    S0 = gen.round_fp32(np.random.default_rng(2).standard_normal((1, 4, 64, 128)) * 0.05)
+    y, so = gpu_block(inp, "bf16", S0, commit=False)
+    assert so is None
+    assert maxrel(y, O.block_update(inp, S0)[0]) <= TOL["bf16"]
+
+
+def test_block_update_equals_forward_from_the_same_state():
+    w = W["block_update"].replace(Z=2, H=8, seed=13)
+    inp = gen.make_inputs(w)
+    S0 = gen.round_fp32(np.random.default_rng(3).standard_normal((2, 8, 64, 128)) * 0.05)
+    T = to_dev(inp, "bf16")
+    fwd, rev = dirs(T)
+    s_in = f32_dev(S0)
+    fs = torch.empty_like(s_in)
+    yf = ssd.bissd_forward(T["x"], fwd, rev, T["D"], chunk=64, init_state=s_in, final_state=fs)
+    yb, so = ssd.bissd_block_update(s_in, T["x"], fwd, rev, T["D"], chunk=64)
+    torch.cuda.synchronize()
+    assert torch.equal(yf, yb)
+    assert torch.equal(fs, so)
+
+
+def test_cache_consistency_prefix_then_block():
+    """Forward scan over [prefix | block] restricted to the block equals the
+    block update from the prefix's final state (forward part), and the
+    block's reverse part equals a scan of the block alone."""
+    Lp, Lb = 1000, 64
+    w = W["layer130m_L1k"].replace(Z=2, L=Lp + Lb, H=8, seed=21)
+    for mode in ("fwd", "rev"):
+        full = gen.make_inputs(w, mode=mode)
+        pre = {k: (v[:, :Lp] if v.ndim > 1 else v) for k, v in full.items()}
+        blk = {k: (v[:, Lp:] if v.ndim > 1 else v) for k, v in full.items()}
+        Tf, Tp, Tb = to_dev(full, "bf16"), to_dev(pre, "bf16"), to_dev(blk, "bf16")
+        fs = torch.empty((2, 8, 64, 128), device=Tp["x"].device)
+        ssd.bissd_forward(Tp["x"], *dirs(Tp), Tp["D"], chunk=256, final_state=fs)
+        y_full = ssd.bissd_forward(Tf["x"], *dirs(Tf), Tf["D"], chunk=256)
+        y_blk, _ = ssd.bissd_block_update(fs, Tb["x"], *dirs(Tb), Tb["D"], chunk=64)
+        y_alone = ssd.bissd_forward(Tb["x"], *dirs(Tb), Tb["D"], chunk=64)
+        torch.cuda.synchronize()
+        if mode == "fwd":
+            ref = O.forward(full)[:, Lp:]
+            assert maxrel(host(y_blk), ref) <= TOL["bf16"]
+            assert maxrel(host(y_blk), host(y_full)[:, Lp:]) <= TOL["bf16"]
+        else:
+            assert torch.equal(y_blk, y_alone)
