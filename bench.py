@@ -1,0 +1,395 @@
+#!/usr/bin/env python3
+"""Throughput of the bidirectional SSD (Mamba-2) scan on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one bissd_forward call (chunk states -> carry pass -> fused
+bidirectional output) over the 130M-class layer workload: batch 8, L=1024,
+24 heads x head dim 64, d_state 128, one B/C group, chunk 256, bf16 inputs
+with fp32 accumulation, synthetic seeded inputs already resident in HBM.
+W untimed warm-up steps, then exactly K timed steps between two device
+synchronisations; `value` is tokens per second over the timed region.
+
+The same run also measures, live with HIP events on the launch stream, the
+average duration of each of the three kernels (via bissd_forward_phase), the
+long-context L=65536 scan, and the block update with a cached 262,144-token
+prefix state; and times the fp64 CPU oracle on a bounded sample of the same
+workload.  One JSON line is printed.
+
+Profiling helpers (for rocprofv3 runs):
+    python bench.py --profile-phase {0,1,2,all} [--workload W] [--iters R]
+    python bench.py --copy-calibrate
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "bidir SSD scan tokens/s at L=1K/65K; achieved HBM GB/s and MFMA %"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
+PHASE_NAMES = {0: "k1_chunk_state", 1: "k2_state_pass", 2: "k3_chunk_out"}
+KERNEL_SOURCES = ("state_space_denoisers_amd/csrc/bissd_fwd.hip",
+                  "state_space_denoisers_amd/csrc/bissd_device.hpp")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_sha() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ------------------------------------------------------------------ inputs
+
+def device_inputs(w, mode="full"):
+    import torch
+    from synth import gen
+    inp = gen.make_inputs(w, mode=mode)
+    dev = torch.device("cuda", 0)
+    T = {k: gen.as_torch(inp[k], w.dtype, dev) for k in
+         ("x", "dt_f", "B_f", "C_f", "dt_r", "B_r", "C_r")}
+    for k in ("A_f", "A_r", "D"):
+        T[k] = gen.as_torch(inp[k], "fp32", dev)
+    return inp, T
+
+
+def dirs(T):
+    return ((T["dt_f"], T["A_f"], T["B_f"], T["C_f"]),
+            (T["dt_r"], T["A_r"], T["B_r"], T["C_r"]))
+
+
+class Forward:
+    """Preallocated forward call on one workload."""
+
+    def __init__(self, w):
+        import torch
+        import state_space_denoisers_amd as ssd
+        from state_space_denoisers_amd import _abi
+        self.ssd, self.w = ssd, w
+        self.inp, self.T = device_inputs(w)
+        self.fwd, self.rev = dirs(self.T)
+        self.y = torch.empty_like(self.T["x"])
+        shape = ssd.shape_of(self.T["x"], self.T["B_f"], w.chunk)
+        n = ssd.bissd_workspace_size(shape, _abi.OP_FORWARD)
+        self.ws = torch.empty(n, dtype=torch.uint8, device=self.y.device)
+
+    def __call__(self):
+        self.ssd.bissd_forward(self.T["x"], self.fwd, self.rev, self.T["D"], chunk=self.w.chunk,
+                               y=self.y, workspace=self.ws)
+
+    def phase(self, p):
+        self.ssd.bissd_forward_phase(p, self.T["x"], self.fwd, self.rev, self.T["D"],
+                                     chunk=self.w.chunk, y=self.y, workspace=self.ws)
+
+
+# ----------------------------------------------------------------- timing
+
+def event_time_ms(fn, reps):
+    """Average ms per call of fn over reps calls, HIP events on the current
+    stream (the stream every library launch goes to)."""
+    import torch
+    s = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(s)
+    for _ in range(reps):
+        fn()
+    b.record(s)
+    b.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def phase_times_us(f: Forward, reps):
+    import torch
+    f()
+    torch.cuda.synchronize()
+    t0 = event_time_ms(lambda: f.phase(0), reps)
+    t01 = event_time_ms(lambda: (f.phase(0), f.phase(1)), reps)
+    t2 = event_time_ms(lambda: f.phase(2), reps)
+    f()  # leave a consistent workspace / y
+    torch.cuda.synchronize()
+    return {PHASE_NAMES[0]: 1e3 * t0, PHASE_NAMES[1]: 1e3 * max(t01 - t0, 0.0),
+            PHASE_NAMES[2]: 1e3 * t2}
+
+
+def per_token_bytes(w):
+    """Algorithmic HBM bytes per token of the whole path: read x, dt and
+    B/C of both directions once, write y once."""
+    e = 2 if w.dtype == "bf16" else 4
+    return 2 * w.H * w.P * e + 2 * w.H * e + 4 * w.G * w.N * e
+
+
+def k3_flops_per_token(w):
+    """Matrix-core work of the fused output kernel per token (both
+    directions): C.B^T on causal 64x64 block pairs, the masked product with
+    x per head, and the carry-in contraction C S^T per head."""
+    nrb = w.chunk // 64
+    pairs = nrb * (nrb + 1) / 2 / nrb          # block pairs per row-block, per direction
+    gram = pairs * 64 * 64 * w.N * 2 / 64 * w.G
+    intra = pairs * 64 * 64 * w.P * 2 / 64 * w.H
+    inter = 2 * w.N * w.P * w.H
+    return 2 * (gram + intra + inter)
+
+
+def phase_bytes_per_token(w, phase):
+    e = 2 if w.dtype == "bf16" else 4
+    state_bytes = 2 * w.H * w.P * w.N * 4 / w.chunk   # both directions
+    if phase == 0:
+        return w.H * w.P * e + 2 * w.H * e + 2 * w.G * w.N * e + state_bytes
+    if phase == 1:
+        return 2 * state_bytes
+    return per_token_bytes(w)
+
+
+def stored_traffic(kernel, workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", "counters.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+        rec = d["kernels"][f"{kernel}@{workload}"]
+        if rec.get("source_sha") != source_sha():
+            return None
+        return float(rec["fetch_bytes"] + rec["write_bytes"])
+    except Exception:
+        return None
+
+
+# ------------------------------------------------------------ cpu baseline
+
+def cpu_baseline(w, budget_s=12.0):
+    from oracle import oracle as O
+    from synth import gen
+    inp = gen.make_inputs(w)
+    n = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or O.thread_count(0)
+    n = min(n, O.thread_count(0))
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        O.forward(inp, nthreads=n)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or el * (reps + 1) / reps > 30.0:
+            break
+    return {"value": reps * w.tokens / el, "unit": "tokens/s", "cores": n, "kind": "oracle",
+            "sample": f"{reps} x the full {w.name} batch ({w.Z}x{w.L} tokens, 24 heads, both "
+                      f"directions, fp64 sequential recurrence), {el:.1f} s wall"}
+
+
+# ------------------------------------------------------------ extra cases
+
+def bench_long(steps):
+    from synth import gen
+    import torch
+    w = gen.WORKLOADS["long_L65k"]
+    f = Forward(w)
+    for _ in range(2):
+        f()
+    torch.cuda.synchronize()
+    ms = event_time_ms(f, steps)
+    ph = phase_times_us(f, max(3, steps // 2))
+    return {"workload": w.name, "tokens_per_s": w.tokens / (ms * 1e-3), "ms_per_call": ms,
+            "hbm_algorithmic_GBs": per_token_bytes(w) * w.tokens / (ms * 1e-3) / 1e9,
+            "kernels_us": ph}
+
+
+def bench_block(reps):
+    """Block update on Z=4 rows of a 64-token active block (16 mask-token
+    positions per row) continuing from the forward state of a 262,144-token
+    prefix.  The prefix is drawn on the device and its state computed by
+    bissd_forward (final_state)."""
+    import torch
+    import state_space_denoisers_amd as ssd
+    from synth import gen
+    w = gen.WORKLOADS["block_update"]
+    dev = torch.device("cuda", 0)
+    inp, T = device_inputs(w)
+    fwd, rev = dirs(T)
+    pre = gen.prefix_on_device(w, w.prefix_len, dev)
+    state = torch.empty((w.Z, w.H, w.P, w.N), dtype=torch.float32, device=dev)
+    pf = (pre["dt_f"], T["A_f"], pre["B_f"], pre["C_f"])
+    ssd.bissd_forward(pre["x"], pf, pf, T["D"], chunk=256, final_state=state)
+    torch.cuda.synchronize()
+    del pre
+    y = torch.empty_like(T["x"])
+    s_out = torch.empty_like(state)
+    from state_space_denoisers_amd import _abi
+    shape = ssd.shape_of(T["x"], T["B_f"], w.chunk)
+    ws = torch.empty(max(256, ssd.bissd_workspace_size(shape, _abi.OP_BLOCK)),
+                     dtype=torch.uint8, device=dev)
+
+    def upd(commit):
+        ssd.bissd_block_update(state, T["x"], fwd, rev, T["D"], chunk=w.chunk, y_blk=y,
+                               state_out=s_out if commit else None, commit=commit, workspace=ws)
+
+    out = {"workload": w.name, "prefix_tokens": w.prefix_len, "block_tokens": w.L, "batch": w.Z}
+    for commit in (False, True):
+        for _ in range(5):
+            upd(commit)
+        torch.cuda.synchronize()
+        ms = event_time_ms(lambda: upd(commit), reps)
+        key = "commit" if commit else "no_commit"
+        out[f"us_per_update_{key}"] = 1e3 * ms
+        # replay of a captured HIP graph of the same call
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            upd(commit)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=s):
+                upd(commit)
+        torch.cuda.current_stream().wait_stream(s)
+        g.replay()
+        torch.cuda.synchronize()
+        out[f"us_per_update_{key}_graph"] = 1e3 * event_time_ms(g.replay, reps)
+        del g
+    return out
+
+
+# ------------------------------------------------------------- profiling
+
+def profile_phase(args):
+    import torch
+    from synth import gen
+    w = gen.WORKLOADS[args.workload]
+    f = Forward(w)
+    f()
+    torch.cuda.synchronize()
+    print(f"profiling {args.profile_phase} on {w.name} x{args.iters}", flush=True)
+    for _ in range(args.iters):
+        if args.profile_phase == "all":
+            f()
+        else:
+            f.phase(int(args.profile_phase))
+    torch.cuda.synchronize()
+    print("done", flush=True)
+
+
+def copy_calibrate():
+    """A plain device copy of known size, for scaling HBM byte counters."""
+    import torch
+    n = 1 << 28  # 256 MiB
+    a = torch.ones(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(f"copy_calibrate bytes_read={n} bytes_written={n} launches=5", flush=True)
+
+
+# ------------------------------------------------------------------ main
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--profile-phase", choices=["0", "1", "2", "all"])
+    ap.add_argument("--workload", default="layer130m_L1k")
+    ap.add_argument("--iters", type=int, default=20)
+    ap.add_argument("--copy-calibrate", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(sharding is described in the design notes); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.copy_calibrate:
+        return copy_calibrate()
+    if args.profile_phase is not None:
+        return profile_phase(args)
+
+    from synth import gen
+    w = gen.WORKLOADS["layer130m_L1k"]
+    log(f"bench: {w.name} Z={w.Z} L={w.L} H={w.H} P={w.P} N={w.N} chunk={w.chunk} {w.dtype}")
+    f = Forward(w)
+    for _ in range(args.warmup):
+        f()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(s)
+    for _ in range(args.steps):
+        f()
+    ev1.record(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = 1e3 * wall / args.steps
+    ev_ms = ev0.elapsed_time(ev1) / args.steps
+    tokens = w.tokens
+    log(f"bench: {ms_step * 1e3:.1f} us/step wall, {ev_ms * 1e3:.1f} us/step events")
+
+    ph = phase_times_us(f, max(20, args.steps // 4))
+    log(f"bench: kernels {ph}")
+    dom = max(ph, key=ph.get)
+    pidx = {v: k for k, v in PHASE_NAMES.items()}[dom]
+    dur_s = ph[dom] * 1e-6
+    alg_bytes = phase_bytes_per_token(w, pidx) * tokens
+    achieved = alg_bytes / dur_s / 1e9
+    roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": stored_traffic(dom, w.name),
+            "algorithmic_bytes_per_launch": alg_bytes, "avg_launch_us": round(ph[dom], 2)}
+    mfma = None
+    if pidx == 2 or PHASE_NAMES[2] in ph:
+        fl = k3_flops_per_token(w) * tokens
+        mfma = {"kernel": PHASE_NAMES[2], "achieved_TFLOPs": round(fl / (ph[PHASE_NAMES[2]] * 1e-6) / 1e12, 1),
+                "peak_TFLOPs": BF16_PEAK_TFLOPS,
+                "frac": round(fl / (ph[PHASE_NAMES[2]] * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                "flops_per_launch": fl}
+
+    extra = {"kernels_us": {k: round(v, 2) for k, v in ph.items()},
+             "path_hbm_algorithmic_GBs": round(per_token_bytes(w) * tokens / (ev_ms * 1e-3) / 1e9, 1),
+             "k3_mfma": mfma}
+    if not args.no_extra:
+        try:
+            extra["long_L65k"] = bench_long(max(5, args.steps // 20))
+            log(f"bench: long {extra['long_L65k']['tokens_per_s']:.3e} tokens/s")
+        except Exception as exc:  # report, do not hide
+            extra["long_L65k"] = {"error": repr(exc)}
+        try:
+            extra["block_update"] = bench_block(max(50, args.steps))
+            log(f"bench: block {extra['block_update']}")
+        except Exception as exc:
+            extra["block_update"] = {"error": repr(exc)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w)
+        log(f"bench: cpu baseline {cpu}")
+
+    out = {"metric": METRIC, "value": tokens / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic",
+           "config": {"workload": w.name, "batch": w.Z, "seq_len": w.L, "heads": w.H,
+                      "headdim": w.P, "dstate": w.N, "ngroups": w.G, "chunk": w.chunk,
+                      "parallelism": "none (1 GPU)"},
+           "roofline": roof, "cpu_baseline": cpu, "extra": extra,
+           "kernel_source_sha": source_sha()}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -159,6 +159,21 @@ int bissd_block_update(const bissd_shape_t *shape, const float *state_in,
                        const float *D, void *y_blk, float *state_out, void *workspace,
                        size_t workspace_bytes, void *stream);
 
+/*
+ * Diagnostics for timing and profiling single kernels: enqueue only one
+ * phase of bissd_forward with the same arguments and validation.
+ *   phase 0: per-chunk local states and chunk decays (written to workspace)
+ *   phase 1: carry pass over chunks (workspace in place; final_state)
+ *   phase 2: fused bidirectional output (reads workspace, writes y)
+ * A phase reads what the phases before it left in the same workspace, so
+ * phase 2 repeated after one full bissd_forward recomputes the same y.
+ * Phase 1 rewrites the workspace in place and is not idempotent.
+ */
+int bissd_forward_phase(const bissd_shape_t *shape, const void *x, bissd_dir_t fwd,
+                        bissd_dir_t rev, const float *D, const float *init_state, void *y,
+                        float *final_state, void *workspace, size_t workspace_bytes,
+                        void *stream, int phase);
+
 /* Text of a status code (static storage). */
 const char *bissd_status_string(int status);
 

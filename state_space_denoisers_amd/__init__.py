@@ -22,7 +22,7 @@ import torch
 
 from . import _abi
 
-__all__ = ["Dir", "bissd_forward", "bissd_block_update", "bissd_backward",
+__all__ = ["Dir", "bissd_forward", "bissd_forward_phase", "bissd_block_update", "bissd_backward",
            "bissd_workspace_size", "shape_of", "library_path", "BissdError"]
 
 BissdError = _abi.BissdError
@@ -103,6 +103,22 @@ def bissd_forward(x: torch.Tensor, fwd, rev, D: torch.Tensor, *, chunk: int = 25
                            C.c_size_t(nws), _stream(x.device, stream))
     _abi.check("bissd_forward", st)
     return y
+
+
+def bissd_forward_phase(phase: int, x: torch.Tensor, fwd, rev, D: torch.Tensor, *,
+                        chunk: int = 256, y: torch.Tensor, workspace: torch.Tensor,
+                        init_state: Optional[torch.Tensor] = None,
+                        final_state: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Enqueue one phase of bissd_forward (0 chunk states, 1 carry pass,
+    2 output) for timing single kernels (include/bissd.h)."""
+    lib = _abi.load()
+    fwd, rev = Dir(*fwd), Dir(*rev)
+    shape = shape_of(x, fwd.B, chunk)
+    st = lib.bissd_forward_phase(C.byref(shape), _ptr(x), _dir(fwd), _dir(rev), _ptr(D),
+                                 _ptr(init_state), _ptr(y), _ptr(final_state), _ptr(workspace),
+                                 C.c_size_t(workspace.numel() * workspace.element_size()),
+                                 _stream(x.device, stream), int(phase))
+    _abi.check("bissd_forward_phase", st)
 
 
 def bissd_block_update(state_in: torch.Tensor, x_blk: torch.Tensor, fwd, rev,

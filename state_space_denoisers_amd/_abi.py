@@ -24,7 +24,8 @@ STATUS = {
 
 # every symbol include/bissd.h declares
 EXPORTS = ("bissd_workspace_size", "bissd_forward", "bissd_backward", "bissd_block_update",
-           "bissd_status_string", "bissd_last_hip_error", "bissd_version")
+           "bissd_forward_phase", "bissd_status_string", "bissd_last_hip_error",
+           "bissd_version")
 
 
 class Shape(C.Structure):
@@ -71,6 +72,8 @@ def load(path: str = LIB_PATH) -> C.CDLL:
         lib.bissd_forward.argtypes = [C.POINTER(Shape), C.c_void_p, Dir, Dir, C.c_void_p,
                                       C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                       C.c_size_t, C.c_void_p]
+        lib.bissd_forward_phase.restype = C.c_int
+        lib.bissd_forward_phase.argtypes = lib.bissd_forward.argtypes + [C.c_int]
         lib.bissd_backward.restype = C.c_int
         lib.bissd_backward.argtypes = [C.POINTER(Shape), C.c_void_p, Dir, Dir, C.c_void_p,
                                        C.c_void_p, C.c_void_p, C.c_void_p, Grad, Grad,

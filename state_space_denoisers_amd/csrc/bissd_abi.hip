@@ -43,18 +43,23 @@ int check_shape(const bissd_shape_t *s, int op) {
   return BISSD_OK;
 }
 
+// Workspace: fp32 chunk-local states, the carry-in states in the compute
+// dtype (forward only; the block update reads its fp32 start state
+// directly) and the chunk log2-decays.
 struct WsLayout {
-  size_t states = 0, cdecay = 0, total = 0;
+  size_t states = 0, sin_t = 0, cdecay = 0, total = 0;
 };
 
 WsLayout ws_layout(const bissd_shape_t *s, int op) {
   WsLayout w;
   const int64_t nc = op == BISSD_OP_BLOCK ? 1 : ceil_div(s->seqlen, s->chunk);
   const int64_t ndir = op == BISSD_OP_BLOCK ? 1 : 2;
-  const size_t st = (size_t)(ndir * s->batch * nc * s->nheads * s->headdim * s->dstate) * 4;
+  const size_t nst = (size_t)(ndir * s->batch * nc * s->nheads * s->headdim * s->dstate);
+  const size_t esz = s->dtype == BISSD_BF16 ? 2 : 4;
   const size_t cd = (size_t)(ndir * s->batch * nc * s->nheads) * 4;
   w.states = 0;
-  w.cdecay = align256(st);
+  w.sin_t = align256(nst * 4);
+  w.cdecay = w.sin_t + (op == BISSD_OP_BLOCK ? 0 : align256(nst * esz));
   w.total = w.cdecay + align256(cd);
   return w;
 }
@@ -158,9 +163,9 @@ size_t bissd_workspace_size(const bissd_shape_t *s, int op) {
   return ws_layout(s, op).total;
 }
 
-int bissd_forward(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, bissd_dir_t rev,
-                  const float *D, const float *init_state, void *y, float *final_state,
-                  void *workspace, size_t workspace_bytes, void *stream) {
+static int forward_impl(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, bissd_dir_t rev,
+                        const float *D, const float *init_state, void *y, float *final_state,
+                        void *workspace, size_t workspace_bytes, void *stream, int phase) {
   int rc = check_shape(s, BISSD_OP_FORWARD);
   if (rc) return rc;
   if (!x || !D || !y) return BISSD_ERR_NULL;
@@ -194,15 +199,33 @@ int bissd_forward(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, bissd_
   a.init_state = init_state;
   a.final_state = final_state;
   const int64_t PN = s->headdim * s->dstate;
+  a.sin_t = ws + wl.sin_t;
+  const size_t esz = s->dtype == BISSD_BF16 ? 2 : 4;
   for (int d = 0; d < 2; ++d) {
-    a.sin[d] = a.states + (int64_t)d * a.Z * a.nchunks * a.H * PN;
+    a.sin[d] = (const char *)a.sin_t + (size_t)d * a.Z * a.nchunks * a.H * PN * esz;
     a.sin_bstride[d] = (int64_t)a.nchunks * a.H * PN;
     a.sin_cstride[d] = (int64_t)a.H * PN;
+    a.sin_f32[d] = 0;
   }
-  hipError_t e = bissd::launch_scan_phase(a, bissd::PHASE_CHUNK_STATE, st);
-  if (e == hipSuccess) e = bissd::launch_scan_phase(a, bissd::PHASE_STATE_PASS, st);
-  if (e == hipSuccess) e = bissd::launch_scan_phase(a, bissd::PHASE_CHUNK_OUT, st);
+  hipError_t e = hipSuccess;
+  for (int ph = bissd::PHASE_CHUNK_STATE; ph <= bissd::PHASE_CHUNK_OUT && e == hipSuccess; ++ph)
+    if (phase < 0 || phase == ph) e = bissd::launch_scan_phase(a, ph, st);
   return finish(e);
+}
+
+int bissd_forward(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, bissd_dir_t rev,
+                  const float *D, const float *init_state, void *y, float *final_state,
+                  void *workspace, size_t workspace_bytes, void *stream) {
+  return forward_impl(s, x, fwd, rev, D, init_state, y, final_state, workspace, workspace_bytes,
+                      stream, -1);
+}
+
+int bissd_forward_phase(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, bissd_dir_t rev,
+                        const float *D, const float *init_state, void *y, float *final_state,
+                        void *workspace, size_t workspace_bytes, void *stream, int phase) {
+  if (phase < 0 || phase > 2) return BISSD_ERR_UNSUPPORTED;
+  return forward_impl(s, x, fwd, rev, D, init_state, y, final_state, workspace, workspace_bytes,
+                      stream, phase);
 }
 
 int bissd_block_update(const bissd_shape_t *s, const float *state_in, const void *x_blk,
@@ -248,7 +271,9 @@ int bissd_block_update(const bissd_shape_t *s, const float *state_in, const void
   a.sin[0] = state_in;
   a.sin_bstride[0] = (int64_t)a.H * PN;
   a.sin_cstride[0] = 0;
+  a.sin_f32[0] = 1;
   a.sin[1] = nullptr;
+  a.sin_t = nullptr;
   // order matters when state_out == state_in: the output phase reads
   // state_in before the state pass overwrites it
   hipError_t e = hipSuccess;

@@ -231,6 +231,138 @@ __device__ __forceinline__ void stage_cols(T *lds, const T *g, int64_t rs, int n
   }
 }
 
+// ------------------------------------------------ register-prefetched slabs
+//
+// A slab is 64 token rows of a row-major global tensor.  Its bytes are
+// fetched as 16-byte vectors spread over the workgroup into registers
+// (`prefetch`), so the loads of the next slab are in flight while the
+// current one is being multiplied, and later written into LDS (`commit`).
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x4 gload16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+__device__ __forceinline__ u32x4 zero16() { return u32x4{0u, 0u, 0u, 0u}; }
+
+// 16 raw bytes holding EPV elements of T, widened to fp32
+__device__ __forceinline__ void unpack16(float (&o)[8], u32x4 v, const bf16 *) {
+  const bf16x8 b = __builtin_bit_cast(bf16x8, v);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = (float)b[e];
+}
+__device__ __forceinline__ void unpack16(float (&o)[8], u32x4 v, const float *) {
+  const f32x4 f = __builtin_bit_cast(f32x4, v);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = f[e];
+}
+
+// Row-major slab [64][W] -> LDS [token][col] (pitch RowPitch), no conversion.
+template <typename T, int W> struct SlabRows {
+  static constexpr int EPV = 16 / (int)sizeof(T);
+  static constexpr int VPR = W / EPV;
+  static constexpr int NV = (kRB * VPR + kThreads - 1) / kThreads;  // vectors per thread
+  static constexpr int PT = RowPitch<T, W>::value;
+
+  __device__ static __forceinline__ void prefetch(u32x4 *pf, const T *g, int64_t rs, int nvalid) {
+#pragma unroll
+    for (int m = 0; m < NV; ++m) {
+      const int vi = threadIdx.x + m * kThreads;
+      const int s = vi / VPR, c = vi % VPR;
+      pf[m] = (vi < kRB * VPR && s < nvalid) ? gload16(g + (int64_t)s * rs + c * EPV) : zero16();
+    }
+  }
+  __device__ static __forceinline__ void commit(T *lds, const u32x4 *pf) {
+#pragma unroll
+    for (int m = 0; m < NV; ++m) {
+      const int vi = threadIdx.x + m * kThreads;
+      if (vi < kRB * VPR) {
+        const int s = vi / VPR, c = vi % VPR;
+        *reinterpret_cast<u32x4 *>(lds + s * PT + c * EPV) = pf[m];
+      }
+    }
+  }
+};
+
+// Row-major slab [64][W] -> LDS transposed [col][token] (pitch TokPitch),
+// token row s multiplied by scale[s] before the single rounding to T.
+// bf16 items carry two consecutive tokens so each LDS write is one word.
+template <typename T, int W> struct SlabCols {
+  static constexpr int EPV = 16 / (int)sizeof(T);
+  static constexpr int VPR = W / EPV;
+  static constexpr int PAIR = sizeof(T) == 2 ? 2 : 1;
+  static constexpr int ITEMS = (kRB / PAIR) * VPR;
+  static constexpr int NI = (ITEMS + kThreads - 1) / kThreads;  // items per thread
+  static constexpr int NV = NI * PAIR;                          // vectors per thread
+  static constexpr int PT = TokPitch<T>::value;
+
+  __device__ static __forceinline__ void prefetch(u32x4 *pf, const T *g, int64_t rs, int nvalid) {
+#pragma unroll
+    for (int m = 0; m < NI; ++m) {
+      const int it = threadIdx.x + m * kThreads;
+      const int c = it % VPR, s0 = (it / VPR) * PAIR;
+#pragma unroll
+      for (int q = 0; q < PAIR; ++q)
+        pf[m * PAIR + q] = (it < ITEMS && s0 + q < nvalid)
+                               ? gload16(g + (int64_t)(s0 + q) * rs + c * EPV) : zero16();
+    }
+  }
+  __device__ static __forceinline__ void commit(T *lds, const u32x4 *pf, const float *scale) {
+#pragma unroll
+    for (int m = 0; m < NI; ++m) {
+      const int it = threadIdx.x + m * kThreads;
+      if (it >= ITEMS) continue;
+      const int c = it % VPR, s0 = (it / VPR) * PAIR;
+      if constexpr (sizeof(T) == 2) {
+        float v0[8], v1[8];
+        unpack16(v0, pf[m * 2], (const T *)nullptr);
+        unpack16(v1, pf[m * 2 + 1], (const T *)nullptr);
+        const float a0 = scale ? scale[s0] : 1.0f, a1 = scale ? scale[s0 + 1] : 1.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          bf16x2 pr;
+          pr[0] = (bf16)(v0[e] * a0);
+          pr[1] = (bf16)(v1[e] * a1);
+          *reinterpret_cast<bf16x2 *>(lds + (c * EPV + e) * PT + s0) = pr;
+        }
+      } else {
+        float v[8];
+        unpack16(v, pf[m], (const T *)nullptr);
+        const float a0 = scale ? scale[s0] : 1.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) reinterpret_cast<float *>(lds)[(c * EPV + e) * PT + s0] = v[e] * a0;
+      }
+    }
+  }
+};
+
+// A [64][N] state slab (row-major, source type S) -> LDS [row][col] in T
+// (pitch RowPitch), every element multiplied by `sc` before rounding.
+template <typename T, typename S, int N> struct SlabState {
+  static constexpr int EPV = 16 / (int)sizeof(S);
+  static constexpr int VPR = N / EPV;
+  static constexpr int NV = (kP * VPR + kThreads - 1) / kThreads;
+  static constexpr int PT = RowPitch<T, N>::value;
+
+  __device__ static __forceinline__ void prefetch(u32x4 *pf, const S *g) {
+#pragma unroll
+    for (int m = 0; m < NV; ++m) {
+      const int vi = threadIdx.x + m * kThreads;
+      pf[m] = vi < kP * VPR ? gload16(g + (int64_t)vi * EPV) : zero16();
+    }
+  }
+  __device__ static __forceinline__ void commit(T *lds, const u32x4 *pf, float sc) {
+#pragma unroll
+    for (int m = 0; m < NV; ++m) {
+      const int vi = threadIdx.x + m * kThreads;
+      if (vi >= kP * VPR) continue;
+      const int r = vi / VPR, c = vi % VPR;
+      float v[8];
+      unpack16(v, pf[m], (const S *)nullptr);
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) lds[r * PT + c * EPV + e] = from_f<T>(v[e] * sc);
+    }
+  }
+};
+
 // ------------------------------------------------------ wavefront scans
 
 __device__ __forceinline__ float wave_scan_up(float v) {

@@ -17,8 +17,10 @@ struct ScanArgs {
   void *y;
   float *states;  // [ndir][Z][nchunks][H][P][N] chunk states (workspace)
   float *cdecay;  // [ndir][Z][nchunks][H] chunk total log2-decay (workspace)
-  const float *sin[2];  // carry-in state of each chunk, per direction (nullptr = none)
-  int64_t sin_bstride[2], sin_cstride[2];
+  const void *sin[2];  // carry-in state of each chunk, per direction (nullptr = none)
+  int64_t sin_bstride[2], sin_cstride[2];  // element strides of sin per batch row / chunk
+  int sin_f32[2];       // 1: sin is fp32; 0: sin has the compute dtype
+  void *sin_t;          // carry-in states in the compute dtype, written by the state pass
   const float *init_state;  // forward start state for the state pass
   float *final_state;       // forward end state written by the state pass
   int64_t L;
