@@ -231,6 +231,51 @@ __device__ __forceinline__ void stage_cols(T *lds, const T *g, int64_t rs, int n
   }
 }
 
+// -------------------------------------------- k-along-rows fragments
+//
+// ds_read_b64_tr_b16 (gfx950) works on groups of 16 lanes: if lane k of a
+// group supplies the address of 4 consecutive 16-bit elements M[k][0..3],
+// lane i receives M[4e + i/4][i%4] for e = 0..3.  Lane k therefore points at
+// row r0 + k/4, columns c0 + 4(k%4) .. +3 of a row-major tile, and lane i
+// receives tile[r0 + e][c0 + i]: four consecutive k values (rows) of its own
+// column -- an MFMA operand fragment with k running down the rows, read
+// without transposing the tile in LDS.
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x4 lds_tr4(const bf16 *p) {
+  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4 *)(p));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+// Fragment with k along rows: elements 0..3 = tile[r0 + 0..3][c0 + l%16],
+// elements 4..7 = tile[r1 + 0..3][c0 + l%16]  (row-major tile, pitch `pt`).
+__device__ __forceinline__ void frag_rows(Frag<bf16> &f, const bf16 *tile, int pt, int r0, int r1,
+                                          int c0) {
+  const int i = threadIdx.x & 15;
+  const int off = (i >> 2) * pt + c0 + 4 * (i & 3);
+  const bf16x4 a = lds_tr4(tile + r0 * pt + off);
+  const bf16x4 b = lds_tr4(tile + r1 * pt + off);
+  f.v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ void frag_rows(Frag<float> &f, const float *tile, int pt, int r0, int r1,
+                                          int c0) {
+  const int i = threadIdx.x & 15;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f.v[e] = tile[(r0 + e) * pt + c0 + i];
+    f.v[4 + e] = tile[(r1 + e) * pt + c0 + i];
+  }
+}
+
+// Row pitch (elements) of row-major tiles read with frag_rows: a 16-lane
+// group reads 4 rows x 32 bytes; a pitch of W + 32 bytes puts the 4 rows on
+// disjoint banks.
+template <typename T, int W> struct TrPitch {
+  static constexpr int value = W + 32 / (int)sizeof(T);
+};
+
 // ------------------------------------------------ register-prefetched slabs
 //
 // A slab is 64 token rows of a row-major global tensor.  Its bytes are
@@ -242,6 +287,18 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ u32x4 gload16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 __device__ __forceinline__ u32x4 zero16() { return u32x4{0u, 0u, 0u, 0u}; }
+
+// Buffer resource over [base, base + nbytes): raw buffer loads take a 32-bit
+// byte offset, and any 16-byte load at or beyond nbytes returns zeros.  A
+// resource spans one batch row of a tensor, so tokens past the sequence end
+// read as zero without a bounds check.
+typedef __amdgpu_buffer_rsrc_t bufres;
+__device__ __forceinline__ bufres make_buf(const void *base, uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)nbytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload16(bufres r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
 
 // 16 raw bytes holding EPV elements of T, widened to fp32
 __device__ __forceinline__ void unpack16(float (&o)[8], u32x4 v, const bf16 *) {
@@ -255,26 +312,27 @@ __device__ __forceinline__ void unpack16(float (&o)[8], u32x4 v, const float *) 
   for (int e = 0; e < 4; ++e) o[e] = f[e];
 }
 
-// Row-major slab [64][W] -> LDS [token][col] (pitch RowPitch), no conversion.
-template <typename T, int W> struct SlabRows {
+// Row-major slab [64][W] -> LDS [token][col] (pitch PT), no conversion.
+// The slab's rows start at byte `off0` of buffer `r`, `rs` bytes apart.
+template <typename T, int W, int PT = RowPitch<T, W>::value> struct SlabRows {
   static constexpr int EPV = 16 / (int)sizeof(T);
   static constexpr int VPR = W / EPV;
   static constexpr int NV = (kRB * VPR + kThreads - 1) / kThreads;  // vectors per thread
-  static constexpr int PT = RowPitch<T, W>::value;
+  static constexpr bool FULL = (kRB * VPR) % kThreads == 0;
 
-  __device__ static __forceinline__ void prefetch(u32x4 *pf, const T *g, int64_t rs, int nvalid) {
+  __device__ static __forceinline__ void prefetch(u32x4 *pf, bufres r, uint32_t off0, uint32_t rs) {
 #pragma unroll
     for (int m = 0; m < NV; ++m) {
       const int vi = threadIdx.x + m * kThreads;
       const int s = vi / VPR, c = vi % VPR;
-      pf[m] = (vi < kRB * VPR && s < nvalid) ? gload16(g + (int64_t)s * rs + c * EPV) : zero16();
+      if (FULL || vi < kRB * VPR) pf[m] = bload16(r, off0 + s * rs + c * 16);
     }
   }
   __device__ static __forceinline__ void commit(T *lds, const u32x4 *pf) {
 #pragma unroll
     for (int m = 0; m < NV; ++m) {
       const int vi = threadIdx.x + m * kThreads;
-      if (vi < kRB * VPR) {
+      if (FULL || vi < kRB * VPR) {
         const int s = vi / VPR, c = vi % VPR;
         *reinterpret_cast<u32x4 *>(lds + s * PT + c * EPV) = pf[m];
       }
@@ -334,6 +392,46 @@ template <typename T, int W> struct SlabCols {
   }
 };
 
+// Row-major slab [64][W] -> LDS row-major [token][col] with pitch PT, token
+// row s multiplied by scale[s] before the single rounding to T.  Rows start
+// at byte `off0` of buffer `r`, `rs` bytes apart.
+template <typename T, int W, int PT> struct SlabRowsScaled {
+  static constexpr int EPV = 16 / (int)sizeof(T);
+  static constexpr int VPR = W / EPV;
+  static constexpr int NV = (kRB * VPR + kThreads - 1) / kThreads;
+  static_assert((kRB * VPR) % kThreads == 0, "slab must split evenly");
+
+  __device__ static __forceinline__ void prefetch(u32x4 *pf, bufres r, uint32_t off0, uint32_t rs) {
+#pragma unroll
+    for (int m = 0; m < NV; ++m) {
+      const int vi = threadIdx.x + m * kThreads;
+      const int s = vi / VPR, c = vi % VPR;
+      pf[m] = bload16(r, off0 + s * rs + c * 16);
+    }
+  }
+  __device__ static __forceinline__ void commit(T *lds, const u32x4 *pf, const float *scale) {
+#pragma unroll
+    for (int m = 0; m < NV; ++m) {
+      const int vi = threadIdx.x + m * kThreads;
+      const int s = vi / VPR, c = vi % VPR;
+      const float a0 = scale ? scale[s] : 1.0f;
+      float v[8];
+      unpack16(v, pf[m], (const T *)nullptr);
+      if constexpr (sizeof(T) == 2) {
+        bf16x8 o;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = (bf16)(v[e] * a0);
+        *reinterpret_cast<bf16x8 *>(lds + s * PT + c * EPV) = o;
+      } else {
+        f32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = v[e] * a0;
+        *reinterpret_cast<f32x4 *>(lds + s * PT + c * EPV) = o;
+      }
+    }
+  }
+};
+
 // A [64][N] state slab (row-major, source type S) -> LDS [row][col] in T
 // (pitch RowPitch), every element multiplied by `sc` before rounding.
 template <typename T, typename S, int N> struct SlabState {
@@ -341,24 +439,38 @@ template <typename T, typename S, int N> struct SlabState {
   static constexpr int VPR = N / EPV;
   static constexpr int NV = (kP * VPR + kThreads - 1) / kThreads;
   static constexpr int PT = RowPitch<T, N>::value;
+  static_assert((kP * VPR) % kThreads == 0, "state slab must split evenly");
 
   __device__ static __forceinline__ void prefetch(u32x4 *pf, const S *g) {
 #pragma unroll
     for (int m = 0; m < NV; ++m) {
       const int vi = threadIdx.x + m * kThreads;
-      pf[m] = vi < kP * VPR ? gload16(g + (int64_t)vi * EPV) : zero16();
+      pf[m] = gload16(g + (int64_t)vi * EPV);
     }
   }
   __device__ static __forceinline__ void commit(T *lds, const u32x4 *pf, float sc) {
 #pragma unroll
     for (int m = 0; m < NV; ++m) {
       const int vi = threadIdx.x + m * kThreads;
-      if (vi >= kP * VPR) continue;
       const int r = vi / VPR, c = vi % VPR;
       float v[8];
       unpack16(v, pf[m], (const S *)nullptr);
+      if constexpr (sizeof(T) == 2 && sizeof(S) == 2) {
+        bf16x8 o;
 #pragma unroll
-      for (int e = 0; e < EPV; ++e) lds[r * PT + c * EPV + e] = from_f<T>(v[e] * sc);
+        for (int e = 0; e < 8; ++e) o[e] = (bf16)(v[e] * sc);
+        *reinterpret_cast<bf16x8 *>(lds + r * PT + c * EPV) = o;
+      } else if constexpr (sizeof(T) == 2) {
+        bf16x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = (bf16)(v[e] * sc);
+        *reinterpret_cast<bf16x4 *>(lds + r * PT + c * EPV) = o;
+      } else {
+        f32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = v[e] * sc;
+        *reinterpret_cast<f32x4 *>(lds + r * PT + c * EPV) = o;
+      }
     }
   }
 };

@@ -23,6 +23,8 @@
 //   K3 chunk_out   : per (batch, chunk, 64-token row-block, head tile) both
 //                    directions' intra-chunk and carry-in terms plus D x,
 //                    writing y exactly once.
+#include <type_traits>
+
 #include "bissd_device.hpp"
 #include "bissd_internal.hpp"
 
@@ -31,25 +33,28 @@ namespace bissd {
 // =================================================================== K1
 
 template <typename T, int N, int HT> struct K1Lds {
-  static constexpr int XP = TokPitch<T>::value;
+  static constexpr int BPT = TrPitch<T, N>::value;
+  static constexpr int XPT = TrPitch<T, kP>::value;
   float lam[HT][kQmax];
   float dtv[HT][kQmax];
   float scale[HT][kQmax];
-  T Bt[N][XP];
-  T Xs[HT][kP][XP];
+  T Bs[kRB][BPT];
+  T Xs[HT][kRB][XPT];
 };
 
 // Chunk-local state S_loc = sum_s w_s x_s (outer) B_s with
 // w_s = dt_s 2^(lam_last - lam_s) (forward) or dt_s 2^(rho_first - rho_s)
 // (reverse), for one (batch, chunk, direction, head tile), plus the chunk's
 // total log2-decay.  64-token slabs are fetched into registers one slab
-// ahead of the matrix-core work.  Output states[d][b][c][h][p][n] (fp32),
-// cdecay[d][b][c][h].  Wave w owns state columns n in [w N/4, (w+1) N/4).
+// ahead of the matrix-core work and stored row-major; both operands are read
+// with k (the token) running down the rows.  Output
+// states[d][b][c][h][p][n] (fp32), cdecay[d][b][c][h].  Wave w owns state
+// columns n in [w N/4, (w+1) N/4).
 template <typename T, int N, int HT>
 __global__ __launch_bounds__(kThreads) void k1_chunk_state(ScanArgs a) {
   using Sm = K1Lds<T, N, HT>;
-  using SB = SlabCols<T, N>;
-  using SX = SlabCols<T, kP>;
+  using SB = SlabRows<T, N, Sm::BPT>;
+  using SX = SlabRowsScaled<T, kP, Sm::XPT>;
   __shared__ Sm sm;
   constexpr int NT = N / 64;  // 16-wide column tiles per wave
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
@@ -64,14 +69,20 @@ __global__ __launch_bounds__(kThreads) void k1_chunk_state(ScanArgs a) {
   const int qlen = (int)((L - t0) < Q ? (L - t0) : Q);
   const int gidx = h0 / (H / G);
   const T *dt = reinterpret_cast<const T *>(a.dt[d]);
-  const T *Bg = reinterpret_cast<const T *>(a.B[d]) + (((int64_t)b * L + t0) * G + gidx) * N;
-  const T *xg = reinterpret_cast<const T *>(a.x) + (((int64_t)b * L + t0) * H + h0) * kP;
-  const int64_t brs = (int64_t)G * N, xrs = (int64_t)H * kP;
+  constexpr uint32_t ES = sizeof(T);
+  // one buffer per batch row: tokens past L read as zero
+  const bufres rB = make_buf(reinterpret_cast<const T *>(a.B[d]) + (int64_t)b * L * G * N,
+                             (uint32_t)(L * G * N * ES));
+  const bufres rX = make_buf(reinterpret_cast<const T *>(a.x) + (int64_t)b * L * H * kP,
+                             (uint32_t)(L * H * kP * ES));
+  const uint32_t brs = (uint32_t)(G * N * ES), xrs = (uint32_t)(H * kP * ES);
+  const uint32_t boff = (uint32_t)(t0 * G + gidx) * N * ES;
+  const uint32_t xoff = (uint32_t)(t0 * H + h0) * kP * ES;
 
   u32x4 pfB[SB::NV], pfX[HT][SX::NV];
-  SB::prefetch(pfB, Bg, brs, qlen);
+  SB::prefetch(pfB, rB, boff, brs);
 #pragma unroll
-  for (int hh = 0; hh < HT; ++hh) SX::prefetch(pfX[hh], xg + hh * kP, xrs, qlen);
+  for (int hh = 0; hh < HT; ++hh) SX::prefetch(pfX[hh], rX, xoff + hh * kP * ES, xrs);
 
   for (int hh = w; hh < HT; hh += 4)
     chunk_decay_scan<T>(dt + ((int64_t)b * L + t0) * H + h0 + hh, H, qlen, Q,
@@ -100,33 +111,32 @@ __global__ __launch_bounds__(kThreads) void k1_chunk_state(ScanArgs a) {
   for (int k = 0; k < nslab; ++k) {
     const int s0 = k * kRB;
     __syncthreads();
-    SB::commit(&sm.Bt[0][0], pfB, nullptr);
+    SB::commit(&sm.Bs[0][0], pfB);
 #pragma unroll
     for (int hh = 0; hh < HT; ++hh) SX::commit(&sm.Xs[hh][0][0], pfX[hh], &sm.scale[hh][s0]);
     __syncthreads();
     if (k + 1 < nslab) {
-      const int s1 = s0 + kRB;
-      SB::prefetch(pfB, Bg + s1 * brs, brs, qlen - s1);
+      const uint32_t s1 = s0 + kRB;
+      SB::prefetch(pfB, rB, boff + s1 * brs, brs);
 #pragma unroll
-      for (int hh = 0; hh < HT; ++hh) SX::prefetch(pfX[hh], xg + s1 * xrs + hh * kP, xrs, qlen - s1);
+      for (int hh = 0; hh < HT; ++hh) SX::prefetch(pfX[hh], rX, xoff + s1 * xrs + hh * kP * ES, xrs);
     }
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
+      const int r0 = 32 * q + 4 * g4, r1 = r0 + 16;
       Frag<T> bf[NT];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        frag_ld4x2(bf[nt], &sm.Bt[nb + 16 * nt + r16][32 * q + 4 * g4],
-                   &sm.Bt[nb + 16 * nt + r16][32 * q + 16 + 4 * g4]);
+      for (int nt = 0; nt < NT; ++nt) frag_rows(bf[nt], &sm.Bs[0][0], Sm::BPT, r0, r1, nb + 16 * nt);
 #pragma unroll
-      for (int hh = 0; hh < HT; ++hh)
+      for (int hh = 0; hh < HT; ++hh) {
+        Frag<T> xf[4];
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) {
-          Frag<T> xf;
-          frag_ld4x2(xf, &sm.Xs[hh][16 * pt + r16][32 * q + 4 * g4],
-                     &sm.Xs[hh][16 * pt + r16][32 * q + 16 + 4 * g4]);
+        for (int pt = 0; pt < 4; ++pt) frag_rows(xf[pt], &sm.Xs[hh][0][0], Sm::XPT, r0, r1, 16 * pt);
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) mma(acc[hh][pt][nt], xf, bf[nt]);
-        }
+        for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) mma(acc[hh][pt][nt], xf[pt], bf[nt]);
+      }
     }
   }
 
@@ -191,31 +201,31 @@ __global__ __launch_bounds__(kThreads) void k2_state_pass(ScanArgs a, int PN) {
 // =================================================================== K3
 
 template <typename T, int N, int HT> struct K3Lds {
-  static constexpr int BP = RowPitch<T, N>::value;
-  static constexpr int XP = TokPitch<T>::value;
+  static constexpr int BP = RowPitch<T, N>::value;  // natural-read rows
+  static constexpr int XPT = TrPitch<T, kP>::value; // k-along-rows tile
   static constexpr int OP = kP + 4;
   float lam[2][HT][kQmax];
-  float dtv[2][HT][kQmax];
-  float scale[2][HT][kQmax];
+  float scale[2][HT][kQmax];  // holds dt until the scales are formed
+  float dtd[2][HT][kRB];      // dt of the diagonal block (exact path)
   float refb[2][HT];
   float amax[2][HT];
   union U {
     struct S {
       T Bs[kRB][BP];
-      T Xs[HT][kP][XP];
+      T Xs[HT][kRB][XPT];
     } s;
-    T Sst[kP][BP];
-    float Out[kRB][OP];
+    T Sst[HT < 2 ? HT : 2][kP][BP];
+    float Out[HT < 2 ? HT : 2][kRB][OP];
   } u;
 };
 
-template <typename T, int N, int HT> struct K3Pf {
+template <typename T, int N, int HT, bool SF32> struct K3Pf {
+  static constexpr int IH = HT < 2 ? HT : 2;  // heads per carry-in / output stage
   using SB = SlabRows<T, N>;
-  using SX = SlabCols<T, kP>;
-  using SS = SlabState<T, T, N>;
-  using SF = SlabState<T, float, N>;
+  using SX = SlabRowsScaled<T, kP, K3Lds<T, N, HT>::XPT>;
+  using SS = SlabState<T, typename std::conditional<SF32, float, T>::type, N>;
   static constexpr int SBLK = SB::NV + HT * SX::NV;
-  static constexpr int NPF = SBLK > SF::NV ? SBLK : SF::NV;
+  static constexpr int NPF = SBLK > IH * SS::NV ? SBLK : IH * SS::NV;
 };
 
 // Workgroup = (batch b, chunk c, row-block j, head tile).  Wave w owns the 16
@@ -226,21 +236,27 @@ template <typename T, int N, int HT> struct K3Pf {
 // before the row-block; reverse: rho at the token after it):
 //   2^(lam_t - lam_s) = 2^(lam_t - m) * 2^(m - lam_s),
 // both factors <= 1, so C.B^T feeds the matrix cores unchanged, x is staged
-// pre-multiplied by dt_s 2^(m - lam_s), the carry-in state by 2^m, and the
-// row factor 2^(lam_t - m) is applied once to the sum.  The diagonal slab
-// uses a reference per 16-token tile and is masked elementwise.
+// pre-multiplied by dt_s 2^(m - lam_s), and the row factor 2^(lam_t - m) is
+// applied once to the sum.  The carry-in term 2^lam_t C S_in^T uses the
+// states as stored and applies 2^lam_t to its own small accumulator.  The
+// diagonal slab uses a reference per 16-token tile and is masked
+// elementwise.
 //
-// Work runs as a pipeline of stages -- the s-blocks and then one carry-in
-// stage per head, forward first, then reverse -- and the global loads of
-// stage i+1 are issued into registers before the matrix-core work of stage i.
-template <typename T, int N, int HT>
+// Work runs as a pipeline of stages -- the s-blocks, then the carry-in
+// states two heads per stage, forward first, then reverse -- and the global
+// loads of the next stage are issued into registers before the matrix-core
+// work of the current one.
+// SF32: the carry-in states are fp32 (the block update's cached state)
+// rather than the compute dtype written by the state pass.
+template <typename T, int N, int HT, bool SF32>
 __global__ __launch_bounds__(kThreads) void k3_chunk_out(ScanArgs a) {
   using Sm = K3Lds<T, N, HT>;
-  using PF = K3Pf<T, N, HT>;
+  using PF = K3Pf<T, N, HT, SF32>;
   using SB = typename PF::SB;
   using SX = typename PF::SX;
   using SS = typename PF::SS;
-  using SF = typename PF::SF;
+  using SSrc = typename std::conditional<SF32, float, T>::type;
+  constexpr int IH = PF::IH;
   __shared__ Sm sm;
   constexpr int NK = N / 32;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
@@ -256,47 +272,45 @@ __global__ __launch_bounds__(kThreads) void k3_chunk_out(ScanArgs a) {
   if (j * kRB >= qlen) return;
   const int gidx = h0 / (H / G);
   const T *xg = reinterpret_cast<const T *>(a.x) + (((int64_t)b * L + t0) * H + h0) * kP;
-  const int64_t xrs = (int64_t)H * kP, brs = (int64_t)G * N;
+  const int64_t xrs = (int64_t)H * kP;
+  constexpr uint32_t ES = sizeof(T);
+  // one buffer per batch row: tokens past L read as zero
+  const bufres rX = make_buf(reinterpret_cast<const T *>(a.x) + (int64_t)b * L * H * kP,
+                             (uint32_t)(L * H * kP * ES));
+  const bufres rB[2] = {
+      make_buf(reinterpret_cast<const T *>(a.B[0]) + (int64_t)b * L * G * N, (uint32_t)(L * G * N * ES)),
+      make_buf(reinterpret_cast<const T *>(a.B[1]) + (int64_t)b * L * G * N, (uint32_t)(L * G * N * ES))};
+  const uint32_t brs_b = (uint32_t)(G * N * ES), xrs_b = (uint32_t)(H * kP * ES);
+  const uint32_t boff = (uint32_t)(t0 * G + gidx) * N * ES;
+  const uint32_t xoff = (uint32_t)(t0 * H + h0) * kP * ES;
   const int klast = (qlen - 1) / kRB;
+  const bool has_in0 = a.sin[0] != nullptr, has_in1 = a.sin[1] != nullptr;
 
-  // ---- stage list
-  const int n0 = j + 1;
-  const int n1 = a.sin[0] ? HT : 0;
-  const int n2 = klast - j + 1;
-  const int n3 = a.sin[1] ? HT : 0;
-  const int nst = n0 + n1 + n2 + n3;
-  auto decode = [&](int i, int &kind, int &d, int &kk) __attribute__((always_inline)) {
-    if (i < n0) { kind = 0; d = 0; kk = i; }
-    else if (i < n0 + n1) { kind = 1; d = 0; kk = i - n0; }
-    else if (i < n0 + n1 + n2) { kind = 0; d = 1; kk = j + (i - n0 - n1); }
-    else { kind = 1; d = 1; kk = i - n0 - n1 - n2; }
-  };
   u32x4 pf[PF::NPF];
-  auto prefetch = [&](int i) __attribute__((always_inline)) {
-    int kind, d, kk;
-    decode(i, kind, d, kk);
-    if (kind == 0) {
-      const int s0 = kk * kRB;
-      SB::prefetch(pf, reinterpret_cast<const T *>(a.B[d]) + (((int64_t)b * L + t0 + s0) * G + gidx) * N,
-                   brs, qlen - s0);
+  auto prefetch_sblock = [&](int d, int k) __attribute__((always_inline)) {
+    const uint32_t s0 = k * kRB;
+    SB::prefetch(pf, d == 0 ? rB[0] : rB[1], boff + s0 * brs_b, brs_b);
 #pragma unroll
-      for (int hh = 0; hh < HT; ++hh)
-        SX::prefetch(pf + SB::NV + hh * SX::NV, xg + s0 * xrs + hh * kP, xrs, qlen - s0);
-    } else {
+    for (int hh = 0; hh < HT; ++hh)
+      SX::prefetch(pf + SB::NV + hh * SX::NV, rX, xoff + s0 * xrs_b + hh * kP * ES, xrs_b);
+  };
+  // carry-in states of heads ih*IH .. ih*IH + IH - 1
+  auto prefetch_state = [&](int d, int ih) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < IH; ++q) {
       const int64_t off = (int64_t)b * a.sin_bstride[d] + (int64_t)c * a.sin_cstride[d] +
-                          (int64_t)(h0 + kk) * kP * N;
-      if (a.sin_f32[d]) SF::prefetch(pf, reinterpret_cast<const float *>(a.sin[d]) + off);
-      else SS::prefetch(pf, reinterpret_cast<const T *>(a.sin[d]) + off);
+                          (int64_t)(h0 + ih * IH + q) * kP * N;
+      SS::prefetch(pf + q * SS::NV, reinterpret_cast<const SSrc *>(a.sin[d]) + off);
     }
   };
-  if (nst > 0) prefetch(0);
+  prefetch_sblock(0, 0);
 
   // ---- decay scans (forward prefix and reverse suffix) for the whole chunk
   for (int pr = w; pr < 2 * HT; pr += 4) {
     const int d = pr / HT, hh = pr % HT;
     const float am = chunk_decay_scan<T>(
         reinterpret_cast<const T *>(a.dt[d]) + ((int64_t)b * L + t0) * H + h0 + hh, H, qlen, Q,
-        a.A[d][h0 + hh] * kLog2e, d == 1, sm.lam[d][hh], sm.dtv[d][hh]);
+        a.A[d][h0 + hh] * kLog2e, d == 1, sm.lam[d][hh], sm.scale[d][hh]);
     if (lane == 0) sm.amax[d][hh] = am;
   }
 
@@ -324,6 +338,10 @@ __global__ __launch_bounds__(kThreads) void k3_chunk_out(ScanArgs a) {
     sm.refb[d][hh] = d == 0 ? (j > 0 ? sm.lam[0][hh][j * kRB - 1] : 0.0f)
                             : ((j + 1) * kRB < Q ? sm.lam[1][hh][(j + 1) * kRB] : 0.0f);
   }
+  for (int it = tid; it < 2 * HT * kRB; it += kThreads) {
+    const int d = it / (HT * kRB), hh = (it / kRB) % HT, sl = it % kRB;
+    sm.dtd[d][hh][sl] = sm.scale[d][hh][j * kRB + sl];
+  }
   // The factored diagonal slab multiplies by 2^(lam_t - lam_end) <= 2^(15 max|a|)
   // on one side; chunks whose decays could overflow that take the exact
   // per-element path instead (x staged unscaled, full 2^(lam_t - lam_s) dt_s
@@ -338,8 +356,16 @@ __global__ __launch_bounds__(kThreads) void k3_chunk_out(ScanArgs a) {
     const int d = it / (HT * Q), hh = (it / Q) % HT, s = it % Q;
     const bool dg = (s / kRB) == j;
     const float ref = dg ? (d == 0 ? sm.lam[0][hh][s | 15] : sm.lam[1][hh][s & ~15]) : sm.refb[d][hh];
-    const float dv = sm.dtv[d][hh][s];
+    const float dv = sm.scale[d][hh][s];
     sm.scale[d][hh][s] = (dg && exact) ? 1.0f : (dv != 0.0f ? dv * exp2_fast(ref - sm.lam[d][hh][s]) : 0.0f);
+  }
+
+  // lane masks of the own 16-token tile: forward keeps s <= t, reverse s >= t
+  float mk[2][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    mk[0][i] = (4 * g4 + i <= r16) ? 1.0f : 0.0f;
+    mk[1][i] = (4 * g4 + i >= r16) ? 1.0f : 0.0f;
   }
 
   f32x4 acc[HT][4], tmp[HT][4];
@@ -351,33 +377,25 @@ __global__ __launch_bounds__(kThreads) void k3_chunk_out(ScanArgs a) {
       zero4(tmp[hh][v]);
     }
 
-  for (int i = 0; i < nst; ++i) {
-    int kind, d, kk;
-    decode(i, kind, d, kk);
-    __syncthreads();
-    // ---- commit stage i to LDS
-    if (kind == 0) {
+  // one direction; D is a compile-time constant so every register array
+  // (C fragments, masks, accumulators) is indexed statically
+  auto run_direction = [&](auto dc) __attribute__((always_inline)) {
+    constexpr int d = decltype(dc)::value;
+    const int kb = d == 0 ? 0 : j, ke = d == 0 ? j : klast;
+    // ---------------- s-blocks of direction d
+    for (int k = kb; k <= ke; ++k) {
+      const int s0 = k * kRB;
+      __syncthreads();
       SB::commit(&sm.u.s.Bs[0][0], pf);
 #pragma unroll
       for (int hh = 0; hh < HT; ++hh)
-        SX::commit(&sm.u.s.Xs[hh][0][0], pf + SB::NV + hh * SX::NV, &sm.scale[d][hh][kk * kRB]);
-    } else {
-      const float sc = exp2_fast(sm.refb[d][kk]);
-      if (a.sin_f32[d]) SF::commit(&sm.u.Sst[0][0], pf, sc);
-      else SS::commit(&sm.u.Sst[0][0], pf, sc);
-    }
-    __syncthreads();
-    if (i + 1 < nst) prefetch(i + 1);
+        SX::commit(&sm.u.s.Xs[hh][0][0], pf + SB::NV + hh * SX::NV, &sm.scale[d][hh][s0]);
+      __syncthreads();
+      if (k < ke) prefetch_sblock(d, k + 1);
+      else if (d == 0 ? has_in0 : has_in1) prefetch_state(d, 0);
+      else if (d == 0) prefetch_sblock(1, j);
 
-    // ---- compute stage i
-    // this direction's C fragments (a select, so no register array is
-    // indexed by the runtime direction)
-    Frag<T> cd[NK];
-#pragma unroll
-    for (int ks = 0; ks < NK; ++ks) cd[ks] = d ? cf[1][ks] : cf[0][ks];
-    if (kind == 0) {
-      const bool diag = (kk == j);
-      const int s0 = kk * kRB;
+      const bool diag = (k == j);
       int ulo = 0, uhi = 3;
       if (diag) {
         if (d == 0) uhi = w;
@@ -386,16 +404,16 @@ __global__ __launch_bounds__(kThreads) void k3_chunk_out(ScanArgs a) {
       // cb[u]: lane holds (C.B^T)[t = 16w + r16][s = 16u + 4 g4 + i]
       f32x4 cb[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        zero4(cb[u]);
-        if (u >= ulo && u <= uhi) {
+      for (int u = 0; u < 4; ++u) zero4(cb[u]);
 #pragma unroll
-          for (int ks = 0; ks < NK; ++ks) {
-            Frag<T> bfr;
-            frag_ld8(bfr, &sm.u.s.Bs[16 * u + r16][32 * ks + 8 * g4]);
-            mma(cb[u], bfr, cd[ks]);
-          }
-        }
+      for (int ks = 0; ks < NK; ++ks) {
+        Frag<T> bfr[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (u >= ulo && u <= uhi) frag_ld8(bfr[u], &sm.u.s.Bs[16 * u + r16][32 * ks + 8 * g4]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (u >= ulo && u <= uhi) mma(cb[u], bfr[u], cf[d][ks]);
       }
       if (!diag) {
         Frag<T> mf[2];
@@ -412,25 +430,23 @@ __global__ __launch_bounds__(kThreads) void k3_chunk_out(ScanArgs a) {
 #pragma unroll
         for (int hh = 0; hh < HT; ++hh)
 #pragma unroll
-          for (int q = 0; q < 2; ++q)
+          for (int q = 0; q < 2; ++q) {
+            Frag<T> xf[4];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              Frag<T> xf;
-              frag_ld4x2(xf, &sm.u.s.Xs[hh][16 * v + r16][32 * q + 4 * g4],
-                         &sm.u.s.Xs[hh][16 * v + r16][32 * q + 16 + 4 * g4]);
-              mma(tmp[hh][v], mf[q], xf);
-            }
+            for (int v = 0; v < 4; ++v)
+              frag_rows(xf[v], &sm.u.s.Xs[hh][0][0], Sm::XPT, 32 * q + 4 * g4, 32 * q + 16 + 4 * g4, 16 * v);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) mma(tmp[hh][v], mf[q], xf[v]);
+          }
       } else {
 #pragma unroll
         for (int hh = 0; hh < HT; ++hh) {
           const float lt = sm.lam[d][hh][s0 + 16 * w + r16];
           float f[4];
-          if (!exact) {
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const float ru = d == 0 ? sm.lam[0][hh][s0 + 16 * u + 15] : sm.lam[1][hh][s0 + 16 * u];
-              f[u] = (u >= ulo && u <= uhi) ? exp2_fast(lt - ru) : 0.0f;
-            }
+          for (int u = 0; u < 4; ++u) {
+            const float ru = d == 0 ? sm.lam[0][hh][s0 + 16 * u + 15] : sm.lam[1][hh][s0 + 16 * u];
+            f[u] = (u >= ulo && u <= uhi && !exact) ? exp2_fast(fminf(lt - ru, 120.0f)) : 0.0f;
           }
 #pragma unroll
           for (int q = 0; q < 2; ++q) {
@@ -439,85 +455,109 @@ __global__ __launch_bounds__(kThreads) void k3_chunk_out(ScanArgs a) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
               const int u = 2 * q + (e >> 2), i2 = e & 3;
-              const int sl = 4 * g4 + i2;  // position inside tile u
-              bool ok = (u >= ulo && u <= uhi);
-              if (u == w) ok = ok && (d == 0 ? (sl <= r16) : (sl >= r16));
               float wgt;
               if (exact) {
-                const int sc = s0 + 16 * u + sl;
-                wgt = ok ? exp2_fast(lt - sm.lam[d][hh][sc]) * sm.dtv[d][hh][sc] : 0.0f;
+                const int sl = 16 * u + 4 * g4 + i2;
+                wgt = exp2_fast(fminf(lt - sm.lam[d][hh][s0 + sl], 0.0f)) * sm.dtd[d][hh][sl];
               } else {
                 wgt = f[u];
               }
+              // select, never multiply by a 0/1 mask: masked positions must
+              // not turn a large factor into 0 * inf
+              bool ok = (u >= ulo && u <= uhi);
+              if (u == w) ok = ok && (mk[d][i2] != 0.0f);
               m[e] = ok ? cb[u][i2] * wgt : 0.0f;
             }
             Frag<T> mf;
             frag_from(mf, m);
+            Frag<T> xf[4];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              Frag<T> xf;
-              frag_ld4x2(xf, &sm.u.s.Xs[hh][16 * v + r16][32 * q + 4 * g4],
-                         &sm.u.s.Xs[hh][16 * v + r16][32 * q + 16 + 4 * g4]);
-              mma(acc[hh][v], mf, xf);
-            }
+            for (int v = 0; v < 4; ++v)
+              frag_rows(xf[v], &sm.u.s.Xs[hh][0][0], Sm::XPT, 32 * q + 4 * g4, 32 * q + 16 + 4 * g4, 16 * v);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) mma(acc[hh][v], mf, xf[v]);
           }
         }
       }
-    } else {
-      // carry-in term of head kk: C (16 rows) x (2^m S_in)^T
+    }
+    // ---------------- carry-in term 2^lam_t C S_in^T, IH heads per stage.
+    // The states are staged as stored; the row factor 2^lam_t (<= 1) is
+    // applied to a transient accumulator per head.
+    if (d == 0 ? has_in0 : has_in1) {
 #pragma unroll
-      for (int hh = 0; hh < HT; ++hh) {
-        if (hh != kk) continue;
+      for (int ih = 0; ih < HT / IH; ++ih) {
+        __syncthreads();
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
+        for (int q = 0; q < IH; ++q) SS::commit(&sm.u.Sst[q][0][0], pf + q * SS::NV, 1.0f);
+        __syncthreads();
+        if (ih + 1 < HT / IH) prefetch_state(d, ih + 1);
+        else if (d == 0) prefetch_sblock(1, j);
+#pragma unroll
+        for (int q = 0; q < IH; ++q) {
+          const int hh = ih * IH + q;
+          f32x4 t2[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) zero4(t2[v]);
 #pragma unroll
           for (int ks = 0; ks < NK; ++ks) {
-            Frag<T> sf;
-            frag_ld8(sf, &sm.u.Sst[16 * v + r16][32 * ks + 8 * g4]);
-            mma(tmp[hh][v], cd[ks], sf);
+            Frag<T> sf[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) frag_ld8(sf[v], &sm.u.Sst[q][16 * v + r16][32 * ks + 8 * g4]);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) mma(t2[v], cf[d][ks], sf[v]);
           }
-      }
-    }
-
-    // ---- end of a direction: row factor 2^(lam_t - m) on the factored part
-    const bool last_of_dir = (i == n0 + n1 - 1) || (i == nst - 1);
-    if (last_of_dir) {
 #pragma unroll
-      for (int hh = 0; hh < HT; ++hh) {
-        const float rb = sm.refb[d][hh];
+          for (int i2 = 0; i2 < 4; ++i2) {
+            const float et = exp2_fast(sm.lam[d][hh][j * kRB + 16 * w + 4 * g4 + i2]);
 #pragma unroll
-        for (int i2 = 0; i2 < 4; ++i2) {
-          const float ut = exp2_fast(sm.lam[d][hh][j * kRB + 16 * w + 4 * g4 + i2] - rb);
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            acc[hh][v][i2] += ut * tmp[hh][v][i2];
-            tmp[hh][v][i2] = 0.0f;
+            for (int v = 0; v < 4; ++v) acc[hh][v][i2] += et * t2[v][i2];
           }
         }
       }
     }
-  }
+    // ---------------- row factor 2^(lam_t - m) on the factored part
+#pragma unroll
+    for (int hh = 0; hh < HT; ++hh) {
+      const float rb = sm.refb[d][hh];
+#pragma unroll
+      for (int i2 = 0; i2 < 4; ++i2) {
+        const float ut = exp2_fast(sm.lam[d][hh][j * kRB + 16 * w + 4 * g4 + i2] - rb);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          acc[hh][v][i2] += ut * tmp[hh][v][i2];
+          tmp[hh][v][i2] = 0.0f;
+        }
+      }
+    }
+  };
+  run_direction(std::integral_constant<int, 0>{});
+  run_direction(std::integral_constant<int, 1>{});
 
-  // y = acc + D x, staged through LDS so that every lane writes 16 bytes
+  // y = acc + D x, IH heads at a time staged through LDS so that every lane
+  // writes 16 contiguous bytes
   T *yg = reinterpret_cast<T *>(a.y) + (((int64_t)b * L + t0 + j * kRB) * H + h0) * kP;
   const T *xo = xg + (int64_t)j * kRB * xrs;
 #pragma unroll
-  for (int hh = 0; hh < HT; ++hh) {
+  for (int ih = 0; ih < HT / IH; ++ih) {
     __syncthreads();
 #pragma unroll
-    for (int v = 0; v < 4; ++v)
+    for (int q = 0; q < IH; ++q)
 #pragma unroll
-      for (int i2 = 0; i2 < 4; ++i2) sm.u.Out[16 * w + 4 * g4 + i2][16 * v + r16] = acc[hh][v][i2];
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2)
+          sm.u.Out[q][16 * w + 4 * g4 + i2][16 * v + r16] = acc[ih * IH + q][v][i2];
     __syncthreads();
-    const float Dh = a.D[h0 + hh];
-    for (int it = tid; it < kRB * 8; it += kThreads) {
-      const int r = it >> 3, p0 = (it & 7) * 8;
+    for (int it = tid; it < IH * kRB * 8; it += kThreads) {
+      const int q = it / (kRB * 8), r = (it >> 3) % kRB, p0 = (it & 7) * 8;
       if (j * kRB + r >= qlen) continue;
+      const int hh = ih * IH + q;
+      const float Dh = a.D[h0 + hh];
       const int64_t off = (int64_t)r * xrs + hh * kP + p0;
       float xv[8], o[8];
       gload8(xv, xo + off);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = sm.u.Out[r][p0 + e] + Dh * xv[e];
+      for (int e = 0; e < 8; ++e) o[e] = sm.u.Out[q][r][p0 + e] + Dh * xv[e];
       gstore8(yg + off, o);
     }
   }
@@ -536,7 +576,10 @@ static void launch_t(const ScanArgs &a, int phase, hipStream_t st) {
     hipLaunchKernelGGL(k2_state_pass<T>, g2, dim3(kThreads), 0, st, a, PN);
   } else {
     dim3 g((unsigned)(a.Z * a.nchunks * (a.chunk / kRB)), (unsigned)(a.H / HT));
-    hipLaunchKernelGGL((k3_chunk_out<T, N, HT>), g, dim3(kThreads), 0, st, a);
+    if (a.sin_f32[0] || a.sin_f32[1])
+      hipLaunchKernelGGL((k3_chunk_out<T, N, HT, true>), g, dim3(kThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL((k3_chunk_out<T, N, HT, false>), g, dim3(kThreads), 0, st, a);
   }
 }
 
