@@ -38,7 +38,10 @@ int check_shape(const bissd_shape_t *s, int op) {
   if (s->batch > (1 << 20) || s->nheads > 4096 || s->seqlen > ((int64_t)1 << 31))
     return BISSD_ERR_UNSUPPORTED;
   const int64_t nc = ceil_div(s->seqlen, s->chunk);
-  if (s->batch * nc * (s->chunk / 64) * 2 >= ((int64_t)1 << 31)) return BISSD_ERR_UNSUPPORTED;
+  if (s->batch * nc * (s->chunk / 64) * 2 * s->nheads >= ((int64_t)1 << 31)) return BISSD_ERR_UNSUPPORTED;
+  // per-batch-row buffer resources address at most 4 GiB
+  if (s->seqlen * s->nheads * s->headdim * 4 >= ((int64_t)1 << 32)) return BISSD_ERR_UNSUPPORTED;
+  if (s->seqlen * s->ngroups * s->dstate * 4 >= ((int64_t)1 << 32)) return BISSD_ERR_UNSUPPORTED;
   if (s->batch * s->seqlen * s->nheads * s->headdim > kMaxElems) return BISSD_ERR_UNSUPPORTED;
   return BISSD_OK;
 }

@@ -475,6 +475,19 @@ template <typename T, typename S, int N> struct SlabState {
   }
 };
 
+// ------------------------------------------------------- XCD-aware order
+//
+// MI355X dispatches consecutive workgroup ids round-robin over its 8 XCDs,
+// each with its own L2.  Remapping the id so that every XCD receives one
+// contiguous range of work items keeps workgroups that read the same chunk
+// of B, C and x on one XCD, where the second and later reads hit its L2.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_linear_id(int bid, int nwg) {
+  const int per = nwg / kXcds, rem = nwg % kXcds;
+  const int xcd = bid % kXcds, slot = bid / kXcds;
+  return xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+}
+
 // ------------------------------------------------------ wavefront scans
 
 __device__ __forceinline__ float wave_scan_up(float v) {

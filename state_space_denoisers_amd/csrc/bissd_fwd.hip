@@ -58,11 +58,13 @@ __global__ __launch_bounds__(kThreads) void k1_chunk_state(ScanArgs a) {
   __shared__ Sm sm;
   constexpr int NT = N / 64;  // 16-wide column tiles per wave
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
-  int bx = blockIdx.x;
+  // work item = ((b * nchunks + c) * ndir + dir) * (H / HT) + head tile
+  int bx = xcd_linear_id(blockIdx.x, gridDim.x);
+  const int h0 = (bx % (a.H / HT)) * HT;
+  bx /= a.H / HT;
   const int d = a.dir0 + bx % a.ndir;
   bx /= a.ndir;
   const int c = bx % a.nchunks, b = bx / a.nchunks;
-  const int h0 = blockIdx.y * HT;
   const int Q = a.chunk, H = a.H, G = a.G;
   const int64_t L = a.L;
   const int64_t t0 = (int64_t)c * Q;
@@ -235,9 +237,9 @@ template <typename T, int N, int HT, bool SF32> struct K3Pf {
 // factored form around a per-head reference m (forward: lam at the token
 // before the row-block; reverse: rho at the token after it):
 //   2^(lam_t - lam_s) = 2^(lam_t - m) * 2^(m - lam_s),
-// both factors <= 1, so C.B^T feeds the matrix cores unchanged, x is staged
-// pre-multiplied by dt_s 2^(m - lam_s), and the row factor 2^(lam_t - m) is
-// applied once to the sum.  The carry-in term 2^lam_t C S_in^T uses the
+// both factors <= 1: x is staged pre-multiplied by dt_s 2^(m - lam_s) and
+// each lane multiplies its C.B^T values by the row factor of its row t
+// before they feed the matrix cores.  The carry-in term 2^lam_t C S_in^T uses the
 // states as stored and applies 2^lam_t to its own small accumulator.  The
 // diagonal slab uses a reference per 16-token tile and is masked
 // elementwise.
@@ -262,11 +264,14 @@ __global__ __launch_bounds__(kThreads) void k3_chunk_out(ScanArgs a) {
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
   const int Q = a.chunk, NRB = Q / kRB, H = a.H, G = a.G;
   const int64_t L = a.L;
-  int bx = blockIdx.x;
+  // work item = ((b * nchunks + c) * NRB + j) * (H / HT) + head tile, so all
+  // workgroups of one chunk run back to back on one XCD
+  int bx = xcd_linear_id(blockIdx.x, gridDim.x);
+  const int h0 = (bx % (H / HT)) * HT;
+  bx /= H / HT;
   const int j = bx % NRB;
   bx /= NRB;
   const int c = bx % a.nchunks, b = bx / a.nchunks;
-  const int h0 = blockIdx.y * HT;
   const int64_t t0 = (int64_t)c * Q;
   const int qlen = (int)((L - t0) < Q ? (L - t0) : Q);
   if (j * kRB >= qlen) return;
@@ -314,23 +319,22 @@ __global__ __launch_bounds__(kThreads) void k3_chunk_out(ScanArgs a) {
     if (lane == 0) sm.amax[d][hh] = am;
   }
 
-  // C rows of this wave (operand for both C.B^T and the carry-in product)
+  // C rows of this wave (operand for both C.B^T and the carry-in product),
+  // loaded per direction
   const int trow = j * kRB + 16 * w + r16;
-  Frag<T> cf[2][NK];
-#pragma unroll
-  for (int d = 0; d < 2; ++d) {
+  auto load_c = [&](int d, Frag<T> (&cfd)[NK]) __attribute__((always_inline)) {
     const T *Cp = reinterpret_cast<const T *>(a.C[d]) + (((int64_t)b * L + t0 + trow) * G + gidx) * N;
 #pragma unroll
     for (int ks = 0; ks < NK; ++ks) {
       if (trow < qlen) {
         float v[8];
         gload8(v, Cp + 32 * ks + 8 * g4);
-        frag_from(cf[d][ks], v);
+        frag_from(cfd[ks], v);
       } else {
-        frag_zero(cf[d][ks]);
+        frag_zero(cfd[ks]);
       }
     }
-  }
+  };
   __syncthreads();
 
   if (tid < 2 * HT) {
@@ -360,28 +364,25 @@ __global__ __launch_bounds__(kThreads) void k3_chunk_out(ScanArgs a) {
     sm.scale[d][hh][s] = (dg && exact) ? 1.0f : (dv != 0.0f ? dv * exp2_fast(ref - sm.lam[d][hh][s]) : 0.0f);
   }
 
-  // lane masks of the own 16-token tile: forward keeps s <= t, reverse s >= t
-  float mk[2][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    mk[0][i] = (4 * g4 + i <= r16) ? 1.0f : 0.0f;
-    mk[1][i] = (4 * g4 + i >= r16) ? 1.0f : 0.0f;
-  }
-
-  f32x4 acc[HT][4], tmp[HT][4];
+  f32x4 acc[HT][4];
 #pragma unroll
   for (int hh = 0; hh < HT; ++hh)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      zero4(acc[hh][v]);
-      zero4(tmp[hh][v]);
-    }
+    for (int v = 0; v < 4; ++v) zero4(acc[hh][v]);
 
   // one direction; D is a compile-time constant so every register array
   // (C fragments, masks, accumulators) is indexed statically
   auto run_direction = [&](auto dc) __attribute__((always_inline)) {
     constexpr int d = decltype(dc)::value;
     const int kb = d == 0 ? 0 : j, ke = d == 0 ? j : klast;
+    Frag<T> cfd[NK];
+    load_c(d, cfd);
+    // per-head row factor 2^(lam_t - m) of this lane's Gram row t = 16w + r16,
+    // applied to C.B^T before the product with the pre-scaled x
+    float ut[HT];
+#pragma unroll
+    for (int hh = 0; hh < HT; ++hh)
+      ut[hh] = exp2_fast(sm.lam[d][hh][j * kRB + 16 * w + r16] - sm.refb[d][hh]);
     // ---------------- s-blocks of direction d
     for (int k = kb; k <= ke; ++k) {
       const int s0 = k * kRB;
@@ -413,30 +414,27 @@ __global__ __launch_bounds__(kThreads) void k3_chunk_out(ScanArgs a) {
           if (u >= ulo && u <= uhi) frag_ld8(bfr[u], &sm.u.s.Bs[16 * u + r16][32 * ks + 8 * g4]);
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-          if (u >= ulo && u <= uhi) mma(cb[u], bfr[u], cf[d][ks]);
+          if (u >= ulo && u <= uhi) mma(cb[u], bfr[u], cfd[ks]);
       }
       if (!diag) {
-        Frag<T> mf[2];
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          float m[8];
-#pragma unroll
-          for (int i2 = 0; i2 < 4; ++i2) {
-            m[i2] = cb[2 * q][i2];
-            m[4 + i2] = cb[2 * q + 1][i2];
-          }
-          frag_from(mf[q], m);
-        }
 #pragma unroll
         for (int hh = 0; hh < HT; ++hh)
 #pragma unroll
           for (int q = 0; q < 2; ++q) {
+            float m[8];
+#pragma unroll
+            for (int i2 = 0; i2 < 4; ++i2) {
+              m[i2] = cb[2 * q][i2] * ut[hh];
+              m[4 + i2] = cb[2 * q + 1][i2] * ut[hh];
+            }
+            Frag<T> mf;
+            frag_from(mf, m);
             Frag<T> xf[4];
 #pragma unroll
             for (int v = 0; v < 4; ++v)
               frag_rows(xf[v], &sm.u.s.Xs[hh][0][0], Sm::XPT, 32 * q + 4 * g4, 32 * q + 16 + 4 * g4, 16 * v);
 #pragma unroll
-            for (int v = 0; v < 4; ++v) mma(tmp[hh][v], mf[q], xf[v]);
+            for (int v = 0; v < 4; ++v) mma(acc[hh][v], mf, xf[v]);
           }
       } else {
 #pragma unroll
@@ -465,7 +463,7 @@ __global__ __launch_bounds__(kThreads) void k3_chunk_out(ScanArgs a) {
               // select, never multiply by a 0/1 mask: masked positions must
               // not turn a large factor into 0 * inf
               bool ok = (u >= ulo && u <= uhi);
-              if (u == w) ok = ok && (mk[d][i2] != 0.0f);
+              if (u == w) ok = ok && (d == 0 ? (4 * g4 + i2 <= r16) : (4 * g4 + i2 >= r16));
               m[e] = ok ? cb[u][i2] * wgt : 0.0f;
             }
             Frag<T> mf;
@@ -504,7 +502,7 @@ __global__ __launch_bounds__(kThreads) void k3_chunk_out(ScanArgs a) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) frag_ld8(sf[v], &sm.u.Sst[q][16 * v + r16][32 * ks + 8 * g4]);
 #pragma unroll
-            for (int v = 0; v < 4; ++v) mma(t2[v], cf[d][ks], sf[v]);
+            for (int v = 0; v < 4; ++v) mma(t2[v], cfd[ks], sf[v]);
           }
 #pragma unroll
           for (int i2 = 0; i2 < 4; ++i2) {
@@ -512,20 +510,6 @@ __global__ __launch_bounds__(kThreads) void k3_chunk_out(ScanArgs a) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) acc[hh][v][i2] += et * t2[v][i2];
           }
-        }
-      }
-    }
-    // ---------------- row factor 2^(lam_t - m) on the factored part
-#pragma unroll
-    for (int hh = 0; hh < HT; ++hh) {
-      const float rb = sm.refb[d][hh];
-#pragma unroll
-      for (int i2 = 0; i2 < 4; ++i2) {
-        const float ut = exp2_fast(sm.lam[d][hh][j * kRB + 16 * w + 4 * g4 + i2] - rb);
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          acc[hh][v][i2] += ut * tmp[hh][v][i2];
-          tmp[hh][v][i2] = 0.0f;
         }
       }
     }
@@ -568,14 +552,14 @@ __global__ __launch_bounds__(kThreads) void k3_chunk_out(ScanArgs a) {
 template <typename T, int N, int HT>
 static void launch_t(const ScanArgs &a, int phase, hipStream_t st) {
   if (phase == PHASE_CHUNK_STATE) {
-    dim3 g((unsigned)(a.Z * a.nchunks * a.ndir), (unsigned)(a.H / HT));
+    dim3 g((unsigned)(a.Z * a.nchunks * a.ndir * (a.H / HT)));
     hipLaunchKernelGGL((k1_chunk_state<T, N, HT>), g, dim3(kThreads), 0, st, a);
   } else if (phase == PHASE_STATE_PASS) {
     const int PN = kP * N;
     dim3 g2((unsigned)((PN / 4 + kThreads - 1) / kThreads), (unsigned)a.H, (unsigned)(a.Z * a.ndir));
     hipLaunchKernelGGL(k2_state_pass<T>, g2, dim3(kThreads), 0, st, a, PN);
   } else {
-    dim3 g((unsigned)(a.Z * a.nchunks * (a.chunk / kRB)), (unsigned)(a.H / HT));
+    dim3 g((unsigned)(a.Z * a.nchunks * (a.chunk / kRB) * (a.H / HT)));
     if (a.sin_f32[0] || a.sin_f32[1])
       hipLaunchKernelGGL((k3_chunk_out<T, N, HT, true>), g, dim3(kThreads), 0, st, a);
     else
@@ -593,14 +577,15 @@ static void launch_n(const ScanArgs &a, int phase, hipStream_t st, int HT) {
 // Heads of one tile must share their B/C group: the tile is 4, 2 or 1 heads,
 // whichever divides the heads per group.
 #ifndef BISSD_MAX_HEAD_TILE
-#define BISSD_MAX_HEAD_TILE 4
+#define BISSD_MAX_HEAD_TILE 2
 #endif
 
 hipError_t launch_scan_phase(const ScanArgs &a, int phase, hipStream_t st) {
   const int hpg = a.H / a.G;
   int HT = (hpg % 4 == 0) ? 4 : (hpg % 2 == 0 ? 2 : 1);
   if (HT > BISSD_MAX_HEAD_TILE) HT = BISSD_MAX_HEAD_TILE;
-  if (a.dtype == 0 && HT > 2) HT = 2;  // fp32 tiles of 4 heads exceed the register file
+  // tiles of 2 heads keep the output kernel at two waves per SIMD
+  if (HT > 2) HT = 2;
   if (a.dtype == 1) {
     if (a.N == 128) launch_n<bf16, 128>(a, phase, st, HT);
     else launch_n<bf16, 64>(a, phase, st, HT);
