@@ -47,10 +47,17 @@ int check_shape(const bissd_shape_t *s, int op) {
 }
 
 // Workspace: fp32 chunk-local states, the carry-in states in the compute
-// dtype (forward only; the block update reads its fp32 start state
-// directly) and the chunk log2-decays.
+// dtype (not for the block update, which reads its fp32 start state
+// directly) and the chunk log2-decays.  The backward pass adds a second fp32
+// state buffer (A-tangent chunk states, then adjoint chunk states), the
+// A-tangent and adjoint carries (compute dtype), chunk dt sums, the
+// per-token dy.y_d and x.(G_t B_t) values (fp32 [2][Z][L][H]) and the
+// partial sums of the reductions.
 struct WsLayout {
-  size_t states = 0, sin_t = 0, cdecay = 0, total = 0;
+  size_t states = 0, sin_t = 0, cdecay = 0;
+  size_t tstates = 0, sa_t = 0, gin_t = 0, dtsum = 0, ydot = 0, qx = 0, qxs = 0, ddpart = 0, dAintra = 0,
+         dAx1 = 0, dAx2 = 0, rpart = 0;
+  size_t total = 0;
 };
 
 WsLayout ws_layout(const bissd_shape_t *s, int op) {
@@ -60,10 +67,32 @@ WsLayout ws_layout(const bissd_shape_t *s, int op) {
   const size_t nst = (size_t)(ndir * s->batch * nc * s->nheads * s->headdim * s->dstate);
   const size_t esz = s->dtype == BISSD_BF16 ? 2 : 4;
   const size_t cd = (size_t)(ndir * s->batch * nc * s->nheads) * 4;
-  w.states = 0;
-  w.sin_t = align256(nst * 4);
-  w.cdecay = w.sin_t + (op == BISSD_OP_BLOCK ? 0 : align256(nst * esz));
-  w.total = w.cdecay + align256(cd);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align256(bytes);
+    return at;
+  };
+  w.states = take(nst * 4);
+  if (op != BISSD_OP_BLOCK) w.sin_t = take(nst * esz);
+  w.cdecay = take(cd);
+  if (op == BISSD_OP_BACKWARD) {
+    const size_t tok = (size_t)(2 * s->batch * s->seqlen * s->nheads) * 4;
+    const size_t rb = (size_t)(s->batch * nc * (s->chunk / 64) * s->nheads) * 4;
+    w.tstates = take(nst * 4);
+    w.sa_t = take(nst * esz);
+    w.gin_t = take(nst * esz);
+    w.dtsum = take(cd);
+    w.ydot = take(tok);
+    w.qx = take(tok);
+    w.qxs = take(tok);
+    w.ddpart = take(rb);
+    w.dAintra = take(2 * rb);
+    w.dAx1 = take(cd);
+    w.dAx2 = take(cd);
+    w.rpart = take(cd * (size_t)(s->headdim * s->dstate / 256));
+  }
+  w.total = o;
   return w;
 }
 
@@ -290,10 +319,6 @@ int bissd_backward(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, bissd
                    const float *D, const float *init_state, const void *dy, float *dx,
                    bissd_grad_t gfwd, bissd_grad_t grev, float *dD, void *workspace,
                    size_t workspace_bytes, void *stream) {
-  (void)init_state;
-  (void)workspace;
-  (void)workspace_bytes;
-  (void)stream;
   int rc = check_shape(s, BISSD_OP_BACKWARD);
   if (rc) return rc;
   if (!x || !D || !dy || !dx || !dD) return BISSD_ERR_NULL;
@@ -301,7 +326,167 @@ int bissd_backward(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, bissd
   if (!gfwd.ddt || !gfwd.dA || !gfwd.dB || !gfwd.dC || !grev.ddt || !grev.dA || !grev.dB ||
       !grev.dC)
     return BISSD_ERR_NULL;
-  return BISSD_ERR_UNSUPPORTED;
+  const void *outs[] = {dx, gfwd.ddt, gfwd.dA, gfwd.dB, gfwd.dC,
+                        grev.ddt, grev.dA, grev.dB, grev.dC, dD};
+  if (!aligned16(x) || !aligned16(D) || !aligned16(dy) || (init_state && !aligned16(init_state)))
+    return BISSD_ERR_ALIGN;
+  for (const void *o : outs)
+    if (!aligned16(o)) return BISSD_ERR_ALIGN;
+  const WsLayout wl = ws_layout(s, BISSD_OP_BACKWARD);
+  if (!workspace || workspace_bytes < wl.total) return BISSD_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return BISSD_ERR_ALIGN;
+  const Sizes z = sizes(s);
+  const size_t tokh = (size_t)(s->batch * s->seqlen * s->nheads) * 4;
+  const size_t bcn = (size_t)(s->batch * s->seqlen * s->ngroups * s->dstate) * 4;
+  const size_t olen[] = {z.x / esize(s) * 4, tokh, z.vec, bcn, bcn, tokh, z.vec, bcn, bcn, z.vec};
+  // outputs overlap neither an input, the workspace nor each other
+  for (int i = 0; i < 10; ++i) {
+    if (hits_inputs(outs[i], olen[i], z, x, fwd, rev, D) || overlap(outs[i], olen[i], dy, z.x) ||
+        overlap(outs[i], olen[i], init_state, z.state) ||
+        overlap(outs[i], olen[i], workspace, wl.total))
+      return BISSD_ERR_ALIAS;
+    for (int k = 0; k < i; ++k)
+      if (overlap(outs[i], olen[i], outs[k], olen[k])) return BISSD_ERR_ALIAS;
+  }
+  if (hits_inputs(workspace, wl.total, z, x, fwd, rev, D) || overlap(workspace, wl.total, dy, z.x) ||
+      overlap(workspace, wl.total, init_state, z.state))
+    return BISSD_ERR_ALIAS;
+
+  hipStream_t st = (hipStream_t)stream;
+  char *ws = (char *)workspace;
+  const int nc = (int)ceil_div(s->seqlen, s->chunk);
+  const int64_t PN = s->headdim * s->dstate;
+  const size_t esz = esize(s);
+  const size_t dirst = (size_t)s->batch * nc * s->nheads * PN * esz;  // bytes per direction
+
+  // primal chunk states and carry-ins
+  ScanArgs a = base_args(s, x, fwd, rev, D);
+  a.states = (float *)(ws + wl.states);
+  a.cdecay = (float *)(ws + wl.cdecay);
+  a.nchunks = nc;
+  a.dir0 = 0;
+  a.ndir = 2;
+  a.init_state = init_state;
+  a.sin_t = ws + wl.sin_t;
+  for (int d = 0; d < 2; ++d) {
+    a.sin[d] = ws + wl.sin_t + d * dirst;
+    a.sin_bstride[d] = (int64_t)nc * a.H * PN;
+    a.sin_cstride[d] = (int64_t)a.H * PN;
+  }
+  hipError_t e = bissd::launch_scan_phase(a, bissd::PHASE_CHUNK_STATE, st);
+  if (e == hipSuccess) e = bissd::launch_scan_phase(a, bissd::PHASE_STATE_PASS, st);
+
+  // A-tangent chunk states (dt-sum weighted), chunk dt sums, and the
+  // A-tangent carry-ins S^A_in
+  ScanArgs ta = a;
+  ta.states = (float *)(ws + wl.tstates);
+  ta.out1 = (float *)(ws + wl.dtsum);
+  if (e == hipSuccess) e = bissd::launch_scan_phase(ta, bissd::PHASE_TAN_STATE, st);
+  ScanArgs tp = a;
+  tp.states2 = (const float *)(ws + wl.tstates);
+  tp.dtsum = (const float *)(ws + wl.dtsum);
+  tp.sin_t = ws + wl.sa_t;
+  if (e == hipSuccess) e = bissd::launch_scan_phase(tp, bissd::PHASE_TAN_PASS, st);
+
+  // adjoint chunk states sum_t 2^cum_t dy_t (outer) C_t (into the tangent
+  // buffer, now consumed) with <G_loc, S^A_in>, then their carries with the
+  // chunk-boundary inner products, then <G^T_loc, S_in>
+  ScanArgs g = a;
+  g.x = dy;
+  g.B[0] = fwd.C;
+  g.B[1] = rev.C;
+  g.init_state = nullptr;
+  g.states = (float *)(ws + wl.tstates);
+  for (int d = 0; d < 2; ++d) g.sin[d] = ws + wl.sa_t + d * dirst;
+  g.out0 = (float *)(ws + wl.dAx1);
+  if (e == hipSuccess) e = bissd::launch_scan_phase(g, bissd::PHASE_ADJ_STATE, st);
+  ScanArgs gp = g;
+  for (int d = 0; d < 2; ++d) gp.sin[d] = a.sin[d];
+  gp.sin_t = ws + wl.gin_t;
+  gp.out0 = (float *)(ws + wl.rpart);
+  if (e == hipSuccess) e = bissd::launch_scan_phase(gp, bissd::PHASE_ADJ_PASS, st);
+  ScanArgs gt = g;
+  for (int d = 0; d < 2; ++d) gt.sin[d] = a.sin[d];
+  gt.out0 = (float *)(ws + wl.dAx2);
+  if (e == hipSuccess) e = bissd::launch_scan_phase(gt, bissd::PHASE_ADJ_TAN, st);
+
+  // dy.y_d per direction (forward output recomputed from the carry-ins)
+  ScanArgs yd = a;
+  yd.aux = dy;
+  yd.out0 = (float *)(ws + wl.ydot);
+  yd.slot_dir[0] = 0;
+  yd.slot_dir[1] = 1;
+  if (e == hipSuccess) e = bissd::launch_scan_phase(yd, bissd::PHASE_YDOT, st);
+
+  // dx and x.(G_t B_t): slot 0 (causal) takes the reverse direction's
+  // adjoint, slot 1 the forward one; B and C trade places
+  ScanArgs q = a;
+  q.x = dy;
+  q.aux = x;
+  q.dt[0] = rev.dt;
+  q.A[0] = rev.A;
+  q.B[0] = rev.C;
+  q.C[0] = rev.B;
+  q.dt[1] = fwd.dt;
+  q.A[1] = fwd.A;
+  q.B[1] = fwd.C;
+  q.C[1] = fwd.B;
+  q.sin[0] = ws + wl.gin_t + dirst;
+  q.sin[1] = ws + wl.gin_t;
+  q.out0 = (float *)(ws + wl.qx);
+  q.out1 = dx;
+  q.out2 = (float *)(ws + wl.ddpart);
+  q.out3 = (float *)(ws + wl.qxs);
+  q.slot_dir[0] = 1;
+  q.slot_dir[1] = 0;
+  if (e == hipSuccess) e = bissd::launch_scan_phase(q, bissd::PHASE_DX, st);
+
+  bissd::BwdArgs b;
+  memset(&b, 0, sizeof(b));
+  b.x = x;
+  b.dy = dy;
+  b.dt[0] = fwd.dt;
+  b.dt[1] = rev.dt;
+  b.A[0] = fwd.A;
+  b.A[1] = rev.A;
+  b.B[0] = fwd.B;
+  b.B[1] = rev.B;
+  b.C[0] = fwd.C;
+  b.C[1] = rev.C;
+  for (int d = 0; d < 2; ++d) {
+    b.sin[d] = ws + wl.sin_t + d * dirst;
+    b.gin[d] = ws + wl.gin_t + d * dirst;
+  }
+  b.st_bstride = (int64_t)nc * a.H * PN;
+  b.st_cstride = (int64_t)a.H * PN;
+  b.ydot = (const float *)(ws + wl.ydot);
+  b.qx = (const float *)(ws + wl.qx);
+  b.qxs = (const float *)(ws + wl.qxs);
+  b.dB[0] = gfwd.dB;
+  b.dB[1] = grev.dB;
+  b.dC[0] = gfwd.dC;
+  b.dC[1] = grev.dC;
+  b.ddt[0] = gfwd.ddt;
+  b.ddt[1] = grev.ddt;
+  b.dA[0] = gfwd.dA;
+  b.dA[1] = grev.dA;
+  b.dD = dD;
+  b.rpart = (const float *)(ws + wl.rpart);
+  b.dAintra = (float *)(ws + wl.dAintra);
+  b.dAx1 = (const float *)(ws + wl.dAx1);
+  b.dAx2 = (const float *)(ws + wl.dAx2);
+  b.ddpart = (const float *)(ws + wl.ddpart);
+  b.L = s->seqlen;
+  b.Z = (int)s->batch;
+  b.H = (int)s->nheads;
+  b.G = (int)s->ngroups;
+  b.N = (int)s->dstate;
+  b.chunk = (int)s->chunk;
+  b.nchunks = nc;
+  b.dtype = s->dtype;
+  if (e == hipSuccess) e = bissd::launch_bwd_panels(b, st);
+  if (e == hipSuccess) e = bissd::launch_bwd_decay(b, st);
+  return finish(e);
 }
 
 }  // extern "C"

@@ -1,0 +1,433 @@
+// bissd_bwd.hip -- backward-only kernels of the bidirectional SSD scan
+// (gfx950): the dB / dC panels, the decay gradients, and the final
+// deterministic reductions.
+//
+// Gradients of Loss = sum(dy * y) through the per-direction recurrence
+// S_t = exp(dt_t A) S_{t-1} + dt_t x_t (outer) B_t, y_t = S_t C_t ("DiffMamba
+// Checkpoints", Model details; the reverse direction runs the same recurrence
+// over the flipped sequence).  Write cum_t for the direction's inclusive
+// log2-decay sum inside a chunk (forward prefix lam, reverse suffix rho) and
+// "s before t" for scan order (s <= t forward, s >= t reverse).  Unrolling the
+// chunked recurrence (plain algebra):
+//
+//   W_h[t][s] = (dy_t . x_s) 2^(cum_t - cum_s) dt_s            (s before t)
+//   dC_t = sum_h [ sum_s W_h[t][s] B_s + 2^cum_t dy_t S_in,h ]
+//   dB_s = sum_h [ sum_t W_h[t][s] C_t + dt_s 2^(cum_end - cum_s) x_s Gc_h ]
+//
+// where S_in is the forward carry-in state of the chunk and Gc the adjoint
+// carry arriving from the chunks after it in scan order (both P x N per
+// head).  Because B and C are shared by the heads of a group, the heads' W
+// are summed first and multiplied by B (or C) once per group.
+//
+// With d_lam_t = dy_t . y_d,t - dt_t x_t . (G_t B_t) (the gradient with
+// respect to the cumulative log-decay at t) the decay gradient of token t is
+// the sum of d_lam over t and every later token in scan order.  Summed over
+// the tokens after the chunk that sum equals <Gc, S_out>, the adjoint carry
+// times the state leaving the chunk, so each chunk's sum restarts from that
+// exact boundary value:  ddt_t = x_t . (G_t B_t) + A dalpha_t.
+//
+// dA is taken in forward mode instead (sum_t dy_t . dy_t/dA), which has only
+// non-negative weights and so none of the cancellation a sum of dt dalpha
+// over every token would carry.  With T_t the cumulative dt in scan order,
+// d/dA of 2^(cum_t - cum_s) is (T_t - T_s) times it, and
+//   dA = sum_chunks [ sum_{s before t in the chunk} E[t][s] (T_t - T_s)
+//                     + <G^T_loc, S_in> + <G_loc, S^A_in> ]
+// with E[t][s] = W[t][s] (C_t . B_s), G_loc = sum_t 2^cum_t dy_t (outer) C_t,
+// G^T_loc its (T_t - T_chunk start)-weighted version and S^A_in the A-tangent
+// of the carry-in state.  The first sum is taken here, from the dC panel's
+// weight tiles; the inner products come from the chunk-state kernels.
+#include <type_traits>
+
+#include "bissd_device.hpp"
+#include "bissd_internal.hpp"
+
+namespace bissd {
+
+// Operand fragment of 8 consecutive elements read straight from a buffer
+// resource (zeros past its end).
+__device__ __forceinline__ void frag_bload(Frag<bf16> &f, bufres r, uint32_t off) {
+  f.v = __builtin_bit_cast(bf16x8, bload16(r, off));
+}
+__device__ __forceinline__ void frag_bload(Frag<float> &f, bufres r, uint32_t off) {
+  const f32x4 a = __builtin_bit_cast(f32x4, bload16(r, off));
+  const f32x4 b = __builtin_bit_cast(f32x4, bload16(r, off + 16));
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f.v[e] = a[e];
+    f.v[4 + e] = b[e];
+  }
+}
+
+// ============================================================ dB / dC panel
+
+template <typename T, int N> struct PanelLds {
+  static constexpr int CP = RowPitch<T, kP>::value;  // column-source slab, natural reads
+  static constexpr int SP = TrPitch<T, N>::value;    // state / value slabs, k along rows
+  float lam[2][kQmax];
+  float dtv[2][kQmax];
+  float cdt[2][kQmax];  // cumulative dt (dC panel)
+  float red[2][4];
+  union U {
+    struct S {
+      T Cs[kRB][CP];
+      T St[kP][SP];
+    } s;
+    T Vs[kRB][SP];
+  } u;
+};
+
+// Workgroup = (batch b, chunk c, direction d, group g, 64-token row-block j)
+// of one panel.  PNL 0 produces dC rows t: the row source is dy, the column
+// source x, the columns s run before t in scan order, and the carried state
+// is the forward carry-in S_in.  PNL 1 produces dB rows s: the row source is
+// x, the column source dy, the columns t run after s, and the carried state
+// is the adjoint carry.  Wave w owns rows 16 w .. 16 w + 15 of the block.
+//
+// Per head of the group: the Gram tiles D[col][row] = ColSrc_col . RowSrc_row
+// come out of the matrix cores already laid out as the A operand of the
+// later product, are weighted elementwise by 2^(cum_later - cum_earlier) dt
+// (exact per element, masked by selection) and summed over heads in fp32
+// registers; the carried-state term RowSrc_row . State is added per head
+// with its row factor.  After the last head the summed weights multiply the
+// value rows (B for dC, C for dB), staged one 64-row slab at a time.
+// The dC panel also forms C.B^T for its tiles once (before the heads) and
+// sums E[t][s] (T_t - T_s) per head: the within-chunk part of dA.
+template <typename T, int N, int PNL>
+__global__ __launch_bounds__(kThreads) void k_bwd_panel(BwdArgs a) {
+  using Sm = PanelLds<T, N>;
+  using SC = SlabRows<T, kP, Sm::CP>;
+  using SS = SlabRows<T, N, Sm::SP>;
+  __shared__ Sm sm;
+  constexpr int NT = N / 16;
+  constexpr uint32_t ES = sizeof(T);
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
+  const int Q = a.chunk, NRB = Q / kRB, H = a.H, G = a.G, hpg = H / G;
+  const int64_t L = a.L;
+  // work item = (((b * nchunks + c) * 2 + d) * G + g) * NRB + j
+  int bx = xcd_linear_id(blockIdx.x, gridDim.x);
+  const int j = bx % NRB;
+  bx /= NRB;
+  const int g = bx % G;
+  bx /= G;
+  const int d = bx % 2;
+  bx /= 2;
+  const int c = bx % a.nchunks, b = bx / a.nchunks;
+  const int64_t t0 = (int64_t)c * Q;
+  const int qlen = (int)((L - t0) < Q ? (L - t0) : Q);
+  if (j * kRB >= qlen) return;
+  const int klast = (qlen - 1) / kRB;
+  // columns before the row in index order: dC forward, dB reverse
+  const bool colLE = (PNL == 0) == (d == 0);
+  const int kb = colLE ? 0 : j, ke = colLE ? j : klast;
+
+  const T *rowsrc = reinterpret_cast<const T *>(PNL == 0 ? a.dy : a.x);
+  const T *colsrc = reinterpret_cast<const T *>(PNL == 0 ? a.x : a.dy);
+  const T *valsrc = reinterpret_cast<const T *>(PNL == 0 ? a.B[d] : a.C[d]);
+  const T *stsrc = reinterpret_cast<const T *>(PNL == 0 ? a.sin[d] : a.gin[d]);
+  const bufres rRow = make_buf(rowsrc + (int64_t)b * L * H * kP, (uint32_t)(L * H * kP * ES));
+  const bufres rCol = make_buf(colsrc + (int64_t)b * L * H * kP, (uint32_t)(L * H * kP * ES));
+  const bufres rVal = make_buf(valsrc + (int64_t)b * L * G * N, (uint32_t)(L * G * N * ES));
+  const uint32_t xrs = (uint32_t)(H * kP * ES), vrs = (uint32_t)(G * N * ES);
+  const int rrow = j * kRB + 16 * w + r16;  // this lane's row as Gram operand
+
+  f32x4 wsum[4][4], oacc[NT];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) zero4(wsum[k][u]);
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) zero4(oacc[nt]);
+
+  u32x4 pf[SS::NV > SC::NV ? SS::NV : SC::NV];
+
+  // dC panel: cbt[k][u][i] = C_row . B_col in the Gram tiles' layout
+  f32x4 cbt[4][4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) zero4(cbt[k][u]);
+  if constexpr (PNL == 0) {
+    const bufres rC = make_buf(reinterpret_cast<const T *>(a.C[d]) + (int64_t)b * L * G * N,
+                               (uint32_t)(L * G * N * ES));
+    Frag<T> cfr[N / 32];
+#pragma unroll
+    for (int ks = 0; ks < N / 32; ++ks)
+      frag_bload(cfr[ks], rC, (uint32_t)((t0 + rrow) * G + g) * N * ES + (32 * ks + 8 * g4) * ES);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (k < kb || k > ke) continue;
+      SS::prefetch(pf, rVal, (uint32_t)((t0 + k * kRB) * G + g) * N * ES, vrs);
+      __syncthreads();
+      SS::commit(&sm.u.Vs[0][0], pf);
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int ks = 0; ks < N / 32; ++ks) {
+          Frag<T> bf;
+          frag_ld8(bf, &sm.u.Vs[16 * u + r16][32 * ks + 8 * g4]);
+          mma(cbt[k][u], bf, cfr[ks]);
+        }
+    }
+  }
+
+  for (int hi = 0; hi < hpg; ++hi) {
+    const int h = g * hpg + hi, buf = hi & 1;
+    const T *dth = reinterpret_cast<const T *>(a.dt[d]) + ((int64_t)b * L + t0) * H + h;
+    if (w == 0)
+      chunk_decay_scan<T>(dth, H, qlen, Q, a.A[d][h] * kLog2e, d == 1, sm.lam[buf], sm.dtv[buf]);
+    if (PNL == 0 && w == 1) chunk_decay_scan<T>(dth, H, qlen, Q, 1.0f, d == 1, sm.cdt[buf], sm.dtv[buf]);
+    float dai = 0.0f;
+    // row-source fragments of this lane's row (k = head-dim index)
+    Frag<T> rf[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      frag_bload(rf[ks], rRow, (uint32_t)((t0 + rrow) * H + h) * kP * ES + (32 * ks + 8 * g4) * ES);
+    const float *lam = sm.lam[buf], *dtv = sm.dtv[buf];
+
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (k < kb || k > ke) continue;
+      SC::prefetch(pf, rCol, (uint32_t)((t0 + k * kRB) * H + h) * kP * ES, xrs);
+      __syncthreads();
+      SC::commit(&sm.u.s.Cs[0][0], pf);
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        f32x4 dg;
+        zero4(dg);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          Frag<T> cf;
+          frag_ld8(cf, &sm.u.s.Cs[16 * u + r16][32 * ks + 8 * g4]);
+          mma(dg, cf, rf[ks]);
+        }
+        // dg[i] = ColSrc[col] . RowSrc[row], col = 64k + 16u + 4 g4 + i
+        const float lrow = lam[rrow], drow = dtv[rrow];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int col = k * kRB + 16 * u + 4 * g4 + i;
+          bool ok = true;
+          if (k == j) ok = colLE ? (col <= rrow) : (col >= rrow);
+          const float lcol = lam[col];
+          const float ex = PNL == 0 ? lrow - lcol : lcol - lrow;
+          const float dtf = PNL == 0 ? dtv[col] : drow;
+          const float wv = ok ? dg[i] * (exp2_fast(fminf(ex, 0.0f)) * dtf) : 0.0f;
+          wsum[k][u][i] += wv;
+          if (PNL == 0) dai += wv * cbt[k][u][i] * (sm.cdt[buf][rrow] - sm.cdt[buf][col]);
+        }
+      }
+    }
+    if (PNL == 0) {
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) dai += __shfl_xor(dai, o, 64);
+      if (lane == 0) sm.red[buf][w] = dai;
+    }
+
+    // carried-state term: rows r = 64 j + 16 w + 4 g4 + i, columns n
+    const int64_t soff = (int64_t)b * a.st_bstride + (int64_t)c * a.st_cstride + (int64_t)h * kP * N;
+    const bufres rSt = make_buf(stsrc + soff, (uint32_t)(kP * N * ES));
+    SS::prefetch(pf, rSt, 0u, (uint32_t)(N * ES));
+    __syncthreads();
+    SS::commit(&sm.u.s.St[0][0], pf);
+    __syncthreads();
+    if (PNL == 0 && tid == 0)
+      a.dAintra[((((int64_t)d * a.Z + b) * a.nchunks + c) * NRB + j) * H + h] =
+          (sm.red[buf][0] + sm.red[buf][1]) + (sm.red[buf][2] + sm.red[buf][3]);
+    float fr[4];
+    const float lend = d == 0 ? lam[Q - 1] : lam[0];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = j * kRB + 16 * w + 4 * g4 + i;
+      fr[i] = PNL == 0 ? exp2_fast(lam[r]) : dtv[r] * exp2_fast(fminf(lend - lam[r], 0.0f));
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      f32x4 t2;
+      zero4(t2);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        Frag<T> sf;
+        frag_rows(sf, &sm.u.s.St[0][0], Sm::SP, 32 * ks + 8 * g4, 32 * ks + 8 * g4 + 4, 16 * nt);
+        mma(t2, rf[ks], sf);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) oacc[nt][i] += fr[i] * t2[i];
+    }
+  }
+
+  // summed weights x value rows, one 64-row slab per column block
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (k < kb || k > ke) continue;
+    SS::prefetch(pf, rVal, (uint32_t)((t0 + k * kRB) * G + g) * N * ES, vrs);
+    __syncthreads();
+    SS::commit(&sm.u.Vs[0][0], pf);
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      float m[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        m[i] = wsum[k][2 * q][i];
+        m[4 + i] = wsum[k][2 * q + 1][i];
+      }
+      Frag<T> mf;
+      frag_from(mf, m);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        Frag<T> vf;
+        frag_rows(vf, &sm.u.Vs[0][0], Sm::SP, 32 * q + 4 * g4, 32 * q + 16 + 4 * g4, 16 * nt);
+        mma(oacc[nt], mf, vf);
+      }
+    }
+  }
+
+  float *out = PNL == 0 ? a.dC[d] : a.dB[d];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = j * kRB + 16 * w + 4 * g4 + i;
+    if (r >= qlen) continue;
+    float *o = out + ((((int64_t)b * L + t0 + r) * G + g) * N);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) o[16 * nt + r16] = oacc[nt][i];
+  }
+}
+
+// ====================================================== decay gradients
+
+// One wavefront per (batch, direction, head) sequence, one chunk per step:
+// d_lam_t = dy.y_d,t - dt_t x_t.(G_t B_t) (both taken without their common
+// t' = t term, which cancels); dalpha_t = the in-chunk sum of
+// d_lam over t and the tokens after it in scan order, plus the chunk's
+// boundary value (the wave partials of <adjoint carry, state after the
+// chunk>, summed in a fixed order); ddt_t = x_t.(G_t B_t) + A dalpha_t.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_bwd_decay(BwdArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int seq = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  const int H = a.H;
+  if (seq >= a.Z * 2 * H) return;
+  const int h = seq % H, d = (seq / H) % 2, b = seq / (2 * H);
+  const int64_t L = a.L;
+  const int Q = a.chunk, K = Q / 64, nwv = kP * a.N / 256;
+  const T *dt = reinterpret_cast<const T *>(a.dt[d]) + (int64_t)b * L * H + h;
+  const float *yd = a.ydot + ((int64_t)d * a.Z + b) * L * H + h;
+  const float *qx = a.qx + ((int64_t)d * a.Z + b) * L * H + h;
+  const float *qxs = a.qxs + ((int64_t)d * a.Z + b) * L * H + h;
+  float *ddt = a.ddt[d] + (int64_t)b * L * H + h;
+  const float A = a.A[d][h];
+  for (int c = 0; c < a.nchunks; ++c) {
+    const float *rp = a.rpart + ((((int64_t)d * a.Z + b) * a.nchunks + c) * H + h) * nwv;
+    float R = 0.0f;
+    for (int k = 0; k < nwv; ++k) R += rp[k];
+    const int64_t base = (int64_t)c * Q + lane * K;
+    float v[4], ql[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t t = base + i;
+      const bool ok = i < K && t < L;
+      ql[i] = ok ? qx[t * H] : 0.0f;
+      // dy.y_d and x.(G_t B_t) both without their common t' = t term
+      v[i] = ok ? yd[t * H] - to_f(dt[t * H]) * qxs[t * H] : 0.0f;
+    }
+    float run = 0.0f, acc[4];
+    if (d == 0) {
+#pragma unroll
+      for (int i = 3; i >= 0; --i) {
+        run += v[i];
+        acc[i] = run;
+      }
+      const float incl = wave_scan_down(run);
+      float excl = __shfl_down(incl, 1, 64);
+      if (lane == 63) excl = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] += excl + R;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        run += v[i];
+        acc[i] = run;
+      }
+      const float incl = wave_scan_up(run);
+      float excl = __shfl_up(incl, 1, 64);
+      if (lane == 0) excl = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] += excl + R;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t t = base + i;
+      if (i < K && t < L) ddt[t * H] = ql[i] + A * acc[i];
+    }
+  }
+}
+
+// dA[d][h]: the cross-chunk inner products of every (batch, chunk) plus the
+// within-chunk sums of every (batch, chunk, row-block) that holds tokens;
+// dD[h]: the dy.x partials of those row-blocks.  One workgroup per output;
+// fixed-order strided sums, then a fixed tree.
+__global__ __launch_bounds__(kThreads) void k_bwd_reduce(BwdArgs a) {
+  __shared__ float red[kThreads];
+  const int tid = threadIdx.x, H = a.H, NRB = a.chunk / kRB;
+  const int o = blockIdx.x;  // 0 .. 2H-1: dA, 2H .. 3H-1: dD
+  const int d = o < 2 * H ? o / H : 0, h = o < 2 * H ? o % H : o - 2 * H;
+  float s = 0.0f;
+  if (o < 2 * H) {
+    const int64_t nbc = (int64_t)a.Z * a.nchunks;
+    for (int64_t i = tid; i < nbc; i += kThreads) {
+      const int64_t k = ((int64_t)d * nbc + i) * H + h;
+      s += a.dAx1[k] + a.dAx2[k];
+    }
+  }
+  const int64_t n = (int64_t)a.Z * a.nchunks * NRB;
+  for (int64_t i = tid; i < n; i += kThreads) {
+    const int j = (int)(i % NRB);
+    const int64_t c = (i / NRB) % a.nchunks;
+    const int64_t rem = a.L - c * a.chunk;
+    const int qlen = (int)(rem < a.chunk ? rem : a.chunk);
+    if (j * kRB >= qlen) continue;
+    s += o < 2 * H ? a.dAintra[((int64_t)d * n + i) * H + h] : a.ddpart[i * H + h];
+  }
+  red[tid] = s;
+  __syncthreads();
+  for (int k = kThreads / 2; k > 0; k >>= 1) {
+    if (tid < k) red[tid] += red[tid + k];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    if (o < 2 * H) a.dA[d][h] = red[0];
+    else a.dD[h] = red[0];
+  }
+}
+
+// ============================================================= launchers
+
+template <typename T, int N>
+static void launch_panels_t(const BwdArgs &a, hipStream_t st) {
+  dim3 g((unsigned)(a.Z * a.nchunks * 2 * a.G * (a.chunk / kRB)));
+  hipLaunchKernelGGL((k_bwd_panel<T, N, 0>), g, dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((k_bwd_panel<T, N, 1>), g, dim3(kThreads), 0, st, a);
+}
+
+hipError_t launch_bwd_panels(const BwdArgs &a, hipStream_t st) {
+  if (a.dtype == 1) {
+    if (a.N == 128) launch_panels_t<bf16, 128>(a, st);
+    else launch_panels_t<bf16, 64>(a, st);
+  } else {
+    if (a.N == 128) launch_panels_t<float, 128>(a, st);
+    else launch_panels_t<float, 64>(a, st);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_decay(const BwdArgs &a, hipStream_t st) {
+  const int nseq = a.Z * 2 * a.H;
+  dim3 g((unsigned)((nseq + 3) / 4));
+  if (a.dtype == 1) hipLaunchKernelGGL(k_bwd_decay<bf16>, g, dim3(kThreads), 0, st, a);
+  else hipLaunchKernelGGL(k_bwd_decay<float>, g, dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL(k_bwd_reduce, dim3((unsigned)(3 * a.H)), dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace bissd

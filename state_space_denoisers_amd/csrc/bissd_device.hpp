@@ -518,12 +518,13 @@ __device__ __forceinline__ float wave_max(float v) {
 // Log2-decay cumulative sums of one chunk for one (direction, head), run by
 // one wavefront.  a_s = dt_s * A * log2(e) for the chunk's Q tokens (tokens
 // at or beyond qlen count as dt = 0).  Forward: lam[s] = sum_{k<=s} a_k.
-// Reverse: lam[s] = sum_{k>=s} a_k.  dtv[s] receives dt_s.  Returns the
+// Reverse: lam[s] = sum_{k>=s} a_k.  With `exclusive` the sums leave out
+// a_s itself (sum_{k<s}, sum_{k>s}).  dtv[s] receives dt_s.  Returns the
 // largest |a_s| of the chunk (in every lane).
 template <typename T>
 __device__ __forceinline__ float chunk_decay_scan(const T *dt, int64_t stride, int qlen, int Q,
                                                   float A2, bool reverse, float *lam,
-                                                  float *dtv) {
+                                                  float *dtv, bool exclusive = false) {
   const int lane = threadIdx.x & 63;
   const int K = Q / 64;  // 1, 2 or 4 tokens per lane
   float a[4], d[4], amax = 0.0f;
@@ -535,10 +536,12 @@ __device__ __forceinline__ float chunk_decay_scan(const T *dt, int64_t stride, i
     amax = fmaxf(amax, fabsf(a[i]));
   }
   amax = wave_max(amax);
+  float pre[4];
   if (!reverse) {
     float run = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      pre[i] = run;
       run += a[i];
       a[i] = run;
     }
@@ -548,13 +551,14 @@ __device__ __forceinline__ float chunk_decay_scan(const T *dt, int64_t stride, i
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (i < K) {
-        lam[lane * K + i] = excl + a[i];
+        lam[lane * K + i] = excl + (exclusive ? pre[i] : a[i]);
         dtv[lane * K + i] = d[i];
       }
   } else {
     float run = 0.0f;
 #pragma unroll
     for (int i = 3; i >= 0; --i) {
+      pre[i] = run;
       if (i < K) {
         run += a[i];
         a[i] = run;
@@ -566,7 +570,7 @@ __device__ __forceinline__ float chunk_decay_scan(const T *dt, int64_t stride, i
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (i < K) {
-        lam[lane * K + i] = excl + a[i];
+        lam[lane * K + i] = excl + (exclusive ? pre[i] : a[i]);
         dtv[lane * K + i] = d[i];
       }
   }

@@ -38,6 +38,8 @@ template <typename T, int N, int HT> struct K1Lds {
   float lam[HT][kQmax];
   float dtv[HT][kQmax];
   float scale[HT][kQmax];
+  float cdt[HT][kQmax];  // cumulative dt in scan order (tangent modes)
+  float red[4][HT];
   T Bs[kRB][BPT];
   T Xs[HT][kRB][XPT];
 };
@@ -45,12 +47,20 @@ template <typename T, int N, int HT> struct K1Lds {
 // Chunk-local state S_loc = sum_s w_s x_s (outer) B_s with
 // w_s = dt_s 2^(lam_last - lam_s) (forward) or dt_s 2^(rho_first - rho_s)
 // (reverse), for one (batch, chunk, direction, head tile), plus the chunk's
-// total log2-decay.  64-token slabs are fetched into registers one slab
+// total log2-decay (MODE 0).  The backward pass reuses the kernel with other
+// weights; T_s below is the cumulative dt inside the chunk in scan order
+// (the A-derivative of the decay exponent):
+//   MODE 1  w_s = 2^cum_s              adjoint state sum_t 2^cum_t dy_t (outer) C_t
+//                                      (dy passed as x, C as B), also <state, sin>
+//   MODE 2  w_s = dt_s 2^(cum_end - cum_s) (T_end - T_s)   A-tangent state, and
+//                                      T_end per chunk to out1
+//   MODE 3  w_s = 2^cum_s T_s          (dy, C as in MODE 1) only <state, sin>
+// MODEs 1-3 leave the chunk decays as MODE 0 wrote them.  64-token slabs are fetched into registers one slab
 // ahead of the matrix-core work and stored row-major; both operands are read
 // with k (the token) running down the rows.  Output
 // states[d][b][c][h][p][n] (fp32), cdecay[d][b][c][h].  Wave w owns state
 // columns n in [w N/4, (w+1) N/4).
-template <typename T, int N, int HT>
+template <typename T, int N, int HT, int MODE>
 __global__ __launch_bounds__(kThreads) void k1_chunk_state(ScanArgs a) {
   using Sm = K1Lds<T, N, HT>;
   using SB = SlabRows<T, N, Sm::BPT>;
@@ -86,18 +96,33 @@ __global__ __launch_bounds__(kThreads) void k1_chunk_state(ScanArgs a) {
 #pragma unroll
   for (int hh = 0; hh < HT; ++hh) SX::prefetch(pfX[hh], rX, xoff + hh * kP * ES, xrs);
 
-  for (int hh = w; hh < HT; hh += 4)
-    chunk_decay_scan<T>(dt + ((int64_t)b * L + t0) * H + h0 + hh, H, qlen, Q,
-                        a.A[d][h0 + hh] * kLog2e, d == 1, sm.lam[hh], sm.dtv[hh]);
+  constexpr bool TAN = MODE >= 2;
+  for (int pr = w; pr < (TAN ? 2 : 1) * HT; pr += 4) {
+    const int hh = pr % HT;
+    const T *dtp = dt + ((int64_t)b * L + t0) * H + h0 + hh;
+    if (pr < HT)
+      chunk_decay_scan<T>(dtp, H, qlen, Q, a.A[d][h0 + hh] * kLog2e, d == 1, sm.lam[hh], sm.dtv[hh]);
+    else
+      chunk_decay_scan<T>(dtp, H, qlen, Q, 1.0f, d == 1, sm.cdt[hh], sm.dtv[hh]);
+  }
   __syncthreads();
-  if (tid < HT)
-    a.cdecay[(((int64_t)d * a.Z + b) * a.nchunks + c) * H + h0 + tid] =
-        d == 0 ? sm.lam[tid][Q - 1] : sm.lam[tid][0];
+  const int64_t chi = (((int64_t)d * a.Z + b) * a.nchunks + c) * H + h0;  // (d, b, c, h0)
+  if (MODE == 0 && tid < HT) a.cdecay[chi + tid] = d == 0 ? sm.lam[tid][Q - 1] : sm.lam[tid][0];
+  if (MODE == 2 && tid < HT) a.out1[chi + tid] = d == 0 ? sm.cdt[tid][Q - 1] : sm.cdt[tid][0];
   for (int it = tid; it < HT * Q; it += kThreads) {
     const int hh = it / Q, s = it % Q;
     const float ref = d == 0 ? sm.lam[hh][Q - 1] : sm.lam[hh][0];
     const float dv = sm.dtv[hh][s];
-    sm.scale[hh][s] = dv != 0.0f ? dv * exp2_fast(ref - sm.lam[hh][s]) : 0.0f;
+    float v;
+    if (MODE == 1) {
+      v = exp2_fast(sm.lam[hh][s]);
+    } else if (MODE == 3) {
+      v = exp2_fast(sm.lam[hh][s]) * sm.cdt[hh][s];
+    } else {
+      v = dv != 0.0f ? dv * exp2_fast(ref - sm.lam[hh][s]) : 0.0f;
+      if (MODE == 2) v *= (d == 0 ? sm.cdt[hh][Q - 1] : sm.cdt[hh][0]) - sm.cdt[hh][s];
+    }
+    sm.scale[hh][s] = v;
   }
 
   f32x4 acc[HT][4][NT];
@@ -142,17 +167,42 @@ __global__ __launch_bounds__(kThreads) void k1_chunk_state(ScanArgs a) {
     }
   }
 
-  float *out = a.states + ((((int64_t)d * a.Z + b) * a.nchunks + c) * H + h0) * (int64_t)(kP * N);
+  if constexpr (MODE <= 2) {
+    float *out = a.states + chi * (int64_t)(kP * N);
 #pragma unroll
-  for (int hh = 0; hh < HT; ++hh)
+    for (int hh = 0; hh < HT; ++hh)
 #pragma unroll
-    for (int pt = 0; pt < 4; ++pt)
+      for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
+        for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          out[(int64_t)hh * kP * N + (16 * pt + 4 * g4 + i) * N + nb + 16 * nt + r16] =
-              acc[hh][pt][nt][i];
+          for (int i = 0; i < 4; ++i)
+            out[(int64_t)hh * kP * N + (16 * pt + 4 * g4 + i) * N + nb + 16 * nt + r16] =
+                acc[hh][pt][nt][i];
+  }
+  if constexpr (MODE == 1 || MODE == 3) {
+    // Frobenius product with the given state of the same (direction, batch,
+    // chunk, head), reduced in a fixed order
+    const T *ref = reinterpret_cast<const T *>(a.sin[d]) + (int64_t)b * a.sin_bstride[d] +
+                   (int64_t)c * a.sin_cstride[d] + (int64_t)h0 * kP * N;
+#pragma unroll
+    for (int hh = 0; hh < HT; ++hh) {
+      float v = 0.0f;
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            v += acc[hh][pt][nt][i] *
+                 to_f(ref[(int64_t)hh * kP * N + (16 * pt + 4 * g4 + i) * N + nb + 16 * nt + r16]);
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+      if (lane == 0) sm.red[w][hh] = v;
+    }
+    __syncthreads();
+    if (tid < HT) a.out0[chi + tid] = (sm.red[0][tid] + sm.red[1][tid]) + (sm.red[2][tid] + sm.red[3][tid]);
+  }
 }
 
 // =================================================================== K2
@@ -162,13 +212,18 @@ __global__ __launch_bounds__(kThreads) void k1_chunk_state(ScanArgs a) {
 // from zero.  Each chunk's carry-in is written, rounded once to T, to the
 // sin_t buffer that the output kernel reads; the carry itself stays fp32 in
 // registers and the forward state after the last chunk goes to final_state.
+// flip: the adjoint carries of the backward pass, which run against their
+// direction (forward: c downwards, reverse: c upwards), from zero.
+// With flip, out0 (if set) receives per-wave partial sums of <carry arriving
+// at chunk c, primal state after chunk c> (the primal carry-in of the next
+// chunk in scan order, from sin[d]): the chunk-boundary value of the decay
+// gradient.  Laid out [d][b][c][h][PN / 256].
 template <typename T>
-__global__ __launch_bounds__(kThreads) void k2_state_pass(ScanArgs a, int PN) {
-  const int e = (blockIdx.x * kThreads + threadIdx.x) * 4;
+__global__ __launch_bounds__(kThreads) void k2_state_pass(ScanArgs a, int PN, int flip) {
+  const int e = (blockIdx.x * kThreads + threadIdx.x) * 4;  // PN is a multiple of 1024
   const int h = blockIdx.y;
   const int d = a.dir0 + (int)(blockIdx.z % a.ndir);
   const int b = (int)(blockIdx.z / a.ndir);
-  if (e >= PN) return;
   const int nc = a.nchunks, H = a.H;
   const int64_t cs = (int64_t)H * PN;
   const int64_t base = (((int64_t)d * a.Z + b) * nc * H + h) * (int64_t)PN + e;
@@ -176,13 +231,33 @@ __global__ __launch_bounds__(kThreads) void k2_state_pass(ScanArgs a, int PN) {
   T *dst = a.sin_t ? reinterpret_cast<T *>(a.sin_t) + base : nullptr;
   const float *dec = a.cdecay + ((int64_t)d * a.Z + b) * nc * H + h;
   f32x4 S = {0.0f, 0.0f, 0.0f, 0.0f};
-  if (d == 0 && a.init_state)
+  const bool primal_fwd = d == 0 && !flip;
+  if (primal_fwd && a.init_state)
     S = *reinterpret_cast<const f32x4 *>(a.init_state + ((int64_t)b * H + h) * PN + e);
-  const int step = d == 0 ? 1 : -1;
-  int c = d == 0 ? 0 : nc - 1;
+  const bool up = (d == 0) != (flip != 0);
+  const int step = up ? 1 : -1;
+  int c = up ? 0 : nc - 1;
+  const bool rpart = flip && a.out0;
+  const int nwv = PN / 256, wv = (blockIdx.x * kThreads + threadIdx.x) >> 6;
   for (int n = 0; n < nc; ++n, c += step) {
     const f32x4 loc = *reinterpret_cast<const f32x4 *>(src + c * cs);
     const float g = exp2_fast(dec[(int64_t)c * H]);
+    if (rpart) {
+      // primal state after chunk c = primal carry-in of chunk c + 1 (forward)
+      // or c - 1 (reverse)
+      const int cn = d == 0 ? c + 1 : c - 1;
+      float v = 0.0f;
+      if (cn >= 0 && cn < nc) {
+        const T *sp = reinterpret_cast<const T *>(a.sin[d]) + (int64_t)b * a.sin_bstride[d] +
+                      (int64_t)cn * a.sin_cstride[d] + (int64_t)h * PN + e;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v += S[i] * to_f(sp[i]);
+      }
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+      if ((threadIdx.x & 63) == 0)
+        a.out0[((((int64_t)d * a.Z + b) * nc + c) * H + h) * nwv + wv] = v;
+    }
     if (dst) {
       if constexpr (sizeof(T) == 2) {
         bf16x4 o;
@@ -196,8 +271,50 @@ __global__ __launch_bounds__(kThreads) void k2_state_pass(ScanArgs a, int PN) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) S[i] = g * S[i] + loc[i];
   }
-  if (d == 0 && a.final_state)
+  if (primal_fwd && a.final_state)
     *reinterpret_cast<f32x4 *>(a.final_state + ((int64_t)b * H + h) * PN + e) = S;
+}
+
+// A-tangent of the carry-in states, four elements per thread:
+// SA_in(c+1) = 2^cdecay(c) (SA_in(c) + Tsum(c) S_in(c)) + ST_loc(c), from zero,
+// alongside the primal carry S_in (from init_state or zero), in each
+// direction's scan order; SA_in of every chunk goes to sin_t in T.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k2_tangent_pass(ScanArgs a, int PN) {
+  const int e = (blockIdx.x * kThreads + threadIdx.x) * 4;
+  const int h = blockIdx.y;
+  const int d = (int)(blockIdx.z % 2);
+  const int b = (int)(blockIdx.z / 2);
+  const int nc = a.nchunks, H = a.H;
+  const int64_t cs = (int64_t)H * PN;
+  const int64_t base = (((int64_t)d * a.Z + b) * nc * H + h) * (int64_t)PN + e;
+  const float *sl = a.states + base, *tl = a.states2 + base;
+  T *dst = reinterpret_cast<T *>(a.sin_t) + base;
+  const float *dec = a.cdecay + ((int64_t)d * a.Z + b) * nc * H + h;
+  const float *tsum = a.dtsum + ((int64_t)d * a.Z + b) * nc * H + h;
+  f32x4 S = {0.0f, 0.0f, 0.0f, 0.0f}, SA = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (d == 0 && a.init_state)
+    S = *reinterpret_cast<const f32x4 *>(a.init_state + ((int64_t)b * H + h) * PN + e);
+  const int step = d == 0 ? 1 : -1;
+  int c = d == 0 ? 0 : nc - 1;
+  for (int n = 0; n < nc; ++n, c += step) {
+    const f32x4 loc = *reinterpret_cast<const f32x4 *>(sl + c * cs);
+    const f32x4 tloc = *reinterpret_cast<const f32x4 *>(tl + c * cs);
+    const float g = exp2_fast(dec[(int64_t)c * H]), ts = tsum[(int64_t)c * H];
+    if constexpr (sizeof(T) == 2) {
+      bf16x4 o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = (bf16)SA[i];
+      *reinterpret_cast<bf16x4 *>(dst + c * cs) = o;
+    } else {
+      *reinterpret_cast<f32x4 *>(dst + c * cs) = SA;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      SA[i] = g * (SA[i] + ts * S[i]) + tloc[i];
+      S[i] = g * S[i] + loc[i];
+    }
+  }
 }
 
 // =================================================================== K3
@@ -211,6 +328,8 @@ template <typename T, int N, int HT> struct K3Lds {
   float dtd[2][HT][kRB];      // dt of the diagonal block (exact path)
   float refb[2][HT];
   float amax[2][HT];
+  float red[4][HT];  // per-wave partial sums (PHASE_DX)
+  float bcd[2][kRB];  // B_t . C_t of the row-block's tokens (PHASE_DX)
   union U {
     struct S {
       T Bs[kRB][BP];
@@ -250,7 +369,24 @@ template <typename T, int N, int HT, bool SF32> struct K3Pf {
 // work of the current one.
 // SF32: the carry-in states are fp32 (the block update's cached state)
 // rather than the compute dtype written by the state pass.
-template <typename T, int N, int HT, bool SF32>
+//
+// MODE 0 writes y.  The backward pass runs the same kernel twice more:
+// MODE 1 recomputes each direction's output y_d and stores only dy.y_d per
+// (token, head); MODE 2 evaluates the adjoint product G_t B_t, where
+// G_t = sum_{t' at or after t in scan order} 2^(cum_t' - cum_t) dy_t' (outer) C_t'
+// plus the carried adjoint.  That is this kernel's structure with the row
+// and column operands swapped (B_t as the row, C_t' as the column), dy in
+// place of x, no dt on the staged side, and exclusive cumulative decays; slot
+// 0 (causal) carries the reverse direction and slot 1 the forward one.  It
+// writes dx = dt_f G_f B + dt_r G_r B + D dy, x.(G_t B_t) per direction and
+// partial sums of dy.x.
+// In both backward modes the diagonal tile is masked strictly (t' != t):
+// the t' = t term is the same product E_tt = dt_t (dy_t.x_t)(B_t.C_t) in
+// dy.y_d and in dt_t x.(G_t B_t), and the decay gradient needs only their
+// difference, so leaving it out of both removes a cancellation that large
+// |A| would amplify.  MODE 2 adds the term back where it is a plain part of
+// the result: dy_t (B_t.C_t) into G_t B_t for dx and x.(G_t B_t).
+template <typename T, int N, int HT, bool SF32, int MODE>
 __global__ __launch_bounds__(kThreads) void k3_chunk_out(ScanArgs a) {
   using Sm = K3Lds<T, N, HT>;
   using PF = K3Pf<T, N, HT, SF32>;
@@ -315,7 +451,7 @@ __global__ __launch_bounds__(kThreads) void k3_chunk_out(ScanArgs a) {
     const int d = pr / HT, hh = pr % HT;
     const float am = chunk_decay_scan<T>(
         reinterpret_cast<const T *>(a.dt[d]) + ((int64_t)b * L + t0) * H + h0 + hh, H, qlen, Q,
-        a.A[d][h0 + hh] * kLog2e, d == 1, sm.lam[d][hh], sm.scale[d][hh]);
+        a.A[d][h0 + hh] * kLog2e, d == 1, sm.lam[d][hh], sm.scale[d][hh], MODE == 2);
     if (lane == 0) sm.amax[d][hh] = am;
   }
 
@@ -361,7 +497,11 @@ __global__ __launch_bounds__(kThreads) void k3_chunk_out(ScanArgs a) {
     const bool dg = (s / kRB) == j;
     const float ref = dg ? (d == 0 ? sm.lam[0][hh][s | 15] : sm.lam[1][hh][s & ~15]) : sm.refb[d][hh];
     const float dv = sm.scale[d][hh][s];
-    sm.scale[d][hh][s] = (dg && exact) ? 1.0f : (dv != 0.0f ? dv * exp2_fast(ref - sm.lam[d][hh][s]) : 0.0f);
+    float v;
+    if (dg && exact) v = 1.0f;
+    else if (MODE == 2) v = exp2_fast(ref - sm.lam[d][hh][s]);
+    else v = dv != 0.0f ? dv * exp2_fast(ref - sm.lam[d][hh][s]) : 0.0f;
+    sm.scale[d][hh][s] = v;
   }
 
   f32x4 acc[HT][4];
@@ -416,6 +556,16 @@ __global__ __launch_bounds__(kThreads) void k3_chunk_out(ScanArgs a) {
         for (int u = 0; u < 4; ++u)
           if (u >= ulo && u <= uhi) mma(cb[u], bfr[u], cfd[ks]);
       }
+      if (MODE == 2 && diag && g4 == (r16 >> 2)) {
+        // this lane holds the diagonal (row t = 16w + r16, column s = t)
+        float v = 0.0f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int i2 = 0; i2 < 4; ++i2)
+            if (u == w && i2 == (r16 & 3)) v = cb[u][i2];
+        sm.bcd[d][16 * w + r16] = v;
+      }
       if (!diag) {
 #pragma unroll
         for (int hh = 0; hh < HT; ++hh)
@@ -456,14 +606,18 @@ __global__ __launch_bounds__(kThreads) void k3_chunk_out(ScanArgs a) {
               float wgt;
               if (exact) {
                 const int sl = 16 * u + 4 * g4 + i2;
-                wgt = exp2_fast(fminf(lt - sm.lam[d][hh][s0 + sl], 0.0f)) * sm.dtd[d][hh][sl];
+                wgt = exp2_fast(fminf(lt - sm.lam[d][hh][s0 + sl], 0.0f)) *
+                      (MODE == 2 ? 1.0f : sm.dtd[d][hh][sl]);
               } else {
                 wgt = f[u];
               }
               // select, never multiply by a 0/1 mask: masked positions must
               // not turn a large factor into 0 * inf
               bool ok = (u >= ulo && u <= uhi);
-              if (u == w) ok = ok && (d == 0 ? (4 * g4 + i2 <= r16) : (4 * g4 + i2 >= r16));
+              if (u == w) {
+                if (MODE == 0) ok = ok && (d == 0 ? (4 * g4 + i2 <= r16) : (4 * g4 + i2 >= r16));
+                else ok = ok && (d == 0 ? (4 * g4 + i2 < r16) : (4 * g4 + i2 > r16));
+              }
               m[e] = ok ? cb[u][i2] * wgt : 0.0f;
             }
             Frag<T> mf;
@@ -514,36 +668,149 @@ __global__ __launch_bounds__(kThreads) void k3_chunk_out(ScanArgs a) {
       }
     }
   };
-  run_direction(std::integral_constant<int, 0>{});
-  run_direction(std::integral_constant<int, 1>{});
+  if constexpr (MODE == 0) {
+    run_direction(std::integral_constant<int, 0>{});
+    run_direction(std::integral_constant<int, 1>{});
 
-  // y = acc + D x, IH heads at a time staged through LDS so that every lane
-  // writes 16 contiguous bytes
-  T *yg = reinterpret_cast<T *>(a.y) + (((int64_t)b * L + t0 + j * kRB) * H + h0) * kP;
-  const T *xo = xg + (int64_t)j * kRB * xrs;
+    // y = acc + D x, IH heads at a time staged through LDS so that every lane
+    // writes 16 contiguous bytes
+    T *yg = reinterpret_cast<T *>(a.y) + (((int64_t)b * L + t0 + j * kRB) * H + h0) * kP;
+    const T *xo = xg + (int64_t)j * kRB * xrs;
 #pragma unroll
-  for (int ih = 0; ih < HT / IH; ++ih) {
-    __syncthreads();
+    for (int ih = 0; ih < HT / IH; ++ih) {
+      __syncthreads();
 #pragma unroll
-    for (int q = 0; q < IH; ++q)
+      for (int q = 0; q < IH; ++q)
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
+        for (int v = 0; v < 4; ++v)
 #pragma unroll
-        for (int i2 = 0; i2 < 4; ++i2)
-          sm.u.Out[q][16 * w + 4 * g4 + i2][16 * v + r16] = acc[ih * IH + q][v][i2];
-    __syncthreads();
-    for (int it = tid; it < IH * kRB * 8; it += kThreads) {
-      const int q = it / (kRB * 8), r = (it >> 3) % kRB, p0 = (it & 7) * 8;
-      if (j * kRB + r >= qlen) continue;
-      const int hh = ih * IH + q;
-      const float Dh = a.D[h0 + hh];
-      const int64_t off = (int64_t)r * xrs + hh * kP + p0;
-      float xv[8], o[8];
-      gload8(xv, xo + off);
+          for (int i2 = 0; i2 < 4; ++i2)
+            sm.u.Out[q][16 * w + 4 * g4 + i2][16 * v + r16] = acc[ih * IH + q][v][i2];
+      __syncthreads();
+      for (int it = tid; it < IH * kRB * 8; it += kThreads) {
+        const int q = it / (kRB * 8), r = (it >> 3) % kRB, p0 = (it & 7) * 8;
+        if (j * kRB + r >= qlen) continue;
+        const int hh = ih * IH + q;
+        const float Dh = a.D[h0 + hh];
+        const int64_t off = (int64_t)r * xrs + hh * kP + p0;
+        float xv[8], o[8];
+        gload8(xv, xo + off);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = sm.u.Out[q][r][p0 + e] + Dh * xv[e];
-      gstore8(yg + off, o);
+        for (int e = 0; e < 8; ++e) o[e] = sm.u.Out[q][r][p0 + e] + Dh * xv[e];
+        gstore8(yg + off, o);
+      }
     }
+  } else {
+    // Backward modes: each slot's accumulator is finished on its own.  Rows
+    // are staged through LDS; 8 consecutive lanes hold one row of one head
+    // (8 elements each) and reduce their dot products with shuffles.
+    const T *xo = xg + (int64_t)j * kRB * xrs;  // MODE 1: x, MODE 2: dy
+    const T *auxo = reinterpret_cast<const T *>(a.aux) + (((int64_t)b * L + t0 + j * kRB) * H + h0) * kP;
+    float ddp[HT];
+#pragma unroll
+    for (int hh = 0; hh < HT; ++hh) ddp[hh] = 0.0f;
+    auto slot_epilogue = [&](auto dc) __attribute__((always_inline)) {
+      constexpr int d = decltype(dc)::value;
+      const int sd = a.slot_dir[d];
+#pragma unroll
+      for (int ih = 0; ih < HT / IH; ++ih) {
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < IH; ++q)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+#pragma unroll
+            for (int i2 = 0; i2 < 4; ++i2)
+              sm.u.Out[q][16 * w + 4 * g4 + i2][16 * v + r16] = acc[ih * IH + q][v][i2];
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < IH; ++q) {
+          const int hh = ih * IH + q;
+#pragma unroll
+          for (int m2 = 0; m2 < (kRB * 8) / kThreads; ++m2) {
+            const int it = tid + m2 * kThreads;
+            const int r = it >> 3, p0 = (it & 7) * 8;
+            const int64_t tok = t0 + j * kRB + r;
+            const bool valid = j * kRB + r < qlen;
+            const int64_t off = (int64_t)r * xrs + hh * kP + p0;
+            float o[8], v[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = sm.u.Out[q][r][p0 + e];
+            if (valid) gload8(v, auxo + off);
+            else
+#pragma unroll
+              for (int e = 0; e < 8; ++e) v[e] = 0.0f;
+            float part = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) part += o[e] * v[e];
+            part += __shfl_xor(part, 1, 64);
+            part += __shfl_xor(part, 2, 64);
+            part += __shfl_xor(part, 4, 64);
+            const int64_t oix = (((int64_t)sd * a.Z + b) * L + tok) * H + h0 + hh;
+            if constexpr (MODE == 1) {
+              if ((tid & 7) == 0 && valid) a.out0[oix] = part;
+            } else {
+              // part = x.(G_t B_t) without t' = t; add dy_t (B_t.C_t)
+              const float dtr = sm.dtd[d][hh][r], bc = sm.bcd[d][r];
+              float *dxp = a.out1 + (((int64_t)b * L + tok) * H + h0 + hh) * kP + p0;
+              float dyv[8], dxo[8];
+              if (valid) gload8(dyv, xo + off);
+              else
+#pragma unroll
+                for (int e = 0; e < 8; ++e) dyv[e] = 0.0f;
+              float pin = 0.0f;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                o[e] += bc * dyv[e];
+                pin += o[e] * v[e];
+              }
+              pin += __shfl_xor(pin, 1, 64);
+              pin += __shfl_xor(pin, 2, 64);
+              pin += __shfl_xor(pin, 4, 64);
+              if ((tid & 7) == 0 && valid) {
+                a.out0[oix] = pin;
+                a.out3[oix] = part;
+              }
+              if (d == 0) {
+                const float Dh = a.D[h0 + hh];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                  dxo[e] = Dh * dyv[e] + dtr * o[e];
+                  ddp[hh] += dyv[e] * v[e];
+                }
+              } else if (valid) {
+                gload8(dxo, dxp);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) dxo[e] += dtr * o[e];
+              }
+              if (valid) gstore8(dxp, dxo);
+            }
+          }
+        }
+      }
+      if constexpr (MODE == 2 && d == 0) {
+        // dy.x of this row-block, per head, in a fixed order
+#pragma unroll
+        for (int hh = 0; hh < HT; ++hh) {
+          float v = ddp[hh];
+#pragma unroll
+          for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+          if (lane == 0) sm.red[w][hh] = v;
+        }
+        __syncthreads();
+        if (tid < HT)
+          a.out2[(((int64_t)b * a.nchunks + c) * NRB + j) * H + h0 + tid] =
+              (sm.red[0][tid] + sm.red[1][tid]) + (sm.red[2][tid] + sm.red[3][tid]);
+      }
+    };
+    run_direction(std::integral_constant<int, 0>{});
+    slot_epilogue(std::integral_constant<int, 0>{});
+#pragma unroll
+    for (int hh = 0; hh < HT; ++hh)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) zero4(acc[hh][v]);
+    run_direction(std::integral_constant<int, 1>{});
+    slot_epilogue(std::integral_constant<int, 1>{});
   }
 }
 
@@ -551,41 +818,51 @@ __global__ __launch_bounds__(kThreads) void k3_chunk_out(ScanArgs a) {
 
 template <typename T, int N, int HT>
 static void launch_t(const ScanArgs &a, int phase, hipStream_t st) {
-  if (phase == PHASE_CHUNK_STATE) {
+  if (phase == PHASE_CHUNK_STATE || phase == PHASE_ADJ_STATE || phase == PHASE_TAN_STATE ||
+      phase == PHASE_ADJ_TAN) {
     dim3 g((unsigned)(a.Z * a.nchunks * a.ndir * (a.H / HT)));
-    hipLaunchKernelGGL((k1_chunk_state<T, N, HT>), g, dim3(kThreads), 0, st, a);
-  } else if (phase == PHASE_STATE_PASS) {
+    if (phase == PHASE_CHUNK_STATE)
+      hipLaunchKernelGGL((k1_chunk_state<T, N, HT, 0>), g, dim3(kThreads), 0, st, a);
+    else if (phase == PHASE_ADJ_STATE)
+      hipLaunchKernelGGL((k1_chunk_state<T, N, HT, 1>), g, dim3(kThreads), 0, st, a);
+    else if (phase == PHASE_TAN_STATE)
+      hipLaunchKernelGGL((k1_chunk_state<T, N, HT, 2>), g, dim3(kThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL((k1_chunk_state<T, N, HT, 3>), g, dim3(kThreads), 0, st, a);
+  } else if (phase == PHASE_TAN_PASS) {
+    const int PN = kP * N;
+    dim3 g2((unsigned)(PN / 4 / kThreads), (unsigned)a.H, (unsigned)(a.Z * 2));
+    hipLaunchKernelGGL(k2_tangent_pass<T>, g2, dim3(kThreads), 0, st, a, PN);
+  } else if (phase == PHASE_STATE_PASS || phase == PHASE_ADJ_PASS) {
     const int PN = kP * N;
     dim3 g2((unsigned)((PN / 4 + kThreads - 1) / kThreads), (unsigned)a.H, (unsigned)(a.Z * a.ndir));
-    hipLaunchKernelGGL(k2_state_pass<T>, g2, dim3(kThreads), 0, st, a, PN);
+    hipLaunchKernelGGL(k2_state_pass<T>, g2, dim3(kThreads), 0, st, a, PN,
+                       phase == PHASE_ADJ_PASS ? 1 : 0);
   } else {
     dim3 g((unsigned)(a.Z * a.nchunks * (a.chunk / kRB) * (a.H / HT)));
-    if (a.sin_f32[0] || a.sin_f32[1])
-      hipLaunchKernelGGL((k3_chunk_out<T, N, HT, true>), g, dim3(kThreads), 0, st, a);
+    if (phase == PHASE_YDOT)
+      hipLaunchKernelGGL((k3_chunk_out<T, N, HT, false, 1>), g, dim3(kThreads), 0, st, a);
+    else if (phase == PHASE_DX)
+      hipLaunchKernelGGL((k3_chunk_out<T, N, HT, false, 2>), g, dim3(kThreads), 0, st, a);
+    else if (a.sin_f32[0] || a.sin_f32[1])
+      hipLaunchKernelGGL((k3_chunk_out<T, N, HT, true, 0>), g, dim3(kThreads), 0, st, a);
     else
-      hipLaunchKernelGGL((k3_chunk_out<T, N, HT, false>), g, dim3(kThreads), 0, st, a);
+      hipLaunchKernelGGL((k3_chunk_out<T, N, HT, false, 0>), g, dim3(kThreads), 0, st, a);
   }
 }
 
 template <typename T, int N>
 static void launch_n(const ScanArgs &a, int phase, hipStream_t st, int HT) {
-  if (HT == 4) launch_t<T, N, 4>(a, phase, st);
-  else if (HT == 2) launch_t<T, N, 2>(a, phase, st);
+  if (HT == 2) launch_t<T, N, 2>(a, phase, st);
   else launch_t<T, N, 1>(a, phase, st);
 }
 
-// Heads of one tile must share their B/C group: the tile is 4, 2 or 1 heads,
-// whichever divides the heads per group.
-#ifndef BISSD_MAX_HEAD_TILE
-#define BISSD_MAX_HEAD_TILE 2
-#endif
-
 hipError_t launch_scan_phase(const ScanArgs &a, int phase, hipStream_t st) {
+  // Heads of one tile share their B/C group: 2 heads when the heads per
+  // group are even (which keeps the output kernel at two waves per SIMD),
+  // else 1.
   const int hpg = a.H / a.G;
-  int HT = (hpg % 4 == 0) ? 4 : (hpg % 2 == 0 ? 2 : 1);
-  if (HT > BISSD_MAX_HEAD_TILE) HT = BISSD_MAX_HEAD_TILE;
-  // tiles of 2 heads keep the output kernel at two waves per SIMD
-  if (HT > 2) HT = 2;
+  const int HT = hpg % 2 == 0 ? 2 : 1;
   if (a.dtype == 1) {
     if (a.N == 128) launch_n<bf16, 128>(a, phase, st, HT);
     else launch_n<bf16, 64>(a, phase, st, HT);

@@ -27,10 +27,55 @@ struct ScanArgs {
   int Z, H, G, N, chunk, nchunks;
   int dir0, ndir;  // directions handled by the chunk-state / state-pass phases
   int dtype;       // 0 fp32, 1 bf16
+  // backward phases only
+  const void *aux;  // PHASE_YDOT: dy; PHASE_DX: x (x above then holds dy)
+  float *out0;      // PHASE_YDOT: dy.y_d; PHASE_DX: x.(G_t B_t); [2][Z][L][H], by direction.
+                    // PHASE_ADJ_STATE / PHASE_ADJ_TAN: <state, sin> per [2][Z][nchunks][H].
+                    // PHASE_ADJ_PASS: wave partials of <adjoint carry, state after the chunk>
+  float *out1;      // PHASE_DX: dx [Z][L][H][P]; PHASE_TAN_STATE: chunk dt sums [2][Z][nchunks][H]
+  float *out2;      // PHASE_DX: partial sums of dy.x per (b, chunk, row-block, head)
+  float *out3;      // PHASE_DX: x.(G_t B_t) without the t' = t term, [2][Z][L][H]
+  const float *states2;  // PHASE_TAN_PASS: tangent chunk states
+  const float *dtsum;    // PHASE_TAN_PASS: chunk dt sums
+  int slot_dir[2];  // direction under which each output-kernel slot stores out0
 };
 
-enum { PHASE_CHUNK_STATE = 0, PHASE_STATE_PASS = 1, PHASE_CHUNK_OUT = 2 };
+enum {
+  PHASE_CHUNK_STATE = 0,  // chunk-local states and chunk decays
+  PHASE_STATE_PASS = 1,   // carry-in states
+  PHASE_CHUNK_OUT = 2,    // y
+  PHASE_ADJ_STATE = 3,    // chunk-local adjoint states sum_t 2^cum_t dy_t (outer) C_t
+  PHASE_ADJ_PASS = 4,     // adjoint carries, flowing against each direction
+  PHASE_YDOT = 5,         // per-direction dy.y_d (forward output recomputed)
+  PHASE_DX = 6,           // dx and x.(G_t B_t)
+  PHASE_TAN_STATE = 7,    // chunk-local A-tangent states (dt-sum weighted)
+  PHASE_TAN_PASS = 8,     // A-tangent carry-in states
+  PHASE_ADJ_TAN = 9,      // <dt-sum weighted adjoint chunk state, carry-in state>
+};
 
 hipError_t launch_scan_phase(const ScanArgs &a, int phase, hipStream_t st);
+
+// Arguments of the backward-only kernels (dB / dC panels, decay gradients,
+// final reductions).
+struct BwdArgs {
+  const void *x, *dy;
+  const void *dt[2];
+  const float *A[2];
+  const void *B[2], *C[2];
+  const void *sin[2];  // forward carry-in states per direction, compute dtype
+  const void *gin[2];  // adjoint carries per direction, compute dtype
+  int64_t st_bstride, st_cstride;  // element strides of sin / gin
+  const float *ydot, *qx, *qxs;    // [2][Z][L][H]; qxs leaves out the t' = t term
+  float *dB[2], *dC[2], *ddt[2], *dA[2], *dD;
+  const float *rpart;   // [2][Z][nchunks][H][P N / 256] wave partials of the chunk-boundary dalpha
+  float *dAintra;       // [2][Z][nchunks][chunk/64][H] within-chunk A-tangent sums
+  const float *dAx1, *dAx2;  // [2][Z][nchunks][H] cross-chunk A-tangent inner products
+  const float *ddpart;  // [Z][nchunks][chunk/64][H]
+  int64_t L;
+  int Z, H, G, N, chunk, nchunks, dtype;
+};
+
+hipError_t launch_bwd_panels(const BwdArgs &a, hipStream_t st);
+hipError_t launch_bwd_decay(const BwdArgs &a, hipStream_t st);
 
 }  // namespace bissd

@@ -134,3 +134,31 @@ def test_status_strings(lib):
     for code in _abi.STATUS:
         assert lib.bissd_status_string(code)
     assert b"unknown" in lib.bissd_status_string(99)
+
+
+def call_backward(lib, s, **over):
+    args = dict(x=addr(0), fwd=dirs(1), rev=dirs(5), D=addr(9), init=None, dy=addr(10),
+                dx=addr(11), gf=_abi.Grad(addr(12), addr(13), addr(14), addr(15)),
+                gr=_abi.Grad(addr(16), addr(17), addr(18), addr(19)), dD=addr(20),
+                ws=addr(21), nws=1 << 40)
+    args.update(over)
+    return lib.bissd_backward(C.byref(s), args["x"], args["fwd"], args["rev"], args["D"],
+                              args["init"], args["dy"], args["dx"], args["gf"], args["gr"],
+                              args["dD"], args["ws"], C.c_size_t(args["nws"]), None)
+
+
+def test_backward_validation(lib):
+    """Every rejected backward call returns before anything is enqueued
+    (these pointers are fake; a call that passed validation would launch)."""
+    s = shape(seqlen=100)  # every tensor fits in the 1 MiB spacing
+    assert lib.bissd_workspace_size(C.byref(s), _abi.OP_BACKWARD) > \
+        lib.bissd_workspace_size(C.byref(s), _abi.OP_FORWARD)
+    assert call_backward(lib, s, dy=None) == -1
+    assert call_backward(lib, s, gr=_abi.Grad(addr(16), None, addr(18), addr(19))) == -1
+    assert call_backward(lib, s, dx=C.c_void_p(A * 12 + 8)) == -4
+    assert call_backward(lib, s, nws=64) == -5
+    assert call_backward(lib, s, dx=addr(0)) == -7                     # dx over x
+    assert call_backward(lib, s, dD=addr(10)) == -7                    # dD over dy
+    assert call_backward(lib, s, gf=_abi.Grad(addr(12), addr(13), addr(14), addr(14))) == -7
+    assert call_backward(lib, s, ws=addr(11)) == -7                    # workspace over dx
+    assert call_backward(lib, shape(seqlen=100, headdim=32)) == -3

@@ -1,0 +1,137 @@
+"""GPU parity of the backward pass (bissd_backward) against the fp64 oracle's
+reverse-mode recurrence, element by element on the same seeded inputs.
+
+Every gradient (dx, ddt, dA, dB, dC per direction, dD) must satisfy
+max|gpu - oracle| / max|oracle| <= 1e-4 (fp32) or 2e-2 (bf16), in the check
+modes "full" (as configured) and "scan" (D = 0).
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from synth import gen
+from tests.gpu_util import TOL, dirs, f32_dev, host, maxrel, select_rows, to_dev
+
+pytestmark = pytest.mark.gpu
+
+W = gen.WORKLOADS
+KEYS = ("dx", "ddt_f", "dA_f", "dB_f", "dC_f", "ddt_r", "dA_r", "dB_r", "dC_r", "dD")
+
+
+def gpu_backward(inp, dtype, chunk, init_state=None):
+    import state_space_denoisers_amd as ssd
+    T = to_dev(inp, dtype)
+    fwd, rev = dirs(T)
+    init = None if init_state is None else f32_dev(init_state)
+    g = ssd.bissd_backward(T["x"], fwd, rev, T["D"], T["dy"], chunk=chunk, init_state=init)
+    torch.cuda.synchronize()
+    return {k: host(v) for k, v in g.items()}
+
+
+def check(inp, dtype, chunk, init_state=None, rows=None):
+    g = gpu_backward(inp, dtype, chunk, init_state)
+    ref_in = inp if rows is None else select_rows(inp, rows)
+    r = O.backward(ref_in, ref_in["dy"], init_state=init_state)
+    errs = {}
+    for k in KEYS:
+        gk = g[k]
+        if rows is not None and gk.ndim > 1:
+            gk = gk[rows]
+        if rows is not None and gk.ndim == 1:
+            continue  # batch-reduced gradients need every row
+        assert np.all(np.isfinite(gk)), k
+        errs[k] = maxrel(gk, r[k])
+    print(" ".join(f"{k}={v:.1e}" for k, v in errs.items()), flush=True)
+    bad = {k: v for k, v in errs.items() if v > TOL[dtype]}
+    assert not bad, (bad, errs)
+    return errs
+
+
+@pytest.mark.parametrize("mode", ("full", "scan"))
+def test_tiny_fp32(mode):
+    w = W["tiny_fp32"]
+    inp = gen.make_inputs(w, mode=mode, with_dy=True)
+    print("bwd tiny_fp32", mode, flush=True)
+    check(inp, "fp32", w.chunk)
+
+
+@pytest.mark.parametrize("chunk,L", [(64, 1), (64, 63), (64, 65), (128, 255), (256, 257),
+                                     (256, 1000), (128, 1000)])
+def test_chunks_and_ragged_lengths_fp32(chunk, L):
+    w = W["tiny_fp32"].replace(L=L, chunk=chunk, Z=2)
+    inp = gen.make_inputs(w, mode="scan", with_dy=True)
+    print("bwd ragged", chunk, L, flush=True)
+    check(inp, "fp32", chunk)
+
+
+@pytest.mark.parametrize("dtype", ("fp32", "bf16"))
+def test_groups_and_dstate(dtype):
+    w = W["tiny_fp32"].replace(L=300, H=8, G=2, N=128, chunk=128, Z=2, dtype=dtype)
+    inp = gen.make_inputs(w, with_dy=True)
+    print("bwd groups", dtype, flush=True)
+    check(inp, dtype, w.chunk)
+
+
+def test_init_state_fp32():
+    w = W["tiny_fp32"].replace(L=200, Z=2)
+    inp = gen.make_inputs(w, with_dy=True)
+    S0 = np.random.default_rng(77).standard_normal((2, w.H, 64, w.N)).astype(np.float32) * 0.5
+    print("bwd init_state", flush=True)
+    check(inp, "fp32", w.chunk, init_state=S0.astype(np.float64))
+
+
+def test_weight_tied_directions():
+    w = W["tiny_fp32"].replace(L=190, Z=2)
+    inp = gen.make_inputs(w, with_dy=True)
+    for k in ("dt", "A", "B", "C"):
+        inp[k + "_r"] = inp[k + "_f"]
+    print("bwd weight-tied", flush=True)
+    check(inp, "fp32", 64)
+
+
+@pytest.mark.parametrize("mode", ("full", "scan"))
+def test_layer_bf16(mode):
+    """bf16, N=128, chunk 256, ragged last chunk."""
+    w = W["train_L2k"].replace(Z=2, L=700, H=6)
+    inp = gen.make_inputs(w, mode=mode, with_dy=True)
+    print("bwd layer bf16", mode, flush=True)
+    check(inp, "bf16", w.chunk)
+
+
+def test_train_L2k_full():
+    """The training workload at full size (Z=16, L=2048, 24 heads, N=128,
+    chunk 256, bf16); every gradient against the oracle on every row."""
+    w = W["train_L2k"]
+    inp = gen.make_inputs(w, with_dy=True)
+    print("bwd train_L2k", flush=True)
+    check(inp, "bf16", w.chunk)
+
+
+def test_extreme_decays_fp32():
+    """Large dt A (decays underflow inside a chunk) and dt = 0 tokens."""
+    w = W["tiny_fp32"].replace(L=256, Z=1, chunk=128)
+    inp = gen.make_inputs(w, with_dy=True)
+    inp["dt_f"][:, ::7] = 0.0
+    inp["A_f"][:] = -40.0
+    inp["A_r"][0] = -1e4
+    print("bwd extreme decays", flush=True)
+    check(inp, "fp32", w.chunk)
+
+
+def test_determinism_bitwise():
+    w = W["tiny_fp32"].replace(L=777, Z=2, H=8, N=128, chunk=256, dtype="bf16")
+    inp = gen.make_inputs(w, with_dy=True)
+    a = gpu_backward(inp, "bf16", 256)
+    b = gpu_backward(inp, "bf16", 256)
+    for k in KEYS:
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_chunk_invariance_fp32():
+    w = W["tiny_fp32"].replace(L=512, Z=1)
+    inp = gen.make_inputs(w, with_dy=True)
+    a = gpu_backward(inp, "fp32", 64)
+    b = gpu_backward(inp, "fp32", 256)
+    for k in KEYS:
+        assert maxrel(a[k], b[k]) <= 1e-5, k
