@@ -11,13 +11,15 @@ W untimed warm-up steps, then exactly K timed steps between two device
 synchronisations; `value` is tokens per second over the timed region.
 
 The same run also measures, live with HIP events on the launch stream, the
-average duration of each of the three kernels (via bissd_forward_phase), the
-long-context L=65536 scan, and the block update with a cached 262,144-token
-prefix state; and times the fp64 CPU oracle on a bounded sample of the same
-workload.  One JSON line is printed.
+average duration of each of the three kernels inside complete forward calls
+(enqueued phase by phase through bissd_forward_phase), the
+long-context L=65536 scan, the training step (forward + backward, batch 16,
+L=2048), and the block update with a cached 262,144-token prefix state; and
+times the fp64 CPU oracle on a bounded sample of the same workload.  One
+JSON line is printed.
 
 Profiling helpers (for rocprofv3 runs):
-    python bench.py --profile-phase {0,1,2,all} [--workload W] [--iters R]
+    python bench.py --profile-phase {0,1,2,all,backward} [--workload W] [--iters R]
     python bench.py --copy-calibrate
 """
 from __future__ import annotations
@@ -113,16 +115,26 @@ def event_time_ms(fn, reps):
 
 
 def phase_times_us(f: Forward, reps):
+    """Average duration of each forward kernel inside complete forward calls:
+    every call is enqueued as its three phases with a HIP event recorded
+    between them on the launch stream, so each kernel runs in the same
+    context (caches, preceding kernels) as in the timed region."""
     import torch
     f()
     torch.cuda.synchronize()
-    t0 = event_time_ms(lambda: f.phase(0), reps)
-    t01 = event_time_ms(lambda: (f.phase(0), f.phase(1)), reps)
-    t2 = event_time_ms(lambda: f.phase(2), reps)
-    f()  # leave a consistent workspace / y
+    s = torch.cuda.current_stream()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
+    for r in range(reps):
+        evs[r][0].record(s)
+        for p in range(3):
+            f.phase(p)
+            evs[r][p + 1].record(s)
     torch.cuda.synchronize()
-    return {PHASE_NAMES[0]: 1e3 * t0, PHASE_NAMES[1]: 1e3 * max(t01 - t0, 0.0),
-            PHASE_NAMES[2]: 1e3 * t2}
+    tot = [0.0, 0.0, 0.0]
+    for r in range(reps):
+        for p in range(3):
+            tot[p] += evs[r][p].elapsed_time(evs[r][p + 1])
+    return {PHASE_NAMES[p]: 1e3 * tot[p] / reps for p in range(3)}
 
 
 def per_token_bytes(w):
@@ -261,12 +273,76 @@ def bench_block(reps):
     return out
 
 
+class Train:
+    """Preallocated forward + backward call on one workload (a training
+    step of the scan: y, then every gradient of sum(dy * y))."""
+
+    def __init__(self, w):
+        import torch
+        import state_space_denoisers_amd as ssd
+        from state_space_denoisers_amd import _abi
+        from synth import gen
+        self.ssd, self.w = ssd, w
+        self.f = Forward(w)
+        dev = self.f.y.device
+        inp = gen.make_inputs(w, with_dy=True)
+        self.dy = gen.as_torch(inp["dy"], w.dtype, dev)
+        shape = ssd.shape_of(self.f.T["x"], self.f.T["B_f"], w.chunk)
+        n = ssd.bissd_workspace_size(shape, _abi.OP_BACKWARD)
+        self.ws = torch.empty(n, dtype=torch.uint8, device=dev)
+        self.grads = ssd.bissd_backward(self.f.T["x"], self.f.fwd, self.f.rev, self.f.T["D"],
+                                        self.dy, chunk=w.chunk, workspace=self.ws)
+
+    def backward(self):
+        self.ssd.bissd_backward(self.f.T["x"], self.f.fwd, self.f.rev, self.f.T["D"], self.dy,
+                                chunk=self.w.chunk, grads=self.grads, workspace=self.ws)
+
+    def __call__(self):
+        self.f()
+        self.backward()
+
+
+def train_bytes_per_token(w):
+    """Algorithmic HBM bytes per token of forward + backward: the forward's
+    reads and y write, then the backward reads x, dy, dt and B/C of both
+    directions and writes dx, ddt, dB and dC (fp32 gradients)."""
+    e = 2 if w.dtype == "bf16" else 4
+    bwd = (2 * w.H * w.P * e + 2 * w.H * e + 4 * w.G * w.N * e
+           + w.H * w.P * 4 + 2 * w.H * 4 + 4 * w.G * w.N * 4)
+    return per_token_bytes(w) + bwd
+
+
+def bench_train(steps):
+    import torch
+    from synth import gen
+    w = gen.WORKLOADS["train_L2k"]
+    t = Train(w)
+    for _ in range(3):
+        t()
+    torch.cuda.synchronize()
+    ms_f = event_time_ms(t.f, steps)
+    ms_b = event_time_ms(t.backward, steps)
+    ms = event_time_ms(t, steps)
+    return {"workload": w.name, "batch": w.Z, "seq_len": w.L, "tokens_per_s": w.tokens / (ms * 1e-3),
+            "ms_per_step": ms, "ms_forward": ms_f, "ms_backward": ms_b,
+            "hbm_algorithmic_GBs": train_bytes_per_token(w) * w.tokens / (ms * 1e-3) / 1e9}
+
+
 # ------------------------------------------------------------- profiling
 
 def profile_phase(args):
     import torch
     from synth import gen
     w = gen.WORKLOADS[args.workload]
+    if args.profile_phase == "backward":
+        t = Train(w)
+        torch.cuda.synchronize()
+        print(f"profiling backward on {w.name} x{args.iters}", flush=True)
+        for _ in range(args.iters):
+            t.backward()
+        torch.cuda.synchronize()
+        print("done", flush=True)
+        return
     f = Forward(w)
     f()
     torch.cuda.synchronize()
@@ -299,7 +375,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--profile-phase", choices=["0", "1", "2", "all"])
+    ap.add_argument("--profile-phase", choices=["0", "1", "2", "all", "backward"])
     ap.add_argument("--workload", default="layer130m_L1k")
     ap.add_argument("--iters", type=int, default=20)
     ap.add_argument("--copy-calibrate", action="store_true")
@@ -368,6 +444,11 @@ def main():
             log(f"bench: long {extra['long_L65k']['tokens_per_s']:.3e} tokens/s")
         except Exception as exc:  # report, do not hide
             extra["long_L65k"] = {"error": repr(exc)}
+        try:
+            extra["train_L2k"] = bench_train(max(5, args.steps // 20))
+            log(f"bench: train {extra['train_L2k']}")
+        except Exception as exc:
+            extra["train_L2k"] = {"error": repr(exc)}
         try:
             extra["block_update"] = bench_block(max(50, args.steps))
             log(f"bench: block {extra['block_update']}")

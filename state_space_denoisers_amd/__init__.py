@@ -147,21 +147,32 @@ def bissd_block_update(state_in: torch.Tensor, x_blk: torch.Tensor, fwd, rev,
     return y_blk, state_out
 
 
+GRAD_KEYS = ("dx", "ddt_f", "dA_f", "dB_f", "dC_f", "ddt_r", "dA_r", "dB_r", "dC_r", "dD")
+
+
 def bissd_backward(x: torch.Tensor, fwd, rev, D: torch.Tensor, dy: torch.Tensor, *,
                    chunk: int = 256, init_state: Optional[torch.Tensor] = None,
-                   workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+                   grads: Optional[dict] = None, workspace: Optional[torch.Tensor] = None,
+                   stream=None) -> dict:
     """Gradients of sum(dy * y) (include/bissd.h, bissd_backward).  Returns a
-    dict with dx, ddt_f, dA_f, dB_f, dC_f, ddt_r, dA_r, dB_r, dC_r, dD (fp32)."""
+    dict with dx, ddt_f, dA_f, dB_f, dC_f, ddt_r, dA_r, dB_r, dC_r, dD (fp32);
+    ``grads`` may hold preallocated tensors under those keys."""
     lib = _abi.load()
     fwd, rev = Dir(*fwd), Dir(*rev)
     shape = shape_of(x, fwd.B, chunk)
     f32 = dict(dtype=torch.float32, device=x.device)
-    g = {"dx": torch.empty(x.shape, **f32), "dD": torch.empty(D.shape, **f32)}
+    g = dict(grads) if grads is not None else {}
+    if "dx" not in g:
+        g["dx"] = torch.empty(x.shape, **f32)
+    if "dD" not in g:
+        g["dD"] = torch.empty(D.shape, **f32)
     for d, p in (("f", fwd), ("r", rev)):
-        g[f"ddt_{d}"] = torch.empty(p.dt.shape, **f32)
-        g[f"dA_{d}"] = torch.empty(p.A.shape, **f32)
-        g[f"dB_{d}"] = torch.empty(p.B.shape, **f32)
-        g[f"dC_{d}"] = torch.empty(p.C.shape, **f32)
+        for k, like in (("ddt", p.dt), ("dA", p.A), ("dB", p.B), ("dC", p.C)):
+            if f"{k}_{d}" not in g:
+                g[f"{k}_{d}"] = torch.empty(like.shape, **f32)
+    for k in GRAD_KEYS:
+        if g[k].dtype != torch.float32:
+            raise TypeError(f"{k} must be float32")
     gf = _abi.Grad(_ptr(g["ddt_f"]), _ptr(g["dA_f"]), _ptr(g["dB_f"]), _ptr(g["dC_f"]))
     gr = _abi.Grad(_ptr(g["ddt_r"]), _ptr(g["dA_r"]), _ptr(g["dB_r"]), _ptr(g["dC_r"]))
     ws, nws = _workspace(shape, _abi.OP_BACKWARD, x.device, workspace)
