@@ -61,20 +61,14 @@ __device__ __forceinline__ void frag_bload(Frag<float> &f, bufres r, uint32_t of
 // ============================================================ dB / dC panel
 
 template <typename T, int N> struct PanelLds {
-  static constexpr int CP = RowPitch<T, kP>::value;  // column-source slab, natural reads
-  static constexpr int SP = TrPitch<T, N>::value;    // state / value slabs, k along rows
   float lam[2][kQmax];
   float dtv[2][kQmax];
   float cdt[2][kQmax];  // cumulative dt (dC panel)
   float red[2][4];
-  union U {
-    struct S {
-      T Cs[kRB][CP];
-      T St[kP][SP];
-    } s;
-    T Vs[kRB][SP];
-  } u;
 };
+
+// vector-memory count 0, other counters left alone
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Workgroup = (batch b, chunk c, direction d, group g, 64-token row-block j)
 // of one panel.  PNL 0 produces dC rows t: the row source is dy, the column
@@ -89,17 +83,29 @@ template <typename T, int N> struct PanelLds {
 // (exact per element, masked by selection) and summed over heads in fp32
 // registers; the carried-state term RowSrc_row . State is added per head
 // with its row factor.  After the last head the summed weights multiply the
-// value rows (B for dC, C for dB), staged one 64-row slab at a time.
+// value rows (B for dC, C for dB), one 64-row slab at a time.
 // The dC panel also forms C.B^T for its tiles once (before the heads) and
 // sums E[t][s] (T_t - T_s) per head: the within-chunk part of dA.
+//
+// Every head's column slabs and state are copied buffer -> LDS directly into
+// a tile.  With two tiles (the bf16 dC panel) the copies for head h + 1 are
+// in flight while head h is multiplied; with one, two workgroups per CU
+// overlap each other's copies.  Each head costs one or two barriers.
 template <typename T, int N, int PNL>
 __global__ __launch_bounds__(kThreads) void k_bwd_panel(BwdArgs a) {
   using Sm = PanelLds<T, N>;
-  using SC = SlabRows<T, kP, Sm::CP>;
-  using SS = SlabRows<T, N, Sm::SP>;
-  __shared__ Sm sm;
-  constexpr int NT = N / 16;
   constexpr uint32_t ES = sizeof(T);
+  constexpr int CRB = kP * ES, SRB = N * ES;
+  constexpr int CSB = 4 * kRB * CRB, STB = kP * SRB;
+  // two tiles for the dC panel (register-bound to one workgroup per CU
+  // anyway); one for the dB panel, which then fits two workgroups per CU
+  constexpr bool DBUF = sizeof(T) == 2 && PNL == 0;
+  using DC = DmaTile<CRB>;
+  using DS = DmaTile<SRB>;
+  __shared__ Sm sm;
+  __shared__ __attribute__((aligned(16))) char bufA[CSB + STB];
+  __shared__ __attribute__((aligned(16))) char bufB[DBUF ? CSB + STB : 16];
+  constexpr int NT = N / 16;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
   const int Q = a.chunk, NRB = Q / kRB, H = a.H, G = a.G, hpg = H / G;
   const int64_t L = a.L;
@@ -138,14 +144,27 @@ __global__ __launch_bounds__(kThreads) void k_bwd_panel(BwdArgs a) {
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) zero4(oacc[nt]);
 
-  u32x4 pf[SS::NV > SC::NV ? SS::NV : SC::NV];
+  // one head's column slabs kb..ke and carried state -> a tile
+  auto issue_head = [&](int h, char *tile) __attribute__((always_inline)) {
+    for (int k = kb; k <= ke; ++k)
+      DC::load(tile + k * kRB * CRB, rCol, (uint32_t)((t0 + k * kRB) * H + h) * kP * ES, xrs, kRB);
+    const int64_t soff = (int64_t)b * a.st_bstride + (int64_t)c * a.st_cstride + (int64_t)h * kP * N;
+    DS::load(tile + CSB, make_buf(stsrc + soff, (uint32_t)(kP * N * ES)), 0u, (uint32_t)SRB, kP);
+  };
+  auto issue_val = [&](int k, char *tile) __attribute__((always_inline)) {
+    DS::load(tile, rVal, (uint32_t)((t0 + k * kRB) * G + g) * N * ES, vrs, kRB);
+  };
+  // row-source fragments of this lane's row (k = head-dim index)
+  auto ld_rows = [&](int h, Frag<T> (&r)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      frag_bload(r[ks], rRow, (uint32_t)((t0 + rrow) * H + h) * kP * ES + (32 * ks + 8 * g4) * ES);
+  };
 
-  // dC panel: cbt[k][u][i] = C_row . B_col in the Gram tiles' layout
-  f32x4 cbt[4][4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k)
-#pragma unroll
-    for (int u = 0; u < 4; ++u) zero4(cbt[k][u]);
+  // dC panel: cbt[k][u][i] = C_row . B_col in the Gram tiles' layout, kept
+  // in the compute dtype
+  using CBV = typename std::conditional<sizeof(T) == 2, bf16x4, f32x4>::type;
+  CBV cbt[4][4];
   if constexpr (PNL == 0) {
     const bufres rC = make_buf(reinterpret_cast<const T *>(a.C[d]) + (int64_t)b * L * G * N,
                                (uint32_t)(L * G * N * ES));
@@ -156,42 +175,80 @@ __global__ __launch_bounds__(kThreads) void k_bwd_panel(BwdArgs a) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       if (k < kb || k > ke) continue;
-      SS::prefetch(pf, rVal, (uint32_t)((t0 + k * kRB) * G + g) * N * ES, vrs);
       __syncthreads();
-      SS::commit(&sm.u.Vs[0][0], pf);
+      issue_val(k, bufA);
+      wait_vmem();
       __syncthreads();
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < 4; ++u) {
+        f32x4 t;
+        zero4(t);
 #pragma unroll
         for (int ks = 0; ks < N / 32; ++ks) {
           Frag<T> bf;
-          frag_ld8(bf, &sm.u.Vs[16 * u + r16][32 * ks + 8 * g4]);
-          mma(cbt[k][u], bf, cfr[ks]);
+          frag_ld8_swz<SRB>(bf, bufA, 16 * u + r16, 32 * ks + 8 * g4);
+          mma(t, bf, cfr[ks]);
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cbt[k][u][i] = from_f<T>(t[i]);
+      }
     }
+    __syncthreads();
   }
 
-  for (int hi = 0; hi < hpg; ++hi) {
-    const int h = g * hpg + hi, buf = hi & 1;
-    const T *dth = reinterpret_cast<const T *>(a.dt[d]) + ((int64_t)b * L + t0) * H + h;
-    if (w == 0)
-      chunk_decay_scan<T>(dth, H, qlen, Q, a.A[d][h] * kLog2e, d == 1, sm.lam[buf], sm.dtv[buf]);
-    if (PNL == 0 && w == 1) chunk_decay_scan<T>(dth, H, qlen, Q, 1.0f, d == 1, sm.cdt[buf], sm.dtv[buf]);
-    float dai = 0.0f;
-    // row-source fragments of this lane's row (k = head-dim index)
-    Frag<T> rf[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-      frag_bload(rf[ks], rRow, (uint32_t)((t0 + rrow) * H + h) * kP * ES + (32 * ks + 8 * g4) * ES);
-    const float *lam = sm.lam[buf], *dtv = sm.dtv[buf];
+  // dt of one batch row; tokens past L read as zero
+  const bufres rDt = make_buf(reinterpret_cast<const T *>(a.dt[d]) + (int64_t)b * L * H,
+                              (uint32_t)(L * H * ES));
+  auto ld_dt = [&](int h, uint32_t (&raw)[4]) __attribute__((always_inline)) {
+    chunk_dt_bload<T>(rDt, (uint32_t)(t0 * H + h) * ES, (uint32_t)(H * ES), Q, raw);
+  };
+  const int64_t dai_base = (((int64_t)d * a.Z + b) * a.nchunks + c) * NRB + j;
+  {
+    uint32_t r0[4];
+    float d0[4];
+    ld_dt(g * hpg, r0);
+    chunk_dt_decode<T>(r0, Q, d0);
+    if (w == 0) chunk_decay_scan_vals(d0, Q, a.A[d][g * hpg] * kLog2e, d == 1, sm.lam[0], sm.dtv[0]);
+    if (PNL == 0 && w == 1) chunk_decay_scan_vals(d0, Q, 1.0f, d == 1, sm.cdt[0], sm.dtv[0]);
+  }
+  Frag<T> rf[2];
+  ld_rows(g * hpg, rf);
+  issue_head(g * hpg, bufA);
 
+  auto do_head = [&](int hi, char *cur, char *nxt) __attribute__((always_inline)) {
+    const int h = g * hpg + hi, lb = hi & 1;
+    wait_vmem();
+    __syncthreads();  // head hi's tiles, decay sums and row fragments are ready
+    if (PNL == 0 && hi > 0 && tid == 0)
+      a.dAintra[dai_base * H + h - 1] = (sm.red[lb ^ 1][0] + sm.red[lb ^ 1][1]) +
+                                        (sm.red[lb ^ 1][2] + sm.red[lb ^ 1][3]);
+    // per-row values are read before the next head's copies are issued (an
+    // LDS read the compiler cannot tell apart from their destination would
+    // otherwise wait for them)
+    const float *lam = sm.lam[lb], *dtv = sm.dtv[lb];
+    float dai = 0.0f;
+    const float lrow = lam[rrow], drow = dtv[rrow];
+    const float crow = PNL == 0 ? sm.cdt[lb][rrow] : 0.0f;
+    float fr[4];
+    {
+      const float lend = d == 0 ? lam[Q - 1] : lam[0];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = j * kRB + 16 * w + 4 * g4 + i;
+        fr[i] = PNL == 0 ? exp2_fast(lam[r]) : dtv[r] * exp2_fast(fminf(lend - lam[r], 0.0f));
+      }
+    }
+    Frag<T> rfn[2];
+    uint32_t dtn[4];
+    if (DBUF && hi + 1 < hpg) {
+      issue_head(h + 1, nxt);
+      ld_rows(h + 1, rfn);
+      ld_dt(h + 1, dtn);
+    }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       if (k < kb || k > ke) continue;
-      SC::prefetch(pf, rCol, (uint32_t)((t0 + k * kRB) * H + h) * kP * ES, xrs);
-      __syncthreads();
-      SC::commit(&sm.u.s.Cs[0][0], pf);
-      __syncthreads();
+      const char *cs = cur + k * kRB * CRB;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         f32x4 dg;
@@ -199,11 +256,10 @@ __global__ __launch_bounds__(kThreads) void k_bwd_panel(BwdArgs a) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           Frag<T> cf;
-          frag_ld8(cf, &sm.u.s.Cs[16 * u + r16][32 * ks + 8 * g4]);
+          frag_ld8_swz<CRB>(cf, cs, 16 * u + r16, 32 * ks + 8 * g4);
           mma(dg, cf, rf[ks]);
         }
         // dg[i] = ColSrc[col] . RowSrc[row], col = 64k + 16u + 4 g4 + i
-        const float lrow = lam[rrow], drow = dtv[rrow];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int col = k * kRB + 16 * u + 4 * g4 + i;
@@ -214,33 +270,17 @@ __global__ __launch_bounds__(kThreads) void k_bwd_panel(BwdArgs a) {
           const float dtf = PNL == 0 ? dtv[col] : drow;
           const float wv = ok ? dg[i] * (exp2_fast(fminf(ex, 0.0f)) * dtf) : 0.0f;
           wsum[k][u][i] += wv;
-          if (PNL == 0) dai += wv * cbt[k][u][i] * (sm.cdt[buf][rrow] - sm.cdt[buf][col]);
+          if (PNL == 0) dai += wv * (float)cbt[k][u][i] * (crow - sm.cdt[lb][col]);
         }
       }
     }
     if (PNL == 0) {
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) dai += __shfl_xor(dai, o, 64);
-      if (lane == 0) sm.red[buf][w] = dai;
+      if (lane == 0) sm.red[lb][w] = dai;
     }
 
     // carried-state term: rows r = 64 j + 16 w + 4 g4 + i, columns n
-    const int64_t soff = (int64_t)b * a.st_bstride + (int64_t)c * a.st_cstride + (int64_t)h * kP * N;
-    const bufres rSt = make_buf(stsrc + soff, (uint32_t)(kP * N * ES));
-    SS::prefetch(pf, rSt, 0u, (uint32_t)(N * ES));
-    __syncthreads();
-    SS::commit(&sm.u.s.St[0][0], pf);
-    __syncthreads();
-    if (PNL == 0 && tid == 0)
-      a.dAintra[((((int64_t)d * a.Z + b) * a.nchunks + c) * NRB + j) * H + h] =
-          (sm.red[buf][0] + sm.red[buf][1]) + (sm.red[buf][2] + sm.red[buf][3]);
-    float fr[4];
-    const float lend = d == 0 ? lam[Q - 1] : lam[0];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = j * kRB + 16 * w + 4 * g4 + i;
-      fr[i] = PNL == 0 ? exp2_fast(lam[r]) : dtv[r] * exp2_fast(fminf(lend - lam[r], 0.0f));
-    }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       f32x4 t2;
@@ -248,21 +288,50 @@ __global__ __launch_bounds__(kThreads) void k_bwd_panel(BwdArgs a) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         Frag<T> sf;
-        frag_rows(sf, &sm.u.s.St[0][0], Sm::SP, 32 * ks + 8 * g4, 32 * ks + 8 * g4 + 4, 16 * nt);
+        frag_rows_swz<SRB>(sf, cur + CSB, 32 * ks + 8 * g4, 32 * ks + 8 * g4 + 4, 16 * nt);
         mma(t2, rf[ks], sf);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) oacc[nt][i] += fr[i] * t2[i];
     }
+
+    if (hi + 1 < hpg) {
+      if (!DBUF) {
+        // single tile: the next head's copies wait for this head's reads
+        __syncthreads();
+        issue_head(h + 1, cur);
+        ld_rows(h + 1, rfn);
+        ld_dt(h + 1, dtn);
+      }
+      // decay sums of the next head into the other buffer.  The empty asm
+      // keeps the decode of the raw dt bits (and so the wait for their loads,
+      // issued behind the next head's copies) from being hoisted to the top
+      // of the head.
+#pragma unroll
+      for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(dtn[i]) : : "memory");
+      float dn[4];
+      chunk_dt_decode<T>(dtn, Q, dn);
+      if (w == 0) chunk_decay_scan_vals(dn, Q, a.A[d][h + 1] * kLog2e, d == 1, sm.lam[lb ^ 1], sm.dtv[lb ^ 1]);
+      if (PNL == 0 && w == 1) chunk_decay_scan_vals(dn, Q, 1.0f, d == 1, sm.cdt[lb ^ 1], sm.dtv[lb ^ 1]);
+      rf[0] = rfn[0];
+      rf[1] = rfn[1];
+    }
+  };
+  for (int hi = 0; hi < hpg; hi += 2) {
+    do_head(hi, bufA, bufB);
+    if (hi + 1 < hpg) do_head(hi + 1, DBUF ? bufB : bufA, bufA);
   }
+  __syncthreads();
+  if (PNL == 0 && tid == 0)
+    a.dAintra[dai_base * H + g * hpg + hpg - 1] = (sm.red[(hpg - 1) & 1][0] + sm.red[(hpg - 1) & 1][1]) +
+                                                  (sm.red[(hpg - 1) & 1][2] + sm.red[(hpg - 1) & 1][3]);
 
   // summed weights x value rows, one 64-row slab per column block
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     if (k < kb || k > ke) continue;
-    SS::prefetch(pf, rVal, (uint32_t)((t0 + k * kRB) * G + g) * N * ES, vrs);
-    __syncthreads();
-    SS::commit(&sm.u.Vs[0][0], pf);
+    issue_val(k, bufA);
+    wait_vmem();
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -277,10 +346,11 @@ __global__ __launch_bounds__(kThreads) void k_bwd_panel(BwdArgs a) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         Frag<T> vf;
-        frag_rows(vf, &sm.u.Vs[0][0], Sm::SP, 32 * q + 4 * g4, 32 * q + 16 + 4 * g4, 16 * nt);
+        frag_rows_swz<SRB>(vf, bufA, 32 * q + 4 * g4, 32 * q + 16 + 4 * g4, 16 * nt);
         mma(oacc[nt], mf, vf);
       }
     }
+    __syncthreads();
   }
 
   float *out = PNL == 0 ? a.dC[d] : a.dB[d];

@@ -475,6 +475,78 @@ template <typename T, typename S, int N> struct SlabState {
   }
 };
 
+// ------------------------------------------------- direct buffer -> LDS slabs
+//
+// gfx950 buffer loads can write LDS directly: each lane's 16 bytes land at
+// (wave-uniform base) + 16 * lane, and lanes outside the buffer resource
+// write zeros.  A slab of 64 rows of RB bytes is copied as 1 KB pieces into a
+// dense tile whose 16-byte chunks are XOR-swizzled by row (chunk c of row y
+// is stored at chunk c ^ swz(y)), so that the fragment reads below hit
+// distinct LDS banks without padding.  No registers hold the data in flight;
+// the loads complete when every wave has waited for its vector-memory count
+// and the workgroup has passed a barrier.
+typedef __attribute__((address_space(3))) void *lds_vptr;
+
+template <int RB> struct DmaTile {
+  static constexpr int CPR = RB / 16;    // 16-byte chunks per row
+  static constexpr int RPP = 1024 / RB;  // rows per 1 KB piece
+  __device__ static __forceinline__ int swz(int y) {
+    return RB == 128 ? ((y >> 1) & 7) : (RB == 256 ? 2 * (y & 3) : 0);
+  }
+  // byte offset of logical (row y, byte x) in the tile (x within a chunk
+  // keeps its low 4 bits)
+  __device__ static __forceinline__ int at(int y, int x) {
+    return y * RB + ((((x >> 4) ^ swz(y)) << 4) | (x & 15));
+  }
+  // copy rows [0, nrows) (nrows a multiple of RPP) of the slab starting at
+  // byte off0 of r, rows rs bytes apart
+  __device__ static __forceinline__ void load(char *tile, bufres r, uint32_t off0, uint32_t rs,
+                                              int nrows) {
+    const int wv = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int np = nrows / RPP;
+    for (int p = wv; p < np; p += kThreads / 64) {
+      const int y = p * RPP + l / CPR, c = l % CPR;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_vptr)(tile + p * 1024), 16,
+                                               off0 + y * rs + 16 * (c ^ swz(y)), 0, 0, 0);
+    }
+  }
+};
+
+// natural-mapping fragment (8 consecutive elements at row y, column x) from
+// a swizzled tile
+template <int RB>
+__device__ __forceinline__ void frag_ld8_swz(Frag<bf16> &f, const char *tile, int y, int x) {
+  f.v = *reinterpret_cast<const bf16x8 *>(tile + DmaTile<RB>::at(y, 2 * x));
+}
+template <int RB>
+__device__ __forceinline__ void frag_ld8_swz(Frag<float> &f, const char *tile, int y, int x) {
+  const f32x4 a = *reinterpret_cast<const f32x4 *>(tile + DmaTile<RB>::at(y, 4 * x));
+  const f32x4 b = *reinterpret_cast<const f32x4 *>(tile + DmaTile<RB>::at(y, 4 * x + 16));
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f.v[e] = a[e];
+    f.v[4 + e] = b[e];
+  }
+}
+// k-along-rows fragment (frag_rows semantics) from a swizzled tile
+template <int RB>
+__device__ __forceinline__ void frag_rows_swz(Frag<bf16> &f, const char *tile, int r0, int r1, int c0) {
+  const int i = threadIdx.x & 15;
+  const int y = i >> 2, x = 2 * (c0 + 4 * (i & 3));
+  const bf16x4 a = lds_tr4(reinterpret_cast<const bf16 *>(tile + DmaTile<RB>::at(r0 + y, x)));
+  const bf16x4 b = lds_tr4(reinterpret_cast<const bf16 *>(tile + DmaTile<RB>::at(r1 + y, x)));
+  f.v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+template <int RB>
+__device__ __forceinline__ void frag_rows_swz(Frag<float> &f, const char *tile, int r0, int r1, int c0) {
+  const int i = threadIdx.x & 15;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f.v[e] = *reinterpret_cast<const float *>(tile + DmaTile<RB>::at(r0 + e, 4 * (c0 + i)));
+    f.v[4 + e] = *reinterpret_cast<const float *>(tile + DmaTile<RB>::at(r1 + e, 4 * (c0 + i)));
+  }
+}
+
 // ------------------------------------------------------- XCD-aware order
 //
 // MI355X dispatches consecutive workgroup ids round-robin over its 8 XCDs,
@@ -515,23 +587,64 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// Log2-decay cumulative sums of one chunk for one (direction, head), run by
-// one wavefront.  a_s = dt_s * A * log2(e) for the chunk's Q tokens (tokens
-// at or beyond qlen count as dt = 0).  Forward: lam[s] = sum_{k<=s} a_k.
-// Reverse: lam[s] = sum_{k>=s} a_k.  With `exclusive` the sums leave out
-// a_s itself (sum_{k<s}, sum_{k>s}).  dtv[s] receives dt_s.  Returns the
-// largest |a_s| of the chunk (in every lane).
+// dt of one chunk for one head, in the lane order chunk_decay_scan_vals
+// expects: lane l holds tokens l K .. l K + K - 1 (K = Q / 64) in d[0..K-1];
+// tokens at or beyond qlen read as 0.  Split from the scan so the loads can
+// be issued well before the values are needed.
 template <typename T>
-__device__ __forceinline__ float chunk_decay_scan(const T *dt, int64_t stride, int qlen, int Q,
-                                                  float A2, bool reverse, float *lam,
-                                                  float *dtv, bool exclusive = false) {
+__device__ __forceinline__ void chunk_dt_load(const T *dt, int64_t stride, int qlen, int Q,
+                                              float (&d)[4]) {
   const int lane = threadIdx.x & 63;
-  const int K = Q / 64;  // 1, 2 or 4 tokens per lane
-  float a[4], d[4], amax = 0.0f;
+  const int K = Q / 64;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int s = lane * K + i;
     d[i] = (i < K && s < qlen) ? to_f(dt[(int64_t)s * stride]) : 0.0f;
+  }
+}
+
+// The same values through a buffer resource, with no branch: tokens past
+// the resource read as zero, so every load is issued unconditionally.  The
+// raw bits are kept as loaded (any arithmetic on them would make the
+// compiler wait for the load at once); chunk_dt_decode turns them into dt.
+// off0: byte offset of (first token of the chunk, head); rs: bytes between
+// tokens.
+template <typename T>
+__device__ __forceinline__ void chunk_dt_bload(bufres r, uint32_t off0, uint32_t rs, int Q,
+                                               uint32_t (&raw)[4]) {
+  const int lane = threadIdx.x & 63;
+  const int K = Q / 64;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t off = off0 + (uint32_t)(lane * K + i) * rs;
+    if constexpr (sizeof(T) == 2) raw[i] = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+    else raw[i] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  }
+}
+template <typename T>
+__device__ __forceinline__ void chunk_dt_decode(const uint32_t (&raw)[4], int Q, float (&d)[4]) {
+  const int K = Q / 64;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float f = __builtin_bit_cast(float, sizeof(T) == 2 ? raw[i] << 16 : raw[i]);
+    d[i] = i < K ? f : 0.0f;
+  }
+}
+
+// Log2-decay cumulative sums of one chunk for one (direction, head), run by
+// one wavefront from dt loaded by chunk_dt_load.  a_s = dt_s * A2 (A2 = A
+// log2(e), or 1 for plain cumulative dt).  Forward: lam[s] = sum_{k<=s} a_k.
+// Reverse: lam[s] = sum_{k>=s} a_k.  With `exclusive` the sums leave out
+// a_s itself (sum_{k<s}, sum_{k>s}).  dtv[s] receives dt_s.  Returns the
+// largest |a_s| of the chunk (in every lane).
+__device__ __forceinline__ float chunk_decay_scan_vals(const float (&d)[4], int Q, float A2,
+                                                       bool reverse, float *lam, float *dtv,
+                                                       bool exclusive = false) {
+  const int lane = threadIdx.x & 63;
+  const int K = Q / 64;  // 1, 2 or 4 tokens per lane
+  float a[4], amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
     a[i] = d[i] * A2;
     amax = fmaxf(amax, fabsf(a[i]));
   }
@@ -575,6 +688,16 @@ __device__ __forceinline__ float chunk_decay_scan(const T *dt, int64_t stride, i
       }
   }
   return amax;
+}
+
+// chunk_dt_load followed by chunk_decay_scan_vals.
+template <typename T>
+__device__ __forceinline__ float chunk_decay_scan(const T *dt, int64_t stride, int qlen, int Q,
+                                                  float A2, bool reverse, float *lam,
+                                                  float *dtv, bool exclusive = false) {
+  float d[4];
+  chunk_dt_load(dt, stride, qlen, Q, d);
+  return chunk_decay_scan_vals(d, Q, A2, reverse, lam, dtv, exclusive);
 }
 
 }  // namespace bissd

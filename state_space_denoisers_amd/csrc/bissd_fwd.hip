@@ -387,7 +387,9 @@ template <typename T, int N, int HT, bool SF32> struct K3Pf {
 // |A| would amplify.  MODE 2 adds the term back where it is a plain part of
 // the result: dy_t (B_t.C_t) into G_t B_t for dx and x.(G_t B_t).
 template <typename T, int N, int HT, bool SF32, int MODE>
-__global__ __launch_bounds__(kThreads) void k3_chunk_out(ScanArgs a) {
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu((MODE != 0 && sizeof(T) == 2) ? 2 : 1)))
+void k3_chunk_out(ScanArgs a) {
   using Sm = K3Lds<T, N, HT>;
   using PF = K3Pf<T, N, HT, SF32>;
   using SB = typename PF::SB;
@@ -515,6 +517,10 @@ __global__ __launch_bounds__(kThreads) void k3_chunk_out(ScanArgs a) {
   auto run_direction = [&](auto dc) __attribute__((always_inline)) {
     constexpr int d = decltype(dc)::value;
     const int kb = d == 0 ? 0 : j, ke = d == 0 ? j : klast;
+    // MODE 0 prefetches the reverse's first slab during the forward's last
+    // stage; the backward modes finish each slot with an epilogue first and
+    // issue it here, so the prefetch registers are not live across it
+    if (MODE != 0 && d == 1) prefetch_sblock(1, j);
     Frag<T> cfd[NK];
     load_c(d, cfd);
     // per-head row factor 2^(lam_t - m) of this lane's Gram row t = 16w + r16,
@@ -534,7 +540,7 @@ __global__ __launch_bounds__(kThreads) void k3_chunk_out(ScanArgs a) {
       __syncthreads();
       if (k < ke) prefetch_sblock(d, k + 1);
       else if (d == 0 ? has_in0 : has_in1) prefetch_state(d, 0);
-      else if (d == 0) prefetch_sblock(1, j);
+      else if (d == 0 && MODE == 0) prefetch_sblock(1, j);
 
       const bool diag = (k == j);
       int ulo = 0, uhi = 3;
@@ -643,7 +649,7 @@ __global__ __launch_bounds__(kThreads) void k3_chunk_out(ScanArgs a) {
         for (int q = 0; q < IH; ++q) SS::commit(&sm.u.Sst[q][0][0], pf + q * SS::NV, 1.0f);
         __syncthreads();
         if (ih + 1 < HT / IH) prefetch_state(d, ih + 1);
-        else if (d == 0) prefetch_sblock(1, j);
+        else if (d == 0 && MODE == 0) prefetch_sblock(1, j);
 #pragma unroll
         for (int q = 0; q < IH; ++q) {
           const int hh = ih * IH + q;
