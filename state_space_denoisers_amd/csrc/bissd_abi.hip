@@ -46,10 +46,11 @@ int check_shape(const bissd_shape_t *s, int op) {
   return BISSD_OK;
 }
 
-// Workspace: fp32 chunk-local states, the carry-in states in the compute
-// dtype (not for the block update, which reads its fp32 start state
-// directly) and the chunk log2-decays.  The backward pass adds a second fp32
-// state buffer (A-tangent chunk states, then adjoint chunk states), the
+// Workspace: chunk-local states and the carry-in states, both in the compute
+// dtype (no carry-in buffer for the block update, which reads its fp32 start
+// state directly), and the chunk log2-decays.  The backward pass adds a
+// second chunk-state buffer (A-tangent chunk states, then adjoint chunk
+// states), the
 // A-tangent and adjoint carries (compute dtype), chunk dt sums, the
 // per-token dy.y_d and x.(G_t B_t) values (fp32 [2][Z][L][H]) and the
 // partial sums of the reductions.
@@ -73,13 +74,13 @@ WsLayout ws_layout(const bissd_shape_t *s, int op) {
     o += align256(bytes);
     return at;
   };
-  w.states = take(nst * 4);
+  w.states = take(nst * esz);
   if (op != BISSD_OP_BLOCK) w.sin_t = take(nst * esz);
   w.cdecay = take(cd);
   if (op == BISSD_OP_BACKWARD) {
     const size_t tok = (size_t)(2 * s->batch * s->seqlen * s->nheads) * 4;
     const size_t rb = (size_t)(s->batch * nc * (s->chunk / 64) * s->nheads) * 4;
-    w.tstates = take(nst * 4);
+    w.tstates = take(nst * esz);
     w.sa_t = take(nst * esz);
     w.gin_t = take(nst * esz);
     w.dtsum = take(cd);
@@ -222,7 +223,7 @@ static int forward_impl(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, 
   hipStream_t st = (hipStream_t)stream;
   ScanArgs a = base_args(s, x, fwd, rev, D);
   char *ws = (char *)workspace;
-  a.states = (float *)(ws + wl.states);
+  a.states = (void *)(ws + wl.states);
   a.cdecay = (float *)(ws + wl.cdecay);
   a.nchunks = (int)ceil_div(s->seqlen, s->chunk);
   a.y = y;
@@ -291,7 +292,7 @@ int bissd_block_update(const bissd_shape_t *s, const float *state_in, const void
   hipStream_t st = (hipStream_t)stream;
   ScanArgs a = base_args(s, x_blk, fwd, rev, D);
   char *ws = (char *)workspace;
-  a.states = (float *)(ws + wl.states);
+  a.states = (void *)(ws + wl.states);
   a.cdecay = (float *)(ws + wl.cdecay);
   a.nchunks = 1;
   a.y = y_blk;
@@ -361,7 +362,7 @@ int bissd_backward(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, bissd
 
   // primal chunk states and carry-ins
   ScanArgs a = base_args(s, x, fwd, rev, D);
-  a.states = (float *)(ws + wl.states);
+  a.states = (void *)(ws + wl.states);
   a.cdecay = (float *)(ws + wl.cdecay);
   a.nchunks = nc;
   a.dir0 = 0;
@@ -379,11 +380,11 @@ int bissd_backward(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, bissd
   // A-tangent chunk states (dt-sum weighted), chunk dt sums, and the
   // A-tangent carry-ins S^A_in
   ScanArgs ta = a;
-  ta.states = (float *)(ws + wl.tstates);
+  ta.states = (void *)(ws + wl.tstates);
   ta.out1 = (float *)(ws + wl.dtsum);
   if (e == hipSuccess) e = bissd::launch_scan_phase(ta, bissd::PHASE_TAN_STATE, st);
   ScanArgs tp = a;
-  tp.states2 = (const float *)(ws + wl.tstates);
+  tp.states2 = (const void *)(ws + wl.tstates);
   tp.dtsum = (const float *)(ws + wl.dtsum);
   tp.sin_t = ws + wl.sa_t;
   if (e == hipSuccess) e = bissd::launch_scan_phase(tp, bissd::PHASE_TAN_PASS, st);
@@ -396,7 +397,7 @@ int bissd_backward(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, bissd
   g.B[0] = fwd.C;
   g.B[1] = rev.C;
   g.init_state = nullptr;
-  g.states = (float *)(ws + wl.tstates);
+  g.states = (void *)(ws + wl.tstates);
   for (int d = 0; d < 2; ++d) g.sin[d] = ws + wl.sa_t + d * dirst;
   g.out0 = (float *)(ws + wl.dAx1);
   if (e == hipSuccess) e = bissd::launch_scan_phase(g, bissd::PHASE_ADJ_STATE, st);

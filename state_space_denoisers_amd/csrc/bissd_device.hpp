@@ -448,6 +448,16 @@ template <typename T, typename S, int N> struct SlabState {
       pf[m] = gload16(g + (int64_t)vi * EPV);
     }
   }
+  // the prefetched bytes as they are (S == T)
+  __device__ static __forceinline__ void commit_raw(T *lds, const u32x4 *pf) {
+    static_assert(sizeof(S) == sizeof(T), "raw commit needs the state in the compute dtype");
+#pragma unroll
+    for (int m = 0; m < NV; ++m) {
+      const int vi = threadIdx.x + m * kThreads;
+      const int r = vi / VPR, c = vi % VPR;
+      *reinterpret_cast<u32x4 *>(lds + r * PT + c * EPV) = pf[m];
+    }
+  }
   __device__ static __forceinline__ void commit(T *lds, const u32x4 *pf, float sc) {
 #pragma unroll
     for (int m = 0; m < NV; ++m) {

@@ -58,7 +58,8 @@ template <typename T, int N, int HT> struct K1Lds {
 // MODEs 1-3 leave the chunk decays as MODE 0 wrote them.  64-token slabs are fetched into registers one slab
 // ahead of the matrix-core work and stored row-major; both operands are read
 // with k (the token) running down the rows.  Output
-// states[d][b][c][h][p][n] (fp32), cdecay[d][b][c][h].  Wave w owns state
+// states[d][b][c][h][p][n] (compute dtype, rounded once from the fp32
+// accumulators), cdecay[d][b][c][h].  Wave w owns state
 // columns n in [w N/4, (w+1) N/4).
 template <typename T, int N, int HT, int MODE>
 __global__ __launch_bounds__(kThreads) void k1_chunk_state(ScanArgs a) {
@@ -168,7 +169,7 @@ __global__ __launch_bounds__(kThreads) void k1_chunk_state(ScanArgs a) {
   }
 
   if constexpr (MODE <= 2) {
-    float *out = a.states + chi * (int64_t)(kP * N);
+    T *out = reinterpret_cast<T *>(a.states) + chi * (int64_t)(kP * N);
 #pragma unroll
     for (int hh = 0; hh < HT; ++hh)
 #pragma unroll
@@ -178,7 +179,7 @@ __global__ __launch_bounds__(kThreads) void k1_chunk_state(ScanArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             out[(int64_t)hh * kP * N + (16 * pt + 4 * g4 + i) * N + nb + 16 * nt + r16] =
-                acc[hh][pt][nt][i];
+                from_f<T>(acc[hh][pt][nt][i]);
   }
   if constexpr (MODE == 1 || MODE == 3) {
     // Frobenius product with the given state of the same (direction, batch,
@@ -207,6 +208,13 @@ __global__ __launch_bounds__(kThreads) void k1_chunk_state(ScanArgs a) {
 
 // =================================================================== K2
 
+// four consecutive elements (8- or 16-byte aligned) widened to fp32
+__device__ __forceinline__ f32x4 load4f(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+__device__ __forceinline__ f32x4 load4f(const bf16 *p) {
+  const bf16x4 v = *reinterpret_cast<const bf16x4 *>(p);
+  return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+
 // Four state elements per thread.  Forward: S_in(0) = init (or 0),
 // S_in(c+1) = 2^cdecay(c) S_in(c) + S_loc(c); the reverse runs c downwards
 // from zero.  Each chunk's carry-in is written, rounded once to T, to the
@@ -227,7 +235,7 @@ __global__ __launch_bounds__(kThreads) void k2_state_pass(ScanArgs a, int PN, in
   const int nc = a.nchunks, H = a.H;
   const int64_t cs = (int64_t)H * PN;
   const int64_t base = (((int64_t)d * a.Z + b) * nc * H + h) * (int64_t)PN + e;
-  const float *src = a.states + base;
+  const T *src = reinterpret_cast<const T *>(a.states) + base;
   T *dst = a.sin_t ? reinterpret_cast<T *>(a.sin_t) + base : nullptr;
   const float *dec = a.cdecay + ((int64_t)d * a.Z + b) * nc * H + h;
   f32x4 S = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -240,7 +248,7 @@ __global__ __launch_bounds__(kThreads) void k2_state_pass(ScanArgs a, int PN, in
   const bool rpart = flip && a.out0;
   const int nwv = PN / 256, wv = (blockIdx.x * kThreads + threadIdx.x) >> 6;
   for (int n = 0; n < nc; ++n, c += step) {
-    const f32x4 loc = *reinterpret_cast<const f32x4 *>(src + c * cs);
+    const f32x4 loc = load4f(src + c * cs);
     const float g = exp2_fast(dec[(int64_t)c * H]);
     if (rpart) {
       // primal state after chunk c = primal carry-in of chunk c + 1 (forward)
@@ -288,7 +296,8 @@ __global__ __launch_bounds__(kThreads) void k2_tangent_pass(ScanArgs a, int PN) 
   const int nc = a.nchunks, H = a.H;
   const int64_t cs = (int64_t)H * PN;
   const int64_t base = (((int64_t)d * a.Z + b) * nc * H + h) * (int64_t)PN + e;
-  const float *sl = a.states + base, *tl = a.states2 + base;
+  const T *sl = reinterpret_cast<const T *>(a.states) + base;
+  const T *tl = reinterpret_cast<const T *>(a.states2) + base;
   T *dst = reinterpret_cast<T *>(a.sin_t) + base;
   const float *dec = a.cdecay + ((int64_t)d * a.Z + b) * nc * H + h;
   const float *tsum = a.dtsum + ((int64_t)d * a.Z + b) * nc * H + h;
@@ -298,8 +307,8 @@ __global__ __launch_bounds__(kThreads) void k2_tangent_pass(ScanArgs a, int PN) 
   const int step = d == 0 ? 1 : -1;
   int c = d == 0 ? 0 : nc - 1;
   for (int n = 0; n < nc; ++n, c += step) {
-    const f32x4 loc = *reinterpret_cast<const f32x4 *>(sl + c * cs);
-    const f32x4 tloc = *reinterpret_cast<const f32x4 *>(tl + c * cs);
+    const f32x4 loc = load4f(sl + c * cs);
+    const f32x4 tloc = load4f(tl + c * cs);
     const float g = exp2_fast(dec[(int64_t)c * H]), ts = tsum[(int64_t)c * H];
     if constexpr (sizeof(T) == 2) {
       bf16x4 o;
@@ -646,7 +655,10 @@ void k3_chunk_out(ScanArgs a) {
       for (int ih = 0; ih < HT / IH; ++ih) {
         __syncthreads();
 #pragma unroll
-        for (int q = 0; q < IH; ++q) SS::commit(&sm.u.Sst[q][0][0], pf + q * SS::NV, 1.0f);
+        for (int q = 0; q < IH; ++q) {
+          if constexpr (SF32) SS::commit(&sm.u.Sst[q][0][0], pf + q * SS::NV, 1.0f);
+          else SS::commit_raw(&sm.u.Sst[q][0][0], pf + q * SS::NV);
+        }
         __syncthreads();
         if (ih + 1 < HT / IH) prefetch_state(d, ih + 1);
         else if (d == 0 && MODE == 0) prefetch_sblock(1, j);

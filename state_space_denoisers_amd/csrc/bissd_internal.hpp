@@ -15,7 +15,7 @@ struct ScanArgs {
   const void *C[2];
   const float *D;
   void *y;
-  float *states;  // [ndir][Z][nchunks][H][P][N] chunk states (workspace)
+  void *states;   // [ndir][Z][nchunks][H][P][N] chunk-local states, compute dtype (workspace)
   float *cdecay;  // [ndir][Z][nchunks][H] chunk total log2-decay (workspace)
   const void *sin[2];  // carry-in state of each chunk, per direction (nullptr = none)
   int64_t sin_bstride[2], sin_cstride[2];  // element strides of sin per batch row / chunk
@@ -35,7 +35,7 @@ struct ScanArgs {
   float *out1;      // PHASE_DX: dx [Z][L][H][P]; PHASE_TAN_STATE: chunk dt sums [2][Z][nchunks][H]
   float *out2;      // PHASE_DX: partial sums of dy.x per (b, chunk, row-block, head)
   float *out3;      // PHASE_DX: x.(G_t B_t) without the t' = t term, [2][Z][L][H]
-  const float *states2;  // PHASE_TAN_PASS: tangent chunk states
+  const void *states2;   // PHASE_TAN_PASS: tangent chunk states, compute dtype
   const float *dtsum;    // PHASE_TAN_PASS: chunk dt sums
   int slot_dir[2];  // direction under which each output-kernel slot stores out0
 };
