@@ -208,11 +208,27 @@ __global__ __launch_bounds__(kThreads) void k1_chunk_state(ScanArgs a) {
 
 // =================================================================== K2
 
-// four consecutive elements (8- or 16-byte aligned) widened to fp32
-__device__ __forceinline__ f32x4 load4f(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
-__device__ __forceinline__ f32x4 load4f(const bf16 *p) {
-  const bf16x4 v = *reinterpret_cast<const bf16x4 *>(p);
-  return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+// Four consecutive elements (8- or 16-byte aligned) loaded as raw bits and
+// widened to fp32 only when used.  Any arithmetic on a loaded value makes the
+// compiler wait for that load where it happens, and since loads complete in
+// order that wait also covers every load issued before it; the empty asm in
+// widen4 pins the widening at the point of use.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+template <typename T> struct Raw4 {
+  using type = typename std::conditional<sizeof(T) == 2, u32x2, f32x4>::type;
+};
+template <typename T>
+__device__ __forceinline__ typename Raw4<T>::type load4raw(const T *p) {
+  return *reinterpret_cast<const typename Raw4<T>::type *>(p);
+}
+__device__ __forceinline__ f32x4 widen4(u32x2 r) {
+  asm volatile("" : "+v"(r));
+  return f32x4{__builtin_bit_cast(float, r[0] << 16), __builtin_bit_cast(float, r[0] & 0xffff0000u),
+               __builtin_bit_cast(float, r[1] << 16), __builtin_bit_cast(float, r[1] & 0xffff0000u)};
+}
+__device__ __forceinline__ f32x4 widen4(f32x4 r) {
+  asm volatile("" : "+v"(r));
+  return r;
 }
 
 // Four state elements per thread.  Forward: S_in(0) = init (or 0),
@@ -244,40 +260,70 @@ __global__ __launch_bounds__(kThreads) void k2_state_pass(ScanArgs a, int PN, in
     S = *reinterpret_cast<const f32x4 *>(a.init_state + ((int64_t)b * H + h) * PN + e);
   const bool up = (d == 0) != (flip != 0);
   const int step = up ? 1 : -1;
-  int c = up ? 0 : nc - 1;
+  const int c0 = up ? 0 : nc - 1;
   const bool rpart = flip && a.out0;
   const int nwv = PN / 256, wv = (blockIdx.x * kThreads + threadIdx.x) >> 6;
-  for (int n = 0; n < nc; ++n, c += step) {
-    const f32x4 loc = load4f(src + c * cs);
-    const float g = exp2_fast(dec[(int64_t)c * H]);
+  const T *sinb = rpart ? reinterpret_cast<const T *>(a.sin[d]) + (int64_t)b * a.sin_bstride[d] +
+                              (int64_t)h * PN + e
+                        : nullptr;
+  // The chunks' inputs are independent of the carry: a ring of D slots keeps
+  // the loads of the next D chunks in flight (the loop is latency-bound for
+  // long sequences otherwise).  Every load is unconditional: the primal
+  // state after chunk c (for the boundary products) is read from a clamped,
+  // always valid chunk and discarded by selection where there is none.
+  constexpr int D = 4;
+  typename Raw4<T>::type rl[D], rn[D];
+  float rg[D];
+  auto fetch = [&](int slot, int cc) __attribute__((always_inline)) {
+    rl[slot] = load4raw(src + cc * cs);
+    rg[slot] = dec[(int64_t)cc * H];
     if (rpart) {
-      // primal state after chunk c = primal carry-in of chunk c + 1 (forward)
-      // or c - 1 (reverse)
-      const int cn = d == 0 ? c + 1 : c - 1;
-      float v = 0.0f;
-      if (cn >= 0 && cn < nc) {
-        const T *sp = reinterpret_cast<const T *>(a.sin[d]) + (int64_t)b * a.sin_bstride[d] +
-                      (int64_t)cn * a.sin_cstride[d] + (int64_t)h * PN + e;
+      int cn = d == 0 ? cc + 1 : cc - 1;
+      cn = cn < 0 ? 0 : (cn >= nc ? nc - 1 : cn);
+      rn[slot] = load4raw(sinb + (int64_t)cn * a.sin_cstride[d]);
+    }
+  };
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v += S[i] * to_f(sp[i]);
+  for (int i = 0; i < D; ++i)
+    if (i < nc) fetch(i, c0 + i * step);
+  for (int n = 0; n < nc; n += D) {
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      const int nn = n + i;
+      if (nn >= nc) break;
+      const int c = c0 + nn * step;
+      // widen this slot before refilling it, so the refill can reuse its
+      // registers (a copy of an in-flight load would wait for it)
+      const f32x4 loc = widen4(rl[i]);
+      const f32x4 nb = rpart ? widen4(rn[i]) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      const float g = exp2_fast(rg[i]);
+      if (nn + D < nc) fetch(i, c + D * step);
+      if (rpart) {
+        // primal state after chunk c = primal carry-in of chunk c + 1
+        // (forward) or c - 1 (reverse)
+        const int cn = d == 0 ? c + 1 : c - 1;
+        float v = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v += S[k] * nb[k];
+        v = (cn >= 0 && cn < nc) ? v : 0.0f;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+        if ((threadIdx.x & 63) == 0)
+          a.out0[((((int64_t)d * a.Z + b) * nc + c) * H + h) * nwv + wv] = v;
+      }
+      if (dst) {
+        if constexpr (sizeof(T) == 2) {
+          bf16x4 o;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) o[k] = (bf16)S[k];
+          *reinterpret_cast<bf16x4 *>(dst + c * cs) = o;
+        } else {
+          *reinterpret_cast<f32x4 *>(dst + c * cs) = S;
+        }
       }
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
-      if ((threadIdx.x & 63) == 0)
-        a.out0[((((int64_t)d * a.Z + b) * nc + c) * H + h) * nwv + wv] = v;
+      for (int k = 0; k < 4; ++k) S[k] = g * S[k] + loc[k];
     }
-    if (dst) {
-      if constexpr (sizeof(T) == 2) {
-        bf16x4 o;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = (bf16)S[i];
-        *reinterpret_cast<bf16x4 *>(dst + c * cs) = o;
-      } else {
-        *reinterpret_cast<f32x4 *>(dst + c * cs) = S;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) S[i] = g * S[i] + loc[i];
   }
   if (primal_fwd && a.final_state)
     *reinterpret_cast<f32x4 *>(a.final_state + ((int64_t)b * H + h) * PN + e) = S;
@@ -286,7 +332,8 @@ __global__ __launch_bounds__(kThreads) void k2_state_pass(ScanArgs a, int PN, in
 // A-tangent of the carry-in states, four elements per thread:
 // SA_in(c+1) = 2^cdecay(c) (SA_in(c) + Tsum(c) S_in(c)) + ST_loc(c), from zero,
 // alongside the primal carry S_in (from init_state or zero), in each
-// direction's scan order; SA_in of every chunk goes to sin_t in T.
+// direction's scan order; SA_in of every chunk goes to sin_t in T.  Loads run
+// D chunks ahead as in the state pass.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k2_tangent_pass(ScanArgs a, int PN) {
   const int e = (blockIdx.x * kThreads + threadIdx.x) * 4;
@@ -305,23 +352,41 @@ __global__ __launch_bounds__(kThreads) void k2_tangent_pass(ScanArgs a, int PN) 
   if (d == 0 && a.init_state)
     S = *reinterpret_cast<const f32x4 *>(a.init_state + ((int64_t)b * H + h) * PN + e);
   const int step = d == 0 ? 1 : -1;
-  int c = d == 0 ? 0 : nc - 1;
-  for (int n = 0; n < nc; ++n, c += step) {
-    const f32x4 loc = load4f(sl + c * cs);
-    const f32x4 tloc = load4f(tl + c * cs);
-    const float g = exp2_fast(dec[(int64_t)c * H]), ts = tsum[(int64_t)c * H];
-    if constexpr (sizeof(T) == 2) {
-      bf16x4 o;
+  const int c0 = d == 0 ? 0 : nc - 1;
+  constexpr int D = 4;
+  typename Raw4<T>::type rl[D], rt[D];
+  float rg[D], rs[D];
+  auto fetch = [&](int slot, int cc) __attribute__((always_inline)) {
+    rl[slot] = load4raw(sl + cc * cs);
+    rt[slot] = load4raw(tl + cc * cs);
+    rg[slot] = dec[(int64_t)cc * H];
+    rs[slot] = tsum[(int64_t)cc * H];
+  };
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = (bf16)SA[i];
-      *reinterpret_cast<bf16x4 *>(dst + c * cs) = o;
-    } else {
-      *reinterpret_cast<f32x4 *>(dst + c * cs) = SA;
-    }
+  for (int i = 0; i < D; ++i)
+    if (i < nc) fetch(i, c0 + i * step);
+  for (int n = 0; n < nc; n += D) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      SA[i] = g * (SA[i] + ts * S[i]) + tloc[i];
-      S[i] = g * S[i] + loc[i];
+    for (int i = 0; i < D; ++i) {
+      const int nn = n + i;
+      if (nn >= nc) break;
+      const int c = c0 + nn * step;
+      const f32x4 loc = widen4(rl[i]), tloc = widen4(rt[i]);
+      const float g = exp2_fast(rg[i]), ts = rs[i];
+      if (nn + D < nc) fetch(i, c + D * step);
+      if constexpr (sizeof(T) == 2) {
+        bf16x4 o;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) o[k] = (bf16)SA[k];
+        *reinterpret_cast<bf16x4 *>(dst + c * cs) = o;
+      } else {
+        *reinterpret_cast<f32x4 *>(dst + c * cs) = SA;
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        SA[k] = g * (SA[k] + ts * S[k]) + tloc[k];
+        S[k] = g * S[k] + loc[k];
+      }
     }
   }
 }
