@@ -67,9 +67,6 @@ template <typename T, int N> struct PanelLds {
   float red[2][4];
 };
 
-// vector-memory count 0, other counters left alone
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
 // Workgroup = (batch b, chunk c, direction d, group g, 64-token row-block j)
 // of one panel.  PNL 0 produces dC rows t: the row source is dy, the column
 // source x, the columns s run before t in scan order, and the carried state
@@ -100,8 +97,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_panel(BwdArgs a) {
   // two tiles for the dC panel (register-bound to one workgroup per CU
   // anyway); one for the dB panel, which then fits two workgroups per CU
   constexpr bool DBUF = sizeof(T) == 2 && PNL == 0;
-  using DC = DmaTile<CRB>;
-  using DS = DmaTile<SRB>;
+  using DC = DmaTile<CRB, SW_NAT>;
+  using DS = DmaTile<SRB, SW_TR>;
   __shared__ Sm sm;
   __shared__ __attribute__((aligned(16))) char bufA[CSB + STB];
   __shared__ __attribute__((aligned(16))) char bufB[DBUF ? CSB + STB : 16];
@@ -186,7 +183,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_panel(BwdArgs a) {
 #pragma unroll
         for (int ks = 0; ks < N / 32; ++ks) {
           Frag<T> bf;
-          frag_ld8_swz<SRB>(bf, bufA, 16 * u + r16, 32 * ks + 8 * g4);
+          frag_ld8_swz<DS>(bf, bufA, 16 * u + r16, 32 * ks + 8 * g4);
           mma(t, bf, cfr[ks]);
         }
 #pragma unroll
@@ -256,7 +253,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_panel(BwdArgs a) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           Frag<T> cf;
-          frag_ld8_swz<CRB>(cf, cs, 16 * u + r16, 32 * ks + 8 * g4);
+          frag_ld8_swz<DC>(cf, cs, 16 * u + r16, 32 * ks + 8 * g4);
           mma(dg, cf, rf[ks]);
         }
         // dg[i] = ColSrc[col] . RowSrc[row], col = 64k + 16u + 4 g4 + i
@@ -288,7 +285,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_panel(BwdArgs a) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         Frag<T> sf;
-        frag_rows_swz<SRB>(sf, cur + CSB, 32 * ks + 8 * g4, 32 * ks + 8 * g4 + 4, 16 * nt);
+        frag_rows_swz<DS>(sf, cur + CSB, 32 * ks + 8 * g4, 32 * ks + 8 * g4 + 4, 16 * nt);
         mma(t2, rf[ks], sf);
       }
 #pragma unroll
@@ -346,7 +343,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_panel(BwdArgs a) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         Frag<T> vf;
-        frag_rows_swz<SRB>(vf, bufA, 32 * q + 4 * g4, 32 * q + 16 + 4 * g4, 16 * nt);
+        frag_rows_swz<DS>(vf, bufA, 32 * q + 4 * g4, 32 * q + 16 + 4 * g4, 16 * nt);
         mma(oacc[nt], mf, vf);
       }
     }

@@ -489,22 +489,27 @@ template <typename T, typename S, int N> struct SlabState {
 //
 // gfx950 buffer loads can write LDS directly: each lane's 16 bytes land at
 // (wave-uniform base) + 16 * lane, and lanes outside the buffer resource
-// write zeros.  A slab of 64 rows of RB bytes is copied as 1 KB pieces into a
+// write zeros.  A slab of rows of RB bytes is copied as 1 KB pieces into a
 // dense tile whose 16-byte chunks are XOR-swizzled by row (chunk c of row y
-// is stored at chunk c ^ swz(y)), so that the fragment reads below hit
-// distinct LDS banks without padding.  No registers hold the data in flight;
-// the loads complete when every wave has waited for its vector-memory count
-// and the workgroup has passed a barrier.
+// is stored at chunk c ^ swz(y)), so that fragment reads hit distinct LDS
+// banks without padding.  No registers hold the data in flight; the copies
+// are complete once every wave has waited for its vector-memory count and
+// the workgroup has passed a barrier.
+//
+// Swizzle SW_NAT suits natural reads (16 lanes read 16 consecutive rows at
+// one chunk); SW_TR suits transpose reads (16 lanes read 4 consecutive rows,
+// 32 bytes each).
 typedef __attribute__((address_space(3))) void *lds_vptr;
+enum { SW_NAT = 0, SW_TR = 1 };
 
-template <int RB> struct DmaTile {
+template <int RB, int SW> struct DmaTile {
   static constexpr int CPR = RB / 16;    // 16-byte chunks per row
   static constexpr int RPP = 1024 / RB;  // rows per 1 KB piece
   __device__ static __forceinline__ int swz(int y) {
-    return RB == 128 ? ((y >> 1) & 7) : (RB == 256 ? 2 * (y & 3) : 0);
+    if (SW == SW_NAT) return RB == 128 ? ((y >> 1) & 7) : (y & 15);
+    return RB == 128 ? 2 * ((y >> 1) & 3) : (RB == 256 ? 2 * (y & 3) : 0);
   }
-  // byte offset of logical (row y, byte x) in the tile (x within a chunk
-  // keeps its low 4 bits)
+  // byte offset of logical (row y, byte x) in the tile
   __device__ static __forceinline__ int at(int y, int x) {
     return y * RB + ((((x >> 4) ^ swz(y)) << 4) | (x & 15));
   }
@@ -524,38 +529,56 @@ template <int RB> struct DmaTile {
 
 // natural-mapping fragment (8 consecutive elements at row y, column x) from
 // a swizzled tile
-template <int RB>
+template <class DT>
 __device__ __forceinline__ void frag_ld8_swz(Frag<bf16> &f, const char *tile, int y, int x) {
-  f.v = *reinterpret_cast<const bf16x8 *>(tile + DmaTile<RB>::at(y, 2 * x));
+  f.v = *reinterpret_cast<const bf16x8 *>(tile + DT::at(y, 2 * x));
 }
-template <int RB>
+template <class DT>
 __device__ __forceinline__ void frag_ld8_swz(Frag<float> &f, const char *tile, int y, int x) {
-  const f32x4 a = *reinterpret_cast<const f32x4 *>(tile + DmaTile<RB>::at(y, 4 * x));
-  const f32x4 b = *reinterpret_cast<const f32x4 *>(tile + DmaTile<RB>::at(y, 4 * x + 16));
+  const f32x4 a = *reinterpret_cast<const f32x4 *>(tile + DT::at(y, 4 * x));
+  const f32x4 b = *reinterpret_cast<const f32x4 *>(tile + DT::at(y, 4 * x + 16));
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     f.v[e] = a[e];
     f.v[4 + e] = b[e];
   }
 }
+// the same from an fp32 tile into a bf16 fragment (one rounding)
+template <class DT>
+__device__ __forceinline__ void frag_ld8_swz_f32(Frag<bf16> &f, const char *tile, int y, int x) {
+  const f32x4 a = *reinterpret_cast<const f32x4 *>(tile + DT::at(y, 4 * x));
+  const f32x4 b = *reinterpret_cast<const f32x4 *>(tile + DT::at(y, 4 * x + 16));
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f.v[e] = (bf16)a[e];
+    f.v[4 + e] = (bf16)b[e];
+  }
+}
+template <class DT>
+__device__ __forceinline__ void frag_ld8_swz_f32(Frag<float> &f, const char *tile, int y, int x) {
+  frag_ld8_swz<DT>(f, tile, y, x);
+}
 // k-along-rows fragment (frag_rows semantics) from a swizzled tile
-template <int RB>
+template <class DT>
 __device__ __forceinline__ void frag_rows_swz(Frag<bf16> &f, const char *tile, int r0, int r1, int c0) {
   const int i = threadIdx.x & 15;
   const int y = i >> 2, x = 2 * (c0 + 4 * (i & 3));
-  const bf16x4 a = lds_tr4(reinterpret_cast<const bf16 *>(tile + DmaTile<RB>::at(r0 + y, x)));
-  const bf16x4 b = lds_tr4(reinterpret_cast<const bf16 *>(tile + DmaTile<RB>::at(r1 + y, x)));
+  const bf16x4 a = lds_tr4(reinterpret_cast<const bf16 *>(tile + DT::at(r0 + y, x)));
+  const bf16x4 b = lds_tr4(reinterpret_cast<const bf16 *>(tile + DT::at(r1 + y, x)));
   f.v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
-template <int RB>
+template <class DT>
 __device__ __forceinline__ void frag_rows_swz(Frag<float> &f, const char *tile, int r0, int r1, int c0) {
   const int i = threadIdx.x & 15;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    f.v[e] = *reinterpret_cast<const float *>(tile + DmaTile<RB>::at(r0 + e, 4 * (c0 + i)));
-    f.v[4 + e] = *reinterpret_cast<const float *>(tile + DmaTile<RB>::at(r1 + e, 4 * (c0 + i)));
+    f.v[e] = *reinterpret_cast<const float *>(tile + DT::at(r0 + e, 4 * (c0 + i)));
+    f.v[4 + e] = *reinterpret_cast<const float *>(tile + DT::at(r1 + e, 4 * (c0 + i)));
   }
 }
+
+// vector-memory count 0, other counters left alone
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // ------------------------------------------------------- XCD-aware order
 //
