@@ -307,6 +307,8 @@ int bissd_block_update(const bissd_shape_t *s, const float *state_in, const void
   a.sin_f32[0] = 1;
   a.sin[1] = nullptr;
   a.sin_t = nullptr;
+  // blocks of at most 64 tokens: one launch does everything
+  if (s->seqlen <= 64) return finish(bissd::launch_block_update(a, st));
   // order matters when state_out == state_in: the output phase reads
   // state_in before the state pass overwrites it
   hipError_t e = hipSuccess;

@@ -1,0 +1,223 @@
+// bissd_block.hip -- single-launch block update for active blocks of at most
+// 64 tokens (gfx950).
+//
+// Block-wise denoising with a cached prefix ("Training Hybrid Block Diffusion
+// Language Models with Partial Bidirectionality", Methodology and Technical
+// Contribution): the forward scan continues from the cached state after the
+// prefix, the reverse scan starts from zero at the block end and never
+// leaves the block, and y = y_f + y_r + D x.  Committing the block advances
+// the cached state over it:
+//
+//   forward : y_t = 2^lam_t C_t S_in + sum_{s<=t} (C_t.B_s) 2^(lam_t - lam_s) dt_s x_s
+//   reverse : y_t =                    sum_{s>=t} (C'_t.B'_s) 2^(rho_t - rho_s) dt'_s x_s
+//   S_out   = 2^lam_last S_in + sum_s 2^(lam_last - lam_s) dt_s x_s (outer) B_s
+//
+// The block is one chunk of the chunked scan, so the work of one (batch,
+// head) fits one workgroup, and the call is bound by latency rather than by
+// bandwidth or matrix-core time: every input of the workgroup is requested
+// at once (B_f, B'_r and x rows and the cached state copied buffer -> LDS,
+// C rows and dt into registers), the workgroup waits once, and both
+// directions, the skip and the committed state follow without another
+// global round trip.
+#include "bissd_device.hpp"
+#include "bissd_internal.hpp"
+
+namespace bissd {
+
+template <typename T, int N> struct BlockLds {
+  static constexpr int BRB = N * (int)sizeof(T);
+  static constexpr int XRB = kP * (int)sizeof(T);
+  static constexpr int SRB = N * 4;
+  using DB = DmaTile<BRB, SW_NAT>;
+  using DX = DmaTile<XRB, SW_TR>;
+  using DS = DmaTile<SRB, SW_NAT>;
+  float lam[2][kRB];
+  float dtv[2][kRB];
+};
+
+// Workgroup = (batch b, head h); wave w owns block rows t = 16 w .. 16 w + 15
+// (and, for the committed state, state rows p = 16 w .. 16 w + 15).  Decay
+// weights are formed exactly per element (the block is a single 64 x 64
+// tile), masked by selection.
+template <typename T, int N>
+__global__ __launch_bounds__(kThreads) void k_block_update(ScanArgs a) {
+  using Sm = BlockLds<T, N>;
+  using DB = typename Sm::DB;
+  using DX = typename Sm::DX;
+  using DS = typename Sm::DS;
+  __shared__ Sm sm;
+  __shared__ __attribute__((aligned(16))) char tBf[kRB * Sm::BRB];
+  __shared__ __attribute__((aligned(16))) char tBr[kRB * Sm::BRB];
+  __shared__ __attribute__((aligned(16))) char tX[kRB * Sm::XRB];
+  __shared__ __attribute__((aligned(16))) char tS[kP * Sm::SRB];
+  constexpr int NK = N / 32, NT = N / 16;
+  constexpr uint32_t ES = sizeof(T);
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
+  const int h = blockIdx.x % a.H, b = blockIdx.x / a.H;
+  const int H = a.H, G = a.G, gidx = h / (H / G);
+  const int L = (int)a.L;  // block length, 1..64
+  const uint32_t brs = (uint32_t)(G * N * ES), xrs = (uint32_t)(H * kP * ES);
+
+  // ---- every load of the workgroup, issued at once
+  const bufres rBf = make_buf(reinterpret_cast<const T *>(a.B[0]) + (int64_t)b * L * G * N, (uint32_t)(L * G * N * ES));
+  const bufres rBr = make_buf(reinterpret_cast<const T *>(a.B[1]) + (int64_t)b * L * G * N, (uint32_t)(L * G * N * ES));
+  const bufres rCf = make_buf(reinterpret_cast<const T *>(a.C[0]) + (int64_t)b * L * G * N, (uint32_t)(L * G * N * ES));
+  const bufres rCr = make_buf(reinterpret_cast<const T *>(a.C[1]) + (int64_t)b * L * G * N, (uint32_t)(L * G * N * ES));
+  const bufres rX = make_buf(reinterpret_cast<const T *>(a.x) + (int64_t)b * L * H * kP, (uint32_t)(L * H * kP * ES));
+  const float *sin = a.init_state + ((int64_t)b * H + h) * kP * N;
+  DB::load(tBf, rBf, (uint32_t)gidx * N * ES, brs, kRB);
+  DB::load(tBr, rBr, (uint32_t)gidx * N * ES, brs, kRB);
+  DX::load(tX, rX, (uint32_t)h * kP * ES, xrs, kRB);
+  DS::load(tS, make_buf(sin, (uint32_t)(kP * N * 4)), 0u, (uint32_t)Sm::SRB, kP);
+  const int trow = 16 * w + r16;
+  Frag<T> cf[NK], cr[NK];
+#pragma unroll
+  for (int ks = 0; ks < NK; ++ks) {
+    const uint32_t off = (uint32_t)(trow * G + gidx) * N * ES + (32 * ks + 8 * g4) * ES;
+    frag_bload(cf[ks], rCf, off);
+    frag_bload(cr[ks], rCr, off);
+  }
+  for (int d = w; d < 2; d += 4)
+    chunk_decay_scan<T>(reinterpret_cast<const T *>(a.dt[d]) + (int64_t)b * L * H + h, H, L, kRB,
+                        a.A[d][h] * kLog2e, d == 1, sm.lam[d], sm.dtv[d]);
+  wait_vmem();
+  __syncthreads();
+
+  f32x4 acc[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) zero4(acc[v]);
+
+  // ---- both directions' within-block terms
+  auto direction = [&](auto dc) __attribute__((always_inline)) {
+    constexpr int d = decltype(dc)::value;
+    const char *Bt = d == 0 ? tBf : tBr;
+    const int ulo = d == 0 ? 0 : w, uhi = d == 0 ? w : 3;
+    // cb[u]: lane holds (C.B^T)[t = 16w + r16][s = 16u + 4 g4 + i]
+    f32x4 cb[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) zero4(cb[u]);
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (u < ulo || u > uhi) continue;
+        Frag<T> bf;
+        frag_ld8_swz<DB>(bf, Bt, 16 * u + r16, 32 * ks + 8 * g4);
+        mma(cb[u], bf, d == 0 ? cf[ks] : cr[ks]);
+      }
+    }
+    const float lt = sm.lam[d][trow];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      if (2 * q + 1 < ulo || 2 * q > uhi) continue;
+      float m[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int u = 2 * q + (e >> 2), i2 = e & 3;
+        const int s = 16 * u + 4 * g4 + i2;
+        const bool ok = d == 0 ? s <= trow : s >= trow;
+        const float wgt = exp2_fast(fminf(lt - sm.lam[d][s], 0.0f)) * sm.dtv[d][s];
+        m[e] = ok ? cb[u][i2] * wgt : 0.0f;
+      }
+      Frag<T> mf;
+      frag_from(mf, m);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        Frag<T> xf;
+        frag_rows_swz<DX>(xf, tX, 32 * q + 4 * g4, 32 * q + 16 + 4 * g4, 16 * v);
+        mma(acc[v], mf, xf);
+      }
+    }
+    if constexpr (d == 0) {
+      // carried state: 2^lam_t C_t S_in^T (rows t = 16w + 4 g4 + i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        f32x4 t2;
+        zero4(t2);
+#pragma unroll
+        for (int ks = 0; ks < NK; ++ks) {
+          Frag<T> sf;
+          frag_ld8_swz_f32<DS>(sf, tS, 16 * v + r16, 32 * ks + 8 * g4);
+          mma(t2, cf[ks], sf);
+        }
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2) acc[v][i2] += exp2_fast(sm.lam[0][16 * w + 4 * g4 + i2]) * t2[i2];
+      }
+    }
+  };
+  direction(std::integral_constant<int, 0>{});
+  direction(std::integral_constant<int, 1>{});
+
+  // ---- committed state: S_out = 2^lam_last S_in + sum_s w_s x_s (outer) B_s,
+  // w_s = 2^(lam_last - lam_s) dt_s; wave w owns state rows p = 16w..16w+15
+  if (a.final_state) {
+    const float lend = sm.lam[0][kRB - 1];  // tokens past the block have dt = 0
+    f32x4 sacc[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) zero4(sacc[nt]);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      // A operand: x^T rows p = 16w + r16, k = s = 32ks + 8 g4 + e, scaled by w_s
+      Frag<T> xa;
+      frag_rows_swz<DX>(xa, tX, 32 * ks + 8 * g4, 32 * ks + 8 * g4 + 4, 16 * w);
+      float xv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int s = 32 * ks + 8 * g4 + e;
+        const float dv = sm.dtv[0][s];
+        xv[e] = (float)xa.v[e] * (dv != 0.0f ? dv * exp2_fast(lend - sm.lam[0][s]) : 0.0f);
+      }
+      frag_from(xa, xv);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        Frag<T> bfr;
+        frag_rows_swz<DB>(bfr, tBf, 32 * ks + 8 * g4, 32 * ks + 8 * g4 + 4, 16 * nt);
+        mma(sacc[nt], xa, bfr);
+      }
+    }
+    const float gam = exp2_fast(lend);
+    float *so = a.final_state + ((int64_t)b * H + h) * kP * N;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int i2 = 0; i2 < 4; ++i2) {
+        const int p = 16 * w + 4 * g4 + i2, n = 16 * nt + r16;
+        const float s0 = *reinterpret_cast<const float *>(tS + DS::at(p, 4 * n));
+        so[p * N + n] = gam * s0 + sacc[nt][i2];
+      }
+  }
+
+  // ---- y = acc + D x from registers (rows 16w + 4 g4 + i, columns
+  // 16 v + r16; 16 lanes store one contiguous row segment), x from its tile
+  const float Dh = a.D[h];
+  T *yg = reinterpret_cast<T *>(a.y) + ((int64_t)b * L * H + h) * kP;
+#pragma unroll
+  for (int i2 = 0; i2 < 4; ++i2) {
+    const int t = 16 * w + 4 * g4 + i2;
+    if (t >= L) continue;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int p = 16 * v + r16;
+      const float xv = to_f(*reinterpret_cast<const T *>(tX + DX::at(t, (int)ES * p)));
+      yg[(int64_t)t * H * kP + p] = from_f<T>(acc[v][i2] + Dh * xv);
+    }
+  }
+}
+
+template <typename T, int N>
+static void launch_block_t(const ScanArgs &a, hipStream_t st) {
+  hipLaunchKernelGGL((k_block_update<T, N>), dim3((unsigned)(a.Z * a.H)), dim3(kThreads), 0, st, a);
+}
+
+hipError_t launch_block_update(const ScanArgs &a, hipStream_t st) {
+  if (a.dtype == 1) {
+    if (a.N == 128) launch_block_t<bf16, 128>(a, st);
+    else launch_block_t<bf16, 64>(a, st);
+  } else {
+    if (a.N == 128) launch_block_t<float, 128>(a, st);
+    else launch_block_t<float, 64>(a, st);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace bissd

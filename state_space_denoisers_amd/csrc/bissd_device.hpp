@@ -485,6 +485,21 @@ template <typename T, typename S, int N> struct SlabState {
   }
 };
 
+// Operand fragment of 8 consecutive elements read straight from a buffer
+// resource (zeros past its end).
+__device__ __forceinline__ void frag_bload(Frag<bf16> &f, bufres r, uint32_t off) {
+  f.v = __builtin_bit_cast(bf16x8, bload16(r, off));
+}
+__device__ __forceinline__ void frag_bload(Frag<float> &f, bufres r, uint32_t off) {
+  const f32x4 a = __builtin_bit_cast(f32x4, bload16(r, off));
+  const f32x4 b = __builtin_bit_cast(f32x4, bload16(r, off + 16));
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f.v[e] = a[e];
+    f.v[4 + e] = b[e];
+  }
+}
+
 // ------------------------------------------------- direct buffer -> LDS slabs
 //
 // gfx950 buffer loads can write LDS directly: each lane's 16 bytes land at

@@ -55,6 +55,12 @@ enum {
 
 hipError_t launch_scan_phase(const ScanArgs &a, int phase, hipStream_t st);
 
+// Whole block update (both directions, skip, optional committed state) in
+// one launch, for blocks of at most 64 tokens: x, dt, A, B, C, D, y as in
+// the scan; init_state = the cached state; final_state = the committed
+// state or nullptr (may equal init_state); L = block length.
+hipError_t launch_block_update(const ScanArgs &a, hipStream_t st);
+
 // Arguments of the backward-only kernels (dB / dC panels, decay gradients,
 // final reductions).
 struct BwdArgs {
