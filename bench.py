@@ -19,7 +19,7 @@ times the fp64 CPU oracle on a bounded sample of the same workload.  One
 JSON line is printed.
 
 Profiling helpers (for rocprofv3 runs):
-    python bench.py --profile-phase {0,1,2,all,backward} [--workload W] [--iters R]
+    python bench.py --profile-phase {0,1,2,all,backward,block} [--workload W] [--iters R]
     python bench.py --copy-calibrate
 """
 from __future__ import annotations
@@ -249,14 +249,16 @@ def bench_block(reps):
                                state_out=s_out if commit else None, commit=commit, workspace=ws)
 
     out = {"workload": w.name, "prefix_tokens": w.prefix_len, "block_tokens": w.L, "batch": w.Z}
+    per_graph = 50
     for commit in (False, True):
         for _ in range(5):
             upd(commit)
         torch.cuda.synchronize()
         ms = event_time_ms(lambda: upd(commit), reps)
         key = "commit" if commit else "no_commit"
+        # eager calls from Python: bounded by host submission for a call this small
         out[f"us_per_update_{key}"] = 1e3 * ms
-        # replay of a captured HIP graph of the same call
+        # device time: a captured HIP graph of 50 back-to-back updates
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
@@ -264,11 +266,12 @@ def bench_block(reps):
             upd(commit)
             torch.cuda.synchronize()
             with torch.cuda.graph(g, stream=s):
-                upd(commit)
+                for _ in range(per_graph):
+                    upd(commit)
         torch.cuda.current_stream().wait_stream(s)
         g.replay()
         torch.cuda.synchronize()
-        out[f"us_per_update_{key}_graph"] = 1e3 * event_time_ms(g.replay, reps)
+        out[f"us_per_update_{key}_graph"] = 1e3 * event_time_ms(g.replay, max(5, reps // per_graph)) / per_graph
         del g
     return out
 
@@ -334,6 +337,18 @@ def profile_phase(args):
     import torch
     from synth import gen
     w = gen.WORKLOADS[args.workload]
+    if args.profile_phase == "block":
+        import state_space_denoisers_amd as ssd
+        inp, T = device_inputs(w)
+        fwd, rev = dirs(T)
+        state = torch.zeros((w.Z, w.H, w.P, w.N), dtype=torch.float32, device=T["x"].device)
+        torch.cuda.synchronize()
+        print(f"profiling block update on {w.name} x{args.iters}", flush=True)
+        for _ in range(args.iters):
+            ssd.bissd_block_update(state, T["x"], fwd, rev, T["D"], commit=True)
+        torch.cuda.synchronize()
+        print("done", flush=True)
+        return
     if args.profile_phase == "backward":
         t = Train(w)
         torch.cuda.synchronize()
@@ -375,7 +390,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--profile-phase", choices=["0", "1", "2", "all", "backward"])
+    ap.add_argument("--profile-phase", choices=["0", "1", "2", "all", "backward", "block"])
     ap.add_argument("--workload", default="layer130m_L1k")
     ap.add_argument("--iters", type=int, default=20)
     ap.add_argument("--copy-calibrate", action="store_true")

@@ -49,6 +49,7 @@ template <typename T, int N> struct PanelLds {
   float lam[2][kQmax];
   float dtv[2][kQmax];
   float cdt[2][kQmax];  // cumulative dt (dC panel)
+  float colf[2][kQmax]; // column factors of the off-diagonal blocks
   float red[2][4];
 };
 
@@ -62,8 +63,11 @@ template <typename T, int N> struct PanelLds {
 // Per head of the group: the Gram tiles D[col][row] = ColSrc_col . RowSrc_row
 // come out of the matrix cores already laid out as the A operand of the
 // later product, are weighted elementwise by 2^(cum_later - cum_earlier) dt
-// (exact per element, masked by selection) and summed over heads in fp32
-// registers; the carried-state term RowSrc_row . State is added per head
+// and summed over heads in fp32 registers.  Off-diagonal column blocks use
+// the factored weight 2^(cum_row - m) 2^(m - cum_col) (or its mirror), m the
+// decay sum at the block boundary, so both factors are <= 1: a per-lane row
+// factor times a per-column factor formed once per head; the diagonal block
+// is weighted exactly per element and masked by selection; the carried-state term RowSrc_row . State is added per head
 // with its row factor.  After the last head the summed weights multiply the
 // value rows (B for dC, C for dB), one 64-row slab at a time.
 // The dC panel also forms C.B^T for its tiles once (before the heads) and
@@ -143,6 +147,24 @@ __global__ __launch_bounds__(kThreads) void k_bwd_panel(BwdArgs a) {
       frag_bload(r[ks], rRow, (uint32_t)((t0 + rrow) * H + h) * kP * ES + (32 * ks + 8 * g4) * ES);
   };
 
+  // Reference for the factored off-diagonal weights: the decay sum at the
+  // boundary token between the row block and its off-diagonal columns (dC:
+  // the token before the block in scan order; dB: the block's last token in
+  // scan order).  Tokens outside the chunk only occur when there are no
+  // off-diagonal blocks.
+  const int mtok = PNL == 0 ? (d == 0 ? j * kRB - 1 : (j + 1) * kRB) : (d == 0 ? j * kRB + kRB - 1 : j * kRB);
+  const bool mok = mtok >= 0 && mtok < Q;
+  // column factors of one head, by the wave that just wrote its decay sums:
+  // dC 2^(m - cum_s) dt_s, dB 2^(cum_t - m)
+  auto build_colf = [&](int buf) __attribute__((always_inline)) {
+    const float m = mok ? sm.lam[buf][mtok] : 0.0f;
+    for (int s2 = lane; s2 < Q; s2 += 64) {
+      const float l = sm.lam[buf][s2];
+      sm.colf[buf][s2] = PNL == 0 ? exp2_fast(fminf(m - l, 0.0f)) * sm.dtv[buf][s2]
+                                  : exp2_fast(fminf(l - m, 0.0f));
+    }
+  };
+
   // dC panel: cbt[k][u][i] = C_row . B_col in the Gram tiles' layout, kept
   // in the compute dtype
   using CBV = typename std::conditional<sizeof(T) == 2, bf16x4, f32x4>::type;
@@ -190,7 +212,10 @@ __global__ __launch_bounds__(kThreads) void k_bwd_panel(BwdArgs a) {
     float d0[4];
     ld_dt(g * hpg, r0);
     chunk_dt_decode<T>(r0, Q, d0);
-    if (w == 0) chunk_decay_scan_vals(d0, Q, a.A[d][g * hpg] * kLog2e, d == 1, sm.lam[0], sm.dtv[0]);
+    if (w == 0) {
+      chunk_decay_scan_vals(d0, Q, a.A[d][g * hpg] * kLog2e, d == 1, sm.lam[0], sm.dtv[0]);
+      build_colf(0);
+    }
     if (PNL == 0 && w == 1) chunk_decay_scan_vals(d0, Q, 1.0f, d == 1, sm.cdt[0], sm.dtv[0]);
   }
   Frag<T> rf[2];
@@ -211,6 +236,9 @@ __global__ __launch_bounds__(kThreads) void k_bwd_panel(BwdArgs a) {
     float dai = 0.0f;
     const float lrow = lam[rrow], drow = dtv[rrow];
     const float crow = PNL == 0 ? sm.cdt[lb][rrow] : 0.0f;
+    // row factor of the off-diagonal blocks (dC 2^(cum_t - m), dB dt_s 2^(m - cum_s))
+    const float mref = mok ? lam[mtok] : 0.0f;
+    const float rowf = PNL == 0 ? exp2_fast(fminf(lrow - mref, 0.0f)) : drow * exp2_fast(fminf(mref - lrow, 0.0f));
     float fr[4];
     {
       const float lend = d == 0 ? lam[Q - 1] : lam[0];
@@ -242,17 +270,27 @@ __global__ __launch_bounds__(kThreads) void k_bwd_panel(BwdArgs a) {
           mma(dg, cf, rf[ks]);
         }
         // dg[i] = ColSrc[col] . RowSrc[row], col = 64k + 16u + 4 g4 + i
+        const int col0 = k * kRB + 16 * u + 4 * g4;
+        if (k != j) {
+          const f32x4 cf4 = *reinterpret_cast<const f32x4 *>(&sm.colf[lb][col0]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int col = k * kRB + 16 * u + 4 * g4 + i;
-          bool ok = true;
-          if (k == j) ok = colLE ? (col <= rrow) : (col >= rrow);
-          const float lcol = lam[col];
-          const float ex = PNL == 0 ? lrow - lcol : lcol - lrow;
-          const float dtf = PNL == 0 ? dtv[col] : drow;
-          const float wv = ok ? dg[i] * (exp2_fast(fminf(ex, 0.0f)) * dtf) : 0.0f;
-          wsum[k][u][i] += wv;
-          if (PNL == 0) dai += wv * (float)cbt[k][u][i] * (crow - sm.cdt[lb][col]);
+          for (int i = 0; i < 4; ++i) {
+            const float wv = dg[i] * (rowf * cf4[i]);
+            wsum[k][u][i] += wv;
+            if (PNL == 0) dai += wv * (float)cbt[k][u][i] * (crow - sm.cdt[lb][col0 + i]);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int col = col0 + i;
+            const bool ok = colLE ? (col <= rrow) : (col >= rrow);
+            const float lcol = lam[col];
+            const float ex = PNL == 0 ? lrow - lcol : lcol - lrow;
+            const float dtf = PNL == 0 ? dtv[col] : drow;
+            const float wv = ok ? dg[i] * (exp2_fast(fminf(ex, 0.0f)) * dtf) : 0.0f;
+            wsum[k][u][i] += wv;
+            if (PNL == 0) dai += wv * (float)cbt[k][u][i] * (crow - sm.cdt[lb][col]);
+          }
         }
       }
     }
@@ -293,7 +331,10 @@ __global__ __launch_bounds__(kThreads) void k_bwd_panel(BwdArgs a) {
       for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(dtn[i]) : : "memory");
       float dn[4];
       chunk_dt_decode<T>(dtn, Q, dn);
-      if (w == 0) chunk_decay_scan_vals(dn, Q, a.A[d][h + 1] * kLog2e, d == 1, sm.lam[lb ^ 1], sm.dtv[lb ^ 1]);
+      if (w == 0) {
+        chunk_decay_scan_vals(dn, Q, a.A[d][h + 1] * kLog2e, d == 1, sm.lam[lb ^ 1], sm.dtv[lb ^ 1]);
+        build_colf(lb ^ 1);
+      }
       if (PNL == 0 && w == 1) chunk_decay_scan_vals(dn, Q, 1.0f, d == 1, sm.cdt[lb ^ 1], sm.dtv[lb ^ 1]);
       rf[0] = rfn[0];
       rf[1] = rfn[1];
@@ -348,19 +389,22 @@ __global__ __launch_bounds__(kThreads) void k_bwd_panel(BwdArgs a) {
 
 // ====================================================== decay gradients
 
-// One wavefront per (batch, direction, head) sequence, one chunk per step:
+// One wavefront per (batch, direction, head, chunk); the chunks are
+// independent once their boundary values are known:
 // d_lam_t = dy.y_d,t - dt_t x_t.(G_t B_t) (both taken without their common
-// t' = t term, which cancels); dalpha_t = the in-chunk sum of
-// d_lam over t and the tokens after it in scan order, plus the chunk's
-// boundary value (the wave partials of <adjoint carry, state after the
-// chunk>, summed in a fixed order); ddt_t = x_t.(G_t B_t) + A dalpha_t.
+// t' = t term, which cancels); dalpha_t = the in-chunk sum of d_lam over t
+// and the tokens after it in scan order, plus the chunk's boundary value
+// (the wave partials of <adjoint carry, state after the chunk>, summed in a
+// fixed order); ddt_t = x_t.(G_t B_t) + A dalpha_t.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_bwd_decay(BwdArgs a) {
   const int lane = threadIdx.x & 63;
-  const int seq = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-  const int H = a.H;
-  if (seq >= a.Z * 2 * H) return;
-  const int h = seq % H, d = (seq / H) % 2, b = seq / (2 * H);
+  const int64_t item = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  const int H = a.H, nc = a.nchunks;
+  if (item >= (int64_t)a.Z * 2 * H * nc) return;
+  const int c = (int)(item % nc);
+  const int h = (int)((item / nc) % H), d = (int)((item / ((int64_t)nc * H)) % 2);
+  const int b = (int)(item / ((int64_t)nc * H * 2));
   const int64_t L = a.L;
   const int Q = a.chunk, K = Q / 64, nwv = kP * a.N / 256;
   const T *dt = reinterpret_cast<const T *>(a.dt[d]) + (int64_t)b * L * H + h;
@@ -369,49 +413,47 @@ __global__ __launch_bounds__(kThreads) void k_bwd_decay(BwdArgs a) {
   const float *qxs = a.qxs + ((int64_t)d * a.Z + b) * L * H + h;
   float *ddt = a.ddt[d] + (int64_t)b * L * H + h;
   const float A = a.A[d][h];
-  for (int c = 0; c < a.nchunks; ++c) {
-    const float *rp = a.rpart + ((((int64_t)d * a.Z + b) * a.nchunks + c) * H + h) * nwv;
-    float R = 0.0f;
-    for (int k = 0; k < nwv; ++k) R += rp[k];
-    const int64_t base = (int64_t)c * Q + lane * K;
-    float v[4], ql[4];
+  const float *rp = a.rpart + ((((int64_t)d * a.Z + b) * nc + c) * H + h) * nwv;
+  float R = 0.0f;
+  for (int k = 0; k < nwv; ++k) R += rp[k];
+  const int64_t base = (int64_t)c * Q + lane * K;
+  float v[4], ql[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t t = base + i;
+    const bool ok = i < K && t < L;
+    ql[i] = ok ? qx[t * H] : 0.0f;
+    // dy.y_d and x.(G_t B_t) both without their common t' = t term
+    v[i] = ok ? yd[t * H] - to_f(dt[t * H]) * qxs[t * H] : 0.0f;
+  }
+  float run = 0.0f, acc[4];
+  if (d == 0) {
+#pragma unroll
+    for (int i = 3; i >= 0; --i) {
+      run += v[i];
+      acc[i] = run;
+    }
+    const float incl = wave_scan_down(run);
+    float excl = __shfl_down(incl, 1, 64);
+    if (lane == 63) excl = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] += excl + R;
+  } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int64_t t = base + i;
-      const bool ok = i < K && t < L;
-      ql[i] = ok ? qx[t * H] : 0.0f;
-      // dy.y_d and x.(G_t B_t) both without their common t' = t term
-      v[i] = ok ? yd[t * H] - to_f(dt[t * H]) * qxs[t * H] : 0.0f;
+      run += v[i];
+      acc[i] = run;
     }
-    float run = 0.0f, acc[4];
-    if (d == 0) {
+    const float incl = wave_scan_up(run);
+    float excl = __shfl_up(incl, 1, 64);
+    if (lane == 0) excl = 0.0f;
 #pragma unroll
-      for (int i = 3; i >= 0; --i) {
-        run += v[i];
-        acc[i] = run;
-      }
-      const float incl = wave_scan_down(run);
-      float excl = __shfl_down(incl, 1, 64);
-      if (lane == 63) excl = 0.0f;
+    for (int i = 0; i < 4; ++i) acc[i] += excl + R;
+  }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] += excl + R;
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        run += v[i];
-        acc[i] = run;
-      }
-      const float incl = wave_scan_up(run);
-      float excl = __shfl_up(incl, 1, 64);
-      if (lane == 0) excl = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] += excl + R;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t t = base + i;
-      if (i < K && t < L) ddt[t * H] = ql[i] + A * acc[i];
-    }
+  for (int i = 0; i < 4; ++i) {
+    const int64_t t = base + i;
+    if (i < K && t < L) ddt[t * H] = ql[i] + A * acc[i];
   }
 }
 
@@ -474,8 +516,8 @@ hipError_t launch_bwd_panels(const BwdArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_bwd_decay(const BwdArgs &a, hipStream_t st) {
-  const int nseq = a.Z * 2 * a.H;
-  dim3 g((unsigned)((nseq + 3) / 4));
+  const int64_t items = (int64_t)a.Z * 2 * a.H * a.nchunks;
+  dim3 g((unsigned)((items + 3) / 4));
   if (a.dtype == 1) hipLaunchKernelGGL(k_bwd_decay<bf16>, g, dim3(kThreads), 0, st, a);
   else hipLaunchKernelGGL(k_bwd_decay<float>, g, dim3(kThreads), 0, st, a);
   hipLaunchKernelGGL(k_bwd_reduce, dim3((unsigned)(3 * a.H)), dim3(kThreads), 0, st, a);

@@ -169,17 +169,27 @@ __global__ __launch_bounds__(kThreads) void k1_chunk_state(ScanArgs a) {
   }
 
   if constexpr (MODE <= 2) {
+    // one head at a time through LDS (the B tile, no longer read), so that
+    // every thread stores 16 contiguous bytes
+    constexpr int EPV = 16 / (int)sizeof(T);
+    static_assert(kP * N * sizeof(T) <= sizeof(sm.Bs), "state tile must fit the B tile");
+    T *stile = &sm.Bs[0][0];
     T *out = reinterpret_cast<T *>(a.states) + chi * (int64_t)(kP * N);
 #pragma unroll
-    for (int hh = 0; hh < HT; ++hh)
+    for (int hh = 0; hh < HT; ++hh) {
+      __syncthreads();
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            out[(int64_t)hh * kP * N + (16 * pt + 4 * g4 + i) * N + nb + 16 * nt + r16] =
-                from_f<T>(acc[hh][pt][nt][i]);
+            stile[(16 * pt + 4 * g4 + i) * N + nb + 16 * nt + r16] = from_f<T>(acc[hh][pt][nt][i]);
+      __syncthreads();
+      for (int v = tid; v < kP * N / EPV; v += kThreads)
+        *reinterpret_cast<u32x4 *>(out + (int64_t)hh * kP * N + v * EPV) =
+            *reinterpret_cast<const u32x4 *>(stile + v * EPV);
+    }
   }
   if constexpr (MODE == 1 || MODE == 3) {
     // Frobenius product with the given state of the same (direction, batch,
