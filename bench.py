@@ -11,7 +11,7 @@ W untimed warm-up steps, then exactly K timed steps between two device
 synchronisations; `value` is tokens per second over the timed region.
 
 The same run also measures, live with HIP events on the launch stream, the
-average duration of each of the three kernels inside complete forward calls
+average duration of each of the four kernels inside complete forward calls
 (enqueued phase by phase through bissd_forward_phase), the
 long-context L=65536 scan, the training step (forward + backward, batch 16,
 L=2048), and the block update with a cached 262,144-token prefix state; and
@@ -19,7 +19,7 @@ times the fp64 CPU oracle on a bounded sample of the same workload.  One
 JSON line is printed.
 
 Profiling helpers (for rocprofv3 runs):
-    python bench.py --profile-phase {0,1,2,all,backward,block} [--workload W] [--iters R]
+    python bench.py --profile-phase {0,1,2,3,all,backward,block} [--workload W] [--iters R]
     python bench.py --copy-calibrate
 """
 from __future__ import annotations
@@ -38,7 +38,8 @@ if ROOT not in sys.path:
 METRIC = "bidir SSD scan tokens/s at L=1K/65K; achieved HBM GB/s and MFMA %"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
-PHASE_NAMES = {0: "k1_chunk_state", 1: "k2_state_pass", 2: "k3_chunk_out"}
+PHASE_NAMES = {0: "k1_chunk_state", 3: "k_gram", 1: "k2_state_pass", 2: "k3_chunk_out"}
+PHASE_ORDER = (0, 3, 1, 2)   # the order bissd_forward runs them in
 KERNEL_SOURCES = ("state_space_denoisers_amd/csrc/bissd_fwd.hip",
                   "state_space_denoisers_amd/csrc/bissd_device.hpp")
 
@@ -116,25 +117,26 @@ def event_time_ms(fn, reps):
 
 def phase_times_us(f: Forward, reps):
     """Average duration of each forward kernel inside complete forward calls:
-    every call is enqueued as its three phases with a HIP event recorded
+    every call is enqueued as its four phases with a HIP event recorded
     between them on the launch stream, so each kernel runs in the same
     context (caches, preceding kernels) as in the timed region."""
     import torch
     f()
     torch.cuda.synchronize()
     s = torch.cuda.current_stream()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
+    n = len(PHASE_ORDER)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(reps)]
     for r in range(reps):
         evs[r][0].record(s)
-        for p in range(3):
+        for i, p in enumerate(PHASE_ORDER):
             f.phase(p)
-            evs[r][p + 1].record(s)
+            evs[r][i + 1].record(s)
     torch.cuda.synchronize()
-    tot = [0.0, 0.0, 0.0]
+    tot = [0.0] * n
     for r in range(reps):
-        for p in range(3):
-            tot[p] += evs[r][p].elapsed_time(evs[r][p + 1])
-    return {PHASE_NAMES[p]: 1e3 * tot[p] / reps for p in range(3)}
+        for i in range(n):
+            tot[i] += evs[r][i].elapsed_time(evs[r][i + 1])
+    return {PHASE_NAMES[p]: 1e3 * tot[i] / reps for i, p in enumerate(PHASE_ORDER)}
 
 
 def per_token_bytes(w):
@@ -146,14 +148,21 @@ def per_token_bytes(w):
 
 def k3_flops_per_token(w):
     """Matrix-core work of the fused output kernel per token (both
-    directions): C.B^T on causal 64x64 block pairs, the masked product with
-    x per head, and the carry-in contraction C S^T per head."""
+    directions): the masked product of the precomputed C.B^T tiles with x
+    on causal 64x64 block pairs per head, and the carry-in contraction
+    C S^T per head."""
     nrb = w.chunk // 64
     pairs = nrb * (nrb + 1) / 2 / nrb          # block pairs per row-block, per direction
-    gram = pairs * 64 * 64 * w.N * 2 / 64 * w.G
     intra = pairs * 64 * 64 * w.P * 2 / 64 * w.H
     inter = 2 * w.N * w.P * w.H
-    return 2 * (gram + intra + inter)
+    return 2 * (intra + inter)
+
+
+def gram_tiles_per_chunk(w):
+    """16x64 Gram tiles one slot keeps per chunk (row tile tt needs column
+    blocks 0..tt/4 on the causal side, tt/4..end on the other)."""
+    qt, nrb = w.chunk // 16, w.chunk // 64
+    return sum(tt // 4 + 1 for tt in range(qt)), nrb
 
 
 def phase_bytes_per_token(w, phase):
@@ -163,6 +172,9 @@ def phase_bytes_per_token(w, phase):
         return w.H * w.P * e + 2 * w.H * e + 2 * w.G * w.N * e + state_bytes
     if phase == 1:
         return 2 * state_bytes
+    if phase == 3:
+        tiles, _ = gram_tiles_per_chunk(w)
+        return 2 * 2 * w.G * w.N * e + 2 * w.G * tiles * 16 * 64 * 4 / w.chunk
     return per_token_bytes(w)
 
 
@@ -390,7 +402,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--profile-phase", choices=["0", "1", "2", "all", "backward", "block"])
+    ap.add_argument("--profile-phase", choices=["0", "1", "2", "3", "all", "backward", "block"])
     ap.add_argument("--workload", default="layer130m_L1k")
     ap.add_argument("--iters", type=int, default=20)
     ap.add_argument("--copy-calibrate", action="store_true")

@@ -115,8 +115,10 @@ typedef struct {
 
 /*
  * Bytes of device workspace that `op` needs for `shape` (0 on a bad shape).
- * The workspace holds the per-chunk carry states (fp32) and is overwritten
- * by every call; its contents between calls mean nothing.
+ * The workspace holds the per-chunk states and carries (compute dtype), the
+ * chunk decays and the chunk Gram tiles C.B^T (fp32), plus the backward
+ * pass's adjoint and reduction buffers; it is overwritten by every call and
+ * its contents between calls mean nothing.
  */
 size_t bissd_workspace_size(const bissd_shape_t *shape, int op);
 
@@ -163,10 +165,12 @@ int bissd_block_update(const bissd_shape_t *shape, const float *state_in,
  * Diagnostics for timing and profiling single kernels: enqueue only one
  * phase of bissd_forward with the same arguments and validation.
  *   phase 0: per-chunk local states and chunk decays (written to workspace)
+ *   phase 3: per-chunk Gram tiles C.B^T of both directions (workspace)
  *   phase 1: carry pass over chunks (workspace in place; final_state)
  *   phase 2: fused bidirectional output (reads workspace, writes y)
- * A phase reads what the phases before it left in the same workspace, so
- * phase 2 repeated after one full bissd_forward recomputes the same y.
+ * bissd_forward runs them in the order 0, 3, 1, 2.  A phase reads what the
+ * phases before it left in the same workspace, so phase 2 repeated after one
+ * full bissd_forward recomputes the same y.
  * Phase 1 rewrites the workspace in place and is not idempotent.
  */
 int bissd_forward_phase(const bissd_shape_t *shape, const void *x, bissd_dir_t fwd,

@@ -109,7 +109,7 @@ def bissd_forward_phase(phase: int, x: torch.Tensor, fwd, rev, D: torch.Tensor, 
                         chunk: int = 256, y: torch.Tensor, workspace: torch.Tensor,
                         init_state: Optional[torch.Tensor] = None,
                         final_state: Optional[torch.Tensor] = None, stream=None) -> None:
-    """Enqueue one phase of bissd_forward (0 chunk states, 1 carry pass,
+    """Enqueue one phase of bissd_forward (0 chunk states, 3 Gram tiles, 1 carry pass,
     2 output) for timing single kernels (include/bissd.h)."""
     lib = _abi.load()
     fwd, rev = Dir(*fwd), Dir(*rev)

@@ -39,6 +39,9 @@ int check_shape(const bissd_shape_t *s, int op) {
     return BISSD_ERR_UNSUPPORTED;
   const int64_t nc = ceil_div(s->seqlen, s->chunk);
   if (s->batch * nc * (s->chunk / 64) * 2 * s->nheads >= ((int64_t)1 << 31)) return BISSD_ERR_UNSUPPORTED;
+  const int64_t nrb = s->chunk / 64;
+  if (s->batch * nc * 2 * s->ngroups * (nrb * (nrb + 1) / 2) >= ((int64_t)1 << 31))
+    return BISSD_ERR_UNSUPPORTED;
   // per-batch-row buffer resources address at most 4 GiB
   if (s->seqlen * s->nheads * s->headdim * 4 >= ((int64_t)1 << 32)) return BISSD_ERR_UNSUPPORTED;
   if (s->seqlen * s->ngroups * s->dstate * 4 >= ((int64_t)1 << 32)) return BISSD_ERR_UNSUPPORTED;
@@ -48,14 +51,16 @@ int check_shape(const bissd_shape_t *s, int op) {
 
 // Workspace: chunk-local states and the carry-in states, both in the compute
 // dtype (no carry-in buffer for the block update, which reads its fp32 start
-// state directly), and the chunk log2-decays.  The backward pass adds a
+// state directly), the chunk log2-decays, and the chunk Gram tiles C.B^T of
+// both slots (fp32; none for a block update of at most 64 tokens, whose
+// single kernel forms them itself).  The backward pass adds a
 // second chunk-state buffer (A-tangent chunk states, then adjoint chunk
 // states), the
 // A-tangent and adjoint carries (compute dtype), chunk dt sums, the
 // per-token dy.y_d and x.(G_t B_t) values (fp32 [2][Z][L][H]) and the
 // partial sums of the reductions.
 struct WsLayout {
-  size_t states = 0, sin_t = 0, cdecay = 0;
+  size_t states = 0, sin_t = 0, cdecay = 0, gram = 0;
   size_t tstates = 0, sa_t = 0, gin_t = 0, dtsum = 0, ydot = 0, qx = 0, qxs = 0, ddpart = 0, dAintra = 0,
          dAx1 = 0, dAx2 = 0, rpart = 0;
   size_t total = 0;
@@ -77,6 +82,8 @@ WsLayout ws_layout(const bissd_shape_t *s, int op) {
   w.states = take(nst * esz);
   if (op != BISSD_OP_BLOCK) w.sin_t = take(nst * esz);
   w.cdecay = take(cd);
+  if (op != BISSD_OP_BLOCK || s->seqlen > 64)
+    w.gram = take((size_t)(2 * s->batch * nc * s->ngroups) * (size_t)(s->chunk * s->chunk) * 4);
   if (op == BISSD_OP_BACKWARD) {
     const size_t tok = (size_t)(2 * s->batch * s->seqlen * s->nheads) * 4;
     const size_t rb = (size_t)(s->batch * nc * (s->chunk / 64) * s->nheads) * 4;
@@ -225,6 +232,7 @@ static int forward_impl(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, 
   char *ws = (char *)workspace;
   a.states = (void *)(ws + wl.states);
   a.cdecay = (float *)(ws + wl.cdecay);
+  a.gram = (float *)(ws + wl.gram);
   a.nchunks = (int)ceil_div(s->seqlen, s->chunk);
   a.y = y;
   a.dir0 = 0;
@@ -240,9 +248,14 @@ static int forward_impl(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, 
     a.sin_cstride[d] = (int64_t)a.H * PN;
     a.sin_f32[d] = 0;
   }
+  // chunk states, Gram tiles, carry pass, output; phase 3 is the Gram kernel
+  const int order[4][2] = {{0, bissd::PHASE_CHUNK_STATE},
+                           {3, bissd::PHASE_GRAM},
+                           {1, bissd::PHASE_STATE_PASS},
+                           {2, bissd::PHASE_CHUNK_OUT}};
   hipError_t e = hipSuccess;
-  for (int ph = bissd::PHASE_CHUNK_STATE; ph <= bissd::PHASE_CHUNK_OUT && e == hipSuccess; ++ph)
-    if (phase < 0 || phase == ph) e = bissd::launch_scan_phase(a, ph, st);
+  for (int i = 0; i < 4 && e == hipSuccess; ++i)
+    if (phase < 0 || phase == order[i][0]) e = bissd::launch_scan_phase(a, order[i][1], st);
   return finish(e);
 }
 
@@ -256,7 +269,7 @@ int bissd_forward(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, bissd_
 int bissd_forward_phase(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, bissd_dir_t rev,
                         const float *D, const float *init_state, void *y, float *final_state,
                         void *workspace, size_t workspace_bytes, void *stream, int phase) {
-  if (phase < 0 || phase > 2) return BISSD_ERR_UNSUPPORTED;
+  if (phase < 0 || phase > 3) return BISSD_ERR_UNSUPPORTED;
   return forward_impl(s, x, fwd, rev, D, init_state, y, final_state, workspace, workspace_bytes,
                       stream, phase);
 }
@@ -294,6 +307,7 @@ int bissd_block_update(const bissd_shape_t *s, const float *state_in, const void
   char *ws = (char *)workspace;
   a.states = (void *)(ws + wl.states);
   a.cdecay = (float *)(ws + wl.cdecay);
+  a.gram = (float *)(ws + wl.gram);
   a.nchunks = 1;
   a.y = y_blk;
   a.dir0 = 0;
@@ -313,6 +327,7 @@ int bissd_block_update(const bissd_shape_t *s, const float *state_in, const void
   // state_in before the state pass overwrites it
   hipError_t e = hipSuccess;
   if (state_out) e = bissd::launch_scan_phase(a, bissd::PHASE_CHUNK_STATE, st);
+  if (e == hipSuccess) e = bissd::launch_scan_phase(a, bissd::PHASE_GRAM, st);
   if (e == hipSuccess) e = bissd::launch_scan_phase(a, bissd::PHASE_CHUNK_OUT, st);
   if (e == hipSuccess && state_out) e = bissd::launch_scan_phase(a, bissd::PHASE_STATE_PASS, st);
   return finish(e);
@@ -366,6 +381,7 @@ int bissd_backward(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, bissd
   ScanArgs a = base_args(s, x, fwd, rev, D);
   a.states = (void *)(ws + wl.states);
   a.cdecay = (float *)(ws + wl.cdecay);
+  a.gram = (float *)(ws + wl.gram);
   a.nchunks = nc;
   a.dir0 = 0;
   a.ndir = 2;
@@ -419,6 +435,7 @@ int bissd_backward(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, bissd
   yd.out0 = (float *)(ws + wl.ydot);
   yd.slot_dir[0] = 0;
   yd.slot_dir[1] = 1;
+  if (e == hipSuccess) e = bissd::launch_scan_phase(yd, bissd::PHASE_GRAM, st);
   if (e == hipSuccess) e = bissd::launch_scan_phase(yd, bissd::PHASE_YDOT, st);
 
   // dx and x.(G_t B_t): slot 0 (causal) takes the reverse direction's
@@ -442,6 +459,9 @@ int bissd_backward(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, bissd
   q.out3 = (float *)(ws + wl.qxs);
   q.slot_dir[0] = 1;
   q.slot_dir[1] = 0;
+  // the Gram tiles of the swapped operands overwrite the primal ones, which
+  // the dy.y_d launch above has consumed (stream order)
+  if (e == hipSuccess) e = bissd::launch_scan_phase(q, bissd::PHASE_GRAM, st);
   if (e == hipSuccess) e = bissd::launch_scan_phase(q, bissd::PHASE_DX, st);
 
   bissd::BwdArgs b;

@@ -401,6 +401,76 @@ __global__ __launch_bounds__(kThreads) void k2_tangent_pass(ScanArgs a, int PN) 
   }
 }
 
+// ================================================================= Gram
+
+// The output kernel's C.B^T tiles, computed once per (batch, chunk, group)
+// instead of once per head tile.  Workgroup = (batch, chunk, slot d, group,
+// one (row-block j, column block kb) pair on the side slot d reads: kb <= j
+// for d = 0, kb >= j for d = 1); wave w forms the 16 x 64 tile of rows
+// t = 64 j + 16 w + (0..15) and columns s = 64 kb + (0..63).  Lane (r16, g4)
+// holds (C.B^T)[t = 64 j + 16 w + r16][s = 64 kb + 16 u + 4 g4 + i] in
+// accumulator u, element i -- the lane order in which the output kernel's
+// wave needs them -- accumulated over the state dimension in the order that
+// kernel used when it formed them itself.  Rows and columns past the
+// sequence end are zero.
+// Layout: [2][Z][nchunks][G][chunk * chunk] fp32; tile (16-row tile tt,
+// column block kb) at (tt * (chunk / 64) + kb) * 1024, value (u, lane, i) at
+// u * 256 + lane * 4 + i, so every store and load of one accumulator moves a
+// contiguous kilobyte.
+// Work items are grouped so that all the workgroups of one (batch, chunk)
+// run on one XCD and share its L2 copy of the B and C rows.
+template <typename T, int N>
+__global__ __launch_bounds__(kThreads) void k_gram(ScanArgs a) {
+  constexpr int NK = N / 32;
+  constexpr uint32_t ES = sizeof(T);
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, r16 = lane & 15, g4 = lane >> 4;
+  const int Q = a.chunk, NRB = Q / kRB, G = a.G;
+  const int npair = NRB * (NRB + 1) / 2;
+  int item = xcd_linear_id(blockIdx.x, gridDim.x);
+  int pr = item % npair;
+  item /= npair;
+  const int g = item % G;
+  item /= G;
+  const int d = item % 2;
+  item /= 2;
+  const int c = item % a.nchunks, b = item / a.nchunks;
+  // pair index -> (j, kb): row-block j holds j + 1 pairs (d = 0) or NRB - j (d = 1)
+  int j = 0, kb = 0;
+  for (int jj = 0; jj < NRB; ++jj) {
+    const int n = d == 0 ? jj + 1 : NRB - jj;
+    if (pr < n) {
+      j = jj;
+      kb = d == 0 ? pr : jj + pr;
+      break;
+    }
+    pr -= n;
+  }
+  const int64_t L = a.L, t0 = (int64_t)c * Q;
+  const bufres rC = make_buf(reinterpret_cast<const T *>(a.C[d]) + (int64_t)b * L * G * N, (uint32_t)(L * G * N * ES));
+  const bufres rB = make_buf(reinterpret_cast<const T *>(a.B[d]) + (int64_t)b * L * G * N, (uint32_t)(L * G * N * ES));
+  Frag<T> cf[NK], bf[4][NK];
+#pragma unroll
+  for (int ks = 0; ks < NK; ++ks)
+    frag_bload(cf[ks], rC, (uint32_t)((t0 + j * kRB + 16 * w + r16) * G + g) * N * ES + (32 * ks + 8 * g4) * ES);
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks)
+      frag_bload(bf[u][ks], rB, (uint32_t)((t0 + kb * kRB + 16 * u + r16) * G + g) * N * ES + (32 * ks + 8 * g4) * ES);
+  f32x4 cb[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) zero4(cb[u]);
+#pragma unroll
+  for (int ks = 0; ks < NK; ++ks)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) mma(cb[u], bf[u][ks], cf[ks]);
+  f32x4 *out = reinterpret_cast<f32x4 *>(a.gram) +
+               ((((int64_t)d * a.Z + b) * a.nchunks + c) * G + g) * (int64_t)Q * Q / 4 +
+               (int64_t)((4 * j + w) * NRB + kb) * 256 + lane;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) out[u * 64] = cb[u];
+}
+
 // =================================================================== K3
 
 template <typename T, int N, int HT> struct K3Lds {
@@ -416,7 +486,6 @@ template <typename T, int N, int HT> struct K3Lds {
   float bcd[2][kRB];  // B_t . C_t of the row-block's tokens (PHASE_DX)
   union U {
     struct S {
-      T Bs[kRB][BP];
       T Xs[HT][kRB][XPT];
     } s;
     T Sst[HT < 2 ? HT : 2][kP][BP];
@@ -426,10 +495,10 @@ template <typename T, int N, int HT> struct K3Lds {
 
 template <typename T, int N, int HT, bool SF32> struct K3Pf {
   static constexpr int IH = HT < 2 ? HT : 2;  // heads per carry-in / output stage
-  using SB = SlabRows<T, N>;
+  static constexpr int NG = 4;                // 16-byte vectors of one lane's Gram tile
   using SX = SlabRowsScaled<T, kP, K3Lds<T, N, HT>::XPT>;
   using SS = SlabState<T, typename std::conditional<SF32, float, T>::type, N>;
-  static constexpr int SBLK = SB::NV + HT * SX::NV;
+  static constexpr int SBLK = NG + HT * SX::NV;
   static constexpr int NPF = SBLK > IH * SS::NV ? SBLK : IH * SS::NV;
 };
 
@@ -446,6 +515,10 @@ template <typename T, int N, int HT, bool SF32> struct K3Pf {
 // states as stored and applies 2^lam_t to its own small accumulator.  The
 // diagonal slab uses a reference per 16-token tile and is masked
 // elementwise.
+//
+// The C.B^T tiles come precomputed from the Gram kernel, one fp32 16 x 64
+// tile per wave and s-block, already in the lane order of the matrix-core
+// accumulators.
 //
 // Work runs as a pipeline of stages -- the s-blocks, then the carry-in
 // states two heads per stage, forward first, then reverse -- and the global
@@ -476,7 +549,7 @@ __attribute__((amdgpu_waves_per_eu((MODE != 0 && sizeof(T) == 2) ? 2 : 1)))
 void k3_chunk_out(ScanArgs a) {
   using Sm = K3Lds<T, N, HT>;
   using PF = K3Pf<T, N, HT, SF32>;
-  using SB = typename PF::SB;
+  constexpr int NG = PF::NG;
   using SX = typename PF::SX;
   using SS = typename PF::SS;
   using SSrc = typename std::conditional<SF32, float, T>::type;
@@ -504,11 +577,15 @@ void k3_chunk_out(ScanArgs a) {
   // one buffer per batch row: tokens past L read as zero
   const bufres rX = make_buf(reinterpret_cast<const T *>(a.x) + (int64_t)b * L * H * kP,
                              (uint32_t)(L * H * kP * ES));
-  const bufres rB[2] = {
-      make_buf(reinterpret_cast<const T *>(a.B[0]) + (int64_t)b * L * G * N, (uint32_t)(L * G * N * ES)),
-      make_buf(reinterpret_cast<const T *>(a.B[1]) + (int64_t)b * L * G * N, (uint32_t)(L * G * N * ES))};
-  const uint32_t brs_b = (uint32_t)(G * N * ES), xrs_b = (uint32_t)(H * kP * ES);
-  const uint32_t boff = (uint32_t)(t0 * G + gidx) * N * ES;
+  const bufres rC[2] = {
+      make_buf(reinterpret_cast<const T *>(a.C[0]) + (int64_t)b * L * G * N, (uint32_t)(L * G * N * ES)),
+      make_buf(reinterpret_cast<const T *>(a.C[1]) + (int64_t)b * L * G * N, (uint32_t)(L * G * N * ES))};
+  const uint32_t xrs_b = (uint32_t)(H * kP * ES);
+  // this wave's Gram tiles (16-row tile 4 j + w), s-block k at + k * 64 vectors
+  const int64_t gslot = (int64_t)a.Z * a.nchunks * G * Q * Q / 4;
+  const u32x4 *gt0 = reinterpret_cast<const u32x4 *>(a.gram) +
+                     (((int64_t)b * a.nchunks + c) * G + gidx) * (int64_t)Q * Q / 4 +
+                     (int64_t)(4 * j + w) * NRB * 256 + lane;
   const uint32_t xoff = (uint32_t)(t0 * H + h0) * kP * ES;
   const int klast = (qlen - 1) / kRB;
   const bool has_in0 = a.sin[0] != nullptr, has_in1 = a.sin[1] != nullptr;
@@ -516,10 +593,12 @@ void k3_chunk_out(ScanArgs a) {
   u32x4 pf[PF::NPF];
   auto prefetch_sblock = [&](int d, int k) __attribute__((always_inline)) {
     const uint32_t s0 = k * kRB;
-    SB::prefetch(pf, d == 0 ? rB[0] : rB[1], boff + s0 * brs_b, brs_b);
+    const u32x4 *gp = gt0 + d * gslot + k * 256;
+#pragma unroll
+    for (int u = 0; u < NG; ++u) pf[u] = gp[u * 64];
 #pragma unroll
     for (int hh = 0; hh < HT; ++hh)
-      SX::prefetch(pf + SB::NV + hh * SX::NV, rX, xoff + s0 * xrs_b + hh * kP * ES, xrs_b);
+      SX::prefetch(pf + NG + hh * SX::NV, rX, xoff + s0 * xrs_b + hh * kP * ES, xrs_b);
   };
   // carry-in states of heads ih*IH .. ih*IH + IH - 1
   auto prefetch_state = [&](int d, int ih) __attribute__((always_inline)) {
@@ -541,21 +620,13 @@ void k3_chunk_out(ScanArgs a) {
     if (lane == 0) sm.amax[d][hh] = am;
   }
 
-  // C rows of this wave (operand for both C.B^T and the carry-in product),
-  // loaded per direction
+  // C rows of this wave (operand of the carry-in product), loaded per
+  // direction; rows past the sequence end read as zero
   const int trow = j * kRB + 16 * w + r16;
   auto load_c = [&](int d, Frag<T> (&cfd)[NK]) __attribute__((always_inline)) {
-    const T *Cp = reinterpret_cast<const T *>(a.C[d]) + (((int64_t)b * L + t0 + trow) * G + gidx) * N;
 #pragma unroll
-    for (int ks = 0; ks < NK; ++ks) {
-      if (trow < qlen) {
-        float v[8];
-        gload8(v, Cp + 32 * ks + 8 * g4);
-        frag_from(cfd[ks], v);
-      } else {
-        frag_zero(cfd[ks]);
-      }
-    }
+    for (int ks = 0; ks < NK; ++ks)
+      frag_bload(cfd[ks], rC[d], (uint32_t)((t0 + trow) * G + gidx) * N * ES + (32 * ks + 8 * g4) * ES);
   };
   __syncthreads();
 
@@ -617,10 +688,13 @@ void k3_chunk_out(ScanArgs a) {
     for (int k = kb; k <= ke; ++k) {
       const int s0 = k * kRB;
       __syncthreads();
-      SB::commit(&sm.u.s.Bs[0][0], pf);
+      // cb[u]: lane holds (C.B^T)[t = 16w + r16][s = 16u + 4 g4 + i]
+      f32x4 cb[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) cb[u] = __builtin_bit_cast(f32x4, pf[u]);
 #pragma unroll
       for (int hh = 0; hh < HT; ++hh)
-        SX::commit(&sm.u.s.Xs[hh][0][0], pf + SB::NV + hh * SX::NV, &sm.scale[d][hh][s0]);
+        SX::commit(&sm.u.s.Xs[hh][0][0], pf + NG + hh * SX::NV, &sm.scale[d][hh][s0]);
       __syncthreads();
       if (k < ke) prefetch_sblock(d, k + 1);
       else if (d == 0 ? has_in0 : has_in1) prefetch_state(d, 0);
@@ -631,20 +705,6 @@ void k3_chunk_out(ScanArgs a) {
       if (diag) {
         if (d == 0) uhi = w;
         else ulo = w;
-      }
-      // cb[u]: lane holds (C.B^T)[t = 16w + r16][s = 16u + 4 g4 + i]
-      f32x4 cb[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) zero4(cb[u]);
-#pragma unroll
-      for (int ks = 0; ks < NK; ++ks) {
-        Frag<T> bfr[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (u >= ulo && u <= uhi) frag_ld8(bfr[u], &sm.u.s.Bs[16 * u + r16][32 * ks + 8 * g4]);
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (u >= ulo && u <= uhi) mma(cb[u], bfr[u], cfd[ks]);
       }
       if (MODE == 2 && diag && g4 == (r16 >> 2)) {
         // this lane holds the diagonal (row t = 16w + r16, column s = t)
@@ -922,6 +982,12 @@ static void launch_t(const ScanArgs &a, int phase, hipStream_t st) {
       hipLaunchKernelGGL((k1_chunk_state<T, N, HT, 2>), g, dim3(kThreads), 0, st, a);
     else
       hipLaunchKernelGGL((k1_chunk_state<T, N, HT, 3>), g, dim3(kThreads), 0, st, a);
+  } else if (phase == PHASE_GRAM) {
+    // one workgroup per (batch, chunk, slot, group, row-block / column-block
+    // pair on the slot's side)
+    const int nrb = a.chunk / kRB;
+    dim3 g((unsigned)((int64_t)a.Z * a.nchunks * 2 * a.G * (nrb * (nrb + 1) / 2)));
+    hipLaunchKernelGGL((k_gram<T, N>), g, dim3(kThreads), 0, st, a);
   } else if (phase == PHASE_TAN_PASS) {
     const int PN = kP * N;
     dim3 g2((unsigned)(PN / 4 / kThreads), (unsigned)a.H, (unsigned)(a.Z * 2));

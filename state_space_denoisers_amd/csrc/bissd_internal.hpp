@@ -38,6 +38,9 @@ struct ScanArgs {
   const void *states2;   // PHASE_TAN_PASS: tangent chunk states, compute dtype
   const float *dtsum;    // PHASE_TAN_PASS: chunk dt sums
   int slot_dir[2];  // direction under which each output-kernel slot stores out0
+  float *gram;      // per slot: the chunk Gram tiles C.B^T in the output kernel's
+                    // lane order, fp32, [2][Z][nchunks][G][chunk * chunk]; written by
+                    // PHASE_GRAM, read by the output kernel (every mode)
 };
 
 enum {
@@ -51,6 +54,7 @@ enum {
   PHASE_TAN_STATE = 7,    // chunk-local A-tangent states (dt-sum weighted)
   PHASE_TAN_PASS = 8,     // A-tangent carry-in states
   PHASE_ADJ_TAN = 9,      // <dt-sum weighted adjoint chunk state, carry-in state>
+  PHASE_GRAM = 10,        // chunk Gram tiles for the output kernel
 };
 
 hipError_t launch_scan_phase(const ScanArgs &a, int phase, hipStream_t st);

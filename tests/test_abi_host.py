@@ -130,6 +130,34 @@ def test_block_update_validation(lib):
     assert rc == -7
 
 
+def test_forward_phase_range(lib):
+    """Phases 0..3 exist (3 = Gram tiles); any other index is rejected before
+    the shape or a pointer is looked at."""
+    s = shape()
+    for bad in (-1, 4, 100):
+        rc = lib.bissd_forward_phase(C.byref(s), addr(0), dirs(1), dirs(5), addr(9), None,
+                                     addr(10), None, addr(12), C.c_size_t(1 << 40), None, bad)
+        assert rc == -3, bad
+    # a valid phase index still validates the arguments
+    rc = lib.bissd_forward_phase(C.byref(s), None, dirs(1), dirs(5), addr(9), None, addr(10),
+                                 None, addr(12), C.c_size_t(1 << 40), None, 3)
+    assert rc == -1
+
+
+def test_workspace_holds_gram_tiles(lib):
+    """The forward workspace holds both slots' fp32 chunk Gram tiles
+    (2 x batch x chunks x groups x chunk^2 x 4 bytes) besides the states; a
+    block update of at most 64 tokens needs none."""
+    s = shape(seqlen=1024, ngroups=2, nheads=8)
+    n = lib.bissd_workspace_size(C.byref(s), _abi.OP_FORWARD)
+    states = 2 * 2 * 2 * 4 * 8 * 64 * 128 * 2
+    gram = 2 * 2 * 4 * 2 * 256 * 256 * 4
+    assert n >= states + gram
+    small = lib.bissd_workspace_size(C.byref(shape(seqlen=64, chunk=64)), _abi.OP_BLOCK)
+    big = lib.bissd_workspace_size(C.byref(shape(seqlen=65, chunk=128)), _abi.OP_BLOCK)
+    assert big - small >= 2 * 2 * 128 * 128 * 4
+
+
 def test_status_strings(lib):
     for code in _abi.STATUS:
         assert lib.bissd_status_string(code)

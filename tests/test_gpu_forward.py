@@ -12,7 +12,7 @@ import pytest
 
 from oracle import oracle as O
 from synth import gen
-from tests.gpu_util import TOL, gpu_forward, maxrel, select_heads, select_rows
+from tests.gpu_util import TOL, dirs, gpu_forward, host, maxrel, select_heads, select_rows, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -202,3 +202,28 @@ def test_every_decay_zero():
     g = gpu_forward(inp, "fp32", 64)
     assert np.all(np.isfinite(g))
     assert maxrel(g, O.forward(inp)) <= TOL["fp32"]
+
+
+@pytest.mark.parametrize("dtype,L", [("bf16", 1000), ("fp32", 300)])
+def test_phases_compose(dtype, L):
+    """The four phases enqueued one by one in the documented order (chunk
+    states, Gram tiles, carry pass, output) give bissd_forward's y bit for
+    bit, and the output phase alone repeated after them recomputes it."""
+    import torch
+    import state_space_denoisers_amd as ssd
+    w = W["tiny_fp32"].replace(Z=2, L=L, H=4, N=128, chunk=256, dtype=dtype, seed=31)
+    T = to_dev(gen.make_inputs(w), dtype)
+    fwd, rev = dirs(T)
+    full = host(ssd.bissd_forward(T["x"], fwd, rev, T["D"], chunk=256))
+    shape = ssd.shape_of(T["x"], T["B_f"], 256)
+    nws = ssd.bissd_workspace_size(shape, 0)
+    ws = torch.empty(nws, dtype=torch.uint8, device=T["x"].device)
+    y = torch.full_like(T["x"], float("nan"))
+    for p in (0, 3, 1, 2):
+        ssd.bissd_forward_phase(p, T["x"], fwd, rev, T["D"], chunk=256, y=y, workspace=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(y), full)
+    y.fill_(float("nan"))
+    ssd.bissd_forward_phase(2, T["x"], fwd, rev, T["D"], chunk=256, y=y, workspace=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(y), full)
