@@ -545,7 +545,7 @@ template <typename T, int N, int HT, bool SF32> struct K3Pf {
 // the result: dy_t (B_t.C_t) into G_t B_t for dx and x.(G_t B_t).
 template <typename T, int N, int HT, bool SF32, int MODE>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu((MODE != 0 && sizeof(T) == 2) ? 2 : 1)))
+__attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? (MODE != 0 ? 2 : (SF32 ? 1 : 3)) : 1)))
 void k3_chunk_out(ScanArgs a) {
   using Sm = K3Lds<T, N, HT>;
   using PF = K3Pf<T, N, HT, SF32>;
@@ -671,22 +671,32 @@ void k3_chunk_out(ScanArgs a) {
   // (C fragments, masks, accumulators) is indexed statically
   auto run_direction = [&](auto dc) __attribute__((always_inline)) {
     constexpr int d = decltype(dc)::value;
-    const int kb = d == 0 ? 0 : j, ke = d == 0 ? j : klast;
     // MODE 0 prefetches the reverse's first slab during the forward's last
     // stage; the backward modes finish each slot with an epilogue first and
     // issue it here, so the prefetch registers are not live across it
-    if (MODE != 0 && d == 1) prefetch_sblock(1, j);
-    Frag<T> cfd[NK];
-    load_c(d, cfd);
+    if (MODE != 0 && d == 1) prefetch_sblock(1, klast);
     // per-head row factor 2^(lam_t - m) of this lane's Gram row t = 16w + r16,
     // applied to C.B^T before the product with the pre-scaled x
     float ut[HT];
 #pragma unroll
     for (int hh = 0; hh < HT; ++hh)
       ut[hh] = exp2_fast(sm.lam[d][hh][j * kRB + 16 * w + r16] - sm.refb[d][hh]);
-    // ---------------- s-blocks of direction d
-    for (int k = kb; k <= ke; ++k) {
+    // ---------------- s-blocks of direction d.  One stage: commit the
+    // staged x, turn this wave's Gram tile into the masked, decay-weighted
+    // operand mf (so the prefetch registers are free again), issue the next
+    // stage's loads, then multiply with x from LDS.  Both directions visit
+    // their off-diagonal s-blocks first (forward: 0 .. j - 1; reverse:
+    // klast down to j + 1) and the diagonal one (k = j) last, as an instance
+    // of its own: inside the loop the next stage is always an s-block, whose
+    // loads go to the same registers.
+    auto stage = [&](int k, auto diagc) __attribute__((always_inline)) {
+      constexpr bool DIAG = decltype(diagc)::value;
       const int s0 = k * kRB;
+      int ulo = 0, uhi = 3;
+      if (DIAG) {
+        if (d == 0) uhi = w;
+        else ulo = w;
+      }
       __syncthreads();
       // cb[u]: lane holds (C.B^T)[t = 16w + r16][s = 16u + 4 g4 + i]
       f32x4 cb[4];
@@ -695,28 +705,8 @@ void k3_chunk_out(ScanArgs a) {
 #pragma unroll
       for (int hh = 0; hh < HT; ++hh)
         SX::commit(&sm.u.s.Xs[hh][0][0], pf + NG + hh * SX::NV, &sm.scale[d][hh][s0]);
-      __syncthreads();
-      if (k < ke) prefetch_sblock(d, k + 1);
-      else if (d == 0 ? has_in0 : has_in1) prefetch_state(d, 0);
-      else if (d == 0 && MODE == 0) prefetch_sblock(1, j);
-
-      const bool diag = (k == j);
-      int ulo = 0, uhi = 3;
-      if (diag) {
-        if (d == 0) uhi = w;
-        else ulo = w;
-      }
-      if (MODE == 2 && diag && g4 == (r16 >> 2)) {
-        // this lane holds the diagonal (row t = 16w + r16, column s = t)
-        float v = 0.0f;
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int i2 = 0; i2 < 4; ++i2)
-            if (u == w && i2 == (r16 & 3)) v = cb[u][i2];
-        sm.bcd[d][16 * w + r16] = v;
-      }
-      if (!diag) {
+      Frag<T> mf[HT][2];
+      if constexpr (!DIAG) {
 #pragma unroll
         for (int hh = 0; hh < HT; ++hh)
 #pragma unroll
@@ -727,16 +717,19 @@ void k3_chunk_out(ScanArgs a) {
               m[i2] = cb[2 * q][i2] * ut[hh];
               m[4 + i2] = cb[2 * q + 1][i2] * ut[hh];
             }
-            Frag<T> mf;
-            frag_from(mf, m);
-            Frag<T> xf[4];
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-              frag_rows(xf[v], &sm.u.s.Xs[hh][0][0], Sm::XPT, 32 * q + 4 * g4, 32 * q + 16 + 4 * g4, 16 * v);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) mma(acc[hh][v], mf, xf[v]);
+            frag_from(mf[hh][q], m);
           }
       } else {
+        if (MODE == 2 && g4 == (r16 >> 2)) {
+          // this lane holds the diagonal (row t = 16w + r16, column s = t)
+          float v = 0.0f;
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int i2 = 0; i2 < 4; ++i2)
+              if (u == w && i2 == (r16 & 3)) v = cb[u][i2];
+          sm.bcd[d][16 * w + r16] = v;
+        }
 #pragma unroll
         for (int hh = 0; hh < HT; ++hh) {
           const float lt = sm.lam[d][hh][s0 + 16 * w + r16];
@@ -770,22 +763,39 @@ void k3_chunk_out(ScanArgs a) {
               }
               m[e] = ok ? cb[u][i2] * wgt : 0.0f;
             }
-            Frag<T> mf;
-            frag_from(mf, m);
-            Frag<T> xf[4];
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-              frag_rows(xf[v], &sm.u.s.Xs[hh][0][0], Sm::XPT, 32 * q + 4 * g4, 32 * q + 16 + 4 * g4, 16 * v);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) mma(acc[hh][v], mf, xf[v]);
+            frag_from(mf[hh][q], m);
           }
         }
       }
+      __syncthreads();
+      if (!DIAG) prefetch_sblock(d, d == 0 ? k + 1 : k - 1);
+      else if (d == 0 ? has_in0 : has_in1) prefetch_state(d, 0);
+      else if (d == 0 && MODE == 0) prefetch_sblock(1, klast);
+#pragma unroll
+      for (int hh = 0; hh < HT; ++hh)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          if (DIAG && (2 * q + 1 < ulo || 2 * q > uhi)) continue;
+          Frag<T> xf[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            frag_rows(xf[v], &sm.u.s.Xs[hh][0][0], Sm::XPT, 32 * q + 4 * g4, 32 * q + 16 + 4 * g4, 16 * v);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) mma(acc[hh][v], mf[hh][q], xf[v]);
+        }
+    };
+    if constexpr (d == 0) {
+      for (int k = 0; k < j; ++k) stage(k, std::false_type{});
+    } else {
+      for (int k = klast; k > j; --k) stage(k, std::false_type{});
     }
+    stage(j, std::true_type{});
     // ---------------- carry-in term 2^lam_t C S_in^T, IH heads per stage.
     // The states are staged as stored; the row factor 2^lam_t (<= 1) is
     // applied to a transient accumulator per head.
     if (d == 0 ? has_in0 : has_in1) {
+      Frag<T> cfd[NK];
+      load_c(d, cfd);
 #pragma unroll
       for (int ih = 0; ih < HT / IH; ++ih) {
         __syncthreads();
@@ -796,7 +806,7 @@ void k3_chunk_out(ScanArgs a) {
         }
         __syncthreads();
         if (ih + 1 < HT / IH) prefetch_state(d, ih + 1);
-        else if (d == 0 && MODE == 0) prefetch_sblock(1, j);
+        else if (d == 0 && MODE == 0) prefetch_sblock(1, klast);
 #pragma unroll
         for (int q = 0; q < IH; ++q) {
           const int hh = ih * IH + q;
