@@ -52,7 +52,7 @@ __global__ __launch_bounds__(kThreads) void k_block_update(ScanArgs a) {
   __shared__ __attribute__((aligned(16))) char tS[kP * Sm::SRB];
   constexpr int NK = N / 32, NT = N / 16;
   constexpr uint32_t ES = sizeof(T);
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
+  const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
   const int h = blockIdx.x % a.H, b = blockIdx.x / a.H;
   const int H = a.H, G = a.G, gidx = h / (H / G);
   const int L = (int)a.L;  // block length, 1..64

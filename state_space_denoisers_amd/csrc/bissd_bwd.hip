@@ -92,7 +92,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_panel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) char bufA[CSB + STB];
   __shared__ __attribute__((aligned(16))) char bufB[DBUF ? CSB + STB : 16];
   constexpr int NT = N / 16;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
+  const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
   const int Q = a.chunk, NRB = Q / kRB, H = a.H, G = a.G, hpg = H / G;
   const int64_t L = a.L;
   // work item = (((b * nchunks + c) * 2 + d) * G + g) * NRB + j

@@ -500,6 +500,11 @@ __device__ __forceinline__ void frag_bload(Frag<float> &f, bufres r, uint32_t of
   }
 }
 
+// Index of the calling wavefront in its workgroup, as a wave-uniform
+// (scalar) value, so that branches and addresses that depend only on it stay
+// on the scalar unit.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
 // ------------------------------------------------- direct buffer -> LDS slabs
 //
 // gfx950 buffer loads can write LDS directly: each lane's 16 bytes land at
@@ -532,7 +537,7 @@ template <int RB, int SW> struct DmaTile {
   // byte off0 of r, rows rs bytes apart
   __device__ static __forceinline__ void load(char *tile, bufres r, uint32_t off0, uint32_t rs,
                                               int nrows) {
-    const int wv = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int wv = wave_id(), l = threadIdx.x & 63;
     const int np = nrows / RPP;
     for (int p = wv; p < np; p += kThreads / 64) {
       const int y = p * RPP + l / CPR, c = l % CPR;

@@ -68,7 +68,7 @@ __global__ __launch_bounds__(kThreads) void k1_chunk_state(ScanArgs a) {
   using SX = SlabRowsScaled<T, kP, Sm::XPT>;
   __shared__ Sm sm;
   constexpr int NT = N / 64;  // 16-wide column tiles per wave
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
+  const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
   // work item = ((b * nchunks + c) * ndir + dir) * (H / HT) + head tile
   int bx = xcd_linear_id(blockIdx.x, gridDim.x);
   const int h0 = (bx % (a.H / HT)) * HT;
@@ -92,19 +92,36 @@ __global__ __launch_bounds__(kThreads) void k1_chunk_state(ScanArgs a) {
   const uint32_t boff = (uint32_t)(t0 * G + gidx) * N * ES;
   const uint32_t xoff = (uint32_t)(t0 * H + h0) * kP * ES;
 
+  // decay scans, wave w taking head w % HT (waves HT .. 2 HT - 1: the plain
+  // cumulative dt of the tangent modes).  The dt loads go out first, raw and
+  // unconditional (tokens past L read as zero), then the first slab's loads.
+  constexpr bool TAN = MODE >= 2;
+  constexpr int NPR = (TAN ? 2 : 1) * HT;
+  static_assert(NPR <= kThreads / 64, "one decay scan per wave");
+  uint32_t dtraw[4];
+  float Ah = 1.0f;
+  if (w < NPR) {
+    chunk_dt_bload<T>(make_buf(dt + (int64_t)b * L * H, (uint32_t)(L * H * ES)),
+                      (uint32_t)(t0 * H + h0 + w % HT) * ES, (uint32_t)(H * ES), Q, dtraw);
+    if (w < HT) Ah = a.A[d][h0 + w];
+  }
+
   u32x4 pfB[SB::NV], pfX[HT][SX::NV];
   SB::prefetch(pfB, rB, boff, brs);
 #pragma unroll
   for (int hh = 0; hh < HT; ++hh) SX::prefetch(pfX[hh], rX, xoff + hh * kP * ES, xrs);
 
-  constexpr bool TAN = MODE >= 2;
-  for (int pr = w; pr < (TAN ? 2 : 1) * HT; pr += 4) {
-    const int hh = pr % HT;
-    const T *dtp = dt + ((int64_t)b * L + t0) * H + h0 + hh;
-    if (pr < HT)
-      chunk_decay_scan<T>(dtp, H, qlen, Q, a.A[d][h0 + hh] * kLog2e, d == 1, sm.lam[hh], sm.dtv[hh]);
+  if (w < NPR) {
+    const int hh = w % HT;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(dtraw[i]) : : "memory");
+    asm volatile("" : "+v"(Ah) : : "memory");
+    float dv[4];
+    chunk_dt_decode<T>(dtraw, Q, dv);
+    if (w < HT)
+      chunk_decay_scan_vals(dv, Q, Ah * kLog2e, d == 1, sm.lam[hh], sm.dtv[hh]);
     else
-      chunk_decay_scan<T>(dtp, H, qlen, Q, 1.0f, d == 1, sm.cdt[hh], sm.dtv[hh]);
+      chunk_decay_scan_vals(dv, Q, 1.0f, d == 1, sm.cdt[hh], sm.dtv[hh]);
   }
   __syncthreads();
   const int64_t chi = (((int64_t)d * a.Z + b) * a.nchunks + c) * H + h0;  // (d, b, c, h0)
@@ -423,7 +440,7 @@ template <typename T, int N>
 __global__ __launch_bounds__(kThreads) void k_gram(ScanArgs a) {
   constexpr int NK = N / 32;
   constexpr uint32_t ES = sizeof(T);
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, r16 = lane & 15, g4 = lane >> 4;
+  const int w = wave_id(), lane = threadIdx.x & 63, r16 = lane & 15, g4 = lane >> 4;
   const int Q = a.chunk, NRB = Q / kRB, G = a.G;
   const int npair = NRB * (NRB + 1) / 2;
   int item = xcd_linear_id(blockIdx.x, gridDim.x);
@@ -556,7 +573,7 @@ void k3_chunk_out(ScanArgs a) {
   constexpr int IH = PF::IH;
   __shared__ Sm sm;
   constexpr int NK = N / 32;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
+  const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
   const int Q = a.chunk, NRB = Q / kRB, H = a.H, G = a.G;
   const int64_t L = a.L;
   // work item = ((b * nchunks + c) * NRB + j) * (H / HT) + head tile, so all
@@ -609,15 +626,31 @@ void k3_chunk_out(ScanArgs a) {
       SS::prefetch(pf + q * SS::NV, reinterpret_cast<const SSrc *>(a.sin[d]) + off);
     }
   };
+  // ---- decay scans (forward prefix and reverse suffix) for the whole
+  // chunk, wave w taking (direction w / HT, head w % HT).  The dt loads go
+  // out first, raw and unconditional (tokens past L read as zero), then the
+  // first stage's loads, so neither waits for the other.
+  static_assert(2 * HT <= kThreads / 64, "one decay scan per wave");
+  const int pd = w / HT, ph = w % HT;
+  uint32_t dtraw[4];
+  float Ah = 0.0f;
+  if (w < 2 * HT) {
+    chunk_dt_bload<T>(make_buf(reinterpret_cast<const T *>(a.dt[pd]) + (int64_t)b * L * H, (uint32_t)(L * H * ES)),
+                      (uint32_t)(t0 * H + h0 + ph) * ES, (uint32_t)(H * ES), Q, dtraw);
+    Ah = a.A[pd][h0 + ph];
+  }
   prefetch_sblock(0, 0);
-
-  // ---- decay scans (forward prefix and reverse suffix) for the whole chunk
-  for (int pr = w; pr < 2 * HT; pr += 4) {
-    const int d = pr / HT, hh = pr % HT;
-    const float am = chunk_decay_scan<T>(
-        reinterpret_cast<const T *>(a.dt[d]) + ((int64_t)b * L + t0) * H + h0 + hh, H, qlen, Q,
-        a.A[d][h0 + hh] * kLog2e, d == 1, sm.lam[d][hh], sm.scale[d][hh], MODE == 2);
-    if (lane == 0) sm.amax[d][hh] = am;
+  if (w < 2 * HT) {
+    // the empty asm keeps the decode (and so the wait for the dt loads)
+    // behind the stage loads above
+#pragma unroll
+    for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(dtraw[i]) : : "memory");
+    asm volatile("" : "+v"(Ah) : : "memory");
+    float dv[4];
+    chunk_dt_decode<T>(dtraw, Q, dv);
+    const float am = chunk_decay_scan_vals(dv, Q, Ah * kLog2e, pd == 1, sm.lam[pd][ph],
+                                           sm.scale[pd][ph], MODE == 2);
+    if (lane == 0) sm.amax[pd][ph] = am;
   }
 
   // C rows of this wave (operand of the carry-in product), loaded per
