@@ -115,6 +115,16 @@ def event_time_ms(fn, reps):
     return a.elapsed_time(b) / reps
 
 
+def gram_in_chunk_state_kernel(w) -> bool:
+    """The chunk-state kernel forms the Gram tiles itself (and phase 3
+    launches nothing) when every B/C group has a head tile per (row-block,
+    column-block) pair: the rule documented with bissd_forward_phase."""
+    hpg = w.H // w.G
+    ht = 2 if hpg % 2 == 0 else 1
+    nrb = w.chunk // 64
+    return hpg // ht >= nrb * (nrb + 1) // 2
+
+
 def phase_times_us(f: Forward, reps):
     """Average duration of each forward kernel inside complete forward calls:
     every call is enqueued as its four phases with a HIP event recorded
@@ -124,11 +134,15 @@ def phase_times_us(f: Forward, reps):
     f()
     torch.cuda.synchronize()
     s = torch.cuda.current_stream()
-    n = len(PHASE_ORDER)
+    order = [p for p in PHASE_ORDER if not (p == 3 and gram_in_chunk_state_kernel(f.w))]
+    names = dict(PHASE_NAMES)
+    if 3 not in order:
+        names[0] = "k1_chunk_state+gram"
+    n = len(order)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(reps)]
     for r in range(reps):
         evs[r][0].record(s)
-        for i, p in enumerate(PHASE_ORDER):
+        for i, p in enumerate(order):
             f.phase(p)
             evs[r][i + 1].record(s)
     torch.cuda.synchronize()
@@ -136,7 +150,7 @@ def phase_times_us(f: Forward, reps):
     for r in range(reps):
         for i in range(n):
             tot[i] += evs[r][i].elapsed_time(evs[r][i + 1])
-    return {PHASE_NAMES[p]: 1e3 * tot[i] / reps for i, p in enumerate(PHASE_ORDER)}
+    return {names[p]: 1e3 * tot[i] / reps for i, p in enumerate(order)}
 
 
 def per_token_bytes(w):
@@ -446,7 +460,7 @@ def main():
     ph = phase_times_us(f, max(20, args.steps // 4))
     log(f"bench: kernels {ph}")
     dom = max(ph, key=ph.get)
-    pidx = {v: k for k, v in PHASE_NAMES.items()}[dom]
+    pidx = {v: k for k, v in PHASE_NAMES.items()}[dom.split("+")[0]]
     dur_s = ph[dom] * 1e-6
     alg_bytes = phase_bytes_per_token(w, pidx) * tokens
     achieved = alg_bytes / dur_s / 1e9

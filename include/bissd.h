@@ -165,7 +165,11 @@ int bissd_block_update(const bissd_shape_t *shape, const float *state_in,
  * Diagnostics for timing and profiling single kernels: enqueue only one
  * phase of bissd_forward with the same arguments and validation.
  *   phase 0: per-chunk local states and chunk decays (written to workspace)
- *   phase 3: per-chunk Gram tiles C.B^T of both directions (workspace)
+ *   phase 3: per-chunk Gram tiles C.B^T of both directions (workspace);
+ *            nothing to do when phase 0 forms them itself, which it does
+ *            when every B/C group has at least (chunk/64)(chunk/64 + 1)/2
+ *            head tiles (a tile is 2 heads if a group's head count is even,
+ *            else 1)
  *   phase 1: carry pass over chunks (workspace in place; final_state)
  *   phase 2: fused bidirectional output (reads workspace, writes y)
  * bissd_forward runs them in the order 0, 3, 1, 2.  A phase reads what the

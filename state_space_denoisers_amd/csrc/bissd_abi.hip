@@ -233,6 +233,7 @@ static int forward_impl(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, 
   a.states = (void *)(ws + wl.states);
   a.cdecay = (float *)(ws + wl.cdecay);
   a.gram = (float *)(ws + wl.gram);
+  a.gram_k1 = bissd::gram_in_k1(a.H, a.G, a.chunk) ? 1 : 0;
   a.nchunks = (int)ceil_div(s->seqlen, s->chunk);
   a.y = y;
   a.dir0 = 0;
@@ -248,14 +249,17 @@ static int forward_impl(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, 
     a.sin_cstride[d] = (int64_t)a.H * PN;
     a.sin_f32[d] = 0;
   }
-  // chunk states, Gram tiles, carry pass, output; phase 3 is the Gram kernel
+  // chunk states, Gram tiles (phase 3; formed by the chunk-state kernel
+  // itself when the head tiles suffice), carry pass, output
   const int order[4][2] = {{0, bissd::PHASE_CHUNK_STATE},
                            {3, bissd::PHASE_GRAM},
                            {1, bissd::PHASE_STATE_PASS},
                            {2, bissd::PHASE_CHUNK_OUT}};
   hipError_t e = hipSuccess;
-  for (int i = 0; i < 4 && e == hipSuccess; ++i)
+  for (int i = 0; i < 4 && e == hipSuccess; ++i) {
+    if (order[i][1] == bissd::PHASE_GRAM && a.gram_k1) continue;
     if (phase < 0 || phase == order[i][0]) e = bissd::launch_scan_phase(a, order[i][1], st);
+  }
   return finish(e);
 }
 
@@ -382,6 +386,7 @@ int bissd_backward(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, bissd
   a.states = (void *)(ws + wl.states);
   a.cdecay = (float *)(ws + wl.cdecay);
   a.gram = (float *)(ws + wl.gram);
+  a.gram_k1 = bissd::gram_in_k1(a.H, a.G, a.chunk) ? 1 : 0;
   a.nchunks = nc;
   a.dir0 = 0;
   a.ndir = 2;
@@ -435,7 +440,8 @@ int bissd_backward(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, bissd
   yd.out0 = (float *)(ws + wl.ydot);
   yd.slot_dir[0] = 0;
   yd.slot_dir[1] = 1;
-  if (e == hipSuccess) e = bissd::launch_scan_phase(yd, bissd::PHASE_GRAM, st);
+  // the primal Gram tiles: from the chunk-state launch above, or here
+  if (e == hipSuccess && !a.gram_k1) e = bissd::launch_scan_phase(yd, bissd::PHASE_GRAM, st);
   if (e == hipSuccess) e = bissd::launch_scan_phase(yd, bissd::PHASE_YDOT, st);
 
   // dx and x.(G_t B_t): slot 0 (causal) takes the reverse direction's

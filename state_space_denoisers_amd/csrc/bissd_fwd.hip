@@ -30,6 +30,23 @@
 
 namespace bissd {
 
+// Gram tile pairs: for slot d, the (row-block j, column-block kb) pairs of
+// one chunk that the output kernel reads (kb <= j for d = 0, kb >= j for
+// d = 1), numbered row-block by row-block.
+__device__ __forceinline__ void gram_pair(int pr, int d, int NRB, int &j, int &kb) {
+  j = 0;
+  kb = 0;
+  for (int jj = 0; jj < NRB; ++jj) {
+    const int n = d == 0 ? jj + 1 : NRB - jj;
+    if (pr < n) {
+      j = jj;
+      kb = d == 0 ? pr : jj + pr;
+      return;
+    }
+    pr -= n;
+  }
+}
+
 // =================================================================== K1
 
 template <typename T, int N, int HT> struct K1Lds {
@@ -61,8 +78,15 @@ template <typename T, int N, int HT> struct K1Lds {
 // states[d][b][c][h][p][n] (compute dtype, rounded once from the fp32
 // accumulators), cdecay[d][b][c][h].  Wave w owns state
 // columns n in [w N/4, (w+1) N/4).
+// With gram_k1 (MODE 0 over both directions) the workgroup of head tile tg
+// within its B/C group also forms the Gram tiles of pair tg of its direction
+// (the output kernel's C.B^T, as the Gram kernel below lays them out) while
+// the pair's B slab is in LDS; the host sets it only when every pair has a
+// workgroup.
 template <typename T, int N, int HT, int MODE>
-__global__ __launch_bounds__(kThreads) void k1_chunk_state(ScanArgs a) {
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu((MODE == 0 && sizeof(T) == 2) ? 3 : 1)))
+void k1_chunk_state(ScanArgs a) {
   using Sm = K1Lds<T, N, HT>;
   using SB = SlabRows<T, N, Sm::BPT>;
   using SX = SlabRowsScaled<T, kP, Sm::XPT>;
@@ -98,6 +122,20 @@ __global__ __launch_bounds__(kThreads) void k1_chunk_state(ScanArgs a) {
   constexpr bool TAN = MODE >= 2;
   constexpr int NPR = (TAN ? 2 : 1) * HT;
   static_assert(NPR <= kThreads / 64, "one decay scan per wave");
+  // Gram pair of this workgroup and the C rows of its row-block (raw loads,
+  // first in the queue)
+  const int NRB = Q / kRB, tpg = (H / G) / HT, tg = (h0 / HT) % tpg;
+  const bool do_gram = MODE == 0 && a.gram_k1 && tg < NRB * (NRB + 1) / 2;
+  int gj = 0, gkb = -1;
+  Frag<T> gcf[N / 32];
+  if (do_gram) {
+    gram_pair(tg, d, NRB, gj, gkb);
+    const bufres rC = make_buf(reinterpret_cast<const T *>(a.C[d]) + (int64_t)b * L * G * N,
+                               (uint32_t)(L * G * N * ES));
+#pragma unroll
+    for (int ks = 0; ks < N / 32; ++ks)
+      frag_bload(gcf[ks], rC, (uint32_t)((t0 + gj * kRB + 16 * w + r16) * G + gidx) * N * ES + (32 * ks + 8 * g4) * ES);
+  }
   uint32_t dtraw[4];
   float Ah = 1.0f;
   if (w < NPR) {
@@ -165,6 +203,26 @@ __global__ __launch_bounds__(kThreads) void k1_chunk_state(ScanArgs a) {
       SB::prefetch(pfB, rB, boff + s1 * brs, brs);
 #pragma unroll
       for (int hh = 0; hh < HT; ++hh) SX::prefetch(pfX[hh], rX, xoff + s1 * xrs + hh * kP * ES, xrs);
+    }
+    if (do_gram && k == gkb) {
+      // Gram tile rows 64 gj + 16 w + (0..15), columns of this slab, in the
+      // Gram kernel's order of accumulation and layout
+      f32x4 cb[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) zero4(cb[u]);
+#pragma unroll
+      for (int ks = 0; ks < N / 32; ++ks)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          Frag<T> bq;
+          frag_ld8(bq, &sm.Bs[16 * u + r16][32 * ks + 8 * g4]);
+          mma(cb[u], bq, gcf[ks]);
+        }
+      f32x4 *go = reinterpret_cast<f32x4 *>(a.gram) +
+                  ((((int64_t)d * a.Z + b) * a.nchunks + c) * G + gidx) * (int64_t)Q * Q / 4 +
+                  (int64_t)((4 * gj + w) * NRB + gkb) * 256 + lane;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) go[u * 64] = cb[u];
     }
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -451,17 +509,8 @@ __global__ __launch_bounds__(kThreads) void k_gram(ScanArgs a) {
   const int d = item % 2;
   item /= 2;
   const int c = item % a.nchunks, b = item / a.nchunks;
-  // pair index -> (j, kb): row-block j holds j + 1 pairs (d = 0) or NRB - j (d = 1)
-  int j = 0, kb = 0;
-  for (int jj = 0; jj < NRB; ++jj) {
-    const int n = d == 0 ? jj + 1 : NRB - jj;
-    if (pr < n) {
-      j = jj;
-      kb = d == 0 ? pr : jj + pr;
-      break;
-    }
-    pr -= n;
-  }
+  int j, kb;
+  gram_pair(pr, d, NRB, j, kb);
   const int64_t L = a.L, t0 = (int64_t)c * Q;
   const bufres rC = make_buf(reinterpret_cast<const T *>(a.C[d]) + (int64_t)b * L * G * N, (uint32_t)(L * G * N * ES));
   const bufres rB = make_buf(reinterpret_cast<const T *>(a.B[d]) + (int64_t)b * L * G * N, (uint32_t)(L * G * N * ES));
@@ -1057,6 +1106,11 @@ template <typename T, int N>
 static void launch_n(const ScanArgs &a, int phase, hipStream_t st, int HT) {
   if (HT == 2) launch_t<T, N, 2>(a, phase, st);
   else launch_t<T, N, 1>(a, phase, st);
+}
+
+bool gram_in_k1(int H, int G, int chunk) {
+  const int hpg = H / G, HT = hpg % 2 == 0 ? 2 : 1, nrb = chunk / kRB;
+  return hpg / HT >= nrb * (nrb + 1) / 2;
 }
 
 hipError_t launch_scan_phase(const ScanArgs &a, int phase, hipStream_t st) {

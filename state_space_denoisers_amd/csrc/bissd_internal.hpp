@@ -40,7 +40,10 @@ struct ScanArgs {
   int slot_dir[2];  // direction under which each output-kernel slot stores out0
   float *gram;      // per slot: the chunk Gram tiles C.B^T in the output kernel's
                     // lane order, fp32, [2][Z][nchunks][G][chunk * chunk]; written by
-                    // PHASE_GRAM, read by the output kernel (every mode)
+                    // PHASE_GRAM (or by PHASE_CHUNK_STATE when gram_k1 is set), read
+                    // by the output kernel (every mode)
+  int gram_k1;      // PHASE_CHUNK_STATE over both directions also writes the Gram
+                    // tiles (set by the host when gram_in_k1() holds)
 };
 
 enum {
@@ -58,6 +61,10 @@ enum {
 };
 
 hipError_t launch_scan_phase(const ScanArgs &a, int phase, hipStream_t st);
+// True if the chunk-state kernel can form every Gram tile itself: each of
+// its workgroups takes one (row-block, column-block) pair of its direction,
+// so a group needs at least as many head tiles as there are pairs.
+bool gram_in_k1(int H, int G, int chunk);
 
 // Whole block update (both directions, skip, optional committed state) in
 // one launch, for blocks of at most 64 tokens: x, dt, A, B, C, D, y as in
