@@ -812,40 +812,61 @@ void k3_chunk_out(ScanArgs a) {
               if (u == w && i2 == (r16 & 3)) v = cb[u][i2];
           sm.bcd[d][16 * w + r16] = v;
         }
+        // this lane's mask on the diagonal 16 x 16 tile (u == w): causal
+        // side of the direction, strict in the backward modes
+        bool lm[4];
 #pragma unroll
-        for (int hh = 0; hh < HT; ++hh) {
-          const float lt = sm.lam[d][hh][s0 + 16 * w + r16];
-          float f[4];
+        for (int i2 = 0; i2 < 4; ++i2) {
+          const int sc = 4 * g4 + i2;
+          lm[i2] = MODE == 0 ? (d == 0 ? sc <= r16 : sc >= r16) : (d == 0 ? sc < r16 : sc > r16);
+        }
+        // masked positions are selected away, never multiplied by a 0/1
+        // mask: a large factor must not meet a 0 as 0 * inf.  Tiles u outside
+        // [ulo, uhi] get the factor 0 (C.B^T is finite).
+        if (!exact) {
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const float ru = d == 0 ? sm.lam[0][hh][s0 + 16 * u + 15] : sm.lam[1][hh][s0 + 16 * u];
-            f[u] = (u >= ulo && u <= uhi && !exact) ? exp2_fast(fminf(lt - ru, 120.0f)) : 0.0f;
-          }
+          for (int hh = 0; hh < HT; ++hh) {
+            const float lt = sm.lam[d][hh][s0 + 16 * w + r16];
+            float f[4];
 #pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            if (2 * q + 1 < ulo || 2 * q > uhi) continue;
-            float m[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int u = 2 * q + (e >> 2), i2 = e & 3;
-              float wgt;
-              if (exact) {
-                const int sl = 16 * u + 4 * g4 + i2;
-                wgt = exp2_fast(fminf(lt - sm.lam[d][hh][s0 + sl], 0.0f)) *
-                      (MODE == 2 ? 1.0f : sm.dtd[d][hh][sl]);
-              } else {
-                wgt = f[u];
-              }
-              // select, never multiply by a 0/1 mask: masked positions must
-              // not turn a large factor into 0 * inf
-              bool ok = (u >= ulo && u <= uhi);
-              if (u == w) {
-                if (MODE == 0) ok = ok && (d == 0 ? (4 * g4 + i2 <= r16) : (4 * g4 + i2 >= r16));
-                else ok = ok && (d == 0 ? (4 * g4 + i2 < r16) : (4 * g4 + i2 > r16));
-              }
-              m[e] = ok ? cb[u][i2] * wgt : 0.0f;
+            for (int u = 0; u < 4; ++u) {
+              const float ru = d == 0 ? sm.lam[0][hh][s0 + 16 * u + 15] : sm.lam[1][hh][s0 + 16 * u];
+              const float fu = exp2_fast(fminf(lt - ru, 120.0f));
+              f[u] = (u >= ulo && u <= uhi) ? fu : 0.0f;
             }
-            frag_from(mf[hh][q], m);
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              if (2 * q + 1 < ulo || 2 * q > uhi) continue;
+              float m[8];
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const int u = 2 * q + (e >> 2), i2 = e & 3;
+                const float v = cb[u][i2] * f[u];
+                m[e] = (u == w && !lm[i2]) ? 0.0f : v;
+              }
+              frag_from(mf[hh][q], m);
+            }
+          }
+        } else {
+          // exact per-element weights 2^(lam_t - lam_s) dt_s (x staged unscaled)
+#pragma unroll
+          for (int hh = 0; hh < HT; ++hh) {
+            const float lt = sm.lam[d][hh][s0 + 16 * w + r16];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              if (2 * q + 1 < ulo || 2 * q > uhi) continue;
+              float m[8];
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const int u = 2 * q + (e >> 2), i2 = e & 3;
+                const int sl = 16 * u + 4 * g4 + i2;
+                const float wgt = exp2_fast(fminf(lt - sm.lam[d][hh][s0 + sl], 0.0f)) *
+                                  (MODE == 2 ? 1.0f : sm.dtd[d][hh][sl]);
+                const bool ok = (u >= ulo && u <= uhi) && !(u == w && !lm[i2]);
+                m[e] = ok ? cb[u][i2] * wgt : 0.0f;
+              }
+              frag_from(mf[hh][q], m);
+            }
           }
         }
       }
