@@ -544,7 +544,7 @@ template <typename T, int N, int HT> struct K3Lds {
   static constexpr int XPT = TrPitch<T, kP>::value; // k-along-rows tile
   static constexpr int OP = kP + 4;
   float lam[2][HT][kQmax];
-  float scale[2][HT][kQmax];  // holds dt until the scales are formed
+  alignas(16) float scale[2][HT][kQmax];  // holds dt until the scales are formed
   float dtd[2][HT][kRB];      // dt of the diagonal block (exact path)
   float refb[2][HT];
   float amax[2][HT];
@@ -562,7 +562,7 @@ template <typename T, int N, int HT> struct K3Lds {
 template <typename T, int N, int HT, bool SF32> struct K3Pf {
   static constexpr int IH = HT < 2 ? HT : 2;  // heads per carry-in / output stage
   static constexpr int NG = 4;                // 16-byte vectors of one lane's Gram tile
-  using SX = SlabRowsScaled<T, kP, K3Lds<T, N, HT>::XPT>;
+  using SX = SlabRows<T, kP, K3Lds<T, N, HT>::XPT>;
   using SS = SlabState<T, typename std::conditional<SF32, float, T>::type, N>;
   static constexpr int SBLK = NG + HT * SX::NV;
   static constexpr int NPF = SBLK > IH * SS::NV ? SBLK : IH * SS::NV;
@@ -575,9 +575,10 @@ template <typename T, int N, int HT, bool SF32> struct K3Pf {
 // factored form around a per-head reference m (forward: lam at the token
 // before the row-block; reverse: rho at the token after it):
 //   2^(lam_t - lam_s) = 2^(lam_t - m) * 2^(m - lam_s),
-// both factors <= 1: x is staged pre-multiplied by dt_s 2^(m - lam_s) and
-// each lane multiplies its C.B^T values by the row factor of its row t
-// before they feed the matrix cores.  The carry-in term 2^lam_t C S_in^T uses the
+// both factors <= 1: each lane multiplies its C.B^T values by the row
+// factor 2^(lam_t - m) of its row t and by the column factor
+// dt_s 2^(m - lam_s) of each column s before they feed the matrix cores,
+// with x staged as stored.  The carry-in term 2^lam_t C S_in^T uses the
 // states as stored and applies 2^lam_t to its own small accumulator.  The
 // diagonal slab uses a reference per 16-token tile and is masked
 // elementwise.
@@ -723,7 +724,7 @@ void k3_chunk_out(ScanArgs a) {
   }
   // The factored diagonal slab multiplies by 2^(lam_t - lam_end) <= 2^(15 max|a|)
   // on one side; chunks whose decays could overflow that take the exact
-  // per-element path instead (x staged unscaled, full 2^(lam_t - lam_s) dt_s
+  // per-element path instead (column factor 1, full 2^(lam_t - lam_s) dt_s
   // per element).
   bool exact = false;
 #pragma unroll
@@ -758,7 +759,7 @@ void k3_chunk_out(ScanArgs a) {
     // issue it here, so the prefetch registers are not live across it
     if (MODE != 0 && d == 1) prefetch_sblock(1, klast);
     // per-head row factor 2^(lam_t - m) of this lane's Gram row t = 16w + r16,
-    // applied to C.B^T before the product with the pre-scaled x
+    // applied to C.B^T together with the column factors
     float ut[HT];
 #pragma unroll
     for (int hh = 0; hh < HT; ++hh)
@@ -785,22 +786,31 @@ void k3_chunk_out(ScanArgs a) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) cb[u] = __builtin_bit_cast(f32x4, pf[u]);
 #pragma unroll
-      for (int hh = 0; hh < HT; ++hh)
-        SX::commit(&sm.u.s.Xs[hh][0][0], pf + NG + hh * SX::NV, &sm.scale[d][hh][s0]);
+      for (int hh = 0; hh < HT; ++hh) SX::commit(&sm.u.s.Xs[hh][0][0], pf + NG + hh * SX::NV);
+      // column factors (the staged operand's per-token scale) of this lane's
+      // 16 columns s = s0 + 16 u + 4 g4 + i
+      auto col_scale = [&](int hh, f32x4 (&sc)[4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          sc[u] = *reinterpret_cast<const f32x4 *>(&sm.scale[d][hh][s0 + 16 * u + 4 * g4]);
+      };
       Frag<T> mf[HT][2];
       if constexpr (!DIAG) {
 #pragma unroll
-        for (int hh = 0; hh < HT; ++hh)
+        for (int hh = 0; hh < HT; ++hh) {
+          f32x4 sc[4];
+          col_scale(hh, sc);
 #pragma unroll
           for (int q = 0; q < 2; ++q) {
             float m[8];
 #pragma unroll
             for (int i2 = 0; i2 < 4; ++i2) {
-              m[i2] = cb[2 * q][i2] * ut[hh];
-              m[4 + i2] = cb[2 * q + 1][i2] * ut[hh];
+              m[i2] = cb[2 * q][i2] * (ut[hh] * sc[2 * q][i2]);
+              m[4 + i2] = cb[2 * q + 1][i2] * (ut[hh] * sc[2 * q + 1][i2]);
             }
             frag_from(mf[hh][q], m);
           }
+        }
       } else {
         if (MODE == 2 && g4 == (r16 >> 2)) {
           // this lane holds the diagonal (row t = 16w + r16, column s = t)
@@ -834,6 +844,8 @@ void k3_chunk_out(ScanArgs a) {
               const float fu = exp2_fast(fminf(lt - ru, 120.0f));
               f[u] = (u >= ulo && u <= uhi) ? fu : 0.0f;
             }
+            f32x4 sc[4];
+            col_scale(hh, sc);
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
               if (2 * q + 1 < ulo || 2 * q > uhi) continue;
@@ -841,14 +853,14 @@ void k3_chunk_out(ScanArgs a) {
 #pragma unroll
               for (int e = 0; e < 8; ++e) {
                 const int u = 2 * q + (e >> 2), i2 = e & 3;
-                const float v = cb[u][i2] * f[u];
+                const float v = cb[u][i2] * (f[u] * sc[u][i2]);
                 m[e] = (u == w && !lm[i2]) ? 0.0f : v;
               }
               frag_from(mf[hh][q], m);
             }
           }
         } else {
-          // exact per-element weights 2^(lam_t - lam_s) dt_s (x staged unscaled)
+          // exact per-element weights 2^(lam_t - lam_s) dt_s (column factor 1)
 #pragma unroll
           for (int hh = 0; hh < HT; ++hh) {
             const float lt = sm.lam[d][hh][s0 + 16 * w + r16];
