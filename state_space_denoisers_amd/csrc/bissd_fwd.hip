@@ -700,7 +700,30 @@ void k3_chunk_out(ScanArgs a) {
     chunk_dt_decode<T>(dtraw, Q, dv);
     const float am = chunk_decay_scan_vals(dv, Q, Ah * kLog2e, pd == 1, sm.lam[pd][ph],
                                            sm.scale[pd][ph], MODE == 2);
-    if (lane == 0) sm.amax[pd][ph] = am;
+    // The same wave (its LDS accesses complete in order) then forms this
+    // pair's references and column factors: the row-block reference m
+    // (forward: lam at the token before the row-block; reverse: rho at the
+    // token after it), dt of the diagonal block, and for every token s the
+    // factor dt_s 2^(ref - lam_s) (no dt in the dx pass), ref = m off the
+    // diagonal block and the 16-token tile's end (forward) or start
+    // (reverse) on it.
+    const float *lm = sm.lam[pd][ph];
+    float *sc = sm.scale[pd][ph];
+    const float rb = pd == 0 ? (j > 0 ? lm[j * kRB - 1] : 0.0f) : ((j + 1) * kRB < Q ? lm[(j + 1) * kRB] : 0.0f);
+    if (lane == 0) {
+      sm.amax[pd][ph] = am;
+      sm.refb[pd][ph] = rb;
+    }
+    sm.dtd[pd][ph][lane] = sc[j * kRB + lane];
+#pragma unroll
+    for (int m = 0; m < kQmax / kRB; ++m) {
+      if (m * kRB >= Q) break;
+      const int s2 = m * kRB + lane;
+      const float ref = m == j ? (pd == 0 ? lm[s2 | 15] : lm[s2 & ~15]) : rb;
+      const float dv = sc[s2];
+      const float e = exp2_fast(ref - lm[s2]);
+      sc[s2] = MODE == 2 ? e : (dv != 0.0f ? dv * e : 0.0f);
+    }
   }
 
   // C rows of this wave (operand of the carry-in product), loaded per
@@ -713,15 +736,6 @@ void k3_chunk_out(ScanArgs a) {
   };
   __syncthreads();
 
-  if (tid < 2 * HT) {
-    const int d = tid / HT, hh = tid % HT;
-    sm.refb[d][hh] = d == 0 ? (j > 0 ? sm.lam[0][hh][j * kRB - 1] : 0.0f)
-                            : ((j + 1) * kRB < Q ? sm.lam[1][hh][(j + 1) * kRB] : 0.0f);
-  }
-  for (int it = tid; it < 2 * HT * kRB; it += kThreads) {
-    const int d = it / (HT * kRB), hh = (it / kRB) % HT, sl = it % kRB;
-    sm.dtd[d][hh][sl] = sm.scale[d][hh][j * kRB + sl];
-  }
   // The factored diagonal slab multiplies by 2^(lam_t - lam_end) <= 2^(15 max|a|)
   // on one side; chunks whose decays could overflow that take the exact
   // per-element path instead (column factor 1, full 2^(lam_t - lam_s) dt_s
@@ -731,18 +745,6 @@ void k3_chunk_out(ScanArgs a) {
   for (int d = 0; d < 2; ++d)
 #pragma unroll
     for (int hh = 0; hh < HT; ++hh) exact = exact || (sm.amax[d][hh] >= 8.0f);
-  __syncthreads();
-  for (int it = tid; it < 2 * HT * Q; it += kThreads) {
-    const int d = it / (HT * Q), hh = (it / Q) % HT, s = it % Q;
-    const bool dg = (s / kRB) == j;
-    const float ref = dg ? (d == 0 ? sm.lam[0][hh][s | 15] : sm.lam[1][hh][s & ~15]) : sm.refb[d][hh];
-    const float dv = sm.scale[d][hh][s];
-    float v;
-    if (dg && exact) v = 1.0f;
-    else if (MODE == 2) v = exp2_fast(ref - sm.lam[d][hh][s]);
-    else v = dv != 0.0f ? dv * exp2_fast(ref - sm.lam[d][hh][s]) : 0.0f;
-    sm.scale[d][hh][s] = v;
-  }
 
   f32x4 acc[HT][4];
 #pragma unroll
