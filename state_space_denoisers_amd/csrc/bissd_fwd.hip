@@ -165,8 +165,9 @@ void k1_chunk_state(ScanArgs a) {
   const int64_t chi = (((int64_t)d * a.Z + b) * a.nchunks + c) * H + h0;  // (d, b, c, h0)
   if (MODE == 0 && tid < HT) a.cdecay[chi + tid] = d == 0 ? sm.lam[tid][Q - 1] : sm.lam[tid][0];
   if (MODE == 2 && tid < HT) a.out1[chi + tid] = d == 0 ? sm.cdt[tid][Q - 1] : sm.cdt[tid][0];
+  const int lq = 31 - __builtin_clz(Q);  // the chunk length is a power of two
   for (int it = tid; it < HT * Q; it += kThreads) {
-    const int hh = it / Q, s = it % Q;
+    const int hh = it >> lq, s = it & (Q - 1);
     const float ref = d == 0 ? sm.lam[hh][Q - 1] : sm.lam[hh][0];
     const float dv = sm.dtv[hh][s];
     float v;
@@ -655,7 +656,12 @@ void k3_chunk_out(ScanArgs a) {
                      (int64_t)(4 * j + w) * NRB * 256 + lane;
   const uint32_t xoff = (uint32_t)(t0 * H + h0) * kP * ES;
   const int klast = (qlen - 1) / kRB;
-  const bool has_in0 = a.sin[0] != nullptr, has_in1 = a.sin[1] != nullptr;
+  // carry-in terms that can be nonzero: slot 0's carry starts from zero at
+  // chunk 0 (the forward scan unless it continues from an initial state;
+  // the reverse direction's adjoint in the dx pass), slot 1's at the last
+  // chunk (the reverse scan; the forward direction's adjoint)
+  const bool has_in0 = a.sin[0] != nullptr && (c > 0 || (MODE != 2 && a.init_state != nullptr));
+  const bool has_in1 = a.sin[1] != nullptr && c < a.nchunks - 1;
 
   u32x4 pf[PF::NPF];
   auto prefetch_sblock = [&](int d, int k) __attribute__((always_inline)) {
