@@ -94,17 +94,18 @@ void k1_chunk_state(ScanArgs a) {
   constexpr int NT = N / 64;  // 16-wide column tiles per wave
   const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
   // work item = ((b * nchunks + c) * ndir + dir) * (H / HT) + head tile
-  int bx = xcd_linear_id(blockIdx.x, gridDim.x);
-  const int h0 = (bx % (a.H / HT)) * HT;
-  bx /= a.H / HT;
-  const int d = a.dir0 + bx % a.ndir;
-  bx /= a.ndir;
-  const int c = bx % a.nchunks, b = bx / a.nchunks;
+  uint32_t bx = (uint32_t)xcd_linear_id(blockIdx.x, gridDim.x), rem;
+  bx = a.fd_tiles.divmod(bx, rem);
+  const int h0 = (int)rem * HT;
+  const int d = a.dir0 + (a.ndir == 2 ? (int)(bx & 1) : 0);
+  bx = a.ndir == 2 ? bx >> 1 : bx;
+  bx = a.fd_nc.divmod(bx, rem);
+  const int c = (int)rem, b = (int)bx;
   const int Q = a.chunk, H = a.H, G = a.G;
   const int64_t L = a.L;
   const int64_t t0 = (int64_t)c * Q;
   const int qlen = (int)((L - t0) < Q ? (L - t0) : Q);
-  const int gidx = h0 / (H / G);
+  const int gidx = (int)a.fd_hpg.div((uint32_t)h0);
   const T *dt = reinterpret_cast<const T *>(a.dt[d]);
   constexpr uint32_t ES = sizeof(T);
   // one buffer per batch row: tokens past L read as zero
@@ -124,7 +125,7 @@ void k1_chunk_state(ScanArgs a) {
   static_assert(NPR <= kThreads / 64, "one decay scan per wave");
   // Gram pair of this workgroup and the C rows of its row-block (raw loads,
   // first in the queue)
-  const int NRB = Q / kRB, tpg = (H / G) / HT, tg = (h0 / HT) % tpg;
+  const int NRB = Q / kRB, tpg = (H / G) / HT, tg = h0 / HT - gidx * tpg;
   const bool do_gram = MODE == 0 && a.gram_k1 && tg < NRB * (NRB + 1) / 2;
   int gj = 0, gkb = -1;
   Frag<T> gcf[N / 32];
@@ -501,15 +502,14 @@ __global__ __launch_bounds__(kThreads) void k_gram(ScanArgs a) {
   constexpr uint32_t ES = sizeof(T);
   const int w = wave_id(), lane = threadIdx.x & 63, r16 = lane & 15, g4 = lane >> 4;
   const int Q = a.chunk, NRB = Q / kRB, G = a.G;
-  const int npair = NRB * (NRB + 1) / 2;
-  int item = xcd_linear_id(blockIdx.x, gridDim.x);
-  int pr = item % npair;
-  item /= npair;
-  const int g = item % G;
-  item /= G;
-  const int d = item % 2;
-  item /= 2;
-  const int c = item % a.nchunks, b = item / a.nchunks;
+  uint32_t item = (uint32_t)xcd_linear_id(blockIdx.x, gridDim.x), rem;
+  item = a.fd_pairs.divmod(item, rem);
+  const int pr = (int)rem;
+  item = a.fd_g.divmod(item, rem);
+  const int g = (int)rem;
+  const int d = (int)(item & 1);
+  item = a.fd_nc.divmod(item >> 1, rem);
+  const int c = (int)rem, b = (int)item;
   int j, kb;
   gram_pair(pr, d, NRB, j, kb);
   const int64_t L = a.L, t0 = (int64_t)c * Q;
@@ -629,16 +629,17 @@ void k3_chunk_out(ScanArgs a) {
   const int64_t L = a.L;
   // work item = ((b * nchunks + c) * NRB + j) * (H / HT) + head tile, so all
   // workgroups of one chunk run back to back on one XCD
-  int bx = xcd_linear_id(blockIdx.x, gridDim.x);
-  const int h0 = (bx % (H / HT)) * HT;
-  bx /= H / HT;
-  const int j = bx % NRB;
-  bx /= NRB;
-  const int c = bx % a.nchunks, b = bx / a.nchunks;
+  uint32_t bx = (uint32_t)xcd_linear_id(blockIdx.x, gridDim.x), rem;
+  bx = a.fd_tiles.divmod(bx, rem);
+  const int h0 = (int)rem * HT;
+  const int j = (int)(bx & (uint32_t)(NRB - 1));  // NRB is 1, 2 or 4
+  bx >>= __builtin_ctz((unsigned)NRB);
+  bx = a.fd_nc.divmod(bx, rem);
+  const int c = (int)rem, b = (int)bx;
   const int64_t t0 = (int64_t)c * Q;
   const int qlen = (int)((L - t0) < Q ? (L - t0) : Q);
   if (j * kRB >= qlen) return;
-  const int gidx = h0 / (H / G);
+  const int gidx = (int)a.fd_hpg.div((uint32_t)h0);
   const T *xg = reinterpret_cast<const T *>(a.x) + (((int64_t)b * L + t0) * H + h0) * kP;
   const int64_t xrs = (int64_t)H * kP;
   constexpr uint32_t ES = sizeof(T);
@@ -1154,12 +1155,18 @@ bool gram_in_k1(int H, int G, int chunk) {
   return hpg / HT >= nrb * (nrb + 1) / 2;
 }
 
-hipError_t launch_scan_phase(const ScanArgs &a, int phase, hipStream_t st) {
+hipError_t launch_scan_phase(const ScanArgs &args, int phase, hipStream_t st) {
   // Heads of one tile share their B/C group: 2 heads when the heads per
-  // group are even (which keeps the output kernel at two waves per SIMD),
-  // else 1.
-  const int hpg = a.H / a.G;
+  // group are even, else 1.
+  const int hpg = args.H / args.G;
   const int HT = hpg % 2 == 0 ? 2 : 1;
+  ScanArgs a = args;
+  const int nrb = a.chunk / kRB;
+  a.fd_tiles = FastDiv((uint32_t)(a.H / HT));
+  a.fd_nc = FastDiv((uint32_t)a.nchunks);
+  a.fd_hpg = FastDiv((uint32_t)hpg);
+  a.fd_g = FastDiv((uint32_t)a.G);
+  a.fd_pairs = FastDiv((uint32_t)(nrb * (nrb + 1) / 2));
   if (a.dtype == 1) {
     if (a.N == 128) launch_n<bf16, 128>(a, phase, st, HT);
     else launch_n<bf16, 64>(a, phase, st, HT);

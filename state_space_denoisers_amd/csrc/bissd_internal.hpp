@@ -7,6 +7,31 @@
 
 namespace bissd {
 
+// Division by a runtime constant d (1 <= d < 2^31) of numerators n < 2^31 as
+// a multiply-high and a shift: with s = ceil(log2 d) and
+// m = floor(2^32 (2^s - d) / d) + 1, n / d = (mulhi(n, m) + n) >> s.  The
+// host forms (m, s) once per launch, so the kernels split their workgroup
+// index without an integer division.
+struct FastDiv {
+  uint32_t d = 1, m = 1, s = 0;
+  FastDiv() = default;
+  explicit FastDiv(uint32_t dv) : d(dv) {
+    s = 0;
+    while ((1ull << s) < dv) ++s;
+    m = (uint32_t)(((1ull << 32) * ((1ull << s) - dv)) / dv + 1);
+  }
+  __host__ __device__ __forceinline__ uint32_t div(uint32_t n) const {
+    const uint32_t hi = (uint32_t)(((uint64_t)n * m) >> 32);
+    return (hi + n) >> s;
+  }
+  // n / d, leaving n % d in rem
+  __host__ __device__ __forceinline__ uint32_t divmod(uint32_t n, uint32_t &rem) const {
+    const uint32_t q = div(n);
+    rem = n - q * d;
+    return q;
+  }
+};
+
 struct ScanArgs {
   const void *x;
   const void *dt[2];  // [0] forward, [1] reverse
@@ -38,6 +63,10 @@ struct ScanArgs {
   const void *states2;   // PHASE_TAN_PASS: tangent chunk states, compute dtype
   const float *dtsum;    // PHASE_TAN_PASS: chunk dt sums
   int slot_dir[2];  // direction under which each output-kernel slot stores out0
+  // divisors of the workgroup-index splits (set by launch_scan_phase): head
+  // tiles per batch-chunk-row-block, chunks, heads per B/C group, groups,
+  // Gram pairs per chunk
+  FastDiv fd_tiles, fd_nc, fd_hpg, fd_g, fd_pairs;
   float *gram;      // per slot: the chunk Gram tiles C.B^T in the output kernel's
                     // lane order, fp32, [2][Z][nchunks][G][chunk * chunk]; written by
                     // PHASE_GRAM (or by PHASE_CHUNK_STATE when gram_k1 is set), read
