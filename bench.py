@@ -41,7 +41,8 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
 PHASE_NAMES = {0: "k1_chunk_state", 3: "k_gram", 1: "k2_state_pass", 2: "k3_chunk_out"}
 PHASE_ORDER = (0, 3, 1, 2)   # the order bissd_forward runs them in
 KERNEL_SOURCES = ("state_space_denoisers_amd/csrc/bissd_fwd.hip",
-                  "state_space_denoisers_amd/csrc/bissd_device.hpp")
+                  "state_space_denoisers_amd/csrc/bissd_device.hpp",
+                  "state_space_denoisers_amd/csrc/bissd_internal.hpp")
 
 
 def log(*a):
