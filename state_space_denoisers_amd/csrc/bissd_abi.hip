@@ -57,12 +57,13 @@ int check_shape(const bissd_shape_t *s, int op) {
 // second chunk-state buffer (A-tangent chunk states, then adjoint chunk
 // states), the
 // A-tangent and adjoint carries (compute dtype), chunk dt sums, the
-// per-token dy.y_d and x.(G_t B_t) values (fp32 [2][Z][L][H]) and the
+// per-token dy.y_d and x.(G_t B_t) values (fp32 [2][Z][L][H]), each
+// token's in-chunk decay sum and cumulative dt (fp32 [2][Z][H][L]) and the
 // partial sums of the reductions.
 struct WsLayout {
   size_t states = 0, sin_t = 0, cdecay = 0, gram = 0;
   size_t tstates = 0, sa_t = 0, gin_t = 0, dtsum = 0, ydot = 0, qx = 0, qxs = 0, ddpart = 0, dAintra = 0,
-         dAx1 = 0, dAx2 = 0, rpart = 0;
+         dAx1 = 0, dAx2 = 0, rpart = 0, lamg = 0, cdtg = 0;
   size_t total = 0;
 };
 
@@ -99,6 +100,8 @@ WsLayout ws_layout(const bissd_shape_t *s, int op) {
     w.dAx1 = take(cd);
     w.dAx2 = take(cd);
     w.rpart = take(cd * (size_t)(s->headdim * s->dstate / 256));
+    w.lamg = take(tok);
+    w.cdtg = take(tok);
   }
   w.total = o;
   return w;
@@ -397,14 +400,18 @@ int bissd_backward(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, bissd
     a.sin_bstride[d] = (int64_t)nc * a.H * PN;
     a.sin_cstride[d] = (int64_t)a.H * PN;
   }
-  hipError_t e = bissd::launch_scan_phase(a, bissd::PHASE_CHUNK_STATE, st);
+  // the primal chunk states also keep every token's decay sum for the panels
+  ScanArgs a0 = a;
+  a0.cum_out = (float *)(ws + wl.lamg);
+  hipError_t e = bissd::launch_scan_phase(a0, bissd::PHASE_CHUNK_STATE, st);
   if (e == hipSuccess) e = bissd::launch_scan_phase(a, bissd::PHASE_STATE_PASS, st);
 
-  // A-tangent chunk states (dt-sum weighted), chunk dt sums, and the
-  // A-tangent carry-ins S^A_in
+  // A-tangent chunk states (dt-sum weighted), chunk dt sums (and every
+  // token's cumulative dt), and the A-tangent carry-ins S^A_in
   ScanArgs ta = a;
   ta.states = (void *)(ws + wl.tstates);
   ta.out1 = (float *)(ws + wl.dtsum);
+  ta.cum_out = (float *)(ws + wl.cdtg);
   if (e == hipSuccess) e = bissd::launch_scan_phase(ta, bissd::PHASE_TAN_STATE, st);
   ScanArgs tp = a;
   tp.states2 = (const void *)(ws + wl.tstates);
@@ -505,6 +512,8 @@ int bissd_backward(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, bissd
   b.dAx1 = (const float *)(ws + wl.dAx1);
   b.dAx2 = (const float *)(ws + wl.dAx2);
   b.ddpart = (const float *)(ws + wl.ddpart);
+  b.lamg = (const float *)(ws + wl.lamg);
+  b.cdtg = (const float *)(ws + wl.cdtg);
   b.L = s->seqlen;
   b.Z = (int)s->batch;
   b.H = (int)s->nheads;

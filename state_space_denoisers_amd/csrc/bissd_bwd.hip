@@ -78,14 +78,14 @@ template <typename T, int N> struct PanelLds {
 // in flight while head h is multiplied; with one, two workgroups per CU
 // overlap each other's copies.  Each head costs one or two barriers.
 template <typename T, int N, int PNL>
-__global__ __launch_bounds__(kThreads) void k_bwd_panel(BwdArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1)))
+void k_bwd_panel(BwdArgs a) {
   using Sm = PanelLds<T, N>;
   constexpr uint32_t ES = sizeof(T);
   constexpr int CRB = kP * ES, SRB = N * ES;
   constexpr int CSB = 4 * kRB * CRB, STB = kP * SRB;
-  // two tiles for the dC panel (register-bound to one workgroup per CU
-  // anyway); one for the dB panel, which then fits two workgroups per CU
-  constexpr bool DBUF = sizeof(T) == 2 && PNL == 0;
+  // one tile: two workgroups share a CU and overlap each other's copies
+  constexpr bool DBUF = false;
   using DC = DmaTile<CRB, SW_NAT>;
   using DS = DmaTile<SRB, SW_TR>;
   __shared__ Sm sm;
@@ -154,14 +154,35 @@ __global__ __launch_bounds__(kThreads) void k_bwd_panel(BwdArgs a) {
   // off-diagonal blocks.
   const int mtok = PNL == 0 ? (d == 0 ? j * kRB - 1 : (j + 1) * kRB) : (d == 0 ? j * kRB + kRB - 1 : j * kRB);
   const bool mok = mtok >= 0 && mtok < Q;
-  // column factors of one head, by the wave that just wrote its decay sums:
-  // dC 2^(m - cum_s) dt_s, dB 2^(cum_t - m)
-  auto build_colf = [&](int buf) __attribute__((always_inline)) {
-    const float m = mok ? sm.lam[buf][mtok] : 0.0f;
-    for (int s2 = lane; s2 < Q; s2 += 64) {
-      const float l = sm.lam[buf][s2];
-      sm.colf[buf][s2] = PNL == 0 ? exp2_fast(fminf(m - l, 0.0f)) * sm.dtv[buf][s2]
-                                  : exp2_fast(fminf(l - m, 0.0f));
+  // Per-token values of one head, thread tid taking token tid of the chunk:
+  // the decay sum and cumulative dt the chunk-state kernels kept (fp32,
+  // [2][Z][H][L]), dt, and the decay sum at the reference token.  Loaded raw
+  // (tokens past L read as zero) well before tok_put turns them into the
+  // LDS rows: decay sums, dt, cumulative dt and the column factors
+  // (dC 2^(m - cum_s) dt_s, dB 2^(cum_t - m)).
+  const int64_t cbase = ((int64_t)d * a.Z + b) * H;
+  // dt of one batch row; tokens past L read as zero
+  const bufres rDt = make_buf(reinterpret_cast<const T *>(a.dt[d]) + (int64_t)b * L * H,
+                              (uint32_t)(L * H * ES));
+  auto tok_ld = [&](int h, uint32_t (&raw)[4]) __attribute__((always_inline)) {
+    const bufres rl = make_buf(a.lamg + (cbase + h) * L, (uint32_t)(L * 4));
+    const uint32_t off = (uint32_t)(t0 + tid) * 4u;
+    raw[0] = __builtin_amdgcn_raw_buffer_load_b32(rl, off, 0, 0);
+    raw[1] = PNL == 0 ? __builtin_amdgcn_raw_buffer_load_b32(make_buf(a.cdtg + (cbase + h) * L, (uint32_t)(L * 4)), off, 0, 0) : 0u;
+    const uint32_t doff = (uint32_t)((t0 + tid) * H + h) * ES;
+    if constexpr (sizeof(T) == 2) raw[2] = __builtin_amdgcn_raw_buffer_load_b16(rDt, doff, 0, 0);
+    else raw[2] = __builtin_amdgcn_raw_buffer_load_b32(rDt, doff, 0, 0);
+    raw[3] = __builtin_amdgcn_raw_buffer_load_b32(rl, (uint32_t)(t0 + (mok ? mtok : 0)) * 4u, 0, 0);
+  };
+  auto tok_put = [&](const uint32_t (&raw)[4], int buf) __attribute__((always_inline)) {
+    if (tid < Q) {
+      const float l = __builtin_bit_cast(float, raw[0]);
+      const float dtv = __builtin_bit_cast(float, sizeof(T) == 2 ? raw[2] << 16 : raw[2]);
+      const float m = mok ? __builtin_bit_cast(float, raw[3]) : 0.0f;
+      sm.lam[buf][tid] = l;
+      sm.dtv[buf][tid] = dtv;
+      if (PNL == 0) sm.cdt[buf][tid] = __builtin_bit_cast(float, raw[1]);
+      sm.colf[buf][tid] = PNL == 0 ? exp2_fast(fminf(m - l, 0.0f)) * dtv : exp2_fast(fminf(l - m, 0.0f));
     }
   };
 
@@ -200,23 +221,11 @@ __global__ __launch_bounds__(kThreads) void k_bwd_panel(BwdArgs a) {
     __syncthreads();
   }
 
-  // dt of one batch row; tokens past L read as zero
-  const bufres rDt = make_buf(reinterpret_cast<const T *>(a.dt[d]) + (int64_t)b * L * H,
-                              (uint32_t)(L * H * ES));
-  auto ld_dt = [&](int h, uint32_t (&raw)[4]) __attribute__((always_inline)) {
-    chunk_dt_bload<T>(rDt, (uint32_t)(t0 * H + h) * ES, (uint32_t)(H * ES), Q, raw);
-  };
   const int64_t dai_base = (((int64_t)d * a.Z + b) * a.nchunks + c) * NRB + j;
   {
     uint32_t r0[4];
-    float d0[4];
-    ld_dt(g * hpg, r0);
-    chunk_dt_decode<T>(r0, Q, d0);
-    if (w == 0) {
-      chunk_decay_scan_vals(d0, Q, a.A[d][g * hpg] * kLog2e, d == 1, sm.lam[0], sm.dtv[0]);
-      build_colf(0);
-    }
-    if (PNL == 0 && w == 1) chunk_decay_scan_vals(d0, Q, 1.0f, d == 1, sm.cdt[0], sm.dtv[0]);
+    tok_ld(g * hpg, r0);
+    tok_put(r0, 0);
   }
   Frag<T> rf[2];
   ld_rows(g * hpg, rf);
@@ -241,7 +250,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_panel(BwdArgs a) {
     const float rowf = PNL == 0 ? exp2_fast(fminf(lrow - mref, 0.0f)) : drow * exp2_fast(fminf(mref - lrow, 0.0f));
     float fr[4];
     {
-      const float lend = d == 0 ? lam[Q - 1] : lam[0];
+      const float lend = d == 0 ? lam[qlen - 1] : lam[0];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = j * kRB + 16 * w + 4 * g4 + i;
@@ -250,10 +259,11 @@ __global__ __launch_bounds__(kThreads) void k_bwd_panel(BwdArgs a) {
     }
     Frag<T> rfn[2];
     uint32_t dtn[4];
+    // the next head's per-token values, consumed after this head's products
+    if (hi + 1 < hpg) tok_ld(h + 1, dtn);
     if (DBUF && hi + 1 < hpg) {
       issue_head(h + 1, nxt);
       ld_rows(h + 1, rfn);
-      ld_dt(h + 1, dtn);
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -321,21 +331,13 @@ __global__ __launch_bounds__(kThreads) void k_bwd_panel(BwdArgs a) {
         __syncthreads();
         issue_head(h + 1, cur);
         ld_rows(h + 1, rfn);
-        ld_dt(h + 1, dtn);
       }
-      // decay sums of the next head into the other buffer.  The empty asm
-      // keeps the decode of the raw dt bits (and so the wait for their loads,
-      // issued behind the next head's copies) from being hoisted to the top
-      // of the head.
+      // per-token rows of the next head into the other buffer.  The empty
+      // asm keeps their use (and so the wait for their loads, issued before
+      // this head's products) here rather than at the top of the head.
 #pragma unroll
       for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(dtn[i]) : : "memory");
-      float dn[4];
-      chunk_dt_decode<T>(dtn, Q, dn);
-      if (w == 0) {
-        chunk_decay_scan_vals(dn, Q, a.A[d][h + 1] * kLog2e, d == 1, sm.lam[lb ^ 1], sm.dtv[lb ^ 1]);
-        build_colf(lb ^ 1);
-      }
-      if (PNL == 0 && w == 1) chunk_decay_scan_vals(dn, Q, 1.0f, d == 1, sm.cdt[lb ^ 1], sm.dtv[lb ^ 1]);
+      tok_put(dtn, lb ^ 1);
       rf[0] = rfn[0];
       rf[1] = rfn[1];
     }

@@ -163,10 +163,19 @@ void k1_chunk_state(ScanArgs a) {
       chunk_decay_scan_vals(dv, Q, 1.0f, d == 1, sm.cdt[hh], sm.dtv[hh]);
   }
   __syncthreads();
+  const int lq = 31 - __builtin_clz(Q);  // the chunk length is a power of two
+  if ((MODE == 0 || MODE == 2) && a.cum_out) {
+    // the backward pass keeps the decay sums (MODE 0) and cumulative dt
+    // (MODE 2) of every token, [2][Z][H][L], token-contiguous per head
+    for (int it = tid; it < HT * Q; it += kThreads) {
+      const int hh = it >> lq, s = it & (Q - 1);
+      if (s < qlen)
+        a.cum_out[(((int64_t)d * a.Z + b) * H + h0 + hh) * L + t0 + s] = MODE == 0 ? sm.lam[hh][s] : sm.cdt[hh][s];
+    }
+  }
   const int64_t chi = (((int64_t)d * a.Z + b) * a.nchunks + c) * H + h0;  // (d, b, c, h0)
   if (MODE == 0 && tid < HT) a.cdecay[chi + tid] = d == 0 ? sm.lam[tid][Q - 1] : sm.lam[tid][0];
   if (MODE == 2 && tid < HT) a.out1[chi + tid] = d == 0 ? sm.cdt[tid][Q - 1] : sm.cdt[tid][0];
-  const int lq = 31 - __builtin_clz(Q);  // the chunk length is a power of two
   for (int it = tid; it < HT * Q; it += kThreads) {
     const int hh = it >> lq, s = it & (Q - 1);
     const float ref = d == 0 ? sm.lam[hh][Q - 1] : sm.lam[hh][0];

@@ -73,6 +73,9 @@ struct ScanArgs {
                     // by the output kernel (every mode)
   int gram_k1;      // PHASE_CHUNK_STATE over both directions also writes the Gram
                     // tiles (set by the host when gram_in_k1() holds)
+  float *cum_out;   // if set, PHASE_CHUNK_STATE writes each token's in-chunk log2-decay
+                    // sum and PHASE_TAN_STATE its in-chunk cumulative dt, both in scan
+                    // order, fp32 [2][Z][H][L]
 };
 
 enum {
@@ -117,6 +120,8 @@ struct BwdArgs {
   float *dAintra;       // [2][Z][nchunks][chunk/64][H] within-chunk A-tangent sums
   const float *dAx1, *dAx2;  // [2][Z][nchunks][H] cross-chunk A-tangent inner products
   const float *ddpart;  // [Z][nchunks][chunk/64][H]
+  const float *lamg;    // [2][Z][H][L] in-chunk log2-decay sums (scan order)
+  const float *cdtg;    // [2][Z][H][L] in-chunk cumulative dt (scan order)
   int64_t L;
   int Z, H, G, N, chunk, nchunks, dtype;
 };
