@@ -367,7 +367,7 @@ __global__ __launch_bounds__(kThreads) void k2_state_pass(ScanArgs a, int PN, in
   // long sequences otherwise).  Every load is unconditional: the primal
   // state after chunk c (for the boundary products) is read from a clamped,
   // always valid chunk and discarded by selection where there is none.
-  constexpr int D = 4;
+  constexpr int D = 8;
   typename Raw4<T>::type rl[D], rn[D];
   float rg[D];
   auto fetch = [&](int slot, int cc) __attribute__((always_inline)) {
