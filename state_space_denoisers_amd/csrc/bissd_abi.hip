@@ -445,6 +445,8 @@ int bissd_backward(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, bissd
   ScanArgs yd = a;
   yd.aux = dy;
   yd.out0 = (float *)(ws + wl.ydot);
+  yd.cdt_in = (const float *)(ws + wl.cdtg);
+  yd.dai_out = (float *)(ws + wl.dAintra);
   yd.slot_dir[0] = 0;
   yd.slot_dir[1] = 1;
   // the primal Gram tiles: from the chunk-state launch above, or here

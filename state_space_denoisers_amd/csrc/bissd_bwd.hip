@@ -34,8 +34,10 @@
 //                     + <G^T_loc, S_in> + <G_loc, S^A_in> ]
 // with E[t][s] = W[t][s] (C_t . B_s), G_loc = sum_t 2^cum_t dy_t (outer) C_t,
 // G^T_loc its (T_t - T_chunk start)-weighted version and S^A_in the A-tangent
-// of the carry-in state.  The first sum is taken here, from the dC panel's
-// weight tiles; the inner products come from the chunk-state kernels.
+// of the carry-in state.  The first sum comes from the dy.y_d pass of the
+// output kernel (a second product whose Gram operand carries (T_t - T_s) per
+// element), the inner products from the chunk-state kernels; they are added
+// here.
 #include <type_traits>
 
 #include "bissd_device.hpp"
@@ -48,9 +50,7 @@ namespace bissd {
 template <typename T, int N> struct PanelLds {
   float lam[2][kQmax];
   float dtv[2][kQmax];
-  float cdt[2][kQmax];  // cumulative dt (dC panel)
   float colf[2][kQmax]; // column factors of the off-diagonal blocks
-  float red[2][4];
 };
 
 // Workgroup = (batch b, chunk c, direction d, group g, 64-token row-block j)
@@ -70,8 +70,6 @@ template <typename T, int N> struct PanelLds {
 // is weighted exactly per element and masked by selection; the carried-state term RowSrc_row . State is added per head
 // with its row factor.  After the last head the summed weights multiply the
 // value rows (B for dC, C for dB), one 64-row slab at a time.
-// The dC panel also forms C.B^T for its tiles once (before the heads) and
-// sums E[t][s] (T_t - T_s) per head: the within-chunk part of dA.
 //
 // Every head's column slabs and state are copied buffer -> LDS directly into
 // a tile.  With two tiles (the bf16 dC panel) the copies for head h + 1 are
@@ -168,7 +166,7 @@ void k_bwd_panel(BwdArgs a) {
     const bufres rl = make_buf(a.lamg + (cbase + h) * L, (uint32_t)(L * 4));
     const uint32_t off = (uint32_t)(t0 + tid) * 4u;
     raw[0] = __builtin_amdgcn_raw_buffer_load_b32(rl, off, 0, 0);
-    raw[1] = PNL == 0 ? __builtin_amdgcn_raw_buffer_load_b32(make_buf(a.cdtg + (cbase + h) * L, (uint32_t)(L * 4)), off, 0, 0) : 0u;
+    raw[1] = 0u;
     const uint32_t doff = (uint32_t)((t0 + tid) * H + h) * ES;
     if constexpr (sizeof(T) == 2) raw[2] = __builtin_amdgcn_raw_buffer_load_b16(rDt, doff, 0, 0);
     else raw[2] = __builtin_amdgcn_raw_buffer_load_b32(rDt, doff, 0, 0);
@@ -181,47 +179,10 @@ void k_bwd_panel(BwdArgs a) {
       const float m = mok ? __builtin_bit_cast(float, raw[3]) : 0.0f;
       sm.lam[buf][tid] = l;
       sm.dtv[buf][tid] = dtv;
-      if (PNL == 0) sm.cdt[buf][tid] = __builtin_bit_cast(float, raw[1]);
       sm.colf[buf][tid] = PNL == 0 ? exp2_fast(fminf(m - l, 0.0f)) * dtv : exp2_fast(fminf(l - m, 0.0f));
     }
   };
 
-  // dC panel: cbt[k][u][i] = C_row . B_col in the Gram tiles' layout, kept
-  // in the compute dtype
-  using CBV = typename std::conditional<sizeof(T) == 2, bf16x4, f32x4>::type;
-  CBV cbt[4][4];
-  if constexpr (PNL == 0) {
-    const bufres rC = make_buf(reinterpret_cast<const T *>(a.C[d]) + (int64_t)b * L * G * N,
-                               (uint32_t)(L * G * N * ES));
-    Frag<T> cfr[N / 32];
-#pragma unroll
-    for (int ks = 0; ks < N / 32; ++ks)
-      frag_bload(cfr[ks], rC, (uint32_t)((t0 + rrow) * G + g) * N * ES + (32 * ks + 8 * g4) * ES);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if (k < kb || k > ke) continue;
-      __syncthreads();
-      issue_val(k, bufA);
-      wait_vmem();
-      __syncthreads();
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        f32x4 t;
-        zero4(t);
-#pragma unroll
-        for (int ks = 0; ks < N / 32; ++ks) {
-          Frag<T> bf;
-          frag_ld8_swz<DS>(bf, bufA, 16 * u + r16, 32 * ks + 8 * g4);
-          mma(t, bf, cfr[ks]);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) cbt[k][u][i] = from_f<T>(t[i]);
-      }
-    }
-    __syncthreads();
-  }
-
-  const int64_t dai_base = (((int64_t)d * a.Z + b) * a.nchunks + c) * NRB + j;
   {
     uint32_t r0[4];
     tok_ld(g * hpg, r0);
@@ -235,16 +196,11 @@ void k_bwd_panel(BwdArgs a) {
     const int h = g * hpg + hi, lb = hi & 1;
     wait_vmem();
     __syncthreads();  // head hi's tiles, decay sums and row fragments are ready
-    if (PNL == 0 && hi > 0 && tid == 0)
-      a.dAintra[dai_base * H + h - 1] = (sm.red[lb ^ 1][0] + sm.red[lb ^ 1][1]) +
-                                        (sm.red[lb ^ 1][2] + sm.red[lb ^ 1][3]);
     // per-row values are read before the next head's copies are issued (an
     // LDS read the compiler cannot tell apart from their destination would
     // otherwise wait for them)
     const float *lam = sm.lam[lb], *dtv = sm.dtv[lb];
-    float dai = 0.0f;
     const float lrow = lam[rrow], drow = dtv[rrow];
-    const float crow = PNL == 0 ? sm.cdt[lb][rrow] : 0.0f;
     // row factor of the off-diagonal blocks (dC 2^(cum_t - m), dB dt_s 2^(m - cum_s))
     const float mref = mok ? lam[mtok] : 0.0f;
     const float rowf = PNL == 0 ? exp2_fast(fminf(lrow - mref, 0.0f)) : drow * exp2_fast(fminf(mref - lrow, 0.0f));
@@ -287,7 +243,6 @@ void k_bwd_panel(BwdArgs a) {
           for (int i = 0; i < 4; ++i) {
             const float wv = dg[i] * (rowf * cf4[i]);
             wsum[k][u][i] += wv;
-            if (PNL == 0) dai += wv * (float)cbt[k][u][i] * (crow - sm.cdt[lb][col0 + i]);
           }
         } else {
 #pragma unroll
@@ -299,15 +254,9 @@ void k_bwd_panel(BwdArgs a) {
             const float dtf = PNL == 0 ? dtv[col] : drow;
             const float wv = ok ? dg[i] * (exp2_fast(fminf(ex, 0.0f)) * dtf) : 0.0f;
             wsum[k][u][i] += wv;
-            if (PNL == 0) dai += wv * (float)cbt[k][u][i] * (crow - sm.cdt[lb][col]);
           }
         }
       }
-    }
-    if (PNL == 0) {
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) dai += __shfl_xor(dai, o, 64);
-      if (lane == 0) sm.red[lb][w] = dai;
     }
 
     // carried-state term: rows r = 64 j + 16 w + 4 g4 + i, columns n
@@ -347,9 +296,6 @@ void k_bwd_panel(BwdArgs a) {
     if (hi + 1 < hpg) do_head(hi + 1, DBUF ? bufB : bufA, bufA);
   }
   __syncthreads();
-  if (PNL == 0 && tid == 0)
-    a.dAintra[dai_base * H + g * hpg + hpg - 1] = (sm.red[(hpg - 1) & 1][0] + sm.red[(hpg - 1) & 1][1]) +
-                                                  (sm.red[(hpg - 1) & 1][2] + sm.red[(hpg - 1) & 1][3]);
 
   // summed weights x value rows, one 64-row slab per column block
 #pragma unroll

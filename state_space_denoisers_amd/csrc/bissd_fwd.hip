@@ -606,7 +606,10 @@ template <typename T, int N, int HT, bool SF32> struct K3Pf {
 //
 // MODE 0 writes y.  The backward pass runs the same kernel twice more:
 // MODE 1 recomputes each direction's output y_d and stores only dy.y_d per
-// (token, head); MODE 2 evaluates the adjoint product G_t B_t, where
+// (token, head), and with a second product of the same x tiles, whose Gram
+// operand carries the extra factor (T_t - T_s) per element (T the in-chunk
+// cumulative dt in scan order), the within-chunk part of dA:
+// sum_{s before t} E[t][s] (T_t - T_s) per (row-block, head); MODE 2 evaluates the adjoint product G_t B_t, where
 // G_t = sum_{t' at or after t in scan order} 2^(cum_t' - cum_t) dy_t' (outer) C_t'
 // plus the carried adjoint.  That is this kernel's structure with the row
 // and column operands swapped (B_t as the row, C_t' as the column), dy in
@@ -631,7 +634,10 @@ void k3_chunk_out(ScanArgs a) {
   using SS = typename PF::SS;
   using SSrc = typename std::conditional<SF32, float, T>::type;
   constexpr int IH = PF::IH;
+  constexpr bool DAI = MODE == 1;  // the within-chunk dA product
   __shared__ Sm sm;
+  // MODE 1: in-chunk cumulative dt of every token, per (direction, head)
+  __shared__ __attribute__((aligned(16))) float smcdt[DAI ? 2 : 1][HT][DAI ? kQmax : 4];
   constexpr int NK = N / 32;
   const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
   const int Q = a.chunk, NRB = Q / kRB, H = a.H, G = a.G;
@@ -698,12 +704,19 @@ void k3_chunk_out(ScanArgs a) {
   // first stage's loads, so neither waits for the other.
   static_assert(2 * HT <= kThreads / 64, "one decay scan per wave");
   const int pd = w / HT, ph = w % HT;
-  uint32_t dtraw[4];
+  uint32_t dtraw[4], cdraw[kQmax / kRB];
   float Ah = 0.0f;
   if (w < 2 * HT) {
     chunk_dt_bload<T>(make_buf(reinterpret_cast<const T *>(a.dt[pd]) + (int64_t)b * L * H, (uint32_t)(L * H * ES)),
                       (uint32_t)(t0 * H + h0 + ph) * ES, (uint32_t)(H * ES), Q, dtraw);
     Ah = a.A[pd][h0 + ph];
+    if constexpr (DAI) {
+      // token m 64 + lane of the chunk; past L reads as zero
+      const bufres rc = make_buf(a.cdt_in + (((int64_t)pd * a.Z + b) * H + h0 + ph) * L, (uint32_t)(L * 4));
+#pragma unroll
+      for (int m = 0; m < kQmax / kRB; ++m)
+        cdraw[m] = __builtin_amdgcn_raw_buffer_load_b32(rc, (uint32_t)(t0 + m * kRB + lane) * 4u, 0, 0);
+    }
   }
   prefetch_sblock(0, 0);
   if (w < 2 * HT) {
@@ -712,6 +725,13 @@ void k3_chunk_out(ScanArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(dtraw[i]) : : "memory");
     asm volatile("" : "+v"(Ah) : : "memory");
+    if constexpr (DAI) {
+#pragma unroll
+      for (int m = 0; m < kQmax / kRB; ++m) {
+        asm volatile("" : "+v"(cdraw[m]) : : "memory");
+        if (m * kRB < Q) smcdt[pd][ph][m * kRB + lane] = __builtin_bit_cast(float, cdraw[m]);
+      }
+    }
     float dv[4];
     chunk_dt_decode<T>(dtraw, Q, dv);
     const float am = chunk_decay_scan_vals(dv, Q, Ah * kLog2e, pd == 1, sm.lam[pd][ph],
@@ -762,11 +782,15 @@ void k3_chunk_out(ScanArgs a) {
 #pragma unroll
     for (int hh = 0; hh < HT; ++hh) exact = exact || (sm.amax[d][hh] >= 8.0f);
 
-  f32x4 acc[HT][4];
+  f32x4 acc[HT][4], acc2[DAI ? HT : 1][4];
 #pragma unroll
   for (int hh = 0; hh < HT; ++hh)
 #pragma unroll
     for (int v = 0; v < 4; ++v) zero4(acc[hh][v]);
+#pragma unroll
+  for (int hh = 0; hh < (DAI ? HT : 1); ++hh)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) zero4(acc2[hh][v]);
 
   // one direction; D is a compile-time constant so every register array
   // (C fragments, masks, accumulators) is indexed statically
@@ -778,10 +802,13 @@ void k3_chunk_out(ScanArgs a) {
     if (MODE != 0 && d == 1) prefetch_sblock(1, klast);
     // per-head row factor 2^(lam_t - m) of this lane's Gram row t = 16w + r16,
     // applied to C.B^T together with the column factors
-    float ut[HT];
+    float ut[HT], trow[HT];
 #pragma unroll
-    for (int hh = 0; hh < HT; ++hh)
+    for (int hh = 0; hh < HT; ++hh) {
       ut[hh] = exp2_fast(sm.lam[d][hh][j * kRB + 16 * w + r16] - sm.refb[d][hh]);
+      trow[hh] = 0.0f;
+      if constexpr (DAI) trow[hh] = smcdt[d][hh][j * kRB + 16 * w + r16];
+    }
     // ---------------- s-blocks of direction d.  One stage: commit the
     // staged x, turn this wave's Gram tile into the masked, decay-weighted
     // operand mf (so the prefetch registers are free again), issue the next
@@ -812,7 +839,22 @@ void k3_chunk_out(ScanArgs a) {
         for (int u = 0; u < 4; ++u)
           sc[u] = *reinterpret_cast<const f32x4 *>(&sm.scale[d][hh][s0 + 16 * u + 4 * g4]);
       };
-      Frag<T> mf[HT][2];
+      Frag<T> mf[HT][2], mf2[DAI ? HT : 1][2];
+      // MODE 1: the same operand times (T_t - T_s), T_s of this lane's 16
+      // columns read as the column factors are
+      auto dai_frag = [&](int hh, int q, const float (&m)[8]) __attribute__((always_inline)) {
+        if constexpr (DAI) {
+          const f32x4 ta = *reinterpret_cast<const f32x4 *>(&smcdt[d][hh][s0 + 32 * q + 4 * g4]);
+          const f32x4 tb = *reinterpret_cast<const f32x4 *>(&smcdt[d][hh][s0 + 32 * q + 16 + 4 * g4]);
+          float m2[8];
+#pragma unroll
+          for (int i2 = 0; i2 < 4; ++i2) {
+            m2[i2] = m[i2] * (trow[hh] - ta[i2]);
+            m2[4 + i2] = m[4 + i2] * (trow[hh] - tb[i2]);
+          }
+          frag_from(mf2[hh][q], m2);
+        }
+      };
       if constexpr (!DIAG) {
 #pragma unroll
         for (int hh = 0; hh < HT; ++hh) {
@@ -827,6 +869,7 @@ void k3_chunk_out(ScanArgs a) {
               m[4 + i2] = cb[2 * q + 1][i2] * (ut[hh] * sc[2 * q + 1][i2]);
             }
             frag_from(mf[hh][q], m);
+            dai_frag(hh, q, m);
           }
         }
       } else {
@@ -875,6 +918,7 @@ void k3_chunk_out(ScanArgs a) {
                 m[e] = (u == w && !lm[i2]) ? 0.0f : v;
               }
               frag_from(mf[hh][q], m);
+              dai_frag(hh, q, m);
             }
           }
         } else {
@@ -896,6 +940,7 @@ void k3_chunk_out(ScanArgs a) {
                 m[e] = ok ? cb[u][i2] * wgt : 0.0f;
               }
               frag_from(mf[hh][q], m);
+              dai_frag(hh, q, m);
             }
           }
         }
@@ -915,6 +960,9 @@ void k3_chunk_out(ScanArgs a) {
             frag_rows(xf[v], &sm.u.s.Xs[hh][0][0], Sm::XPT, 32 * q + 4 * g4, 32 * q + 16 + 4 * g4, 16 * v);
 #pragma unroll
           for (int v = 0; v < 4; ++v) mma(acc[hh][v], mf[hh][q], xf[v]);
+          if constexpr (DAI)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) mma(acc2[hh][v], mf2[hh][q], xf[v]);
         }
     };
     if constexpr (d == 0) {
@@ -1083,6 +1131,54 @@ void k3_chunk_out(ScanArgs a) {
             }
           }
         }
+      }
+      if constexpr (DAI) {
+        // within-chunk dA of this row-block, per head: sum over its rows of
+        // dy . acc2, rows staged through LDS as above, reduced in a fixed order
+        float dsum[HT];
+#pragma unroll
+        for (int hh = 0; hh < HT; ++hh) dsum[hh] = 0.0f;
+#pragma unroll
+        for (int ih = 0; ih < HT / IH; ++ih) {
+          __syncthreads();
+#pragma unroll
+          for (int q = 0; q < IH; ++q)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+#pragma unroll
+              for (int i2 = 0; i2 < 4; ++i2)
+                sm.u.Out[q][16 * w + 4 * g4 + i2][16 * v + r16] = acc2[ih * IH + q][v][i2];
+          __syncthreads();
+#pragma unroll
+          for (int q = 0; q < IH; ++q) {
+            const int hh = ih * IH + q;
+#pragma unroll
+            for (int m2 = 0; m2 < (kRB * 8) / kThreads; ++m2) {
+              const int it = tid + m2 * kThreads;
+              const int r = it >> 3, p0 = (it & 7) * 8;
+              if (j * kRB + r >= qlen) continue;
+              float v[8];
+              gload8(v, auxo + (int64_t)r * xrs + hh * kP + p0);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) dsum[hh] += sm.u.Out[q][r][p0 + e] * v[e];
+            }
+          }
+        }
+#pragma unroll
+        for (int hh = 0; hh < HT; ++hh) {
+          float v = dsum[hh];
+#pragma unroll
+          for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+          if (lane == 0) sm.red[w][hh] = v;
+        }
+        __syncthreads();
+        if (tid < HT)
+          a.dai_out[((((int64_t)sd * a.Z + b) * a.nchunks + c) * NRB + j) * H + h0 + tid] =
+              (sm.red[0][tid] + sm.red[1][tid]) + (sm.red[2][tid] + sm.red[3][tid]);
+#pragma unroll
+        for (int hh = 0; hh < HT; ++hh)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) zero4(acc2[hh][v]);
       }
       if constexpr (MODE == 2 && d == 0) {
         // dy.x of this row-block, per head, in a fixed order

@@ -76,6 +76,11 @@ struct ScanArgs {
   float *cum_out;   // if set, PHASE_CHUNK_STATE writes each token's in-chunk log2-decay
                     // sum and PHASE_TAN_STATE its in-chunk cumulative dt, both in scan
                     // order, fp32 [2][Z][H][L]
+  const float *cdt_in;  // PHASE_YDOT: each token's in-chunk cumulative dt (scan order),
+                        // fp32 [2][Z][H][L]
+  float *dai_out;       // PHASE_YDOT: within-chunk A-tangent sums
+                        // sum_{s before t} E[t][s] (T_t - T_s) per (dir, b, chunk,
+                        // row-block, head), [2][Z][nchunks][chunk/64][H]
 };
 
 enum {
