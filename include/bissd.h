@@ -116,7 +116,7 @@ typedef struct {
 /*
  * Bytes of device workspace that `op` needs for `shape` (0 on a bad shape).
  * The workspace holds the per-chunk states and carries (compute dtype), the
- * chunk decays and the chunk Gram tiles C.B^T (fp32), plus the backward
+ * chunk decays and the chunk Gram tiles C.B^T (compute dtype), plus the backward
  * pass's adjoint and reduction buffers; it is overwritten by every call and
  * its contents between calls mean nothing.
  */

@@ -52,7 +52,7 @@ int check_shape(const bissd_shape_t *s, int op) {
 // Workspace: chunk-local states and the carry-in states, both in the compute
 // dtype (no carry-in buffer for the block update, which reads its fp32 start
 // state directly), the chunk log2-decays, and the chunk Gram tiles C.B^T of
-// both slots (fp32; none for a block update of at most 64 tokens, whose
+// both slots (compute dtype; none for a block update of at most 64 tokens, whose
 // single kernel forms them itself).  The backward pass adds a
 // second chunk-state buffer (A-tangent chunk states, then adjoint chunk
 // states), the
@@ -84,7 +84,7 @@ WsLayout ws_layout(const bissd_shape_t *s, int op) {
   if (op != BISSD_OP_BLOCK) w.sin_t = take(nst * esz);
   w.cdecay = take(cd);
   if (op != BISSD_OP_BLOCK || s->seqlen > 64)
-    w.gram = take((size_t)(2 * s->batch * nc * s->ngroups) * (size_t)(s->chunk * s->chunk) * 4);
+    w.gram = take((size_t)(2 * s->batch * nc * s->ngroups) * (size_t)(s->chunk * s->chunk) * esz);
   if (op == BISSD_OP_BACKWARD) {
     const size_t tok = (size_t)(2 * s->batch * s->seqlen * s->nheads) * 4;
     const size_t rb = (size_t)(s->batch * nc * (s->chunk / 64) * s->nheads) * 4;
@@ -235,7 +235,7 @@ static int forward_impl(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, 
   char *ws = (char *)workspace;
   a.states = (void *)(ws + wl.states);
   a.cdecay = (float *)(ws + wl.cdecay);
-  a.gram = (float *)(ws + wl.gram);
+  a.gram = (void *)(ws + wl.gram);
   a.gram_k1 = bissd::gram_in_k1(a.H, a.G, a.chunk) ? 1 : 0;
   a.nchunks = (int)ceil_div(s->seqlen, s->chunk);
   a.y = y;
@@ -314,7 +314,7 @@ int bissd_block_update(const bissd_shape_t *s, const float *state_in, const void
   char *ws = (char *)workspace;
   a.states = (void *)(ws + wl.states);
   a.cdecay = (float *)(ws + wl.cdecay);
-  a.gram = (float *)(ws + wl.gram);
+  a.gram = (void *)(ws + wl.gram);
   a.nchunks = 1;
   a.y = y_blk;
   a.dir0 = 0;
@@ -388,7 +388,7 @@ int bissd_backward(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, bissd
   ScanArgs a = base_args(s, x, fwd, rev, D);
   a.states = (void *)(ws + wl.states);
   a.cdecay = (float *)(ws + wl.cdecay);
-  a.gram = (float *)(ws + wl.gram);
+  a.gram = (void *)(ws + wl.gram);
   a.gram_k1 = bissd::gram_in_k1(a.H, a.G, a.chunk) ? 1 : 0;
   a.nchunks = nc;
   a.dir0 = 0;

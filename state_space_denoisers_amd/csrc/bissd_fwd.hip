@@ -47,6 +47,47 @@ __device__ __forceinline__ void gram_pair(int pr, int d, int NRB, int &j, int &k
   }
 }
 
+// Gram tiles are stored in the compute dtype.  One lane's 16 values
+// (accumulator u, element i) are GV = sizeof(T) 16-byte vectors, 64 lanes
+// apart: fp32 vector v holds accumulator v; bf16 vector v holds
+// accumulators 2v and 2v + 1.  A 16 x 64 tile is 64 GV vectors.
+template <typename T> struct GramIO {
+  static constexpr int GV = (int)sizeof(T);
+  __device__ static __forceinline__ void put(u32x4 *p, const f32x4 (&cb)[4]) {
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int v = 0; v < 2; ++v) {
+        bf16x8 o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          o[i] = (bf16)cb[2 * v][i];
+          o[4 + i] = (bf16)cb[2 * v + 1][i];
+        }
+        p[v * 64] = __builtin_bit_cast(u32x4, o);
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) p[v * 64] = __builtin_bit_cast(u32x4, cb[v]);
+    }
+  }
+  __device__ static __forceinline__ void get(f32x4 (&cb)[4], const u32x4 *pf) {
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int v = 0; v < 2; ++v) {
+        const bf16x8 o = __builtin_bit_cast(bf16x8, pf[v]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          cb[2 * v][i] = (float)o[i];
+          cb[2 * v + 1][i] = (float)o[4 + i];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) cb[v] = __builtin_bit_cast(f32x4, pf[v]);
+    }
+  }
+};
+
 // =================================================================== K1
 
 template <typename T, int N, int HT> struct K1Lds {
@@ -229,11 +270,11 @@ void k1_chunk_state(ScanArgs a) {
           frag_ld8(bq, &sm.Bs[16 * u + r16][32 * ks + 8 * g4]);
           mma(cb[u], bq, gcf[ks]);
         }
-      f32x4 *go = reinterpret_cast<f32x4 *>(a.gram) +
-                  ((((int64_t)d * a.Z + b) * a.nchunks + c) * G + gidx) * (int64_t)Q * Q / 4 +
-                  (int64_t)((4 * gj + w) * NRB + gkb) * 256 + lane;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) go[u * 64] = cb[u];
+      constexpr int GV = GramIO<T>::GV;
+      u32x4 *go = reinterpret_cast<u32x4 *>(a.gram) +
+                  ((((int64_t)d * a.Z + b) * a.nchunks + c) * G + gidx) * (int64_t)Q * Q * GV / 16 +
+                  (int64_t)((4 * gj + w) * NRB + gkb) * 64 * GV + lane;
+      GramIO<T>::put(go, cb);
     }
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -496,12 +537,11 @@ __global__ __launch_bounds__(kThreads) void k2_tangent_pass(ScanArgs a, int PN) 
 // t = 64 j + 16 w + (0..15) and columns s = 64 kb + (0..63).  Lane (r16, g4)
 // holds (C.B^T)[t = 64 j + 16 w + r16][s = 64 kb + 16 u + 4 g4 + i] in
 // accumulator u, element i -- the lane order in which the output kernel's
-// wave needs them -- accumulated over the state dimension in the order that
-// kernel used when it formed them itself.  Rows and columns past the
-// sequence end are zero.
-// Layout: [2][Z][nchunks][G][chunk * chunk] fp32; tile (16-row tile tt,
-// column block kb) at (tt * (chunk / 64) + kb) * 1024, value (u, lane, i) at
-// u * 256 + lane * 4 + i, so every store and load of one accumulator moves a
+// wave needs them -- accumulated in fp32 and rounded once to the compute
+// dtype.  Rows and columns past the sequence end are zero.
+// Layout: [2][Z][nchunks][G][chunk * chunk] in the compute dtype; tile
+// (16-row tile tt, column block kb) at element (tt * (chunk / 64) + kb) * 1024,
+// each lane's values as GramIO lays them out, so every store and load moves a
 // contiguous kilobyte.
 // Work items are grouped so that all the workgroups of one (batch, chunk)
 // run on one XCD and share its L2 copy of the B and C rows.
@@ -540,11 +580,11 @@ __global__ __launch_bounds__(kThreads) void k_gram(ScanArgs a) {
   for (int ks = 0; ks < NK; ++ks)
 #pragma unroll
     for (int u = 0; u < 4; ++u) mma(cb[u], bf[u][ks], cf[ks]);
-  f32x4 *out = reinterpret_cast<f32x4 *>(a.gram) +
-               ((((int64_t)d * a.Z + b) * a.nchunks + c) * G + g) * (int64_t)Q * Q / 4 +
-               (int64_t)((4 * j + w) * NRB + kb) * 256 + lane;
-#pragma unroll
-  for (int u = 0; u < 4; ++u) out[u * 64] = cb[u];
+  constexpr int GV = GramIO<T>::GV;
+  u32x4 *out = reinterpret_cast<u32x4 *>(a.gram) +
+               ((((int64_t)d * a.Z + b) * a.nchunks + c) * G + g) * (int64_t)Q * Q * GV / 16 +
+               (int64_t)((4 * j + w) * NRB + kb) * 64 * GV + lane;
+  GramIO<T>::put(out, cb);
 }
 
 // =================================================================== K3
@@ -571,7 +611,7 @@ template <typename T, int N, int HT> struct K3Lds {
 
 template <typename T, int N, int HT, bool SF32> struct K3Pf {
   static constexpr int IH = HT < 2 ? HT : 2;  // heads per carry-in / output stage
-  static constexpr int NG = 4;                // 16-byte vectors of one lane's Gram tile
+  static constexpr int NG = GramIO<T>::GV;    // 16-byte vectors of one lane's Gram tile
   using SX = SlabRows<T, kP, K3Lds<T, N, HT>::XPT>;
   using SS = SlabState<T, typename std::conditional<SF32, float, T>::type, N>;
   static constexpr int SBLK = NG + HT * SX::NV;
@@ -593,9 +633,9 @@ template <typename T, int N, int HT, bool SF32> struct K3Pf {
 // diagonal slab uses a reference per 16-token tile and is masked
 // elementwise.
 //
-// The C.B^T tiles come precomputed from the Gram kernel, one fp32 16 x 64
-// tile per wave and s-block, already in the lane order of the matrix-core
-// accumulators.
+// The C.B^T tiles come precomputed (chunk-state or Gram kernel), one 16 x 64
+// tile per wave and s-block in the compute dtype, already in the lane order
+// of the matrix-core accumulators.
 //
 // Work runs as a pipeline of stages -- the s-blocks, then the carry-in
 // states two heads per stage, forward first, then reverse -- and the global
@@ -666,10 +706,10 @@ void k3_chunk_out(ScanArgs a) {
       make_buf(reinterpret_cast<const T *>(a.C[1]) + (int64_t)b * L * G * N, (uint32_t)(L * G * N * ES))};
   const uint32_t xrs_b = (uint32_t)(H * kP * ES);
   // this wave's Gram tiles (16-row tile 4 j + w), s-block k at + k * 64 vectors
-  const int64_t gslot = (int64_t)a.Z * a.nchunks * G * Q * Q / 4;
+  const int64_t gslot = (int64_t)a.Z * a.nchunks * G * Q * Q * NG / 16;
   const u32x4 *gt0 = reinterpret_cast<const u32x4 *>(a.gram) +
-                     (((int64_t)b * a.nchunks + c) * G + gidx) * (int64_t)Q * Q / 4 +
-                     (int64_t)(4 * j + w) * NRB * 256 + lane;
+                     (((int64_t)b * a.nchunks + c) * G + gidx) * (int64_t)Q * Q * NG / 16 +
+                     (int64_t)(4 * j + w) * NRB * 64 * NG + lane;
   const uint32_t xoff = (uint32_t)(t0 * H + h0) * kP * ES;
   const int klast = (qlen - 1) / kRB;
   // carry-in terms that can be nonzero: slot 0's carry starts from zero at
@@ -682,7 +722,7 @@ void k3_chunk_out(ScanArgs a) {
   u32x4 pf[PF::NPF];
   auto prefetch_sblock = [&](int d, int k) __attribute__((always_inline)) {
     const uint32_t s0 = k * kRB;
-    const u32x4 *gp = gt0 + d * gslot + k * 256;
+    const u32x4 *gp = gt0 + d * gslot + k * 64 * NG;
 #pragma unroll
     for (int u = 0; u < NG; ++u) pf[u] = gp[u * 64];
 #pragma unroll
@@ -828,8 +868,7 @@ void k3_chunk_out(ScanArgs a) {
       __syncthreads();
       // cb[u]: lane holds (C.B^T)[t = 16w + r16][s = 16u + 4 g4 + i]
       f32x4 cb[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) cb[u] = __builtin_bit_cast(f32x4, pf[u]);
+      GramIO<T>::get(cb, pf);
 #pragma unroll
       for (int hh = 0; hh < HT; ++hh) SX::commit(&sm.u.s.Xs[hh][0][0], pf + NG + hh * SX::NV);
       // column factors (the staged operand's per-token scale) of this lane's

@@ -67,8 +67,8 @@ struct ScanArgs {
   // tiles per batch-chunk-row-block, chunks, heads per B/C group, groups,
   // Gram pairs per chunk
   FastDiv fd_tiles, fd_nc, fd_hpg, fd_g, fd_pairs;
-  float *gram;      // per slot: the chunk Gram tiles C.B^T in the output kernel's
-                    // lane order, fp32, [2][Z][nchunks][G][chunk * chunk]; written by
+  void *gram;       // per slot: the chunk Gram tiles C.B^T in the output kernel's
+                    // lane order, compute dtype, [2][Z][nchunks][G][chunk * chunk]; written by
                     // PHASE_GRAM (or by PHASE_CHUNK_STATE when gram_k1 is set), read
                     // by the output kernel (every mode)
   int gram_k1;      // PHASE_CHUNK_STATE over both directions also writes the Gram

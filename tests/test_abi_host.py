@@ -145,17 +145,20 @@ def test_forward_phase_range(lib):
 
 
 def test_workspace_holds_gram_tiles(lib):
-    """The forward workspace holds both slots' fp32 chunk Gram tiles
-    (2 x batch x chunks x groups x chunk^2 x 4 bytes) besides the states; a
-    block update of at most 64 tokens needs none."""
-    s = shape(seqlen=1024, ngroups=2, nheads=8)
+    """The forward workspace holds both slots' chunk Gram tiles in the compute
+    dtype (2 x batch x chunks x groups x chunk^2 elements) besides the states;
+    a block update of at most 64 tokens needs none."""
+    s = shape(seqlen=1024, ngroups=2, nheads=8)  # bf16
     n = lib.bissd_workspace_size(C.byref(s), _abi.OP_FORWARD)
     states = 2 * 2 * 2 * 4 * 8 * 64 * 128 * 2
-    gram = 2 * 2 * 4 * 2 * 256 * 256 * 4
+    gram = 2 * 2 * 4 * 2 * 256 * 256 * 2
     assert n >= states + gram
+    n32 = lib.bissd_workspace_size(C.byref(shape(seqlen=1024, ngroups=2, nheads=8,
+                                                 dtype=_abi.BISSD_F32)), _abi.OP_FORWARD)
+    assert n32 >= 2 * states + 2 * gram
     small = lib.bissd_workspace_size(C.byref(shape(seqlen=64, chunk=64)), _abi.OP_BLOCK)
     big = lib.bissd_workspace_size(C.byref(shape(seqlen=65, chunk=128)), _abi.OP_BLOCK)
-    assert big - small >= 2 * 2 * 128 * 128 * 4
+    assert big - small >= 2 * 2 * 128 * 128 * 2
 
 
 def test_status_strings(lib):
