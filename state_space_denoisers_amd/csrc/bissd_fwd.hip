@@ -604,13 +604,13 @@ template <typename T, int N, int HT> struct K3Lds {
     struct S {
       T Xs[HT][kRB][XPT];
     } s;
-    T Sst[HT < 2 ? HT : 2][kP][BP];
-    float Out[HT < 2 ? HT : 2][kRB][OP];
+    T Sst[1][kP][BP];
+    float Out[1][kRB][OP];
   } u;
 };
 
 template <typename T, int N, int HT, bool SF32> struct K3Pf {
-  static constexpr int IH = HT < 2 ? HT : 2;  // heads per carry-in / output stage
+  static constexpr int IH = 1;  // heads per carry-in / output stage (LDS for four workgroups per CU)
   static constexpr int NG = GramIO<T>::GV;    // 16-byte vectors of one lane's Gram tile
   using SX = SlabRows<T, kP, K3Lds<T, N, HT>::XPT>;
   using SS = SlabState<T, typename std::conditional<SF32, float, T>::type, N>;
@@ -638,7 +638,7 @@ template <typename T, int N, int HT, bool SF32> struct K3Pf {
 // of the matrix-core accumulators.
 //
 // Work runs as a pipeline of stages -- the s-blocks, then the carry-in
-// states two heads per stage, forward first, then reverse -- and the global
+// states one head per stage, forward first, then reverse -- and the global
 // loads of the next stage are issued into registers before the matrix-core
 // work of the current one.
 // SF32: the carry-in states are fp32 (the block update's cached state)
@@ -665,7 +665,7 @@ template <typename T, int N, int HT, bool SF32> struct K3Pf {
 // the result: dy_t (B_t.C_t) into G_t B_t for dx and x.(G_t B_t).
 template <typename T, int N, int HT, bool SF32, int MODE>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? (MODE != 0 ? 2 : (SF32 ? 1 : 3)) : 1)))
+__attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? (MODE != 0 ? 2 : (SF32 ? 1 : 4)) : 1)))
 void k3_chunk_out(ScanArgs a) {
   using Sm = K3Lds<T, N, HT>;
   using PF = K3Pf<T, N, HT, SF32>;
@@ -1010,7 +1010,7 @@ void k3_chunk_out(ScanArgs a) {
       for (int k = klast; k > j; --k) stage(k, std::false_type{});
     }
     stage(j, std::true_type{});
-    // ---------------- carry-in term 2^lam_t C S_in^T, IH heads per stage.
+    // ---------------- carry-in term 2^lam_t C S_in^T, one head per stage.
     // The states are staged as stored; the row factor 2^lam_t (<= 1) is
     // applied to a transient accumulator per head.
     if (d == 0 ? has_in0 : has_in1) {
@@ -1055,7 +1055,7 @@ void k3_chunk_out(ScanArgs a) {
     run_direction(std::integral_constant<int, 0>{});
     run_direction(std::integral_constant<int, 1>{});
 
-    // y = acc + D x, IH heads at a time staged through LDS so that every lane
+    // y = acc + D x, one head at a time staged through LDS so that every lane
     // writes 16 contiguous bytes
     T *yg = reinterpret_cast<T *>(a.y) + (((int64_t)b * L + t0 + j * kRB) * H + h0) * kP;
     const T *xo = xg + (int64_t)j * kRB * xrs;
