@@ -18,6 +18,12 @@ itself in each scan), which is the literal reading of "forward plus
 flipped-reverse" (DiffMamba Checkpoints, Model details; DiffuMamba Technical
 Summary, Methodology / Core Architecture).
 
+A block-segmented reverse scan (blocks of RB tokens, each its own reverse
+scan: the full-block objective of "Training Hybrid Block Diffusion Language
+Models with Partial Bidirectionality", Methodology) keeps only the entries of
+M_r whose row and column fall in the same block:
+M_r[t, s] = 0 unless floor(t / RB) = floor(s / RB).
+
 Written with plain torch CPU float64 ops so that autograd gives exact
 reference gradients of sum(dy * y) for the backward pins.  Sized for tiny
 inputs only (L up to a few hundred).
@@ -34,12 +40,15 @@ def _t(a, requires_grad=False):
     return t
 
 
-def direction_matrices(dt_f, A_f, B_f, C_f, dt_r, A_r, B_r, C_r):
+def direction_matrices(dt_f, A_f, B_f, C_f, dt_r, A_r, B_r, C_r, rev_block=0):
     """M_f, M_r for one (batch row, head): dt [L], A scalar, B/C [L, N]."""
     L = dt_f.shape[0]
     idx = torch.arange(L)
     lower = idx[:, None] >= idx[None, :]   # s <= t
     upper = idx[:, None] <= idx[None, :]   # s >= t
+    if rev_block:
+        blk = idx // rev_block
+        upper = upper & (blk[:, None] == blk[None, :])
     cf = torch.cumsum(dt_f, 0)             # sum_{k<=t}
     seg_f = cf[:, None] - cf[None, :]      # sum_{k=s+1..t}
     ef = torch.where(lower, A_f * seg_f, torch.full_like(seg_f, -torch.inf))
@@ -51,7 +60,7 @@ def direction_matrices(dt_f, A_f, B_f, C_f, dt_r, A_r, B_r, C_r):
     return Mf, Mr
 
 
-def forward_torch(T: dict, init_state=None):
+def forward_torch(T: dict, init_state=None, rev_block=0):
     """y (and per-direction parts) from torch float64 tensors in the GPU
     library's layouts.  Differentiable."""
     x = T["x"]
@@ -64,7 +73,8 @@ def forward_torch(T: dict, init_state=None):
             g = h * G // H
             Mf, Mr = direction_matrices(
                 T["dt_f"][b, :, h], T["A_f"][h], T["B_f"][b, :, g], T["C_f"][b, :, g],
-                T["dt_r"][b, :, h], T["A_r"][h], T["B_r"][b, :, g], T["C_r"][b, :, g])
+                T["dt_r"][b, :, h], T["A_r"][h], T["B_r"][b, :, g], T["C_r"][b, :, g],
+                rev_block)
             xh = x[b, :, h]
             yf = Mf @ xh
             if init_state is not None:
@@ -84,21 +94,21 @@ def forward_torch(T: dict, init_state=None):
 KEYS = ("x", "dt_f", "A_f", "B_f", "C_f", "dt_r", "A_r", "B_r", "C_r", "D")
 
 
-def forward(inp: dict, init_state=None) -> dict:
+def forward(inp: dict, init_state=None, rev_block=0) -> dict:
     """numpy in, numpy out: y, y_f, y_r."""
     T = {k: _t(inp[k]) for k in KEYS}
     S0 = None if init_state is None else _t(init_state)
     with torch.no_grad():
-        y, yf, yr = forward_torch(T, S0)
+        y, yf, yr = forward_torch(T, S0, rev_block)
     return {"y": y.numpy(), "y_f": yf.numpy(), "y_r": yr.numpy()}
 
 
-def gradients(inp: dict, dy, init_state=None) -> dict:
+def gradients(inp: dict, dy, init_state=None, rev_block=0) -> dict:
     """Reverse-mode gradients of sum(dy * y) by torch autograd on the dense
     form: dx, ddt_f, dA_f, dB_f, dC_f, ddt_r, dA_r, dB_r, dC_r, dD."""
     T = {k: _t(inp[k], requires_grad=True) for k in KEYS}
     S0 = None if init_state is None else _t(init_state)
-    y, _, _ = forward_torch(T, S0)
+    y, _, _ = forward_torch(T, S0, rev_block)
     loss = (y * _t(dy)).sum()
     loss.backward()
     out = {("d" + k): T[k].grad.numpy().copy() for k in KEYS}

@@ -22,7 +22,8 @@ _lib = None
 
 class _Shape(C.Structure):
     _fields_ = [("Z", C.c_int64), ("L", C.c_int64), ("H", C.c_int64),
-                ("P", C.c_int64), ("N", C.c_int64), ("G", C.c_int64)]
+                ("P", C.c_int64), ("N", C.c_int64), ("G", C.c_int64),
+                ("RB", C.c_int64)]
 
 
 class _Dir(C.Structure):
@@ -57,11 +58,11 @@ def _ptr(a):
     return None if a is None else a.ctypes.data_as(C.c_void_p)
 
 
-def _shape_of(inp):
+def _shape_of(inp, rev_block=0):
     Z, L, H, P = inp["x"].shape
     N = inp["B_f"].shape[-1]
     G = inp["B_f"].shape[-2]
-    return _Shape(Z, L, H, P, N, G)
+    return _Shape(Z, L, H, P, N, G, int(rev_block))
 
 
 def _dirs(inp, keep):
@@ -74,14 +75,16 @@ def _dirs(inp, keep):
 
 
 def forward(inp: dict, init_state=None, parts: bool = False, final_state: bool = False,
-            nthreads: int = 0):
+            nthreads: int = 0, rev_block: int = 0):
     """y = y_fwd + y_rev + D x.  Returns y, or a dict with y, y_f, y_r and
-    final_state when ``parts`` or ``final_state`` is set."""
+    final_state when ``parts`` or ``final_state`` is set.  ``rev_block`` > 0
+    restarts the reverse scan from zero at the end of every block of that
+    many tokens (0: one reverse scan over the whole sequence)."""
     keep = []
     x = _f64(inp["x"])
     D = _f64(inp["D"])
     fwd, rev = _dirs(inp, keep)
-    s = _shape_of(inp)
+    s = _shape_of(inp, rev_block)
     y = np.empty_like(x)
     yf = np.empty_like(x) if parts else None
     yr = np.empty_like(x) if parts else None
@@ -114,15 +117,15 @@ def block_update(inp: dict, state_in, want_state_out: bool = True, nthreads: int
     return y, so
 
 
-def backward(inp: dict, dy, init_state=None, nthreads: int = 0) -> dict:
+def backward(inp: dict, dy, init_state=None, nthreads: int = 0, rev_block: int = 0) -> dict:
     """Gradients of sum(dy * y): dx, ddt_f, dA_f, dB_f, dC_f, ddt_r, dA_r,
-    dB_r, dC_r, dD."""
+    dB_r, dC_r, dD (``rev_block`` as in forward)."""
     keep = []
     x = _f64(inp["x"])
     D = _f64(inp["D"])
     dyv = _f64(dy)
     fwd, rev = _dirs(inp, keep)
-    s = _shape_of(inp)
+    s = _shape_of(inp, rev_block)
     S0 = None if init_state is None else _f64(init_state)
     Z, L, H, P, N, G = s.Z, s.L, s.H, s.P, s.N, s.G
     g = {

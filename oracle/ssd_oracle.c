@@ -30,6 +30,15 @@
  *   the forward scan continues from a cached prefix state and the reverse scan
  *   is confined to the active block, starting from zero at the block end.
  *
+ *   Block-segmented reverse (same page, Methodology and Key Results: the
+ *   full-block training objective builds the same caches as inference).
+ *   Read here as: over a whole training sequence every block of RB tokens is
+ *   an active block for its own reverse scan, so the reverse state restarts
+ *   from zero after the last token of every block (tokens RB k .. RB k + RB - 1,
+ *   the last block possibly shorter), while the forward scan runs over the
+ *   whole sequence as usual.  RB = 0 means one reverse scan over the whole
+ *   sequence.
+ *
  *   Backward: reverse-mode differentiation of the same recurrence for the
  *   loss  sum(dy * y), walking the visited order backwards with an adjoint
  *   state G = dLoss/dS.
@@ -54,6 +63,7 @@
 
 typedef struct {
   int64_t Z, L, H, P, N, G;
+  int64_t RB; /* reverse block length (0: the reverse scan spans the sequence) */
 } ssdo_shape;
 
 typedef struct {
@@ -137,12 +147,20 @@ static inline int64_t group_of(const ssdo_shape *s, int64_t h) {
   return h * s->G / s->H;
 }
 
+/* 1 if direction d's state restarts from zero just before it visits token t:
+ * the reverse scan with RB > 0 at the last token of each block. */
+static inline int restarts_at(const ssdo_shape *s, int d, int64_t t) {
+  return d == 1 && s->RB > 0 && (t + 1) % s->RB == 0;
+}
+
 /*
  * One direction of one head of one batch row: the Mamba-2 recurrence
  *   S <- exp(dt_t A) S + dt_t x_t (outer) B_t,   y_t = S C_t
  * over the visited order (forward: t ascending; reverse: t descending).
- * S starts from S0 (P*N, NULL = zero); the state after the last visited
- * token is left in S.  Writes this direction's y_t at its natural position.
+ * S starts from S0 (P*N, NULL = zero) and, for a block-segmented reverse
+ * scan, is set back to zero before each block's last token is visited; the
+ * state after the last visited token is left in S.  Writes this direction's
+ * y_t at its natural position.
  */
 static void scan_one(const ssdo_shape *s, int64_t b, int64_t h, int reverse,
                      const double *x, ssdo_dir p, const double *S0, double *yd,
@@ -154,6 +172,7 @@ static void scan_one(const ssdo_shape *s, int64_t b, int64_t h, int reverse,
   else memset(S, 0, sizeof(double) * (size_t)(P * N));
   for (int64_t k = 0; k < L; ++k) {
     const int64_t t = reverse ? L - 1 - k : k;
+    if (restarts_at(s, reverse, t)) memset(S, 0, sizeof(double) * (size_t)(P * N));
     const double dtv = p.dt[(b * L + t) * H + h];
     const double a = exp(dtv * A);
     const double *xt = x + ((b * L + t) * H + h) * P;
@@ -199,7 +218,7 @@ static void fwd_unit(void *vctx, int64_t u, double *S) {
 
 static int shape_ok(const ssdo_shape *s) {
   return s && s->Z > 0 && s->L > 0 && s->H > 0 && s->P > 0 && s->N > 0 &&
-         s->G > 0 && s->H % s->G == 0;
+         s->G > 0 && s->H % s->G == 0 && s->RB >= 0;
 }
 
 /*
@@ -208,7 +227,8 @@ static int shape_ok(const ssdo_shape *s) {
  * y_f / y_r (optional, may be NULL) receive the two scan outputs separately.
  * init_state (optional) seeds the forward direction; final_state (optional)
  * receives the forward state after token L-1.  The reverse direction always
- * starts from zero after token L-1.
+ * starts from zero after token L-1 and, with s->RB > 0, again after the last
+ * token of every block of RB tokens.
  * Returns 0, or -1 on a bad shape / allocation failure.
  */
 int ssdo_forward(const ssdo_shape *s, const double *x, ssdo_dir fwd, ssdo_dir rev,
@@ -265,7 +285,7 @@ int ssdo_forward(const ssdo_shape *s, const double *x, ssdo_dir fwd, ssdo_dir re
 int ssdo_block_update(const ssdo_shape *s, const double *state_in, const double *x_blk,
                       ssdo_dir fwd, ssdo_dir rev, const double *D, double *y_blk,
                       double *state_out, int nthreads) {
-  if (!state_in) return -1;
+  if (!state_in || s->RB != 0) return -1;
   return ssdo_forward(s, x_blk, fwd, rev, D, state_in, y_blk, NULL, NULL, state_out,
                       nthreads);
 }
@@ -291,6 +311,9 @@ typedef struct {
  *             dC_k += S_k^T dy_k,  dx_k += dt_k G B_k,  dB_k += dt_k G^T x_k,
  *             ddt_k = x_k^T G B_k + A a_k <G, S_{k-1}>,
  *             dA += dt_k a_k <G, S_{k-1}>,   then G <- a_k G.
+ * At a restart of a block-segmented reverse scan the factor on S_{k-1} is 0
+ * instead of a_k, in the recomputed states, in the two <G, S_{k-1}> terms and
+ * in the final G <- 0.
  * States are checkpointed every `seg` visited tokens and each segment is
  * recomputed once, so memory stays (L/seg + seg) * P * N doubles.
  */
@@ -315,6 +338,7 @@ static void bwd_one(bwd_ctx *c, int64_t b, int64_t h, int d, double *ws) {
   for (int64_t k = 0; k < L; ++k) {
     if (k % seg == 0) memcpy(ckpt + (k / seg) * PN, S, sizeof(double) * (size_t)PN);
     const int64_t t = d ? L - 1 - k : k;
+    if (restarts_at(s, d, t)) memset(S, 0, sizeof(double) * (size_t)PN);
     const double dtv = p.dt[(b * L + t) * H + h];
     const double a = exp(dtv * A);
     const double *xt = c->x + ((b * L + t) * H + h) * P;
@@ -338,13 +362,16 @@ static void bwd_one(bwd_ctx *c, int64_t b, int64_t h, int d, double *ws) {
       const double *Bt = p.B + ((b * L + t) * G + g) * N;
       const double *Sp = segS + (k - k0) * PN;
       double *Sn = segS + (k - k0 + 1) * PN;
+      /* factor on the previous state: zero at a restart */
+      const double ap = restarts_at(s, d, t) ? 0.0 : a;
       for (int64_t i = 0; i < P; ++i)
-        for (int64_t n = 0; n < N; ++n) Sn[i * N + n] = a * Sp[i * N + n] + dtv * xt[i] * Bt[n];
+        for (int64_t n = 0; n < N; ++n) Sn[i * N + n] = ap * Sp[i * N + n] + dtv * xt[i] * Bt[n];
     }
     for (int64_t k = k1 - 1; k >= k0; --k) {
       const int64_t t = d ? L - 1 - k : k;
       const double dtv = p.dt[(b * L + t) * H + h];
       const double a = exp(dtv * A);
+      const double ap = restarts_at(s, d, t) ? 0.0 : a;
       const double *xt = c->x + ((b * L + t) * H + h) * P;
       const double *dyt = c->dy + ((b * L + t) * H + h) * P;
       const double *Bt = p.B + ((b * L + t) * G + g) * N;
@@ -380,9 +407,9 @@ static void bwd_one(bwd_ctx *c, int64_t b, int64_t h, int d, double *ws) {
       /* <G, S_{t-1}> */
       double ip = 0.0;
       for (int64_t e = 0; e < PN; ++e) ip += Gm[e] * Sprev[e];
-      c->ddt[d][(b * L + t) * H + h] = xgb + A * a * ip;
-      dA += dtv * a * ip;
-      for (int64_t e = 0; e < PN; ++e) Gm[e] *= a;
+      c->ddt[d][(b * L + t) * H + h] = xgb + A * ap * ip;
+      dA += dtv * ap * ip;
+      for (int64_t e = 0; e < PN; ++e) Gm[e] *= ap;
     }
   }
   c->dA_part[(b * 2 + d) * H + h] = dA;

@@ -299,3 +299,85 @@ def test_thread_count_does_not_change_results():
     gb = O.backward(inp, dy, nthreads=4)
     for k in ga:
         assert np.array_equal(ga[k], gb[k]), k
+
+
+# ------------------------------------------- P12 block-segmented reverse
+
+def _slice_tokens(inp, lo, hi):
+    out = {}
+    for k, v in inp.items():
+        out[k] = v if k in ("A_f", "A_r", "D") else v[:, lo:hi]
+    return out
+
+
+@pytest.mark.parametrize("shape,rb", [((2, 37, 3, 5, 4, 1), 8), ((1, 130, 4, 8, 6, 2), 64),
+                                      ((1, 64, 6, 3, 5, 3), 1), ((2, 40, 2, 3, 4, 1), 13)])
+def test_segmented_reverse_matches_dense_block_mask(shape, rb):
+    """The recurrence with restarts against the materialised reverse matrix
+    with its cross-block entries removed."""
+    inp = rand_inputs(*shape, seed=31)
+    o = O.forward(inp, parts=True, rev_block=rb)
+    d = dense.forward(inp, rev_block=rb)
+    assert rel(o["y_f"], d["y_f"]) < 1e-12
+    assert rel(o["y_r"], d["y_r"]) < 1e-12
+    assert rel(o["y"], d["y"]) < 1e-12
+    # the restarts change the result (the pin is not vacuous)
+    assert rel(o["y_r"], O.forward(inp, parts=True)["y_r"]) > 1e-3
+
+
+@pytest.mark.parametrize("L,rb", [(100, 16), (96, 32), (70, 70), (5, 2)])
+def test_segmented_reverse_is_one_reverse_scan_per_block(L, rb):
+    """Each block's reverse output equals a whole-sequence scan of that block
+    alone, operation for operation; the forward direction is untouched."""
+    inp = rand_inputs(2, L, 3, 4, 5, 1, seed=32)
+    seg = O.forward(inp, parts=True, rev_block=rb)
+    full = O.forward(inp, parts=True)
+    assert np.array_equal(seg["y_f"], full["y_f"])
+    for lo in range(0, L, rb):
+        hi = min(lo + rb, L)
+        blk = O.forward(_slice_tokens(inp, lo, hi), parts=True)
+        assert np.array_equal(seg["y_r"][:, lo:hi], blk["y_r"]), lo
+
+
+def test_reverse_block_longer_than_the_sequence_is_no_segmentation():
+    inp = rand_inputs(1, 50, 2, 3, 4, 1, seed=33)
+    dy = np.random.default_rng(34).standard_normal(inp["x"].shape)
+    for rb in (50, 64, 1000):
+        assert np.array_equal(O.forward(inp, rev_block=rb), O.forward(inp))
+        ga, gb = O.backward(inp, dy, rev_block=rb), O.backward(inp, dy)
+        for k in ga:
+            assert np.array_equal(ga[k], gb[k]), (rb, k)
+
+
+@pytest.mark.parametrize("shape,rb", [((1, 20, 2, 3, 4, 1), 6), ((2, 33, 4, 3, 2, 2), 8),
+                                      ((1, 150, 2, 3, 4, 1), 64), ((1, 150, 2, 3, 4, 1), 37)])
+def test_segmented_backward_matches_autograd_of_masked_dense_form(shape, rb):
+    """L = 150 spans three checkpoint segments of the oracle's backward."""
+    inp = rand_inputs(*shape, seed=35)
+    S0 = np.random.default_rng(36).standard_normal((shape[0], shape[2], shape[3], shape[4]))
+    dy = np.random.default_rng(37).standard_normal(inp["x"].shape)
+    g = O.backward(inp, dy, init_state=S0, rev_block=rb)
+    ref = dense.gradients(inp, dy, init_state=S0, rev_block=rb)
+    for k in KEYS:
+        assert rel(g["d" + k], ref["d" + k]) < 1e-11, k
+
+
+def test_segmented_backward_reverse_gradients_come_block_by_block():
+    """The reverse direction's parameter gradients of each block are those of
+    that block alone (dA summed over blocks); the forward direction's are
+    those of the unsegmented scan."""
+    Z, L, H, P, N, G, rb = 2, 90, 3, 4, 5, 1, 32
+    inp = rand_inputs(Z, L, H, P, N, G, seed=38)
+    dy = np.random.default_rng(39).standard_normal(inp["x"].shape)
+    seg = O.backward(inp, dy, rev_block=rb)
+    full = O.backward(inp, dy)
+    for k in ("ddt_f", "dA_f", "dB_f", "dC_f", "dD"):
+        assert np.array_equal(seg[k], full[k]), k
+    dA = np.zeros(H)
+    for lo in range(0, L, rb):
+        hi = min(lo + rb, L)
+        blk = O.backward(_slice_tokens(inp, lo, hi), dy[:, lo:hi])
+        for k in ("ddt_r", "dB_r", "dC_r"):
+            assert rel(seg[k][:, lo:hi], blk[k]) < 1e-13, (k, lo)
+        dA += blk["dA_r"]
+    assert rel(seg["dA_r"], dA) < 1e-12
