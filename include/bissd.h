@@ -20,6 +20,16 @@
  * init_state (or zero); the reverse state always starts from zero after the
  * last token.
  *
+ * Block-segmented reverse ("Training Hybrid Block Diffusion Language Models
+ * with Partial Bidirectionality", Methodology and Key Results: training with
+ * a full-block objective builds the same caches inference uses).  With
+ * shape->rev_block = RB > 0, every block of RB tokens of the training
+ * sequence is an active block for its own reverse scan: S' restarts from
+ * zero after each block's last token, so yr[t] sees only the tokens of t's
+ * block from t onwards, while the forward scan -- whose states are the
+ * prefix caches -- runs over the whole sequence.  bissd_forward and
+ * bissd_backward take it; for RB >= L it is the unsegmented scan.
+ *
  * Block update ("Training Hybrid Block Diffusion Language Models with Partial
  * Bidirectionality", Methodology and Technical Contribution): during
  * block-wise denoising the forward state after the prefix is a cache that is
@@ -52,7 +62,8 @@
  * the ABI.
  *
  * Support.  headdim == 64; dstate in {64, 128}; chunk in {64, 128, 256};
- * nheads % ngroups == 0; any seqlen >= 1; dtype BISSD_F32 or BISSD_BF16.
+ * nheads % ngroups == 0; any seqlen >= 1; dtype BISSD_F32 or BISSD_BF16;
+ * rev_block 0, or a multiple of 64 that divides chunk or is a multiple of it.
  * All arithmetic accumulates in fp32; bf16 operands feed the matrix cores.
  */
 #ifndef BISSD_H
@@ -72,8 +83,10 @@ enum { BISSD_F32 = 0, BISSD_BF16 = 1 };
 enum {
   BISSD_OK = 0,
   BISSD_ERR_NULL = -1,        /* a required pointer is NULL */
-  BISSD_ERR_SHAPE = -2,       /* a dim <= 0, nheads % ngroups != 0, or block longer than chunk */
-  BISSD_ERR_UNSUPPORTED = -3, /* headdim, dstate, chunk or dtype outside the supported set */
+  BISSD_ERR_SHAPE = -2,       /* a dim <= 0, rev_block < 0, nheads % ngroups != 0, or block
+                                 longer than chunk */
+  BISSD_ERR_UNSUPPORTED = -3, /* headdim, dstate, chunk, rev_block or dtype outside the
+                                 supported set */
   BISSD_ERR_ALIGN = -4,       /* a pointer not aligned to 16 bytes */
   BISSD_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than bissd_workspace_size() */
   BISSD_ERR_HIP = -6,         /* a HIP launch failed; see bissd_last_hip_error() */
@@ -93,7 +106,14 @@ typedef struct {
   int64_t chunk;    /* chunk length of the chunked evaluation (a tiling choice;
                        the result does not depend on it beyond rounding) */
   int32_t dtype;    /* BISSD_F32 or BISSD_BF16 */
-  int32_t reserved; /* must be 0 */
+  int32_t rev_block; /* 0: one reverse scan over the whole sequence.  > 0: the
+                        block-segmented reverse scan -- the reverse state
+                        restarts from zero after the last token of every
+                        block of rev_block tokens (tokens k rev_block ..
+                        (k+1) rev_block - 1, the last block possibly shorter),
+                        while the forward scan still runs over the whole
+                        sequence.  A multiple of 64 that divides chunk or is
+                        a multiple of it; bissd_block_update takes 0 only. */
 } bissd_shape_t;
 
 /* One scan direction's parameters.  dt is already positive (no softplus,

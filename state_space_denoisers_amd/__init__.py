@@ -47,10 +47,10 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
-def shape_of(x: torch.Tensor, B: torch.Tensor, chunk: int) -> _abi.Shape:
+def shape_of(x: torch.Tensor, B: torch.Tensor, chunk: int, rev_block: int = 0) -> _abi.Shape:
     Z, L, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
-    return _abi.Shape(Z, L, H, P, N, G, int(chunk), _dtype_code(x), 0)
+    return _abi.Shape(Z, L, H, P, N, G, int(chunk), _dtype_code(x), int(rev_block))
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -88,13 +88,15 @@ def _workspace(shape, op, device, workspace):
 
 
 def bissd_forward(x: torch.Tensor, fwd, rev, D: torch.Tensor, *, chunk: int = 256,
-                  init_state: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
-                  final_state: Optional[torch.Tensor] = None,
+                  rev_block: int = 0, init_state: Optional[torch.Tensor] = None,
+                  y: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
                   workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """y = yf + yr + D x (see include/bissd.h, bissd_forward)."""
+    """y = yf + yr + D x (see include/bissd.h, bissd_forward).  ``rev_block``
+    > 0 restarts the reverse scan at the end of every block of that many
+    tokens (the block-segmented reverse of full-block training)."""
     lib = _abi.load()
     fwd, rev = Dir(*fwd), Dir(*rev)
-    shape = shape_of(x, fwd.B, chunk)
+    shape = shape_of(x, fwd.B, chunk, rev_block)
     if y is None:
         y = torch.empty_like(x)
     ws, nws = _workspace(shape, _abi.OP_FORWARD, x.device, workspace)
@@ -106,14 +108,14 @@ def bissd_forward(x: torch.Tensor, fwd, rev, D: torch.Tensor, *, chunk: int = 25
 
 
 def bissd_forward_phase(phase: int, x: torch.Tensor, fwd, rev, D: torch.Tensor, *,
-                        chunk: int = 256, y: torch.Tensor, workspace: torch.Tensor,
-                        init_state: Optional[torch.Tensor] = None,
+                        chunk: int = 256, rev_block: int = 0, y: torch.Tensor,
+                        workspace: torch.Tensor, init_state: Optional[torch.Tensor] = None,
                         final_state: Optional[torch.Tensor] = None, stream=None) -> None:
     """Enqueue one phase of bissd_forward (0 chunk states, 3 Gram tiles, 1 carry pass,
     2 output) for timing single kernels (include/bissd.h)."""
     lib = _abi.load()
     fwd, rev = Dir(*fwd), Dir(*rev)
-    shape = shape_of(x, fwd.B, chunk)
+    shape = shape_of(x, fwd.B, chunk, rev_block)
     st = lib.bissd_forward_phase(C.byref(shape), _ptr(x), _dir(fwd), _dir(rev), _ptr(D),
                                  _ptr(init_state), _ptr(y), _ptr(final_state), _ptr(workspace),
                                  C.c_size_t(workspace.numel() * workspace.element_size()),
@@ -151,15 +153,16 @@ GRAD_KEYS = ("dx", "ddt_f", "dA_f", "dB_f", "dC_f", "ddt_r", "dA_r", "dB_r", "dC
 
 
 def bissd_backward(x: torch.Tensor, fwd, rev, D: torch.Tensor, dy: torch.Tensor, *,
-                   chunk: int = 256, init_state: Optional[torch.Tensor] = None,
-                   grads: Optional[dict] = None, workspace: Optional[torch.Tensor] = None,
-                   stream=None) -> dict:
+                   chunk: int = 256, rev_block: int = 0,
+                   init_state: Optional[torch.Tensor] = None, grads: Optional[dict] = None,
+                   workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
     """Gradients of sum(dy * y) (include/bissd.h, bissd_backward).  Returns a
     dict with dx, ddt_f, dA_f, dB_f, dC_f, ddt_r, dA_r, dB_r, dC_r, dD (fp32);
-    ``grads`` may hold preallocated tensors under those keys."""
+    ``grads`` may hold preallocated tensors under those keys.  ``rev_block``
+    as in bissd_forward."""
     lib = _abi.load()
     fwd, rev = Dir(*fwd), Dir(*rev)
-    shape = shape_of(x, fwd.B, chunk)
+    shape = shape_of(x, fwd.B, chunk, rev_block)
     f32 = dict(dtype=torch.float32, device=x.device)
     g = dict(grads) if grads is not None else {}
     if "dx" not in g:

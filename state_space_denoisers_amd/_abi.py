@@ -31,7 +31,7 @@ EXPORTS = ("bissd_workspace_size", "bissd_forward", "bissd_backward", "bissd_blo
 class Shape(C.Structure):
     _fields_ = [("batch", C.c_int64), ("seqlen", C.c_int64), ("nheads", C.c_int64),
                 ("headdim", C.c_int64), ("dstate", C.c_int64), ("ngroups", C.c_int64),
-                ("chunk", C.c_int64), ("dtype", C.c_int32), ("reserved", C.c_int32)]
+                ("chunk", C.c_int64), ("dtype", C.c_int32), ("rev_block", C.c_int32)]
 
 
 class Dir(C.Structure):

@@ -26,8 +26,13 @@ int check_shape(const bissd_shape_t *s, int op) {
       s->ngroups <= 0 || s->chunk <= 0)
     return BISSD_ERR_SHAPE;
   if (s->nheads % s->ngroups != 0) return BISSD_ERR_SHAPE;
-  if (s->reserved != 0) return BISSD_ERR_SHAPE;
+  if (s->rev_block < 0) return BISSD_ERR_SHAPE;
   if (op != BISSD_OP_FORWARD && op != BISSD_OP_BACKWARD && op != BISSD_OP_BLOCK)
+    return BISSD_ERR_UNSUPPORTED;
+  // the reverse blocks are whole 64-token tiles and either split a chunk
+  // evenly or span whole chunks
+  if (s->rev_block > 0 && (op == BISSD_OP_BLOCK || s->rev_block % 64 != 0 ||
+                           (s->chunk % s->rev_block != 0 && s->rev_block % s->chunk != 0)))
     return BISSD_ERR_UNSUPPORTED;
   if (s->headdim != 64) return BISSD_ERR_UNSUPPORTED;
   if (s->dstate != 64 && s->dstate != 128) return BISSD_ERR_UNSUPPORTED;
@@ -147,6 +152,17 @@ bool hits_inputs(const void *out, size_t n, const Sizes &z, const void *x, const
   return false;
 }
 
+// The block-segmented reverse in the kernels' terms: chunks per reverse
+// block (1 when a block is no longer than a chunk, so that every chunk
+// boundary restarts the reverse scan; 0 without segmentation) and 64-token
+// tiles per block when a block is shorter than a chunk (0 otherwise).
+void set_rev_blocks(const bissd_shape_t *s, int &chunks, int &tiles) {
+  chunks = tiles = 0;
+  if (s->rev_block <= 0 || s->rev_block >= s->seqlen) return;
+  chunks = s->rev_block >= s->chunk ? (int)(s->rev_block / s->chunk) : 1;
+  tiles = s->rev_block < s->chunk ? (int)(s->rev_block / 64) : 0;
+}
+
 ScanArgs base_args(const bissd_shape_t *s, const void *x, const bissd_dir_t &f,
                    const bissd_dir_t &r, const float *D) {
   ScanArgs a;
@@ -168,6 +184,7 @@ ScanArgs base_args(const bissd_shape_t *s, const void *x, const bissd_dir_t &f,
   a.N = (int)s->dstate;
   a.chunk = (int)s->chunk;
   a.dtype = s->dtype;
+  set_rev_blocks(s, a.rseg_chunks, a.rseg_tiles);
   return a;
 }
 
@@ -524,6 +541,7 @@ int bissd_backward(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, bissd
   b.chunk = (int)s->chunk;
   b.nchunks = nc;
   b.dtype = s->dtype;
+  b.rseg_tiles = a.rseg_tiles;
   if (e == hipSuccess) e = bissd::launch_bwd_panels(b, st);
   if (e == hipSuccess) e = bissd::launch_bwd_decay(b, st);
   return finish(e);

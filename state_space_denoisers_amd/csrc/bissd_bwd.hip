@@ -106,9 +106,13 @@ void k_bwd_panel(BwdArgs a) {
   const int qlen = (int)((L - t0) < Q ? (L - t0) : Q);
   if (j * kRB >= qlen) return;
   const int klast = (qlen - 1) / kRB;
-  // columns before the row in index order: dC forward, dB reverse
+  // columns before the row in index order: dC forward, dB reverse.  A
+  // block-segmented reverse keeps its columns inside the row's block.
   const bool colLE = (PNL == 0) == (d == 0);
-  const int kb = colLE ? 0 : j, ke = colLE ? j : klast;
+  const int segt = d == 1 ? a.rseg_tiles : 0;
+  const int kseg0 = segt ? (j & ~(segt - 1)) : 0;
+  const int kseg1 = segt ? min(kseg0 + segt - 1, klast) : klast;
+  const int kb = colLE ? kseg0 : j, ke = colLE ? j : kseg1;
 
   const T *rowsrc = reinterpret_cast<const T *>(PNL == 0 ? a.dy : a.x);
   const T *colsrc = reinterpret_cast<const T *>(PNL == 0 ? a.x : a.dy);

@@ -375,6 +375,8 @@ __device__ __forceinline__ f32x4 widen4(f32x4 r) {
 // registers and the forward state after the last chunk goes to final_state.
 // flip: the adjoint carries of the backward pass, which run against their
 // direction (forward: c downwards, reverse: c upwards), from zero.
+// Block-segmented reverse: the reverse carry (primal or adjoint) restarts
+// from zero at every chunk boundary that is a reverse block boundary.
 // With flip, out0 (if set) receives per-wave partial sums of <carry arriving
 // at chunk c, primal state after chunk c> (the primal carry-in of the next
 // chunk in scan order, from sin[d]): the chunk-boundary value of the decay
@@ -399,6 +401,7 @@ __global__ __launch_bounds__(kThreads) void k2_state_pass(ScanArgs a, int PN, in
   const int step = up ? 1 : -1;
   const int c0 = up ? 0 : nc - 1;
   const bool rpart = flip && a.out0;
+  const bool segrev = d == 1 && a.rseg_chunks > 0;
   const int nwv = PN / 256, wv = (blockIdx.x * kThreads + threadIdx.x) >> 6;
   const T *sinb = rpart ? reinterpret_cast<const T *>(a.sin[d]) + (int64_t)b * a.sin_bstride[d] +
                               (int64_t)h * PN + e
@@ -435,6 +438,9 @@ __global__ __launch_bounds__(kThreads) void k2_state_pass(ScanArgs a, int PN, in
       const f32x4 nb = rpart ? widen4(rn[i]) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       const float g = exp2_fast(rg[i]);
       if (nn + D < nc) fetch(i, c + D * step);
+      // the carry arriving at chunk c crosses chunk boundary c (from c - 1)
+      // or c + 1 (from c + 1)
+      if (segrev && (up ? c : c + 1) % a.rseg_chunks == 0) S = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       if (rpart) {
         // primal state after chunk c = primal carry-in of chunk c + 1
         // (forward) or c - 1 (reverse)
@@ -470,7 +476,8 @@ __global__ __launch_bounds__(kThreads) void k2_state_pass(ScanArgs a, int PN, in
 // SA_in(c+1) = 2^cdecay(c) (SA_in(c) + Tsum(c) S_in(c)) + ST_loc(c), from zero,
 // alongside the primal carry S_in (from init_state or zero), in each
 // direction's scan order; SA_in of every chunk goes to sin_t in T.  Loads run
-// D chunks ahead as in the state pass.
+// D chunks ahead as in the state pass.  Both carries of a block-segmented
+// reverse restart from zero at its block boundaries.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k2_tangent_pass(ScanArgs a, int PN) {
   const int e = (blockIdx.x * kThreads + threadIdx.x) * 4;
@@ -511,6 +518,10 @@ __global__ __launch_bounds__(kThreads) void k2_tangent_pass(ScanArgs a, int PN) 
       const f32x4 loc = widen4(rl[i]), tloc = widen4(rt[i]);
       const float g = exp2_fast(rg[i]), ts = rs[i];
       if (nn + D < nc) fetch(i, c + D * step);
+      if (d == 1 && a.rseg_chunks > 0 && (c + 1) % a.rseg_chunks == 0) {
+        S = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        SA = S;
+      }
       if constexpr (sizeof(T) == 2) {
         bf16x4 o;
 #pragma unroll
@@ -716,8 +727,20 @@ void k3_chunk_out(ScanArgs a) {
   // chunk 0 (the forward scan unless it continues from an initial state;
   // the reverse direction's adjoint in the dx pass), slot 1's at the last
   // chunk (the reverse scan; the forward direction's adjoint)
-  const bool has_in0 = a.sin[0] != nullptr && (c > 0 || (MODE != 2 && a.init_state != nullptr));
-  const bool has_in1 = a.sin[1] != nullptr && c < a.nchunks - 1;
+  // Block-segmented reverse: the slot that carries the reverse direction
+  // (slot 1; slot 0 in the dx pass) takes only the s-blocks of the row-block's
+  // reverse block, and no carry-in across a block boundary (the reverse's
+  // own carry crosses chunk boundary c + 1, its adjoint chunk boundary c).
+  constexpr int RSLOT = MODE == 2 ? 0 : 1;
+  const int segt = a.rseg_tiles;  // 0, 1 or 2
+  const int kseg0 = segt ? (j & ~(segt - 1)) : 0;
+  const int kseg1 = segt ? min(kseg0 + segt - 1, klast) : klast;
+  const int kf0 = RSLOT == 0 ? kseg0 : 0;      // slot 0's first s-block
+  const int kr0 = RSLOT == 1 ? kseg1 : klast;  // slot 1's first s-block
+  const bool cut = a.rseg_chunks > 0 && (RSLOT == 0 ? c : c + 1) % a.rseg_chunks == 0;
+  const bool has_in0 = a.sin[0] != nullptr && (c > 0 || (MODE != 2 && a.init_state != nullptr)) &&
+                       !(RSLOT == 0 && cut);
+  const bool has_in1 = a.sin[1] != nullptr && c < a.nchunks - 1 && !(RSLOT == 1 && cut);
 
   u32x4 pf[PF::NPF];
   auto prefetch_sblock = [&](int d, int k) __attribute__((always_inline)) {
@@ -758,7 +781,7 @@ void k3_chunk_out(ScanArgs a) {
         cdraw[m] = __builtin_amdgcn_raw_buffer_load_b32(rc, (uint32_t)(t0 + m * kRB + lane) * 4u, 0, 0);
     }
   }
-  prefetch_sblock(0, 0);
+  prefetch_sblock(0, kf0);
   if (w < 2 * HT) {
     // the empty asm keeps the decode (and so the wait for the dt loads)
     // behind the stage loads above
@@ -839,7 +862,7 @@ void k3_chunk_out(ScanArgs a) {
     // MODE 0 prefetches the reverse's first slab during the forward's last
     // stage; the backward modes finish each slot with an epilogue first and
     // issue it here, so the prefetch registers are not live across it
-    if (MODE != 0 && d == 1) prefetch_sblock(1, klast);
+    if (MODE != 0 && d == 1) prefetch_sblock(1, kr0);
     // per-head row factor 2^(lam_t - m) of this lane's Gram row t = 16w + r16,
     // applied to C.B^T together with the column factors
     float ut[HT], trow[HT];
@@ -854,7 +877,7 @@ void k3_chunk_out(ScanArgs a) {
     // operand mf (so the prefetch registers are free again), issue the next
     // stage's loads, then multiply with x from LDS.  Both directions visit
     // their off-diagonal s-blocks first (forward: 0 .. j - 1; reverse:
-    // klast down to j + 1) and the diagonal one (k = j) last, as an instance
+    // kr0 down to j + 1) and the diagonal one (k = j) last, as an instance
     // of its own: inside the loop the next stage is always an s-block, whose
     // loads go to the same registers.
     auto stage = [&](int k, auto diagc) __attribute__((always_inline)) {
@@ -987,7 +1010,7 @@ void k3_chunk_out(ScanArgs a) {
       __syncthreads();
       if (!DIAG) prefetch_sblock(d, d == 0 ? k + 1 : k - 1);
       else if (d == 0 ? has_in0 : has_in1) prefetch_state(d, 0);
-      else if (d == 0 && MODE == 0) prefetch_sblock(1, klast);
+      else if (d == 0 && MODE == 0) prefetch_sblock(1, kr0);
 #pragma unroll
       for (int hh = 0; hh < HT; ++hh)
 #pragma unroll
@@ -1005,9 +1028,9 @@ void k3_chunk_out(ScanArgs a) {
         }
     };
     if constexpr (d == 0) {
-      for (int k = 0; k < j; ++k) stage(k, std::false_type{});
+      for (int k = kf0; k < j; ++k) stage(k, std::false_type{});
     } else {
-      for (int k = klast; k > j; --k) stage(k, std::false_type{});
+      for (int k = kr0; k > j; --k) stage(k, std::false_type{});
     }
     stage(j, std::true_type{});
     // ---------------- carry-in term 2^lam_t C S_in^T, one head per stage.
@@ -1026,7 +1049,7 @@ void k3_chunk_out(ScanArgs a) {
         }
         __syncthreads();
         if (ih + 1 < HT / IH) prefetch_state(d, ih + 1);
-        else if (d == 0 && MODE == 0) prefetch_sblock(1, klast);
+        else if (d == 0 && MODE == 0) prefetch_sblock(1, kr0);
 #pragma unroll
         for (int q = 0; q < IH; ++q) {
           const int hh = ih * IH + q;

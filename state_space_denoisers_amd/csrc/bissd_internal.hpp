@@ -81,6 +81,13 @@ struct ScanArgs {
   float *dai_out;       // PHASE_YDOT: within-chunk A-tangent sums
                         // sum_{s before t} E[t][s] (T_t - T_s) per (dir, b, chunk,
                         // row-block, head), [2][Z][nchunks][chunk/64][H]
+  // Block-segmented reverse scan (0, 0: none).  rseg_chunks: chunks per
+  // reverse block, 1 when a block is no longer than a chunk; the reverse
+  // carries (primal, A-tangent, adjoint) are zero across every chunk
+  // boundary c * chunk with c % rseg_chunks == 0.  rseg_tiles: 64-token tiles
+  // per reverse block when a block is shorter than a chunk (1 or 2); the
+  // reverse direction's within-chunk pairs then stay inside their block.
+  int rseg_chunks, rseg_tiles;
 };
 
 enum {
@@ -129,6 +136,7 @@ struct BwdArgs {
   const float *cdtg;    // [2][Z][H][L] in-chunk cumulative dt (scan order)
   int64_t L;
   int Z, H, G, N, chunk, nchunks, dtype;
+  int rseg_tiles;  // as in ScanArgs: the reverse panels' column blocks stay in the row's block
 };
 
 hipError_t launch_bwd_panels(const BwdArgs &a, hipStream_t st);

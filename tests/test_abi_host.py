@@ -48,7 +48,7 @@ def test_no_torch_types_in_the_header():
 
 def shape(**kw):
     d = dict(batch=2, seqlen=300, nheads=8, headdim=64, dstate=128, ngroups=1, chunk=256,
-             dtype=_abi.BISSD_BF16, reserved=0)
+             dtype=_abi.BISSD_BF16, rev_block=0)
     d.update(kw)
     return _abi.Shape(**d)
 
@@ -89,10 +89,27 @@ def test_workspace_size(lib):
 @pytest.mark.parametrize("over,code", [
     (dict(batch=0), -2), (dict(seqlen=0), -2), (dict(nheads=6, ngroups=4), -2),
     (dict(headdim=32), -3), (dict(dstate=96), -3), (dict(chunk=100), -3),
-    (dict(dtype=7), -3), (dict(reserved=1), -2),
+    (dict(dtype=7), -3), (dict(rev_block=-64), -2), (dict(rev_block=32), -3),
+    (dict(rev_block=192), -3), (dict(rev_block=384), -3), (dict(rev_block=96, chunk=128), -3),
 ])
 def test_bad_shapes(lib, over, code):
     assert call_forward(lib, shape(**over)) == code
+
+
+@pytest.mark.parametrize("rb,chunk", [(64, 256), (128, 256), (256, 256), (512, 256), (1024, 256),
+                                      (64, 64), (192, 64), (128, 128)])
+def test_supported_reverse_blocks(lib, rb, chunk):
+    """Multiples of the 64-token tile that split a chunk evenly or span whole
+    chunks pass validation (the call then fails only on the fake workspace)."""
+    assert call_forward(lib, shape(rev_block=rb, chunk=chunk), nws=16) == -5
+
+
+def test_block_update_takes_no_reverse_block(lib):
+    s = shape(seqlen=64, chunk=64, rev_block=64)
+    rc = lib.bissd_block_update(C.byref(s), addr(20), addr(0), dirs(1), dirs(5), addr(9),
+                                addr(10), None, addr(12), C.c_size_t(1 << 40), None)
+    assert rc == -3
+    assert lib.bissd_workspace_size(C.byref(s), _abi.OP_BLOCK) == 0
 
 
 def test_null_and_alignment(lib):
