@@ -77,27 +77,29 @@ def dirs(T):
 
 
 class Forward:
-    """Preallocated forward call on one workload."""
+    """Preallocated forward call on one workload (rev_block > 0: the
+    block-segmented reverse of full-block training)."""
 
-    def __init__(self, w):
+    def __init__(self, w, rev_block=0):
         import torch
         import state_space_denoisers_amd as ssd
         from state_space_denoisers_amd import _abi
-        self.ssd, self.w = ssd, w
+        self.ssd, self.w, self.rb = ssd, w, rev_block
         self.inp, self.T = device_inputs(w)
         self.fwd, self.rev = dirs(self.T)
         self.y = torch.empty_like(self.T["x"])
-        shape = ssd.shape_of(self.T["x"], self.T["B_f"], w.chunk)
+        shape = ssd.shape_of(self.T["x"], self.T["B_f"], w.chunk, rev_block)
         n = ssd.bissd_workspace_size(shape, _abi.OP_FORWARD)
         self.ws = torch.empty(n, dtype=torch.uint8, device=self.y.device)
 
     def __call__(self):
         self.ssd.bissd_forward(self.T["x"], self.fwd, self.rev, self.T["D"], chunk=self.w.chunk,
-                               y=self.y, workspace=self.ws)
+                               rev_block=self.rb, y=self.y, workspace=self.ws)
 
     def phase(self, p):
         self.ssd.bissd_forward_phase(p, self.T["x"], self.fwd, self.rev, self.T["D"],
-                                     chunk=self.w.chunk, y=self.y, workspace=self.ws)
+                                     chunk=self.w.chunk, rev_block=self.rb, y=self.y,
+                                     workspace=self.ws)
 
 
 # ----------------------------------------------------------------- timing
@@ -307,25 +309,27 @@ class Train:
     """Preallocated forward + backward call on one workload (a training
     step of the scan: y, then every gradient of sum(dy * y))."""
 
-    def __init__(self, w):
+    def __init__(self, w, rev_block=0):
         import torch
         import state_space_denoisers_amd as ssd
         from state_space_denoisers_amd import _abi
         from synth import gen
-        self.ssd, self.w = ssd, w
-        self.f = Forward(w)
+        self.ssd, self.w, self.rb = ssd, w, rev_block
+        self.f = Forward(w, rev_block)
         dev = self.f.y.device
         inp = gen.make_inputs(w, with_dy=True)
         self.dy = gen.as_torch(inp["dy"], w.dtype, dev)
-        shape = ssd.shape_of(self.f.T["x"], self.f.T["B_f"], w.chunk)
+        shape = ssd.shape_of(self.f.T["x"], self.f.T["B_f"], w.chunk, rev_block)
         n = ssd.bissd_workspace_size(shape, _abi.OP_BACKWARD)
         self.ws = torch.empty(n, dtype=torch.uint8, device=dev)
         self.grads = ssd.bissd_backward(self.f.T["x"], self.f.fwd, self.f.rev, self.f.T["D"],
-                                        self.dy, chunk=w.chunk, workspace=self.ws)
+                                        self.dy, chunk=w.chunk, rev_block=rev_block,
+                                        workspace=self.ws)
 
     def backward(self):
         self.ssd.bissd_backward(self.f.T["x"], self.f.fwd, self.f.rev, self.f.T["D"], self.dy,
-                                chunk=self.w.chunk, grads=self.grads, workspace=self.ws)
+                                chunk=self.w.chunk, rev_block=self.rb, grads=self.grads,
+                                workspace=self.ws)
 
     def __call__(self):
         self.f()
@@ -342,20 +346,98 @@ def train_bytes_per_token(w):
     return per_token_bytes(w) + bwd
 
 
-def bench_train(steps):
+def bench_train(steps, rev_block=0):
+    """Forward + backward of the training workload; rev_block > 0 times the
+    full-block objective (reverse restarting at every block of that many
+    tokens)."""
     import torch
     from synth import gen
     w = gen.WORKLOADS["train_L2k"]
-    t = Train(w)
+    t = Train(w, rev_block)
     for _ in range(3):
         t()
     torch.cuda.synchronize()
     ms_f = event_time_ms(t.f, steps)
     ms_b = event_time_ms(t.backward, steps)
     ms = event_time_ms(t, steps)
-    return {"workload": w.name, "batch": w.Z, "seq_len": w.L, "tokens_per_s": w.tokens / (ms * 1e-3),
+    name = w.name + (f"_rev{rev_block}" if rev_block else "")
+    return {"workload": name, "batch": w.Z, "seq_len": w.L, "rev_block": rev_block,
+            "tokens_per_s": w.tokens / (ms * 1e-3),
             "ms_per_step": ms, "ms_forward": ms_f, "ms_backward": ms_b,
             "hbm_algorithmic_GBs": train_bytes_per_token(w) * w.tokens / (ms * 1e-3) / 1e9}
+
+
+def bench_generation(steps_per_block=8, blocks=2, prefix=65536):
+    """Block-wise generation after a long prefix, two ways, same kernels:
+    (a) a full-sequence bidirectional model re-scans prefix + every block so
+    far at each denoising step (bissd_forward over the whole sequence);
+    (b) the partially bidirectional model continues the cached prefix state
+    (bissd_block_update per step, committing the state after each block's
+    last step).  Batch 4, blocks of 64 tokens, bf16, 24 heads, N = 128.
+    The prefix's own encode is done once for (b) and not timed.  Both give
+    the active block the same output (the full scan's reverse over the last
+    block sees only that block), which is checked."""
+    import torch
+    import state_space_denoisers_amd as ssd
+    from synth import gen
+    w = gen.WORKLOADS["block_update"]
+    dev = torch.device("cuda", 0)
+    Lb = w.L
+    Lmax = prefix + blocks * Lb
+    seq = gen.prefix_on_device(w, Lmax, dev, seed=w.seed + 17)
+    A = gen.as_torch(gen.make_inputs(w)["A_f"], "fp32", dev)
+    D = gen.as_torch(gen.make_inputs(w)["D"], "fp32", dev)
+
+    def cut(lo, hi):
+        return {k: v[:, lo:hi].contiguous() for k, v in seq.items()}
+
+    full = [cut(0, prefix + (k + 1) * Lb) for k in range(blocks)]
+    blk = [cut(prefix + k * Lb, prefix + (k + 1) * Lb) for k in range(blocks)]
+    p = lambda T: (T["dt_f"], A, T["B_f"], T["C_f"])  # weight-tied directions
+    y_full = [torch.empty_like(f["x"]) for f in full]
+    from state_space_denoisers_amd import _abi
+    ws_full = [torch.empty(ssd.bissd_workspace_size(ssd.shape_of(f["x"], f["B_f"], 256),
+                                                    _abi.OP_FORWARD), dtype=torch.uint8, device=dev)
+               for f in full]
+    ws_blk = torch.empty(max(256, ssd.bissd_workspace_size(ssd.shape_of(blk[0]["x"], blk[0]["B_f"], 64),
+                                                            _abi.OP_BLOCK)), dtype=torch.uint8, device=dev)
+    y_blk = [torch.empty_like(b["x"]) for b in blk]
+    state0 = torch.empty((w.Z, w.H, w.P, w.N), dtype=torch.float32, device=dev)
+    pre = cut(0, prefix)
+    ssd.bissd_forward(pre["x"], p(pre), p(pre), D, chunk=256, final_state=state0)
+    del pre
+    state = torch.empty_like(state0)
+
+    def run_full():
+        for k in range(blocks):
+            for _ in range(steps_per_block):
+                ssd.bissd_forward(full[k]["x"], p(full[k]), p(full[k]), D, chunk=256,
+                                  y=y_full[k], workspace=ws_full[k])
+
+    def run_cached():
+        state.copy_(state0)
+        for k in range(blocks):
+            for s in range(steps_per_block):
+                last = s == steps_per_block - 1
+                ssd.bissd_block_update(state, blk[k]["x"], p(blk[k]), p(blk[k]), D, chunk=64,
+                                       y_blk=y_blk[k], state_out=state if last else None,
+                                       commit=last, workspace=ws_blk)
+
+    for fn in (run_full, run_cached):
+        fn()
+    torch.cuda.synchronize()
+    ms_full = event_time_ms(run_full, 3)
+    ms_cached = event_time_ms(run_cached, 10)
+    nstep = blocks * steps_per_block
+    agree = 0.0
+    for k in range(blocks):
+        ref = y_full[k][:, prefix + k * Lb:].float()
+        agree = max(agree, float((y_blk[k].float() - ref).abs().max() / ref.abs().max()))
+    return {"workload": f"generation_L{prefix // 1024}k", "prefix_tokens": prefix,
+            "block_tokens": Lb, "batch": w.Z, "blocks": blocks,
+            "steps_per_block": steps_per_block,
+            "ms_per_step_full_rescan": ms_full / nstep, "ms_per_step_block_update": ms_cached / nstep,
+            "speedup": ms_full / ms_cached, "active_block_y_maxrel_full_vs_cached": agree}
 
 
 # ------------------------------------------------------------- profiling
@@ -492,10 +574,20 @@ def main():
         except Exception as exc:
             extra["train_L2k"] = {"error": repr(exc)}
         try:
+            extra["train_L2k_rev64"] = bench_train(max(5, args.steps // 20), rev_block=64)
+            log(f"bench: train rev64 {extra['train_L2k_rev64']}")
+        except Exception as exc:
+            extra["train_L2k_rev64"] = {"error": repr(exc)}
+        try:
             extra["block_update"] = bench_block(max(50, args.steps))
             log(f"bench: block {extra['block_update']}")
         except Exception as exc:
             extra["block_update"] = {"error": repr(exc)}
+        try:
+            extra["generation_L64k"] = bench_generation()
+            log(f"bench: generation {extra['generation_L64k']}")
+        except Exception as exc:
+            extra["generation_L64k"] = {"error": repr(exc)}
 
     cpu = None
     if not args.no_cpu_baseline:

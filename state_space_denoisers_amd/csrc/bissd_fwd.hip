@@ -401,7 +401,11 @@ __global__ __launch_bounds__(kThreads) void k2_state_pass(ScanArgs a, int PN, in
   const int step = up ? 1 : -1;
   const int c0 = up ? 0 : nc - 1;
   const bool rpart = flip && a.out0;
-  const bool segrev = d == 1 && a.rseg_chunks > 0;
+  // block-segmented reverse: index of the chunk boundary the carry arriving
+  // at chunk c crosses (c from c - 1 upwards, c + 1 from c + 1 downwards),
+  // kept modulo the chunks per block as c steps, so the loop divides nothing
+  const int rsc = d == 1 ? a.rseg_chunks : 0;
+  int bmod = rsc ? (up ? c0 : c0 + 1) % rsc : 1;
   const int nwv = PN / 256, wv = (blockIdx.x * kThreads + threadIdx.x) >> 6;
   const T *sinb = rpart ? reinterpret_cast<const T *>(a.sin[d]) + (int64_t)b * a.sin_bstride[d] +
                               (int64_t)h * PN + e
@@ -438,9 +442,10 @@ __global__ __launch_bounds__(kThreads) void k2_state_pass(ScanArgs a, int PN, in
       const f32x4 nb = rpart ? widen4(rn[i]) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       const float g = exp2_fast(rg[i]);
       if (nn + D < nc) fetch(i, c + D * step);
-      // the carry arriving at chunk c crosses chunk boundary c (from c - 1)
-      // or c + 1 (from c + 1)
-      if (segrev && (up ? c : c + 1) % a.rseg_chunks == 0) S = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      const bool cut = rsc != 0 && bmod == 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) S[k] = cut ? 0.0f : S[k];
+      bmod = up ? (bmod + 1 == rsc ? 0 : bmod + 1) : (bmod == 0 ? rsc - 1 : bmod - 1);
       if (rpart) {
         // primal state after chunk c = primal carry-in of chunk c + 1
         // (forward) or c - 1 (reverse)
@@ -497,6 +502,10 @@ __global__ __launch_bounds__(kThreads) void k2_tangent_pass(ScanArgs a, int PN) 
     S = *reinterpret_cast<const f32x4 *>(a.init_state + ((int64_t)b * H + h) * PN + e);
   const int step = d == 0 ? 1 : -1;
   const int c0 = d == 0 ? 0 : nc - 1;
+  // block-segmented reverse: the carry into chunk c crosses boundary c + 1,
+  // kept modulo the chunks per block as c steps down
+  const int rsc = d == 1 ? a.rseg_chunks : 0;
+  int bmod = rsc ? (c0 + 1) % rsc : 1;
   constexpr int D = 4;
   typename Raw4<T>::type rl[D], rt[D];
   float rg[D], rs[D];
@@ -518,10 +527,13 @@ __global__ __launch_bounds__(kThreads) void k2_tangent_pass(ScanArgs a, int PN) 
       const f32x4 loc = widen4(rl[i]), tloc = widen4(rt[i]);
       const float g = exp2_fast(rg[i]), ts = rs[i];
       if (nn + D < nc) fetch(i, c + D * step);
-      if (d == 1 && a.rseg_chunks > 0 && (c + 1) % a.rseg_chunks == 0) {
-        S = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        SA = S;
+      const bool cut = rsc != 0 && bmod == 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        S[k] = cut ? 0.0f : S[k];
+        SA[k] = cut ? 0.0f : SA[k];
       }
+      bmod = bmod == 0 ? rsc - 1 : bmod - 1;
       if constexpr (sizeof(T) == 2) {
         bf16x4 o;
 #pragma unroll
