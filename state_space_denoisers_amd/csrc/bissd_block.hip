@@ -18,7 +18,12 @@
 // at once (B_f, B'_r and x rows and the cached state copied buffer -> LDS,
 // C rows and dt into registers), the workgroup waits once, and both
 // directions, the skip and the committed state follow without another
-// global round trip.
+// global round trip.  The two directions run side by side in two groups of
+// four waves (a batch of a few rows leaves most compute units idle, so each
+// workgroup's critical path is what counts): the forward group adds the
+// carried state, the reverse group forms the committed state, and the
+// reverse outputs reach the forward group through LDS for the one write of
+// y.
 #include "bissd_device.hpp"
 #include "bissd_internal.hpp"
 
@@ -35,12 +40,15 @@ template <typename T, int N> struct BlockLds {
   float dtv[2][kRB];
 };
 
-// Workgroup = (batch b, head h); wave w owns block rows t = 16 w .. 16 w + 15
-// (and, for the committed state, state rows p = 16 w .. 16 w + 15).  Decay
+constexpr int kBlkThreads = 2 * kThreads;  // two groups of four waves
+
+// Workgroup = (batch b, head h), two groups of four waves: group d takes
+// direction d.  Wave w of a group owns block rows t = 16 w .. 16 w + 15 (and,
+// in the reverse group, committed state rows p = 16 w .. 16 w + 15).  Decay
 // weights are formed exactly per element (the block is a single 64 x 64
 // tile), masked by selection.
 template <typename T, int N>
-__global__ __launch_bounds__(kThreads) void k_block_update(ScanArgs a) {
+__global__ __launch_bounds__(kBlkThreads) void k_block_update(ScanArgs a) {
   using Sm = BlockLds<T, N>;
   using DB = typename Sm::DB;
   using DX = typename Sm::DX;
@@ -50,36 +58,38 @@ __global__ __launch_bounds__(kThreads) void k_block_update(ScanArgs a) {
   __shared__ __attribute__((aligned(16))) char tBr[kRB * Sm::BRB];
   __shared__ __attribute__((aligned(16))) char tX[kRB * Sm::XRB];
   __shared__ __attribute__((aligned(16))) char tS[kP * Sm::SRB];
+  // the reverse group's outputs, [row block of wave w][v][lane] as f32x4
+  __shared__ __attribute__((aligned(16))) f32x4 xchg[4][4][64];
   constexpr int NK = N / 32, NT = N / 16;
   constexpr uint32_t ES = sizeof(T);
-  const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
+  const int tid = threadIdx.x, wv = wave_id(), lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
+  const int grp = wv >> 2, w = wv & 3;
   const int h = blockIdx.x % a.H, b = blockIdx.x / a.H;
   const int H = a.H, G = a.G, gidx = h / (H / G);
   const int L = (int)a.L;  // block length, 1..64
   const uint32_t brs = (uint32_t)(G * N * ES), xrs = (uint32_t)(H * kP * ES);
 
-  // ---- every load of the workgroup, issued at once
-  const bufres rBf = make_buf(reinterpret_cast<const T *>(a.B[0]) + (int64_t)b * L * G * N, (uint32_t)(L * G * N * ES));
-  const bufres rBr = make_buf(reinterpret_cast<const T *>(a.B[1]) + (int64_t)b * L * G * N, (uint32_t)(L * G * N * ES));
-  const bufres rCf = make_buf(reinterpret_cast<const T *>(a.C[0]) + (int64_t)b * L * G * N, (uint32_t)(L * G * N * ES));
-  const bufres rCr = make_buf(reinterpret_cast<const T *>(a.C[1]) + (int64_t)b * L * G * N, (uint32_t)(L * G * N * ES));
-  const bufres rX = make_buf(reinterpret_cast<const T *>(a.x) + (int64_t)b * L * H * kP, (uint32_t)(L * H * kP * ES));
+  // ---- every load of the workgroup, issued at once: the forward group
+  // copies B_f and x, the reverse group B'_r and the cached state; each
+  // group loads its own C rows and one of its waves its dt
+  const bufres rB = make_buf(reinterpret_cast<const T *>(a.B[grp]) + (int64_t)b * L * G * N, (uint32_t)(L * G * N * ES));
+  const bufres rC = make_buf(reinterpret_cast<const T *>(a.C[grp]) + (int64_t)b * L * G * N, (uint32_t)(L * G * N * ES));
   const float *sin = a.init_state + ((int64_t)b * H + h) * kP * N;
-  DB::load(tBf, rBf, (uint32_t)gidx * N * ES, brs, kRB);
-  DB::load(tBr, rBr, (uint32_t)gidx * N * ES, brs, kRB);
-  DX::load(tX, rX, (uint32_t)h * kP * ES, xrs, kRB);
-  DS::load(tS, make_buf(sin, (uint32_t)(kP * N * 4)), 0u, (uint32_t)Sm::SRB, kP);
-  const int trow = 16 * w + r16;
-  Frag<T> cf[NK], cr[NK];
-#pragma unroll
-  for (int ks = 0; ks < NK; ++ks) {
-    const uint32_t off = (uint32_t)(trow * G + gidx) * N * ES + (32 * ks + 8 * g4) * ES;
-    frag_bload(cf[ks], rCf, off);
-    frag_bload(cr[ks], rCr, off);
+  DB::load(grp == 0 ? tBf : tBr, rB, (uint32_t)gidx * N * ES, brs, kRB, w, 4);
+  if (grp == 0) {
+    const bufres rX = make_buf(reinterpret_cast<const T *>(a.x) + (int64_t)b * L * H * kP, (uint32_t)(L * H * kP * ES));
+    DX::load(tX, rX, (uint32_t)h * kP * ES, xrs, kRB, w, 4);
+  } else {
+    DS::load(tS, make_buf(sin, (uint32_t)(kP * N * 4)), 0u, (uint32_t)Sm::SRB, kP, w, 4);
   }
-  for (int d = w; d < 2; d += 4)
-    chunk_decay_scan<T>(reinterpret_cast<const T *>(a.dt[d]) + (int64_t)b * L * H + h, H, L, kRB,
-                        a.A[d][h] * kLog2e, d == 1, sm.lam[d], sm.dtv[d]);
+  const int trow = 16 * w + r16;
+  Frag<T> cf[NK];
+#pragma unroll
+  for (int ks = 0; ks < NK; ++ks)
+    frag_bload(cf[ks], rC, (uint32_t)(trow * G + gidx) * N * ES + (32 * ks + 8 * g4) * ES);
+  if (w == 0)
+    chunk_decay_scan<T>(reinterpret_cast<const T *>(a.dt[grp]) + (int64_t)b * L * H + h, H, L, kRB,
+                        a.A[grp][h] * kLog2e, grp == 1, sm.lam[grp], sm.dtv[grp]);
   wait_vmem();
   __syncthreads();
 
@@ -87,7 +97,7 @@ __global__ __launch_bounds__(kThreads) void k_block_update(ScanArgs a) {
 #pragma unroll
   for (int v = 0; v < 4; ++v) zero4(acc[v]);
 
-  // ---- both directions' within-block terms
+  // ---- one direction's within-block terms (cf holds this group's C rows)
   auto direction = [&](auto dc) __attribute__((always_inline)) {
     constexpr int d = decltype(dc)::value;
     const char *Bt = d == 0 ? tBf : tBr;
@@ -103,7 +113,7 @@ __global__ __launch_bounds__(kThreads) void k_block_update(ScanArgs a) {
         if (u < ulo || u > uhi) continue;
         Frag<T> bf;
         frag_ld8_swz<DB>(bf, Bt, 16 * u + r16, 32 * ks + 8 * g4);
-        mma(cb[u], bf, d == 0 ? cf[ks] : cr[ks]);
+        mma(cb[u], bf, cf[ks]);
       }
     }
     const float lt = sm.lam[d][trow];
@@ -145,12 +155,18 @@ __global__ __launch_bounds__(kThreads) void k_block_update(ScanArgs a) {
       }
     }
   };
-  direction(std::integral_constant<int, 0>{});
-  direction(std::integral_constant<int, 1>{});
+  if (grp == 0) {
+    direction(std::integral_constant<int, 0>{});
+  } else {
+    direction(std::integral_constant<int, 1>{});
+#pragma unroll
+    for (int v = 0; v < 4; ++v) xchg[w][v][lane] = acc[v];
+  }
 
-  // ---- committed state: S_out = 2^lam_last S_in + sum_s w_s x_s (outer) B_s,
-  // w_s = 2^(lam_last - lam_s) dt_s; wave w owns state rows p = 16w..16w+15
-  if (a.final_state) {
+  // ---- committed state (reverse group): S_out = 2^lam_last S_in +
+  // sum_s w_s x_s (outer) B_s, w_s = 2^(lam_last - lam_s) dt_s; wave w owns
+  // state rows p = 16w..16w+15
+  if (grp == 1 && a.final_state) {
     const float lend = sm.lam[0][kRB - 1];  // tokens past the block have dt = 0
     f32x4 sacc[NT];
 #pragma unroll
@@ -187,8 +203,17 @@ __global__ __launch_bounds__(kThreads) void k_block_update(ScanArgs a) {
       }
   }
 
-  // ---- y = acc + D x from registers (rows 16w + 4 g4 + i, columns
-  // 16 v + r16; 16 lanes store one contiguous row segment), x from its tile
+  __syncthreads();
+  if (grp == 1) return;
+  // ---- y = forward + reverse + D x (forward group; rows 16w + 4 g4 + i,
+  // columns 16 v + r16; 16 lanes store one contiguous row segment), x from
+  // its tile
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const f32x4 r = xchg[w][v][lane];
+#pragma unroll
+    for (int i2 = 0; i2 < 4; ++i2) acc[v][i2] += r[i2];
+  }
   const float Dh = a.D[h];
   T *yg = reinterpret_cast<T *>(a.y) + ((int64_t)b * L * H + h) * kP;
 #pragma unroll
@@ -206,7 +231,7 @@ __global__ __launch_bounds__(kThreads) void k_block_update(ScanArgs a) {
 
 template <typename T, int N>
 static void launch_block_t(const ScanArgs &a, hipStream_t st) {
-  hipLaunchKernelGGL((k_block_update<T, N>), dim3((unsigned)(a.Z * a.H)), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((k_block_update<T, N>), dim3((unsigned)(a.Z * a.H)), dim3(kBlkThreads), 0, st, a);
 }
 
 hipError_t launch_block_update(const ScanArgs &a, hipStream_t st) {

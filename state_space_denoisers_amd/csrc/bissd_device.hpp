@@ -534,12 +534,13 @@ template <int RB, int SW> struct DmaTile {
     return y * RB + ((((x >> 4) ^ swz(y)) << 4) | (x & 15));
   }
   // copy rows [0, nrows) (nrows a multiple of RPP) of the slab starting at
-  // byte off0 of r, rows rs bytes apart
+  // byte off0 of r, rows rs bytes apart; the pieces are spread over nw
+  // waves, of which the calling one is wave wv
   __device__ static __forceinline__ void load(char *tile, bufres r, uint32_t off0, uint32_t rs,
-                                              int nrows) {
-    const int wv = wave_id(), l = threadIdx.x & 63;
+                                              int nrows, int wv = wave_id(), int nw = kThreads / 64) {
+    const int l = threadIdx.x & 63;
     const int np = nrows / RPP;
-    for (int p = wv; p < np; p += kThreads / 64) {
+    for (int p = wv; p < np; p += nw) {
       const int y = p * RPP + l / CPR, c = l % CPR;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_vptr)(tile + p * 1024), 16,
                                                off0 + y * rs + 16 * (c ^ swz(y)), 0, 0, 0);

@@ -126,7 +126,7 @@ template <typename T, int N, int HT> struct K1Lds {
 // workgroup.
 template <typename T, int N, int HT, int MODE>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu((MODE == 0 && sizeof(T) == 2) ? 3 : 1)))
+__attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 3 : 1)))
 void k1_chunk_state(ScanArgs a) {
   using Sm = K1Lds<T, N, HT>;
   using SB = SlabRows<T, N, Sm::BPT>;
@@ -688,7 +688,7 @@ template <typename T, int N, int HT, bool SF32> struct K3Pf {
 // the result: dy_t (B_t.C_t) into G_t B_t for dx and x.(G_t B_t).
 template <typename T, int N, int HT, bool SF32, int MODE>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? (MODE != 0 ? 2 : (SF32 ? 1 : 4)) : 1)))
+__attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? (MODE == 1 ? 3 : MODE == 2 ? 2 : (SF32 ? 1 : 4)) : 1)))
 void k3_chunk_out(ScanArgs a) {
   using Sm = K3Lds<T, N, HT>;
   using PF = K3Pf<T, N, HT, SF32>;
