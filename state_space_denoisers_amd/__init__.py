@@ -47,27 +47,38 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
+_SHAPES: dict = {}
+
+
 def shape_of(x: torch.Tensor, B: torch.Tensor, chunk: int, rev_block: int = 0) -> _abi.Shape:
-    Z, L, H, P = x.shape
-    G, N = B.shape[2], B.shape[3]
-    return _abi.Shape(Z, L, H, P, N, G, int(chunk), _dtype_code(x), int(rev_block))
+    """The ABI shape struct for x / B (memoised: block updates call this in
+    tight loops, and the C side only reads it)."""
+    key = (x.shape, B.shape, x.dtype, chunk, rev_block)
+    s = _SHAPES.get(key)
+    if s is None:
+        Z, L, H, P = x.shape
+        G, N = B.shape[2], B.shape[3]
+        s = _abi.Shape(Z, L, H, P, N, G, int(chunk), _dtype_code(x), int(rev_block))
+        if len(_SHAPES) > 1024:
+            _SHAPES.clear()
+        _SHAPES[key] = s
+    return s
 
 
 def _ptr(t: Optional[torch.Tensor]):
+    """Device address of a contiguous tensor (None for NULL)."""
     if t is None:
         return None
     if not t.is_contiguous():
         raise ValueError("tensors passed to libbissd must be contiguous")
-    return C.c_void_p(t.data_ptr())
+    return t.data_ptr()
 
 
 def _dir(d) -> _abi.Dir:
-    d = Dir(*d)
-    for name, t, want in (("dt", d.dt, None), ("A", d.A, torch.float32),
-                          ("B", d.B, None), ("C", d.C, None)):
-        if want is not None and t.dtype != want:
-            raise TypeError(f"{name} must be {want}, got {t.dtype}")
-    return _abi.Dir(_ptr(d.dt), _ptr(d.A), _ptr(d.B), _ptr(d.C))
+    dt, A, B, Cm = d
+    if A.dtype != torch.float32:
+        raise TypeError(f"A must be torch.float32, got {A.dtype}")
+    return _abi.Dir(_ptr(dt), _ptr(A), _ptr(B), _ptr(Cm))
 
 
 def _stream(device: torch.device, stream) -> C.c_void_p:
@@ -80,9 +91,9 @@ def bissd_workspace_size(shape: _abi.Shape, op: int) -> int:
 
 
 def _workspace(shape, op, device, workspace):
-    n = bissd_workspace_size(shape, op)
     if workspace is not None:
         return workspace, workspace.numel() * workspace.element_size()
+    n = bissd_workspace_size(shape, op)
     ws = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
     return ws, ws.numel()
 

@@ -260,6 +260,7 @@ static int forward_impl(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, 
   a.ndir = 2;
   a.init_state = init_state;
   a.final_state = final_state;
+  a.skip_edges = 1;
   const int64_t PN = s->headdim * s->dstate;
   a.sin_t = ws + wl.sin_t;
   const size_t esz = s->dtype == BISSD_BF16 ? 2 : 4;

@@ -418,6 +418,15 @@ __global__ __launch_bounds__(kThreads) void k2_state_pass(ScanArgs a, int PN, in
   constexpr int D = 8;
   typename Raw4<T>::type rl[D], rn[D];
   float rg[D];
+  // Forward calls (skip_edges) leave out what the output kernel never reads:
+  // the carry-in of the first chunk in scan order (zero, unless the forward
+  // scan starts from init_state) and the state of the last chunk in scan
+  // order (it only feeds final_state).
+  const bool edge = a.skip_edges && !flip;
+  const bool write_first = !edge || (primal_fwd && a.init_state);
+  const int nload = (edge && !(primal_fwd && a.final_state)) ? nc - 1 : nc;
+#pragma unroll
+  for (int i = 0; i < D; ++i) rl[i] = {};
   auto fetch = [&](int slot, int cc) __attribute__((always_inline)) {
     rl[slot] = load4raw(src + cc * cs);
     rg[slot] = dec[(int64_t)cc * H];
@@ -429,7 +438,7 @@ __global__ __launch_bounds__(kThreads) void k2_state_pass(ScanArgs a, int PN, in
   };
 #pragma unroll
   for (int i = 0; i < D; ++i)
-    if (i < nc) fetch(i, c0 + i * step);
+    if (i < nload) fetch(i, c0 + i * step);
   for (int n = 0; n < nc; n += D) {
 #pragma unroll
     for (int i = 0; i < D; ++i) {
@@ -441,7 +450,7 @@ __global__ __launch_bounds__(kThreads) void k2_state_pass(ScanArgs a, int PN, in
       const f32x4 loc = widen4(rl[i]);
       const f32x4 nb = rpart ? widen4(rn[i]) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       const float g = exp2_fast(rg[i]);
-      if (nn + D < nc) fetch(i, c + D * step);
+      if (nn + D < nload) fetch(i, c + D * step);
       const bool cut = rsc != 0 && bmod == 0;
 #pragma unroll
       for (int k = 0; k < 4; ++k) S[k] = cut ? 0.0f : S[k];
@@ -459,7 +468,7 @@ __global__ __launch_bounds__(kThreads) void k2_state_pass(ScanArgs a, int PN, in
         if ((threadIdx.x & 63) == 0)
           a.out0[((((int64_t)d * a.Z + b) * nc + c) * H + h) * nwv + wv] = v;
       }
-      if (dst) {
+      if (dst && (nn > 0 || write_first)) {
         if constexpr (sizeof(T) == 2) {
           bf16x4 o;
 #pragma unroll
