@@ -381,3 +381,80 @@ def test_segmented_backward_reverse_gradients_come_block_by_block():
             assert rel(seg[k][:, lo:hi], blk[k]) < 1e-13, (k, lo)
         dA += blk["dA_r"]
     assert rel(seg["dA_r"], dA) < 1e-12
+
+
+# ------------------------------------------------- P13 attention (hybrids)
+
+from oracle import attention as AT
+
+
+def _qkv(Z, L, H, D, seed):
+    r = np.random.default_rng(seed)
+    return (r.standard_normal((Z, L, H, D)), r.standard_normal((Z, L, H, D)),
+            r.standard_normal((Z, L, H, D)))
+
+
+def test_attention_zero_queries_average_the_visible_values():
+    """Q = 0: every visible key scores the same, so each query gets the plain
+    mean of the values it may see (full: all L; block-wise: blocks up to its own)."""
+    Z, L, H, D = 2, 37, 3, 8
+    _, k, v = _qkv(Z, L, H, D, 40)
+    q = np.zeros_like(k)
+    o = AT.forward(q, k, v)
+    assert np.allclose(o, np.broadcast_to(v.mean(axis=1, keepdims=True), o.shape), atol=1e-14)
+    ob = AT.forward(q, k, v, block=8)
+    for t in range(L):
+        hi = (t // 8 + 1) * 8
+        assert np.allclose(ob[:, t], v[:, :min(hi, L)].mean(axis=1), atol=1e-14), t
+
+
+def test_attention_sharp_scores_select_one_value():
+    """Keys equal to large multiples of orthonormal directions and each query
+    along one of them: the softmax is one-hot (to fp64 precision) on that key."""
+    Z, L, H, D = 1, 16, 2, 16
+    r = np.random.default_rng(41)
+    basis = np.linalg.qr(r.standard_normal((D, D)))[0]
+    k = np.zeros((Z, L, H, D))
+    v = r.standard_normal((Z, L, H, D))
+    q = np.zeros((Z, L, H, D))
+    perm = r.permutation(L)
+    for h in range(H):
+        k[0, :, h] = basis[:L] * 60.0
+        q[0, :, h] = basis[perm] * 60.0
+    o = AT.forward(q, k, v)
+    for h in range(H):
+        assert np.allclose(o[0, :, h], v[0, perm, h], atol=1e-12)
+
+
+def test_attention_full_is_invariant_to_key_order_and_key_shift():
+    """Full bidirectional attention: permuting keys with their values changes
+    nothing, and adding one vector c to every key shifts all scores of a
+    query by the same q.c, which the softmax removes."""
+    Z, L, H, D = 2, 29, 2, 8
+    q, k, v = _qkv(Z, L, H, D, 42)
+    o = AT.forward(q, k, v)
+    p = np.random.default_rng(43).permutation(L)
+    assert np.allclose(AT.forward(q, k[:, p], v[:, p]), o, atol=1e-12)
+    c = np.random.default_rng(44).standard_normal(D)
+    assert np.allclose(AT.forward(q, k + c, v), o, atol=1e-12)
+
+
+def test_attention_block_wise_is_full_attention_on_the_prefix():
+    """A query of block i, block-wise, equals full attention over the tokens
+    of blocks 0..i: the cache-consistency of block diffusion."""
+    Z, L, H, D, blk = 1, 50, 2, 8, 16
+    q, k, v = _qkv(Z, L, H, D, 45)
+    o = AT.forward(q, k, v, block=blk)
+    for i in range((L + blk - 1) // blk):
+        hi = min((i + 1) * blk, L)
+        full = AT.forward(q[:, :hi], k[:, :hi], v[:, :hi])
+        assert np.allclose(o[:, i * blk:hi], full[:, i * blk:hi], rtol=0, atol=1e-13), i
+
+
+def test_attention_single_token_and_scale():
+    Z, L, H, D = 1, 1, 2, 4
+    q, k, v = _qkv(Z, L, H, D, 46)
+    assert np.allclose(AT.forward(q, k, v), v, atol=1e-15)
+    # scale multiplies the scores: scale s on q is the same as s on the scores
+    q, k, v = _qkv(1, 9, 1, 4, 47)
+    assert np.allclose(AT.forward(q, k, v, scale=0.3), AT.forward(0.3 * q, k, v, scale=1.0), atol=1e-13)
