@@ -202,6 +202,43 @@ int bissd_forward_phase(const bissd_shape_t *shape, const void *x, bissd_dir_t f
                         float *final_state, void *workspace, size_t workspace_bytes,
                         void *stream, int phase);
 
+/*
+ * Multi-head softmax attention of the hybrid backbones, which interleave
+ * attention blocks with the bidirectional Mamba-2 blocks ("DiffMamba
+ * Checkpoints" model card, Hybrid Mamba+attention checkpoints: full
+ * bidirectional attention; "DiffuMamba: High-Throughput Diffusion LMs with
+ * Mamba Backbone", Core Architecture: one multi-head attention block every
+ * five Mamba blocks; "Training Hybrid Block Diffusion Language Models with
+ * Partial Bidirectionality", Methodology: the block-wise BDLM attention).
+ * Per batch row and head:
+ *
+ *   O = softmax(scale Q K^T + M) V      (softmax over the keys)
+ *
+ * M[t][s] = 0 where query t may see key s, -inf elsewhere: everywhere when
+ * block == 0 (full bidirectional attention); with block > 0, where
+ * floor(s / block) <= floor(t / block) (the query's block and the blocks
+ * before it).
+ *   shape  headdim == 64; block 0 or a multiple of 64; dtype BISSD_F32 or
+ *          BISSD_BF16 (q, k, v and o); reserved 0.
+ *   q, k, v, o  [batch][seqlen][nheads][headdim] device pointers, 16-byte
+ *          aligned; o must not overlap q, k or v.
+ *   scale  > 0, or 0 for 1 / sqrt(headdim).
+ * Scores, softmax and the P V accumulation are fp32; o is rounded once.
+ * Asynchronous on `stream`; allocates nothing; status codes as above.
+ */
+typedef struct {
+  int64_t batch;    /* Z */
+  int64_t seqlen;   /* L */
+  int64_t nheads;   /* H (q, k and v have the same heads) */
+  int64_t headdim;  /* 64 */
+  int64_t block;    /* 0: full bidirectional; > 0: block-wise, blocks of this many tokens */
+  int32_t dtype;    /* BISSD_F32 or BISSD_BF16 */
+  int32_t reserved; /* must be 0 */
+} bissd_attn_shape_t;
+
+int bissd_attention_forward(const bissd_attn_shape_t *shape, const void *q, const void *k,
+                            const void *v, float scale, void *o, void *stream);
+
 /* Text of a status code (static storage). */
 const char *bissd_status_string(int status);
 

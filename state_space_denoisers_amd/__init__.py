@@ -23,7 +23,8 @@ import torch
 from . import _abi
 
 __all__ = ["Dir", "bissd_forward", "bissd_forward_phase", "bissd_block_update", "bissd_backward",
-           "bissd_workspace_size", "shape_of", "library_path", "BissdError"]
+           "bissd_attention_forward", "bissd_workspace_size", "shape_of", "library_path",
+           "BissdError"]
 
 BissdError = _abi.BissdError
 
@@ -195,3 +196,22 @@ def bissd_backward(x: torch.Tensor, fwd, rev, D: torch.Tensor, dy: torch.Tensor,
                             _ptr(ws), C.c_size_t(nws), _stream(x.device, stream))
     _abi.check("bissd_backward", st)
     return g
+
+
+def bissd_attention_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
+                            block: int = 0, scale: float = 0.0,
+                            o: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """O = softmax(scale Q K^T + M) V per head (include/bissd.h,
+    bissd_attention_forward): q, k, v [Z, L, H, 64]; block 0 for full
+    bidirectional attention, > 0 for block-wise; scale 0 for 1/sqrt(64)."""
+    lib = _abi.load()
+    Z, L, H, Dh = q.shape
+    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k and v must have one shape and dtype")
+    shape = _abi.AttnShape(Z, L, H, Dh, int(block), _dtype_code(q), 0)
+    if o is None:
+        o = torch.empty_like(q)
+    st = lib.bissd_attention_forward(C.byref(shape), _ptr(q), _ptr(k), _ptr(v), float(scale),
+                                     _ptr(o), _stream(q.device, stream))
+    _abi.check("bissd_attention_forward", st)
+    return o

@@ -24,14 +24,20 @@ STATUS = {
 
 # every symbol include/bissd.h declares
 EXPORTS = ("bissd_workspace_size", "bissd_forward", "bissd_backward", "bissd_block_update",
-           "bissd_forward_phase", "bissd_status_string", "bissd_last_hip_error",
-           "bissd_version")
+           "bissd_forward_phase", "bissd_attention_forward", "bissd_status_string",
+           "bissd_last_hip_error", "bissd_version")
 
 
 class Shape(C.Structure):
     _fields_ = [("batch", C.c_int64), ("seqlen", C.c_int64), ("nheads", C.c_int64),
                 ("headdim", C.c_int64), ("dstate", C.c_int64), ("ngroups", C.c_int64),
                 ("chunk", C.c_int64), ("dtype", C.c_int32), ("rev_block", C.c_int32)]
+
+
+class AttnShape(C.Structure):
+    _fields_ = [("batch", C.c_int64), ("seqlen", C.c_int64), ("nheads", C.c_int64),
+                ("headdim", C.c_int64), ("block", C.c_int64), ("dtype", C.c_int32),
+                ("reserved", C.c_int32)]
 
 
 class Dir(C.Structure):
@@ -82,6 +88,9 @@ def load(path: str = LIB_PATH) -> C.CDLL:
         lib.bissd_block_update.argtypes = [C.POINTER(Shape), C.c_void_p, C.c_void_p, Dir, Dir,
                                            C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                            C.c_size_t, C.c_void_p]
+        lib.bissd_attention_forward.restype = C.c_int
+        lib.bissd_attention_forward.argtypes = [C.POINTER(AttnShape), C.c_void_p, C.c_void_p,
+                                                C.c_void_p, C.c_float, C.c_void_p, C.c_void_p]
         lib.bissd_status_string.restype = C.c_char_p
         lib.bissd_status_string.argtypes = [C.c_int]
         lib.bissd_last_hip_error.restype = C.c_int

@@ -2,6 +2,7 @@
 // argument validation, workspace carving and launch sequencing.  Every check
 // runs on the host before anything is enqueued, so a rejected call launches
 // nothing and touches no output.
+#include <math.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -546,6 +547,39 @@ int bissd_backward(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, bissd
   if (e == hipSuccess) e = bissd::launch_bwd_panels(b, st);
   if (e == hipSuccess) e = bissd::launch_bwd_decay(b, st);
   return finish(e);
+}
+
+int bissd_attention_forward(const bissd_attn_shape_t *s, const void *q, const void *k,
+                            const void *v, float scale, void *o, void *stream) {
+  if (!s) return BISSD_ERR_NULL;
+  if (s->batch <= 0 || s->seqlen <= 0 || s->nheads <= 0 || s->headdim <= 0 || s->block < 0 ||
+      s->reserved != 0 || !(scale >= 0.0f) || !isfinite(scale))
+    return BISSD_ERR_SHAPE;
+  if (s->headdim != bissd::kAttnD || s->block % 64 != 0) return BISSD_ERR_UNSUPPORTED;
+  if (s->dtype != BISSD_F32 && s->dtype != BISSD_BF16) return BISSD_ERR_UNSUPPORTED;
+  const int64_t es = s->dtype == BISSD_BF16 ? 2 : 4;
+  // one buffer resource per batch row (< 4 GiB); grid within 2^31
+  if (s->batch > (1 << 20) || s->nheads > 4096 || s->seqlen * s->nheads * s->headdim * es >= ((int64_t)1 << 32))
+    return BISSD_ERR_UNSUPPORTED;
+  if (s->batch * s->nheads * ceil_div(s->seqlen, 64) >= ((int64_t)1 << 31)) return BISSD_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !o) return BISSD_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return BISSD_ERR_ALIGN;
+  const size_t n = (size_t)(s->batch * s->seqlen * s->nheads * s->headdim * es);
+  if (overlap(o, n, q, n) || overlap(o, n, k, n) || overlap(o, n, v, n)) return BISSD_ERR_ALIAS;
+  bissd::AttnArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.L = s->seqlen;
+  a.block = s->block;
+  a.Z = (int)s->batch;
+  a.H = (int)s->nheads;
+  a.dtype = s->dtype;
+  const float sc = scale > 0.0f ? scale : 1.0f / sqrtf((float)s->headdim);
+  a.scale_log2 = sc * 1.4426950408889634f;
+  return finish(bissd::launch_attention(a, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -1,0 +1,183 @@
+// bissd_attn.hip -- multi-head softmax attention of the hybrid backbones
+// (gfx950): O = softmax(scale Q K^T + M) V per (batch row, head), head dim 64.
+//
+// The hybrids put attention between the bidirectional Mamba-2 blocks: full
+// bidirectional attention ("DiffMamba Checkpoints" model card, Hybrid
+// Mamba+attention checkpoints; "DiffuMamba: High-Throughput Diffusion LMs
+// with Mamba Backbone", Core Architecture: one multi-head attention block
+// every five Mamba blocks), or block-wise attention in block diffusion, where
+// a block sees the prefix before it and itself ("Training Hybrid Block
+// Diffusion Language Models with Partial Bidirectionality", Methodology, the
+// BDLM attention baseline).  M is 0 where a query may see a key and -inf
+// elsewhere.
+//
+// One pass over the keys with a running softmax: each workgroup takes 64
+// queries of one (batch, head) and streams 64-key tiles of K and V through
+// LDS (copied buffer -> LDS, the next tile in flight while the current one
+// is used).  Per tile, each wave forms its 16 queries' scores as S^T = K Q^T
+// on the matrix cores, so that a lane holds one query's scores for 16 keys
+// in exactly the layout of the A operand of the following P V product; the
+// row maximum and sum take two lane exchanges; the output rows are
+// rescaled by exp2(m_old - m_new) before P V is added.  Scores are kept in
+// log2 units (scale * log2(e) folded in), so every exponential is one exp2.
+#include <math.h>
+
+#include "bissd_device.hpp"
+#include "bissd_internal.hpp"
+
+namespace bissd {
+
+template <typename T> struct AttnTiles {
+  static constexpr int RB = kAttnD * (int)sizeof(T);  // bytes of one head's token row
+  using DK = DmaTile<RB, SW_NAT>;  // keys: read as natural rows
+  using DV = DmaTile<RB, SW_TR>;   // values: read along the key index
+};
+
+// Workgroup = (batch b, head h, 64-query tile); wave w owns queries
+// q0 + 16 w + (0..15).  Queries past L compute on zeros and are not stored;
+// keys past the visible end are masked to -inf.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_attn_fwd(AttnArgs a) {
+  using DK = typename AttnTiles<T>::DK;
+  using DV = typename AttnTiles<T>::DV;
+  constexpr int RB = AttnTiles<T>::RB;
+  constexpr uint32_t ES = sizeof(T);
+  __shared__ __attribute__((aligned(16))) char tK[2][kRB * RB];
+  __shared__ __attribute__((aligned(16))) char tV[2][kRB * RB];
+  const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
+  const int H = a.H;
+  const int64_t L = a.L;
+  const int nqt = (int)((L + kRB - 1) / kRB);
+  // work item = (b * H + h) * nqt + query tile: the query tiles of one head,
+  // which read the same keys and values, run on one XCD
+  int bx = xcd_linear_id(blockIdx.x, gridDim.x);
+  const int qt = bx % nqt;
+  bx /= nqt;
+  const int h = bx % H, b = bx / H;
+  const int64_t q0 = (int64_t)qt * kRB;
+  // visible keys [0, kend): all, or up to the end of the query tile's block
+  // (blocks are whole 64-token tiles)
+  const int64_t kend = a.block > 0 ? min(L, (q0 / a.block + 1) * a.block) : L;
+  const int nkt = (int)((kend + kRB - 1) / kRB);
+  const uint32_t rs = (uint32_t)H * kAttnD * ES;  // token stride in bytes
+  const uint32_t nbytes = (uint32_t)(L * H * kAttnD * ES);
+  const int64_t boff = (int64_t)b * L * H * kAttnD;
+  const bufres rQ = make_buf(reinterpret_cast<const T *>(a.q) + boff, nbytes);
+  const bufres rK = make_buf(reinterpret_cast<const T *>(a.k) + boff, nbytes);
+  const bufres rV = make_buf(reinterpret_cast<const T *>(a.v) + boff, nbytes);
+  auto issue = [&](int kt, int buf) __attribute__((always_inline)) {
+    const uint32_t off = (uint32_t)(((int64_t)kt * kRB * H + h) * kAttnD) * ES;
+    DK::load(tK[buf], rK, off, rs, kRB);
+    DV::load(tV[buf], rV, off, rs, kRB);
+  };
+
+  // this lane's query (B operand of S^T = K Q^T), held for the whole pass
+  const int64_t qrow = q0 + 16 * w + r16;
+  Frag<T> qf[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+    frag_bload(qf[ks], rQ, (uint32_t)((qrow * H + h) * kAttnD) * ES + (uint32_t)(32 * ks + 8 * g4) * ES);
+  issue(0, 0);
+
+  f32x4 o[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) zero4(o[v]);
+  float mrow = -INFINITY, lrow = 0.0f;  // running max and sum of query r16
+
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int cur = kt & 1;
+    wait_vmem();
+    __syncthreads();  // tile kt is in LDS; every wave is done with tile kt - 1
+    if (kt + 1 < nkt) issue(kt + 1, cur ^ 1);
+    // s[u][i]: score of query r16 against key k0 + 16 u + 4 g4 + i
+    f32x4 s[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      zero4(s[u]);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        Frag<T> kf;
+        frag_ld8_swz<DK>(kf, tK[cur], 16 * u + r16, 32 * ks + 8 * g4);
+        mma(s[u], kf, qf[ks]);
+      }
+    }
+    const int64_t k0 = (int64_t)kt * kRB;
+    const bool ragged = k0 + kRB > kend;
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float x = s[u][i] * a.scale_log2;
+        if (ragged && k0 + 16 * u + 4 * g4 + i >= kend) x = -INFINITY;
+        s[u][i] = x;
+        tmax = fmaxf(tmax, x);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float mnew = fmaxf(mrow, tmax);  // finite: every tile has a visible key
+    const float alpha = exp2_fast(mrow - mnew);
+    float tsum = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = exp2_fast(s[u][i] - mnew);
+        s[u][i] = p;
+        tsum += p;
+      }
+    tsum += __shfl_xor(tsum, 16, 64);
+    tsum += __shfl_xor(tsum, 32, 64);
+    lrow = lrow * alpha + tsum;
+    mrow = mnew;
+    // output rows 4 g4 + i belong to query 4 g4 + i, whose factor lane
+    // 4 g4 + i holds
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float ai = __shfl(alpha, 4 * g4 + i, 64);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) o[v][i] *= ai;
+    }
+    // O += P V: P (query r16, keys 32 q + 4 g4 + i and 32 q + 16 + 4 g4 + i)
+    // as the A operand, V read along the key index
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      float m[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        m[i] = s[2 * q][i];
+        m[4 + i] = s[2 * q + 1][i];
+      }
+      Frag<T> pf;
+      frag_from(pf, m);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        Frag<T> vf;
+        frag_rows_swz<DV>(vf, tV[cur], 32 * q + 4 * g4, 32 * q + 16 + 4 * g4, 16 * v);
+        mma(o[v], pf, vf);
+      }
+    }
+  }
+
+  // normalise and store rows q0 + 16 w + 4 g4 + i (16 lanes write one
+  // contiguous row segment)
+  T *og = reinterpret_cast<T *>(a.o) + boff;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float inv = 1.0f / __shfl(lrow, 4 * g4 + i, 64);
+    const int64_t t = q0 + 16 * w + 4 * g4 + i;
+    if (t >= L) continue;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) og[(t * H + h) * kAttnD + 16 * v + r16] = from_f<T>(o[v][i] * inv);
+  }
+}
+
+hipError_t launch_attention(const AttnArgs &a, hipStream_t st) {
+  const int64_t nqt = (a.L + kRB - 1) / kRB;
+  dim3 g((unsigned)(a.Z * a.H * nqt));
+  if (a.dtype == 1) hipLaunchKernelGGL(k_attn_fwd<bf16>, g, dim3(kThreads), 0, st, a);
+  else hipLaunchKernelGGL(k_attn_fwd<float>, g, dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace bissd

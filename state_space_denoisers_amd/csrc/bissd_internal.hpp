@@ -143,6 +143,17 @@ struct BwdArgs {
   int rseg_tiles;  // as in ScanArgs: the reverse panels' column blocks stay in the row's block
 };
 
+// Multi-head softmax attention of the hybrid backbones (bissd_attn.hip).
+constexpr int kAttnD = 64;  // head dim
+struct AttnArgs {
+  const void *q, *k, *v;  // [Z][L][H][kAttnD], dtype
+  void *o;                // [Z][L][H][kAttnD], dtype
+  int64_t L, block;       // block: 0 full, > 0 block-wise (a multiple of 64)
+  int Z, H, dtype;
+  float scale_log2;       // scale * log2(e)
+};
+hipError_t launch_attention(const AttnArgs &a, hipStream_t st);
+
 hipError_t launch_bwd_panels(const BwdArgs &a, hipStream_t st);
 hipError_t launch_bwd_decay(const BwdArgs &a, hipStream_t st);
 

@@ -32,6 +32,7 @@ _KEYS = {
     "x": 0, "D": 1, "dt_f": 2, "A_f": 3, "B_f": 4, "C_f": 5,
     "dt_r": 6, "A_r": 7, "B_r": 8, "C_r": 9, "dy": 10,
     "mask_pos": 11, "mask_vec": 12, "prefix": 13,
+    "attn_q": 14, "attn_k": 15, "attn_v": 16,
 }
 
 
@@ -218,3 +219,10 @@ def as_torch(a: np.ndarray, dtype: str, device=None):
     if device is not None:
         t = t.to(device)
     return t.contiguous()
+
+
+def make_attention_inputs(Z: int, L: int, H: int, dtype: str, seed: int, D: int = 64) -> dict:
+    """q, k, v [Z, L, H, D] ~ N(0, 1) for the hybrids' attention layers (the
+    scale of normalised activations), rounded once to ``dtype``."""
+    return {n: quantize(_rng(seed, "attn_" + n).standard_normal((Z, L, H, D)), dtype)
+            for n in ("q", "k", "v")}

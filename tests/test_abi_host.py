@@ -210,3 +210,36 @@ def test_backward_validation(lib):
     assert call_backward(lib, s, gf=_abi.Grad(addr(12), addr(13), addr(14), addr(14))) == -7
     assert call_backward(lib, s, ws=addr(11)) == -7                    # workspace over dx
     assert call_backward(lib, shape(seqlen=100, headdim=32)) == -3
+
+
+def attn_shape(**kw):
+    d = dict(batch=2, seqlen=300, nheads=12, headdim=64, block=0, dtype=_abi.BISSD_BF16,
+             reserved=0)
+    d.update(kw)
+    return _abi.AttnShape(**d)
+
+
+def call_attention(lib, s, scale=0.0, **over):
+    args = dict(q=addr(0), k=addr(1), v=addr(2), o=addr(3), stream=None)
+    args.update(over)
+    return lib.bissd_attention_forward(C.byref(s) if s is not None else None, args["q"],
+                                       args["k"], args["v"], C.c_float(scale), args["o"],
+                                       args["stream"])
+
+
+@pytest.mark.parametrize("over,scale,code", [
+    (dict(headdim=128), 0.0, -3), (dict(block=32), 0.0, -3), (dict(block=-64), 0.0, -2),
+    (dict(seqlen=0), 0.0, -2), (dict(dtype=5), 0.0, -3), (dict(reserved=1), 0.0, -2),
+    (dict(), -1.0, -2), (dict(), float("nan"), -2),
+])
+def test_attention_validation(lib, over, scale, code):
+    assert call_attention(lib, attn_shape(**over), scale) == code
+
+
+def test_attention_pointers(lib):
+    s = attn_shape()
+    assert call_attention(lib, None) == -1
+    assert call_attention(lib, s, q=None) == -1
+    assert call_attention(lib, s, o=C.c_void_p(A + 8)) == -4
+    assert call_attention(lib, s, o=addr(1)) == -7   # o over k
+
