@@ -367,6 +367,39 @@ def bench_train(steps, rev_block=0):
             "hbm_algorithmic_GBs": train_bytes_per_token(w) * w.tokens / (ms * 1e-3) / 1e9}
 
 
+def attention_flops(Z, L, H, block=0, D=64):
+    """Matrix-core flops of one attention call: Q K^T and P V over the
+    visible (query, key) pairs, 2 flops per multiply-add each."""
+    if block <= 0:
+        pairs = L * L
+    else:
+        pairs = sum(min(L, (t // block + 1) * block) for t in range(L))
+    return 4 * Z * H * D * pairs
+
+
+def bench_attention(reps, Z=8, L=1024, H=12, block=0):
+    """The hybrids' attention layer at the 130M-class shape (12 heads of 64),
+    bf16, full bidirectional (block 0) or block-wise."""
+    import torch
+    import state_space_denoisers_amd as ssd
+    from synth import gen
+    dev = torch.device("cuda", 0)
+    inp = gen.make_attention_inputs(Z, L, H, "bf16", 2001)
+    T = {k: gen.as_torch(v, "bf16", dev) for k, v in inp.items()}
+    o = torch.empty_like(T["q"])
+    fn = lambda: ssd.bissd_attention_forward(T["q"], T["k"], T["v"], block=block, o=o)
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    ms = event_time_ms(fn, reps)
+    fl = attention_flops(Z, L, H, block)
+    return {"workload": f"attention_L{L // 1024}k" + (f"_block{block}" if block else ""),
+            "batch": Z, "seq_len": L, "heads": H, "headdim": 64, "block": block,
+            "us_per_call": ms * 1e3, "tokens_per_s": Z * L / (ms * 1e-3),
+            "achieved_TFLOPs": fl / (ms * 1e-3) / 1e12,
+            "frac_bf16_peak": fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+
+
 def bench_generation(steps_per_block=8, blocks=2, prefix=65536):
     """Block-wise generation after a long prefix, two ways, same kernels:
     (a) a full-sequence bidirectional model re-scans prefix + every block so
@@ -583,6 +616,13 @@ def main():
             log(f"bench: block {extra['block_update']}")
         except Exception as exc:
             extra["block_update"] = {"error": repr(exc)}
+        for L, blk in ((1024, 0), (4096, 0), (4096, 256)):
+            key = f"attention_L{L // 1024}k" + (f"_block{blk}" if blk else "")
+            try:
+                extra[key] = bench_attention(max(20, args.steps // 4), L=L, block=blk)
+                log(f"bench: {key} {extra[key]}")
+            except Exception as exc:
+                extra[key] = {"error": repr(exc)}
         try:
             extra["generation_L64k"] = bench_generation()
             log(f"bench: generation {extra['generation_L64k']}")

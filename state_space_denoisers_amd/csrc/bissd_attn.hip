@@ -11,15 +11,19 @@
 // BDLM attention baseline).  M is 0 where a query may see a key and -inf
 // elsewhere.
 //
-// One pass over the keys with a running softmax: each workgroup takes 64
+// One pass over the keys with a running softmax: each workgroup takes 128
 // queries of one (batch, head) and streams 64-key tiles of K and V through
 // LDS (copied buffer -> LDS, the next tile in flight while the current one
-// is used).  Per tile, each wave forms its 16 queries' scores as S^T = K Q^T
+// is used).  Per tile, each wave forms its 32 queries' scores as S^T = K Q^T
 // on the matrix cores, so that a lane holds one query's scores for 16 keys
 // in exactly the layout of the A operand of the following P V product; the
-// row maximum and sum take two lane exchanges; the output rows are
-// rescaled by exp2(m_old - m_new) before P V is added.  Scores are kept in
-// log2 units (scale * log2(e) folded in), so every exponential is one exp2.
+// row maximum and sum take two lane exchanges.  Every exponential is one
+// exp2 of fma(s, c, -m c) with c = scale * log2(e).  The running maximum m
+// of a query only moves when a tile's maximum exceeds it by more than
+// kAttnSlack / c (then the output rows are rescaled by exp2((m_old - m_new) c)),
+// so after the first tiles a wave usually skips the rescale altogether;
+// meanwhile the probabilities stay below 2^kAttnSlack, well inside bf16 and
+// the fp32 sums.
 #include <math.h>
 
 #include "bissd_device.hpp"
@@ -27,17 +31,22 @@
 
 namespace bissd {
 
+constexpr float kAttnSlack = 8.0f;  // log2 units the running maximum may lag
+constexpr int kAttnQ = 128;         // queries per workgroup
+
 template <typename T> struct AttnTiles {
   static constexpr int RB = kAttnD * (int)sizeof(T);  // bytes of one head's token row
   using DK = DmaTile<RB, SW_NAT>;  // keys: read as natural rows
   using DV = DmaTile<RB, SW_TR>;   // values: read along the key index
 };
 
-// Workgroup = (batch b, head h, 64-query tile); wave w owns queries
-// q0 + 16 w + (0..15).  Queries past L compute on zeros and are not stored;
-// keys past the visible end are masked to -inf.
+// Workgroup = (batch b, head h, 128-query tile); wave w owns queries
+// q0 + 32 w + 16 j + (0..15) for j = 0, 1, so every key and value fragment
+// read from LDS feeds two products.  Queries past L compute on zeros and are
+// not stored; keys past a query group's visible end are masked to -inf.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void k_attn_fwd(AttnArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 3 : 1)))
+void k_attn_fwd(AttnArgs a) {
   using DK = typename AttnTiles<T>::DK;
   using DV = typename AttnTiles<T>::DV;
   constexpr int RB = AttnTiles<T>::RB;
@@ -47,18 +56,25 @@ __global__ __launch_bounds__(kThreads) void k_attn_fwd(AttnArgs a) {
   const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
   const int H = a.H;
   const int64_t L = a.L;
-  const int nqt = (int)((L + kRB - 1) / kRB);
+  const int nqt = (int)((L + kAttnQ - 1) / kAttnQ);
   // work item = (b * H + h) * nqt + query tile: the query tiles of one head,
   // which read the same keys and values, run on one XCD
   int bx = xcd_linear_id(blockIdx.x, gridDim.x);
   const int qt = bx % nqt;
   bx /= nqt;
   const int h = bx % H, b = bx / H;
-  const int64_t q0 = (int64_t)qt * kRB;
-  // visible keys [0, kend): all, or up to the end of the query tile's block
-  // (blocks are whole 64-token tiles)
-  const int64_t kend = a.block > 0 ? min(L, (q0 / a.block + 1) * a.block) : L;
-  const int nkt = (int)((kend + kRB - 1) / kRB);
+  const int64_t q0 = (int64_t)qt * kAttnQ;
+  // visible keys [0, kend_j) of query group j: all, or up to the end of its
+  // block (blocks are whole 64-token tiles, so a 16-query group lies in one)
+  int64_t kend[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int64_t g0 = q0 + 32 * w + 16 * j;
+    kend[j] = a.block > 0 ? min(L, (g0 / a.block + 1) * a.block) : L;
+  }
+  const int64_t qlast = min(L, q0 + kAttnQ) - 1;
+  const int64_t kmax = a.block > 0 ? min(L, (qlast / a.block + 1) * a.block) : L;
+  const int nkt = (int)((kmax + kRB - 1) / kRB);
   const uint32_t rs = (uint32_t)H * kAttnD * ES;  // token stride in bytes
   const uint32_t nbytes = (uint32_t)(L * H * kAttnD * ES);
   const int64_t boff = (int64_t)b * L * H * kAttnD;
@@ -71,109 +87,140 @@ __global__ __launch_bounds__(kThreads) void k_attn_fwd(AttnArgs a) {
     DV::load(tV[buf], rV, off, rs, kRB);
   };
 
-  // this lane's query (B operand of S^T = K Q^T), held for the whole pass
-  const int64_t qrow = q0 + 16 * w + r16;
-  Frag<T> qf[2];
+  // this lane's two queries (B operands of S^T = K Q^T), held for the pass
+  Frag<T> qf[2][2];
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
-    frag_bload(qf[ks], rQ, (uint32_t)((qrow * H + h) * kAttnD) * ES + (uint32_t)(32 * ks + 8 * g4) * ES);
+  for (int j = 0; j < 2; ++j) {
+    const int64_t qrow = q0 + 32 * w + 16 * j + r16;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      frag_bload(qf[j][ks], rQ, (uint32_t)((qrow * H + h) * kAttnD) * ES + (uint32_t)(32 * ks + 8 * g4) * ES);
+  }
   issue(0, 0);
 
-  f32x4 o[4];
+  f32x4 o[2][4];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) zero4(o[v]);
-  float mrow = -INFINITY, lrow = 0.0f;  // running max and sum of query r16
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) zero4(o[j][v]);
+  const float c = a.scale_log2;
+  const float slack = kAttnSlack / c;
+  // running reference (raw score units) and sum of query r16 of each group
+  float mrow[2] = {-INFINITY, -INFINITY}, lrow[2] = {0.0f, 0.0f};
 
   for (int kt = 0; kt < nkt; ++kt) {
     const int cur = kt & 1;
     wait_vmem();
     __syncthreads();  // tile kt is in LDS; every wave is done with tile kt - 1
     if (kt + 1 < nkt) issue(kt + 1, cur ^ 1);
-    // s[u][i]: score of query r16 against key k0 + 16 u + 4 g4 + i
-    f32x4 s[4];
+    // s[j][u][i]: score of query r16 of group j against key k0 + 16 u + 4 g4 + i
+    f32x4 s[2][4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      zero4(s[u]);
+      zero4(s[0][u]);
+      zero4(s[1][u]);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         Frag<T> kf;
         frag_ld8_swz<DK>(kf, tK[cur], 16 * u + r16, 32 * ks + 8 * g4);
-        mma(s[u], kf, qf[ks]);
+        mma(s[0][u], kf, qf[0][ks]);
+        mma(s[1][u], kf, qf[1][ks]);
       }
     }
     const int64_t k0 = (int64_t)kt * kRB;
-    const bool ragged = k0 + kRB > kend;
-    float tmax = -INFINITY;
+    bool move[2];
+    float alpha[2];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int j = 0; j < 2; ++j) {
+      if (k0 + kRB > kend[j]) {
+        // keys past the group's visible end score -inf
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float x = s[u][i] * a.scale_log2;
-        if (ragged && k0 + 16 * u + 4 * g4 + i >= kend) x = -INFINITY;
-        s[u][i] = x;
-        tmax = fmaxf(tmax, x);
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (k0 + 16 * u + 4 * g4 + i >= kend[j]) s[j][u][i] = -INFINITY;
       }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float mnew = fmaxf(mrow, tmax);  // finite: every tile has a visible key
-    const float alpha = exp2_fast(mrow - mnew);
-    float tsum = 0.0f;
+      float tmax = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = exp2_fast(s[u][i] - mnew);
-        s[u][i] = p;
-        tsum += p;
-      }
-    tsum += __shfl_xor(tsum, 16, 64);
-    tsum += __shfl_xor(tsum, 32, 64);
-    lrow = lrow * alpha + tsum;
-    mrow = mnew;
+        for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, s[j][u][i]);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      // a tile wholly past the group's end has tmax = -inf and moves nothing;
+      // the first tile always has a visible key for every group
+      move[j] = tmax > mrow[j] + slack;
+      const float mnew = move[j] ? tmax : mrow[j];
+      alpha[j] = move[j] ? exp2_fast((mrow[j] - mnew) * c) : 1.0f;
+      const float nm = -mnew * c;
+      float tsum = 0.0f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = exp2_fast(fmaf(s[j][u][i], c, nm));
+          s[j][u][i] = p;
+          tsum += p;
+        }
+      tsum += __shfl_xor(tsum, 16, 64);
+      tsum += __shfl_xor(tsum, 32, 64);
+      lrow[j] = lrow[j] * alpha[j] + tsum;
+      mrow[j] = mnew;
+    }
     // output rows 4 g4 + i belong to query 4 g4 + i, whose factor lane
-    // 4 g4 + i holds
+    // 4 g4 + i holds; skipped when no query of the wave moved
+    if (__any(move[0] || move[1])) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float ai = __shfl(alpha, 4 * g4 + i, 64);
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) o[v][i] *= ai;
+        for (int i = 0; i < 4; ++i) {
+          const float ai = __shfl(alpha[j], 4 * g4 + i, 64);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) o[j][v][i] *= ai;
+        }
     }
     // O += P V: P (query r16, keys 32 q + 4 g4 + i and 32 q + 16 + 4 g4 + i)
     // as the A operand, V read along the key index
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      float m[8];
+      Frag<T> pf[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        m[i] = s[2 * q][i];
-        m[4 + i] = s[2 * q + 1][i];
+      for (int j = 0; j < 2; ++j) {
+        float m[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          m[i] = s[j][2 * q][i];
+          m[4 + i] = s[j][2 * q + 1][i];
+        }
+        frag_from(pf[j], m);
       }
-      Frag<T> pf;
-      frag_from(pf, m);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         Frag<T> vf;
         frag_rows_swz<DV>(vf, tV[cur], 32 * q + 4 * g4, 32 * q + 16 + 4 * g4, 16 * v);
-        mma(o[v], pf, vf);
+        mma(o[0][v], pf[0], vf);
+        mma(o[1][v], pf[1], vf);
       }
     }
   }
 
-  // normalise and store rows q0 + 16 w + 4 g4 + i (16 lanes write one
+  // normalise and store rows q0 + 32 w + 16 j + 4 g4 + i (16 lanes write one
   // contiguous row segment)
   T *og = reinterpret_cast<T *>(a.o) + boff;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float inv = 1.0f / __shfl(lrow, 4 * g4 + i, 64);
-    const int64_t t = q0 + 16 * w + 4 * g4 + i;
-    if (t >= L) continue;
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) og[(t * H + h) * kAttnD + 16 * v + r16] = from_f<T>(o[v][i] * inv);
-  }
+    for (int i = 0; i < 4; ++i) {
+      const float inv = 1.0f / __shfl(lrow[j], 4 * g4 + i, 64);
+      const int64_t t = q0 + 32 * w + 16 * j + 4 * g4 + i;
+      if (t >= L) continue;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) og[(t * H + h) * kAttnD + 16 * v + r16] = from_f<T>(o[j][v][i] * inv);
+    }
 }
 
 hipError_t launch_attention(const AttnArgs &a, hipStream_t st) {
-  const int64_t nqt = (a.L + kRB - 1) / kRB;
+  const int64_t nqt = (a.L + kAttnQ - 1) / kAttnQ;
   dim3 g((unsigned)(a.Z * a.H * nqt));
   if (a.dtype == 1) hipLaunchKernelGGL(k_attn_fwd<bf16>, g, dim3(kThreads), 0, st, a);
   else hipLaunchKernelGGL(k_attn_fwd<float>, g, dim3(kThreads), 0, st, a);
