@@ -458,3 +458,45 @@ def test_attention_single_token_and_scale():
     # scale multiplies the scores: scale s on q is the same as s on the scores
     q, k, v = _qkv(1, 9, 1, 4, 47)
     assert np.allclose(AT.forward(q, k, v, scale=0.3), AT.forward(0.3 * q, k, v, scale=1.0), atol=1e-13)
+
+
+def _attn_torch(q, k, v, block, scale):
+    """The same layer through torch's own softmax, differentiated by autograd."""
+    import torch
+    Z, L, H, D = q.shape
+    vis = torch.as_tensor(AT.visible(L, block))
+    s = scale * torch.einsum("zthd,zshd->zhts", q, k)
+    s = s.masked_fill(~vis, float("-inf"))
+    return torch.einsum("zhts,zshd->zthd", torch.softmax(s, dim=-1), v)
+
+
+@pytest.mark.parametrize("block", [0, 8, 16])
+def test_attention_backward_matches_autograd(block):
+    import torch
+    Z, L, H, D = 2, 33, 2, 8
+    q, k, v = _qkv(Z, L, H, D, 50)
+    do = np.random.default_rng(51).standard_normal((Z, L, H, D))
+    g = AT.backward(q, k, v, do, block=block)
+    T = [torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (q, k, v)]
+    o = _attn_torch(*T, block, 1.0 / math.sqrt(D))
+    assert np.allclose(o.detach().numpy(), AT.forward(q, k, v, block=block), atol=1e-13)
+    (o * torch.tensor(do)).sum().backward()
+    for name, t in zip(("dq", "dk", "dv"), T):
+        assert rel(g[name], t.grad.numpy()) < 1e-12, name
+
+
+def test_attention_backward_finite_differences():
+    Z, L, H, D = 1, 20, 1, 8
+    q, k, v = _qkv(Z, L, H, D, 52)
+    do = np.random.default_rng(53).standard_normal((Z, L, H, D))
+    g = AT.backward(q, k, v, do, block=8)
+    r = np.random.default_rng(54)
+    eps = 1e-6
+    for name, idx in (("dq", 0), ("dk", 1), ("dv", 2)):
+        d = r.standard_normal((Z, L, H, D))
+        args_p = [q, k, v]
+        args_m = [q, k, v]
+        args_p[idx] = args_p[idx] + eps * d
+        args_m[idx] = args_m[idx] - eps * d
+        fd = (np.sum(AT.forward(*args_p, block=8) * do) - np.sum(AT.forward(*args_m, block=8) * do)) / (2 * eps)
+        assert abs(fd - np.sum(g[name] * d)) <= 1e-7 * max(1.0, abs(fd)), name
