@@ -400,6 +400,31 @@ def bench_attention(reps, Z=8, L=1024, H=12, block=0):
             "frac_bf16_peak": fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
 
 
+def bench_attention_backward(reps, Z=8, L=1024, H=12, block=0):
+    """Backward of the attention layer (dq, dk, dv from the forward's o and
+    lse); TFLOP/s over the algorithmic 5 products (Q K^T recomputed, dP,
+    dV, dK, dQ; 10 L^2 D per head) on the visible pairs."""
+    import torch
+    import state_space_denoisers_amd as ssd
+    from synth import gen
+    dev = torch.device("cuda", 0)
+    inp = gen.make_attention_inputs(Z, L, H, "bf16", 2002)
+    T = {k: gen.as_torch(v, "bf16", dev) for k, v in inp.items()}
+    dout = gen.as_torch(gen.make_attention_inputs(Z, L, H, "bf16", 2003)["q"], "bf16", dev)
+    lse = torch.empty((Z, H, L), dtype=torch.float32, device=dev)
+    o = ssd.bissd_attention_forward(T["q"], T["k"], T["v"], block=block, lse=lse)
+    fn = lambda: ssd.bissd_attention_backward(T["q"], T["k"], T["v"], o, dout, lse, block=block)
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    ms = event_time_ms(fn, reps)
+    fl = attention_flops(Z, L, H, block) * 10 // 4
+    return {"workload": f"attention_bwd_L{L // 1024}k" + (f"_block{block}" if block else ""),
+            "batch": Z, "seq_len": L, "heads": H, "headdim": 64, "block": block,
+            "us_per_call": ms * 1e3, "achieved_TFLOPs": fl / (ms * 1e-3) / 1e12,
+            "frac_bf16_peak": fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+
+
 def bench_generation(steps_per_block=8, blocks=2, prefix=65536):
     """Block-wise generation after a long prefix, two ways, same kernels:
     (a) a full-sequence bidirectional model re-scans prefix + every block so
@@ -623,6 +648,11 @@ def main():
                 log(f"bench: {key} {extra[key]}")
             except Exception as exc:
                 extra[key] = {"error": repr(exc)}
+        try:
+            extra["attention_bwd_L4k"] = bench_attention_backward(max(10, args.steps // 10), L=4096)
+            log(f"bench: attention_bwd_L4k {extra['attention_bwd_L4k']}")
+        except Exception as exc:
+            extra["attention_bwd_L4k"] = {"error": repr(exc)}
         try:
             extra["generation_L64k"] = bench_generation()
             log(f"bench: generation {extra['generation_L64k']}")

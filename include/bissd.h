@@ -223,6 +223,9 @@ int bissd_forward_phase(const bissd_shape_t *shape, const void *x, bissd_dir_t f
  *   q, k, v, o  [batch][seqlen][nheads][headdim] device pointers, 16-byte
  *          aligned; o must not overlap q, k or v.
  *   scale  > 0, or 0 for 1 / sqrt(headdim).
+ *   lse    [batch][nheads][seqlen] fp32 or NULL: receives each query's
+ *          log2-sum-exp of its scaled scores, log2 sum_s 2^(scale log2(e) S[t][s]),
+ *          which bissd_attention_backward needs.
  * Scores, softmax and the P V accumulation are fp32; o is rounded once.
  * Asynchronous on `stream`; allocates nothing; status codes as above.
  */
@@ -237,7 +240,26 @@ typedef struct {
 } bissd_attn_shape_t;
 
 int bissd_attention_forward(const bissd_attn_shape_t *shape, const void *q, const void *k,
-                            const void *v, float scale, void *o, void *stream);
+                            const void *v, float scale, void *o, float *lse, void *stream);
+
+/* Bytes of workspace bissd_attention_backward needs (0 on a bad shape). */
+size_t bissd_attention_workspace_size(const bissd_attn_shape_t *shape);
+
+/*
+ * Gradients of Loss = sum(dout * o) for o = bissd_attention_forward(q, k, v)
+ * (the reverse mode of softmax attention: dV = P^T dO, dS = P (dO V^T - D)
+ * with D_t = dO_t . o_t, dQ = scale dS K, dK = scale dS^T Q).
+ *   o, lse   the forward's output and log2-sum-exp (same q, k, v, shape, scale)
+ *   dout     [batch][seqlen][nheads][headdim], dtype
+ *   dq, dk, dv  [batch][seqlen][nheads][headdim] fp32, overwritten
+ *   workspace   bissd_attention_workspace_size(shape) bytes
+ * Every sum has a fixed order (no atomics): bitwise reproducible.  None of
+ * the outputs may overlap an input, the workspace or each other.
+ */
+int bissd_attention_backward(const bissd_attn_shape_t *shape, const void *q, const void *k,
+                             const void *v, const void *o, const void *dout, const float *lse,
+                             float scale, float *dq, float *dk, float *dv, void *workspace,
+                             size_t workspace_bytes, void *stream);
 
 /* Text of a status code (static storage). */
 const char *bissd_status_string(int status);

@@ -23,8 +23,8 @@ import torch
 from . import _abi
 
 __all__ = ["Dir", "bissd_forward", "bissd_forward_phase", "bissd_block_update", "bissd_backward",
-           "bissd_attention_forward", "bissd_workspace_size", "shape_of", "library_path",
-           "BissdError"]
+           "bissd_attention_forward", "bissd_attention_backward", "bissd_workspace_size",
+           "shape_of", "library_path", "BissdError"]
 
 BissdError = _abi.BissdError
 
@@ -198,20 +198,47 @@ def bissd_backward(x: torch.Tensor, fwd, rev, D: torch.Tensor, dy: torch.Tensor,
     return g
 
 
-def bissd_attention_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
-                            block: int = 0, scale: float = 0.0,
-                            o: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """O = softmax(scale Q K^T + M) V per head (include/bissd.h,
-    bissd_attention_forward): q, k, v [Z, L, H, 64]; block 0 for full
-    bidirectional attention, > 0 for block-wise; scale 0 for 1/sqrt(64)."""
-    lib = _abi.load()
+def _attn_shape(q, k, v, block):
     Z, L, H, Dh = q.shape
     if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k and v must have one shape and dtype")
-    shape = _abi.AttnShape(Z, L, H, Dh, int(block), _dtype_code(q), 0)
+    return _abi.AttnShape(Z, L, H, Dh, int(block), _dtype_code(q), 0)
+
+
+def bissd_attention_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
+                            block: int = 0, scale: float = 0.0,
+                            o: Optional[torch.Tensor] = None,
+                            lse: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """O = softmax(scale Q K^T + M) V per head (include/bissd.h,
+    bissd_attention_forward): q, k, v [Z, L, H, 64]; block 0 for full
+    bidirectional attention, > 0 for block-wise; scale 0 for 1/sqrt(64).
+    ``lse`` (fp32 [Z, H, L]) receives what the backward needs."""
+    lib = _abi.load()
+    shape = _attn_shape(q, k, v, block)
     if o is None:
         o = torch.empty_like(q)
     st = lib.bissd_attention_forward(C.byref(shape), _ptr(q), _ptr(k), _ptr(v), float(scale),
-                                     _ptr(o), _stream(q.device, stream))
+                                     _ptr(o), _ptr(lse), _stream(q.device, stream))
     _abi.check("bissd_attention_forward", st)
     return o
+
+
+def bissd_attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                             o: torch.Tensor, dout: torch.Tensor, lse: torch.Tensor, *,
+                             block: int = 0, scale: float = 0.0,
+                             workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """dq, dk, dv (fp32) of sum(dout * o) for o, lse from bissd_attention_forward
+    with the same arguments (include/bissd.h, bissd_attention_backward)."""
+    lib = _abi.load()
+    shape = _attn_shape(q, k, v, block)
+    g = {n: torch.empty(q.shape, dtype=torch.float32, device=q.device) for n in ("dq", "dk", "dv")}
+    if workspace is None:
+        n = int(lib.bissd_attention_workspace_size(C.byref(shape)))
+        workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
+    st = lib.bissd_attention_backward(C.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                      _ptr(dout), _ptr(lse), float(scale), _ptr(g["dq"]),
+                                      _ptr(g["dk"]), _ptr(g["dv"]), _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(),
+                                      _stream(q.device, stream))
+    _abi.check("bissd_attention_backward", st)
+    return g

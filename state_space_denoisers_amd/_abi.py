@@ -24,8 +24,9 @@ STATUS = {
 
 # every symbol include/bissd.h declares
 EXPORTS = ("bissd_workspace_size", "bissd_forward", "bissd_backward", "bissd_block_update",
-           "bissd_forward_phase", "bissd_attention_forward", "bissd_status_string",
-           "bissd_last_hip_error", "bissd_version")
+           "bissd_forward_phase", "bissd_attention_forward", "bissd_attention_backward",
+           "bissd_attention_workspace_size", "bissd_status_string", "bissd_last_hip_error",
+           "bissd_version")
 
 
 class Shape(C.Structure):
@@ -90,7 +91,13 @@ def load(path: str = LIB_PATH) -> C.CDLL:
                                            C.c_size_t, C.c_void_p]
         lib.bissd_attention_forward.restype = C.c_int
         lib.bissd_attention_forward.argtypes = [C.POINTER(AttnShape), C.c_void_p, C.c_void_p,
-                                                C.c_void_p, C.c_float, C.c_void_p, C.c_void_p]
+                                                C.c_void_p, C.c_float, C.c_void_p, C.c_void_p,
+                                                C.c_void_p]
+        lib.bissd_attention_workspace_size.restype = C.c_size_t
+        lib.bissd_attention_workspace_size.argtypes = [C.POINTER(AttnShape)]
+        lib.bissd_attention_backward.restype = C.c_int
+        lib.bissd_attention_backward.argtypes = [C.POINTER(AttnShape)] + [C.c_void_p] * 6 + [
+            C.c_float, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
         lib.bissd_status_string.restype = C.c_char_p
         lib.bissd_status_string.argtypes = [C.c_int]
         lib.bissd_last_hip_error.restype = C.c_int

@@ -549,37 +549,100 @@ int bissd_backward(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, bissd
   return finish(e);
 }
 
-int bissd_attention_forward(const bissd_attn_shape_t *s, const void *q, const void *k,
-                            const void *v, float scale, void *o, void *stream) {
+static int check_attn(const bissd_attn_shape_t *s, float scale) {
   if (!s) return BISSD_ERR_NULL;
   if (s->batch <= 0 || s->seqlen <= 0 || s->nheads <= 0 || s->headdim <= 0 || s->block < 0 ||
       s->reserved != 0 || !(scale >= 0.0f) || !isfinite(scale))
     return BISSD_ERR_SHAPE;
   if (s->headdim != bissd::kAttnD || s->block % 64 != 0) return BISSD_ERR_UNSUPPORTED;
   if (s->dtype != BISSD_F32 && s->dtype != BISSD_BF16) return BISSD_ERR_UNSUPPORTED;
-  const int64_t es = s->dtype == BISSD_BF16 ? 2 : 4;
-  // one buffer resource per batch row (< 4 GiB); grid within 2^31
-  if (s->batch > (1 << 20) || s->nheads > 4096 || s->seqlen * s->nheads * s->headdim * es >= ((int64_t)1 << 32))
+  // one buffer resource per batch row (< 4 GiB, fp32 gradients included);
+  // grid within 2^31
+  if (s->batch > (1 << 20) || s->nheads > 4096 || s->seqlen * s->nheads * s->headdim * 4 >= ((int64_t)1 << 32))
     return BISSD_ERR_UNSUPPORTED;
   if (s->batch * s->nheads * ceil_div(s->seqlen, 64) >= ((int64_t)1 << 31)) return BISSD_ERR_UNSUPPORTED;
-  if (!q || !k || !v || !o) return BISSD_ERR_NULL;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return BISSD_ERR_ALIGN;
-  const size_t n = (size_t)(s->batch * s->seqlen * s->nheads * s->headdim * es);
-  if (overlap(o, n, q, n) || overlap(o, n, k, n) || overlap(o, n, v, n)) return BISSD_ERR_ALIAS;
+  return BISSD_OK;
+}
+
+static bissd::AttnArgs attn_args(const bissd_attn_shape_t *s, float scale) {
   bissd::AttnArgs a;
   memset(&a, 0, sizeof(a));
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.o = o;
   a.L = s->seqlen;
   a.block = s->block;
   a.Z = (int)s->batch;
   a.H = (int)s->nheads;
   a.dtype = s->dtype;
-  const float sc = scale > 0.0f ? scale : 1.0f / sqrtf((float)s->headdim);
-  a.scale_log2 = sc * 1.4426950408889634f;
+  a.scale = scale > 0.0f ? scale : 1.0f / sqrtf((float)s->headdim);
+  a.scale_log2 = a.scale * 1.4426950408889634f;
+  return a;
+}
+
+int bissd_attention_forward(const bissd_attn_shape_t *s, const void *q, const void *k,
+                            const void *v, float scale, void *o, float *lse, void *stream) {
+  int rc = check_attn(s, scale);
+  if (rc) return rc;
+  if (!q || !k || !v || !o) return BISSD_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned16(lse)))
+    return BISSD_ERR_ALIGN;
+  const size_t n = (size_t)(s->batch * s->seqlen * s->nheads * s->headdim * (s->dtype == BISSD_BF16 ? 2 : 4));
+  const size_t nl = (size_t)(s->batch * s->nheads * s->seqlen) * 4;
+  if (overlap(o, n, q, n) || overlap(o, n, k, n) || overlap(o, n, v, n)) return BISSD_ERR_ALIAS;
+  if (lse && (overlap(lse, nl, q, n) || overlap(lse, nl, k, n) || overlap(lse, nl, v, n) ||
+              overlap(lse, nl, o, n)))
+    return BISSD_ERR_ALIAS;
+  bissd::AttnArgs a = attn_args(s, scale);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
   return finish(bissd::launch_attention(a, (hipStream_t)stream));
+}
+
+size_t bissd_attention_workspace_size(const bissd_attn_shape_t *s) {
+  if (check_attn(s, 0.0f) != BISSD_OK) return 0;
+  return align256((size_t)(s->batch * s->nheads * s->seqlen) * 4);
+}
+
+int bissd_attention_backward(const bissd_attn_shape_t *s, const void *q, const void *k,
+                             const void *v, const void *o, const void *dout, const float *lse,
+                             float scale, float *dq, float *dk, float *dv, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+  int rc = check_attn(s, scale);
+  if (rc) return rc;
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return BISSD_ERR_NULL;
+  const void *ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv};
+  for (const void *p : ptrs)
+    if (!aligned16(p)) return BISSD_ERR_ALIGN;
+  const size_t nws = bissd_attention_workspace_size(s);
+  if (!workspace || workspace_bytes < nws) return BISSD_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return BISSD_ERR_ALIGN;
+  const size_t n = (size_t)(s->batch * s->seqlen * s->nheads * s->headdim * (s->dtype == BISSD_BF16 ? 2 : 4));
+  const size_t n4 = (size_t)(s->batch * s->seqlen * s->nheads * s->headdim) * 4;
+  const size_t nl = (size_t)(s->batch * s->nheads * s->seqlen) * 4;
+  const void *ins[] = {q, k, v, o, dout, lse, workspace};
+  const size_t inl[] = {n, n, n, n, n, nl, nws};
+  float *outs[] = {dq, dk, dv};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 7; ++j)
+      if (overlap(outs[i], n4, ins[j], inl[j])) return BISSD_ERR_ALIAS;
+    for (int j = 0; j < i; ++j)
+      if (overlap(outs[i], n4, outs[j], n4)) return BISSD_ERR_ALIAS;
+  }
+  for (int j = 0; j < 6; ++j)
+    if (overlap(workspace, nws, ins[j], inl[j])) return BISSD_ERR_ALIAS;
+  bissd::AttnArgs a = attn_args(s, scale);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = const_cast<void *>(o);
+  a.lse = const_cast<float *>(lse);
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.delta = (float *)workspace;
+  return finish(bissd::launch_attention_backward(a, (hipStream_t)stream));
 }
 
 }  // extern "C"

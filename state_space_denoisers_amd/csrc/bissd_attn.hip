@@ -204,6 +204,15 @@ void k_attn_fwd(AttnArgs a) {
     }
   }
 
+  // log2-sum-exp of each query's scaled scores (the backward pass rebuilds
+  // P = exp2(c s - lse) from it), one lane per query
+  if (a.lse && g4 == 0) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t t = q0 + 32 * w + 16 * j + r16;
+      if (t < L) a.lse[((int64_t)b * H + h) * L + t] = mrow[j] * c + __builtin_amdgcn_logf(lrow[j]);
+    }
+  }
   // normalise and store rows q0 + 32 w + 16 j + 4 g4 + i (16 lanes write one
   // contiguous row segment)
   T *og = reinterpret_cast<T *>(a.o) + boff;
@@ -217,6 +226,314 @@ void k_attn_fwd(AttnArgs a) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) og[(t * H + h) * kAttnD + 16 * v + r16] = from_f<T>(o[j][v][i] * inv);
     }
+}
+
+// ============================================================== backward
+//
+// Reverse mode of O = softmax(S) V, S = scale Q K^T + M, for an incoming
+// gradient dO (plain matrix calculus):
+//   P = exp2(c S_raw - lse),  dV = P^T dO,  dP = dO V^T,
+//   dS = P * (dP - D),  D_t = sum_d dO[t][d] O[t][d],
+//   dQ = scale dS K,  dK = scale dS^T Q.
+// P is rebuilt from the forward's per-query log2-sum-exp (lse).  Two
+// launches keep every sum in a fixed order (no atomics): k_attn_dq runs
+// over query tiles (dQ, and D as a by-product), then k_attn_dkv over key
+// tiles (dK, dV), each recomputing the scores.  As in the forward, every
+// product is laid out so that its accumulator is the A operand of the next
+// one: per query in k_attn_dq (S^T = K Q^T, dP^T = V dO^T), per key in
+// k_attn_dkv (S = Q K^T, dP = dO V^T).
+
+// Workgroup = (batch b, head h, 64-query tile); wave w owns queries
+// q0 + 16 w + (0..15).  K is staged twice (natural rows for the scores,
+// along the key index for dQ), V once.
+template <typename T>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 3 : 1)))
+void k_attn_dq(AttnArgs a) {
+  using DN = typename AttnTiles<T>::DK;
+  using DTR = typename AttnTiles<T>::DV;
+  constexpr int RB = AttnTiles<T>::RB;
+  constexpr uint32_t ES = sizeof(T);
+  __shared__ __attribute__((aligned(16))) char tKn[2][kRB * RB];
+  __shared__ __attribute__((aligned(16))) char tKt[2][kRB * RB];
+  __shared__ __attribute__((aligned(16))) char tVn[2][kRB * RB];
+  const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
+  const int H = a.H;
+  const int64_t L = a.L;
+  const int nqt = (int)((L + kRB - 1) / kRB);
+  int bx = xcd_linear_id(blockIdx.x, gridDim.x);
+  const int qt = bx % nqt;
+  bx /= nqt;
+  const int h = bx % H, b = bx / H;
+  const int64_t q0 = (int64_t)qt * kRB;
+  const int64_t kend = a.block > 0 ? min(L, (q0 / a.block + 1) * a.block) : L;
+  const int nkt = (int)((kend + kRB - 1) / kRB);
+  const uint32_t rs = (uint32_t)H * kAttnD * ES;
+  const uint32_t nbytes = (uint32_t)(L * H * kAttnD * ES);
+  const int64_t boff = (int64_t)b * L * H * kAttnD;
+  const bufres rQ = make_buf(reinterpret_cast<const T *>(a.q) + boff, nbytes);
+  const bufres rK = make_buf(reinterpret_cast<const T *>(a.k) + boff, nbytes);
+  const bufres rV = make_buf(reinterpret_cast<const T *>(a.v) + boff, nbytes);
+  const bufres rO = make_buf(reinterpret_cast<const T *>(a.o) + boff, nbytes);
+  const bufres rG = make_buf(reinterpret_cast<const T *>(a.dout) + boff, nbytes);
+  auto issue = [&](int kt, int buf) __attribute__((always_inline)) {
+    const uint32_t off = (uint32_t)(((int64_t)kt * kRB * H + h) * kAttnD) * ES;
+    DN::load(tKn[buf], rK, off, rs, kRB);
+    DTR::load(tKt[buf], rK, off, rs, kRB);
+    DN::load(tVn[buf], rV, off, rs, kRB);
+  };
+  // this lane's query: Q and dO fragments (B operands), O for D
+  const int64_t t = q0 + 16 * w + r16;
+  const uint32_t roff = (uint32_t)((t * H + h) * kAttnD) * ES;
+  Frag<T> qf[2], gf[2], of[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const uint32_t off = roff + (uint32_t)(32 * ks + 8 * g4) * ES;
+    frag_bload(qf[ks], rQ, off);
+    frag_bload(gf[ks], rG, off);
+    frag_bload(of[ks], rO, off);
+  }
+  const int64_t vrow = ((int64_t)b * H + h) * L;
+  const float lse = t < L ? a.lse[vrow + t] : INFINITY;
+  issue(0, 0);
+  // D_t = dO_t . O_t: this lane's 16 head-dim entries, then the 4 lanes of the query
+  float dsum = 0.0f;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dsum += to_f(gf[ks].v[e]) * to_f(of[ks].v[e]);
+  dsum += __shfl_xor(dsum, 16, 64);
+  dsum += __shfl_xor(dsum, 32, 64);
+  if (g4 == 0 && t < L) a.delta[vrow + t] = dsum;
+  const float c = a.scale_log2;
+
+  f32x4 dq[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) zero4(dq[v]);
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int cur = kt & 1;
+    wait_vmem();
+    __syncthreads();
+    if (kt + 1 < nkt) issue(kt + 1, cur ^ 1);
+    // s[u][i], dp[u][i]: query r16 against key k0 + 16 u + 4 g4 + i
+    f32x4 s[4], dp[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      zero4(s[u]);
+      zero4(dp[u]);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        Frag<T> kf, vf;
+        frag_ld8_swz<DN>(kf, tKn[cur], 16 * u + r16, 32 * ks + 8 * g4);
+        frag_ld8_swz<DN>(vf, tVn[cur], 16 * u + r16, 32 * ks + 8 * g4);
+        mma(s[u], kf, qf[ks]);
+        mma(dp[u], vf, gf[ks]);
+      }
+    }
+    const int64_t k0 = (int64_t)kt * kRB;
+    const bool ragged = k0 + kRB > kend;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float p = exp2_fast(fmaf(s[u][i], c, -lse));
+        if (ragged && k0 + 16 * u + 4 * g4 + i >= kend) p = 0.0f;
+        s[u][i] = p * (dp[u][i] - dsum);  // dS
+      }
+    // dQ += dS K
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      float m[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        m[i] = s[2 * q][i];
+        m[4 + i] = s[2 * q + 1][i];
+      }
+      Frag<T> df;
+      frag_from(df, m);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        Frag<T> kt2;
+        frag_rows_swz<DTR>(kt2, tKt[cur], 32 * q + 4 * g4, 32 * q + 16 + 4 * g4, 16 * v);
+        mma(dq[v], df, kt2);
+      }
+    }
+  }
+  const float sc = a.scale;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t tt = q0 + 16 * w + 4 * g4 + i;
+    if (tt >= L) continue;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) a.dq[boff + (tt * H + h) * kAttnD + 16 * v + r16] = sc * dq[v][i];
+  }
+}
+
+// Workgroup = (batch b, head h, 64-key tile); wave w owns keys
+// k0 + 16 w + (0..15).  Query tiles run from the key tile's block on (every
+// query there sees these keys); Q and dO are staged twice (natural rows for
+// the scores, along the query index for dK and dV), lse and D once.
+template <typename T>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1)))
+void k_attn_dkv(AttnArgs a) {
+  using DN = typename AttnTiles<T>::DK;
+  using DTR = typename AttnTiles<T>::DV;
+  constexpr int RB = AttnTiles<T>::RB;
+  constexpr uint32_t ES = sizeof(T);
+  __shared__ __attribute__((aligned(16))) char tQn[2][kRB * RB];
+  __shared__ __attribute__((aligned(16))) char tQt[2][kRB * RB];
+  __shared__ __attribute__((aligned(16))) char tGn[2][kRB * RB];
+  __shared__ __attribute__((aligned(16))) char tGt[2][kRB * RB];
+  __shared__ __attribute__((aligned(16))) float tL[2][kRB];  // lse (+inf past L)
+  __shared__ __attribute__((aligned(16))) float tD[2][kRB];  // D
+  const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
+  const int H = a.H;
+  const int64_t L = a.L;
+  const int nkt = (int)((L + kRB - 1) / kRB);
+  int bx = xcd_linear_id(blockIdx.x, gridDim.x);
+  const int kt = bx % nkt;
+  bx /= nkt;
+  const int h = bx % H, b = bx / H;
+  const int64_t k0 = (int64_t)kt * kRB;
+  const int64_t qbeg = a.block > 0 ? (k0 / a.block) * a.block : 0;
+  const int qt0 = (int)(qbeg / kRB), nqt = (int)((L + kRB - 1) / kRB);
+  const uint32_t rs = (uint32_t)H * kAttnD * ES;
+  const uint32_t nbytes = (uint32_t)(L * H * kAttnD * ES);
+  const int64_t boff = (int64_t)b * L * H * kAttnD;
+  const bufres rQ = make_buf(reinterpret_cast<const T *>(a.q) + boff, nbytes);
+  const bufres rK = make_buf(reinterpret_cast<const T *>(a.k) + boff, nbytes);
+  const bufres rV = make_buf(reinterpret_cast<const T *>(a.v) + boff, nbytes);
+  const bufres rG = make_buf(reinterpret_cast<const T *>(a.dout) + boff, nbytes);
+  const int64_t vrow = ((int64_t)b * H + h) * L;
+  const bufres rL = make_buf(a.lse + vrow, (uint32_t)(L * 4));
+  const bufres rD = make_buf(a.delta + vrow, (uint32_t)(L * 4));
+  auto issue = [&](int qt, int buf) __attribute__((always_inline)) {
+    const uint32_t off = (uint32_t)(((int64_t)qt * kRB * H + h) * kAttnD) * ES;
+    DN::load(tQn[buf], rQ, off, rs, kRB);
+    DTR::load(tQt[buf], rQ, off, rs, kRB);
+    DN::load(tGn[buf], rG, off, rs, kRB);
+    DTR::load(tGt[buf], rG, off, rs, kRB);
+  };
+  // per-query lse and D of a query tile, one value per thread of wave 0
+  auto vec_ld = [&](int qt, float &l, float &d) __attribute__((always_inline)) {
+    const uint32_t q = (uint32_t)(qt * kRB + lane);
+    l = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rL, q * 4u, 0, 0));
+    d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rD, q * 4u, 0, 0));
+    if ((int64_t)q >= L) l = INFINITY;  // queries past L contribute nothing
+  };
+  // this lane's key: K and V fragments (B operands of S = Q K^T, dP = dO V^T)
+  const int64_t s = k0 + 16 * w + r16;
+  Frag<T> kf[2], vf[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const uint32_t off = (uint32_t)((s * H + h) * kAttnD) * ES + (uint32_t)(32 * ks + 8 * g4) * ES;
+    frag_bload(kf[ks], rK, off);
+    frag_bload(vf[ks], rV, off);
+  }
+  issue(qt0, 0);
+  float lnext = 0.0f, dnext = 0.0f;
+  if (w == 0) {
+    vec_ld(qt0, lnext, dnext);
+    wait_vmem();
+    tL[0][lane] = lnext;
+    tD[0][lane] = dnext;
+  }
+  const float c = a.scale_log2;
+
+  f32x4 dk[4], dv[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    zero4(dk[v]);
+    zero4(dv[v]);
+  }
+  for (int qt = qt0; qt < nqt; ++qt) {
+    const int cur = (qt - qt0) & 1;
+    wait_vmem();
+    __syncthreads();  // query tile qt staged; every wave is done with the previous one
+    if (qt + 1 < nqt) {
+      issue(qt + 1, cur ^ 1);
+      if (w == 0) vec_ld(qt + 1, lnext, dnext);
+    }
+    // s[u][i], dp[u][i]: key r16 against query q0 + 16 u + 4 g4 + i
+    f32x4 sv[4], dp[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      zero4(sv[u]);
+      zero4(dp[u]);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        Frag<T> qf, gf;
+        frag_ld8_swz<DN>(qf, tQn[cur], 16 * u + r16, 32 * ks + 8 * g4);
+        frag_ld8_swz<DN>(gf, tGn[cur], 16 * u + r16, 32 * ks + 8 * g4);
+        mma(sv[u], qf, kf[ks]);
+        mma(dp[u], gf, vf[ks]);
+      }
+    }
+    float pm[4][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&tL[cur][16 * u + 4 * g4]);
+      const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&tD[cur][16 * u + 4 * g4]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = exp2_fast(fmaf(sv[u][i], c, -l4[i]));
+        pm[u][i] = p;
+        sv[u][i] = p * (dp[u][i] - d4[i]);  // dS
+      }
+    }
+    // dV += P^T dO, dK += dS^T Q (queries along k)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      float mp[8], md[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        mp[i] = pm[2 * q][i];
+        mp[4 + i] = pm[2 * q + 1][i];
+        md[i] = sv[2 * q][i];
+        md[4 + i] = sv[2 * q + 1][i];
+      }
+      Frag<T> pf, df;
+      frag_from(pf, mp);
+      frag_from(df, md);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        Frag<T> gt, qt2;
+        frag_rows_swz<DTR>(gt, tGt[cur], 32 * q + 4 * g4, 32 * q + 16 + 4 * g4, 16 * v);
+        frag_rows_swz<DTR>(qt2, tQt[cur], 32 * q + 4 * g4, 32 * q + 16 + 4 * g4, 16 * v);
+        mma(dv[v], pf, gt);
+        mma(dk[v], df, qt2);
+      }
+    }
+    if (qt + 1 < nqt && w == 0) {
+      // the other buffer's previous readers passed the barrier above
+      asm volatile("" : "+v"(lnext), "+v"(dnext) : : "memory");
+      tL[cur ^ 1][lane] = lnext;
+      tD[cur ^ 1][lane] = dnext;
+    }
+  }
+  const float sc = a.scale;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t ss = k0 + 16 * w + 4 * g4 + i;
+    if (ss >= L) continue;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      a.dk[boff + (ss * H + h) * kAttnD + 16 * v + r16] = sc * dk[v][i];
+      a.dv[boff + (ss * H + h) * kAttnD + 16 * v + r16] = dv[v][i];
+    }
+  }
+}
+
+hipError_t launch_attention_backward(const AttnArgs &a, hipStream_t st) {
+  const int64_t nt = (a.L + kRB - 1) / kRB;
+  dim3 g((unsigned)(a.Z * a.H * nt));
+  if (a.dtype == 1) {
+    hipLaunchKernelGGL(k_attn_dq<bf16>, g, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(k_attn_dkv<bf16>, g, dim3(kThreads), 0, st, a);
+  } else {
+    hipLaunchKernelGGL(k_attn_dq<float>, g, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(k_attn_dkv<float>, g, dim3(kThreads), 0, st, a);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_attention(const AttnArgs &a, hipStream_t st) {

@@ -147,12 +147,19 @@ struct BwdArgs {
 constexpr int kAttnD = 64;  // head dim
 struct AttnArgs {
   const void *q, *k, *v;  // [Z][L][H][kAttnD], dtype
-  void *o;                // [Z][L][H][kAttnD], dtype
+  void *o;                // forward: output; backward: the forward's output (read)
+  float *lse;             // [Z][H][L] per-query log2-sum-exp of c * scores (forward: written
+                          // if set; backward: read)
+  const void *dout;       // backward: dO, [Z][L][H][kAttnD], dtype
+  float *dq, *dk, *dv;    // backward: fp32 gradients, [Z][L][H][kAttnD]
+  float *delta;           // backward: D = rowsum(dO * O), [Z][H][L] (workspace)
   int64_t L, block;       // block: 0 full, > 0 block-wise (a multiple of 64)
   int Z, H, dtype;
+  float scale;            // softmax scale
   float scale_log2;       // scale * log2(e)
 };
 hipError_t launch_attention(const AttnArgs &a, hipStream_t st);
+hipError_t launch_attention_backward(const AttnArgs &a, hipStream_t st);
 
 hipError_t launch_bwd_panels(const BwdArgs &a, hipStream_t st);
 hipError_t launch_bwd_decay(const BwdArgs &a, hipStream_t st);

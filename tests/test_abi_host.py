@@ -220,11 +220,11 @@ def attn_shape(**kw):
 
 
 def call_attention(lib, s, scale=0.0, **over):
-    args = dict(q=addr(0), k=addr(1), v=addr(2), o=addr(3), stream=None)
+    args = dict(q=addr(0), k=addr(1), v=addr(2), o=addr(3), lse=None, stream=None)
     args.update(over)
     return lib.bissd_attention_forward(C.byref(s) if s is not None else None, args["q"],
                                        args["k"], args["v"], C.c_float(scale), args["o"],
-                                       args["stream"])
+                                       args["lse"], args["stream"])
 
 
 @pytest.mark.parametrize("over,scale,code", [
@@ -242,4 +242,25 @@ def test_attention_pointers(lib):
     assert call_attention(lib, s, q=None) == -1
     assert call_attention(lib, s, o=C.c_void_p(A + 8)) == -4
     assert call_attention(lib, s, o=addr(1)) == -7   # o over k
+
+
+def test_attention_backward_validation(lib):
+    s = attn_shape()
+    n = lib.bissd_attention_workspace_size(C.byref(s))
+    assert n >= 2 * 12 * 300 * 4
+    assert lib.bissd_attention_workspace_size(C.byref(attn_shape(headdim=32))) == 0
+
+    def bwd(**over):
+        args = dict(q=addr(0), k=addr(1), v=addr(2), o=addr(3), do=addr(4), lse=addr(5),
+                    dq=addr(6), dk=addr(7), dv=addr(8), ws=addr(9), nws=1 << 30)
+        args.update(over)
+        return lib.bissd_attention_backward(C.byref(s), args["q"], args["k"], args["v"],
+                                            args["o"], args["do"], args["lse"], C.c_float(0.0),
+                                            args["dq"], args["dk"], args["dv"], args["ws"],
+                                            C.c_size_t(args["nws"]), None)
+    assert bwd(lse=None) == -1
+    assert bwd(nws=16) == -5
+    assert bwd(dq=C.c_void_p(A * 7 + 8)) == -4
+    assert bwd(dk=addr(6)) == -7      # dk over dq
+    assert bwd(ws=addr(0)) == -7      # workspace over q
 

@@ -62,3 +62,46 @@ def test_block_wise_matches_full_attention_on_each_prefix():
         part = {k: v[:, :hi].contiguous() for k, v in T.items()}
         of = host(ssd.bissd_attention_forward(part["q"], part["k"], part["v"]))
         assert np.array_equal(ob[:, i * blk:hi], of[:, i * blk:hi]), i
+
+
+def run_bwd(Z, L, H, dtype, block=0, seed=11):
+    import state_space_denoisers_amd as ssd
+    inp = gen.make_attention_inputs(Z, L, H, dtype, seed)
+    dout = gen.make_attention_inputs(Z, L, H, dtype, seed + 1)["q"]
+    T = {k: gen.as_torch(v, dtype, device()) for k, v in inp.items()}
+    G = gen.as_torch(dout, dtype, device())
+    lse = torch.empty((Z, H, L), dtype=torch.float32, device=device())
+    o = ssd.bissd_attention_forward(T["q"], T["k"], T["v"], block=block, lse=lse)
+    g = ssd.bissd_attention_backward(T["q"], T["k"], T["v"], o, G, lse, block=block)
+    torch.cuda.synchronize()
+    ref = AT.backward(inp["q"], inp["k"], inp["v"], dout, block=block)
+    errs = {n: maxrel(host(g[n]), ref[n]) for n in ("dq", "dk", "dv")}
+    print(f"attn bwd {dtype} Z={Z} L={L} H={H} block={block} " +
+          " ".join(f"{n}={e:.1e}" for n, e in errs.items()), flush=True)
+    return errs
+
+
+@pytest.mark.parametrize("L", [1, 63, 65, 200, 513])
+@pytest.mark.parametrize("block", [0, 64, 128])
+def test_backward_fp32(L, block):
+    errs = run_bwd(2, L, 3, "fp32", block)
+    assert max(errs.values()) <= TOL["fp32"], errs
+
+
+@pytest.mark.parametrize("block", [0, 256])
+def test_backward_bf16_hybrid_layer(block):
+    errs = run_bwd(2, 1024, 12, "bf16", block)
+    assert max(errs.values()) <= TOL["bf16"], errs
+
+
+def test_backward_deterministic():
+    import state_space_denoisers_amd as ssd
+    Z, L, H = 1, 700, 4
+    inp = gen.make_attention_inputs(Z, L, H, "bf16", 13)
+    T = {k: gen.as_torch(v, "bf16", device()) for k, v in inp.items()}
+    lse = torch.empty((Z, H, L), dtype=torch.float32, device=device())
+    o = ssd.bissd_attention_forward(T["q"], T["k"], T["v"], lse=lse)
+    a = ssd.bissd_attention_backward(T["q"], T["k"], T["v"], o, T["v"], lse)
+    b = ssd.bissd_attention_backward(T["q"], T["k"], T["v"], o, T["v"], lse)
+    for n in a:
+        assert torch.equal(a[n], b[n]), n
