@@ -243,8 +243,9 @@ void k_attn_fwd(AttnArgs a) {
 // one: per query in k_attn_dq (S^T = K Q^T, dP^T = V dO^T), per key in
 // k_attn_dkv (S = Q K^T, dP = dO V^T).
 
-// Workgroup = (batch b, head h, 64-query tile); wave w owns queries
-// q0 + 16 w + (0..15).  K is staged twice (natural rows for the scores,
+// Workgroup = (batch b, head h, 128-query tile); wave w owns queries
+// q0 + 32 w + 16 j + (0..15), j = 0, 1, so every K and V fragment read from
+// LDS feeds two products.  K is staged twice (natural rows for the scores,
 // along the key index for dQ), V once.
 template <typename T>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 3 : 1)))
@@ -259,14 +260,21 @@ void k_attn_dq(AttnArgs a) {
   const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
   const int H = a.H;
   const int64_t L = a.L;
-  const int nqt = (int)((L + kRB - 1) / kRB);
+  const int nqt = (int)((L + kAttnQ - 1) / kAttnQ);
   int bx = xcd_linear_id(blockIdx.x, gridDim.x);
   const int qt = bx % nqt;
   bx /= nqt;
   const int h = bx % H, b = bx / H;
-  const int64_t q0 = (int64_t)qt * kRB;
-  const int64_t kend = a.block > 0 ? min(L, (q0 / a.block + 1) * a.block) : L;
-  const int nkt = (int)((kend + kRB - 1) / kRB);
+  const int64_t q0 = (int64_t)qt * kAttnQ;
+  int64_t kend[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int64_t g0 = q0 + 32 * w + 16 * j;
+    kend[j] = a.block > 0 ? min(L, (g0 / a.block + 1) * a.block) : L;
+  }
+  const int64_t qlast = min(L, q0 + kAttnQ) - 1;
+  const int64_t kmax = a.block > 0 ? min(L, (qlast / a.block + 1) * a.block) : L;
+  const int nkt = (int)((kmax + kRB - 1) / kRB);
   const uint32_t rs = (uint32_t)H * kAttnD * ES;
   const uint32_t nbytes = (uint32_t)(L * H * kAttnD * ES);
   const int64_t boff = (int64_t)b * L * H * kAttnD;
@@ -281,97 +289,122 @@ void k_attn_dq(AttnArgs a) {
     DTR::load(tKt[buf], rK, off, rs, kRB);
     DN::load(tVn[buf], rV, off, rs, kRB);
   };
-  // this lane's query: Q and dO fragments (B operands), O for D
-  const int64_t t = q0 + 16 * w + r16;
-  const uint32_t roff = (uint32_t)((t * H + h) * kAttnD) * ES;
-  Frag<T> qf[2], gf[2], of[2];
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    const uint32_t off = roff + (uint32_t)(32 * ks + 8 * g4) * ES;
-    frag_bload(qf[ks], rQ, off);
-    frag_bload(gf[ks], rG, off);
-    frag_bload(of[ks], rO, off);
-  }
+  // this lane's two queries: Q and dO fragments (B operands), and
+  // D_t = dO_t . O_t (this lane's 16 head-dim entries, then the 4 lanes of
+  // the query), written for the dK / dV pass
   const int64_t vrow = ((int64_t)b * H + h) * L;
-  const float lse = t < L ? a.lse[vrow + t] : INFINITY;
+  Frag<T> qf[2][2], gf[2][2];
+  float lse[2], dsum[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int64_t t = q0 + 32 * w + 16 * j + r16;
+    const uint32_t roff = (uint32_t)((t * H + h) * kAttnD) * ES;
+    float ds = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const uint32_t off = roff + (uint32_t)(32 * ks + 8 * g4) * ES;
+      Frag<T> of;
+      frag_bload(qf[j][ks], rQ, off);
+      frag_bload(gf[j][ks], rG, off);
+      frag_bload(of, rO, off);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ds += to_f(gf[j][ks].v[e]) * to_f(of.v[e]);
+    }
+    ds += __shfl_xor(ds, 16, 64);
+    ds += __shfl_xor(ds, 32, 64);
+    dsum[j] = ds;
+    lse[j] = t < L ? a.lse[vrow + t] : INFINITY;
+    if (g4 == 0 && t < L) a.delta[vrow + t] = ds;
+  }
   issue(0, 0);
-  // D_t = dO_t . O_t: this lane's 16 head-dim entries, then the 4 lanes of the query
-  float dsum = 0.0f;
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) dsum += to_f(gf[ks].v[e]) * to_f(of[ks].v[e]);
-  dsum += __shfl_xor(dsum, 16, 64);
-  dsum += __shfl_xor(dsum, 32, 64);
-  if (g4 == 0 && t < L) a.delta[vrow + t] = dsum;
   const float c = a.scale_log2;
 
-  f32x4 dq[4];
+  f32x4 dq[2][4];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) zero4(dq[v]);
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) zero4(dq[j][v]);
   for (int kt = 0; kt < nkt; ++kt) {
     const int cur = kt & 1;
     wait_vmem();
     __syncthreads();
     if (kt + 1 < nkt) issue(kt + 1, cur ^ 1);
-    // s[u][i], dp[u][i]: query r16 against key k0 + 16 u + 4 g4 + i
-    f32x4 s[4], dp[4];
+    // s[j][u][i], dp[j][u][i]: query r16 of group j against key k0 + 16 u + 4 g4 + i
+    f32x4 s[2][4], dp[2][4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      zero4(s[u]);
-      zero4(dp[u]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        zero4(s[j][u]);
+        zero4(dp[j][u]);
+      }
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         Frag<T> kf, vf;
         frag_ld8_swz<DN>(kf, tKn[cur], 16 * u + r16, 32 * ks + 8 * g4);
         frag_ld8_swz<DN>(vf, tVn[cur], 16 * u + r16, 32 * ks + 8 * g4);
-        mma(s[u], kf, qf[ks]);
-        mma(dp[u], vf, gf[ks]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          mma(s[j][u], kf, qf[j][ks]);
+          mma(dp[j][u], vf, gf[j][ks]);
+        }
       }
     }
     const int64_t k0 = (int64_t)kt * kRB;
-    const bool ragged = k0 + kRB > kend;
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int j = 0; j < 2; ++j) {
+      const bool ragged = k0 + kRB > kend[j];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float p = exp2_fast(fmaf(s[u][i], c, -lse));
-        if (ragged && k0 + 16 * u + 4 * g4 + i >= kend) p = 0.0f;
-        s[u][i] = p * (dp[u][i] - dsum);  // dS
-      }
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float p = exp2_fast(fmaf(s[j][u][i], c, -lse[j]));
+          if (ragged && k0 + 16 * u + 4 * g4 + i >= kend[j]) p = 0.0f;
+          s[j][u][i] = p * (dp[j][u][i] - dsum[j]);  // dS
+        }
+    }
     // dQ += dS K
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      float m[8];
+      Frag<T> df[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        m[i] = s[2 * q][i];
-        m[4 + i] = s[2 * q + 1][i];
+      for (int j = 0; j < 2; ++j) {
+        float m[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          m[i] = s[j][2 * q][i];
+          m[4 + i] = s[j][2 * q + 1][i];
+        }
+        frag_from(df[j], m);
       }
-      Frag<T> df;
-      frag_from(df, m);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         Frag<T> kt2;
         frag_rows_swz<DTR>(kt2, tKt[cur], 32 * q + 4 * g4, 32 * q + 16 + 4 * g4, 16 * v);
-        mma(dq[v], df, kt2);
+        mma(dq[0][v], df[0], kt2);
+        mma(dq[1][v], df[1], kt2);
       }
     }
   }
   const float sc = a.scale;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t tt = q0 + 16 * w + 4 * g4 + i;
-    if (tt >= L) continue;
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) a.dq[boff + (tt * H + h) * kAttnD + 16 * v + r16] = sc * dq[v][i];
-  }
+    for (int i = 0; i < 4; ++i) {
+      const int64_t tt = q0 + 32 * w + 16 * j + 4 * g4 + i;
+      if (tt >= L) continue;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) a.dq[boff + (tt * H + h) * kAttnD + 16 * v + r16] = sc * dq[j][v][i];
+    }
 }
 
-// Workgroup = (batch b, head h, 64-key tile); wave w owns keys
-// k0 + 16 w + (0..15).  Query tiles run from the key tile's block on (every
-// query there sees these keys); Q and dO are staged twice (natural rows for
-// the scores, along the query index for dK and dV), lse and D once.
+// Workgroup = (batch b, head h, 128-key tile); wave w owns keys
+// k0 + 32 w + 16 j + (0..15), j = 0, 1, so every Q and dO fragment read from
+// LDS feeds two products.  Query tiles run from the first key group's block
+// on (every later query sees the keys of its block and before); a key group
+// whose block starts later skips the tiles before it.  Q and dO are staged
+// twice (natural rows for the scores, along the query index for dK and dV),
+// lse and D once.
 template <typename T>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1)))
 void k_attn_dkv(AttnArgs a) {
@@ -388,14 +421,21 @@ void k_attn_dkv(AttnArgs a) {
   const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
   const int H = a.H;
   const int64_t L = a.L;
-  const int nkt = (int)((L + kRB - 1) / kRB);
+  const int nkt = (int)((L + kAttnQ - 1) / kAttnQ);
   int bx = xcd_linear_id(blockIdx.x, gridDim.x);
   const int kt = bx % nkt;
   bx /= nkt;
   const int h = bx % H, b = bx / H;
-  const int64_t k0 = (int64_t)kt * kRB;
-  const int64_t qbeg = a.block > 0 ? (k0 / a.block) * a.block : 0;
-  const int qt0 = (int)(qbeg / kRB), nqt = (int)((L + kRB - 1) / kRB);
+  const int64_t k0 = (int64_t)kt * kAttnQ;
+  // first query tile each key group needs (its block's start; 0 when full)
+  int qbeg[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int64_t g0 = k0 + 32 * w + 16 * j;
+    qbeg[j] = a.block > 0 ? (int)((g0 / a.block) * a.block / kRB) : 0;
+  }
+  const int qt0 = a.block > 0 ? (int)((k0 / a.block) * a.block / kRB) : 0;
+  const int nqt = (int)((L + kRB - 1) / kRB);
   const uint32_t rs = (uint32_t)H * kAttnD * ES;
   const uint32_t nbytes = (uint32_t)(L * H * kAttnD * ES);
   const int64_t boff = (int64_t)b * L * H * kAttnD;
@@ -420,14 +460,17 @@ void k_attn_dkv(AttnArgs a) {
     d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rD, q * 4u, 0, 0));
     if ((int64_t)q >= L) l = INFINITY;  // queries past L contribute nothing
   };
-  // this lane's key: K and V fragments (B operands of S = Q K^T, dP = dO V^T)
-  const int64_t s = k0 + 16 * w + r16;
-  Frag<T> kf[2], vf[2];
+  // this lane's two keys: K and V fragments (B operands of S = Q K^T, dP = dO V^T)
+  Frag<T> kf[2][2], vf[2][2];
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    const uint32_t off = (uint32_t)((s * H + h) * kAttnD) * ES + (uint32_t)(32 * ks + 8 * g4) * ES;
-    frag_bload(kf[ks], rK, off);
-    frag_bload(vf[ks], rV, off);
+  for (int j = 0; j < 2; ++j) {
+    const int64_t s = k0 + 32 * w + 16 * j + r16;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const uint32_t off = (uint32_t)((s * H + h) * kAttnD) * ES + (uint32_t)(32 * ks + 8 * g4) * ES;
+      frag_bload(kf[j][ks], rK, off);
+      frag_bload(vf[j][ks], rV, off);
+    }
   }
   issue(qt0, 0);
   float lnext = 0.0f, dnext = 0.0f;
@@ -439,12 +482,14 @@ void k_attn_dkv(AttnArgs a) {
   }
   const float c = a.scale_log2;
 
-  f32x4 dk[4], dv[4];
+  f32x4 dk[2][4], dv[2][4];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    zero4(dk[v]);
-    zero4(dv[v]);
-  }
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      zero4(dk[j][v]);
+      zero4(dv[j][v]);
+    }
   for (int qt = qt0; qt < nqt; ++qt) {
     const int cur = (qt - qt0) & 1;
     wait_vmem();
@@ -453,54 +498,70 @@ void k_attn_dkv(AttnArgs a) {
       issue(qt + 1, cur ^ 1);
       if (w == 0) vec_ld(qt + 1, lnext, dnext);
     }
-    // s[u][i], dp[u][i]: key r16 against query q0 + 16 u + 4 g4 + i
-    f32x4 sv[4], dp[4];
+    // sv[j][u][i], dp[j][u][i]: key r16 of group j against query q0 + 16 u + 4 g4 + i
+    f32x4 sv[2][4], dp[2][4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      zero4(sv[u]);
-      zero4(dp[u]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        zero4(sv[j][u]);
+        zero4(dp[j][u]);
+      }
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         Frag<T> qf, gf;
         frag_ld8_swz<DN>(qf, tQn[cur], 16 * u + r16, 32 * ks + 8 * g4);
         frag_ld8_swz<DN>(gf, tGn[cur], 16 * u + r16, 32 * ks + 8 * g4);
-        mma(sv[u], qf, kf[ks]);
-        mma(dp[u], gf, vf[ks]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          mma(sv[j][u], qf, kf[j][ks]);
+          mma(dp[j][u], gf, vf[j][ks]);
+        }
       }
     }
-    float pm[4][4];
+    float pm[2][4][4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&tL[cur][16 * u + 4 * g4]);
       const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&tD[cur][16 * u + 4 * g4]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = exp2_fast(fmaf(sv[u][i], c, -l4[i]));
-        pm[u][i] = p;
-        sv[u][i] = p * (dp[u][i] - d4[i]);  // dS
+      for (int j = 0; j < 2; ++j) {
+        const bool on = qt >= qbeg[j];  // the group's block has begun
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = on ? exp2_fast(fmaf(sv[j][u][i], c, -l4[i])) : 0.0f;
+          pm[j][u][i] = p;
+          sv[j][u][i] = p * (dp[j][u][i] - d4[i]);  // dS
+        }
       }
     }
     // dV += P^T dO, dK += dS^T Q (queries along k)
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      float mp[8], md[8];
+      Frag<T> pf[2], df[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        mp[i] = pm[2 * q][i];
-        mp[4 + i] = pm[2 * q + 1][i];
-        md[i] = sv[2 * q][i];
-        md[4 + i] = sv[2 * q + 1][i];
+      for (int j = 0; j < 2; ++j) {
+        float mp[8], md[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          mp[i] = pm[j][2 * q][i];
+          mp[4 + i] = pm[j][2 * q + 1][i];
+          md[i] = sv[j][2 * q][i];
+          md[4 + i] = sv[j][2 * q + 1][i];
+        }
+        frag_from(pf[j], mp);
+        frag_from(df[j], md);
       }
-      Frag<T> pf, df;
-      frag_from(pf, mp);
-      frag_from(df, md);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         Frag<T> gt, qt2;
         frag_rows_swz<DTR>(gt, tGt[cur], 32 * q + 4 * g4, 32 * q + 16 + 4 * g4, 16 * v);
         frag_rows_swz<DTR>(qt2, tQt[cur], 32 * q + 4 * g4, 32 * q + 16 + 4 * g4, 16 * v);
-        mma(dv[v], pf, gt);
-        mma(dk[v], df, qt2);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          mma(dv[j][v], pf[j], gt);
+          mma(dk[j][v], df[j], qt2);
+        }
       }
     }
     if (qt + 1 < nqt && w == 0) {
@@ -512,26 +573,28 @@ void k_attn_dkv(AttnArgs a) {
   }
   const float sc = a.scale;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t ss = k0 + 16 * w + 4 * g4 + i;
-    if (ss >= L) continue;
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      a.dk[boff + (ss * H + h) * kAttnD + 16 * v + r16] = sc * dk[v][i];
-      a.dv[boff + (ss * H + h) * kAttnD + 16 * v + r16] = dv[v][i];
+    for (int i = 0; i < 4; ++i) {
+      const int64_t ss = k0 + 32 * w + 16 * j + 4 * g4 + i;
+      if (ss >= L) continue;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        a.dk[boff + (ss * H + h) * kAttnD + 16 * v + r16] = sc * dk[j][v][i];
+        a.dv[boff + (ss * H + h) * kAttnD + 16 * v + r16] = dv[j][v][i];
+      }
     }
-  }
 }
 
 hipError_t launch_attention_backward(const AttnArgs &a, hipStream_t st) {
-  const int64_t nt = (a.L + kRB - 1) / kRB;
-  dim3 g((unsigned)(a.Z * a.H * nt));
+  dim3 gq((unsigned)(a.Z * a.H * ((a.L + kAttnQ - 1) / kAttnQ)));
+  dim3 gk((unsigned)(a.Z * a.H * ((a.L + kAttnQ - 1) / kAttnQ)));
   if (a.dtype == 1) {
-    hipLaunchKernelGGL(k_attn_dq<bf16>, g, dim3(kThreads), 0, st, a);
-    hipLaunchKernelGGL(k_attn_dkv<bf16>, g, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(k_attn_dq<bf16>, gq, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(k_attn_dkv<bf16>, gk, dim3(kThreads), 0, st, a);
   } else {
-    hipLaunchKernelGGL(k_attn_dq<float>, g, dim3(kThreads), 0, st, a);
-    hipLaunchKernelGGL(k_attn_dkv<float>, g, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(k_attn_dq<float>, gq, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(k_attn_dkv<float>, gk, dim3(kThreads), 0, st, a);
   }
   return hipGetLastError();
 }
