@@ -503,6 +503,25 @@ def bench_generation(steps_per_block=8, blocks=2, prefix=65536):
 def profile_phase(args):
     import torch
     from synth import gen
+    if args.profile_phase == "attention":
+        # the hybrids' attention layer: forward (with lse) then backward,
+        # Z = 8, L = 4096, 12 heads of 64, bf16, full bidirectional
+        import state_space_denoisers_amd as ssd
+        dev = torch.device("cuda", 0)
+        Z, L, H = 8, 4096, 12
+        inp = gen.make_attention_inputs(Z, L, H, "bf16", 2002)
+        T = {k: gen.as_torch(v, "bf16", dev) for k, v in inp.items()}
+        dout = gen.as_torch(gen.make_attention_inputs(Z, L, H, "bf16", 2003)["q"], "bf16", dev)
+        lse = torch.empty((Z, H, L), dtype=torch.float32, device=dev)
+        o = torch.empty_like(T["q"])
+        torch.cuda.synchronize()
+        print(f"profiling attention forward + backward Z={Z} L={L} H={H} x{args.iters}", flush=True)
+        for _ in range(args.iters):
+            ssd.bissd_attention_forward(T["q"], T["k"], T["v"], o=o, lse=lse)
+            ssd.bissd_attention_backward(T["q"], T["k"], T["v"], o, dout, lse)
+        torch.cuda.synchronize()
+        print("done", flush=True)
+        return
     w = gen.WORKLOADS[args.workload]
     if args.profile_phase == "block":
         import state_space_denoisers_amd as ssd
@@ -557,7 +576,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--profile-phase", choices=["0", "1", "2", "3", "all", "backward", "block"])
+    ap.add_argument("--profile-phase", choices=["0", "1", "2", "3", "all", "backward", "block", "attention"])
     ap.add_argument("--workload", default="layer130m_L1k")
     ap.add_argument("--iters", type=int, default=20)
     ap.add_argument("--copy-calibrate", action="store_true")
