@@ -62,7 +62,16 @@ def direction_matrices(dt_f, A_f, B_f, C_f, dt_r, A_r, B_r, C_r, rev_block=0):
 
 def forward_torch(T: dict, init_state=None, rev_block=0):
     """y (and per-direction parts) from torch float64 tensors in the GPU
-    library's layouts.  Differentiable."""
+    library's layouts.  Differentiable.  A direction with "dt_bias_<d>" in T
+    first maps its dt through clamp(softplus(dt + bias), lo, hi) (torch's own
+    softplus and clamp)."""
+    T = dict(T)
+    for d in ("f", "r"):
+        if T.get(f"dt_bias_{d}") is not None:
+            z = T[f"dt_{d}"] + T[f"dt_bias_{d}"][None, None, :]
+            T[f"dt_{d}"] = torch.clamp(torch.nn.functional.softplus(z, threshold=1e9),
+                                       float(T.get(f"dt_min_{d}", 0.0)),
+                                       float(T.get(f"dt_max_{d}", float("inf"))))
     x = T["x"]
     Z, L, H, P = x.shape
     G = T["B_f"].shape[2]
@@ -105,13 +114,19 @@ def forward(inp: dict, init_state=None, rev_block=0) -> dict:
 
 def gradients(inp: dict, dy, init_state=None, rev_block=0) -> dict:
     """Reverse-mode gradients of sum(dy * y) by torch autograd on the dense
-    form: dx, ddt_f, dA_f, dB_f, dC_f, ddt_r, dA_r, dB_r, dC_r, dD."""
-    T = {k: _t(inp[k], requires_grad=True) for k in KEYS}
+    form: dx, ddt_f, dA_f, dB_f, dC_f, ddt_r, dA_r, dB_r, dC_r, dD (and
+    ddt_bias_<d> for a direction with a dt bias)."""
+    keys = list(KEYS) + [f"dt_bias_{d}" for d in ("f", "r") if inp.get(f"dt_bias_{d}") is not None]
+    T = {k: _t(inp[k], requires_grad=True) for k in keys}
+    for d in ("f", "r"):
+        for lim in ("dt_min", "dt_max"):
+            if f"{lim}_{d}" in inp:
+                T[f"{lim}_{d}"] = inp[f"{lim}_{d}"]
     S0 = None if init_state is None else _t(init_state)
     y, _, _ = forward_torch(T, S0, rev_block)
     loss = (y * _t(dy)).sum()
     loss.backward()
-    out = {("d" + k): T[k].grad.numpy().copy() for k in KEYS}
+    out = {("d" + k): T[k].grad.numpy().copy() for k in keys}
     return out
 
 

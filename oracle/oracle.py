@@ -15,6 +15,7 @@ import threading
 import numpy as np
 
 from . import build as _build
+from . import dt_act as _dt
 
 _lock = threading.Lock()
 _lib = None
@@ -79,7 +80,10 @@ def forward(inp: dict, init_state=None, parts: bool = False, final_state: bool =
     """y = y_fwd + y_rev + D x.  Returns y, or a dict with y, y_f, y_r and
     final_state when ``parts`` or ``final_state`` is set.  ``rev_block`` > 0
     restarts the reverse scan from zero at the end of every block of that
-    many tokens (0: one reverse scan over the whole sequence)."""
+    many tokens (0: one reverse scan over the whole sequence).  A direction
+    with ``dt_bias_<d>`` in ``inp`` takes its dt through the post-processing
+    of dt_act.py first."""
+    inp = _dt.effective(inp)
     keep = []
     x = _f64(inp["x"])
     D = _f64(inp["D"])
@@ -102,6 +106,7 @@ def forward(inp: dict, init_state=None, parts: bool = False, final_state: bool =
 def block_update(inp: dict, state_in, want_state_out: bool = True, nthreads: int = 0):
     """Block update with partial bidirectionality.  ``inp`` holds the active
     block's tensors; returns (y_blk, state_out or None)."""
+    inp = _dt.effective(inp)
     keep = []
     x = _f64(inp["x"])
     D = _f64(inp["D"])
@@ -119,7 +124,11 @@ def block_update(inp: dict, state_in, want_state_out: bool = True, nthreads: int
 
 def backward(inp: dict, dy, init_state=None, nthreads: int = 0, rev_block: int = 0) -> dict:
     """Gradients of sum(dy * y): dx, ddt_f, dA_f, dB_f, dC_f, ddt_r, dA_r,
-    dB_r, dC_r, dD (``rev_block`` as in forward)."""
+    dB_r, dC_r, dD (``rev_block`` as in forward).  For a direction with a dt
+    bias, ddt_<d> is the gradient of its pre-activation dt and ddt_bias_<d>
+    that of the bias."""
+    raw = inp
+    inp = _dt.effective(inp)
     keep = []
     x = _f64(inp["x"])
     D = _f64(inp["D"])
@@ -141,6 +150,11 @@ def backward(inp: dict, dy, init_state=None, nthreads: int = 0, rev_block: int =
                              *[_ptr(g[k]) for k in order], C.c_int(nthreads))
     if rc != 0:
         raise RuntimeError(f"ssdo_backward failed ({rc})")
+    for d in ("f", "r"):
+        if _dt.has_act(raw, d):
+            lo, hi = _dt.limits(raw, d)
+            g[f"ddt_{d}"], g[f"ddt_bias_{d}"] = _dt.backward(raw[f"dt_{d}"], raw[f"dt_bias_{d}"],
+                                                           lo, hi, g[f"ddt_{d}"])
     return g
 
 

@@ -500,3 +500,55 @@ def test_attention_backward_finite_differences():
         args_m[idx] = args_m[idx] - eps * d
         fd = (np.sum(AT.forward(*args_p, block=8) * do) - np.sum(AT.forward(*args_m, block=8) * do)) / (2 * eps)
         assert abs(fd - np.sum(g[name] * d)) <= 1e-7 * max(1.0, abs(fd)), name
+
+
+# ------------------------------------------- P14 dt post-processing
+
+from oracle import dt_act as DTA
+
+
+def _with_dt_act(inp, seed, lo=1e-3, hi=0.1):
+    """Pre-activation dt ~ N(0, 1) with per-head biases around -4 (the
+    synthetic dt recipe's shift) and the recipe's clamp."""
+    r = np.random.default_rng(seed)
+    out = dict(inp)
+    Z, L, H = inp["dt_f"].shape
+    for d in ("f", "r"):
+        out[f"dt_{d}"] = r.standard_normal((Z, L, H))
+        out[f"dt_bias_{d}"] = -4.0 + 0.5 * r.standard_normal(H)
+        out[f"dt_min_{d}"], out[f"dt_max_{d}"] = lo, hi
+    return out
+
+
+def test_dt_post_processing_reduces_to_the_plain_scan():
+    """Feeding softplus^{-1}(dt) - bias with no clamp reproduces the scan
+    of dt itself."""
+    inp = rand_inputs(2, 40, 3, 4, 5, 1, seed=60)
+    q = dict(inp)
+    r = np.random.default_rng(61)
+    for d in ("f", "r"):
+        b = r.standard_normal(3)
+        q[f"dt_bias_{d}"] = b
+        q[f"dt_{d}"] = np.log(np.expm1(inp[f"dt_{d}"])) - b[None, None, :]
+    assert rel(O.forward(q), O.forward(inp)) < 1e-12
+
+
+def test_dt_post_processing_clamps():
+    inp = _with_dt_act(rand_inputs(1, 30, 2, 3, 4, 1, seed=62), 63)
+    eff = DTA.effective(inp)
+    for d in ("f", "r"):
+        assert eff[f"dt_{d}"].min() >= 1e-3 and eff[f"dt_{d}"].max() <= 0.1
+        assert np.any(eff[f"dt_{d}"] == 1e-3) or np.any(eff[f"dt_{d}"] == 0.1)
+
+
+@pytest.mark.parametrize("rb", [0, 8])
+def test_dt_post_processing_backward_matches_autograd(rb):
+    """Chain rule through softplus and clamp (and dbias) against autograd of
+    the dense form with torch's softplus and clamp."""
+    inp = _with_dt_act(rand_inputs(2, 24, 3, 3, 4, 1, seed=64), 65)
+    dy = np.random.default_rng(66).standard_normal(inp["x"].shape)
+    g = O.backward(inp, dy, rev_block=rb)
+    ref = dense.gradients(inp, dy, rev_block=rb)
+    for k in list(KEYS) + ["dt_bias_f", "dt_bias_r"]:
+        assert rel(g["d" + k], ref["d" + k]) < 1e-11, k
+    assert np.any(g["ddt_f"] == 0.0)  # clamped tokens pass no gradient
