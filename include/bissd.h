@@ -116,21 +116,30 @@ typedef struct {
                         a multiple of it; bissd_block_update takes 0 only. */
 } bissd_shape_t;
 
-/* One scan direction's parameters.  dt is already positive (no softplus,
- * bias or clamp is applied by the library). */
+/* One scan direction's parameters.  Without dt_bias, dt is the step itself
+ * (already positive).  With dt_bias, dt holds the mixer's pre-activation and
+ * every kernel reads the step as Mamba-2 forms it,
+ *     dt_step[b][t][h] = clamp(softplus(dt[b][t][h] + dt_bias[h]), dt_min, dt_max),
+ * in fp32, without a separate pass over dt. */
 typedef struct {
-  const void *dt;  /* [Z][L][H] dtype */
-  const float *A;  /* [H] fp32, the per-head scalar decay rate (A <= 0) */
-  const void *B;   /* [Z][L][G][N] dtype */
-  const void *C;   /* [Z][L][G][N] dtype */
+  const void *dt;         /* [Z][L][H] dtype */
+  const float *A;         /* [H] fp32, the per-head scalar decay rate (A <= 0) */
+  const void *B;          /* [Z][L][G][N] dtype */
+  const void *C;          /* [Z][L][G][N] dtype */
+  const float *dt_bias;   /* [H] fp32, or NULL: no post-processing */
+  float dt_min, dt_max;   /* clamp range with dt_bias: 0 <= dt_min <= dt_max
+                             (INFINITY for no upper bound) */
 } bissd_dir_t;
 
 /* One direction's parameter gradients (all fp32, overwritten). */
 typedef struct {
-  float *ddt;  /* [Z][L][H] */
-  float *dA;   /* [H], summed over batch and time */
-  float *dB;   /* [Z][L][G][N], summed over the heads of each group */
-  float *dC;   /* [Z][L][G][N], summed over the heads of each group */
+  float *ddt;       /* [Z][L][H]; with dt_bias, the gradient of the pre-activation dt
+                       (zero where the clamp holds the step at a bound) */
+  float *dA;        /* [H], summed over batch and time */
+  float *dB;        /* [Z][L][G][N], summed over the heads of each group */
+  float *dC;        /* [Z][L][G][N], summed over the heads of each group */
+  float *ddt_bias;  /* [H], summed over batch and time: required when the
+                       direction has dt_bias, ignored otherwise */
 } bissd_grad_t;
 
 /*
@@ -267,7 +276,7 @@ const char *bissd_status_string(int status);
 /* The hipError_t of the last BISSD_ERR_HIP on the calling thread (0 if none). */
 int bissd_last_hip_error(void);
 
-/* ABI version: 1. */
+/* ABI version: 2 (1 had no dt post-processing fields). */
 int bissd_version(void);
 
 #ifdef __cplusplus

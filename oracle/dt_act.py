@@ -13,7 +13,10 @@ with softplus(z) = log(1 + e^z).  Its reverse mode for an incoming ddt:
     draw = ddt * sigmoid(z) * [lo <= softplus(z) <= hi],   dbias[h] = sum_{b,t} draw
 
 (the clamp passes the gradient where the value lies inside [lo, hi], ends
-included).  numpy float64; the scan itself stays in ssd_oracle.c.
+included).  numpy float64; the scan itself stays in ssd_oracle.c.  The
+inside-the-clamp decision is an integer taken from floating point, so it is
+taken in the kernels' precision: softplus in float32 of the float32 sum
+raw + bias.
 """
 from __future__ import annotations
 
@@ -32,8 +35,9 @@ def forward(raw, bias, lo: float, hi: float) -> np.ndarray:
 def backward(raw, bias, lo: float, hi: float, ddt):
     """(draw, dbias) for the gradient ddt with respect to the clamped dt."""
     z = np.asarray(raw, np.float64) + np.asarray(bias, np.float64)[None, None, :]
-    sp = softplus(z)
-    keep = (sp >= lo) & (sp <= hi)
+    z32 = (np.asarray(raw, np.float32) + np.asarray(bias, np.float32)[None, None, :]).astype(np.float32)
+    sp32 = np.maximum(z32, np.float32(0)) + np.log1p(np.exp(-np.abs(z32)))
+    keep = (sp32 >= np.float32(lo)) & (sp32 <= np.float32(hi))
     draw = np.asarray(ddt, np.float64) * (1.0 / (1.0 + np.exp(-z))) * keep
     return draw, draw.sum(axis=(0, 1))
 

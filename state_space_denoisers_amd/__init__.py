@@ -9,9 +9,11 @@ library's HIP kernels.  There is no CPU or PyTorch fallback.
     y, state_out = bissd_block_update(state_in, x_blk, fwd, rev, D)
     grads = bissd_backward(x, fwd, rev, D, dy)
 
-``fwd`` / ``rev`` are (dt, A, B, C) tuples: dt [Z,L,H], A [H] fp32,
-B and C [Z,L,G,N]; x [Z,L,H,P]; D [H] fp32.  x, dt, B, C (and dy) share one
-dtype, torch.float32 or torch.bfloat16.
+``fwd`` / ``rev`` are (dt, A, B, C) tuples or ``Dir``s: dt [Z,L,H], A [H]
+fp32, B and C [Z,L,G,N]; x [Z,L,H,P]; D [H] fp32.  x, dt, B, C (and dy) share
+one dtype, torch.float32 or torch.bfloat16.  A ``Dir`` with ``dt_bias`` ([H]
+fp32) makes the kernels read dt as clamp(softplus(dt + dt_bias), dt_min,
+dt_max).
 """
 from __future__ import annotations
 
@@ -34,6 +36,9 @@ class Dir(NamedTuple):
     A: torch.Tensor
     B: torch.Tensor
     C: torch.Tensor
+    dt_bias: Optional[torch.Tensor] = None
+    dt_min: float = 0.0
+    dt_max: float = float("inf")
 
 
 def library_path() -> str:
@@ -76,10 +81,13 @@ def _ptr(t: Optional[torch.Tensor]):
 
 
 def _dir(d) -> _abi.Dir:
-    dt, A, B, Cm = d
-    if A.dtype != torch.float32:
-        raise TypeError(f"A must be torch.float32, got {A.dtype}")
-    return _abi.Dir(_ptr(dt), _ptr(A), _ptr(B), _ptr(Cm))
+    d = Dir(*d)
+    if d.A.dtype != torch.float32:
+        raise TypeError(f"A must be torch.float32, got {d.A.dtype}")
+    if d.dt_bias is not None and d.dt_bias.dtype != torch.float32:
+        raise TypeError(f"dt_bias must be torch.float32, got {d.dt_bias.dtype}")
+    return _abi.Dir(_ptr(d.dt), _ptr(d.A), _ptr(d.B), _ptr(d.C), _ptr(d.dt_bias),
+                    float(d.dt_min), float(d.dt_max))
 
 
 def _stream(device: torch.device, stream) -> C.c_void_p:
@@ -169,9 +177,9 @@ def bissd_backward(x: torch.Tensor, fwd, rev, D: torch.Tensor, dy: torch.Tensor,
                    init_state: Optional[torch.Tensor] = None, grads: Optional[dict] = None,
                    workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
     """Gradients of sum(dy * y) (include/bissd.h, bissd_backward).  Returns a
-    dict with dx, ddt_f, dA_f, dB_f, dC_f, ddt_r, dA_r, dB_r, dC_r, dD (fp32);
-    ``grads`` may hold preallocated tensors under those keys.  ``rev_block``
-    as in bissd_forward."""
+    dict with dx, ddt_f, dA_f, dB_f, dC_f, ddt_r, dA_r, dB_r, dC_r, dD (fp32),
+    plus ddt_bias_<d> for a direction with a dt bias; ``grads`` may hold
+    preallocated tensors under those keys.  ``rev_block`` as in bissd_forward."""
     lib = _abi.load()
     fwd, rev = Dir(*fwd), Dir(*rev)
     shape = shape_of(x, fwd.B, chunk, rev_block)
@@ -185,11 +193,15 @@ def bissd_backward(x: torch.Tensor, fwd, rev, D: torch.Tensor, dy: torch.Tensor,
         for k, like in (("ddt", p.dt), ("dA", p.A), ("dB", p.B), ("dC", p.C)):
             if f"{k}_{d}" not in g:
                 g[f"{k}_{d}"] = torch.empty(like.shape, **f32)
+        if p.dt_bias is not None and f"ddt_bias_{d}" not in g:
+            g[f"ddt_bias_{d}"] = torch.empty(p.dt_bias.shape, **f32)
     for k in GRAD_KEYS:
         if g[k].dtype != torch.float32:
             raise TypeError(f"{k} must be float32")
-    gf = _abi.Grad(_ptr(g["ddt_f"]), _ptr(g["dA_f"]), _ptr(g["dB_f"]), _ptr(g["dC_f"]))
-    gr = _abi.Grad(_ptr(g["ddt_r"]), _ptr(g["dA_r"]), _ptr(g["dB_r"]), _ptr(g["dC_r"]))
+    gf = _abi.Grad(_ptr(g["ddt_f"]), _ptr(g["dA_f"]), _ptr(g["dB_f"]), _ptr(g["dC_f"]),
+                   _ptr(g.get("ddt_bias_f")))
+    gr = _abi.Grad(_ptr(g["ddt_r"]), _ptr(g["dA_r"]), _ptr(g["dB_r"]), _ptr(g["dC_r"]),
+                   _ptr(g.get("ddt_bias_r")))
     ws, nws = _workspace(shape, _abi.OP_BACKWARD, x.device, workspace)
     st = lib.bissd_backward(C.byref(shape), _ptr(x), _dir(fwd), _dir(rev), _ptr(D),
                             _ptr(init_state), _ptr(dy), _ptr(g["dx"]), gf, gr, _ptr(g["dD"]),

@@ -42,11 +42,13 @@ class AttnShape(C.Structure):
 
 
 class Dir(C.Structure):
-    _fields_ = [("dt", C.c_void_p), ("A", C.c_void_p), ("B", C.c_void_p), ("C", C.c_void_p)]
+    _fields_ = [("dt", C.c_void_p), ("A", C.c_void_p), ("B", C.c_void_p), ("C", C.c_void_p),
+                ("dt_bias", C.c_void_p), ("dt_min", C.c_float), ("dt_max", C.c_float)]
 
 
 class Grad(C.Structure):
-    _fields_ = [("ddt", C.c_void_p), ("dA", C.c_void_p), ("dB", C.c_void_p), ("dC", C.c_void_p)]
+    _fields_ = [("ddt", C.c_void_p), ("dA", C.c_void_p), ("dB", C.c_void_p), ("dC", C.c_void_p),
+                ("ddt_bias", C.c_void_p)]
 
 
 class BissdError(RuntimeError):

@@ -69,7 +69,7 @@ int check_shape(const bissd_shape_t *s, int op) {
 struct WsLayout {
   size_t states = 0, sin_t = 0, cdecay = 0, gram = 0;
   size_t tstates = 0, sa_t = 0, gin_t = 0, dtsum = 0, ydot = 0, qx = 0, qxs = 0, ddpart = 0, dAintra = 0,
-         dAx1 = 0, dAx2 = 0, rpart = 0, lamg = 0, cdtg = 0;
+         dAx1 = 0, dAx2 = 0, rpart = 0, lamg = 0, cdtg = 0, dbpart = 0;
   size_t total = 0;
 };
 
@@ -108,6 +108,7 @@ WsLayout ws_layout(const bissd_shape_t *s, int op) {
     w.rpart = take(cd * (size_t)(s->headdim * s->dstate / 256));
     w.lamg = take(tok);
     w.cdtg = take(tok);
+    w.dbpart = take(cd);
   }
   w.total = o;
   return w;
@@ -138,17 +139,20 @@ Sizes sizes(const bissd_shape_t *s) {
 
 int check_dir(const bissd_dir_t &d) {
   if (!d.dt || !d.A || !d.B || !d.C) return BISSD_ERR_NULL;
-  if (!aligned16(d.dt) || !aligned16(d.A) || !aligned16(d.B) || !aligned16(d.C))
+  if (!aligned16(d.dt) || !aligned16(d.A) || !aligned16(d.B) || !aligned16(d.C) ||
+      (d.dt_bias && !aligned16(d.dt_bias)))
     return BISSD_ERR_ALIGN;
+  // clamp range of the dt post-processing (NaN fails every comparison)
+  if (d.dt_bias && !(d.dt_min >= 0.0f && d.dt_max >= d.dt_min)) return BISSD_ERR_SHAPE;
   return BISSD_OK;
 }
 
 // true if `out` (n bytes) overlaps any input of the scan
 bool hits_inputs(const void *out, size_t n, const Sizes &z, const void *x, const bissd_dir_t &f,
                  const bissd_dir_t &r, const float *D) {
-  const void *bufs[] = {x, f.dt, f.A, f.B, f.C, r.dt, r.A, r.B, r.C, D};
-  const size_t lens[] = {z.x, z.dt, z.vec, z.bc, z.bc, z.dt, z.vec, z.bc, z.bc, z.vec};
-  for (int i = 0; i < 10; ++i)
+  const void *bufs[] = {x, f.dt, f.A, f.B, f.C, r.dt, r.A, r.B, r.C, D, f.dt_bias, r.dt_bias};
+  const size_t lens[] = {z.x, z.dt, z.vec, z.bc, z.bc, z.dt, z.vec, z.bc, z.bc, z.vec, z.vec, z.vec};
+  for (int i = 0; i < 12; ++i)
     if (overlap(out, n, bufs[i], lens[i])) return true;
   return false;
 }
@@ -171,6 +175,12 @@ ScanArgs base_args(const bissd_shape_t *s, const void *x, const bissd_dir_t &f,
   a.x = x;
   a.dt[0] = f.dt;
   a.dt[1] = r.dt;
+  const bissd_dir_t *dirs[2] = {&f, &r};
+  for (int d = 0; d < 2; ++d) {
+    a.dtb[d] = dirs[d]->dt_bias;
+    a.dtlo[d] = dirs[d]->dt_min;
+    a.dthi[d] = dirs[d]->dt_max;
+  }
   a.A[0] = f.A;
   a.A[1] = r.A;
   a.B[0] = f.B;
@@ -201,7 +211,7 @@ int finish(hipError_t e) {
 
 extern "C" {
 
-int bissd_version(void) { return 1; }
+int bissd_version(void) { return 2; }
 
 int bissd_last_hip_error(void) { return g_last_hip; }
 
@@ -370,21 +380,26 @@ int bissd_backward(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, bissd
   if (!gfwd.ddt || !gfwd.dA || !gfwd.dB || !gfwd.dC || !grev.ddt || !grev.dA || !grev.dB ||
       !grev.dC)
     return BISSD_ERR_NULL;
+  if ((fwd.dt_bias && !gfwd.ddt_bias) || (rev.dt_bias && !grev.ddt_bias)) return BISSD_ERR_NULL;
+  // the bias gradients take part only for directions with a dt bias
+  float *dbf = fwd.dt_bias ? gfwd.ddt_bias : nullptr, *dbr = rev.dt_bias ? grev.ddt_bias : nullptr;
   const void *outs[] = {dx, gfwd.ddt, gfwd.dA, gfwd.dB, gfwd.dC,
-                        grev.ddt, grev.dA, grev.dB, grev.dC, dD};
+                        grev.ddt, grev.dA, grev.dB, grev.dC, dD, dbf, dbr};
   if (!aligned16(x) || !aligned16(D) || !aligned16(dy) || (init_state && !aligned16(init_state)))
     return BISSD_ERR_ALIGN;
   for (const void *o : outs)
-    if (!aligned16(o)) return BISSD_ERR_ALIGN;
+    if (o && !aligned16(o)) return BISSD_ERR_ALIGN;
   const WsLayout wl = ws_layout(s, BISSD_OP_BACKWARD);
   if (!workspace || workspace_bytes < wl.total) return BISSD_ERR_WORKSPACE;
   if (!aligned16(workspace)) return BISSD_ERR_ALIGN;
   const Sizes z = sizes(s);
   const size_t tokh = (size_t)(s->batch * s->seqlen * s->nheads) * 4;
   const size_t bcn = (size_t)(s->batch * s->seqlen * s->ngroups * s->dstate) * 4;
-  const size_t olen[] = {z.x / esize(s) * 4, tokh, z.vec, bcn, bcn, tokh, z.vec, bcn, bcn, z.vec};
-  // outputs overlap neither an input, the workspace nor each other
-  for (int i = 0; i < 10; ++i) {
+  const size_t olen[] = {z.x / esize(s) * 4, tokh, z.vec, bcn, bcn, tokh, z.vec, bcn, bcn, z.vec,
+                         z.vec, z.vec};
+  // outputs overlap neither an input, the workspace nor each other (absent
+  // bias gradients overlap nothing)
+  for (int i = 0; i < 12; ++i) {
     if (hits_inputs(outs[i], olen[i], z, x, fwd, rev, D) || overlap(outs[i], olen[i], dy, z.x) ||
         overlap(outs[i], olen[i], init_state, z.state) ||
         overlap(outs[i], olen[i], workspace, wl.total))
@@ -478,6 +493,12 @@ int bissd_backward(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, bissd
   q.x = dy;
   q.aux = x;
   q.dt[0] = rev.dt;
+  q.dtb[0] = rev.dt_bias;
+  q.dtlo[0] = rev.dt_min;
+  q.dthi[0] = rev.dt_max;
+  q.dtb[1] = fwd.dt_bias;
+  q.dtlo[1] = fwd.dt_min;
+  q.dthi[1] = fwd.dt_max;
   q.A[0] = rev.A;
   q.B[0] = rev.C;
   q.C[0] = rev.B;
@@ -504,6 +525,14 @@ int bissd_backward(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, bissd
   b.dy = dy;
   b.dt[0] = fwd.dt;
   b.dt[1] = rev.dt;
+  for (int d = 0; d < 2; ++d) {
+    b.dtb[d] = a.dtb[d];
+    b.dtlo[d] = a.dtlo[d];
+    b.dthi[d] = a.dthi[d];
+  }
+  b.ddtb[0] = dbf;
+  b.ddtb[1] = dbr;
+  b.dbpart = (float *)(ws + wl.dbpart);
   b.A[0] = fwd.A;
   b.A[1] = rev.A;
   b.B[0] = fwd.B;

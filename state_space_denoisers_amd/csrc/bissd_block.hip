@@ -87,9 +87,17 @@ __global__ __launch_bounds__(kBlkThreads) void k_block_update(ScanArgs a) {
 #pragma unroll
   for (int ks = 0; ks < NK; ++ks)
     frag_bload(cf[ks], rC, (uint32_t)(trow * G + gidx) * N * ES + (32 * ks + 8 * g4) * ES);
-  if (w == 0)
+  if (w == 0) {
+    DtPost post;
+    if (a.dtb[grp]) {
+      post.on = true;
+      post.bias = a.dtb[grp][h];
+      post.lo = a.dtlo[grp];
+      post.hi = a.dthi[grp];
+    }
     chunk_decay_scan<T>(reinterpret_cast<const T *>(a.dt[grp]) + (int64_t)b * L * H + h, H, L, kRB,
-                        a.A[grp][h] * kLog2e, grp == 1, sm.lam[grp], sm.dtv[grp]);
+                        a.A[grp][h] * kLog2e, grp == 1, sm.lam[grp], sm.dtv[grp], false, post);
+  }
   wait_vmem();
   __syncthreads();
 

@@ -45,6 +45,19 @@
 
 namespace bissd {
 
+// dt post-processing of direction d, head h (off when the direction has no bias)
+__device__ __forceinline__ DtPost dt_post_of(const BwdArgs &a, int d, int h) {
+  DtPost p;
+  if (a.dtb[d]) {
+    p.on = true;
+    p.bias = a.dtb[d][h];
+    p.lo = a.dtlo[d];
+    p.hi = a.dthi[d];
+  }
+  return p;
+}
+
+
 // ============================================================ dB / dC panel
 
 template <typename T, int N> struct PanelLds {
@@ -170,16 +183,24 @@ void k_bwd_panel(BwdArgs a) {
     const bufres rl = make_buf(a.lamg + (cbase + h) * L, (uint32_t)(L * 4));
     const uint32_t off = (uint32_t)(t0 + tid) * 4u;
     raw[0] = __builtin_amdgcn_raw_buffer_load_b32(rl, off, 0, 0);
-    raw[1] = 0u;
+    raw[1] = a.dtb[d] ? __builtin_bit_cast(uint32_t, a.dtb[d][h]) : 0u;  // dt bias of head h
     const uint32_t doff = (uint32_t)((t0 + tid) * H + h) * ES;
     if constexpr (sizeof(T) == 2) raw[2] = __builtin_amdgcn_raw_buffer_load_b16(rDt, doff, 0, 0);
     else raw[2] = __builtin_amdgcn_raw_buffer_load_b32(rDt, doff, 0, 0);
     raw[3] = __builtin_amdgcn_raw_buffer_load_b32(rl, (uint32_t)(t0 + (mok ? mtok : 0)) * 4u, 0, 0);
   };
+  DtPost post;
+  post.on = a.dtb[d] != nullptr;
+  post.lo = a.dtlo[d];
+  post.hi = a.dthi[d];
   auto tok_put = [&](const uint32_t (&raw)[4], int buf) __attribute__((always_inline)) {
     if (tid < Q) {
       const float l = __builtin_bit_cast(float, raw[0]);
-      const float dtv = __builtin_bit_cast(float, sizeof(T) == 2 ? raw[2] << 16 : raw[2]);
+      DtPost ph = post;
+      ph.bias = __builtin_bit_cast(float, raw[1]);
+      const float draw = __builtin_bit_cast(float, sizeof(T) == 2 ? raw[2] << 16 : raw[2]);
+      // tokens past L keep dt = 0
+      const float dtv = t0 + tid < L ? dt_post(draw, ph) : 0.0f;
       const float m = mok ? __builtin_bit_cast(float, raw[3]) : 0.0f;
       sm.lam[buf][tid] = l;
       sm.dtv[buf][tid] = dtv;
@@ -365,18 +386,22 @@ __global__ __launch_bounds__(kThreads) void k_bwd_decay(BwdArgs a) {
   const float *qxs = a.qxs + ((int64_t)d * a.Z + b) * L * H + h;
   float *ddt = a.ddt[d] + (int64_t)b * L * H + h;
   const float A = a.A[d][h];
+  const DtPost post = dt_post_of(a, d, h);
   const float *rp = a.rpart + ((((int64_t)d * a.Z + b) * nc + c) * H + h) * nwv;
   float R = 0.0f;
   for (int k = 0; k < nwv; ++k) R += rp[k];
   const int64_t base = (int64_t)c * Q + lane * K;
-  float v[4], ql[4];
+  float v[4], ql[4], gr[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t t = base + i;
     const bool ok = i < K && t < L;
     ql[i] = ok ? qx[t * H] : 0.0f;
+    const float draw = ok ? to_f(dt[t * H]) : 0.0f;
+    // d dt / d raw of a post-processed dt (1 without), for the chain rule below
+    gr[i] = ok ? dt_post_grad(draw, post) : 0.0f;
     // dy.y_d and x.(G_t B_t) both without their common t' = t term
-    v[i] = ok ? yd[t * H] - to_f(dt[t * H]) * qxs[t * H] : 0.0f;
+    v[i] = ok ? yd[t * H] - dt_post(draw, post) * qxs[t * H] : 0.0f;
   }
   float run = 0.0f, acc[4];
   if (d == 0) {
@@ -402,10 +427,22 @@ __global__ __launch_bounds__(kThreads) void k_bwd_decay(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] += excl + R;
   }
+  // with dt post-processing, ddt is taken back to the pre-activation and the
+  // chunk's sum of it feeds the bias gradient
+  float bsum = 0.0f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t t = base + i;
-    if (i < K && t < L) ddt[t * H] = ql[i] + A * acc[i];
+    const float g = (ql[i] + A * acc[i]) * gr[i];
+    if (i < K && t < L) {
+      ddt[t * H] = g;
+      bsum += g;
+    }
+  }
+  if (post.on) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) bsum += __shfl_xor(bsum, o, 64);
+    if (lane == 0) a.dbpart[(((int64_t)d * a.Z + b) * nc + c) * H + h] = bsum;
   }
 }
 
@@ -416,7 +453,23 @@ __global__ __launch_bounds__(kThreads) void k_bwd_decay(BwdArgs a) {
 __global__ __launch_bounds__(kThreads) void k_bwd_reduce(BwdArgs a) {
   __shared__ float red[kThreads];
   const int tid = threadIdx.x, H = a.H, NRB = a.chunk / kRB;
-  const int o = blockIdx.x;  // 0 .. 2H-1: dA, 2H .. 3H-1: dD
+  // 0 .. 2H-1: dA, 2H .. 3H-1: dD, 3H .. 5H-1: dt bias gradients
+  const int o = blockIdx.x;
+  if (o >= 3 * H) {
+    const int db = (o - 3 * H) / H, hb = (o - 3 * H) % H;
+    if (!a.ddtb[db]) return;
+    const int64_t nbc = (int64_t)a.Z * a.nchunks;
+    float sb = 0.0f;
+    for (int64_t i = tid; i < nbc; i += kThreads) sb += a.dbpart[((int64_t)db * nbc + i) * H + hb];
+    red[tid] = sb;
+    __syncthreads();
+    for (int k = kThreads / 2; k > 0; k >>= 1) {
+      if (tid < k) red[tid] += red[tid + k];
+      __syncthreads();
+    }
+    if (tid == 0) a.ddtb[db][hb] = red[0];
+    return;
+  }
   const int d = o < 2 * H ? o / H : 0, h = o < 2 * H ? o % H : o - 2 * H;
   float s = 0.0f;
   if (o < 2 * H) {
@@ -472,7 +525,7 @@ hipError_t launch_bwd_decay(const BwdArgs &a, hipStream_t st) {
   dim3 g((unsigned)((items + 3) / 4));
   if (a.dtype == 1) hipLaunchKernelGGL(k_bwd_decay<bf16>, g, dim3(kThreads), 0, st, a);
   else hipLaunchKernelGGL(k_bwd_decay<float>, g, dim3(kThreads), 0, st, a);
-  hipLaunchKernelGGL(k_bwd_reduce, dim3((unsigned)(3 * a.H)), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL(k_bwd_reduce, dim3((unsigned)(5 * a.H)), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

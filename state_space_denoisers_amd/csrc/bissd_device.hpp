@@ -641,19 +641,38 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Mamba-2's dt post-processing, applied wherever a kernel reads dt when the
+// direction carries a per-head bias: dt = clamp(softplus(raw + bias), lo, hi).
+// softplus(z) = max(z, 0) + log1p(e^-|z|) stays accurate for either sign.
+struct DtPost {
+  float bias = 0.0f, lo = 0.0f, hi = 0.0f;
+  bool on = false;
+};
+__device__ __forceinline__ float softplus_f(float z) { return fmaxf(z, 0.0f) + log1pf(expf(-fabsf(z))); }
+__device__ __forceinline__ float dt_post(float raw, const DtPost &p) {
+  return p.on ? fminf(fmaxf(softplus_f(raw + p.bias), p.lo), p.hi) : raw;
+}
+// d dt / d raw: sigmoid(raw + bias) where the softplus lies inside the clamp
+// range (ends included), else 0; 1 without post-processing
+__device__ __forceinline__ float dt_post_grad(float raw, const DtPost &p) {
+  if (!p.on) return 1.0f;
+  const float z = raw + p.bias, sp = softplus_f(z);
+  return (sp >= p.lo && sp <= p.hi) ? 1.0f / (1.0f + expf(-z)) : 0.0f;
+}
+
 // dt of one chunk for one head, in the lane order chunk_decay_scan_vals
 // expects: lane l holds tokens l K .. l K + K - 1 (K = Q / 64) in d[0..K-1];
 // tokens at or beyond qlen read as 0.  Split from the scan so the loads can
 // be issued well before the values are needed.
 template <typename T>
 __device__ __forceinline__ void chunk_dt_load(const T *dt, int64_t stride, int qlen, int Q,
-                                              float (&d)[4]) {
+                                              float (&d)[4], const DtPost &post = DtPost{}) {
   const int lane = threadIdx.x & 63;
   const int K = Q / 64;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int s = lane * K + i;
-    d[i] = (i < K && s < qlen) ? to_f(dt[(int64_t)s * stride]) : 0.0f;
+    d[i] = (i < K && s < qlen) ? dt_post(to_f(dt[(int64_t)s * stride]), post) : 0.0f;
   }
 }
 
@@ -675,13 +694,16 @@ __device__ __forceinline__ void chunk_dt_bload(bufres r, uint32_t off0, uint32_t
     else raw[i] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
   }
 }
+// (tokens at or beyond qlen give 0, also after post-processing)
 template <typename T>
-__device__ __forceinline__ void chunk_dt_decode(const uint32_t (&raw)[4], int Q, float (&d)[4]) {
+__device__ __forceinline__ void chunk_dt_decode(const uint32_t (&raw)[4], int Q, float (&d)[4],
+                                                const DtPost &post, int qlen) {
+  const int lane = threadIdx.x & 63;
   const int K = Q / 64;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float f = __builtin_bit_cast(float, sizeof(T) == 2 ? raw[i] << 16 : raw[i]);
-    d[i] = i < K ? f : 0.0f;
+    d[i] = (i < K && lane * K + i < qlen) ? dt_post(f, post) : 0.0f;
   }
 }
 
@@ -748,9 +770,10 @@ __device__ __forceinline__ float chunk_decay_scan_vals(const float (&d)[4], int 
 template <typename T>
 __device__ __forceinline__ float chunk_decay_scan(const T *dt, int64_t stride, int qlen, int Q,
                                                   float A2, bool reverse, float *lam,
-                                                  float *dtv, bool exclusive = false) {
+                                                  float *dtv, bool exclusive = false,
+                                                  const DtPost &post = DtPost{}) {
   float d[4];
-  chunk_dt_load(dt, stride, qlen, Q, d);
+  chunk_dt_load(dt, stride, qlen, Q, d, post);
   return chunk_decay_scan_vals(d, Q, A2, reverse, lam, dtv, exclusive);
 }
 

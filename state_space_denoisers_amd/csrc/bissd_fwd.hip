@@ -30,6 +30,19 @@
 
 namespace bissd {
 
+// dt post-processing of direction d, head h (off when the direction has no bias)
+__device__ __forceinline__ DtPost dt_post_of(const ScanArgs &a, int d, int h) {
+  DtPost p;
+  if (a.dtb[d]) {
+    p.on = true;
+    p.bias = a.dtb[d][h];
+    p.lo = a.dtlo[d];
+    p.hi = a.dthi[d];
+  }
+  return p;
+}
+
+
 // Gram tile pairs: for slot d, the (row-block j, column-block kb) pairs of
 // one chunk that the output kernel reads (kb <= j for d = 0, kb >= j for
 // d = 1), numbered row-block by row-block.
@@ -180,10 +193,12 @@ void k1_chunk_state(ScanArgs a) {
   }
   uint32_t dtraw[4];
   float Ah = 1.0f;
+  DtPost post;
   if (w < NPR) {
     chunk_dt_bload<T>(make_buf(dt + (int64_t)b * L * H, (uint32_t)(L * H * ES)),
                       (uint32_t)(t0 * H + h0 + w % HT) * ES, (uint32_t)(H * ES), Q, dtraw);
     if (w < HT) Ah = a.A[d][h0 + w];
+    post = dt_post_of(a, d, h0 + w % HT);
   }
 
   u32x4 pfB[SB::NV], pfX[HT][SX::NV];
@@ -197,7 +212,7 @@ void k1_chunk_state(ScanArgs a) {
     for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(dtraw[i]) : : "memory");
     asm volatile("" : "+v"(Ah) : : "memory");
     float dv[4];
-    chunk_dt_decode<T>(dtraw, Q, dv);
+    chunk_dt_decode<T>(dtraw, Q, dv, post, qlen);
     if (w < HT)
       chunk_decay_scan_vals(dv, Q, Ah * kLog2e, d == 1, sm.lam[hh], sm.dtv[hh]);
     else
@@ -790,10 +805,12 @@ void k3_chunk_out(ScanArgs a) {
   const int pd = w / HT, ph = w % HT;
   uint32_t dtraw[4], cdraw[kQmax / kRB];
   float Ah = 0.0f;
+  DtPost post;
   if (w < 2 * HT) {
     chunk_dt_bload<T>(make_buf(reinterpret_cast<const T *>(a.dt[pd]) + (int64_t)b * L * H, (uint32_t)(L * H * ES)),
                       (uint32_t)(t0 * H + h0 + ph) * ES, (uint32_t)(H * ES), Q, dtraw);
     Ah = a.A[pd][h0 + ph];
+    post = dt_post_of(a, pd, h0 + ph);
     if constexpr (DAI) {
       // token m 64 + lane of the chunk; past L reads as zero
       const bufres rc = make_buf(a.cdt_in + (((int64_t)pd * a.Z + b) * H + h0 + ph) * L, (uint32_t)(L * 4));
@@ -817,7 +834,7 @@ void k3_chunk_out(ScanArgs a) {
       }
     }
     float dv[4];
-    chunk_dt_decode<T>(dtraw, Q, dv);
+    chunk_dt_decode<T>(dtraw, Q, dv, post, qlen);
     const float am = chunk_decay_scan_vals(dv, Q, Ah * kLog2e, pd == 1, sm.lam[pd][ph],
                                            sm.scale[pd][ph], MODE == 2);
     // The same wave (its LDS accesses complete in order) then forms this

@@ -35,6 +35,10 @@ struct FastDiv {
 struct ScanArgs {
   const void *x;
   const void *dt[2];  // [0] forward, [1] reverse
+  // per-direction dt post-processing: with dtb[d] set, every read of dt[d]
+  // becomes clamp(softplus(dt + dtb[d][h]), dtlo[d], dthi[d])
+  const float *dtb[2];
+  float dtlo[2], dthi[2];
   const float *A[2];
   const void *B[2];
   const void *C[2];
@@ -125,6 +129,10 @@ hipError_t launch_block_update(const ScanArgs &a, hipStream_t st);
 struct BwdArgs {
   const void *x, *dy;
   const void *dt[2];
+  const float *dtb[2];  // as in ScanArgs
+  float dtlo[2], dthi[2];
+  float *ddtb[2];       // with dtb[d]: gradient of the bias, [H]
+  float *dbpart;        // [2][Z][nchunks][H] per-chunk sums of the pre-activation ddt
   const float *A[2];
   const void *B[2], *C[2];
   const void *sin[2];  // forward carry-in states per direction, compute dtype

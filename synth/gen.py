@@ -33,6 +33,7 @@ _KEYS = {
     "dt_r": 6, "A_r": 7, "B_r": 8, "C_r": 9, "dy": 10,
     "mask_pos": 11, "mask_vec": 12, "prefix": 13,
     "attn_q": 14, "attn_k": 15, "attn_v": 16,
+    "dtraw_f": 17, "dtraw_r": 18, "dtbias_f": 19, "dtbias_r": 20,
 }
 
 
@@ -226,3 +227,19 @@ def make_attention_inputs(Z: int, L: int, H: int, dtype: str, seed: int, D: int 
     scale of normalised activations), rounded once to ``dtype``."""
     return {n: quantize(_rng(seed, "attn_" + n).standard_normal((Z, L, H, D)), dtype)
             for n in ("q", "k", "v")}
+
+
+def with_dt_post(inp: dict, w: Workload, lo: float = 1e-3, hi: float = 0.1) -> dict:
+    """The same inputs with each direction's dt given as the mixer's
+    pre-activation for the library's dt post-processing: raw ~ N(0, 1)
+    (rounded to the workload dtype), per-head bias ~ -shift + 0.5 N(0, 1)
+    (fp32) and the clamp [lo, hi] -- the synthetic dt recipe with the
+    softplus, shift and clamp moved into the scan."""
+    out = dict(inp)
+    Z, L, H = inp["dt_f"].shape
+    for d in ("f", "r"):
+        out[f"dt_{d}"] = quantize(_rng(w.seed, f"dtraw_{d}").standard_normal((Z, L, H)), w.dtype)
+        out[f"dt_bias_{d}"] = round_fp32(-w.dt_shift + 0.5 * _rng(w.seed, f"dtbias_{d}").standard_normal(H))
+        out[f"dt_min_{d}"], out[f"dt_max_{d}"] = lo, hi
+    return out
+

@@ -35,7 +35,7 @@ def test_header_and_binding_agree():
 def test_every_declared_symbol_is_exported(lib):
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert lib.bissd_version() == 1
+    assert lib.bissd_version() == 2
     assert lib.bissd_last_hip_error() == 0
 
 
@@ -263,4 +263,16 @@ def test_attention_backward_validation(lib):
     assert bwd(dq=C.c_void_p(A * 7 + 8)) == -4
     assert bwd(dk=addr(6)) == -7      # dk over dq
     assert bwd(ws=addr(0)) == -7      # workspace over q
+
+
+def test_dt_post_processing_validation(lib):
+    s = shape()
+    bad = _abi.Dir(addr(1), addr(2), addr(3), addr(4), addr(20), 0.2, 0.1)   # dt_min > dt_max
+    assert call_forward(lib, s, fwd=bad) == -2
+    bad = _abi.Dir(addr(1), addr(2), addr(3), addr(4), addr(20), -1.0, 0.1)  # dt_min < 0
+    assert call_forward(lib, s, fwd=bad) == -2
+    bad = _abi.Dir(addr(1), addr(2), addr(3), addr(4), C.c_void_p(A * 21 + 4), 0.0, 1.0)
+    assert call_forward(lib, s, rev=bad) == -4
+    ok = _abi.Dir(addr(1), addr(2), addr(3), addr(4), addr(20), 0.0, float("inf"))
+    assert call_forward(lib, s, fwd=ok, nws=16) == -5   # passes validation up to the workspace
 
