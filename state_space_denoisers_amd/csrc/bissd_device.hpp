@@ -672,7 +672,12 @@ __device__ __forceinline__ void chunk_dt_load(const T *dt, int64_t stride, int q
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int s = lane * K + i;
-    d[i] = (i < K && s < qlen) ? dt_post(to_f(dt[(int64_t)s * stride]), post) : 0.0f;
+    d[i] = (i < K && s < qlen) ? to_f(dt[(int64_t)s * stride]) : 0.0f;
+  }
+  if (post.on) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (i < K && lane * K + i < qlen) d[i] = dt_post(d[i], post);
   }
 }
 
@@ -698,12 +703,17 @@ __device__ __forceinline__ void chunk_dt_bload(bufres r, uint32_t off0, uint32_t
 template <typename T>
 __device__ __forceinline__ void chunk_dt_decode(const uint32_t (&raw)[4], int Q, float (&d)[4],
                                                 const DtPost &post, int qlen) {
-  const int lane = threadIdx.x & 63;
   const int K = Q / 64;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float f = __builtin_bit_cast(float, sizeof(T) == 2 ? raw[i] << 16 : raw[i]);
-    d[i] = (i < K && lane * K + i < qlen) ? dt_post(f, post) : 0.0f;
+    d[i] = i < K ? f : 0.0f;  // tokens past the sequence end read as 0
+  }
+  if (post.on) {  // uniform: the post-processing costs nothing when off
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      d[i] = (i < K && lane * K + i < qlen) ? dt_post(d[i], post) : 0.0f;
   }
 }
 
