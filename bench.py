@@ -226,9 +226,17 @@ def cpu_baseline(w, budget_s=12.0):
         el = time.perf_counter() - t0
         if el >= budget_s or el * (reps + 1) / reps > 30.0:
             break
+    # one thread on one batch row of the same workload
+    w1 = w.replace(Z=1)
+    inp1 = gen.make_inputs(w1)
+    t1 = time.perf_counter()
+    O.forward(inp1, nthreads=1)
+    el1 = time.perf_counter() - t1
     return {"value": reps * w.tokens / el, "unit": "tokens/s", "cores": n, "kind": "oracle",
             "sample": f"{reps} x the full {w.name} batch ({w.Z}x{w.L} tokens, 24 heads, both "
-                      f"directions, fp64 sequential recurrence), {el:.1f} s wall"}
+                      f"directions, fp64 sequential recurrence), {el:.1f} s wall",
+            "value_1_thread": w1.tokens / el1,
+            "sample_1_thread": f"one {w1.L}-token row of the same workload on 1 thread, {el1:.2f} s"}
 
 
 # ------------------------------------------------------------ extra cases
@@ -278,6 +286,11 @@ def bench_block(reps):
                                state_out=s_out if commit else None, commit=commit, workspace=ws)
 
     out = {"workload": w.name, "prefix_tokens": w.prefix_len, "block_tokens": w.L, "batch": w.Z}
+    # algorithmic bytes of one update: cached state read, x / y, dt and B / C
+    # of both directions (and the state written back with commit)
+    e = 2 if w.dtype == "bf16" else 4
+    st_b = w.Z * w.H * w.P * w.N * 4
+    blk_b = w.Z * w.L * (2 * w.H * w.P * e + 2 * w.H * e + 4 * w.G * w.N * e)
     per_graph = 50
     for commit in (False, True):
         for _ in range(5):
@@ -301,6 +314,9 @@ def bench_block(reps):
         g.replay()
         torch.cuda.synchronize()
         out[f"us_per_update_{key}_graph"] = 1e3 * event_time_ms(g.replay, max(5, reps // per_graph)) / per_graph
+        nbytes = st_b * (2 if commit else 1) + blk_b
+        out[f"algorithmic_bytes_{key}"] = nbytes
+        out[f"effective_GBs_{key}_graph"] = nbytes / (out[f"us_per_update_{key}_graph"] * 1e-6) / 1e9
         del g
     return out
 
@@ -423,6 +439,46 @@ def bench_attention_backward(reps, Z=8, L=1024, H=12, block=0):
             "batch": Z, "seq_len": L, "heads": H, "headdim": 64, "block": block,
             "us_per_call": ms * 1e3, "achieved_TFLOPs": fl / (ms * 1e-3) / 1e12,
             "frac_bf16_peak": fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+
+
+def bench_latency_sweep(lengths=(1024, 4096, 16384, 65536, 262144)):
+    """Forward latency of one sequence (Z = 1, the layer shape) against its
+    length, and the least-squares fit t(L) = a L^2 + b L + c the pages use to
+    split latency into quadratic, linear and constant terms.  Inputs drawn on
+    the device (same distributions), directions weight-tied."""
+    import numpy as np
+    import torch
+    import state_space_denoisers_amd as ssd
+    from state_space_denoisers_amd import _abi
+    from synth import gen
+    dev = torch.device("cuda", 0)
+    base = gen.WORKLOADS["layer130m_L1k"].replace(Z=1)
+    small = gen.make_inputs(base.replace(L=64))
+    A = gen.as_torch(small["A_f"], "fp32", dev)
+    D = gen.as_torch(small["D"], "fp32", dev)
+    pts = []
+    for L in lengths:
+        T = gen.prefix_on_device(base, L, dev, seed=base.seed + L)
+        p = (T["dt_f"], A, T["B_f"], T["C_f"])
+        y = torch.empty_like(T["x"])
+        shape = ssd.shape_of(T["x"], T["B_f"], base.chunk)
+        ws = torch.empty(ssd.bissd_workspace_size(shape, _abi.OP_FORWARD), dtype=torch.uint8, device=dev)
+        fn = lambda: ssd.bissd_forward(T["x"], p, p, D, chunk=base.chunk, y=y, workspace=ws)
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        reps = max(5, min(200, int(2e6 // L)))
+        pts.append((L, event_time_ms(fn, reps)))
+        del T, y, ws
+    Ls = np.array([q[0] for q in pts], dtype=np.float64)
+    ts = np.array([q[1] for q in pts], dtype=np.float64)
+    coef, *_ = np.linalg.lstsq(np.stack([Ls ** 2, Ls, np.ones_like(Ls)], 1), ts, rcond=None)
+    return {"workload": "latency_sweep", "batch": 1, "heads": base.H, "dstate": base.N,
+            "points": [{"seq_len": int(L), "ms": round(t, 4), "tokens_per_s": L / (t * 1e-3)}
+                       for L, t in pts],
+            "fit_ms": {"a_per_L2": coef[0], "b_per_L": coef[1], "c": coef[2]},
+            "share_at_max_L": {"quadratic": coef[0] * Ls[-1] ** 2 / ts[-1],
+                               "linear": coef[1] * Ls[-1] / ts[-1], "constant": coef[2] / ts[-1]}}
 
 
 def bench_generation(steps_per_block=8, blocks=2, prefix=65536):
@@ -672,6 +728,11 @@ def main():
             log(f"bench: attention_bwd_L4k {extra['attention_bwd_L4k']}")
         except Exception as exc:
             extra["attention_bwd_L4k"] = {"error": repr(exc)}
+        try:
+            extra["latency_sweep"] = bench_latency_sweep()
+            log(f"bench: latency sweep {extra['latency_sweep']}")
+        except Exception as exc:
+            extra["latency_sweep"] = {"error": repr(exc)}
         try:
             extra["generation_L64k"] = bench_generation()
             log(f"bench: generation {extra['generation_L64k']}")
