@@ -17,7 +17,8 @@
 // is used).  Per tile, each wave forms its 32 queries' scores as S^T = K Q^T
 // on the matrix cores, so that a lane holds one query's scores for 16 keys
 // in exactly the layout of the A operand of the following P V product; the
-// row maximum and sum take two lane exchanges.  Every exponential is one
+// row maximum takes two lane exchanges; the row sums come from the matrix
+// cores (P times a column of ones).  Every exponential is one
 // exp2 of fma(s, c, -m c) with c = scale * log2(e).  The running maximum m
 // of a query only moves when a tile's maximum exceeds it by more than
 // kAttnSlack / c (then the output rows are rescaled by exp2((m_old - m_new) c)),
@@ -98,15 +99,28 @@ void k_attn_fwd(AttnArgs a) {
   }
   issue(0, 0);
 
-  f32x4 o[2][4];
+  // o[j][v]: output rows 4 g4 + i of group j, columns 16 v + r16; osum[j]:
+  // the same rows' probability sums, formed on the matrix cores as P times a
+  // column of ones (so they sit in the output rows' layout and are rescaled
+  // with them)
+  f32x4 o[2][4], osum[2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < 2; ++j) {
+    zero4(osum[j]);
 #pragma unroll
     for (int v = 0; v < 4; ++v) zero4(o[j][v]);
+  }
+  Frag<T> ones;
+  {
+    float one8[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) one8[e] = 1.0f;
+    frag_from(ones, one8);
+  }
   const float c = a.scale_log2;
   const float slack = kAttnSlack / c;
-  // running reference (raw score units) and sum of query r16 of each group
-  float mrow[2] = {-INFINITY, -INFINITY}, lrow[2] = {0.0f, 0.0f};
+  // running reference of query r16 of each group (raw score units)
+  float mrow[2] = {-INFINITY, -INFINITY};
 
   for (int kt = 0; kt < nkt; ++kt) {
     const int cur = kt & 1;
@@ -153,18 +167,10 @@ void k_attn_fwd(AttnArgs a) {
       const float mnew = move[j] ? tmax : mrow[j];
       alpha[j] = move[j] ? exp2_fast((mrow[j] - mnew) * c) : 1.0f;
       const float nm = -mnew * c;
-      float tsum = 0.0f;
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = exp2_fast(fmaf(s[j][u][i], c, nm));
-          s[j][u][i] = p;
-          tsum += p;
-        }
-      tsum += __shfl_xor(tsum, 16, 64);
-      tsum += __shfl_xor(tsum, 32, 64);
-      lrow[j] = lrow[j] * alpha[j] + tsum;
+        for (int i = 0; i < 4; ++i) s[j][u][i] = exp2_fast(fmaf(s[j][u][i], c, nm));
       mrow[j] = mnew;
     }
     // output rows 4 g4 + i belong to query 4 g4 + i, whose factor lane
@@ -175,6 +181,7 @@ void k_attn_fwd(AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float ai = __shfl(alpha[j], 4 * g4 + i, 64);
+          osum[j][i] *= ai;
 #pragma unroll
           for (int v = 0; v < 4; ++v) o[j][v][i] *= ai;
         }
@@ -201,28 +208,25 @@ void k_attn_fwd(AttnArgs a) {
         mma(o[0][v], pf[0], vf);
         mma(o[1][v], pf[1], vf);
       }
+      mma(osum[0], pf[0], ones);
+      mma(osum[1], pf[1], ones);
     }
   }
 
-  // log2-sum-exp of each query's scaled scores (the backward pass rebuilds
-  // P = exp2(c s - lse) from it), one lane per query
-  if (a.lse && g4 == 0) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t t = q0 + 32 * w + 16 * j + r16;
-      if (t < L) a.lse[((int64_t)b * H + h) * L + t] = mrow[j] * c + __builtin_amdgcn_logf(lrow[j]);
-    }
-  }
   // normalise and store rows q0 + 32 w + 16 j + 4 g4 + i (16 lanes write one
-  // contiguous row segment)
+  // contiguous row segment); the lanes of column 0 also write each row's
+  // log2-sum-exp of its scaled scores, from which the backward pass rebuilds
+  // P = exp2(c s - lse)
   T *og = reinterpret_cast<T *>(a.o) + boff;
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float inv = 1.0f / __shfl(lrow[j], 4 * g4 + i, 64);
+      const float inv = 1.0f / osum[j][i];
+      const float mi = __shfl(mrow[j], 4 * g4 + i, 64);
       const int64_t t = q0 + 32 * w + 16 * j + 4 * g4 + i;
       if (t >= L) continue;
+      if (a.lse && r16 == 0) a.lse[((int64_t)b * H + h) * L + t] = mi * c + __builtin_amdgcn_logf(osum[j][i]);
 #pragma unroll
       for (int v = 0; v < 4; ++v) og[(t * H + h) * kAttnD + 16 * v + r16] = from_f<T>(o[j][v][i] * inv);
     }
