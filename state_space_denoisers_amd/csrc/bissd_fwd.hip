@@ -501,6 +501,96 @@ __global__ __launch_bounds__(kThreads) void k2_state_pass(ScanArgs a, int PN, in
     *reinterpret_cast<f32x4 *>(a.final_state + ((int64_t)b * H + h) * PN + e) = S;
 }
 
+// The primal carry pass in bf16 with eight state elements per thread, so
+// every load and store moves 16 bytes; otherwise as k2_state_pass without
+// the adjoint (flip) mode.
+__device__ __forceinline__ void widen8(u32x4 r, f32x4 &lo, f32x4 &hi) {
+  asm volatile("" : "+v"(r));
+  lo = f32x4{__builtin_bit_cast(float, r[0] << 16), __builtin_bit_cast(float, r[0] & 0xffff0000u),
+             __builtin_bit_cast(float, r[1] << 16), __builtin_bit_cast(float, r[1] & 0xffff0000u)};
+  hi = f32x4{__builtin_bit_cast(float, r[2] << 16), __builtin_bit_cast(float, r[2] & 0xffff0000u),
+             __builtin_bit_cast(float, r[3] << 16), __builtin_bit_cast(float, r[3] & 0xffff0000u)};
+}
+__global__ __launch_bounds__(kThreads) void k2_state_pass8(ScanArgs a, int PN) {
+  const int e = (blockIdx.x * kThreads + threadIdx.x) * 8;  // PN is a multiple of 2048
+  const int h = blockIdx.y;
+  const int d = a.dir0 + (int)(blockIdx.z % a.ndir);
+  const int b = (int)(blockIdx.z / a.ndir);
+  const int nc = a.nchunks, H = a.H;
+  const int64_t cs = (int64_t)H * PN;
+  const int64_t base = (((int64_t)d * a.Z + b) * nc * H + h) * (int64_t)PN + e;
+  const bf16 *src = reinterpret_cast<const bf16 *>(a.states) + base;
+  bf16 *dst = a.sin_t ? reinterpret_cast<bf16 *>(a.sin_t) + base : nullptr;
+  const float *dec = a.cdecay + ((int64_t)d * a.Z + b) * nc * H + h;
+  f32x4 S0 = {0.0f, 0.0f, 0.0f, 0.0f}, S1 = S0;
+  const bool primal_fwd = d == 0;
+  if (primal_fwd && a.init_state) {
+    const float *in = a.init_state + ((int64_t)b * H + h) * PN + e;
+    S0 = *reinterpret_cast<const f32x4 *>(in);
+    S1 = *reinterpret_cast<const f32x4 *>(in + 4);
+  }
+  const bool up = d == 0;
+  const int step = up ? 1 : -1;
+  const int c0 = up ? 0 : nc - 1;
+  // block-segmented reverse: boundary index of the incoming carry, stepped
+  const int rsc = d == 1 ? a.rseg_chunks : 0;
+  int bmod = rsc ? (c0 + 1) % rsc : 1;
+  // forward calls skip the first chunk's zero carry-in and the last chunk's
+  // state when it feeds no final_state
+  const bool write_first = !a.skip_edges || (primal_fwd && a.init_state);
+  const int nload = (a.skip_edges && !(primal_fwd && a.final_state)) ? nc - 1 : nc;
+  constexpr int D = 8;
+  u32x4 rl[D];
+  float rg[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) rl[i] = u32x4{0u, 0u, 0u, 0u};
+  auto fetch = [&](int slot, int cc) __attribute__((always_inline)) {
+    rl[slot] = *reinterpret_cast<const u32x4 *>(src + cc * cs);
+    rg[slot] = dec[(int64_t)cc * H];
+  };
+#pragma unroll
+  for (int i = 0; i < D; ++i)
+    if (i < nload) fetch(i, c0 + i * step);
+  for (int n = 0; n < nc; n += D) {
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      const int nn = n + i;
+      if (nn >= nc) break;
+      const int c = c0 + nn * step;
+      f32x4 l0, l1;
+      widen8(rl[i], l0, l1);
+      const float g = exp2_fast(rg[i]);
+      if (nn + D < nload) fetch(i, c + D * step);
+      const bool cut = rsc != 0 && bmod == 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        S0[k] = cut ? 0.0f : S0[k];
+        S1[k] = cut ? 0.0f : S1[k];
+      }
+      bmod = bmod == 0 ? rsc - 1 : bmod - 1;
+      if (dst && (nn > 0 || write_first)) {
+        bf16x8 o;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          o[k] = (bf16)S0[k];
+          o[4 + k] = (bf16)S1[k];
+        }
+        *reinterpret_cast<bf16x8 *>(dst + c * cs) = o;
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        S0[k] = g * S0[k] + l0[k];
+        S1[k] = g * S1[k] + l1[k];
+      }
+    }
+  }
+  if (primal_fwd && a.final_state) {
+    float *out = a.final_state + ((int64_t)b * H + h) * PN + e;
+    *reinterpret_cast<f32x4 *>(out) = S0;
+    *reinterpret_cast<f32x4 *>(out + 4) = S1;
+  }
+}
+
 // A-tangent of the carry-in states, four elements per thread:
 // SA_in(c+1) = 2^cdecay(c) (SA_in(c) + Tsum(c) S_in(c)) + ST_loc(c), from zero,
 // alongside the primal carry S_in (from init_state or zero), in each
@@ -1331,6 +1421,10 @@ static void launch_t(const ScanArgs &a, int phase, hipStream_t st) {
     const int PN = kP * N;
     dim3 g2((unsigned)(PN / 4 / kThreads), (unsigned)a.H, (unsigned)(a.Z * 2));
     hipLaunchKernelGGL(k2_tangent_pass<T>, g2, dim3(kThreads), 0, st, a, PN);
+  } else if (phase == PHASE_STATE_PASS && sizeof(T) == 2) {
+    const int PN = kP * N;
+    dim3 g2((unsigned)(PN / 8 / kThreads), (unsigned)a.H, (unsigned)(a.Z * a.ndir));
+    hipLaunchKernelGGL(k2_state_pass8, g2, dim3(kThreads), 0, st, a, PN);
   } else if (phase == PHASE_STATE_PASS || phase == PHASE_ADJ_PASS) {
     const int PN = kP * N;
     dim3 g2((unsigned)((PN / 4 + kThreads - 1) / kThreads), (unsigned)a.H, (unsigned)(a.Z * a.ndir));
