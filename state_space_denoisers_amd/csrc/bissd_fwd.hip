@@ -501,9 +501,11 @@ __global__ __launch_bounds__(kThreads) void k2_state_pass(ScanArgs a, int PN, in
     *reinterpret_cast<f32x4 *>(a.final_state + ((int64_t)b * H + h) * PN + e) = S;
 }
 
-// The primal carry pass in bf16 with eight state elements per thread, so
-// every load and store moves 16 bytes; otherwise as k2_state_pass without
-// the adjoint (flip) mode.
+// The carry passes in bf16 with eight state elements per thread, so every
+// load and store moves 16 bytes; otherwise as k2_state_pass, FLIP selecting
+// its adjoint mode.  A wave covers 512 consecutive elements, each 32-lane
+// half the 256 of one boundary-product partial, so the partials keep the
+// [d][b][c][h][PN / 256] layout and the same element groups.
 __device__ __forceinline__ void widen8(u32x4 r, f32x4 &lo, f32x4 &hi) {
   asm volatile("" : "+v"(r));
   lo = f32x4{__builtin_bit_cast(float, r[0] << 16), __builtin_bit_cast(float, r[0] & 0xffff0000u),
@@ -511,8 +513,19 @@ __device__ __forceinline__ void widen8(u32x4 r, f32x4 &lo, f32x4 &hi) {
   hi = f32x4{__builtin_bit_cast(float, r[2] << 16), __builtin_bit_cast(float, r[2] & 0xffff0000u),
              __builtin_bit_cast(float, r[3] << 16), __builtin_bit_cast(float, r[3] & 0xffff0000u)};
 }
+__device__ __forceinline__ bf16x8 narrow8(const f32x4 &lo, const f32x4 &hi) {
+  bf16x8 o;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    o[k] = (bf16)lo[k];
+    o[4 + k] = (bf16)hi[k];
+  }
+  return o;
+}
+template <bool FLIP>
 __global__ __launch_bounds__(kThreads) void k2_state_pass8(ScanArgs a, int PN) {
-  const int e = (blockIdx.x * kThreads + threadIdx.x) * 8;  // PN is a multiple of 2048
+  const int gt = blockIdx.x * kThreads + threadIdx.x;
+  const int e = gt * 8;  // PN is a multiple of 2048
   const int h = blockIdx.y;
   const int d = a.dir0 + (int)(blockIdx.z % a.ndir);
   const int b = (int)(blockIdx.z / a.ndir);
@@ -523,30 +536,43 @@ __global__ __launch_bounds__(kThreads) void k2_state_pass8(ScanArgs a, int PN) {
   bf16 *dst = a.sin_t ? reinterpret_cast<bf16 *>(a.sin_t) + base : nullptr;
   const float *dec = a.cdecay + ((int64_t)d * a.Z + b) * nc * H + h;
   f32x4 S0 = {0.0f, 0.0f, 0.0f, 0.0f}, S1 = S0;
-  const bool primal_fwd = d == 0;
+  const bool primal_fwd = d == 0 && !FLIP;
   if (primal_fwd && a.init_state) {
     const float *in = a.init_state + ((int64_t)b * H + h) * PN + e;
     S0 = *reinterpret_cast<const f32x4 *>(in);
     S1 = *reinterpret_cast<const f32x4 *>(in + 4);
   }
-  const bool up = d == 0;
+  const bool up = (d == 0) != FLIP;
   const int step = up ? 1 : -1;
   const int c0 = up ? 0 : nc - 1;
+  const bool rpart = FLIP && a.out0;
   // block-segmented reverse: boundary index of the incoming carry, stepped
   const int rsc = d == 1 ? a.rseg_chunks : 0;
-  int bmod = rsc ? (c0 + 1) % rsc : 1;
+  int bmod = rsc ? (up ? c0 : c0 + 1) % rsc : 1;
+  const int nwv = PN / 256, wv = gt >> 5;
+  const bf16 *sinb = rpart ? reinterpret_cast<const bf16 *>(a.sin[d]) + (int64_t)b * a.sin_bstride[d] +
+                                 (int64_t)h * PN + e
+                           : nullptr;
   // forward calls skip the first chunk's zero carry-in and the last chunk's
   // state when it feeds no final_state
-  const bool write_first = !a.skip_edges || (primal_fwd && a.init_state);
-  const int nload = (a.skip_edges && !(primal_fwd && a.final_state)) ? nc - 1 : nc;
+  const bool edge = a.skip_edges && !FLIP;
+  const bool write_first = !edge || (primal_fwd && a.init_state);
+  const int nload = (edge && !(primal_fwd && a.final_state)) ? nc - 1 : nc;
   constexpr int D = 8;
-  u32x4 rl[D];
+  u32x4 rl[D], rn[FLIP ? D : 1];
   float rg[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) rl[i] = u32x4{0u, 0u, 0u, 0u};
   auto fetch = [&](int slot, int cc) __attribute__((always_inline)) {
     rl[slot] = *reinterpret_cast<const u32x4 *>(src + cc * cs);
     rg[slot] = dec[(int64_t)cc * H];
+    if constexpr (FLIP) {
+      if (rpart) {
+        int cn = d == 0 ? cc + 1 : cc - 1;
+        cn = cn < 0 ? 0 : (cn >= nc ? nc - 1 : cn);
+        rn[slot] = *reinterpret_cast<const u32x4 *>(sinb + (int64_t)cn * a.sin_cstride[d]);
+      }
+    }
   };
 #pragma unroll
   for (int i = 0; i < D; ++i)
@@ -557,8 +583,11 @@ __global__ __launch_bounds__(kThreads) void k2_state_pass8(ScanArgs a, int PN) {
       const int nn = n + i;
       if (nn >= nc) break;
       const int c = c0 + nn * step;
-      f32x4 l0, l1;
+      f32x4 l0, l1, n0 = {0.0f, 0.0f, 0.0f, 0.0f}, n1 = n0;
       widen8(rl[i], l0, l1);
+      if constexpr (FLIP) {
+        if (rpart) widen8(rn[i], n0, n1);
+      }
       const float g = exp2_fast(rg[i]);
       if (nn + D < nload) fetch(i, c + D * step);
       const bool cut = rsc != 0 && bmod == 0;
@@ -567,16 +596,23 @@ __global__ __launch_bounds__(kThreads) void k2_state_pass8(ScanArgs a, int PN) {
         S0[k] = cut ? 0.0f : S0[k];
         S1[k] = cut ? 0.0f : S1[k];
       }
-      bmod = bmod == 0 ? rsc - 1 : bmod - 1;
-      if (dst && (nn > 0 || write_first)) {
-        bf16x8 o;
+      bmod = up ? (bmod + 1 == rsc ? 0 : bmod + 1) : (bmod == 0 ? rsc - 1 : bmod - 1);
+      if constexpr (FLIP) {
+        if (rpart) {
+          // primal state after chunk c = primal carry-in of chunk c + 1
+          // (forward) or c - 1 (reverse)
+          const int cn = d == 0 ? c + 1 : c - 1;
+          float v = 0.0f;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          o[k] = (bf16)S0[k];
-          o[4 + k] = (bf16)S1[k];
+          for (int k = 0; k < 4; ++k) v += S0[k] * n0[k] + S1[k] * n1[k];
+          v = (cn >= 0 && cn < nc) ? v : 0.0f;
+#pragma unroll
+          for (int o = 1; o < 32; o <<= 1) v += __shfl_xor(v, o, 64);
+          if ((threadIdx.x & 31) == 0)
+            a.out0[((((int64_t)d * a.Z + b) * nc + c) * H + h) * nwv + wv] = v;
         }
-        *reinterpret_cast<bf16x8 *>(dst + c * cs) = o;
       }
+      if (dst && (nn > 0 || write_first)) *reinterpret_cast<bf16x8 *>(dst + c * cs) = narrow8(S0, S1);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         S0[k] = g * S0[k] + l0[k];
@@ -660,6 +696,77 @@ __global__ __launch_bounds__(kThreads) void k2_tangent_pass(ScanArgs a, int PN) 
       for (int k = 0; k < 4; ++k) {
         SA[k] = g * (SA[k] + ts * S[k]) + tloc[k];
         S[k] = g * S[k] + loc[k];
+      }
+    }
+  }
+}
+
+// The A-tangent pass in bf16 with eight elements per thread (16-byte loads
+// and stores); otherwise as k2_tangent_pass.
+__global__ __launch_bounds__(kThreads) void k2_tangent_pass8(ScanArgs a, int PN) {
+  const int e = (blockIdx.x * kThreads + threadIdx.x) * 8;  // PN is a multiple of 2048
+  const int h = blockIdx.y;
+  const int d = (int)(blockIdx.z % 2);
+  const int b = (int)(blockIdx.z / 2);
+  const int nc = a.nchunks, H = a.H;
+  const int64_t cs = (int64_t)H * PN;
+  const int64_t base = (((int64_t)d * a.Z + b) * nc * H + h) * (int64_t)PN + e;
+  const bf16 *sl = reinterpret_cast<const bf16 *>(a.states) + base;
+  const bf16 *tl = reinterpret_cast<const bf16 *>(a.states2) + base;
+  bf16 *dst = reinterpret_cast<bf16 *>(a.sin_t) + base;
+  const float *dec = a.cdecay + ((int64_t)d * a.Z + b) * nc * H + h;
+  const float *tsum = a.dtsum + ((int64_t)d * a.Z + b) * nc * H + h;
+  f32x4 S0 = {0.0f, 0.0f, 0.0f, 0.0f}, S1 = S0, A0 = S0, A1 = S0;
+  if (d == 0 && a.init_state) {
+    const float *in = a.init_state + ((int64_t)b * H + h) * PN + e;
+    S0 = *reinterpret_cast<const f32x4 *>(in);
+    S1 = *reinterpret_cast<const f32x4 *>(in + 4);
+  }
+  const int step = d == 0 ? 1 : -1;
+  const int c0 = d == 0 ? 0 : nc - 1;
+  // block-segmented reverse: the carry into chunk c crosses boundary c + 1,
+  // kept modulo the chunks per block as c steps down
+  const int rsc = d == 1 ? a.rseg_chunks : 0;
+  int bmod = rsc ? (c0 + 1) % rsc : 1;
+  constexpr int D = 4;
+  u32x4 rl[D], rt[D];
+  float rg[D], rs[D];
+  auto fetch = [&](int slot, int cc) __attribute__((always_inline)) {
+    rl[slot] = *reinterpret_cast<const u32x4 *>(sl + cc * cs);
+    rt[slot] = *reinterpret_cast<const u32x4 *>(tl + cc * cs);
+    rg[slot] = dec[(int64_t)cc * H];
+    rs[slot] = tsum[(int64_t)cc * H];
+  };
+#pragma unroll
+  for (int i = 0; i < D; ++i)
+    if (i < nc) fetch(i, c0 + i * step);
+  for (int n = 0; n < nc; n += D) {
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      const int nn = n + i;
+      if (nn >= nc) break;
+      const int c = c0 + nn * step;
+      f32x4 l0, l1, t0, t1;
+      widen8(rl[i], l0, l1);
+      widen8(rt[i], t0, t1);
+      const float g = exp2_fast(rg[i]), ts = rs[i];
+      if (nn + D < nc) fetch(i, c + D * step);
+      const bool cut = rsc != 0 && bmod == 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        S0[k] = cut ? 0.0f : S0[k];
+        S1[k] = cut ? 0.0f : S1[k];
+        A0[k] = cut ? 0.0f : A0[k];
+        A1[k] = cut ? 0.0f : A1[k];
+      }
+      bmod = bmod == 0 ? rsc - 1 : bmod - 1;
+      *reinterpret_cast<bf16x8 *>(dst + c * cs) = narrow8(A0, A1);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        A0[k] = g * (A0[k] + ts * S0[k]) + t0[k];
+        A1[k] = g * (A1[k] + ts * S1[k]) + t1[k];
+        S0[k] = g * S0[k] + l0[k];
+        S1[k] = g * S1[k] + l1[k];
       }
     }
   }
@@ -1417,14 +1524,21 @@ static void launch_t(const ScanArgs &a, int phase, hipStream_t st) {
     const int nrb = a.chunk / kRB;
     dim3 g((unsigned)((int64_t)a.Z * a.nchunks * 2 * a.G * (nrb * (nrb + 1) / 2)));
     hipLaunchKernelGGL((k_gram<T, N>), g, dim3(kThreads), 0, st, a);
+  } else if (phase == PHASE_TAN_PASS && sizeof(T) == 2) {
+    const int PN = kP * N;
+    dim3 g2((unsigned)(PN / 8 / kThreads), (unsigned)a.H, (unsigned)(a.Z * 2));
+    hipLaunchKernelGGL(k2_tangent_pass8, g2, dim3(kThreads), 0, st, a, PN);
   } else if (phase == PHASE_TAN_PASS) {
     const int PN = kP * N;
     dim3 g2((unsigned)(PN / 4 / kThreads), (unsigned)a.H, (unsigned)(a.Z * 2));
     hipLaunchKernelGGL(k2_tangent_pass<T>, g2, dim3(kThreads), 0, st, a, PN);
-  } else if (phase == PHASE_STATE_PASS && sizeof(T) == 2) {
+  } else if ((phase == PHASE_STATE_PASS || phase == PHASE_ADJ_PASS) && sizeof(T) == 2) {
     const int PN = kP * N;
     dim3 g2((unsigned)(PN / 8 / kThreads), (unsigned)a.H, (unsigned)(a.Z * a.ndir));
-    hipLaunchKernelGGL(k2_state_pass8, g2, dim3(kThreads), 0, st, a, PN);
+    if (phase == PHASE_ADJ_PASS)
+      hipLaunchKernelGGL(k2_state_pass8<true>, g2, dim3(kThreads), 0, st, a, PN);
+    else
+      hipLaunchKernelGGL(k2_state_pass8<false>, g2, dim3(kThreads), 0, st, a, PN);
   } else if (phase == PHASE_STATE_PASS || phase == PHASE_ADJ_PASS) {
     const int PN = kP * N;
     dim3 g2((unsigned)((PN / 4 + kThreads - 1) / kThreads), (unsigned)a.H, (unsigned)(a.Z * a.ndir));
