@@ -410,9 +410,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_decay(BwdArgs a) {
       run += v[i];
       acc[i] = run;
     }
-    const float incl = wave_scan_down(run);
-    float excl = __shfl_down(incl, 1, 64);
-    if (lane == 63) excl = 0.0f;
+    const float excl = wave_shift_down1(wave_scan_down(run));
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] += excl + R;
   } else {
@@ -421,9 +419,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_decay(BwdArgs a) {
       run += v[i];
       acc[i] = run;
     }
-    const float incl = wave_scan_up(run);
-    float excl = __shfl_up(incl, 1, 64);
-    if (lane == 0) excl = 0.0f;
+    const float excl = wave_shift_up1(wave_scan_up(run));
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] += excl + R;
   }

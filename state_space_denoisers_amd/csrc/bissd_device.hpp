@@ -616,29 +616,56 @@ __device__ __forceinline__ int xcd_linear_id(int bid, int nwg) {
 
 // ------------------------------------------------------ wavefront scans
 
+// Cross-lane moves through DPP (no LDS round trip).  Lanes whose source lies
+// outside the pattern (or whose row is masked off) read 0.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROWS, 0xf, false));
+}
+// Inclusive sum from lane 0 upwards: steps of 1, 2, 4, 8 lanes inside each
+// 16-lane row (row_shr), then each row adds the totals of the rows below it.
 __device__ __forceinline__ float wave_scan_up(float v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const float t = __shfl_up(v, o, 64);
-    if (lane >= o) v += t;
-  }
-  return v;
+  v += dpp_f<0x111>(v);
+  v += dpp_f<0x112>(v);
+  v += dpp_f<0x114>(v);
+  v += dpp_f<0x118>(v);
+  const int row = (threadIdx.x & 63) >> 4;
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 15));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 31));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 47));
+  const float below = row == 0 ? 0.0f : row == 1 ? r0 : row == 2 ? r0 + r1 : (r0 + r1) + r2;
+  return v + below;
 }
+// Inclusive sum from lane 63 downwards (row_shl inside the rows, then the
+// totals of the rows above).
 __device__ __forceinline__ float wave_scan_down(float v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const float t = __shfl_down(v, o, 64);
-    if (lane + o < 64) v += t;
-  }
-  return v;
+  v += dpp_f<0x101>(v);
+  v += dpp_f<0x102>(v);
+  v += dpp_f<0x104>(v);
+  v += dpp_f<0x108>(v);
+  const int row = (threadIdx.x & 63) >> 4;
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  const float above = row == 3 ? 0.0f : row == 2 ? r3 : row == 1 ? r3 + r2 : (r3 + r2) + r1;
+  return v + above;
 }
+// lane l receives lane l - 1 (lane 0: 0) / lane l + 1 (lane 63: 0)
+__device__ __forceinline__ float wave_shift_up1(float v) { return dpp_f<0x138>(v); }
+__device__ __forceinline__ float wave_shift_down1(float v) { return dpp_f<0x130>(v); }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+// Largest value over the wave for v >= 0 (row maxima by row_shr, then the
+// four row results), in every lane.
+__device__ __forceinline__ float wave_max_nonneg(float v) {
+  v = fmaxf(v, dpp_f<0x111>(v));
+  v = fmaxf(v, dpp_f<0x112>(v));
+  v = fmaxf(v, dpp_f<0x114>(v));
+  v = fmaxf(v, dpp_f<0x118>(v));
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 15));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 31));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 47));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
 // Mamba-2's dt post-processing, applied wherever a kernel reads dt when the
@@ -734,7 +761,7 @@ __device__ __forceinline__ float chunk_decay_scan_vals(const float (&d)[4], int 
     a[i] = d[i] * A2;
     amax = fmaxf(amax, fabsf(a[i]));
   }
-  amax = wave_max(amax);
+  amax = wave_max_nonneg(amax);
   float pre[4];
   if (!reverse) {
     float run = 0.0f;
@@ -745,8 +772,7 @@ __device__ __forceinline__ float chunk_decay_scan_vals(const float (&d)[4], int 
       a[i] = run;
     }
     const float incl = wave_scan_up(run);
-    float excl = __shfl_up(incl, 1, 64);
-    if (lane == 0) excl = 0.0f;
+    const float excl = wave_shift_up1(incl);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (i < K) {
@@ -764,8 +790,7 @@ __device__ __forceinline__ float chunk_decay_scan_vals(const float (&d)[4], int 
       }
     }
     const float incl = wave_scan_down(run);
-    float excl = __shfl_down(incl, 1, 64);
-    if (lane == 63) excl = 0.0f;
+    const float excl = wave_shift_down1(incl);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (i < K) {

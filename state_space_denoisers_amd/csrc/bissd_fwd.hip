@@ -1255,6 +1255,20 @@ void k3_chunk_out(ScanArgs a) {
 #pragma unroll
           for (int v = 0; v < 4; ++v)
             frag_rows(xf[v], &sm.u.s.Xs[hh][0][0], Sm::XPT, 32 * q + 4 * g4, 32 * q + 16 + 4 * g4, 16 * v);
+          if constexpr (MODE == 0 && DIAG && d == 0) {
+            // the skip D x: on the diagonal s-block, fragment q = w / 2 holds
+            // x at this lane's own accumulator positions (rows 16 w + 4 g4 +
+            // i, column 16 v + r16), in its low (even w) or high (odd w) half
+            if (q == (w >> 1)) {
+              const float Dh = a.D[h0 + hh];
+              const bool hi = (w & 1) != 0;
+#pragma unroll
+              for (int v = 0; v < 4; ++v)
+#pragma unroll
+                for (int i2 = 0; i2 < 4; ++i2)
+                  acc[hh][v][i2] += Dh * (hi ? (float)xf[v].v[4 + i2] : (float)xf[v].v[i2]);
+            }
+          }
 #pragma unroll
           for (int v = 0; v < 4; ++v) mma(acc[hh][v], mf[hh][q], xf[v]);
           if constexpr (DAI)
@@ -1313,32 +1327,36 @@ void k3_chunk_out(ScanArgs a) {
     run_direction(std::integral_constant<int, 0>{});
     run_direction(std::integral_constant<int, 1>{});
 
-    // y = acc + D x, one head at a time staged through LDS so that every lane
-    // writes 16 contiguous bytes
-    T *yg = reinterpret_cast<T *>(a.y) + (((int64_t)b * L + t0 + j * kRB) * H + h0) * kP;
-    const T *xo = xg + (int64_t)j * kRB * xrs;
+    // y = acc (the skip D x was added on the forward diagonal s-block).
+    // Each wave stages its own 16 rows through LDS, one head at a time, so
+    // that every lane writes 16 contiguous bytes; a wave's LDS accesses
+    // complete in order and no other wave touches those rows, so the only
+    // barrier is the one that frees the shared region.
+    __syncthreads();
+    float *ow = &sm.u.Out[0][16 * w][0];
+    const int rr = lane >> 2, pc = (lane & 3) * 16;  // row of the wave's 16, first of 16 columns
+    const bool rvalid = j * kRB + 16 * w + rr < qlen;
+    T *yg = reinterpret_cast<T *>(a.y) + (((int64_t)b * L + t0 + j * kRB + 16 * w + rr) * H + h0) * kP + pc;
 #pragma unroll
-    for (int ih = 0; ih < HT / IH; ++ih) {
-      __syncthreads();
+    for (int hh = 0; hh < HT; ++hh) {
 #pragma unroll
-      for (int q = 0; q < IH; ++q)
+      for (int v = 0; v < 4; ++v)
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
+        for (int i2 = 0; i2 < 4; ++i2) ow[(4 * g4 + i2) * Sm::OP + 16 * v + r16] = acc[hh][v][i2];
+      float o0[8], o1[8];
 #pragma unroll
-          for (int i2 = 0; i2 < 4; ++i2)
-            sm.u.Out[q][16 * w + 4 * g4 + i2][16 * v + r16] = acc[ih * IH + q][v][i2];
-      __syncthreads();
-      for (int it = tid; it < IH * kRB * 8; it += kThreads) {
-        const int q = it / (kRB * 8), r = (it >> 3) % kRB, p0 = (it & 7) * 8;
-        if (j * kRB + r >= qlen) continue;
-        const int hh = ih * IH + q;
-        const float Dh = a.D[h0 + hh];
-        const int64_t off = (int64_t)r * xrs + hh * kP + p0;
-        float xv[8], o[8];
-        gload8(xv, xo + off);
+      for (int m = 0; m < 2; ++m) {
+        const f32x4 lo = *reinterpret_cast<const f32x4 *>(&ow[rr * Sm::OP + pc + 8 * m]);
+        const f32x4 hi = *reinterpret_cast<const f32x4 *>(&ow[rr * Sm::OP + pc + 8 * m + 4]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = sm.u.Out[q][r][p0 + e] + Dh * xv[e];
-        gstore8(yg + off, o);
+        for (int e = 0; e < 4; ++e) {
+          (m ? o1 : o0)[e] = lo[e];
+          (m ? o1 : o0)[4 + e] = hi[e];
+        }
+      }
+      if (rvalid) {
+        gstore8(yg + hh * kP, o0);
+        gstore8(yg + hh * kP + 8, o1);
       }
     }
   } else {
