@@ -310,7 +310,12 @@ void k1_chunk_state(ScanArgs a) {
     }
   }
 
-  if constexpr (MODE <= 2) {
+  // Forward calls (skip_edges) leave out the states no later kernel reads:
+  // the forward direction's last chunk (unless it feeds final_state) and the
+  // reverse direction's first chunk (the last in its scan order).
+  const bool unread = MODE == 0 && a.skip_edges &&
+                      (d == 0 ? (c == a.nchunks - 1 && a.final_state == nullptr) : c == 0);
+  if constexpr (MODE <= 2) if (!unread) {
     // one head at a time through LDS (the B tile, no longer read), so that
     // every thread stores 16 contiguous bytes
     constexpr int EPV = 16 / (int)sizeof(T);

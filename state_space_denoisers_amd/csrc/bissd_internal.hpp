@@ -92,9 +92,9 @@ struct ScanArgs {
   // per reverse block when a block is shorter than a chunk (1 or 2); the
   // reverse direction's within-chunk pairs then stay inside their block.
   int rseg_chunks, rseg_tiles;
-  // PHASE_STATE_PASS of a forward call: skip what the output kernel never
-  // reads (the first chunk's zero carry-in in scan order, the last chunk's
-  // state unless it feeds final_state)
+  // Forward calls: skip what no later kernel reads -- PHASE_STATE_PASS the
+  // first chunk's zero carry-in in scan order and the last chunk's state
+  // unless it feeds final_state, PHASE_CHUNK_STATE the writes of those states
   int skip_edges;
 };
 
