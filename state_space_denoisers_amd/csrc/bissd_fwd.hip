@@ -611,10 +611,20 @@ __global__ __launch_bounds__(kThreads) void k2_state_pass8(ScanArgs a, int PN) {
 #pragma unroll
           for (int k = 0; k < 4; ++k) v += S0[k] * n0[k] + S1[k] * n1[k];
           v = (cn >= 0 && cn < nc) ? v : 0.0f;
-#pragma unroll
-          for (int o = 1; o < 32; o <<= 1) v += __shfl_xor(v, o, 64);
-          if ((threadIdx.x & 31) == 0)
-            a.out0[((((int64_t)d * a.Z + b) * nc + c) * H + h) * nwv + wv] = v;
+          // row sums by DPP (lane 15 of each 16-lane row), then each 32-lane
+          // half adds its two rows
+          v += dpp_f<0x111>(v);
+          v += dpp_f<0x112>(v);
+          v += dpp_f<0x114>(v);
+          v += dpp_f<0x118>(v);
+          const int vi = __builtin_bit_cast(int, v);
+          const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(vi, 15));
+          const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(vi, 31));
+          const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(vi, 47));
+          const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(vi, 63));
+          float *po = a.out0 + ((((int64_t)d * a.Z + b) * nc + c) * H + h) * nwv + wv;
+          if ((threadIdx.x & 63) == 0) *po = r0 + r1;
+          if ((threadIdx.x & 63) == 32) *po = r2 + r3;
         }
       }
       if (dst && (nn > 0 || write_first)) *reinterpret_cast<bf16x8 *>(dst + c * cs) = narrow8(S0, S1);
