@@ -21,9 +21,9 @@
 // global round trip.  The two directions run side by side in two groups of
 // four waves (a batch of a few rows leaves most compute units idle, so each
 // workgroup's critical path is what counts): the forward group adds the
-// carried state, the reverse group forms the committed state, and the
-// reverse outputs reach the forward group through LDS for the one write of
-// y.
+// carried state, the reverse outputs reach the forward group through LDS for
+// the one write of y, and the two groups form half of the committed state
+// each.
 #include "bissd_device.hpp"
 #include "bissd_internal.hpp"
 
@@ -43,8 +43,9 @@ template <typename T, int N> struct BlockLds {
 constexpr int kBlkThreads = 2 * kThreads;  // two groups of four waves
 
 // Workgroup = (batch b, head h), two groups of four waves: group d takes
-// direction d.  Wave w of a group owns block rows t = 16 w .. 16 w + 15 (and,
-// in the reverse group, committed state rows p = 16 w .. 16 w + 15).  Decay
+// direction d.  Wave w of a group owns block rows t = 16 w .. 16 w + 15 and
+// committed state rows p = 16 w .. 16 w + 15 of its group's half of the
+// state columns.  Decay
 // weights are formed exactly per element (the block is a single 64 x 64
 // tile), masked by selection.
 template <typename T, int N>
@@ -171,14 +172,46 @@ __global__ __launch_bounds__(kBlkThreads) void k_block_update(ScanArgs a) {
     for (int v = 0; v < 4; ++v) xchg[w][v][lane] = acc[v];
   }
 
-  // ---- committed state (reverse group): S_out = 2^lam_last S_in +
-  // sum_s w_s x_s (outer) B_s, w_s = 2^(lam_last - lam_s) dt_s; wave w owns
-  // state rows p = 16w..16w+15
-  if (grp == 1 && a.final_state) {
-    const float lend = sm.lam[0][kRB - 1];  // tokens past the block have dt = 0
-    f32x4 sacc[NT];
+  // the reverse outputs are in LDS for the forward group's write of y; no
+  // tile is written after this point
+  __syncthreads();
+
+  if (grp == 0) {
+    // ---- y = forward + reverse + D x (forward group; rows 16w + 4 g4 + i,
+    // columns 16 v + r16; 16 lanes store one contiguous row segment), x from
+    // its tile
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) zero4(sacc[nt]);
+    for (int v = 0; v < 4; ++v) {
+      const f32x4 r = xchg[w][v][lane];
+#pragma unroll
+      for (int i2 = 0; i2 < 4; ++i2) acc[v][i2] += r[i2];
+    }
+    const float Dh = a.D[h];
+    T *yg = reinterpret_cast<T *>(a.y) + ((int64_t)b * L * H + h) * kP;
+#pragma unroll
+    for (int i2 = 0; i2 < 4; ++i2) {
+      const int t = 16 * w + 4 * g4 + i2;
+      if (t >= L) continue;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int p = 16 * v + r16;
+        const float xv = to_f(*reinterpret_cast<const T *>(tX + DX::at(t, (int)ES * p)));
+        yg[(int64_t)t * H * kP + p] = from_f<T>(acc[v][i2] + Dh * xv);
+      }
+    }
+  }
+
+  // ---- committed state: S_out = 2^lam_last S_in + sum_s w_s x_s (outer)
+  // B_s, w_s = 2^(lam_last - lam_s) dt_s.  Group g forms columns n of its
+  // half (16-column tiles g NT / 2 .. g NT / 2 + NT / 2 - 1); wave w owns
+  // state rows p = 16w..16w+15.
+  if (a.final_state) {
+    constexpr int NH = NT / 2;
+    const int nt0 = grp * NH;
+    const float lend = sm.lam[0][kRB - 1];  // tokens past the block have dt = 0
+    f32x4 sacc[NH];
+#pragma unroll
+    for (int nt = 0; nt < NH; ++nt) zero4(sacc[nt]);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       // A operand: x^T rows p = 16w + r16, k = s = 32ks + 8 g4 + e, scaled by w_s
@@ -193,47 +226,22 @@ __global__ __launch_bounds__(kBlkThreads) void k_block_update(ScanArgs a) {
       }
       frag_from(xa, xv);
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
+      for (int nt = 0; nt < NH; ++nt) {
         Frag<T> bfr;
-        frag_rows_swz<DB>(bfr, tBf, 32 * ks + 8 * g4, 32 * ks + 8 * g4 + 4, 16 * nt);
+        frag_rows_swz<DB>(bfr, tBf, 32 * ks + 8 * g4, 32 * ks + 8 * g4 + 4, 16 * (nt0 + nt));
         mma(sacc[nt], xa, bfr);
       }
     }
     const float gam = exp2_fast(lend);
     float *so = a.final_state + ((int64_t)b * H + h) * kP * N;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+    for (int nt = 0; nt < NH; ++nt)
 #pragma unroll
       for (int i2 = 0; i2 < 4; ++i2) {
-        const int p = 16 * w + 4 * g4 + i2, n = 16 * nt + r16;
+        const int p = 16 * w + 4 * g4 + i2, n = 16 * (nt0 + nt) + r16;
         const float s0 = *reinterpret_cast<const float *>(tS + DS::at(p, 4 * n));
         so[p * N + n] = gam * s0 + sacc[nt][i2];
       }
-  }
-
-  __syncthreads();
-  if (grp == 1) return;
-  // ---- y = forward + reverse + D x (forward group; rows 16w + 4 g4 + i,
-  // columns 16 v + r16; 16 lanes store one contiguous row segment), x from
-  // its tile
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const f32x4 r = xchg[w][v][lane];
-#pragma unroll
-    for (int i2 = 0; i2 < 4; ++i2) acc[v][i2] += r[i2];
-  }
-  const float Dh = a.D[h];
-  T *yg = reinterpret_cast<T *>(a.y) + ((int64_t)b * L * H + h) * kP;
-#pragma unroll
-  for (int i2 = 0; i2 < 4; ++i2) {
-    const int t = 16 * w + 4 * g4 + i2;
-    if (t >= L) continue;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int p = 16 * v + r16;
-      const float xv = to_f(*reinterpret_cast<const T *>(tX + DX::at(t, (int)ES * p)));
-      yg[(int64_t)t * H * kP + p] = from_f<T>(acc[v][i2] + Dh * xv);
-    }
   }
 }
 
