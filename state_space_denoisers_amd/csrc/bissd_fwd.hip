@@ -924,7 +924,7 @@ template <typename T, int N, int HT, bool SF32> struct K3Pf {
 // the result: dy_t (B_t.C_t) into G_t B_t for dx and x.(G_t B_t).
 template <typename T, int N, int HT, bool SF32, int MODE>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? (MODE == 1 ? 3 : MODE == 2 ? 2 : (SF32 ? 1 : 4)) : 1)))
+__attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? (MODE == 1 ? (HT == 1 ? 4 : 3) : MODE == 2 ? 2 : (SF32 ? 1 : 4)) : 1)))
 void k3_chunk_out(ScanArgs a) {
   using Sm = K3Lds<T, N, HT>;
   using PF = K3Pf<T, N, HT, SF32>;
@@ -1603,9 +1603,11 @@ bool gram_in_k1(int H, int G, int chunk) {
 
 hipError_t launch_scan_phase(const ScanArgs &args, int phase, hipStream_t st) {
   // Heads of one tile share their B/C group: 2 heads when the heads per
-  // group are even, else 1.
+  // group are even, else 1.  The dy.y_d pass (two products per stage) takes
+  // one head per tile: with two, its accumulators leave too few registers
+  // for four waves per SIMD without spilling.
   const int hpg = args.H / args.G;
-  const int HT = hpg % 2 == 0 ? 2 : 1;
+  const int HT = (hpg % 2 == 0 && phase != PHASE_YDOT) ? 2 : 1;
   ScanArgs a = args;
   const int nrb = a.chunk / kRB;
   a.fd_tiles = FastDiv((uint32_t)(a.H / HT));
