@@ -68,10 +68,11 @@ template <typename T, int N> struct PanelLds {
 
 // Workgroup = (batch b, chunk c, direction d, group g, 64-token row-block j)
 // of one panel.  PNL 0 produces dC rows t: the row source is dy, the column
-// source x, the columns s run before t in scan order, and the carried state
-// is the forward carry-in S_in.  PNL 1 produces dB rows s: the row source is
-// x, the column source dy, the columns t run after s, and the carried state
-// is the adjoint carry.  Wave w owns rows 16 w .. 16 w + 15 of the block.
+// source x, the columns s run before t in scan order.  PNL 1 produces dB rows
+// s: the row source is x, the column source dy, the columns t run after s.
+// Wave w owns rows 16 w .. 16 w + 15 of the block.  The carried-state term
+// (with the forward carry-in for dC, the adjoint carry for dB) is added by
+// k_bwd_state after the panel.
 //
 // Per head of the group: the Gram tiles D[col][row] = ColSrc_col . RowSrc_row
 // come out of the matrix cores already laid out as the A operand of the
@@ -80,28 +81,28 @@ template <typename T, int N> struct PanelLds {
 // the factored weight 2^(cum_row - m) 2^(m - cum_col) (or its mirror), m the
 // decay sum at the block boundary, so both factors are <= 1: a per-lane row
 // factor times a per-column factor formed once per head; the diagonal block
-// is weighted exactly per element and masked by selection; the carried-state term RowSrc_row . State is added per head
-// with its row factor.  After the last head the summed weights multiply the
-// value rows (B for dC, C for dB), one 64-row slab at a time.
+// is weighted exactly per element and masked by selection.  After the last
+// head the summed weights multiply the value rows (B for dC, C for dB), one
+// 64-row slab at a time.
 //
-// Every head's column slabs and state are copied buffer -> LDS directly into
-// a tile.  With two tiles (the bf16 dC panel) the copies for head h + 1 are
-// in flight while head h is multiplied; with one, two workgroups per CU
-// overlap each other's copies.  Each head costs one or two barriers.
+// Every head's column slabs are copied buffer -> LDS directly into a tile.
+// With two tiles the copies for head h + 1 are in flight while head h is
+// multiplied; with one (used: 38 KB of LDS), three workgroups per CU overlap
+// each other's copies.  Each head costs one or two barriers.
 template <typename T, int N, int PNL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1)))
 void k_bwd_panel(BwdArgs a) {
   using Sm = PanelLds<T, N>;
   constexpr uint32_t ES = sizeof(T);
   constexpr int CRB = kP * ES, SRB = N * ES;
-  constexpr int CSB = 4 * kRB * CRB, STB = kP * SRB;
-  // one tile: two workgroups share a CU and overlap each other's copies
+  constexpr int CSB = 4 * kRB * CRB;
+  // one tile: three workgroups share a CU and overlap each other's copies
   constexpr bool DBUF = false;
   using DC = DmaTile<CRB, SW_NAT>;
   using DS = DmaTile<SRB, SW_TR>;
   __shared__ Sm sm;
-  __shared__ __attribute__((aligned(16))) char bufA[CSB + STB];
-  __shared__ __attribute__((aligned(16))) char bufB[DBUF ? CSB + STB : 16];
+  __shared__ __attribute__((aligned(16))) char bufA[CSB];
+  __shared__ __attribute__((aligned(16))) char bufB[DBUF ? CSB : 16];
   constexpr int NT = N / 16;
   const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
   const int Q = a.chunk, NRB = Q / kRB, H = a.H, G = a.G, hpg = H / G;
@@ -130,7 +131,6 @@ void k_bwd_panel(BwdArgs a) {
   const T *rowsrc = reinterpret_cast<const T *>(PNL == 0 ? a.dy : a.x);
   const T *colsrc = reinterpret_cast<const T *>(PNL == 0 ? a.x : a.dy);
   const T *valsrc = reinterpret_cast<const T *>(PNL == 0 ? a.B[d] : a.C[d]);
-  const T *stsrc = reinterpret_cast<const T *>(PNL == 0 ? a.sin[d] : a.gin[d]);
   const bufres rRow = make_buf(rowsrc + (int64_t)b * L * H * kP, (uint32_t)(L * H * kP * ES));
   const bufres rCol = make_buf(colsrc + (int64_t)b * L * H * kP, (uint32_t)(L * H * kP * ES));
   const bufres rVal = make_buf(valsrc + (int64_t)b * L * G * N, (uint32_t)(L * G * N * ES));
@@ -145,12 +145,10 @@ void k_bwd_panel(BwdArgs a) {
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) zero4(oacc[nt]);
 
-  // one head's column slabs kb..ke and carried state -> a tile
+  // one head's column slabs kb..ke -> a tile
   auto issue_head = [&](int h, char *tile) __attribute__((always_inline)) {
     for (int k = kb; k <= ke; ++k)
       DC::load(tile + k * kRB * CRB, rCol, (uint32_t)((t0 + k * kRB) * H + h) * kP * ES, xrs, kRB);
-    const int64_t soff = (int64_t)b * a.st_bstride + (int64_t)c * a.st_cstride + (int64_t)h * kP * N;
-    DS::load(tile + CSB, make_buf(stsrc + soff, (uint32_t)(kP * N * ES)), 0u, (uint32_t)SRB, kP);
   };
   auto issue_val = [&](int k, char *tile) __attribute__((always_inline)) {
     DS::load(tile, rVal, (uint32_t)((t0 + k * kRB) * G + g) * N * ES, vrs, kRB);
@@ -229,15 +227,6 @@ void k_bwd_panel(BwdArgs a) {
     // row factor of the off-diagonal blocks (dC 2^(cum_t - m), dB dt_s 2^(m - cum_s))
     const float mref = mok ? lam[mtok] : 0.0f;
     const float rowf = PNL == 0 ? exp2_fast(fminf(lrow - mref, 0.0f)) : drow * exp2_fast(fminf(mref - lrow, 0.0f));
-    float fr[4];
-    {
-      const float lend = d == 0 ? lam[qlen - 1] : lam[0];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = j * kRB + 16 * w + 4 * g4 + i;
-        fr[i] = PNL == 0 ? exp2_fast(lam[r]) : dtv[r] * exp2_fast(fminf(lend - lam[r], 0.0f));
-      }
-    }
     Frag<T> rfn[2];
     uint32_t dtn[4];
     // the next head's per-token values, consumed after this head's products
@@ -282,21 +271,6 @@ void k_bwd_panel(BwdArgs a) {
           }
         }
       }
-    }
-
-    // carried-state term: rows r = 64 j + 16 w + 4 g4 + i, columns n
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      f32x4 t2;
-      zero4(t2);
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        Frag<T> sf;
-        frag_rows_swz<DS>(sf, cur + CSB, 32 * ks + 8 * g4, 32 * ks + 8 * g4 + 4, 16 * nt);
-        mma(t2, rf[ks], sf);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) oacc[nt][i] += fr[i] * t2[i];
     }
 
     if (hi + 1 < hpg) {
@@ -358,6 +332,183 @@ void k_bwd_panel(BwdArgs a) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) o[16 * nt + r16] = oacc[nt][i];
   }
+}
+
+// ============================================ carried-state term of dB / dC
+
+// The panels' carried-state term, summed over a group's heads:
+//   dC_t += sum_h 2^cum_t (dy_t . S_in)            (PNL 0, S_in the carry-in)
+//   dB_s += sum_h dt_s 2^(cum_end - cum_s) (x_s . Gc)  (PNL 1, Gc the adjoint carry)
+// with the head-dim product dy_t . S (a 64-vector times a 64 x N state).
+// Workgroup = (batch b, chunk c, direction d, group g), eight waves; wave w
+// owns chunk rows 32 w .. 32 w + 31.  Every head's state goes buffer -> LDS
+// (transposed swizzle, as in the panels) into one of NS tiles, so the copies
+// of the next NS - 1 heads are in flight while one is multiplied; each state
+// tile serves all rows of the chunk.  Added to the panel's output (launched
+// after it on the same stream, so the sum has a fixed order).
+// an empty asm that takes a fragment's registers: the compiler waits for
+// their loads here
+__device__ __forceinline__ void hold(Frag<bf16> &f) { asm volatile("" : "+v"(f.v) : : "memory"); }
+__device__ __forceinline__ void hold(Frag<float> &f) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(f.v[e]) : : "memory");
+}
+constexpr int kStThreads = 512;
+template <typename T, int N, int PNL>
+__global__ __launch_bounds__(kStThreads) void k_bwd_state(BwdArgs a) {
+  constexpr uint32_t ES = sizeof(T);
+  constexpr int SRB = N * (int)ES, STB = kP * SRB;
+  constexpr int NS = sizeof(T) == 2 ? 3 : 2;  // state tiles (heads) in flight
+  constexpr int NT = N / 16;
+  constexpr int NWV = kStThreads / 64;
+  using DS = DmaTile<SRB, SW_TR>;
+  __shared__ __attribute__((aligned(16))) char tiles[NS * STB];
+  const int tid = threadIdx.x, wv = wave_id(), lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
+  const int Q = a.chunk, H = a.H, G = a.G, hpg = H / G;
+  const int64_t L = a.L;
+  // work item = ((b * nchunks + c) * 2 + d) * G + g; consecutive items on one
+  // XCD, so both directions of a chunk read its rows through the same L2
+  int bx = xcd_linear_id(blockIdx.x, gridDim.x);
+  const int g = bx % G;
+  bx /= G;
+  const int d = bx % 2;
+  bx /= 2;
+  const int c = bx % a.nchunks, b = bx / a.nchunks;
+  const int64_t t0 = (int64_t)c * Q;
+  const int qlen = (int)((L - t0) < Q ? (L - t0) : Q);
+  const bool rows = 32 * wv < qlen;  // this wave has rows of the chunk
+
+  const T *rowsrc = reinterpret_cast<const T *>(PNL == 0 ? a.dy : a.x);
+  const T *stsrc = reinterpret_cast<const T *>(PNL == 0 ? a.sin[d] : a.gin[d]);
+  const bufres rRow = make_buf(rowsrc + (int64_t)b * L * H * kP, (uint32_t)(L * H * kP * ES));
+  const bufres rDt = make_buf(reinterpret_cast<const T *>(a.dt[d]) + (int64_t)b * L * H, (uint32_t)(L * H * ES));
+  const int64_t cbase = ((int64_t)d * a.Z + b) * H;
+  DtPost post;
+  post.on = a.dtb[d] != nullptr;
+  post.lo = a.dtlo[d];
+  post.hi = a.dthi[d];
+
+  // per head in flight: row-source fragments of the wave's two 16-row tiles,
+  // the decay sums of the lane's 8 rows (rows 32 w + 16 rt + 4 g4 + i), and
+  // for dB their raw dt
+  Frag<T> rf[NS][2][2];
+  f32x4 lm[NS][2];
+  uint32_t dtr[NS][2][4];
+  auto issue = [&](int hi, int slot) __attribute__((always_inline)) {
+    const int h = g * hpg + hi;
+    const int64_t soff = (int64_t)b * a.st_bstride + (int64_t)c * a.st_cstride + (int64_t)h * kP * N;
+    DS::load(tiles + slot * STB, make_buf(stsrc + soff, (uint32_t)(kP * N * ES)), 0u, (uint32_t)SRB, kP, wv, NWV);
+    // every wave loads its rows, also past the chunk (the next chunk's
+    // tokens, or zeros past L), so that every wave can wait for them
+    {
+      const bufres rl = make_buf(a.lamg + (cbase + h) * L, (uint32_t)(L * 4));
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const int r = 32 * wv + 16 * rt;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          frag_bload(rf[slot][rt][ks], rRow, (uint32_t)((t0 + r + r16) * H + h) * kP * ES + (32 * ks + 8 * g4) * ES);
+        // one load per token: tokens past L read as zero
+        const uint32_t lo = (uint32_t)(t0 + r + 4 * g4) * 4u;
+        lm[slot][rt] = f32x4{__builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, lo, 0, 0)),
+                             __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, lo + 4u, 0, 0)),
+                             __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, lo + 8u, 0, 0)),
+                             __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, lo + 12u, 0, 0))};
+        if constexpr (PNL == 1) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t doff = (uint32_t)((t0 + r + 4 * g4 + i) * H + h) * ES;
+            if constexpr (sizeof(T) == 2) dtr[slot][rt][i] = __builtin_amdgcn_raw_buffer_load_b16(rDt, doff, 0, 0);
+            else dtr[slot][rt][i] = __builtin_amdgcn_raw_buffer_load_b32(rDt, doff, 0, 0);
+          }
+        }
+      }
+    }
+  };
+
+  f32x4 oacc[2][NT];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) zero4(oacc[rt][nt]);
+
+#pragma unroll
+  for (int u = 0; u < NS - 1; ++u)
+    if (u < hpg) issue(u, u);
+  for (int hi0 = 0; hi0 < hpg; hi0 += NS) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const int hi = hi0 + u;
+      if (hi >= hpg) break;
+      // this head's register loads were issued after its state copy and
+      // loads complete in order, so waiting for them (here, before the
+      // barrier) covers the copy too, and leaves the later heads in flight
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) hold(rf[u][rt][ks]);
+        asm volatile("" : "+v"(lm[u][rt]) : : "memory");
+        if constexpr (PNL == 1)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(dtr[u][rt][i]) : : "memory");
+      }
+      // every wave's part of this head's state is in LDS, and every wave is
+      // done with the tile the next copy goes to (read in the last step)
+      __syncthreads();
+      if (hi + NS - 1 < hpg) issue(hi + NS - 1, (u + NS - 1) % NS);
+      if (!rows) continue;
+      const int h = g * hpg + hi;
+      const char *tile = tiles + u * STB;
+      float lend = 0.0f, bias = 0.0f;
+      if constexpr (PNL == 1) {
+        lend = a.lamg[(cbase + h) * L + t0 + (d == 0 ? qlen - 1 : 0)];
+        bias = post.on ? a.dtb[d][h] : 0.0f;
+      }
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        float fr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (PNL == 0) {
+            fr[i] = exp2_fast(lm[u][rt][i]);
+          } else {
+            DtPost ph = post;
+            ph.bias = bias;
+            const int64_t tok = t0 + 32 * wv + 16 * rt + 4 * g4 + i;
+            const float draw = __builtin_bit_cast(float, sizeof(T) == 2 ? dtr[u][rt][i] << 16 : dtr[u][rt][i]);
+            const float dtv = tok < L ? dt_post(draw, ph) : 0.0f;
+            fr[i] = dtv * exp2_fast(fminf(lend - lm[u][rt][i], 0.0f));
+          }
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          f32x4 t2;
+          zero4(t2);
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            Frag<T> sf;
+            frag_rows_swz<DS>(sf, tile, 32 * ks + 8 * g4, 32 * ks + 8 * g4 + 4, 16 * nt);
+            mma(t2, rf[u][rt][ks], sf);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) oacc[rt][nt][i] += fr[i] * t2[i];
+        }
+      }
+    }
+  }
+
+  if (!rows) return;
+  float *out = PNL == 0 ? a.dC[d] : a.dB[d];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 32 * wv + 16 * rt + 4 * g4 + i;
+      if (r >= qlen) continue;
+      float *o = out + ((((int64_t)b * L + t0 + r) * G + g) * N);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) o[16 * nt + r16] += oacc[rt][nt][i];
+    }
 }
 
 // ====================================================== decay gradients
@@ -501,8 +652,11 @@ __global__ __launch_bounds__(kThreads) void k_bwd_reduce(BwdArgs a) {
 template <typename T, int N>
 static void launch_panels_t(const BwdArgs &a, hipStream_t st) {
   dim3 g((unsigned)(a.Z * a.nchunks * 2 * a.G * (a.chunk / kRB)));
+  dim3 gs((unsigned)(a.Z * a.nchunks * 2 * a.G));
   hipLaunchKernelGGL((k_bwd_panel<T, N, 0>), g, dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((k_bwd_state<T, N, 0>), gs, dim3(kStThreads), 0, st, a);
   hipLaunchKernelGGL((k_bwd_panel<T, N, 1>), g, dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((k_bwd_state<T, N, 1>), gs, dim3(kStThreads), 0, st, a);
 }
 
 hipError_t launch_bwd_panels(const BwdArgs &a, hipStream_t st) {
