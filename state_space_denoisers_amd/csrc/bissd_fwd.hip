@@ -949,7 +949,12 @@ void k3_chunk_out(ScanArgs a) {
   const int j = (int)(bx & (uint32_t)(NRB - 1));  // NRB is 1, 2 or 4
   bx >>= __builtin_ctz((unsigned)NRB);
   bx = a.fd_nc.divmod(bx, rem);
-  const int c = (int)rem, b = (int)bx;
+  // the interior chunks of a batch row first, its two edge chunks (one carry-in
+  // direction each, so cheaper) last, so that a last partial round of
+  // workgroups is made of the cheaper ones
+  const int nc = a.nchunks, cp = (int)rem;
+  const int c = nc < 3 ? cp : (cp < nc - 2 ? cp + 1 : (cp == nc - 2 ? 0 : nc - 1));
+  const int b = (int)bx;
   const int64_t t0 = (int64_t)c * Q;
   const int qlen = (int)((L - t0) < Q ? (L - t0) : Q);
   if (j * kRB >= qlen) return;
