@@ -1606,13 +1606,31 @@ bool gram_in_k1(int H, int G, int chunk) {
   return hpg / HT >= nrb * (nrb + 1) / 2;
 }
 
+// Compute units of the current device (queried once per device; 0 if the
+// query fails).
+static int cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
 hipError_t launch_scan_phase(const ScanArgs &args, int phase, hipStream_t st) {
   // Heads of one tile share their B/C group: 2 heads when the heads per
   // group are even, else 1.  The dy.y_d pass (two products per stage) takes
   // one head per tile: with two, its accumulators leave too few registers
-  // for four waves per SIMD without spilling.
+  // for four waves per SIMD without spilling.  So does the output pass of a
+  // small problem, whose one-head workgroups fill at most half of the
+  // compute units' slots: twice the workgroups, each on a shorter path.
   const int hpg = args.H / args.G;
-  const int HT = (hpg % 2 == 0 && phase != PHASE_YDOT) ? 2 : 1;
+  const int64_t items2 = (int64_t)args.Z * args.nchunks * (args.chunk / kRB) * (args.H / 2);
+  const bool small = phase == PHASE_CHUNK_OUT && 2 * items2 <= 2 * (int64_t)cu_count();
+  const int HT = (hpg % 2 == 0 && phase != PHASE_YDOT && !small) ? 2 : 1;
   ScanArgs a = args;
   const int nrb = a.chunk / kRB;
   a.fd_tiles = FastDiv((uint32_t)(a.H / HT));
