@@ -1625,16 +1625,17 @@ hipError_t launch_scan_phase(const ScanArgs &args, int phase, hipStream_t st) {
   // group are even, else 1.  The dy.y_d pass (two products per stage) takes
   // one head per tile: with two, its accumulators leave too few registers
   // for four waves per SIMD without spilling.  So do the chunk-state and
-  // output passes of a small problem, whose one-head workgroups number at
-  // most twice the compute units: twice the workgroups, each on a shorter
-  // path.  (Whether the chunk-state kernel forms the Gram tiles is decided
-  // for two-head tiles, which one-head tiles cover too.)
+  // output passes of a problem whose one-head workgroups still run in one
+  // round (three per compute unit for the chunk states, four for the
+  // output): twice the workgroups, each on a shorter path.  (Whether the
+  // chunk-state kernel forms the Gram tiles is decided for two-head tiles,
+  // which one-head tiles cover too.)
   const int hpg = args.H / args.G;
   const int64_t ncu = cu_count();
   const int64_t items2 = (int64_t)args.Z * args.nchunks * (args.chunk / kRB) * (args.H / 2);
   const int64_t items1 = (int64_t)args.Z * args.nchunks * args.ndir * (args.H / 2);
-  const bool small = (phase == PHASE_CHUNK_OUT && 2 * items2 <= 2 * ncu) ||
-                     (phase == PHASE_CHUNK_STATE && 2 * items1 <= 2 * ncu);
+  const bool small = (phase == PHASE_CHUNK_OUT && 2 * items2 <= 4 * ncu) ||
+                     (phase == PHASE_CHUNK_STATE && 2 * items1 <= 3 * ncu);
   const int HT = (hpg % 2 == 0 && phase != PHASE_YDOT && !small) ? 2 : 1;
   ScanArgs a = args;
   const int nrb = a.chunk / kRB;
