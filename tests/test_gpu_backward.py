@@ -108,6 +108,17 @@ def test_train_L2k_full():
     check(inp, "bf16", w.chunk)
 
 
+def test_two_head_tiles_fp32():
+    """fp32 at Z=8, L=1024, 24 heads, N=128, chunk 256: a size at which the
+    chunk-state pass runs two heads per workgroup (problems that fit one round
+    of one-head workgroups run one); every gradient against the oracle on
+    batch rows 0 and 5."""
+    w = W["train_L2k"].replace(Z=8, L=1024, dtype="fp32")
+    inp = gen.make_inputs(w, with_dy=True)
+    print("bwd two-head tiles fp32", flush=True)
+    check(inp, "fp32", w.chunk, rows=[0, 5])
+
+
 def test_extreme_decays_fp32():
     """Large dt A (decays underflow inside a chunk) and dt = 0 tokens."""
     w = W["tiny_fp32"].replace(L=256, Z=1, chunk=128)

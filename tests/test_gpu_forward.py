@@ -50,6 +50,21 @@ def test_layer130m_L1k(mode):
     assert err <= TOL["bf16"], err
 
 
+def test_two_head_tiles_fp32():
+    """fp32 at the layer130m_L1k shape (Z=8, L=1024, 24 heads, N=128, chunk
+    256): here the chunk-state and output passes run two heads per workgroup
+    (problems that fit one round of one-head workgroups run one); the oracle
+    checks batch rows 0 and 5."""
+    w = W["layer130m_L1k"].replace(dtype="fp32")
+    inp = gen.make_inputs(w)
+    print("layer130m_L1k fp32", flush=True)
+    g = gpu_forward(inp, "fp32", w.chunk)
+    rows = [0, 5]
+    r = O.forward(select_rows(inp, rows))
+    err = maxrel(g[rows], r)
+    assert err <= TOL["fp32"], err
+
+
 @pytest.mark.parametrize("mode", ("full", "fwd", "rev"))
 def test_long_L65k_sampled_heads(mode):
     """L=65536 (256 chunks): the GPU runs every head; the oracle checks heads
