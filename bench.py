@@ -7,7 +7,9 @@ A step is one bissd_forward call (chunk states -> carry pass -> fused
 bidirectional output) over the 130M-class layer workload: batch 8, L=1024,
 24 heads x head dim 64, d_state 128, one B/C group, chunk 256, bf16 inputs
 with fp32 accumulation, synthetic seeded inputs already resident in HBM.
-W untimed warm-up steps, then exactly K timed steps between two device
+Untimed calls for --settle seconds (default 0.5: a GPU that has been idle
+runs its first milliseconds of work below its sustained clocks), W untimed
+warm-up steps, then exactly K timed steps between two device
 synchronisations; `value` is tokens per second over the timed region.
 
 The same run also measures, live with HIP events on the launch stream, the
@@ -19,7 +21,8 @@ times the fp64 CPU oracle on a bounded sample of the same workload.  One
 JSON line is printed.
 
 Profiling helpers (for rocprofv3 runs):
-    python bench.py --profile-phase {0,1,2,3,all,backward,block} [--workload W] [--iters R]
+    python bench.py --profile-phase {0,1,2,3,all,backward,block,attention} [--workload W]
+        [--iters R] [--settle S]   (S seconds of a bf16 matrix product first)
     python bench.py --copy-calibrate
 """
 from __future__ import annotations
@@ -129,10 +132,14 @@ def gram_in_chunk_state_kernel(w) -> bool:
 
 
 def phase_times_us(f: Forward, reps):
-    """Average duration of each forward kernel inside complete forward calls:
-    every call is enqueued as its four phases with a HIP event recorded
-    between them on the launch stream, so each kernel runs in the same
-    context (caches, preceding kernels) as in the timed region."""
+    """Average duration of each forward kernel inside complete forward calls,
+    without markers between the kernels: the growing prefixes of a call
+    (first phase; first two; ...) are each enqueued reps times back to back
+    between two HIP events on the launch stream, and a kernel's time is the
+    difference of two consecutive prefixes.  Every kernel so runs right after
+    the same predecessors as in a complete call (caches, preceding kernels);
+    back-to-back forward kernels leave no measurable gap between them, so the
+    differences are the kernels' own durations."""
     import torch
     f()
     torch.cuda.synchronize()
@@ -141,19 +148,23 @@ def phase_times_us(f: Forward, reps):
     names = dict(PHASE_NAMES)
     if 3 not in order:
         names[0] = "k1_chunk_state+gram"
-    n = len(order)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(reps)]
-    for r in range(reps):
-        evs[r][0].record(s)
-        for i, p in enumerate(order):
+    pref = []
+    for n in range(1, len(order) + 1):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for p in order[:n]:  # one untimed pass of this prefix
             f.phase(p)
-            evs[r][i + 1].record(s)
-    torch.cuda.synchronize()
-    tot = [0.0] * n
-    for r in range(reps):
-        for i in range(n):
-            tot[i] += evs[r][i].elapsed_time(evs[r][i + 1])
-    return {names[p]: 1e3 * tot[i] / reps for i, p in enumerate(order)}
+        a.record(s)
+        for _ in range(reps):
+            for p in order[:n]:
+                f.phase(p)
+        b.record(s)
+        torch.cuda.synchronize()
+        pref.append(a.elapsed_time(b) / reps)
+    out, prev = {}, 0.0
+    for n, p in enumerate(order):
+        out[names[p]] = 1e3 * (pref[n] - prev)
+        prev = pref[n]
+    return out
 
 
 def per_token_bytes(w):
@@ -249,6 +260,7 @@ def bench_long(steps):
     for _ in range(2):
         f()
     torch.cuda.synchronize()
+    settle(f, LEG_SETTLE_S)
     ms = event_time_ms(f, steps)
     ph = phase_times_us(f, max(3, steps // 2))
     return {"workload": w.name, "tokens_per_s": w.tokens / (ms * 1e-3), "ms_per_call": ms,
@@ -296,6 +308,7 @@ def bench_block(reps):
         for _ in range(5):
             upd(commit)
         torch.cuda.synchronize()
+        settle(lambda: upd(commit), LEG_SETTLE_S)
         ms = event_time_ms(lambda: upd(commit), reps)
         key = "commit" if commit else "no_commit"
         # eager calls from Python: bounded by host submission for a call this small
@@ -373,6 +386,7 @@ def bench_train(steps, rev_block=0):
     for _ in range(3):
         t()
     torch.cuda.synchronize()
+    settle(t, LEG_SETTLE_S)
     ms_f = event_time_ms(t.f, steps)
     ms_b = event_time_ms(t.backward, steps)
     ms = event_time_ms(t, steps)
@@ -407,6 +421,7 @@ def bench_attention(reps, Z=8, L=1024, H=12, block=0):
     for _ in range(3):
         fn()
     torch.cuda.synchronize()
+    settle(fn, LEG_SETTLE_S)
     ms = event_time_ms(fn, reps)
     fl = attention_flops(Z, L, H, block)
     return {"workload": f"attention_L{L // 1024}k" + (f"_block{block}" if block else ""),
@@ -433,6 +448,7 @@ def bench_attention_backward(reps, Z=8, L=1024, H=12, block=0):
     for _ in range(3):
         fn()
     torch.cuda.synchronize()
+    settle(fn, LEG_SETTLE_S)
     ms = event_time_ms(fn, reps)
     fl = attention_flops(Z, L, H, block) * 10 // 4
     return {"workload": f"attention_bwd_L{L // 1024}k" + (f"_block{block}" if block else ""),
@@ -468,6 +484,7 @@ def bench_latency_sweep(lengths=(1024, 4096, 16384, 65536, 262144)):
             fn()
         torch.cuda.synchronize()
         reps = max(5, min(200, int(2e6 // L)))
+        settle(fn, LEG_SETTLE_S)
         pts.append((L, event_time_ms(fn, reps)))
         del T, y, ws
     Ls = np.array([q[0] for q in pts], dtype=np.float64)
@@ -540,6 +557,7 @@ def bench_generation(steps_per_block=8, blocks=2, prefix=65536):
     for fn in (run_full, run_cached):
         fn()
     torch.cuda.synchronize()
+    settle(run_cached, LEG_SETTLE_S)
     ms_full = event_time_ms(run_full, 3)
     ms_cached = event_time_ms(run_cached, 10)
     nstep = blocks * steps_per_block
@@ -556,7 +574,34 @@ def bench_generation(steps_per_block=8, blocks=2, prefix=65536):
 
 # ------------------------------------------------------------- profiling
 
+LEG_SETTLE_S = 0.2  # untimed calls before each further leg's timing
+
+
+def settle(fn, seconds):
+    """Untimed calls of fn for at least `seconds`: a GPU that has been idle
+    runs its first milliseconds of work below its sustained clocks."""
+    import torch
+    t = time.perf_counter()
+    while time.perf_counter() - t < seconds:
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+
+
+def settle_with_gemm(seconds):
+    """The same for profiling runs, with a plain bf16 matrix product (a kernel
+    of another library, left out of the committed summaries)."""
+    import torch
+    a = torch.randn(4096, 4096, dtype=torch.bfloat16, device="cuda")
+    b = torch.randn(4096, 4096, dtype=torch.bfloat16, device="cuda")
+    settle(lambda: torch.mm(a, b), seconds)
+
+
 def profile_phase(args):
+    """Kernel launches for rocprofv3.  With --settle S, the profiled call
+    itself runs for S seconds first (the block update: a matrix product),
+    so the profile sees the GPU at its sustained clocks; those calls are part
+    of the statistics."""
     import torch
     from synth import gen
     if args.profile_phase == "attention":
@@ -570,11 +615,14 @@ def profile_phase(args):
         dout = gen.as_torch(gen.make_attention_inputs(Z, L, H, "bf16", 2003)["q"], "bf16", dev)
         lse = torch.empty((Z, H, L), dtype=torch.float32, device=dev)
         o = torch.empty_like(T["q"])
+        def fb():
+            ssd.bissd_attention_forward(T["q"], T["k"], T["v"], o=o, lse=lse)
+            ssd.bissd_attention_backward(T["q"], T["k"], T["v"], o, dout, lse)
+        settle(fb, args.settle)
         torch.cuda.synchronize()
         print(f"profiling attention forward + backward Z={Z} L={L} H={H} x{args.iters}", flush=True)
         for _ in range(args.iters):
-            ssd.bissd_attention_forward(T["q"], T["k"], T["v"], o=o, lse=lse)
-            ssd.bissd_attention_backward(T["q"], T["k"], T["v"], o, dout, lse)
+            fb()
         torch.cuda.synchronize()
         print("done", flush=True)
         return
@@ -584,6 +632,8 @@ def profile_phase(args):
         inp, T = device_inputs(w)
         fwd, rev = dirs(T)
         state = torch.zeros((w.Z, w.H, w.P, w.N), dtype=torch.float32, device=T["x"].device)
+        if args.settle > 0:
+            settle_with_gemm(args.settle)
         torch.cuda.synchronize()
         print(f"profiling block update on {w.name} x{args.iters}", flush=True)
         for _ in range(args.iters):
@@ -593,6 +643,7 @@ def profile_phase(args):
         return
     if args.profile_phase == "backward":
         t = Train(w)
+        settle(t.backward, args.settle)
         torch.cuda.synchronize()
         print(f"profiling backward on {w.name} x{args.iters}", flush=True)
         for _ in range(args.iters):
@@ -602,6 +653,8 @@ def profile_phase(args):
         return
     f = Forward(w)
     f()
+    if args.profile_phase == "all":
+        settle(f, args.settle)
     torch.cuda.synchronize()
     print(f"profiling {args.profile_phase} on {w.name} x{args.iters}", flush=True)
     for _ in range(args.iters):
@@ -638,7 +691,11 @@ def main():
     ap.add_argument("--copy-calibrate", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--settle", type=float, default=None,
+                    help="seconds of untimed work before the warm-up steps (default 0.5; 0 for --profile-phase)")
     args = ap.parse_args()
+    if args.settle is None:
+        args.settle = 0.0 if args.profile_phase is not None else 0.5
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -656,6 +713,7 @@ def main():
     w = gen.WORKLOADS["layer130m_L1k"]
     log(f"bench: {w.name} Z={w.Z} L={w.L} H={w.H} P={w.P} N={w.N} chunk={w.chunk} {w.dtype}")
     f = Forward(w)
+    settle(f, args.settle)
     for _ in range(args.warmup):
         f()
     torch.cuda.synchronize()
@@ -692,7 +750,13 @@ def main():
                 "frac": round(fl / (ph[PHASE_NAMES[2]] * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
                 "flops_per_launch": fl}
 
-    extra = {"kernels_us": {k: round(v, 2) for k, v in ph.items()},
+    # five further trials of the same workload (event-timed on the launch
+    # stream), for their median and spread next to the timed region above
+    trials = [event_time_ms(f, max(20, args.steps // 4)) * 1e3 for _ in range(5)]
+    extra = {"settle_s": args.settle,
+             "kernels_us": {k: round(v, 2) for k, v in ph.items()},
+             "trials_us_per_step": {"values": [round(t, 2) for t in trials],
+                                    "median": round(float(sorted(trials)[2]), 2)},
              "path_hbm_algorithmic_GBs": round(per_token_bytes(w) * tokens / (ev_ms * 1e-3) / 1e9, 1),
              "k3_mfma": mfma}
     if not args.no_extra:
