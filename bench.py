@@ -13,12 +13,13 @@ warm-up steps, then exactly K timed steps between two device
 synchronisations; `value` is tokens per second over the timed region.
 
 The same run also measures, live with HIP events on the launch stream, the
-average duration of each of the four kernels inside complete forward calls
-(enqueued phase by phase through bissd_forward_phase), the
+average duration of each forward kernel (differences of growing prefixes of
+a forward call, enqueued back to back through bissd_forward_phase), the
 long-context L=65536 scan, the training step (forward + backward, batch 16,
-L=2048), and the block update with a cached 262,144-token prefix state; and
-times the fp64 CPU oracle on a bounded sample of the same workload.  One
-JSON line is printed.
+L=2048), the block update with a cached 262,144-token prefix state, the
+generation loop, a latency sweep and the hybrids' attention layer; and times
+the fp64 CPU oracle on a bounded sample of the same workload.  One JSON line
+is printed.
 
 Profiling helpers (for rocprofv3 runs):
     python bench.py --profile-phase {0,1,2,3,all,backward,block,attention} [--workload W]
