@@ -13,10 +13,11 @@ with softplus(z) = log(1 + e^z).  Its reverse mode for an incoming ddt:
     draw = ddt * sigmoid(z) * [lo <= softplus(z) <= hi],   dbias[h] = sum_{b,t} draw
 
 (the clamp passes the gradient where the value lies inside [lo, hi], ends
-included).  numpy float64; the scan itself stays in ssd_oracle.c.  The
-inside-the-clamp decision is an integer taken from floating point, so it is
-taken in the kernels' precision: softplus in float32 of the float32 sum
-raw + bias.
+included: there the clamp is the identity on its argument).  numpy float64
+throughout; the forward value and the backward's pass/stop decision come
+from the one helper `inside`, so the two always agree: the gradient passes
+exactly where the clamped value is the softplus itself.  The scan stays in
+ssd_oracle.c.
 """
 from __future__ import annotations
 
@@ -27,18 +28,28 @@ def softplus(z):
     return np.logaddexp(0.0, z)
 
 
+def preact(raw, bias) -> np.ndarray:
+    """z = raw + bias[h] in float64 (raw [Z, L, H], bias [H])."""
+    return np.asarray(raw, np.float64) + np.asarray(bias, np.float64)[None, None, :]
+
+
+def inside(z, lo: float, hi: float) -> np.ndarray:
+    """Where the clamp is the identity: lo <= softplus(z) <= hi (fp64)."""
+    sp = softplus(z)
+    return (sp >= lo) & (sp <= hi)
+
+
 def forward(raw, bias, lo: float, hi: float) -> np.ndarray:
-    z = np.asarray(raw, np.float64) + np.asarray(bias, np.float64)[None, None, :]
-    return np.clip(softplus(z), lo, hi)
+    z = preact(raw, bias)
+    sp = softplus(z)
+    keep = inside(z, lo, hi)
+    return np.where(keep, sp, np.where(sp < lo, lo, hi))
 
 
 def backward(raw, bias, lo: float, hi: float, ddt):
     """(draw, dbias) for the gradient ddt with respect to the clamped dt."""
-    z = np.asarray(raw, np.float64) + np.asarray(bias, np.float64)[None, None, :]
-    z32 = (np.asarray(raw, np.float32) + np.asarray(bias, np.float32)[None, None, :]).astype(np.float32)
-    sp32 = np.maximum(z32, np.float32(0)) + np.log1p(np.exp(-np.abs(z32)))
-    keep = (sp32 >= np.float32(lo)) & (sp32 <= np.float32(hi))
-    draw = np.asarray(ddt, np.float64) * (1.0 / (1.0 + np.exp(-z))) * keep
+    z = preact(raw, bias)
+    draw = np.asarray(ddt, np.float64) * (1.0 / (1.0 + np.exp(-z))) * inside(z, lo, hi)
     return draw, draw.sum(axis=(0, 1))
 
 

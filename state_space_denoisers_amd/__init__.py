@@ -80,6 +80,95 @@ def _ptr(t: Optional[torch.Tensor]):
     return t.data_ptr()
 
 
+# ------------------------------------------------------------ validation
+#
+# The C library sizes every buffer from x's dtype and from the shapes of x
+# and B, so a tensor of another dtype, shape or device would be read or
+# written past its end.  Every entry point below checks its tensors first:
+# shapes and dtypes, then that every tensor lives on x's GPU.  Nothing is
+# launched when a check fails.
+
+def _need(t, name: str, shape, dtype) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _on_device(named: dict, device: torch.device) -> None:
+    """Every given tensor is a CUDA (HIP) tensor on `device`."""
+    if device.type != "cuda":
+        raise ValueError(f"x must be a GPU tensor, got device {device}")
+    for name, t in named.items():
+        if t is not None and t.device != device:
+            raise ValueError(f"{name} is on {t.device}, expected {device} (the device of x)")
+
+
+def _scan_dims(x: torch.Tensor, B: torch.Tensor):
+    if not isinstance(x, torch.Tensor) or x.dim() != 4:
+        raise ValueError("x must be a 4-D tensor [Z, L, H, P]")
+    _dtype_code(x)
+    if not isinstance(B, torch.Tensor) or B.dim() != 4:
+        raise ValueError("B must be a 4-D tensor [Z, L, G, N]")
+    Z, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    if G <= 0 or H % G != 0:
+        raise ValueError(f"nheads ({H}) must be a multiple of ngroups ({G})")
+    return Z, L, H, P, G, N
+
+
+def _check_dir(d: "Dir", tag: str, x: torch.Tensor, G: int, N: int, named: dict) -> None:
+    Z, L, H, _ = x.shape
+    _need(d.dt, f"{tag}.dt", (Z, L, H), x.dtype)
+    _need(d.A, f"{tag}.A", (H,), torch.float32)
+    _need(d.B, f"{tag}.B", (Z, L, G, N), x.dtype)
+    _need(d.C, f"{tag}.C", (Z, L, G, N), x.dtype)
+    if d.dt_bias is not None:
+        _need(d.dt_bias, f"{tag}.dt_bias", (H,), torch.float32)
+    for k in ("dt", "A", "B", "C", "dt_bias"):
+        named[f"{tag}.{k}"] = getattr(d, k)
+
+
+def _check_scan(x, fwd: "Dir", rev: "Dir", D, *, states=(), acts=(), outs=()) -> dict:
+    """Validate the tensors of one scan call; returns them by name.
+    states: (name, tensor) pairs of [Z, H, P, N] fp32 states (None allowed);
+    acts: (name, tensor) pairs shaped and typed like x; outs: (name, tensor,
+    shape, dtype) of caller-given outputs (None allowed)."""
+    Z, L, H, P, G, N = _scan_dims(x, fwd.B)
+    named = {"x": x}
+    _check_dir(fwd, "fwd", x, G, N, named)
+    _check_dir(rev, "rev", x, G, N, named)
+    _need(D, "D", (H,), torch.float32)
+    named["D"] = D
+    for name, t in states:
+        if t is not None:
+            _need(t, name, (Z, H, P, N), torch.float32)
+            named[name] = t
+    for name, t in acts:
+        if t is not None:
+            _need(t, name, tuple(x.shape), x.dtype)
+            named[name] = t
+    for name, t, shp, dt in outs:
+        if t is not None:
+            _need(t, name, shp, dt)
+            named[name] = t
+    _on_device(named, x.device)
+    return named
+
+
+def _check_workspace(ws, device) -> None:
+    if ws is None:
+        return
+    if not isinstance(ws, torch.Tensor) or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor")
+    if ws.device != device:
+        raise ValueError(f"workspace is on {ws.device}, expected {device}")
+
+
 def _dir(d) -> _abi.Dir:
     d = Dir(*d)
     if d.A.dtype != torch.float32:
@@ -100,11 +189,25 @@ def bissd_workspace_size(shape: _abi.Shape, op: int) -> int:
 
 
 def _workspace(shape, op, device, workspace):
+    """The caller's workspace, or a new one (allocated on the stream the call
+    runs on: see _on_stream)."""
     if workspace is not None:
+        _check_workspace(workspace, device)
         return workspace, workspace.numel() * workspace.element_size()
     n = bissd_workspace_size(shape, op)
     ws = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
     return ws, ws.numel()
+
+
+def _on_stream(device: torch.device, stream):
+    """Context under which a call allocates its outputs and workspace: the
+    caller's stream when one is given, so that torch's caching allocator
+    does not hand that memory to work on another stream while the library's
+    kernels still use it."""
+    import contextlib
+    if stream is None:
+        return contextlib.nullcontext()
+    return torch.cuda.stream(stream)
 
 
 def bissd_forward(x: torch.Tensor, fwd, rev, D: torch.Tensor, *, chunk: int = 256,
@@ -116,10 +219,13 @@ def bissd_forward(x: torch.Tensor, fwd, rev, D: torch.Tensor, *, chunk: int = 25
     tokens (the block-segmented reverse of full-block training)."""
     lib = _abi.load()
     fwd, rev = Dir(*fwd), Dir(*rev)
+    _check_scan(x, fwd, rev, D, states=(("init_state", init_state), ("final_state", final_state)),
+                acts=(("y", y),))
     shape = shape_of(x, fwd.B, chunk, rev_block)
-    if y is None:
-        y = torch.empty_like(x)
-    ws, nws = _workspace(shape, _abi.OP_FORWARD, x.device, workspace)
+    with _on_stream(x.device, stream):
+        if y is None:
+            y = torch.empty_like(x)
+        ws, nws = _workspace(shape, _abi.OP_FORWARD, x.device, workspace)
     st = lib.bissd_forward(C.byref(shape), _ptr(x), _dir(fwd), _dir(rev), _ptr(D),
                            _ptr(init_state), _ptr(y), _ptr(final_state), _ptr(ws),
                            C.c_size_t(nws), _stream(x.device, stream))
@@ -135,6 +241,9 @@ def bissd_forward_phase(phase: int, x: torch.Tensor, fwd, rev, D: torch.Tensor, 
     2 output) for timing single kernels (include/bissd.h)."""
     lib = _abi.load()
     fwd, rev = Dir(*fwd), Dir(*rev)
+    _check_scan(x, fwd, rev, D, states=(("init_state", init_state), ("final_state", final_state)),
+                acts=(("y", y),))
+    _check_workspace(workspace, x.device)
     shape = shape_of(x, fwd.B, chunk, rev_block)
     st = lib.bissd_forward_phase(C.byref(shape), _ptr(x), _dir(fwd), _dir(rev), _ptr(D),
                                  _ptr(init_state), _ptr(y), _ptr(final_state), _ptr(workspace),
@@ -153,15 +262,18 @@ def bissd_block_update(state_in: torch.Tensor, x_blk: torch.Tensor, fwd, rev,
     ``commit`` is false and none was given."""
     lib = _abi.load()
     fwd, rev = Dir(*fwd), Dir(*rev)
+    _check_scan(x_blk, fwd, rev, D, states=(("state_in", state_in), ("state_out", state_out)),
+                acts=(("y_blk", y_blk),))
     L = x_blk.shape[1]
     if chunk is None:
         chunk = 64 if L <= 64 else (128 if L <= 128 else 256)
     shape = shape_of(x_blk, fwd.B, chunk)
-    if y_blk is None:
-        y_blk = torch.empty_like(x_blk)
-    if state_out is None and commit:
-        state_out = torch.empty_like(state_in)
-    ws, nws = _workspace(shape, _abi.OP_BLOCK, x_blk.device, workspace)
+    with _on_stream(x_blk.device, stream):
+        if y_blk is None:
+            y_blk = torch.empty_like(x_blk)
+        if state_out is None and commit:
+            state_out = torch.empty_like(state_in)
+        ws, nws = _workspace(shape, _abi.OP_BLOCK, x_blk.device, workspace)
     st = lib.bissd_block_update(C.byref(shape), _ptr(state_in), _ptr(x_blk), _dir(fwd),
                                 _dir(rev), _ptr(D), _ptr(y_blk), _ptr(state_out), _ptr(ws),
                                 C.c_size_t(nws), _stream(x_blk.device, stream))
@@ -182,27 +294,32 @@ def bissd_backward(x: torch.Tensor, fwd, rev, D: torch.Tensor, dy: torch.Tensor,
     preallocated tensors under those keys.  ``rev_block`` as in bissd_forward."""
     lib = _abi.load()
     fwd, rev = Dir(*fwd), Dir(*rev)
-    shape = shape_of(x, fwd.B, chunk, rev_block)
-    f32 = dict(dtype=torch.float32, device=x.device)
     g = dict(grads) if grads is not None else {}
-    if "dx" not in g:
-        g["dx"] = torch.empty(x.shape, **f32)
-    if "dD" not in g:
-        g["dD"] = torch.empty(D.shape, **f32)
+    Z, L, H, P, G, N = _scan_dims(x, fwd.B)
+    gshape = {"dx": (Z, L, H, P), "dD": (H,)}
     for d, p in (("f", fwd), ("r", rev)):
-        for k, like in (("ddt", p.dt), ("dA", p.A), ("dB", p.B), ("dC", p.C)):
-            if f"{k}_{d}" not in g:
-                g[f"{k}_{d}"] = torch.empty(like.shape, **f32)
-        if p.dt_bias is not None and f"ddt_bias_{d}" not in g:
-            g[f"ddt_bias_{d}"] = torch.empty(p.dt_bias.shape, **f32)
-    for k in GRAD_KEYS:
-        if g[k].dtype != torch.float32:
-            raise TypeError(f"{k} must be float32")
+        gshape.update({f"ddt_{d}": (Z, L, H), f"dA_{d}": (H,), f"dB_{d}": (Z, L, G, N),
+                       f"dC_{d}": (Z, L, G, N)})
+        if p.dt_bias is not None:
+            gshape[f"ddt_bias_{d}"] = (H,)
+    unknown = set(g) - set(gshape)
+    if unknown:
+        raise ValueError(f"unexpected gradient buffers {sorted(unknown)}")
+    _check_scan(x, fwd, rev, D, states=(("init_state", init_state),), acts=(("dy", dy),),
+                outs=tuple((k, g.get(k), shp, torch.float32) for k, shp in gshape.items()))
+    if dy is None:
+        raise ValueError("dy is required")
+    shape = shape_of(x, fwd.B, chunk, rev_block)
+    with _on_stream(x.device, stream):
+        for k, shp in gshape.items():
+            if k not in g:
+                g[k] = torch.empty(shp, dtype=torch.float32, device=x.device)
     gf = _abi.Grad(_ptr(g["ddt_f"]), _ptr(g["dA_f"]), _ptr(g["dB_f"]), _ptr(g["dC_f"]),
                    _ptr(g.get("ddt_bias_f")))
     gr = _abi.Grad(_ptr(g["ddt_r"]), _ptr(g["dA_r"]), _ptr(g["dB_r"]), _ptr(g["dC_r"]),
                    _ptr(g.get("ddt_bias_r")))
-    ws, nws = _workspace(shape, _abi.OP_BACKWARD, x.device, workspace)
+    with _on_stream(x.device, stream):
+        ws, nws = _workspace(shape, _abi.OP_BACKWARD, x.device, workspace)
     st = lib.bissd_backward(C.byref(shape), _ptr(x), _dir(fwd), _dir(rev), _ptr(D),
                             _ptr(init_state), _ptr(dy), _ptr(g["dx"]), gf, gr, _ptr(g["dD"]),
                             _ptr(ws), C.c_size_t(nws), _stream(x.device, stream))
@@ -210,10 +327,22 @@ def bissd_backward(x: torch.Tensor, fwd, rev, D: torch.Tensor, dy: torch.Tensor,
     return g
 
 
-def _attn_shape(q, k, v, block):
+def _attn_shape(q, k, v, block, **more):
+    """ABI shape of q, k, v [Z, L, H, 64] after checking them and the further
+    tensors in `more` (name -> (tensor or None, shape, dtype))."""
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise ValueError("q must be a 4-D tensor [Z, L, H, 64]")
+    _dtype_code(q)
     Z, L, H, Dh = q.shape
-    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
-        raise ValueError("q, k and v must have one shape and dtype")
+    named = {"q": q}
+    for name, t in (("k", k), ("v", v)):
+        _need(t, name, tuple(q.shape), q.dtype)
+        named[name] = t
+    for name, (t, shp, dt) in more.items():
+        if t is not None:
+            _need(t, name, shp, dt)
+            named[name] = t
+    _on_device(named, q.device)
     return _abi.AttnShape(Z, L, H, Dh, int(block), _dtype_code(q), 0)
 
 
@@ -226,9 +355,12 @@ def bissd_attention_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *
     bidirectional attention, > 0 for block-wise; scale 0 for 1/sqrt(64).
     ``lse`` (fp32 [Z, H, L]) receives what the backward needs."""
     lib = _abi.load()
-    shape = _attn_shape(q, k, v, block)
-    if o is None:
-        o = torch.empty_like(q)
+    Z, L, H = q.shape[0], q.shape[1], q.shape[2]
+    shape = _attn_shape(q, k, v, block, o=(o, tuple(q.shape), q.dtype),
+                        lse=(lse, (Z, H, L), torch.float32))
+    with _on_stream(q.device, stream):
+        if o is None:
+            o = torch.empty_like(q)
     st = lib.bissd_attention_forward(C.byref(shape), _ptr(q), _ptr(k), _ptr(v), float(scale),
                                      _ptr(o), _ptr(lse), _stream(q.device, stream))
     _abi.check("bissd_attention_forward", st)
@@ -242,11 +374,17 @@ def bissd_attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     """dq, dk, dv (fp32) of sum(dout * o) for o, lse from bissd_attention_forward
     with the same arguments (include/bissd.h, bissd_attention_backward)."""
     lib = _abi.load()
-    shape = _attn_shape(q, k, v, block)
-    g = {n: torch.empty(q.shape, dtype=torch.float32, device=q.device) for n in ("dq", "dk", "dv")}
-    if workspace is None:
-        n = int(lib.bissd_attention_workspace_size(C.byref(shape)))
-        workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
+    Z, L, H = q.shape[0], q.shape[1], q.shape[2]
+    if o is None or dout is None or lse is None:
+        raise ValueError("o, dout and lse are required")
+    shape = _attn_shape(q, k, v, block, o=(o, tuple(q.shape), q.dtype),
+                        dout=(dout, tuple(q.shape), q.dtype), lse=(lse, (Z, H, L), torch.float32))
+    _check_workspace(workspace, q.device)
+    with _on_stream(q.device, stream):
+        g = {n: torch.empty(q.shape, dtype=torch.float32, device=q.device) for n in ("dq", "dk", "dv")}
+        if workspace is None:
+            n = int(lib.bissd_attention_workspace_size(C.byref(shape)))
+            workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
     st = lib.bissd_attention_backward(C.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                                       _ptr(dout), _ptr(lse), float(scale), _ptr(g["dq"]),
                                       _ptr(g["dk"]), _ptr(g["dv"]), _ptr(workspace),

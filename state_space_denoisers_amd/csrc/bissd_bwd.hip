@@ -362,6 +362,12 @@ __global__ __launch_bounds__(kStThreads) void k_bwd_state(BwdArgs a) {
   constexpr int NT = N / 16;
   constexpr int NWV = kStThreads / 64;
   using DS = DmaTile<SRB, SW_TR>;
+  // vector-memory instructions one head's issue() certainly adds per wave:
+  // the copy pieces, the row fragments (one 16-byte load each in bf16, two
+  // in fp32) and at least one load per row tile of decay sums
+  constexpr int kCopyPieces = kP / DS::RPP;
+  static_assert(kCopyPieces % NWV == 0, "every wave issues the same number of copy pieces");
+  constexpr int kNextMin = kCopyPieces / NWV + (sizeof(T) == 2 ? 4 : 8) + 2;
   __shared__ __attribute__((aligned(16))) char tiles[NS * STB];
   const int tid = threadIdx.x, wv = wave_id(), lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
   const int Q = a.chunk, H = a.H, G = a.G, hpg = H / G;
@@ -394,10 +400,20 @@ __global__ __launch_bounds__(kStThreads) void k_bwd_state(BwdArgs a) {
   Frag<T> rf[NS][2][2];
   f32x4 lm[NS][2];
   uint32_t dtr[NS][2][4];
+  // Issue order, pinned by compiler fences (no memory access moves across
+  // them, in the IR or in the machine scheduler): head after head, and in
+  // each head the state copy before the register loads.  The waits below
+  // count on it.
+  auto fence = []() __attribute__((always_inline)) {
+    asm volatile("" : : : "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
   auto issue = [&](int hi, int slot) __attribute__((always_inline)) {
     const int h = g * hpg + hi;
     const int64_t soff = (int64_t)b * a.st_bstride + (int64_t)c * a.st_cstride + (int64_t)h * kP * N;
+    fence();
     DS::load(tiles + slot * STB, make_buf(stsrc + soff, (uint32_t)(kP * N * ES)), 0u, (uint32_t)SRB, kP, wv, NWV);
+    fence();
     // every wave loads its rows, also past the chunk (the next chunk's
     // tokens, or zeros past L), so that every wave can wait for them
     {
@@ -440,9 +456,16 @@ __global__ __launch_bounds__(kStThreads) void k_bwd_state(BwdArgs a) {
     for (int u = 0; u < NS; ++u) {
       const int hi = hi0 + u;
       if (hi >= hpg) break;
-      // this head's register loads were issued after its state copy and
-      // loads complete in order, so waiting for them (here, before the
-      // barrier) covers the copy too, and leaves the later heads in flight
+      // This head's state copy (and its register loads) must be complete
+      // before the barrier.  Vector-memory loads complete in issue order,
+      // and the only loads issued after this head's are the next head's
+      // (NS = 3, when there is a next head): at least its copy pieces, its
+      // four (fp32: eight) row fragments and two decay-sum loads (the four
+      // per-token loads of each row tile may be merged into one).  Waiting
+      // until no more than that lower bound is outstanding covers this
+      // head's copy and leaves the next head in flight.
+      if (NS > 2 && hi + 1 < hpg) wait_vmem_le<kNextMin>();
+      else wait_vmem_le<0>();
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
 #pragma unroll

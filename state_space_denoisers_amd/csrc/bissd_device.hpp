@@ -600,6 +600,12 @@ __device__ __forceinline__ void frag_rows_swz(Frag<float> &f, const char *tile, 
 
 // vector-memory count 0, other counters left alone
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// vector-memory count at most K (gfx9 encoding: vmcnt bits 3:0 and 15:14,
+// expcnt 6:4 and lgkmcnt 11:8 at their maxima), other counters left alone
+template <int K> __device__ __forceinline__ void wait_vmem_le() {
+  static_assert(K >= 0 && K < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((K & 15) | ((K >> 4) << 14) | 0x0F70);
+}
 
 // ------------------------------------------------------- XCD-aware order
 //

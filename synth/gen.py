@@ -238,8 +238,42 @@ def with_dt_post(inp: dict, w: Workload, lo: float = 1e-3, hi: float = 0.1) -> d
     out = dict(inp)
     Z, L, H = inp["dt_f"].shape
     for d in ("f", "r"):
-        out[f"dt_{d}"] = quantize(_rng(w.seed, f"dtraw_{d}").standard_normal((Z, L, H)), w.dtype)
-        out[f"dt_bias_{d}"] = round_fp32(-w.dt_shift + 0.5 * _rng(w.seed, f"dtbias_{d}").standard_normal(H))
+        raw = quantize(_rng(w.seed, f"dtraw_{d}").standard_normal((Z, L, H)), w.dtype)
+        bias = round_fp32(-w.dt_shift + 0.5 * _rng(w.seed, f"dtbias_{d}").standard_normal(H))
+        out[f"dt_{d}"] = off_clamp_edges(raw, bias, lo, hi, w.dtype)
+        out[f"dt_bias_{d}"] = bias
         out[f"dt_min_{d}"], out[f"dt_max_{d}"] = lo, hi
     return out
+
+
+# Half-width of the band of pre-activations kept clear around each point
+# where the clamp engages.
+CLAMP_EDGE_BAND = 1e-4
+
+
+def off_clamp_edges(raw, bias, lo: float, hi: float, dtype: str,
+                    band: float = CLAMP_EDGE_BAND) -> np.ndarray:
+    """Move every pre-activation raw + bias that lies within `band` of one of
+    the two points where the clamp engages, z_lo = log(e^lo - 1) and
+    z_hi = log(e^hi - 1), to the nearest value of `dtype` that is at least
+    2 * band further away from that point.  Whether such a token sits inside
+    the clamp range is decided by a rounding (it depends on the precision the
+    step is formed in); everywhere else any precision decides alike."""
+    raw = np.array(raw, dtype=np.float64)
+    b = np.asarray(bias, np.float64)[None, None, :]
+    for edge in (lo, hi):
+        if not np.isfinite(edge) or edge <= 0.0:
+            continue
+        ze = math.log(math.expm1(edge))
+        z = raw + b
+        for idx in zip(*np.nonzero(np.abs(z - ze) < band)):
+            sgn = 1.0 if z[idx] >= ze else -1.0
+            step = 2.0 * band
+            while True:
+                cand = float(quantize(np.array([raw[idx] + sgn * step]), dtype)[0])
+                if abs(cand + b[0, 0, idx[2]] - ze) >= 2.0 * band:
+                    break
+                step *= 2.0
+            raw[idx] = cand
+    return raw
 

@@ -99,23 +99,28 @@ def test_layer_bf16(mode):
     check(inp, "bf16", w.chunk)
 
 
-def test_train_L2k_full():
+@pytest.mark.parametrize("mode", ("full", "scan"))
+def test_train_L2k_full(mode):
     """The training workload at full size (Z=16, L=2048, 24 heads, N=128,
-    chunk 256, bf16); every gradient against the oracle on every row."""
+    chunk 256, bf16); every gradient against the oracle on every row.  In
+    mode "scan" (D = 0) the scan part of dx is the whole of dx (with D it is
+    about 1% of it)."""
     w = W["train_L2k"]
-    inp = gen.make_inputs(w, with_dy=True)
-    print("bwd train_L2k", flush=True)
+    inp = gen.make_inputs(w, mode=mode, with_dy=True)
+    print("bwd train_L2k", mode, flush=True)
     check(inp, "bf16", w.chunk)
 
 
-def test_two_head_tiles_fp32():
+@pytest.mark.parametrize("mode", ("full", "scan", "fwd", "rev"))
+def test_two_head_tiles_fp32(mode):
     """fp32 at Z=8, L=1024, 24 heads, N=128, chunk 256: a size at which the
     chunk-state pass runs two heads per workgroup (problems that fit one round
     of one-head workgroups run one); every gradient against the oracle on
-    batch rows 0 and 5."""
+    batch rows 0 and 5, in every check mode ("fwd": C_r = 0, so only the
+    forward scan reaches y; "rev": C_f = 0)."""
     w = W["train_L2k"].replace(Z=8, L=1024, dtype="fp32")
-    inp = gen.make_inputs(w, with_dy=True)
-    print("bwd two-head tiles fp32", flush=True)
+    inp = gen.make_inputs(w, mode=mode, with_dy=True)
+    print("bwd two-head tiles fp32", mode, flush=True)
     check(inp, "fp32", w.chunk, rows=[0, 5])
 
 

@@ -190,3 +190,49 @@ def test_graph_replays_match_eager():
             torch.cuda.synchronize()
             assert torch.equal(y, y_ref)
         del g
+
+
+def test_state_out_may_alias_state_in_long_block():
+    """A 100-token block (chunk 128) runs the chunked kernels in the order
+    chunk state, Gram tiles, output, carry pass; the output reads state_in
+    before the carry pass overwrites it in place."""
+    w = W["block_update"].replace(Z=2, L=100, H=8, chunk=128, mask_count=8, seed=19)
+    for dtype in ("fp32", "bf16"):
+        inp = gen.make_inputs(w.replace(dtype=dtype))
+        S0 = gen.round_fp32(np.random.default_rng(4).standard_normal((2, 8, 64, 128)) * 0.05)
+        y, so = gpu_block(inp, dtype, S0, chunk=128, alias=True)
+        y2, so2 = gpu_block(inp, dtype, S0, chunk=128)
+        ry, rso = O.block_update(inp, S0)
+        assert maxrel(y, ry) <= TOL[dtype] and maxrel(so, rso) <= TOL[dtype]
+        assert np.array_equal(y, y2) and np.array_equal(so, so2)
+
+
+@pytest.mark.parametrize("dtype,Lb,chunk", [("fp32", 64, 64), ("fp32", 37, 64), ("fp32", 100, 128),
+                                            ("fp32", 256, 256), ("bf16", 64, 64), ("bf16", 23, 64),
+                                            ("bf16", 100, 128)])
+def test_block_update_closed_form_bit_exact(dtype, Lb, chunk):
+    """A = 0, B = C = e_0, dt = 1, integer x in {-1, 0, 1} and an integer
+    cached state: the forward part is the cached state's column 0 plus a
+    running sum over the block, the reverse part a running sum from the block
+    end (nothing enters from the right), and the committed state is the
+    cached one with the block's sum added to column 0 -- all integers, so bit
+    for bit, in place (state_out == state_in) and not."""
+    Z, H, N = 2, 4, 128
+    r = np.random.default_rng(Lb + chunk)
+    x = r.integers(-1, 2, (Z, Lb, H, 64)).astype(np.float64)
+    e0 = np.zeros((Z, Lb, 1, N))
+    e0[..., 0] = 1.0
+    inp = {"x": x, "D": np.zeros(H)}
+    for d in ("f", "r"):
+        inp[f"dt_{d}"] = np.ones((Z, Lb, H))
+        inp[f"A_{d}"] = np.zeros(H)
+        inp[f"B_{d}"] = e0
+        inp[f"C_{d}"] = e0
+    S0 = r.integers(-40, 41, (Z, H, 64, N)).astype(np.float64)
+    ey = S0[:, None, :, :, 0] + np.cumsum(x, 1) + np.cumsum(x[:, ::-1], 1)[:, ::-1]
+    eso = S0.copy()
+    eso[..., 0] += x.sum(1)
+    for alias in (False, True):
+        y, so = gpu_block(inp, dtype, S0, chunk=chunk, alias=alias)
+        assert np.array_equal(y, ey), alias
+        assert np.array_equal(so, eso), alias

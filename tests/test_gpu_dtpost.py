@@ -3,7 +3,11 @@ mixer's pre-activation with a per-head bias: the kernels read
 clamp(softplus(dt + bias), lo, hi)) against the fp64 oracle, which applies the
 same map before its scan: forward, block-segmented forward, block update and
 backward (including the pre-activation and bias gradients).
-Tolerance: max|gpu - oracle| / max|oracle| <= 1e-4 (fp32), 2e-2 (bf16).
+Tolerance: max|gpu - oracle| / max|oracle| <= 1e-4 (fp32), 2e-2 (bf16), on
+every output, the bias gradients included.  The inputs keep every
+pre-activation clear of the two points where the clamp engages (synth.gen's
+off_clamp_edges), where the in-range decision would depend on the precision
+the step is formed in.
 """
 import math
 
@@ -78,12 +82,6 @@ def test_backward(dtype, L, chunk, rb):
         gb, graw = host(g[f"ddt_bias_{d}"]), host(g[f"ddt_{d}"])
         # the bias gradient is the fixed-order sum of the pre-activation ddt
         assert maxrel(gb, graw.sum(axis=(0, 1))) <= 1e-5
-        if dtype == "bf16":
-            # a sum whose terms cancel (sum |ddt| is 10-40x |sum ddt| here):
-            # the bar applies to the scale of its terms, as for every per-token ddt
-            scale = np.abs(ref[f"ddt_{d}"]).sum(axis=(0, 1))
-            assert np.all(np.abs(gb - ref[f"ddt_bias_{d}"]) <= TOL[dtype] * scale), d
-            errs.pop(f"ddt_bias_{d}")
     bad = {k: v for k, v in errs.items() if v > TOL[dtype]}
     assert not bad, (bad, errs)
 

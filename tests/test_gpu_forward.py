@@ -50,14 +50,15 @@ def test_layer130m_L1k(mode):
     assert err <= TOL["bf16"], err
 
 
-def test_two_head_tiles_fp32():
+@pytest.mark.parametrize("mode", MODES)
+def test_two_head_tiles_fp32(mode):
     """fp32 at the layer130m_L1k shape (Z=8, L=1024, 24 heads, N=128, chunk
     256): here the chunk-state and output passes run two heads per workgroup
     (problems that fit one round of one-head workgroups run one); the oracle
-    checks batch rows 0 and 5."""
+    checks batch rows 0 and 5, in every check mode."""
     w = W["layer130m_L1k"].replace(dtype="fp32")
-    inp = gen.make_inputs(w)
-    print("layer130m_L1k fp32", flush=True)
+    inp = gen.make_inputs(w, mode=mode)
+    print("layer130m_L1k fp32", mode, flush=True)
     g = gpu_forward(inp, "fp32", w.chunk)
     rows = [0, 5]
     r = O.forward(select_rows(inp, rows))
@@ -242,3 +243,91 @@ def test_phases_compose(dtype, L):
     ssd.bissd_forward_phase(2, T["x"], fwd, rev, T["D"], chunk=256, y=y, workspace=ws)
     torch.cuda.synchronize()
     assert np.array_equal(host(y), full)
+
+
+def flipped(inp: dict) -> dict:
+    """The flip invariant's inputs: time reversed, with the two directions'
+    parameters exchanged (x and dy flipped along time as well)."""
+    out = {"x": inp["x"][:, ::-1].copy(), "D": inp["D"]}
+    for a, b in (("f", "r"), ("r", "f")):
+        for k in ("dt", "B", "C"):
+            out[f"{k}_{a}"] = inp[f"{k}_{b}"][:, ::-1].copy()
+        out[f"A_{a}"] = inp[f"A_{b}"]
+    return out
+
+
+@pytest.mark.parametrize("dtype,L,chunk", [("fp32", 1000, 256), ("bf16", 1000, 256),
+                                           ("fp32", 333, 64)])
+def test_flip_swaps_the_directions(dtype, L, chunk):
+    """Reversing time and exchanging the two directions' parameters reverses
+    y: the reverse scan is the forward scan of the flipped sequence.  The two
+    GPU results agree with each other and with the oracle."""
+    w = W["layer130m_L1k"].replace(Z=2, L=L, H=8, chunk=chunk, dtype=dtype, seed=90 + L)
+    for mode in ("scan", "fwd"):
+        inp = gen.make_inputs(w, mode=mode)
+        print("flip", dtype, L, chunk, mode, flush=True)
+        g = gpu_forward(inp, dtype, chunk)
+        gf = gpu_forward(flipped(inp), dtype, chunk)
+        assert maxrel(gf[:, ::-1], g) <= TOL[dtype]
+        assert maxrel(gf, O.forward(flipped(inp))) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("mode", ("fwd", "rev"))
+def test_long_L262k_sampled_heads(mode):
+    """L=262,144 (1,024 chunks), the long end of the pages' context range:
+    the GPU runs all 24 heads; the oracle checks heads 5 and 20 over the
+    whole sequence."""
+    w = W["long_L65k"].replace(L=262144, seed=1005)
+    print("long_L262k", mode, "inputs", flush=True)
+    inp = gen.make_inputs(w, mode=mode)
+    print("long_L262k", mode, "gpu", flush=True)
+    g = gpu_forward(inp, "bf16", w.chunk)
+    hs = [5, 20]
+    sub = select_heads(inp, hs)
+    del inp
+    print("long_L262k", mode, "oracle", flush=True)
+    r = O.forward(sub)
+    err = maxrel(g[:, :, hs], r)
+    assert err <= TOL["bf16"], err
+
+
+@pytest.mark.parametrize("dtype,L,chunk,rb", [("fp32", 1000, 64, 64), ("fp32", 1000, 128, 64),
+                                              ("fp32", 1000, 256, 128), ("fp32", 1000, 256, 512),
+                                              ("fp32", 1000, 128, 256), ("bf16", 128, 128, 64),
+                                              ("bf16", 128, 64, 64)])
+def test_closed_form_segmented_reverse_bit_exact(dtype, L, chunk, rb):
+    """A = 0, B = C = e_0, dt = 1 with the block-segmented reverse: the
+    forward part is a running sum over the whole sequence and the reverse part
+    a running sum from the end of each token's own block of rb tokens, bit for
+    bit (every block boundary indexed exactly)."""
+    import state_space_denoisers_amd as ssd
+    inp = closed_form_inputs(2, L, 4, 128, seed=L + chunk + rb)
+    T = to_dev(inp, dtype)
+    y = ssd.bissd_forward(T["x"], *dirs(T), T["D"], chunk=chunk, rev_block=rb)
+    g = host(y)
+    x = inp["x"]
+    yr = np.zeros_like(x)
+    for k0 in range(0, L, rb):
+        blk = x[:, k0:k0 + rb]
+        yr[:, k0:k0 + rb] = np.cumsum(blk[:, ::-1], 1)[:, ::-1]
+    expect = np.cumsum(x, 1) + yr
+    assert np.array_equal(g, expect)
+
+
+def test_caller_stream():
+    """A call on a caller's stream that is not the current one allocates its
+    output and workspace on that stream and gives the same y, bit for bit."""
+    import torch
+    import state_space_denoisers_amd as ssd
+    w = W["layer130m_L1k"].replace(Z=2, L=700, H=8, seed=57)
+    inp = gen.make_inputs(w)
+    T = to_dev(inp, "bf16")
+    y0 = ssd.bissd_forward(T["x"], *dirs(T), T["D"], chunk=256)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    ys = [ssd.bissd_forward(T["x"], *dirs(T), T["D"], chunk=256, stream=s) for _ in range(3)]
+    s.synchronize()
+    for y in ys:
+        assert torch.equal(y, y0)
+    assert maxrel(host(y0), O.forward(inp)) <= TOL["bf16"]

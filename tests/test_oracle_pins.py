@@ -552,3 +552,61 @@ def test_dt_post_processing_backward_matches_autograd(rb):
     for k in list(KEYS) + ["dt_bias_f", "dt_bias_r"]:
         assert rel(g["d" + k], ref["d" + k]) < 1e-11, k
     assert np.any(g["ddt_f"] == 0.0)  # clamped tokens pass no gradient
+
+
+def test_dt_post_processing_at_the_exact_clamp_bounds():
+    """The clamp range chosen as softplus(-7) and softplus(-2) (fp64), and
+    pre-activations placed exactly on those points (raw -7.5 and -2.5 with
+    bias 0.5, sums exact in fp64): the step is the bound itself and the
+    gradient passes (ends included); just beyond either point the step is
+    held at the bound and no gradient passes."""
+    lo, hi = float(np.logaddexp(0.0, -7.0)), float(np.logaddexp(0.0, -2.0))
+    eps = 2.0 ** -30
+    raw = np.array([-7.5, -2.5, -7.5 - eps, -2.5 + eps, -5.0]).reshape(1, 5, 1)
+    bias = np.array([0.5])
+    dt = DTA.forward(raw, bias, lo, hi).ravel()
+    assert dt[0] == lo and dt[1] == hi
+    assert dt[2] == lo and dt[3] == hi
+    assert lo < dt[4] < hi
+    ddt = np.full((1, 5, 1), 3.0)
+    draw, dbias = DTA.backward(raw, bias, lo, hi, ddt)
+    z = raw.ravel() + 0.5
+    sig = 1.0 / (1.0 + np.exp(-z))
+    assert draw.ravel()[0] == 3.0 * sig[0] and draw.ravel()[1] == 3.0 * sig[1]
+    assert draw.ravel()[2] == 0.0 and draw.ravel()[3] == 0.0
+    assert draw.ravel()[4] == 3.0 * sig[4]
+    assert dbias[0] == draw.sum()
+
+
+def test_dt_post_processing_forward_and_backward_take_one_decision():
+    """Over pre-activations spread across both bounds, the gradient passes
+    exactly where the clamped step equals the unclamped softplus."""
+    r = np.random.default_rng(67)
+    raw = r.uniform(-9.0, 0.0, (2, 500, 3))
+    bias = r.standard_normal(3)
+    lo, hi = 1e-3, 0.1
+    dt = DTA.forward(raw, bias, lo, hi)
+    draw, _ = DTA.backward(raw, bias, lo, hi, np.ones_like(raw))
+    free = dt == np.logaddexp(0.0, raw + bias[None, None, :])
+    assert np.array_equal(free, draw != 0.0)
+    assert 0 < free.sum() < free.size
+
+
+def test_synthetic_pre_activations_keep_clear_of_the_clamp_edges():
+    """The test inputs hold no pre-activation within the band around either
+    point where the clamp engages (there the in-range decision depends on the
+    precision softplus is formed in), in either dtype."""
+    from synth import gen as G
+    for dtype in ("fp32", "bf16"):
+        w = G.WORKLOADS["tiny_fp32"].replace(Z=4, L=1000, H=6, dtype=dtype)
+        inp = G.with_dt_post(G.make_inputs(w), w)
+        for d in ("f", "r"):
+            z = inp[f"dt_{d}"] + inp[f"dt_bias_{d}"][None, None, :]
+            assert np.array_equal(G.quantize(inp[f"dt_{d}"], dtype), inp[f"dt_{d}"])
+            for edge in (1e-3, 0.1):
+                ze = np.log(np.expm1(edge))
+                assert np.min(np.abs(z - ze)) >= G.CLAMP_EDGE_BAND
+    # a value placed on an edge is moved off it, to a representable value
+    raw = np.full((1, 1, 1), np.log(np.expm1(0.1)) - 0.25)
+    moved = G.off_clamp_edges(G.round_fp32(raw), np.array([0.25]), 1e-3, 0.1, "fp32")
+    assert abs(moved[0, 0, 0] + 0.25 - np.log(np.expm1(0.1))) >= 2 * G.CLAMP_EDGE_BAND
