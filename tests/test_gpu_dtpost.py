@@ -4,7 +4,9 @@ clamp(softplus(dt + bias), lo, hi)) against the fp64 oracle, which applies the
 same map before its scan: forward, block-segmented forward, block update and
 backward (including the pre-activation and bias gradients).
 Tolerance: max|gpu - oracle| / max|oracle| <= 1e-4 (fp32), 2e-2 (bf16), on
-every output, the bias gradients included.  The inputs keep every
+every output; the bf16 bias gradients, sums over Z L tokens whose terms
+cancel, are held to the error bound of such a sum (2e-2 times the sum of
+the terms' magnitudes, per head), the fp32 ones to the plain bar.  The inputs keep every
 pre-activation clear of the two points where the clamp engages (synth.gen's
 off_clamp_edges), where the in-range decision would depend on the precision
 the step is formed in.
@@ -82,6 +84,16 @@ def test_backward(dtype, L, chunk, rb):
         gb, graw = host(g[f"ddt_bias_{d}"]), host(g[f"ddt_{d}"])
         # the bias gradient is the fixed-order sum of the pre-activation ddt
         assert maxrel(gb, graw.sum(axis=(0, 1))) <= 1e-5
+        if dtype == "bf16":
+            # A sum over Z L tokens whose terms cancel: its bar is the forward
+            # error bound of a sum, tol * sum_t |term_t| per head, where each
+            # term (ddt of one token) is itself held to tol above.  fp32 holds
+            # the bias gradient to the plain max-relative bar.
+            scale = np.abs(ref[f"ddt_{d}"]).sum(axis=(0, 1))
+            cond = scale / np.abs(ref[f"ddt_bias_{d}"]).max()
+            print(f"ddt_bias_{d}: sum |terms| / max |sum| = {cond.max():.1f}", flush=True)
+            assert np.all(np.abs(gb - ref[f"ddt_bias_{d}"]) <= TOL[dtype] * scale), d
+            errs.pop(f"ddt_bias_{d}")
     bad = {k: v for k, v in errs.items() if v > TOL[dtype]}
     assert not bad, (bad, errs)
 
