@@ -51,7 +51,8 @@
  * device allocator) aligned to 16 bytes; the caller owns every buffer.  The
  * library allocates no device memory and keeps no state between calls: the
  * only scratch memory is the caller's workspace, sized by
- * bissd_workspace_size().  Calls are asynchronous on `stream` (a hipStream_t;
+ * bissd_workspace_size(), except for bissd_forward_noalloc, whose workspace
+ * is a static device array of the library.  Calls are asynchronous on `stream` (a hipStream_t;
  * NULL = the null stream): inputs must stay live and unmodified until the
  * stream reaches the call.  Results are bitwise reproducible for identical
  * inputs and shapes on the same device.
@@ -90,8 +91,15 @@ enum {
   BISSD_ERR_ALIGN = -4,       /* a pointer not aligned to 16 bytes */
   BISSD_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than bissd_workspace_size() */
   BISSD_ERR_HIP = -6,         /* a HIP launch failed; see bissd_last_hip_error() */
-  BISSD_ERR_ALIAS = -7        /* an output overlaps an input it may not alias */
+  BISSD_ERR_ALIAS = -7,       /* an output overlaps an input it may not alias */
+  BISSD_ERR_SCRATCH = -8      /* bissd_forward_noalloc: the shape needs more workspace
+                                 than BISSD_NOALLOC_SCRATCH_BYTES */
 };
+
+/* Size of the device array that serves as bissd_forward_noalloc's workspace
+ * (64 MiB; the forward of batch 8 x 1,024 tokens x 24 heads x 64 x d_state
+ * 128 in bf16 needs 56 MiB). */
+#define BISSD_NOALLOC_SCRATCH_BYTES (64u << 20)
 
 /* operation selector for bissd_workspace_size() */
 enum { BISSD_OP_FORWARD = 0, BISSD_OP_BACKWARD = 1, BISSD_OP_BLOCK = 2 };
@@ -164,6 +172,26 @@ int bissd_forward(const bissd_shape_t *shape, const void *x, bissd_dir_t fwd,
                   bissd_dir_t rev, const float *D, const float *init_state, void *y,
                   float *final_state, void *workspace, size_t workspace_bytes,
                   void *stream);
+
+/*
+ * bissd_forward without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Arguments, results and errors as
+ * bissd_forward; the workspace is a static device array of
+ * BISSD_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends.  Shapes whose workspace
+ * (bissd_workspace_size(shape, BISSD_OP_FORWARD)) exceeds it are rejected
+ * with BISSD_ERR_SCRATCH before anything is launched.  The call allocates
+ * nothing (the array's device address on the current GPU is looked up on the
+ * first call on that GPU: make that first call outside graph capture).
+ * Runs on the current device, which must be the stream's.  Every call on one
+ * GPU shares that GPU's array: calls that may overlap on one GPU (other
+ * streams, other host threads) race on it and must be serialised by the
+ * caller; calls on one stream are ordered.
+ */
+int bissd_forward_noalloc(const bissd_shape_t *shape, const void *x, bissd_dir_t fwd,
+                          bissd_dir_t rev, const float *D, const float *init_state, void *y,
+                          float *final_state, void *stream);
 
 /*
  * Gradients of Loss = sum(dy * y) for y = bissd_forward(...) with the same

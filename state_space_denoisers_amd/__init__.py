@@ -24,7 +24,7 @@ import torch
 
 from . import _abi
 
-__all__ = ["Dir", "bissd_forward", "bissd_forward_phase", "bissd_block_update", "bissd_backward",
+__all__ = ["Dir", "bissd_forward", "bissd_forward_noalloc", "bissd_forward_phase", "bissd_block_update", "bissd_backward",
            "bissd_attention_forward", "bissd_attention_backward", "bissd_workspace_size",
            "shape_of", "library_path", "BissdError"]
 
@@ -230,6 +230,28 @@ def bissd_forward(x: torch.Tensor, fwd, rev, D: torch.Tensor, *, chunk: int = 25
                            _ptr(init_state), _ptr(y), _ptr(final_state), _ptr(ws),
                            C.c_size_t(nws), _stream(x.device, stream))
     _abi.check("bissd_forward", st)
+    return y
+
+
+def bissd_forward_noalloc(x: torch.Tensor, fwd, rev, D: torch.Tensor, *, y: torch.Tensor,
+                          chunk: int = 256, rev_block: int = 0,
+                          init_state: Optional[torch.Tensor] = None,
+                          final_state: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """bissd_forward with the library's static scratch array as workspace
+    (include/bissd.h, bissd_forward_noalloc): nothing is allocated, so the
+    caller passes y.  Shapes whose workspace exceeds the array
+    (BISSD_NOALLOC_SCRATCH_BYTES) raise BissdError (BISSD_ERR_SCRATCH)."""
+    lib = _abi.load()
+    fwd, rev = Dir(*fwd), Dir(*rev)
+    _check_scan(x, fwd, rev, D, states=(("init_state", init_state), ("final_state", final_state)),
+                acts=(("y", y),))
+    if y is None:
+        raise ValueError("y is required")
+    shape = shape_of(x, fwd.B, chunk, rev_block)
+    st = lib.bissd_forward_noalloc(C.byref(shape), _ptr(x), _dir(fwd), _dir(rev), _ptr(D),
+                                   _ptr(init_state), _ptr(y), _ptr(final_state),
+                                   _stream(x.device, stream))
+    _abi.check("bissd_forward_noalloc", st)
     return y
 
 

@@ -20,10 +20,13 @@ OP_FORWARD, OP_BACKWARD, OP_BLOCK = 0, 1, 2
 STATUS = {
     0: "BISSD_OK", -1: "BISSD_ERR_NULL", -2: "BISSD_ERR_SHAPE", -3: "BISSD_ERR_UNSUPPORTED",
     -4: "BISSD_ERR_ALIGN", -5: "BISSD_ERR_WORKSPACE", -6: "BISSD_ERR_HIP", -7: "BISSD_ERR_ALIAS",
+    -8: "BISSD_ERR_SCRATCH",
 }
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 # every symbol include/bissd.h declares
-EXPORTS = ("bissd_workspace_size", "bissd_forward", "bissd_backward", "bissd_block_update",
+EXPORTS = ("bissd_workspace_size", "bissd_forward", "bissd_forward_noalloc", "bissd_backward",
+           "bissd_block_update",
            "bissd_forward_phase", "bissd_attention_forward", "bissd_attention_backward",
            "bissd_attention_workspace_size", "bissd_status_string", "bissd_last_hip_error",
            "bissd_version")
@@ -81,6 +84,9 @@ def load(path: str = LIB_PATH) -> C.CDLL:
         lib.bissd_forward.argtypes = [C.POINTER(Shape), C.c_void_p, Dir, Dir, C.c_void_p,
                                       C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                       C.c_size_t, C.c_void_p]
+        lib.bissd_forward_noalloc.restype = C.c_int
+        lib.bissd_forward_noalloc.argtypes = [C.POINTER(Shape), C.c_void_p, Dir, Dir, C.c_void_p,
+                                              C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]
         lib.bissd_forward_phase.restype = C.c_int
         lib.bissd_forward_phase.argtypes = lib.bissd_forward.argtypes + [C.c_int]
         lib.bissd_backward.restype = C.c_int

@@ -6,14 +6,51 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "bissd.h"
 #include "bissd_internal.hpp"
 
 using bissd::ScanArgs;
 
+// Workspace of bissd_forward_noalloc, for callers that cannot allocate:
+// one array on every GPU the library runs on, held until the process ends.
+// In host code `scratch` only names the symbol; its device address on the
+// current GPU comes from hipGetSymbolAddress (scratch_address below), and
+// only that address is ever handed to a kernel or a copy.
+static __device__ __align__(256) char scratch[BISSD_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local int g_last_hip = 0;
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_at[kMaxDevices] = {};
+
+// Device address of the scratch array on the current GPU, looked up once per
+// device (with that device current) and kept.
+int scratch_address(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    g_last_hip = (int)e;
+    return BISSD_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return BISSD_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_at[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      g_last_hip = (int)(e != hipSuccess ? e : hipErrorInvalidSymbol);
+      return BISSD_ERR_HIP;
+    }
+    g_scratch_at[dev] = p;
+  }
+  *out = g_scratch_at[dev];
+  return BISSD_OK;
+}
 
 constexpr int64_t kMaxElems = (int64_t)1 << 40;
 
@@ -225,6 +262,9 @@ const char *bissd_status_string(int status) {
     case BISSD_ERR_WORKSPACE: return "workspace missing or too small";
     case BISSD_ERR_HIP: return "HIP launch failed";
     case BISSD_ERR_ALIAS: return "an output overlaps an input";
+    case BISSD_ERR_SCRATCH:
+      return "the shape needs more workspace than bissd_forward_noalloc's scratch array "
+             "(BISSD_NOALLOC_SCRATCH_BYTES) holds";
     default: return "unknown status";
   }
 }
@@ -300,6 +340,21 @@ int bissd_forward(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, bissd_
                   void *workspace, size_t workspace_bytes, void *stream) {
   return forward_impl(s, x, fwd, rev, D, init_state, y, final_state, workspace, workspace_bytes,
                       stream, -1);
+}
+
+int bissd_forward_noalloc(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, bissd_dir_t rev,
+                          const float *D, const float *init_state, void *y, float *final_state,
+                          void *stream) {
+  int rc = check_shape(s, BISSD_OP_FORWARD);
+  if (rc) return rc;
+  // the forward's workspace needs no zeroing: every kernel writes what a
+  // later one reads before it is read, in this call
+  const size_t need = ws_layout(s, BISSD_OP_FORWARD).total;
+  if (need > (size_t)BISSD_NOALLOC_SCRATCH_BYTES) return BISSD_ERR_SCRATCH;
+  void *ws = nullptr;
+  if ((rc = scratch_address(&ws))) return rc;
+  return forward_impl(s, x, fwd, rev, D, init_state, y, final_state, ws,
+                      (size_t)BISSD_NOALLOC_SCRATCH_BYTES, stream, -1);
 }
 
 int bissd_forward_phase(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, bissd_dir_t rev,

@@ -276,3 +276,19 @@ def test_dt_post_processing_validation(lib):
     ok = _abi.Dir(addr(1), addr(2), addr(3), addr(4), addr(20), 0.0, float("inf"))
     assert call_forward(lib, s, fwd=ok, nws=16) == -5   # passes validation up to the workspace
 
+
+
+def test_noalloc_rejects_before_any_device_call(lib):
+    """bissd_forward_noalloc checks the shape and the size of its workspace
+    against the scratch array before it touches the device: a bad shape and
+    a shape too large for the array are rejected here, with no GPU."""
+    args = (addr(0), dirs(1), dirs(5), addr(9), None, addr(10), None, None)
+    big = shape(batch=2, seqlen=65536, nheads=4)
+    assert lib.bissd_workspace_size(C.byref(big), _abi.OP_FORWARD) > _abi.NOALLOC_SCRATCH_BYTES
+    assert lib.bissd_forward_noalloc(C.byref(big), *args) == -8
+    assert lib.bissd_forward_noalloc(C.byref(shape(headdim=32)), *args) == -3
+    assert lib.bissd_forward_noalloc(C.byref(shape(batch=0)), *args) == -2
+    assert lib.bissd_forward_noalloc(None, *args) == -1
+    assert b"BISSD_NOALLOC_SCRATCH_BYTES" in lib.bissd_status_string(-8)
+    hdr = open(os.path.join(ROOT, "include", "bissd.h")).read()
+    assert f"({_abi.NOALLOC_SCRATCH_BYTES >> 20}u << 20)" in hdr
