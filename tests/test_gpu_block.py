@@ -236,3 +236,19 @@ def test_block_update_closed_form_bit_exact(dtype, Lb, chunk):
         y, so = gpu_block(inp, dtype, S0, chunk=chunk, alias=alias)
         assert np.array_equal(y, ey), alias
         assert np.array_equal(so, eso), alias
+
+
+@pytest.mark.parametrize("dtype", ("fp32", "bf16"))
+@pytest.mark.parametrize("Lb", (64, 37))
+def test_block_update_dstate64(dtype, Lb):
+    """d_state 64 (the 130M checkpoint card's d_state) through the
+    single-launch block kernel, with and without an in-place commit."""
+    w = W["block_update"].replace(Z=2, L=Lb, H=6, N=64, dtype=dtype, mask_count=0, seed=60 + Lb)
+    for mode in ("fwd", "rev", "full"):
+        inp = gen.make_inputs(w, mode=mode)
+        S0 = gen.round_fp32(np.random.default_rng(Lb).standard_normal((2, 6, 64, 64)) * 0.05)
+        for alias in (False, True):
+            y, so = gpu_block(inp, dtype, S0, chunk=64, alias=alias)
+            ry, rso = O.block_update(inp, S0)
+            assert maxrel(y, ry) <= TOL[dtype], (mode, alias)
+            assert maxrel(so, rso) <= TOL[dtype], (mode, alias)
