@@ -610,3 +610,94 @@ def test_synthetic_pre_activations_keep_clear_of_the_clamp_edges():
     raw = np.full((1, 1, 1), np.log(np.expm1(0.1)) - 0.25)
     moved = G.off_clamp_edges(G.round_fp32(raw), np.array([0.25]), 1e-3, 0.1, "fp32")
     assert abs(moved[0, 0, 0] + 0.25 - np.log(np.expm1(0.1))) >= 2 * G.CLAMP_EDGE_BAND
+
+
+# ---------------------------------------------------------------- the conv
+
+from oracle import conv as CV  # noqa: E402
+
+
+def _conv_params(H, P, K, seed):
+    r = np.random.default_rng(seed)
+    return r.standard_normal((H, P, K)) * 0.5, r.standard_normal((H, P)) * 0.1
+
+
+@pytest.mark.parametrize("K", [1, 2, 3, 4])
+def test_conv_is_numpy_convolve_per_channel(K):
+    """Forward: the full discrete convolution with the taps reversed,
+    truncated to the sequence (numpy.convolve); reverse: the same of the
+    flipped sequence, flipped back.  No bias or activation."""
+    r = np.random.default_rng(70 + K)
+    x = r.standard_normal((2, 37, 3, 4))
+    w, _ = _conv_params(3, 4, K, 71)
+    cf = CV.conv(x, w, None, "f", act=False)
+    cr = CV.conv(x, w, None, "r", act=False)
+    for z in range(2):
+        for h in range(3):
+            for p in range(4):
+                v = w[h, p, ::-1]
+                assert np.allclose(cf[z, :, h, p], np.convolve(x[z, :, h, p], v)[:37], rtol=0, atol=1e-13)
+                assert np.allclose(cr[z, :, h, p], np.convolve(x[z, ::-1, h, p], v)[:37][::-1], rtol=0, atol=1e-13)
+
+
+def test_conv_activation_is_silu():
+    from scipy.special import expit
+    r = np.random.default_rng(72)
+    x = r.standard_normal((1, 20, 2, 3))
+    w, b = _conv_params(2, 3, 4, 73)
+    pre = CV.conv(x, w, b, "f", act=False)
+    assert np.allclose(CV.conv(x, w, b, "f"), pre * expit(pre), rtol=1e-14, atol=0)
+
+
+def test_conv_identity_taps_leave_the_plain_scan():
+    """Width 1 with tap 1, no bias, no activation: both directions read x."""
+    inp = rand_inputs(2, 50, 3, 4, 5, 1, seed=74)
+    one = (np.ones((3, 4, 1)), None, False)
+    assert rel(CV.forward(inp, {"f": one, "r": one}), O.forward(inp)) < 1e-13
+
+
+@pytest.mark.parametrize("K", [2, 4])
+def test_conv_state_continues_the_prefix_and_the_reverse_stays_in_the_block(K):
+    r = np.random.default_rng(75)
+    x = r.standard_normal((2, 30, 2, 3))
+    w, b = _conv_params(2, 3, K, 76)
+    full_f = CV.conv(x, w, b, "f")
+    blk_f = CV.conv(x[:, 20:], w, b, "f", state=x[:, 20 - (K - 1):20])
+    assert np.array_equal(full_f[:, 20:], blk_f)
+    assert np.array_equal(CV.next_state(x[:, 20:], x[:, 20 - (K - 1):20], K), x[:, 30 - (K - 1):])
+    # a block shorter than the state: the state shifts by the block
+    st = x[:, :K - 1]
+    assert np.array_equal(CV.next_state(x[:, K - 1:K], st, K), x[:, 1:K])
+    # reverse of the block alone == reverse with the sequence ending at the block
+    assert np.array_equal(CV.conv(x[:, 20:], w, b, "r"), CV.conv(x, w, b, "r")[:, 20:])
+    # block-segmented reverse: each block alone
+    seg = CV.conv(x, w, b, "r", rev_block=8)
+    for k0 in range(0, 30, 8):
+        assert np.array_equal(seg[:, k0:k0 + 8], CV.conv(x[:, k0:k0 + 8], w, b, "r"))
+
+
+def test_conv_block_update_is_the_full_scan_restricted_to_the_block():
+    """Cache consistency with the convolution: the forward part of the scan
+    over [prefix | block] restricted to the block equals the block update
+    continuing the prefix's final state and conv state; the reverse part
+    equals the scan of the block alone."""
+    Lp, Lb, K = 40, 16, 4
+    inp = rand_inputs(2, Lp + Lb, 3, 4, 5, 1, seed=77)
+    wf, bf = _conv_params(3, 4, K, 78)
+    wr, br = _conv_params(3, 4, K, 79)
+    convs = {"f": (wf, bf, True), "r": (wr, br, True)}
+    pre = {k: (v[:, :Lp] if v.ndim > 1 else v) for k, v in inp.items()}
+    blk = {k: (v[:, Lp:] if v.ndim > 1 else v) for k, v in inp.items()}
+    # forward-only and reverse-only views (D = 0 and the other C = 0)
+    fwd_only = lambda q: {**q, "C_r": np.zeros_like(q["C_r"]), "D": np.zeros_like(q["D"])}  # noqa: E731
+    rev_only = lambda q: {**q, "C_f": np.zeros_like(q["C_f"]), "D": np.zeros_like(q["D"])}  # noqa: E731
+    xcf_pre = CV.conv(pre["x"], wf, bf, "f")
+    S = O.forward({**fwd_only(pre), "x": xcf_pre}, final_state=True)["final_state"]
+    cst = pre["x"][:, Lp - (K - 1):]
+    yb, so, cso = CV.block_update(fwd_only(blk), convs, S, conv_state=cst)
+    assert rel(yb, CV.forward(fwd_only(inp), convs)[:, Lp:]) < 1e-12
+    yr, _, _ = CV.block_update(rev_only(blk), convs, S, conv_state=cst)
+    assert rel(yr, CV.forward(rev_only(blk), convs)) < 1e-12
+    full_S = O.forward({**fwd_only(inp), "x": CV.conv(inp["x"], wf, bf, "f")}, final_state=True)["final_state"]
+    assert rel(so, full_S) < 1e-12
+    assert np.array_equal(cso, inp["x"][:, -(K - 1):])
