@@ -30,6 +30,20 @@
  * prefix caches -- runs over the whole sequence.  bissd_forward and
  * bissd_backward take it; for RB >= L it is the unsegmented scan.
  *
+ * The mixer's convolution (optional, per direction).  A Mamba-2 layer passes
+ * its x through a short causal depthwise convolution and a SiLU before the
+ * scan; the directions share the pre-convolution x (weight-tied
+ * in-projection, "DiffMamba Checkpoints", Model details) and each has its own
+ * taps.  With shape->conv_width = K > 0 and dir.conv_w set, that direction's
+ * scan reads, per channel c = h * headdim + p,
+ *   forward:  xc[t][c] = act(conv_b[c] + sum_{k<K} conv_w[c][k] x[t - (K-1) + k][c])
+ *   reverse:  xc[t][c] = act(conv_b[c] + sum_{k<K} conv_w[c][k] x[t + (K-1) - k][c])
+ * in place of x (act = SiLU with conv_act, else the identity): the reverse is
+ * the forward convolution of the flipped sequence.  x reads as zero before
+ * the sequence (a block update's forward convolution continues from the
+ * block's conv state instead) and past its end; the reverse never reads past
+ * the end of its reverse block.  The skip stays D x on the x given.
+ *
  * Block update ("Training Hybrid Block Diffusion Language Models with Partial
  * Bidirectionality", Methodology and Technical Contribution): during
  * block-wise denoising the forward state after the prefix is a cache that is
@@ -64,7 +78,8 @@
  *
  * Support.  headdim == 64; dstate in {64, 128}; chunk in {64, 128, 256};
  * nheads % ngroups == 0; any seqlen >= 1; dtype BISSD_F32 or BISSD_BF16;
- * rev_block 0, or a multiple of 64 that divides chunk or is a multiple of it.
+ * rev_block 0, or a multiple of 64 that divides chunk or is a multiple of it;
+ * conv_width 0..4.
  * All arithmetic accumulates in fp32; bf16 operands feed the matrix cores.
  */
 #ifndef BISSD_H
@@ -122,6 +137,10 @@ typedef struct {
                         while the forward scan still runs over the whole
                         sequence.  A multiple of 64 that divides chunk or is
                         a multiple of it; bissd_block_update takes 0 only. */
+  int32_t conv_width; /* 0: no convolution; 1..4: the width K of the directions'
+                         convolutions (each direction with conv_w set uses it;
+                         the workspace has room for their outputs) */
+  int32_t reserved;   /* must be 0 */
 } bissd_shape_t;
 
 /* One scan direction's parameters.  Without dt_bias, dt is the step itself
@@ -137,6 +156,11 @@ typedef struct {
   const float *dt_bias;   /* [H] fp32, or NULL: no post-processing */
   float dt_min, dt_max;   /* clamp range with dt_bias: 0 <= dt_min <= dt_max
                              (INFINITY for no upper bound) */
+  const float *conv_w;    /* [H][P][conv_width] fp32 taps, or NULL: the scan reads x
+                             as given (requires shape->conv_width > 0 when set) */
+  const float *conv_b;    /* [H][P] fp32 bias, or NULL: none */
+  int32_t conv_act;       /* 1: SiLU after the convolution (Mamba-2's); 0: none */
+  int32_t reserved;       /* must be 0 */
 } bissd_dir_t;
 
 /* One direction's parameter gradients (all fp32, overwritten). */
@@ -195,7 +219,8 @@ int bissd_forward_noalloc(const bissd_shape_t *shape, const void *x, bissd_dir_t
 
 /*
  * Gradients of Loss = sum(dy * y) for y = bissd_forward(...) with the same
- * inputs (init_state optional and treated as a constant):
+ * inputs (init_state optional and treated as a constant).  A direction with
+ * a convolution (conv_w) is not supported here (BISSD_ERR_UNSUPPORTED):
  *   dx [Z][L][H][P] fp32; gfwd / grev: per-direction ddt, dA, dB, dC (fp32);
  *   dD [H] fp32.  All outputs are overwritten; dA, dB, dC and dD are
  *   reduced deterministically (no floating-point atomics).
@@ -212,10 +237,18 @@ int bissd_backward(const bissd_shape_t *shape, const void *x, bissd_dir_t fwd,
  *   state_in  [Z][H][P][N] fp32: forward state after the last prefix token.
  *   state_out [Z][H][P][N] fp32 or NULL: forward state after the last block
  *             token (the next block's cache).  May equal state_in.
+ *   conv_state_in  [Z][K-1][H][P] dtype or NULL (zeros): with a convolution
+ *             (K = shape->conv_width > 1), the last K-1 x rows before the
+ *             block, where the forward convolution continues from.
+ *   conv_state_out [Z][K-1][H][P] dtype or NULL: receives the last K-1 x rows
+ *             of [conv_state_in | x_blk] (the next block's conv state).  May
+ *             equal conv_state_in.
+ *   Both conv states are ignored when K <= 1.
  */
 int bissd_block_update(const bissd_shape_t *shape, const float *state_in,
                        const void *x_blk, bissd_dir_t fwd, bissd_dir_t rev,
-                       const float *D, void *y_blk, float *state_out, void *workspace,
+                       const float *D, void *y_blk, float *state_out,
+                       const void *conv_state_in, void *conv_state_out, void *workspace,
                        size_t workspace_bytes, void *stream);
 
 /*
@@ -304,7 +337,7 @@ const char *bissd_status_string(int status);
 /* The hipError_t of the last BISSD_ERR_HIP on the calling thread (0 if none). */
 int bissd_last_hip_error(void);
 
-/* ABI version: 2 (1 had no dt post-processing fields). */
+/* ABI version: 3 (2 had no convolution fields, 1 no dt post-processing fields). */
 int bissd_version(void);
 
 #ifdef __cplusplus

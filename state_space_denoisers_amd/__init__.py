@@ -13,7 +13,9 @@ library's HIP kernels.  There is no CPU or PyTorch fallback.
 fp32, B and C [Z,L,G,N]; x [Z,L,H,P]; D [H] fp32.  x, dt, B, C (and dy) share
 one dtype, torch.float32 or torch.bfloat16.  A ``Dir`` with ``dt_bias`` ([H]
 fp32) makes the kernels read dt as clamp(softplus(dt + dt_bias), dt_min,
-dt_max).
+dt_max); one with ``conv_w`` ([H, P, K] fp32 taps, ``conv_b`` [H, P] fp32,
+``conv_act`` SiLU) makes that direction's scan read its causal (forward) or
+anti-causal (reverse) depthwise convolution of x (include/bissd.h).
 """
 from __future__ import annotations
 
@@ -39,6 +41,9 @@ class Dir(NamedTuple):
     dt_bias: Optional[torch.Tensor] = None
     dt_min: float = 0.0
     dt_max: float = float("inf")
+    conv_w: Optional[torch.Tensor] = None
+    conv_b: Optional[torch.Tensor] = None
+    conv_act: bool = True
 
 
 def library_path() -> str:
@@ -56,15 +61,17 @@ def _dtype_code(t: torch.Tensor) -> int:
 _SHAPES: dict = {}
 
 
-def shape_of(x: torch.Tensor, B: torch.Tensor, chunk: int, rev_block: int = 0) -> _abi.Shape:
+def shape_of(x: torch.Tensor, B: torch.Tensor, chunk: int, rev_block: int = 0,
+             conv_width: int = 0) -> _abi.Shape:
     """The ABI shape struct for x / B (memoised: block updates call this in
     tight loops, and the C side only reads it)."""
-    key = (x.shape, B.shape, x.dtype, chunk, rev_block)
+    key = (x.shape, B.shape, x.dtype, chunk, rev_block, conv_width)
     s = _SHAPES.get(key)
     if s is None:
         Z, L, H, P = x.shape
         G, N = B.shape[2], B.shape[3]
-        s = _abi.Shape(Z, L, H, P, N, G, int(chunk), _dtype_code(x), int(rev_block))
+        s = _abi.Shape(Z, L, H, P, N, G, int(chunk), _dtype_code(x), int(rev_block),
+                       int(conv_width), 0)
         if len(_SHAPES) > 1024:
             _SHAPES.clear()
         _SHAPES[key] = s
@@ -129,7 +136,16 @@ def _check_dir(d: "Dir", tag: str, x: torch.Tensor, G: int, N: int, named: dict)
     _need(d.C, f"{tag}.C", (Z, L, G, N), x.dtype)
     if d.dt_bias is not None:
         _need(d.dt_bias, f"{tag}.dt_bias", (H,), torch.float32)
-    for k in ("dt", "A", "B", "C", "dt_bias"):
+    P = x.shape[3]
+    if d.conv_w is not None:
+        if not isinstance(d.conv_w, torch.Tensor) or d.conv_w.dim() != 3 or not 1 <= d.conv_w.shape[2] <= 4:
+            raise ValueError(f"{tag}.conv_w must be [H, P, K] with 1 <= K <= 4")
+        _need(d.conv_w, f"{tag}.conv_w", (H, P, d.conv_w.shape[2]), torch.float32)
+        if d.conv_b is not None:
+            _need(d.conv_b, f"{tag}.conv_b", (H, P), torch.float32)
+    elif d.conv_b is not None:
+        raise ValueError(f"{tag}.conv_b given without conv_w")
+    for k in ("dt", "A", "B", "C", "dt_bias", "conv_w", "conv_b"):
         named[f"{tag}.{k}"] = getattr(d, k)
 
 
@@ -175,8 +191,17 @@ def _dir(d) -> _abi.Dir:
         raise TypeError(f"A must be torch.float32, got {d.A.dtype}")
     if d.dt_bias is not None and d.dt_bias.dtype != torch.float32:
         raise TypeError(f"dt_bias must be torch.float32, got {d.dt_bias.dtype}")
+    act = int(bool(d.conv_act)) if d.conv_w is not None else 0
     return _abi.Dir(_ptr(d.dt), _ptr(d.A), _ptr(d.B), _ptr(d.C), _ptr(d.dt_bias),
-                    float(d.dt_min), float(d.dt_max))
+                    float(d.dt_min), float(d.dt_max), _ptr(d.conv_w), _ptr(d.conv_b), act, 0)
+
+
+def _conv_width(fwd: "Dir", rev: "Dir") -> int:
+    """The convolution width the directions' taps share (0: none)."""
+    ks = {d.conv_w.shape[-1] for d in (fwd, rev) if d.conv_w is not None}
+    if len(ks) > 1:
+        raise ValueError(f"the directions' convolutions must have one width, got {sorted(ks)}")
+    return ks.pop() if ks else 0
 
 
 def _stream(device: torch.device, stream) -> C.c_void_p:
@@ -221,7 +246,7 @@ def bissd_forward(x: torch.Tensor, fwd, rev, D: torch.Tensor, *, chunk: int = 25
     fwd, rev = Dir(*fwd), Dir(*rev)
     _check_scan(x, fwd, rev, D, states=(("init_state", init_state), ("final_state", final_state)),
                 acts=(("y", y),))
-    shape = shape_of(x, fwd.B, chunk, rev_block)
+    shape = shape_of(x, fwd.B, chunk, rev_block, _conv_width(fwd, rev))
     with _on_stream(x.device, stream):
         if y is None:
             y = torch.empty_like(x)
@@ -247,7 +272,7 @@ def bissd_forward_noalloc(x: torch.Tensor, fwd, rev, D: torch.Tensor, *, y: torc
                 acts=(("y", y),))
     if y is None:
         raise ValueError("y is required")
-    shape = shape_of(x, fwd.B, chunk, rev_block)
+    shape = shape_of(x, fwd.B, chunk, rev_block, _conv_width(fwd, rev))
     st = lib.bissd_forward_noalloc(C.byref(shape), _ptr(x), _dir(fwd), _dir(rev), _ptr(D),
                                    _ptr(init_state), _ptr(y), _ptr(final_state),
                                    _stream(x.device, stream))
@@ -266,7 +291,7 @@ def bissd_forward_phase(phase: int, x: torch.Tensor, fwd, rev, D: torch.Tensor, 
     _check_scan(x, fwd, rev, D, states=(("init_state", init_state), ("final_state", final_state)),
                 acts=(("y", y),))
     _check_workspace(workspace, x.device)
-    shape = shape_of(x, fwd.B, chunk, rev_block)
+    shape = shape_of(x, fwd.B, chunk, rev_block, _conv_width(fwd, rev))
     st = lib.bissd_forward_phase(C.byref(shape), _ptr(x), _dir(fwd), _dir(rev), _ptr(D),
                                  _ptr(init_state), _ptr(y), _ptr(final_state), _ptr(workspace),
                                  C.c_size_t(workspace.numel() * workspace.element_size()),
@@ -278,18 +303,31 @@ def bissd_block_update(state_in: torch.Tensor, x_blk: torch.Tensor, fwd, rev,
                        D: torch.Tensor, *, chunk: Optional[int] = None,
                        y_blk: Optional[torch.Tensor] = None,
                        state_out: Optional[torch.Tensor] = None, commit: bool = True,
+                       conv_state: Optional[torch.Tensor] = None,
+                       conv_state_out: Optional[torch.Tensor] = None,
                        workspace: Optional[torch.Tensor] = None, stream=None):
     """Block update with a cached forward prefix state (include/bissd.h,
     bissd_block_update).  Returns (y_blk, state_out); state_out is None when
-    ``commit`` is false and none was given."""
+    ``commit`` is false and none was given.  With the directions'
+    convolutions (width K), ``conv_state`` [Z, K-1, H, P] holds the last K-1
+    x rows before the block (None: zeros) and ``conv_state_out`` (may be
+    ``conv_state``) receives the last K-1 rows of [conv_state | x_blk]."""
     lib = _abi.load()
     fwd, rev = Dir(*fwd), Dir(*rev)
+    K = _conv_width(fwd, rev)
+    cst = (K - 1, x_blk.shape[2], x_blk.shape[3]) if K > 1 else None
+    outs = ()
+    if cst is not None:
+        outs = tuple((n, t, (x_blk.shape[0],) + cst, x_blk.dtype)
+                     for n, t in (("conv_state", conv_state), ("conv_state_out", conv_state_out)))
+    elif conv_state is not None or conv_state_out is not None:
+        raise ValueError("conv states need directions with a convolution wider than one tap")
     _check_scan(x_blk, fwd, rev, D, states=(("state_in", state_in), ("state_out", state_out)),
-                acts=(("y_blk", y_blk),))
+                acts=(("y_blk", y_blk),), outs=outs)
     L = x_blk.shape[1]
     if chunk is None:
         chunk = 64 if L <= 64 else (128 if L <= 128 else 256)
-    shape = shape_of(x_blk, fwd.B, chunk)
+    shape = shape_of(x_blk, fwd.B, chunk, 0, K)
     with _on_stream(x_blk.device, stream):
         if y_blk is None:
             y_blk = torch.empty_like(x_blk)
@@ -297,7 +335,8 @@ def bissd_block_update(state_in: torch.Tensor, x_blk: torch.Tensor, fwd, rev,
             state_out = torch.empty_like(state_in)
         ws, nws = _workspace(shape, _abi.OP_BLOCK, x_blk.device, workspace)
     st = lib.bissd_block_update(C.byref(shape), _ptr(state_in), _ptr(x_blk), _dir(fwd),
-                                _dir(rev), _ptr(D), _ptr(y_blk), _ptr(state_out), _ptr(ws),
+                                _dir(rev), _ptr(D), _ptr(y_blk), _ptr(state_out),
+                                _ptr(conv_state), _ptr(conv_state_out), _ptr(ws),
                                 C.c_size_t(nws), _stream(x_blk.device, stream))
     _abi.check("bissd_block_update", st)
     return y_blk, state_out
@@ -331,7 +370,7 @@ def bissd_backward(x: torch.Tensor, fwd, rev, D: torch.Tensor, dy: torch.Tensor,
                 outs=tuple((k, g.get(k), shp, torch.float32) for k, shp in gshape.items()))
     if dy is None:
         raise ValueError("dy is required")
-    shape = shape_of(x, fwd.B, chunk, rev_block)
+    shape = shape_of(x, fwd.B, chunk, rev_block, _conv_width(fwd, rev))
     with _on_stream(x.device, stream):
         for k, shp in gshape.items():
             if k not in g:

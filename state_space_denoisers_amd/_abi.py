@@ -35,7 +35,8 @@ EXPORTS = ("bissd_workspace_size", "bissd_forward", "bissd_forward_noalloc", "bi
 class Shape(C.Structure):
     _fields_ = [("batch", C.c_int64), ("seqlen", C.c_int64), ("nheads", C.c_int64),
                 ("headdim", C.c_int64), ("dstate", C.c_int64), ("ngroups", C.c_int64),
-                ("chunk", C.c_int64), ("dtype", C.c_int32), ("rev_block", C.c_int32)]
+                ("chunk", C.c_int64), ("dtype", C.c_int32), ("rev_block", C.c_int32),
+                ("conv_width", C.c_int32), ("reserved", C.c_int32)]
 
 
 class AttnShape(C.Structure):
@@ -46,7 +47,9 @@ class AttnShape(C.Structure):
 
 class Dir(C.Structure):
     _fields_ = [("dt", C.c_void_p), ("A", C.c_void_p), ("B", C.c_void_p), ("C", C.c_void_p),
-                ("dt_bias", C.c_void_p), ("dt_min", C.c_float), ("dt_max", C.c_float)]
+                ("dt_bias", C.c_void_p), ("dt_min", C.c_float), ("dt_max", C.c_float),
+                ("conv_w", C.c_void_p), ("conv_b", C.c_void_p), ("conv_act", C.c_int32),
+                ("reserved", C.c_int32)]
 
 
 class Grad(C.Structure):
@@ -96,7 +99,7 @@ def load(path: str = LIB_PATH) -> C.CDLL:
         lib.bissd_block_update.restype = C.c_int
         lib.bissd_block_update.argtypes = [C.POINTER(Shape), C.c_void_p, C.c_void_p, Dir, Dir,
                                            C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
-                                           C.c_size_t, C.c_void_p]
+                                           C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
         lib.bissd_attention_forward.restype = C.c_int
         lib.bissd_attention_forward.argtypes = [C.POINTER(AttnShape), C.c_void_p, C.c_void_p,
                                                 C.c_void_p, C.c_float, C.c_void_p, C.c_void_p,

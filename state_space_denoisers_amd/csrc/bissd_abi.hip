@@ -64,7 +64,8 @@ int check_shape(const bissd_shape_t *s, int op) {
       s->ngroups <= 0 || s->chunk <= 0)
     return BISSD_ERR_SHAPE;
   if (s->nheads % s->ngroups != 0) return BISSD_ERR_SHAPE;
-  if (s->rev_block < 0) return BISSD_ERR_SHAPE;
+  if (s->rev_block < 0 || s->conv_width < 0 || s->reserved != 0) return BISSD_ERR_SHAPE;
+  if (s->conv_width > 4) return BISSD_ERR_UNSUPPORTED;
   if (op != BISSD_OP_FORWARD && op != BISSD_OP_BACKWARD && op != BISSD_OP_BLOCK)
     return BISSD_ERR_UNSUPPORTED;
   // the reverse blocks are whole 64-token tiles and either split a chunk
@@ -104,7 +105,7 @@ int check_shape(const bissd_shape_t *s, int op) {
 // token's in-chunk decay sum and cumulative dt (fp32 [2][Z][H][L]) and the
 // partial sums of the reductions.
 struct WsLayout {
-  size_t states = 0, sin_t = 0, cdecay = 0, gram = 0;
+  size_t states = 0, sin_t = 0, cdecay = 0, gram = 0, xc = 0, xc_bytes = 0;
   size_t tstates = 0, sa_t = 0, gin_t = 0, dtsum = 0, ydot = 0, qx = 0, qxs = 0, ddpart = 0, dAintra = 0,
          dAx1 = 0, dAx2 = 0, rpart = 0, lamg = 0, cdtg = 0, dbpart = 0;
   size_t total = 0;
@@ -125,6 +126,12 @@ WsLayout ws_layout(const bissd_shape_t *s, int op) {
   };
   w.states = take(nst * esz);
   if (op != BISSD_OP_BLOCK) w.sin_t = take(nst * esz);
+  // the directions' convolved x (the convolution pass's output), except for
+  // a block of at most 64 tokens, whose single kernel forms it in LDS
+  if (s->conv_width > 0 && op != BISSD_OP_BACKWARD && (op == BISSD_OP_FORWARD || s->seqlen > 64)) {
+    w.xc_bytes = align256((size_t)(s->batch * s->seqlen * s->nheads * s->headdim) * esz);
+    w.xc = take(2 * w.xc_bytes);
+  }
   w.cdecay = take(cd);
   if (op != BISSD_OP_BLOCK || s->seqlen > 64)
     w.gram = take((size_t)(2 * s->batch * nc * s->ngroups) * (size_t)(s->chunk * s->chunk) * esz);
@@ -160,7 +167,7 @@ bool overlap(const void *a, size_t na, const void *b, size_t nb) {
 }
 
 struct Sizes {
-  size_t x, dt, bc, vec, state;
+  size_t x, dt, bc, vec, state, cw, cb, cst;
 };
 
 Sizes sizes(const bissd_shape_t *s) {
@@ -171,14 +178,22 @@ Sizes sizes(const bissd_shape_t *s) {
   z.bc = (size_t)(s->batch * s->seqlen * s->ngroups * s->dstate) * e;
   z.vec = (size_t)s->nheads * 4;
   z.state = (size_t)(s->batch * s->nheads * s->headdim * s->dstate) * 4;
+  z.cw = (size_t)(s->nheads * s->headdim * (s->conv_width > 0 ? s->conv_width : 0)) * 4;
+  z.cb = (size_t)(s->nheads * s->headdim) * 4;
+  z.cst = (size_t)(s->batch * (s->conv_width > 1 ? s->conv_width - 1 : 0) * s->nheads * s->headdim) * e;
   return z;
 }
 
-int check_dir(const bissd_dir_t &d) {
+int check_dir(const bissd_dir_t &d, const bissd_shape_t *s) {
   if (!d.dt || !d.A || !d.B || !d.C) return BISSD_ERR_NULL;
   if (!aligned16(d.dt) || !aligned16(d.A) || !aligned16(d.B) || !aligned16(d.C) ||
-      (d.dt_bias && !aligned16(d.dt_bias)))
+      (d.dt_bias && !aligned16(d.dt_bias)) || (d.conv_w && !aligned16(d.conv_w)) ||
+      (d.conv_b && !aligned16(d.conv_b)))
     return BISSD_ERR_ALIGN;
+  // the convolution: taps need a width; a bias or activation needs taps
+  if (d.reserved != 0 || (d.conv_act != 0 && d.conv_act != 1)) return BISSD_ERR_SHAPE;
+  if (d.conv_w && s->conv_width <= 0) return BISSD_ERR_SHAPE;
+  if (!d.conv_w && (d.conv_b || d.conv_act)) return BISSD_ERR_SHAPE;
   // clamp range of the dt post-processing (NaN fails every comparison)
   if (d.dt_bias && !(d.dt_min >= 0.0f && d.dt_max >= d.dt_min)) return BISSD_ERR_SHAPE;
   return BISSD_OK;
@@ -187,9 +202,11 @@ int check_dir(const bissd_dir_t &d) {
 // true if `out` (n bytes) overlaps any input of the scan
 bool hits_inputs(const void *out, size_t n, const Sizes &z, const void *x, const bissd_dir_t &f,
                  const bissd_dir_t &r, const float *D) {
-  const void *bufs[] = {x, f.dt, f.A, f.B, f.C, r.dt, r.A, r.B, r.C, D, f.dt_bias, r.dt_bias};
-  const size_t lens[] = {z.x, z.dt, z.vec, z.bc, z.bc, z.dt, z.vec, z.bc, z.bc, z.vec, z.vec, z.vec};
-  for (int i = 0; i < 12; ++i)
+  const void *bufs[] = {x, f.dt, f.A, f.B, f.C, r.dt, r.A, r.B, r.C, D, f.dt_bias, r.dt_bias,
+                        f.conv_w, f.conv_b, r.conv_w, r.conv_b};
+  const size_t lens[] = {z.x, z.dt, z.vec, z.bc, z.bc, z.dt, z.vec, z.bc, z.bc, z.vec, z.vec, z.vec,
+                         z.cw, z.cb, z.cw, z.cb};
+  for (int i = 0; i < 16; ++i)
     if (overlap(out, n, bufs[i], lens[i])) return true;
   return false;
 }
@@ -236,6 +253,33 @@ ScanArgs base_args(const bissd_shape_t *s, const void *x, const bissd_dir_t &f,
   return a;
 }
 
+// The directions' convolved x for one call (directions without taps read x
+// itself): one pass over x into the workspace's xc region.
+hipError_t run_conv(const bissd_shape_t *s, const void *x, const bissd_dir_t &f, const bissd_dir_t &r,
+                    const void *state, char *ws, const WsLayout &wl, ScanArgs &a, hipStream_t st) {
+  if (!f.conv_w && !r.conv_w) return hipSuccess;
+  bissd::ConvArgs c;
+  memset(&c, 0, sizeof(c));
+  c.x = x;
+  const bissd_dir_t *dirs[2] = {&f, &r};
+  for (int d = 0; d < 2; ++d) {
+    if (!dirs[d]->conv_w) continue;
+    c.xc[d] = ws + wl.xc + d * wl.xc_bytes;
+    c.w[d] = dirs[d]->conv_w;
+    c.b[d] = dirs[d]->conv_b;
+    c.act[d] = dirs[d]->conv_act;
+    a.xs[d] = c.xc[d];
+  }
+  c.state = state;
+  c.L = s->seqlen;
+  c.Z = (int)s->batch;
+  c.HP = (int)(s->nheads * s->headdim);
+  c.K = (int)s->conv_width;
+  c.dtype = s->dtype;
+  c.rev_block = (s->rev_block > 0 && s->rev_block < s->seqlen) ? s->rev_block : 0;
+  return bissd::launch_conv(c, st);
+}
+
 int finish(hipError_t e) {
   if (e != hipSuccess) {
     g_last_hip = (int)e;
@@ -248,7 +292,7 @@ int finish(hipError_t e) {
 
 extern "C" {
 
-int bissd_version(void) { return 2; }
+int bissd_version(void) { return 3; }
 
 int bissd_last_hip_error(void) { return g_last_hip; }
 
@@ -280,7 +324,7 @@ static int forward_impl(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, 
   int rc = check_shape(s, BISSD_OP_FORWARD);
   if (rc) return rc;
   if (!x || !D || !y) return BISSD_ERR_NULL;
-  if ((rc = check_dir(fwd)) || (rc = check_dir(rev))) return rc;
+  if ((rc = check_dir(fwd, s)) || (rc = check_dir(rev, s))) return rc;
   if (!aligned16(x) || !aligned16(D) || !aligned16(y) ||
       (init_state && !aligned16(init_state)) || (final_state && !aligned16(final_state)))
     return BISSD_ERR_ALIGN;
@@ -327,7 +371,13 @@ static int forward_impl(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, 
                            {3, bissd::PHASE_GRAM},
                            {1, bissd::PHASE_STATE_PASS},
                            {2, bissd::PHASE_CHUNK_OUT}};
+  // the directions' convolved x (part of phase 0 when timing phases)
   hipError_t e = hipSuccess;
+  if (phase < 0 || phase == 0) e = run_conv(s, x, fwd, rev, nullptr, ws, wl, a, st);
+  else if (fwd.conv_w || rev.conv_w) {
+    for (int d = 0; d < 2; ++d)
+      if ((d == 0 ? fwd : rev).conv_w) a.xs[d] = ws + wl.xc + d * wl.xc_bytes;
+  }
   for (int i = 0; i < 4 && e == hipSuccess; ++i) {
     if (order[i][1] == bissd::PHASE_GRAM && a.gram_k1) continue;
     if (phase < 0 || phase == order[i][0]) e = bissd::launch_scan_phase(a, order[i][1], st);
@@ -367,15 +417,18 @@ int bissd_forward_phase(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, 
 
 int bissd_block_update(const bissd_shape_t *s, const float *state_in, const void *x_blk,
                        bissd_dir_t fwd, bissd_dir_t rev, const float *D, void *y_blk,
-                       float *state_out, void *workspace, size_t workspace_bytes,
-                       void *stream) {
+                       float *state_out, const void *conv_state_in, void *conv_state_out,
+                       void *workspace, size_t workspace_bytes, void *stream) {
   int rc = check_shape(s, BISSD_OP_BLOCK);
   if (rc) return rc;
   if (!state_in || !x_blk || !D || !y_blk) return BISSD_ERR_NULL;
-  if ((rc = check_dir(fwd)) || (rc = check_dir(rev))) return rc;
+  if ((rc = check_dir(fwd, s)) || (rc = check_dir(rev, s))) return rc;
   if (!aligned16(state_in) || !aligned16(x_blk) || !aligned16(D) || !aligned16(y_blk) ||
-      (state_out && !aligned16(state_out)))
+      (state_out && !aligned16(state_out)) || (conv_state_in && !aligned16(conv_state_in)) ||
+      (conv_state_out && !aligned16(conv_state_out)))
     return BISSD_ERR_ALIGN;
+  // the conv states take part only with a convolution wider than one tap
+  if (s->conv_width <= 1) conv_state_in = conv_state_out = nullptr;
   const WsLayout wl = ws_layout(s, BISSD_OP_BLOCK);
   if (!workspace || workspace_bytes < wl.total) return BISSD_ERR_WORKSPACE;
   if (!aligned16(workspace)) return BISSD_ERR_ALIGN;
@@ -391,6 +444,20 @@ int bissd_block_update(const bissd_shape_t *s, const float *state_in, const void
     return BISSD_ERR_ALIAS;
   if (hits_inputs(workspace, wl.total, z, x_blk, fwd, rev, D) ||
       overlap(workspace, wl.total, state_in, z.state))
+    return BISSD_ERR_ALIAS;
+  // conv_state_out may equal conv_state_in, but overlaps no other buffer
+  if (conv_state_out) {
+    const void *others[] = {y_blk, state_out, state_in, workspace};
+    const size_t olens[] = {z.x, z.state, z.state, wl.total};
+    if (hits_inputs(conv_state_out, z.cst, z, x_blk, fwd, rev, D)) return BISSD_ERR_ALIAS;
+    for (int i = 0; i < 4; ++i)
+      if (overlap(conv_state_out, z.cst, others[i], olens[i])) return BISSD_ERR_ALIAS;
+    if (conv_state_out != conv_state_in && overlap(conv_state_out, z.cst, conv_state_in, z.cst))
+      return BISSD_ERR_ALIAS;
+  }
+  if (conv_state_in && (overlap(conv_state_in, z.cst, y_blk, z.x) ||
+                        overlap(conv_state_in, z.cst, state_out, z.state) ||
+                        overlap(conv_state_in, z.cst, workspace, wl.total)))
     return BISSD_ERR_ALIAS;
 
   hipStream_t st = (hipStream_t)stream;
@@ -413,14 +480,33 @@ int bissd_block_update(const bissd_shape_t *s, const float *state_in, const void
   a.sin[1] = nullptr;
   a.sin_t = nullptr;
   // blocks of at most 64 tokens: one launch does everything
-  if (s->seqlen <= 64) return finish(bissd::launch_block_update(a, st));
-  // order matters when state_out == state_in: the output phase reads
-  // state_in before the state pass overwrites it
-  hipError_t e = hipSuccess;
-  if (state_out) e = bissd::launch_scan_phase(a, bissd::PHASE_CHUNK_STATE, st);
+  if (s->seqlen <= 64) {
+    if (s->conv_width > 0) {
+      const bissd_dir_t *dirs[2] = {&fwd, &rev};
+      for (int d = 0; d < 2; ++d) {
+        a.cw[d] = dirs[d]->conv_w;
+        a.cb[d] = dirs[d]->conv_b;
+        a.cact[d] = dirs[d]->conv_act;
+      }
+      a.ckw = (int)s->conv_width;
+      a.cst_in = conv_state_in;
+      a.cst_out = conv_state_out;
+    }
+    return finish(bissd::launch_block_update(a, st));
+  }
+  // longer blocks: the convolution pass (the forward's taps before the block
+  // read the conv state), then the chunked kernels; order matters when
+  // state_out == state_in (the output phase reads state_in before the state
+  // pass overwrites it) and when conv_state_out == conv_state_in (the
+  // convolution pass reads the old conv state before it is replaced, last)
+  hipError_t e = run_conv(s, x_blk, fwd, rev, conv_state_in, ws, wl, a, st);
+  if (e == hipSuccess && state_out) e = bissd::launch_scan_phase(a, bissd::PHASE_CHUNK_STATE, st);
   if (e == hipSuccess) e = bissd::launch_scan_phase(a, bissd::PHASE_GRAM, st);
   if (e == hipSuccess) e = bissd::launch_scan_phase(a, bissd::PHASE_CHUNK_OUT, st);
   if (e == hipSuccess && state_out) e = bissd::launch_scan_phase(a, bissd::PHASE_STATE_PASS, st);
+  if (e == hipSuccess && conv_state_out)
+    e = bissd::launch_conv_state(x_blk, conv_state_in, conv_state_out, s->seqlen, (int)s->batch,
+                                 (int)(s->nheads * s->headdim), (int)s->conv_width, s->dtype, st);
   return finish(e);
 }
 
@@ -431,7 +517,9 @@ int bissd_backward(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, bissd
   int rc = check_shape(s, BISSD_OP_BACKWARD);
   if (rc) return rc;
   if (!x || !D || !dy || !dx || !dD) return BISSD_ERR_NULL;
-  if ((rc = check_dir(fwd)) || (rc = check_dir(rev))) return rc;
+  if ((rc = check_dir(fwd, s)) || (rc = check_dir(rev, s))) return rc;
+  // the gradients through the convolution are not formed
+  if (fwd.conv_w || rev.conv_w) return BISSD_ERR_UNSUPPORTED;
   if (!gfwd.ddt || !gfwd.dA || !gfwd.dB || !gfwd.dC || !grev.ddt || !grev.dA || !grev.dB ||
       !grev.dC)
     return BISSD_ERR_NULL;

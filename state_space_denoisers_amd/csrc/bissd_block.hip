@@ -24,6 +24,14 @@
 // carried state, the reverse outputs reach the forward group through LDS for
 // the one write of y, and the two groups form half of the committed state
 // each.
+//
+// With the mixer's convolution (ScanArgs cw / ckw), each direction's scan
+// reads its own convolved x, formed in LDS from the block's x tile right after
+// it arrives: the forward's taps before the block read the conv state (the
+// last ckw - 1 x rows of the prefix), the reverse's past the block read zero.
+// The skip reads x itself; the next conv state (the last ckw - 1 rows of
+// [conv state | x_blk]) is written at the end, after every read of the old
+// one, so it may replace it in place.
 #include "bissd_device.hpp"
 #include "bissd_internal.hpp"
 
@@ -58,9 +66,18 @@ __global__ __launch_bounds__(kBlkThreads) void k_block_update(ScanArgs a) {
   __shared__ __attribute__((aligned(16))) char tBf[kRB * Sm::BRB];
   __shared__ __attribute__((aligned(16))) char tBr[kRB * Sm::BRB];
   __shared__ __attribute__((aligned(16))) char tX[kRB * Sm::XRB];
+  // the directions' convolved x (with the mixer's convolution) and the conv
+  // state's rows of this head
+  __shared__ __attribute__((aligned(16))) char tXc[2][kRB * Sm::XRB];
+  __shared__ float cst[3][kP];
   __shared__ __attribute__((aligned(16))) char tS[kP * Sm::SRB];
-  // the reverse group's outputs, [row block of wave w][v][lane] as f32x4
-  __shared__ __attribute__((aligned(16))) f32x4 xchg[4][4][64];
+  // the reverse group's outputs, [row block of wave w][v][lane] as f32x4;
+  // fp32 tiles leave no room for it, so there it takes the reverse's
+  // convolved tile (after a barrier: every reverse wave is done reading it)
+  constexpr bool XALIAS = sizeof(T) == 4;
+  static_assert(!XALIAS || sizeof(f32x4) * 4 * 4 * 64 <= kRB * Sm::XRB, "hand-over fits the tile");
+  __shared__ __attribute__((aligned(16))) f32x4 xchg_own[XALIAS ? 1 : 4][4][64];
+  f32x4 (*xchg)[4][64] = XALIAS ? reinterpret_cast<f32x4 (*)[4][64]>(tXc[1]) : xchg_own;
   constexpr int NK = N / 32, NT = N / 16;
   constexpr uint32_t ES = sizeof(T);
   const int tid = threadIdx.x, wv = wave_id(), lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
@@ -88,6 +105,12 @@ __global__ __launch_bounds__(kBlkThreads) void k_block_update(ScanArgs a) {
 #pragma unroll
   for (int ks = 0; ks < NK; ++ks)
     frag_bload(cf[ks], rC, (uint32_t)(trow * G + gidx) * N * ES + (32 * ks + 8 * g4) * ES);
+  const int K = a.ckw;
+  if (K > 1 && tid < (K - 1) * kP) {
+    const int j = tid / kP, c = tid % kP;
+    cst[j][c] = a.cst_in ? to_f(reinterpret_cast<const T *>(a.cst_in)[(((int64_t)b * (K - 1) + j) * H + h) * kP + c])
+                         : 0.0f;
+  }
   if (w == 0) {
     DtPost post;
     if (a.dtb[grp]) {
@@ -101,6 +124,32 @@ __global__ __launch_bounds__(kBlkThreads) void k_block_update(ScanArgs a) {
   }
   wait_vmem();
   __syncthreads();
+
+  // ---- the directions' convolved x, [t][c] in the x tile's layout
+  const char *tXd[2] = {tX, tX};
+  if (K > 0) {
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      if (!a.cw[d]) continue;
+      const float *wd = a.cw[d] + (int64_t)h * kP * K;
+      const float *bd = a.cb[d] ? a.cb[d] + (int64_t)h * kP : nullptr;
+      for (int e = tid; e < kRB * kP; e += kBlkThreads) {
+        const int t = e / kP, c = e % kP;
+        float v = bd ? bd[c] : 0.0f;
+        for (int k = 0; k < K; ++k) {
+          const int tj = d == 0 ? t - (K - 1) + k : t + (K - 1) - k;
+          float xv = 0.0f;
+          if (tj >= 0 && tj < L) xv = to_f(*reinterpret_cast<const T *>(tX + DX::at(tj, (int)ES * c)));
+          else if (tj < 0) xv = cst[tj + K - 1][c];
+          v += wd[c * K + k] * xv;
+        }
+        if (a.cact[d]) v = v / (1.0f + __expf(-v));
+        *reinterpret_cast<T *>(tXc[d] + DX::at(t, (int)ES * c)) = from_f<T>(t < L ? v : 0.0f);
+      }
+      tXd[d] = tXc[d];
+    }
+    __syncthreads();
+  }
 
   f32x4 acc[4];
 #pragma unroll
@@ -143,7 +192,7 @@ __global__ __launch_bounds__(kBlkThreads) void k_block_update(ScanArgs a) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         Frag<T> xf;
-        frag_rows_swz<DX>(xf, tX, 32 * q + 4 * g4, 32 * q + 16 + 4 * g4, 16 * v);
+        frag_rows_swz<DX>(xf, tXd[d], 32 * q + 4 * g4, 32 * q + 16 + 4 * g4, 16 * v);
         mma(acc[v], mf, xf);
       }
     }
@@ -168,6 +217,9 @@ __global__ __launch_bounds__(kBlkThreads) void k_block_update(ScanArgs a) {
     direction(std::integral_constant<int, 0>{});
   } else {
     direction(std::integral_constant<int, 1>{});
+  }
+  if constexpr (XALIAS) __syncthreads();
+  if (grp == 1) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) xchg[w][v][lane] = acc[v];
   }
@@ -216,7 +268,7 @@ __global__ __launch_bounds__(kBlkThreads) void k_block_update(ScanArgs a) {
     for (int ks = 0; ks < 2; ++ks) {
       // A operand: x^T rows p = 16w + r16, k = s = 32ks + 8 g4 + e, scaled by w_s
       Frag<T> xa;
-      frag_rows_swz<DX>(xa, tX, 32 * ks + 8 * g4, 32 * ks + 8 * g4 + 4, 16 * w);
+      frag_rows_swz<DX>(xa, tXd[0], 32 * ks + 8 * g4, 32 * ks + 8 * g4 + 4, 16 * w);
       float xv[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -242,6 +294,16 @@ __global__ __launch_bounds__(kBlkThreads) void k_block_update(ScanArgs a) {
         const float s0 = *reinterpret_cast<const float *>(tS + DS::at(p, 4 * n));
         so[p * N + n] = gam * s0 + sacc[nt][i2];
       }
+  }
+
+  // ---- the next conv state: row j of [conv state | x_blk] at j + L (the old
+  // rows were read into LDS before the first barrier)
+  if (K > 1 && a.cst_out && tid < (K - 1) * kP) {
+    const int j = tid / kP, c = tid % kP;
+    const int src = j + L;  // row of [conv state | x_blk]
+    const float v = src < K - 1 ? cst[src][c]
+                                : to_f(*reinterpret_cast<const T *>(tX + DX::at(src - (K - 1), (int)ES * c)));
+    reinterpret_cast<T *>(a.cst_out)[(((int64_t)b * (K - 1) + j) * H + h) * kP + c] = from_f<T>(v);
   }
 }
 

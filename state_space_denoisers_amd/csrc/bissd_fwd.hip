@@ -165,7 +165,9 @@ void k1_chunk_state(ScanArgs a) {
   // one buffer per batch row: tokens past L read as zero
   const bufres rB = make_buf(reinterpret_cast<const T *>(a.B[d]) + (int64_t)b * L * G * N,
                              (uint32_t)(L * G * N * ES));
-  const bufres rX = make_buf(reinterpret_cast<const T *>(a.x) + (int64_t)b * L * H * kP,
+  // the direction's scan input (its convolved x when it has one)
+  const void *xsrc = a.xs[d] ? a.xs[d] : a.x;
+  const bufres rX = make_buf(reinterpret_cast<const T *>(xsrc) + (int64_t)b * L * H * kP,
                              (uint32_t)(L * H * kP * ES));
   const uint32_t brs = (uint32_t)(G * N * ES), xrs = (uint32_t)(H * kP * ES);
   const uint32_t boff = (uint32_t)(t0 * G + gidx) * N * ES;
@@ -922,7 +924,10 @@ template <typename T, int N, int HT, bool SF32> struct K3Pf {
 // difference, so leaving it out of both removes a cancellation that large
 // |A| would amplify.  MODE 2 adds the term back where it is a plain part of
 // the result: dy_t (B_t.C_t) into G_t B_t for dx and x.(G_t B_t).
-template <typename T, int N, int HT, bool SF32, int MODE>
+// XCONV (MODE 0): each direction's stages read its own scan input xs[d]
+// (the directions' convolved x), and the skip D x is added from x itself in
+// the epilogue.
+template <typename T, int N, int HT, bool SF32, int MODE, bool XCONV = false>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? (MODE == 1 ? (HT == 1 ? 4 : 3) : MODE == 2 ? 2 : (SF32 ? 1 : 4)) : 1)))
 void k3_chunk_out(ScanArgs a) {
@@ -965,6 +970,10 @@ void k3_chunk_out(ScanArgs a) {
   // one buffer per batch row: tokens past L read as zero
   const bufres rX = make_buf(reinterpret_cast<const T *>(a.x) + (int64_t)b * L * H * kP,
                              (uint32_t)(L * H * kP * ES));
+  // the stages' x per slot: the directions' scan inputs with XCONV
+  const bufres rXs[2] = {
+      XCONV && a.xs[0] ? make_buf(reinterpret_cast<const T *>(a.xs[0]) + (int64_t)b * L * H * kP, (uint32_t)(L * H * kP * ES)) : rX,
+      XCONV && a.xs[1] ? make_buf(reinterpret_cast<const T *>(a.xs[1]) + (int64_t)b * L * H * kP, (uint32_t)(L * H * kP * ES)) : rX};
   const bufres rC[2] = {
       make_buf(reinterpret_cast<const T *>(a.C[0]) + (int64_t)b * L * G * N, (uint32_t)(L * G * N * ES)),
       make_buf(reinterpret_cast<const T *>(a.C[1]) + (int64_t)b * L * G * N, (uint32_t)(L * G * N * ES))};
@@ -1003,7 +1012,7 @@ void k3_chunk_out(ScanArgs a) {
     for (int u = 0; u < NG; ++u) pf[u] = gp[u * 64];
 #pragma unroll
     for (int hh = 0; hh < HT; ++hh)
-      SX::prefetch(pf + NG + hh * SX::NV, rX, xoff + s0 * xrs_b + hh * kP * ES, xrs_b);
+      SX::prefetch(pf + NG + hh * SX::NV, d ? rXs[1] : rXs[0], xoff + s0 * xrs_b + hh * kP * ES, xrs_b);
   };
   // carry-in states of heads ih*IH .. ih*IH + IH - 1
   auto prefetch_state = [&](int d, int ih) __attribute__((always_inline)) {
@@ -1275,7 +1284,7 @@ void k3_chunk_out(ScanArgs a) {
 #pragma unroll
           for (int v = 0; v < 4; ++v)
             frag_rows(xf[v], &sm.u.s.Xs[hh][0][0], Sm::XPT, 32 * q + 4 * g4, 32 * q + 16 + 4 * g4, 16 * v);
-          if constexpr (MODE == 0 && DIAG && d == 0) {
+          if constexpr (MODE == 0 && DIAG && d == 0 && !XCONV) {
             // the skip D x: on the diagonal s-block, fragment q = w / 2 holds
             // x at this lane's own accumulator positions (rows 16 w + 4 g4 +
             // i, column 16 v + r16), in its low (even w) or high (odd w) half
@@ -1347,7 +1356,8 @@ void k3_chunk_out(ScanArgs a) {
     run_direction(std::integral_constant<int, 0>{});
     run_direction(std::integral_constant<int, 1>{});
 
-    // y = acc (the skip D x was added on the forward diagonal s-block).
+    // y = acc (the skip D x was added on the forward diagonal s-block; with
+    // XCONV it is added below).
     // Each wave stages its own 16 rows through LDS, one head at a time, so
     // that every lane writes 16 contiguous bytes; a wave's LDS accesses
     // complete in order and no other wave touches those rows, so the only
@@ -1375,6 +1385,20 @@ void k3_chunk_out(ScanArgs a) {
         }
       }
       if (rvalid) {
+        if constexpr (XCONV) {
+          // the skip D x from x itself (the stages held the convolved x)
+          const T *xr = reinterpret_cast<const T *>(a.x) +
+                        (((int64_t)b * L + t0 + j * kRB + 16 * w + rr) * H + h0 + hh) * kP + pc;
+          float x0[8], x1[8];
+          gload8(x0, xr);
+          gload8(x1, xr + 8);
+          const float Dh = a.D[h0 + hh];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            o0[e] += Dh * x0[e];
+            o1[e] += Dh * x1[e];
+          }
+        }
         gstore8(yg + hh * kP, o0);
         gstore8(yg + hh * kP + 8, o1);
       }
@@ -1588,7 +1612,12 @@ static void launch_t(const ScanArgs &a, int phase, hipStream_t st) {
       hipLaunchKernelGGL((k3_chunk_out<T, N, HT, false, 1>), g, dim3(kThreads), 0, st, a);
     else if (phase == PHASE_DX)
       hipLaunchKernelGGL((k3_chunk_out<T, N, HT, false, 2>), g, dim3(kThreads), 0, st, a);
-    else if (a.sin_f32[0] || a.sin_f32[1])
+    else if (a.xs[0] || a.xs[1]) {
+      if (a.sin_f32[0] || a.sin_f32[1])
+        hipLaunchKernelGGL((k3_chunk_out<T, N, HT, true, 0, true>), g, dim3(kThreads), 0, st, a);
+      else
+        hipLaunchKernelGGL((k3_chunk_out<T, N, HT, false, 0, true>), g, dim3(kThreads), 0, st, a);
+    } else if (a.sin_f32[0] || a.sin_f32[1])
       hipLaunchKernelGGL((k3_chunk_out<T, N, HT, true, 0>), g, dim3(kThreads), 0, st, a);
     else
       hipLaunchKernelGGL((k3_chunk_out<T, N, HT, false, 0>), g, dim3(kThreads), 0, st, a);

@@ -34,6 +34,16 @@ struct FastDiv {
 
 struct ScanArgs {
   const void *x;
+  // the scan's input per direction when it differs from x (the directions'
+  // convolved x); nullptr: x.  x itself stays the skip's input.
+  const void *xs[2];
+  // the block kernel's own convolution (blocks of at most 64 tokens): taps
+  // [H][P][ckw] and bias [H][P] per direction (cw[d] nullptr: none), SiLU
+  // flags, and the conv state [Z][ckw-1][H][P] in / out (may be equal)
+  const float *cw[2], *cb[2];
+  int cact[2], ckw;
+  const void *cst_in;
+  void *cst_out;
   const void *dt[2];  // [0] forward, [1] reverse
   // per-direction dt post-processing: with dtb[d] set, every read of dt[d]
   // becomes clamp(softplus(dt + dtb[d][h]), dtlo[d], dthi[d])
@@ -123,6 +133,27 @@ bool gram_in_k1(int H, int G, int chunk);
 // the scan; init_state = the cached state; final_state = the committed
 // state or nullptr (may equal init_state); L = block length.
 hipError_t launch_block_update(const ScanArgs &a, hipStream_t st);
+
+// The directions' convolutions of x (bissd_conv.hip), one pass over x for
+// both: xc[d][t][c] = act_d(b_d[c] + sum_k w_d[c][k] x[t - (K-1) + k][c])
+// (forward) and x[t + (K-1) - k] (reverse), c = h P + p.  Rows before the
+// sequence come from `state` ([Z][K-1][H][P], nullptr: zeros); rows at or
+// past L, or past the end of the token's reverse block (rev_block > 0), are
+// zero.
+struct ConvArgs {
+  const void *x;          // [Z][L][H][P], dtype
+  void *xc[2];            // [Z][L][H][P], dtype, per direction (nullptr: not formed)
+  const float *w[2], *b[2];
+  int act[2];
+  const void *state;      // forward left halo or nullptr
+  int64_t L;
+  int Z, HP, K, dtype, rev_block;
+};
+hipError_t launch_conv(const ConvArgs &a, hipStream_t st);
+// The conv state after a block: state_out[z][j] = row j + L of [state_in | x]
+// for j < K-1 (in place allowed: every old row is read before any is written).
+hipError_t launch_conv_state(const void *x, const void *state_in, void *state_out, int64_t L,
+                             int Z, int HP, int K, int dtype, hipStream_t st);
 
 // Arguments of the backward-only kernels (dB / dC panels, decay gradients,
 // final reductions).

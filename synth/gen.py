@@ -34,6 +34,7 @@ _KEYS = {
     "mask_pos": 11, "mask_vec": 12, "prefix": 13,
     "attn_q": 14, "attn_k": 15, "attn_v": 16,
     "dtraw_f": 17, "dtraw_r": 18, "dtbias_f": 19, "dtbias_r": 20,
+    "convw_f": 21, "convw_r": 22, "convb_f": 23, "convb_r": 24, "convstate": 25,
 }
 
 
@@ -277,3 +278,24 @@ def off_clamp_edges(raw, bias, lo: float, hi: float, dtype: str,
             raw[idx] = cand
     return raw
 
+
+
+def make_conv(w: Workload, K: int = 4, seed: int | None = None, dirs=("f", "r")) -> dict:
+    """Taps and biases of the mixer's depthwise convolution per direction:
+    conv_w_<d> [H, P, K] ~ U(-1/sqrt(K), 1/sqrt(K)) (the default init of a
+    depthwise Conv1d with K taps per channel), conv_b_<d> [H, P] ~ the same,
+    fp32."""
+    s = w.seed if seed is None else seed
+    bound = 1.0 / math.sqrt(K)
+    out = {}
+    for d in dirs:
+        out[f"conv_w_{d}"] = round_fp32(_rng(s, f"convw_{d}").uniform(-bound, bound, (w.H, w.P, K)))
+        out[f"conv_b_{d}"] = round_fp32(_rng(s, f"convb_{d}").uniform(-bound, bound, (w.H, w.P)))
+    return out
+
+
+def make_conv_state(w: Workload, K: int, seed: int | None = None) -> np.ndarray:
+    """A conv state (the last K-1 x rows before a block), x's distribution,
+    rounded to the workload dtype: [Z, K-1, H, P]."""
+    s = w.seed if seed is None else seed
+    return quantize(_rng(s, "convstate").standard_normal((w.Z, K - 1, w.H, w.P)), w.dtype)

@@ -35,7 +35,7 @@ def test_header_and_binding_agree():
 def test_every_declared_symbol_is_exported(lib):
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert lib.bissd_version() == 2
+    assert lib.bissd_version() == 3
     assert lib.bissd_last_hip_error() == 0
 
 
@@ -107,7 +107,7 @@ def test_supported_reverse_blocks(lib, rb, chunk):
 def test_block_update_takes_no_reverse_block(lib):
     s = shape(seqlen=64, chunk=64, rev_block=64)
     rc = lib.bissd_block_update(C.byref(s), addr(20), addr(0), dirs(1), dirs(5), addr(9),
-                                addr(10), None, addr(12), C.c_size_t(1 << 40), None)
+                                addr(10), None, None, None, addr(12), C.c_size_t(1 << 40), None)
     assert rc == -3
     assert lib.bissd_workspace_size(C.byref(s), _abi.OP_BLOCK) == 0
 
@@ -134,15 +134,15 @@ def test_aliasing_is_rejected(lib):
 def test_block_update_validation(lib):
     s = shape(seqlen=300, chunk=256)
     rc = lib.bissd_block_update(C.byref(s), addr(20), addr(0), dirs(1), dirs(5), addr(9),
-                                addr(10), None, addr(12), C.c_size_t(1 << 40), None)
+                                addr(10), None, None, None, addr(12), C.c_size_t(1 << 40), None)
     assert rc == -2  # block longer than chunk
     s = shape(seqlen=64, chunk=64)
     rc = lib.bissd_block_update(C.byref(s), None, addr(0), dirs(1), dirs(5), addr(9),
-                                addr(10), None, addr(12), C.c_size_t(1 << 40), None)
+                                addr(10), None, None, None, addr(12), C.c_size_t(1 << 40), None)
     assert rc == -1
     # state_out partially overlapping state_in
     rc = lib.bissd_block_update(C.byref(s), addr(20), addr(0), dirs(1), dirs(5), addr(9),
-                                addr(10), C.c_void_p(A * 21 + 4096), addr(12),
+                                addr(10), C.c_void_p(A * 21 + 4096), None, None, addr(12),
                                 C.c_size_t(1 << 40), None)
     assert rc == -7
 
@@ -292,3 +292,55 @@ def test_noalloc_rejects_before_any_device_call(lib):
     assert b"BISSD_NOALLOC_SCRATCH_BYTES" in lib.bissd_status_string(-8)
     hdr = open(os.path.join(ROOT, "include", "bissd.h")).read()
     assert f"({_abi.NOALLOC_SCRATCH_BYTES >> 20}u << 20)" in hdr
+
+
+def conv_dir(base, w=None, b=None, act=0, reserved=0):
+    d = dirs(base)
+    d.conv_w = w
+    d.conv_b = b
+    d.conv_act = act
+    d.reserved = reserved
+    return d
+
+
+def test_convolution_validation(lib):
+    """The mixer's convolution fields are checked before anything is
+    enqueued: taps need a width in the shape, a bias or an activation needs
+    taps, the width is at most 4, reserved fields are zero, pointers are
+    16-byte aligned, and the backward rejects a direction with taps."""
+    ok_w = addr(30)
+    assert call_forward(lib, shape(conv_width=4), fwd=conv_dir(1, ok_w), nws=16) == -5
+    assert call_forward(lib, shape(conv_width=0), fwd=conv_dir(1, ok_w)) == -2
+    assert call_forward(lib, shape(conv_width=5)) == -3
+    assert call_forward(lib, shape(conv_width=-1)) == -2
+    assert call_forward(lib, shape(reserved=1)) == -2
+    assert call_forward(lib, shape(conv_width=4), rev=conv_dir(5, None, addr(31))) == -2
+    assert call_forward(lib, shape(conv_width=4), rev=conv_dir(5, None, None, act=1)) == -2
+    assert call_forward(lib, shape(conv_width=4), rev=conv_dir(5, ok_w, act=2)) == -2
+    assert call_forward(lib, shape(conv_width=4), rev=conv_dir(5, ok_w, reserved=1)) == -2
+    assert call_forward(lib, shape(conv_width=4), fwd=conv_dir(1, C.c_void_p(A * 30 + 4))) == -4
+    # the forward workspace holds both directions' convolved x
+    s0, s4 = shape(), shape(conv_width=4)
+    n0 = lib.bissd_workspace_size(C.byref(s0), _abi.OP_FORWARD)
+    n4 = lib.bissd_workspace_size(C.byref(s4), _abi.OP_FORWARD)
+    assert n4 - n0 >= 2 * 2 * 300 * 8 * 64 * 2
+    # a 64-token block forms it in LDS; a longer one in the workspace
+    b0 = lib.bissd_workspace_size(C.byref(shape(seqlen=64, chunk=64, conv_width=4)), _abi.OP_BLOCK)
+    assert b0 == lib.bissd_workspace_size(C.byref(shape(seqlen=64, chunk=64)), _abi.OP_BLOCK)
+    b1 = lib.bissd_workspace_size(C.byref(shape(seqlen=100, chunk=128, conv_width=4)), _abi.OP_BLOCK)
+    assert b1 > lib.bissd_workspace_size(C.byref(shape(seqlen=100, chunk=128)), _abi.OP_BLOCK)
+    # the backward takes no convolution
+    assert call_backward(lib, shape(conv_width=4), fwd=conv_dir(1, ok_w)) == -3
+
+
+def test_block_update_conv_state_aliasing(lib):
+    s = shape(seqlen=64, chunk=64, conv_width=4)
+    f = conv_dir(1, addr(30))
+
+    def blk(cin, cout):
+        return lib.bissd_block_update(C.byref(s), addr(20), addr(0), f, dirs(5), addr(9),
+                                      addr(10), None, cin, cout, addr(12), C.c_size_t(1 << 40), None)
+    assert blk(addr(40), addr(10)) == -7           # conv_state_out over y
+    assert blk(addr(40), C.c_void_p(A * 41 + 16)) == -7   # partially over conv_state_in
+    assert blk(addr(40), addr(0)) == -7            # over x
+    assert blk(C.c_void_p(A * 40 + 4), None) == -4   # misaligned
