@@ -177,14 +177,13 @@ def per_token_bytes(w):
 
 def k3_flops_per_token(w):
     """Matrix-core work of the fused output kernel per token (both
-    directions): the masked product of the precomputed C.B^T tiles with x
-    on causal 64x64 block pairs per head, and the carry-in contraction
-    C S^T per head."""
-    nrb = w.chunk // 64
-    pairs = nrb * (nrb + 1) / 2 / nrb          # block pairs per row-block, per direction
-    intra = pairs * 64 * 64 * w.P * 2 / 64 * w.H
-    inter = 2 * w.N * w.P * w.H
-    return 2 * (intra + inter)
+    directions), on the method's causal work: per head the intra-chunk
+    product of the decay-weighted C.B^T with x over the causal pairs of a
+    chunk (Q (Q + 1) / 2 pairs per Q tokens, 2 P flops each) and the
+    carry-in contraction C S^T (2 N P)."""
+    intra = (w.chunk + 1) * w.P          # 2 P flops x (Q + 1) / 2 pairs per token
+    inter = 2 * w.N * w.P
+    return 2 * w.H * (intra + inter)
 
 
 def gram_tiles_per_chunk(w):

@@ -218,6 +218,15 @@ int bissd_forward_noalloc(const bissd_shape_t *shape, const void *x, bissd_dir_t
                           float *final_state, void *stream);
 
 /*
+ * Training through the scan ("DiffMamba Checkpoints" model card, Model
+ * details: the bidirectional backbone is trained end to end with AdamW in
+ * bf16-mixed precision; "DiffuMamba", Training & Inference Strategy,
+ * Objective: the denoiser is trained on the masked-diffusion objective; "Training Hybrid
+ * Block Diffusion Language Models with Partial Bidirectionality",
+ * Methodology: the full-block objective trains the same scan with the
+ * block-segmented reverse).  The pages give no gradient formulas; these are
+ * the plain reverse-mode derivatives of the recurrence above.
+ *
  * Gradients of Loss = sum(dy * y) for y = bissd_forward(...) with the same
  * inputs (init_state optional and treated as a constant).  A direction with
  * a convolution (conv_w) is not supported here (BISSD_ERR_UNSUPPORTED):
