@@ -13,8 +13,8 @@ warm-up steps, then exactly K timed steps between two device
 synchronisations; `value` is tokens per second over the timed region.
 
 The same run also measures, live with HIP events on the launch stream, the
-average duration of each forward kernel (differences of growing prefixes of
-a forward call, enqueued back to back through bissd_forward_phase), the
+average duration of each forward kernel (each launch's own dispatch start
+and end, in complete forward calls enqueued through bissd_forward_phase), the
 long-context L=65536 scan, the training step (forward + backward, batch 16,
 L=2048), the block update with a cached 262,144-token prefix state, the
 generation loop, a latency sweep and the hybrids' attention layer; and times
@@ -133,38 +133,30 @@ def gram_in_chunk_state_kernel(w) -> bool:
 
 
 def phase_times_us(f: Forward, reps):
-    """Average duration of each forward kernel inside complete forward calls,
-    without markers between the kernels: the growing prefixes of a call
-    (first phase; first two; ...) are each enqueued reps times back to back
-    between two HIP events on the launch stream, and a kernel's time is the
-    difference of two consecutive prefixes.  Every kernel so runs right after
-    the same predecessors as in a complete call (caches, preceding kernels);
-    back-to-back forward kernels leave no measurable gap between them, so the
-    differences are the kernels' own durations."""
+    """Average duration of each forward kernel inside complete forward calls
+    (the kernels in the call's order, each after the same predecessors):
+    before each kernel's launch a library timer slot is armed, so that launch
+    records its own dispatch start and end in a pair of HIP events on its
+    stream (bissd_timer_arm / bissd_timer_read), with no marker between the
+    kernels; the durations are averaged over reps calls."""
     import torch
+    ssd = f.ssd
     f()
     torch.cuda.synchronize()
-    s = torch.cuda.current_stream()
     order = [p for p in PHASE_ORDER if not (p == 3 and gram_in_chunk_state_kernel(f.w))]
     names = dict(PHASE_NAMES)
     if 3 not in order:
         names[0] = "k1_chunk_state+gram"
-    pref = []
-    for n in range(1, len(order) + 1):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        for p in order[:n]:  # one untimed pass of this prefix
+    reps = min(reps, ssd.TIMER_SLOTS // len(order))
+    for r in range(reps):
+        for i, p in enumerate(order):
+            ssd.bissd_timer_arm(r * len(order) + i)
             f.phase(p)
-        a.record(s)
-        for _ in range(reps):
-            for p in order[:n]:
-                f.phase(p)
-        b.record(s)
-        torch.cuda.synchronize()
-        pref.append(a.elapsed_time(b) / reps)
-    out, prev = {}, 0.0
-    for n, p in enumerate(order):
-        out[names[p]] = 1e3 * (pref[n] - prev)
-        prev = pref[n]
+    ssd.bissd_timer_arm(-1)
+    torch.cuda.synchronize()
+    out = {}
+    for i, p in enumerate(order):
+        out[names[p]] = 1e3 * sum(ssd.bissd_timer_read(r * len(order) + i) for r in range(reps)) / reps
     return out
 
 
@@ -266,6 +258,43 @@ def bench_long(steps):
     return {"workload": w.name, "tokens_per_s": w.tokens / (ms * 1e-3), "ms_per_call": ms,
             "hbm_algorithmic_GBs": per_token_bytes(w) * w.tokens / (ms * 1e-3) / 1e9,
             "kernels_us": ph}
+
+
+def bench_conv(steps, K=4):
+    """The 130M-class layer forward with the mixer's convolution on both
+    directions (width K, bias, SiLU): the convolution pass over x, then the
+    scan on each direction's convolved x (the tokens/s of the whole call,
+    against the same call without the convolution)."""
+    import torch
+    import state_space_denoisers_amd as ssd
+    from synth import gen
+    w = gen.WORKLOADS["layer130m_L1k"]
+    f = Forward(w)
+    cv = gen.make_conv(w, K)
+    dev = f.y.device
+    convs = []
+    for d, p in (("f", f.fwd), ("r", f.rev)):
+        convs.append(ssd.Dir(*p, conv_w=gen.as_torch(cv[f"conv_w_{d}"], "fp32", dev),
+                             conv_b=gen.as_torch(cv[f"conv_b_{d}"], "fp32", dev), conv_act=True))
+    shape = ssd.shape_of(f.T["x"], f.T["B_f"], w.chunk, 0, K)
+    from state_space_denoisers_amd import _abi
+    ws = torch.empty(ssd.bissd_workspace_size(shape, _abi.OP_FORWARD), dtype=torch.uint8, device=dev)
+
+    def call():
+        ssd.bissd_forward(f.T["x"], convs[0], convs[1], f.T["D"], chunk=w.chunk, y=f.y, workspace=ws)
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    settle(call, LEG_SETTLE_S)
+    ms = event_time_ms(call, steps)
+    settle(f, LEG_SETTLE_S)
+    ms0 = event_time_ms(f, steps)
+    # the convolution pass reads x once and writes both directions' xc
+    xbytes = f.T["x"].numel() * f.T["x"].element_size()
+    extra_us = 1e3 * (ms - ms0)
+    return {"workload": w.name + f"_conv{K}", "tokens_per_s": w.tokens / (ms * 1e-3), "us_per_call": 1e3 * ms,
+            "us_per_call_without_conv": 1e3 * ms0, "extra_us": round(extra_us, 2),
+            "conv_pass_algorithmic_bytes": 3 * xbytes}
 
 
 def bench_block(reps):
@@ -775,6 +804,11 @@ def main():
             log(f"bench: train rev64 {extra['train_L2k_rev64']}")
         except Exception as exc:
             extra["train_L2k_rev64"] = {"error": repr(exc)}
+        try:
+            extra["layer130m_L1k_conv4"] = bench_conv(max(20, args.steps // 4))
+            log(f"bench: conv {extra['layer130m_L1k_conv4']}")
+        except Exception as exc:
+            extra["layer130m_L1k_conv4"] = {"error": repr(exc)}
         try:
             extra["block_update"] = bench_block(max(50, args.steps))
             log(f"bench: block {extra['block_update']}")

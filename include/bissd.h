@@ -346,6 +346,25 @@ const char *bissd_status_string(int status);
 /* The hipError_t of the last BISSD_ERR_HIP on the calling thread (0 if none). */
 int bissd_last_hip_error(void);
 
+/*
+ * Kernel timers, for benchmarks that need one kernel's duration inside a
+ * sequence of calls without a marker between kernels.  Every kernel the
+ * library launches goes through hipExtLaunchKernelGGL; bissd_timer_arm(slot)
+ * hands slot `slot`'s pair of HIP events to the NEXT kernel launch the
+ * library makes in this process, on any stream and from any call, which
+ * records its dispatch's start and end timestamps in them; the slot is then
+ * disarmed.  Arming replaces a slot armed before; slot -1 disarms.  The
+ * events are created on a slot's first arming (on the current device) and
+ * kept until the process ends.  bissd_timer_read(slot, &ms) waits for the
+ * slot's end event and returns the kernel's duration in milliseconds
+ * (BISSD_ERR_HIP if that slot has recorded nothing).  Process-wide state:
+ * callers that launch from several threads at once get no defined pairing.
+ *   slot  0 <= slot < BISSD_TIMER_SLOTS (or -1 for bissd_timer_arm)
+ */
+#define BISSD_TIMER_SLOTS 4096
+int bissd_timer_arm(int32_t slot);
+int bissd_timer_read(int32_t slot, float *ms);
+
 /* ABI version: 3 (2 had no convolution fields, 1 no dt post-processing fields). */
 int bissd_version(void);
 

@@ -28,7 +28,7 @@ from . import _abi
 
 __all__ = ["Dir", "bissd_forward", "bissd_forward_noalloc", "bissd_forward_phase", "bissd_block_update", "bissd_backward",
            "bissd_attention_forward", "bissd_attention_backward", "bissd_workspace_size",
-           "shape_of", "library_path", "BissdError"]
+           "bissd_timer_arm", "bissd_timer_read", "shape_of", "library_path", "BissdError"]
 
 BissdError = _abi.BissdError
 
@@ -453,3 +453,21 @@ def bissd_attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                       _stream(q.device, stream))
     _abi.check("bissd_attention_backward", st)
     return g
+
+
+TIMER_SLOTS = 4096
+
+
+def bissd_timer_arm(slot: int) -> None:
+    """Hand timer slot ``slot`` to the library's next kernel launch, which
+    records its dispatch start and end in the slot's events; -1 disarms
+    (include/bissd.h, bissd_timer_arm)."""
+    _abi.check("bissd_timer_arm", _abi.load().bissd_timer_arm(int(slot)))
+
+
+def bissd_timer_read(slot: int) -> float:
+    """Duration in ms of the kernel launch that took timer slot ``slot``
+    (waits for it; include/bissd.h, bissd_timer_read)."""
+    ms = C.c_float(0.0)
+    _abi.check("bissd_timer_read", _abi.load().bissd_timer_read(int(slot), C.byref(ms)))
+    return float(ms.value)

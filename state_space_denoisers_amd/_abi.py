@@ -29,7 +29,7 @@ EXPORTS = ("bissd_workspace_size", "bissd_forward", "bissd_forward_noalloc", "bi
            "bissd_block_update",
            "bissd_forward_phase", "bissd_attention_forward", "bissd_attention_backward",
            "bissd_attention_workspace_size", "bissd_status_string", "bissd_last_hip_error",
-           "bissd_version")
+           "bissd_timer_arm", "bissd_timer_read", "bissd_version")
 
 
 class Shape(C.Structure):
@@ -113,6 +113,10 @@ def load(path: str = LIB_PATH) -> C.CDLL:
         lib.bissd_status_string.argtypes = [C.c_int]
         lib.bissd_last_hip_error.restype = C.c_int
         lib.bissd_last_hip_error.argtypes = []
+        lib.bissd_timer_arm.restype = C.c_int
+        lib.bissd_timer_arm.argtypes = [C.c_int32]
+        lib.bissd_timer_read.restype = C.c_int
+        lib.bissd_timer_read.argtypes = [C.c_int32, C.POINTER(C.c_float)]
         lib.bissd_version.restype = C.c_int
         lib.bissd_version.argtypes = []
         _lib = lib

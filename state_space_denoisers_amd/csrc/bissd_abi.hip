@@ -288,13 +288,60 @@ int finish(hipError_t e) {
   return BISSD_OK;
 }
 
+// Kernel timers: per slot a pair of events (created on the slot's first
+// arming), and the one armed slot (-1: none).
+std::mutex g_timer_mu;
+hipEvent_t g_timer_ev[BISSD_TIMER_SLOTS][2] = {};
+int g_timer_armed = -1;
+
 }  // namespace
+
+void bissd::take_timer(hipEvent_t *start, hipEvent_t *stop) {
+  std::lock_guard<std::mutex> lock(g_timer_mu);
+  if (g_timer_armed < 0) return;
+  *start = g_timer_ev[g_timer_armed][0];
+  *stop = g_timer_ev[g_timer_armed][1];
+  g_timer_armed = -1;
+}
 
 extern "C" {
 
 int bissd_version(void) { return 3; }
 
 int bissd_last_hip_error(void) { return g_last_hip; }
+
+int bissd_timer_arm(int32_t slot) {
+  if (slot < -1 || slot >= BISSD_TIMER_SLOTS) return BISSD_ERR_SHAPE;
+  std::lock_guard<std::mutex> lock(g_timer_mu);
+  if (slot >= 0) {
+    for (int i = 0; i < 2; ++i)
+      if (!g_timer_ev[slot][i]) {
+        const hipError_t e = hipEventCreate(&g_timer_ev[slot][i]);
+        if (e != hipSuccess) {
+          g_timer_ev[slot][i] = nullptr;
+          g_last_hip = (int)e;
+          return BISSD_ERR_HIP;
+        }
+      }
+  }
+  g_timer_armed = slot;
+  return BISSD_OK;
+}
+
+int bissd_timer_read(int32_t slot, float *ms) {
+  if (!ms) return BISSD_ERR_NULL;
+  if (slot < 0 || slot >= BISSD_TIMER_SLOTS) return BISSD_ERR_SHAPE;
+  hipEvent_t e0, e1;
+  {
+    std::lock_guard<std::mutex> lock(g_timer_mu);
+    e0 = g_timer_ev[slot][0];
+    e1 = g_timer_ev[slot][1];
+  }
+  if (!e0 || !e1) return BISSD_ERR_NULL;
+  hipError_t e = hipEventSynchronize(e1);
+  if (e == hipSuccess) e = hipEventElapsedTime(ms, e0, e1);
+  return finish(e);
+}
 
 const char *bissd_status_string(int status) {
   switch (status) {

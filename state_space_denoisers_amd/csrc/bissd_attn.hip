@@ -594,11 +594,11 @@ hipError_t launch_attention_backward(const AttnArgs &a, hipStream_t st) {
   dim3 gq((unsigned)(a.Z * a.H * ((a.L + kAttnQ - 1) / kAttnQ)));
   dim3 gk((unsigned)(a.Z * a.H * ((a.L + kAttnQ - 1) / kAttnQ)));
   if (a.dtype == 1) {
-    hipLaunchKernelGGL(k_attn_dq<bf16>, gq, dim3(kThreads), 0, st, a);
-    hipLaunchKernelGGL(k_attn_dkv<bf16>, gk, dim3(kThreads), 0, st, a);
+    launch_kernel(k_attn_dq<bf16>, gq, dim3(kThreads), 0, st, a);
+    launch_kernel(k_attn_dkv<bf16>, gk, dim3(kThreads), 0, st, a);
   } else {
-    hipLaunchKernelGGL(k_attn_dq<float>, gq, dim3(kThreads), 0, st, a);
-    hipLaunchKernelGGL(k_attn_dkv<float>, gk, dim3(kThreads), 0, st, a);
+    launch_kernel(k_attn_dq<float>, gq, dim3(kThreads), 0, st, a);
+    launch_kernel(k_attn_dkv<float>, gk, dim3(kThreads), 0, st, a);
   }
   return hipGetLastError();
 }
@@ -606,8 +606,8 @@ hipError_t launch_attention_backward(const AttnArgs &a, hipStream_t st) {
 hipError_t launch_attention(const AttnArgs &a, hipStream_t st) {
   const int64_t nqt = (a.L + kAttnQ - 1) / kAttnQ;
   dim3 g((unsigned)(a.Z * a.H * nqt));
-  if (a.dtype == 1) hipLaunchKernelGGL(k_attn_fwd<bf16>, g, dim3(kThreads), 0, st, a);
-  else hipLaunchKernelGGL(k_attn_fwd<float>, g, dim3(kThreads), 0, st, a);
+  if (a.dtype == 1) launch_kernel(k_attn_fwd<bf16>, g, dim3(kThreads), 0, st, a);
+  else launch_kernel(k_attn_fwd<float>, g, dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -309,7 +309,7 @@ __global__ __launch_bounds__(kBlkThreads) void k_block_update(ScanArgs a) {
 
 template <typename T, int N>
 static void launch_block_t(const ScanArgs &a, hipStream_t st) {
-  hipLaunchKernelGGL((k_block_update<T, N>), dim3((unsigned)(a.Z * a.H)), dim3(kBlkThreads), 0, st, a);
+  launch_kernel((k_block_update<T, N>), dim3((unsigned)(a.Z * a.H)), dim3(kBlkThreads), 0, st, a);
 }
 
 hipError_t launch_block_update(const ScanArgs &a, hipStream_t st) {

@@ -676,10 +676,10 @@ template <typename T, int N>
 static void launch_panels_t(const BwdArgs &a, hipStream_t st) {
   dim3 g((unsigned)(a.Z * a.nchunks * 2 * a.G * (a.chunk / kRB)));
   dim3 gs((unsigned)(a.Z * a.nchunks * 2 * a.G));
-  hipLaunchKernelGGL((k_bwd_panel<T, N, 0>), g, dim3(kThreads), 0, st, a);
-  hipLaunchKernelGGL((k_bwd_state<T, N, 0>), gs, dim3(kStThreads), 0, st, a);
-  hipLaunchKernelGGL((k_bwd_panel<T, N, 1>), g, dim3(kThreads), 0, st, a);
-  hipLaunchKernelGGL((k_bwd_state<T, N, 1>), gs, dim3(kStThreads), 0, st, a);
+  launch_kernel((k_bwd_panel<T, N, 0>), g, dim3(kThreads), 0, st, a);
+  launch_kernel((k_bwd_state<T, N, 0>), gs, dim3(kStThreads), 0, st, a);
+  launch_kernel((k_bwd_panel<T, N, 1>), g, dim3(kThreads), 0, st, a);
+  launch_kernel((k_bwd_state<T, N, 1>), gs, dim3(kStThreads), 0, st, a);
 }
 
 hipError_t launch_bwd_panels(const BwdArgs &a, hipStream_t st) {
@@ -696,9 +696,9 @@ hipError_t launch_bwd_panels(const BwdArgs &a, hipStream_t st) {
 hipError_t launch_bwd_decay(const BwdArgs &a, hipStream_t st) {
   const int64_t items = (int64_t)a.Z * 2 * a.H * a.nchunks;
   dim3 g((unsigned)((items + 3) / 4));
-  if (a.dtype == 1) hipLaunchKernelGGL(k_bwd_decay<bf16>, g, dim3(kThreads), 0, st, a);
-  else hipLaunchKernelGGL(k_bwd_decay<float>, g, dim3(kThreads), 0, st, a);
-  hipLaunchKernelGGL(k_bwd_reduce, dim3((unsigned)(5 * a.H)), dim3(kThreads), 0, st, a);
+  if (a.dtype == 1) launch_kernel(k_bwd_decay<bf16>, g, dim3(kThreads), 0, st, a);
+  else launch_kernel(k_bwd_decay<float>, g, dim3(kThreads), 0, st, a);
+  launch_kernel(k_bwd_reduce, dim3((unsigned)(5 * a.H)), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

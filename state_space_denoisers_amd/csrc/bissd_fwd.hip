@@ -1573,54 +1573,54 @@ static void launch_t(const ScanArgs &a, int phase, hipStream_t st) {
       phase == PHASE_ADJ_TAN) {
     dim3 g((unsigned)(a.Z * a.nchunks * a.ndir * (a.H / HT)));
     if (phase == PHASE_CHUNK_STATE)
-      hipLaunchKernelGGL((k1_chunk_state<T, N, HT, 0>), g, dim3(kThreads), 0, st, a);
+      launch_kernel((k1_chunk_state<T, N, HT, 0>), g, dim3(kThreads), 0, st, a);
     else if (phase == PHASE_ADJ_STATE)
-      hipLaunchKernelGGL((k1_chunk_state<T, N, HT, 1>), g, dim3(kThreads), 0, st, a);
+      launch_kernel((k1_chunk_state<T, N, HT, 1>), g, dim3(kThreads), 0, st, a);
     else if (phase == PHASE_TAN_STATE)
-      hipLaunchKernelGGL((k1_chunk_state<T, N, HT, 2>), g, dim3(kThreads), 0, st, a);
+      launch_kernel((k1_chunk_state<T, N, HT, 2>), g, dim3(kThreads), 0, st, a);
     else
-      hipLaunchKernelGGL((k1_chunk_state<T, N, HT, 3>), g, dim3(kThreads), 0, st, a);
+      launch_kernel((k1_chunk_state<T, N, HT, 3>), g, dim3(kThreads), 0, st, a);
   } else if (phase == PHASE_GRAM) {
     // one workgroup per (batch, chunk, slot, group, row-block / column-block
     // pair on the slot's side)
     const int nrb = a.chunk / kRB;
     dim3 g((unsigned)((int64_t)a.Z * a.nchunks * 2 * a.G * (nrb * (nrb + 1) / 2)));
-    hipLaunchKernelGGL((k_gram<T, N>), g, dim3(kThreads), 0, st, a);
+    launch_kernel((k_gram<T, N>), g, dim3(kThreads), 0, st, a);
   } else if (phase == PHASE_TAN_PASS && sizeof(T) == 2) {
     const int PN = kP * N;
     dim3 g2((unsigned)(PN / 8 / kThreads), (unsigned)a.H, (unsigned)(a.Z * 2));
-    hipLaunchKernelGGL(k2_tangent_pass8, g2, dim3(kThreads), 0, st, a, PN);
+    launch_kernel(k2_tangent_pass8, g2, dim3(kThreads), 0, st, a, PN);
   } else if (phase == PHASE_TAN_PASS) {
     const int PN = kP * N;
     dim3 g2((unsigned)(PN / 4 / kThreads), (unsigned)a.H, (unsigned)(a.Z * 2));
-    hipLaunchKernelGGL(k2_tangent_pass<T>, g2, dim3(kThreads), 0, st, a, PN);
+    launch_kernel(k2_tangent_pass<T>, g2, dim3(kThreads), 0, st, a, PN);
   } else if ((phase == PHASE_STATE_PASS || phase == PHASE_ADJ_PASS) && sizeof(T) == 2) {
     const int PN = kP * N;
     dim3 g2((unsigned)(PN / 8 / kThreads), (unsigned)a.H, (unsigned)(a.Z * a.ndir));
     if (phase == PHASE_ADJ_PASS)
-      hipLaunchKernelGGL(k2_state_pass8<true>, g2, dim3(kThreads), 0, st, a, PN);
+      launch_kernel(k2_state_pass8<true>, g2, dim3(kThreads), 0, st, a, PN);
     else
-      hipLaunchKernelGGL(k2_state_pass8<false>, g2, dim3(kThreads), 0, st, a, PN);
+      launch_kernel(k2_state_pass8<false>, g2, dim3(kThreads), 0, st, a, PN);
   } else if (phase == PHASE_STATE_PASS || phase == PHASE_ADJ_PASS) {
     const int PN = kP * N;
     dim3 g2((unsigned)((PN / 4 + kThreads - 1) / kThreads), (unsigned)a.H, (unsigned)(a.Z * a.ndir));
-    hipLaunchKernelGGL(k2_state_pass<T>, g2, dim3(kThreads), 0, st, a, PN,
+    launch_kernel(k2_state_pass<T>, g2, dim3(kThreads), 0, st, a, PN,
                        phase == PHASE_ADJ_PASS ? 1 : 0);
   } else {
     dim3 g((unsigned)(a.Z * a.nchunks * (a.chunk / kRB) * (a.H / HT)));
     if (phase == PHASE_YDOT)
-      hipLaunchKernelGGL((k3_chunk_out<T, N, HT, false, 1>), g, dim3(kThreads), 0, st, a);
+      launch_kernel((k3_chunk_out<T, N, HT, false, 1>), g, dim3(kThreads), 0, st, a);
     else if (phase == PHASE_DX)
-      hipLaunchKernelGGL((k3_chunk_out<T, N, HT, false, 2>), g, dim3(kThreads), 0, st, a);
+      launch_kernel((k3_chunk_out<T, N, HT, false, 2>), g, dim3(kThreads), 0, st, a);
     else if (a.xs[0] || a.xs[1]) {
       if (a.sin_f32[0] || a.sin_f32[1])
-        hipLaunchKernelGGL((k3_chunk_out<T, N, HT, true, 0, true>), g, dim3(kThreads), 0, st, a);
+        launch_kernel((k3_chunk_out<T, N, HT, true, 0, true>), g, dim3(kThreads), 0, st, a);
       else
-        hipLaunchKernelGGL((k3_chunk_out<T, N, HT, false, 0, true>), g, dim3(kThreads), 0, st, a);
+        launch_kernel((k3_chunk_out<T, N, HT, false, 0, true>), g, dim3(kThreads), 0, st, a);
     } else if (a.sin_f32[0] || a.sin_f32[1])
-      hipLaunchKernelGGL((k3_chunk_out<T, N, HT, true, 0>), g, dim3(kThreads), 0, st, a);
+      launch_kernel((k3_chunk_out<T, N, HT, true, 0>), g, dim3(kThreads), 0, st, a);
     else
-      hipLaunchKernelGGL((k3_chunk_out<T, N, HT, false, 0>), g, dim3(kThreads), 0, st, a);
+      launch_kernel((k3_chunk_out<T, N, HT, false, 0>), g, dim3(kThreads), 0, st, a);
   }
 }
 

@@ -2,10 +2,25 @@
 // kernel launchers (not part of the public interface).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace bissd {
+
+// The pair of events armed by bissd_timer_arm, handed to the first launch
+// that asks and then disarmed (both nullptr when none is armed).
+void take_timer(hipEvent_t *start, hipEvent_t *stop);
+
+// Every kernel launch of the library: hipExtLaunchKernelGGL records the
+// dispatch's own start and end timestamps in an armed timer's events.
+template <typename F, typename... Args>
+inline void launch_kernel(F kern, dim3 grid, dim3 block, uint32_t shmem, hipStream_t st,
+                          Args... args) {
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  take_timer(&e0, &e1);
+  hipExtLaunchKernelGGL(kern, grid, block, shmem, st, e0, e1, 0u, args...);
+}
 
 // Division by a runtime constant d (1 <= d < 2^31) of numerators n < 2^31 as
 // a multiply-high and a shift: with s = ceil(log2 d) and

@@ -344,3 +344,16 @@ def test_block_update_conv_state_aliasing(lib):
     assert blk(addr(40), C.c_void_p(A * 41 + 16)) == -7   # partially over conv_state_in
     assert blk(addr(40), addr(0)) == -7            # over x
     assert blk(C.c_void_p(A * 40 + 4), None) == -4   # misaligned
+
+
+def test_timer_validation(lib):
+    # no device call: out-of-range slots, a NULL result pointer, a slot that
+    # has never been armed, and disarming
+    assert lib.bissd_timer_arm(-2) == -2
+    assert lib.bissd_timer_arm(4096) == -2
+    assert lib.bissd_timer_arm(-1) == 0
+    ms = C.c_float(0.0)
+    assert lib.bissd_timer_read(-1, C.byref(ms)) == -2
+    assert lib.bissd_timer_read(4096, C.byref(ms)) == -2
+    assert lib.bissd_timer_read(4095, None) == -1
+    assert lib.bissd_timer_read(4095, C.byref(ms)) == -1
