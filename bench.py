@@ -22,7 +22,7 @@ the fp64 CPU oracle on a bounded sample of the same workload.  One JSON line
 is printed.
 
 Profiling helpers (for rocprofv3 runs):
-    python bench.py --profile-phase {0,1,2,3,all,backward,block,attention} [--workload W]
+    python bench.py --profile-phase {0,1,2,3,all,conv,backward,block,attention} [--workload W]
         [--iters R] [--settle S]   (S seconds of a bf16 matrix product first)
     python bench.py --copy-calibrate
 """
@@ -45,6 +45,7 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
 PHASE_NAMES = {0: "k1_chunk_state", 3: "k_gram", 1: "k2_state_pass", 2: "k3_chunk_out"}
 PHASE_ORDER = (0, 3, 1, 2)   # the order bissd_forward runs them in
 KERNEL_SOURCES = ("state_space_denoisers_amd/csrc/bissd_fwd.hip",
+                  "state_space_denoisers_amd/csrc/bissd_conv.hip",
                   "state_space_denoisers_amd/csrc/bissd_device.hpp",
                   "state_space_denoisers_amd/csrc/bissd_internal.hpp")
 
@@ -260,41 +261,67 @@ def bench_long(steps):
             "kernels_us": ph}
 
 
+class ConvForward:
+    """bissd_forward with the mixer's convolution on both directions (width
+    K, bias, SiLU; taps and biases from gen.make_conv) on workload w."""
+
+    def __init__(self, w, K=4):
+        import torch
+        import state_space_denoisers_amd as ssd
+        from state_space_denoisers_amd import _abi
+        from synth import gen
+        self.ssd, self.w, self.K = ssd, w, K
+        self.f = Forward(w)
+        dev = self.f.y.device
+        cv = gen.make_conv(w, K)
+        self.convs = [ssd.Dir(*p, conv_w=gen.as_torch(cv[f"conv_w_{d}"], "fp32", dev),
+                              conv_b=gen.as_torch(cv[f"conv_b_{d}"], "fp32", dev), conv_act=True)
+                      for d, p in (("f", self.f.fwd), ("r", self.f.rev))]
+        shape = ssd.shape_of(self.f.T["x"], self.f.T["B_f"], w.chunk, 0, K)
+        self.ws = torch.empty(ssd.bissd_workspace_size(shape, _abi.OP_FORWARD), dtype=torch.uint8,
+                              device=dev)
+
+    def __call__(self):
+        f = self.f
+        self.ssd.bissd_forward(f.T["x"], self.convs[0], self.convs[1], f.T["D"], chunk=self.w.chunk,
+                               y=f.y, workspace=self.ws)
+
+    def x_bytes(self):
+        x = self.f.T["x"]
+        return x.numel() * x.element_size()
+
+
 def bench_conv(steps, K=4):
     """The 130M-class layer forward with the mixer's convolution on both
     directions (width K, bias, SiLU): the convolution pass over x, then the
     scan on each direction's convolved x (the tokens/s of the whole call,
-    against the same call without the convolution)."""
+    against the same call without the convolution).  The convolution kernel
+    is the call's first launch; its duration comes from a library timer on
+    that dispatch, and its algorithmic bytes are x read once and the two
+    directions' convolved x written (3 x-sized tensors)."""
     import torch
-    import state_space_denoisers_amd as ssd
     from synth import gen
     w = gen.WORKLOADS["layer130m_L1k"]
-    f = Forward(w)
-    cv = gen.make_conv(w, K)
-    dev = f.y.device
-    convs = []
-    for d, p in (("f", f.fwd), ("r", f.rev)):
-        convs.append(ssd.Dir(*p, conv_w=gen.as_torch(cv[f"conv_w_{d}"], "fp32", dev),
-                             conv_b=gen.as_torch(cv[f"conv_b_{d}"], "fp32", dev), conv_act=True))
-    shape = ssd.shape_of(f.T["x"], f.T["B_f"], w.chunk, 0, K)
-    from state_space_denoisers_amd import _abi
-    ws = torch.empty(ssd.bissd_workspace_size(shape, _abi.OP_FORWARD), dtype=torch.uint8, device=dev)
-
-    def call():
-        ssd.bissd_forward(f.T["x"], convs[0], convs[1], f.T["D"], chunk=w.chunk, y=f.y, workspace=ws)
+    cf = ConvForward(w, K)
+    ssd = cf.ssd
     for _ in range(2):
-        call()
+        cf()
     torch.cuda.synchronize()
-    settle(call, LEG_SETTLE_S)
-    ms = event_time_ms(call, steps)
-    settle(f, LEG_SETTLE_S)
-    ms0 = event_time_ms(f, steps)
-    # the convolution pass reads x once and writes both directions' xc
-    xbytes = f.T["x"].numel() * f.T["x"].element_size()
-    extra_us = 1e3 * (ms - ms0)
+    settle(cf, LEG_SETTLE_S)
+    ms = event_time_ms(cf, steps)
+    reps = min(steps, ssd.TIMER_SLOTS)
+    for r in range(reps):
+        ssd.bissd_timer_arm(r)
+        cf()
+    torch.cuda.synchronize()
+    conv_us = 1e3 * sum(ssd.bissd_timer_read(r) for r in range(reps)) / reps
+    settle(cf.f, LEG_SETTLE_S)
+    ms0 = event_time_ms(cf.f, steps)
+    alg = 3 * cf.x_bytes()
     return {"workload": w.name + f"_conv{K}", "tokens_per_s": w.tokens / (ms * 1e-3), "us_per_call": 1e3 * ms,
-            "us_per_call_without_conv": 1e3 * ms0, "extra_us": round(extra_us, 2),
-            "conv_pass_algorithmic_bytes": 3 * xbytes}
+            "us_per_call_without_conv": 1e3 * ms0, "conv_kernel_us": round(conv_us, 2),
+            "conv_algorithmic_bytes": alg, "conv_achieved_GBs": round(alg / (conv_us * 1e-6) / 1e9, 1),
+            "conv_frac_hbm": round(alg / (conv_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def bench_block(reps):
@@ -670,6 +697,17 @@ def profile_phase(args):
         torch.cuda.synchronize()
         print("done", flush=True)
         return
+    if args.profile_phase == "conv":
+        cf = ConvForward(w)
+        cf()
+        settle(cf, args.settle)
+        torch.cuda.synchronize()
+        print(f"profiling forward with the width-4 convolution on {w.name} x{args.iters}", flush=True)
+        for _ in range(args.iters):
+            cf()
+        torch.cuda.synchronize()
+        print("done", flush=True)
+        return
     if args.profile_phase == "backward":
         t = Train(w)
         settle(t.backward, args.settle)
@@ -714,7 +752,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--profile-phase", choices=["0", "1", "2", "3", "all", "backward", "block", "attention"])
+    ap.add_argument("--profile-phase", choices=["0", "1", "2", "3", "all", "conv", "backward", "block",
+                                                "attention"])
     ap.add_argument("--workload", default="layer130m_L1k")
     ap.add_argument("--iters", type=int, default=20)
     ap.add_argument("--copy-calibrate", action="store_true")

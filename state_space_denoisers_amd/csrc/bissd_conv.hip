@@ -12,6 +12,8 @@
 //
 // (the reverse is the forward convolution of the flipped sequence); bound by
 // HBM.
+#include <type_traits>
+
 #include "bissd_device.hpp"
 #include "bissd_internal.hpp"
 
@@ -19,80 +21,177 @@ namespace bissd {
 
 namespace {
 
-__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+// SiLU on the transcendental unit: z / (1 + e^-z) = z rcp(1 + 2^(-z log2 e)).
+// For z very negative 2^(..) overflows to inf and the result is -0 (the
+// function's limit); for z very positive it is z.
+__device__ __forceinline__ float silu_f(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + exp2_fast(-z * kLog2e));
+}
+
+// C adjacent channels of one row (C = 2, 4 or 8: one 4- to 16-byte access
+// in bf16, 8 to 32 bytes in fp32), as floats
+template <int C> struct Vec;
+template <> struct Vec<2> { typedef __bf16 b __attribute__((ext_vector_type(2))); typedef float f __attribute__((ext_vector_type(2))); };
+template <> struct Vec<4> { typedef __bf16 b __attribute__((ext_vector_type(4))); typedef float f __attribute__((ext_vector_type(4))); };
+template <> struct Vec<8> { typedef __bf16 b __attribute__((ext_vector_type(8))); typedef float f __attribute__((ext_vector_type(4))); };
+
+template <int C>
+__device__ __forceinline__ void load_ch(float (&o)[C], const bf16 *p) {
+  const typename Vec<C>::b v = *reinterpret_cast<const typename Vec<C>::b *>(p);
+#pragma unroll
+  for (int e = 0; e < C; ++e) o[e] = (float)v[e];
+}
+template <int C>
+__device__ __forceinline__ void load_ch(float (&o)[C], const float *p) {
+  constexpr int W = C < 4 ? C : 4;  // floats per access
+#pragma unroll
+  for (int h = 0; h < C / W; ++h) {
+    const typename Vec<W>::f v = *reinterpret_cast<const typename Vec<W>::f *>(p + h * W);
+#pragma unroll
+    for (int e = 0; e < W; ++e) o[h * W + e] = v[e];
+  }
+}
+template <int C>
+__device__ __forceinline__ void store_ch(bf16 *p, const float (&o)[C]) {
+  typename Vec<C>::b v;
+#pragma unroll
+  for (int e = 0; e < C; ++e) v[e] = (bf16)o[e];
+  *reinterpret_cast<typename Vec<C>::b *>(p) = v;
+}
+template <int C>
+__device__ __forceinline__ void store_ch(float *p, const float (&o)[C]) {
+  constexpr int W = C < 4 ? C : 4;
+#pragma unroll
+  for (int h = 0; h < C / W; ++h) {
+    typename Vec<W>::f v;
+#pragma unroll
+    for (int e = 0; e < W; ++e) v[e] = o[h * W + e];
+    *reinterpret_cast<typename Vec<W>::f *>(p + h * W) = v;
+  }
+}
 
 }  // namespace
 
-// One thread: eight channels c0 .. c0 + 7 of a run of kRun consecutive
-// tokens, for both directions.  The run's rows and the K - 1 rows on either
-// side are loaded once (16-byte vectors, all issued before any is used), the
-// taps and biases once per run; consecutive threads take consecutive channel
-// vectors of the same rows, so every load and store is coalesced.
-constexpr int kRun = 8;
-template <typename T, int K>
+// One thread: the CPL channels c0 .. c0 + CPL - 1 of a run of RUN
+// consecutive tokens, both directions.  The run's rows and the K - 1 rows on
+// either side are loaded once, all requests issued before any value is used
+// and none behind a branch (a row outside the range reads a valid row and is
+// then zeroed); consecutive lanes take consecutive channel groups, so a wave
+// reads and writes whole row segments, and its taps (channel-major, K per
+// channel) are one contiguous block.  Runs start at multiples of RUN (a
+// divisor of 64), so a run never straddles a reverse block (a multiple of 64
+// tokens): every row at or past min(L, end of the run's reverse block) reads
+// as zero, which only the reverse direction's taps can reach.
+#ifndef BISSD_CONV_CPL
+#define BISSD_CONV_CPL 2
+#endif
+#ifndef BISSD_CONV_RUN
+#define BISSD_CONV_RUN 32
+#endif
+constexpr int kCpl = BISSD_CONV_CPL;
+constexpr int kRun = BISSD_CONV_RUN;
+static_assert(64 % kRun == 0 && kCpl >= 2 && kCpl <= 8 && 64 % kCpl == 0, "conv tiling");
+
+template <typename T, int K, int CPL, int RUN>
 __global__ __launch_bounds__(256) void k_conv_x(ConvArgs a) {
-  constexpr int NR = kRun + 2 * (K - 1);  // rows t0 - (K-1) .. t0 + kRun - 1 + (K-1)
-  const int nvec = a.HP / 8;
-  const int64_t nrun = (a.L + kRun - 1) / kRun;
+  constexpr int NR = RUN + 2 * (K - 1);  // rows t0 - (K-1) .. t0 + RUN - 1 + (K-1)
+  const int ngrp = a.HP / CPL;
+  const int64_t nrun = (a.L + RUN - 1) / RUN;
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (gid >= (int64_t)a.Z * nrun * nvec) return;
-  const int v = (int)(gid % nvec);
-  const int64_t zr = gid / nvec;
-  const int64_t t0 = (zr % nrun) * kRun;
+  if (gid >= (int64_t)a.Z * nrun * ngrp) return;
+  const int v = (int)(gid % ngrp);
+  const int64_t zr = gid / ngrp;
+  const int64_t t0 = (zr % nrun) * RUN;
   const int b = (int)(zr / nrun);
-  const int c0 = v * 8;
-  const T *xb = reinterpret_cast<const T *>(a.x) + (int64_t)b * a.L * a.HP + c0;
-  const T *sb = a.state ? reinterpret_cast<const T *>(a.state) + (int64_t)b * (K - 1) * a.HP + c0 : nullptr;
-  float row[NR][8];
+  const int c0 = v * CPL;
+  const int64_t HP = a.HP;
+  const T *xb = reinterpret_cast<const T *>(a.x) + (int64_t)b * a.L * HP + c0;
+  const T *sb = a.state ? reinterpret_cast<const T *>(a.state) + (int64_t)b * (K - 1) * HP + c0 : nullptr;
+  const int64_t rend = a.rev_block > 0 ? (t0 / a.rev_block + 1) * a.rev_block : a.L;
+  const int64_t lim = rend < a.L ? rend : a.L;
+  // row j holds token t0 - (K-1) + j: from x for jlo <= j < jhi, from the
+  // state for j < jlo when there is one, else zero
+  const int64_t first = t0 - (K - 1);
+  const int jlo = first >= 0 ? 0 : (int)(-first);
+  const int jhi = (int)((lim - first) < NR ? (lim - first) : NR);
+  float row[NR][CPL];
+  {
+    const T *p = xb + first * HP;  // row 0's address (not read unless valid)
+    // rows before the sequence exist only in the first run (t0 = 0, first =
+    // -(K-1)), where row j < K-1 is state row j
+    const T *q = sb ? sb : xb;
 #pragma unroll
-  for (int j = 0; j < NR; ++j) {
-    const int64_t tj = t0 - (K - 1) + j;
-    if (tj >= 0 && tj < a.L) {
-      gload8(row[j], xb + tj * a.HP);
-    } else if (tj < 0 && sb) {
-      gload8(row[j], sb + (tj + (K - 1)) * a.HP);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) row[j][e] = 0.0f;
+    for (int j = 0; j < NR; ++j) {
+      const bool in_x = j >= jlo && j < jhi;
+      const bool in_s = j < jlo && sb != nullptr;
+      load_ch<CPL>(row[j], in_x ? p : (in_s ? q : xb));
+      p += HP;
+      q += HP;
     }
   }
-  // the reverse reads nothing past the end of the run's reverse block (runs
-  // never straddle one: reverse blocks are multiples of 64 tokens)
-  const int64_t rend = a.rev_block > 0 ? (t0 / a.rev_block + 1) * a.rev_block : a.L;
+  float wv[2][CPL][K], bv[2][CPL];
 #pragma unroll
   for (int d = 0; d < 2; ++d) {
-    if (!a.xc[d]) continue;
-    float wv[8][K], bv[8];
+    // the group's taps: CPL K floats from an offset that is a multiple of 2
+    // floats, read as 8-byte pairs
+    const float *w = a.w[d] ? a.w[d] + (int64_t)c0 * K : nullptr;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int i = 0; i < CPL * K / 2; ++i) {
+      typename Vec<2>::f pr = {0.0f, 0.0f};
+      if (w) pr = *reinterpret_cast<const typename Vec<2>::f *>(w + 2 * i);
 #pragma unroll
-      for (int k = 0; k < K; ++k) wv[e][k] = a.w[d][(c0 + e) * K + k];
-      bv[e] = a.b[d] ? a.b[d][c0 + e] : 0.0f;
+      for (int e = 0; e < 2; ++e) {
+        const int f = 2 * i + e;  // flat index: channel f / K, tap f % K
+        wv[d][f / K][f % K] = pr[e];
+      }
     }
-    T *ob = reinterpret_cast<T *>(a.xc[d]) + (int64_t)b * a.L * a.HP + c0;
 #pragma unroll
-    for (int i = 0; i < kRun; ++i) {
-      const int64_t t = t0 + i;
-      if (t >= a.L) break;
-      float o[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = bv[e];
-#pragma unroll
-      for (int k = 0; k < K; ++k) {
-        // forward tap k reads row t - (K-1) + k (window row i + k); reverse
-        // tap k reads row t + (K-1) - k (window row i + 2(K-1) - k)
-        const int j = d == 0 ? i + k : i + 2 * (K - 1) - k;
-        const bool live = d == 0 || t + (K - 1) - k < rend;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] += live ? wv[e][k] * row[j][e] : 0.0f;
-      }
-      if (a.act[d]) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = silu_f(o[e]);
-      }
-      gstore8(ob + t * a.HP, o);
+    for (int i = 0; i < CPL / 2; ++i) {
+      typename Vec<2>::f bb = {0.0f, 0.0f};
+      if (a.b[d]) bb = *reinterpret_cast<const typename Vec<2>::f *>(a.b[d] + c0 + 2 * i);
+      bv[d][2 * i] = bb[0];
+      bv[d][2 * i + 1] = bb[1];
     }
   }
+#pragma unroll
+  for (int j = 0; j < NR; ++j) {
+    const bool keep = (j >= jlo && j < jhi) || (j < jlo && sb != nullptr);
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) row[j][e] = keep ? row[j][e] : 0.0f;
+  }
+  const int nst = (int)(a.L - t0 < RUN ? a.L - t0 : RUN);
+  auto emit = [&](auto full) {
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      if (!a.xc[d]) continue;
+      T *ob = reinterpret_cast<T *>(a.xc[d]) + ((int64_t)b * a.L + t0) * HP + c0;
+      const bool act = a.act[d] != 0;
+#pragma unroll
+      for (int i = 0; i < RUN; ++i) {
+        float o[CPL];
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) o[e] = bv[d][e];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          // forward tap k reads token t - (K-1) + k (row i + k); reverse tap
+          // k reads token t + (K-1) - k (row i + 2(K-1) - k)
+          const int j = d == 0 ? i + k : i + 2 * (K - 1) - k;
+#pragma unroll
+          for (int e = 0; e < CPL; ++e) o[e] += wv[d][e][k] * row[j][e];
+        }
+        if (act) {
+#pragma unroll
+          for (int e = 0; e < CPL; ++e) o[e] = silu_f(o[e]);
+        }
+        if (decltype(full)::value || i < nst) store_ch<CPL>(ob, o);
+        ob += HP;
+      }
+    }
+  };
+  if (nst == RUN)
+    emit(std::true_type{});
+  else
+    emit(std::false_type{});
 }
 
 template <typename T>
@@ -116,14 +215,14 @@ __global__ __launch_bounds__(256) void k_conv_state(const T *x, const T *sin, T 
 }
 
 hipError_t launch_conv(const ConvArgs &a, hipStream_t st) {
-  const int64_t n = (int64_t)a.Z * ((a.L + kRun - 1) / kRun) * (a.HP / 8);
+  const int64_t n = (int64_t)a.Z * ((a.L + kRun - 1) / kRun) * (a.HP / kCpl);
   const dim3 g((unsigned)((n + 255) / 256));
 #define BISSD_CONV_LAUNCH(TT)                                                           \
   switch (a.K) {                                                                        \
-    case 1: launch_kernel((k_conv_x<TT, 1>), g, dim3(256), 0, st, a); break;       \
-    case 2: launch_kernel((k_conv_x<TT, 2>), g, dim3(256), 0, st, a); break;       \
-    case 3: launch_kernel((k_conv_x<TT, 3>), g, dim3(256), 0, st, a); break;       \
-    default: launch_kernel((k_conv_x<TT, 4>), g, dim3(256), 0, st, a); break;      \
+    case 1: launch_kernel((k_conv_x<TT, 1, kCpl, kRun>), g, dim3(256), 0, st, a); break;       \
+    case 2: launch_kernel((k_conv_x<TT, 2, kCpl, kRun>), g, dim3(256), 0, st, a); break;       \
+    case 3: launch_kernel((k_conv_x<TT, 3, kCpl, kRun>), g, dim3(256), 0, st, a); break;       \
+    default: launch_kernel((k_conv_x<TT, 4, kCpl, kRun>), g, dim3(256), 0, st, a); break;      \
   }
   if (a.dtype == 1) {
     BISSD_CONV_LAUNCH(bf16)
