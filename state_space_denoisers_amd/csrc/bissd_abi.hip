@@ -107,7 +107,7 @@ int check_shape(const bissd_shape_t *s, int op) {
 struct WsLayout {
   size_t states = 0, sin_t = 0, cdecay = 0, gram = 0, xc = 0, xc_bytes = 0;
   size_t tstates = 0, sa_t = 0, gin_t = 0, dtsum = 0, ydot = 0, qx = 0, qxs = 0, ddpart = 0, dAintra = 0,
-         dAx1 = 0, dAx2 = 0, rpart = 0, lamg = 0, cdtg = 0, dbpart = 0;
+         dAx1 = 0, rpart = 0, lamg = 0, cdtg = 0, dbpart = 0;
   size_t total = 0;
 };
 
@@ -148,7 +148,6 @@ WsLayout ws_layout(const bissd_shape_t *s, int op) {
     w.ddpart = take(rb);
     w.dAintra = take(2 * rb);
     w.dAx1 = take(cd);
-    w.dAx2 = take(cd);
     w.rpart = take(cd * (size_t)(s->headdim * s->dstate / 256));
     w.lamg = take(tok);
     w.cdtg = take(tok);
@@ -645,7 +644,8 @@ int bissd_backward(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, bissd
 
   // adjoint chunk states sum_t 2^cum_t dy_t (outer) C_t (into the tangent
   // buffer, now consumed) with <G_loc, S^A_in>, then their carries with the
-  // chunk-boundary inner products, then <G^T_loc, S_in>
+  // chunk-boundary inner products (the other cross-chunk part of dA,
+  // <sum_t 2^cum_t T_t dy_t (outer) C_t, S_in>, comes with the dy.y_d pass)
   ScanArgs g = a;
   g.x = dy;
   g.B[0] = fwd.C;
@@ -660,10 +660,6 @@ int bissd_backward(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, bissd
   gp.sin_t = ws + wl.gin_t;
   gp.out0 = (float *)(ws + wl.rpart);
   if (e == hipSuccess) e = bissd::launch_scan_phase(gp, bissd::PHASE_ADJ_PASS, st);
-  ScanArgs gt = g;
-  for (int d = 0; d < 2; ++d) gt.sin[d] = a.sin[d];
-  gt.out0 = (float *)(ws + wl.dAx2);
-  if (e == hipSuccess) e = bissd::launch_scan_phase(gt, bissd::PHASE_ADJ_TAN, st);
 
   // dy.y_d per direction (forward output recomputed from the carry-ins)
   ScanArgs yd = a;
@@ -750,7 +746,6 @@ int bissd_backward(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, bissd
   b.rpart = (const float *)(ws + wl.rpart);
   b.dAintra = (float *)(ws + wl.dAintra);
   b.dAx1 = (const float *)(ws + wl.dAx1);
-  b.dAx2 = (const float *)(ws + wl.dAx2);
   b.ddpart = (const float *)(ws + wl.ddpart);
   b.lamg = (const float *)(ws + wl.lamg);
   b.cdtg = (const float *)(ws + wl.cdtg);

@@ -646,7 +646,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_reduce(BwdArgs a) {
     const int64_t nbc = (int64_t)a.Z * a.nchunks;
     for (int64_t i = tid; i < nbc; i += kThreads) {
       const int64_t k = ((int64_t)d * nbc + i) * H + h;
-      s += a.dAx1[k] + a.dAx2[k];
+      s += a.dAx1[k];
     }
   }
   const int64_t n = (int64_t)a.Z * a.nchunks * NRB;

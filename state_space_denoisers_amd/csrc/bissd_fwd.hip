@@ -125,8 +125,7 @@ template <typename T, int N, int HT> struct K1Lds {
 //                                      (dy passed as x, C as B), also <state, sin>
 //   MODE 2  w_s = dt_s 2^(cum_end - cum_s) (T_end - T_s)   A-tangent state, and
 //                                      T_end per chunk to out1
-//   MODE 3  w_s = 2^cum_s T_s          (dy, C as in MODE 1) only <state, sin>
-// MODEs 1-3 leave the chunk decays as MODE 0 wrote them.  64-token slabs are fetched into registers one slab
+// MODEs 1 and 2 leave the chunk decays as MODE 0 wrote them.  64-token slabs are fetched into registers one slab
 // ahead of the matrix-core work and stored row-major; both operands are read
 // with k (the token) running down the rows.  Output
 // states[d][b][c][h][p][n] (compute dtype, rounded once from the fp32
@@ -176,7 +175,7 @@ void k1_chunk_state(ScanArgs a) {
   // decay scans, wave w taking head w % HT (waves HT .. 2 HT - 1: the plain
   // cumulative dt of the tangent modes).  The dt loads go out first, raw and
   // unconditional (tokens past L read as zero), then the first slab's loads.
-  constexpr bool TAN = MODE >= 2;
+  constexpr bool TAN = MODE == 2;
   constexpr int NPR = (TAN ? 2 : 1) * HT;
   static_assert(NPR <= kThreads / 64, "one decay scan per wave");
   // Gram pair of this workgroup and the C rows of its row-block (raw loads,
@@ -241,8 +240,6 @@ void k1_chunk_state(ScanArgs a) {
     float v;
     if (MODE == 1) {
       v = exp2_fast(sm.lam[hh][s]);
-    } else if (MODE == 3) {
-      v = exp2_fast(sm.lam[hh][s]) * sm.cdt[hh][s];
     } else {
       v = dv != 0.0f ? dv * exp2_fast(ref - sm.lam[hh][s]) : 0.0f;
       if (MODE == 2) v *= (d == 0 ? sm.cdt[hh][Q - 1] : sm.cdt[hh][0]) - sm.cdt[hh][s];
@@ -340,7 +337,7 @@ void k1_chunk_state(ScanArgs a) {
             *reinterpret_cast<const u32x4 *>(stile + v * EPV);
     }
   }
-  if constexpr (MODE == 1 || MODE == 3) {
+  if constexpr (MODE == 1) {
     // Frobenius product with the given state of the same (direction, batch,
     // chunk, head), reduced in a fixed order
     const T *ref = reinterpret_cast<const T *>(a.sin[d]) + (int64_t)b * a.sin_bstride[d] +
@@ -1351,9 +1348,19 @@ void k3_chunk_out(ScanArgs a) {
           }
 #pragma unroll
           for (int i2 = 0; i2 < 4; ++i2) {
-            const float et = exp2_fast(sm.lam[d][hh][j * kRB + 16 * w + 4 * g4 + i2]);
+            const int tr = j * kRB + 16 * w + 4 * g4 + i2;
+            const float et = exp2_fast(sm.lam[d][hh][tr]);
 #pragma unroll
             for (int v = 0; v < 4; ++v) acc[hh][v][i2] += et * t2[v][i2];
+            if constexpr (DAI) {
+              // the carried state's part of dA: T_t 2^lam_t C_t S_in, whose
+              // dot with dy summed over the chunk is <sum_t 2^lam_t T_t dy_t
+              // (outer) C_t, S_in>, the tangent-weighted adjoint chunk state
+              // against the carry-in
+              const float tt = smcdt[d][hh][tr] * et;
+#pragma unroll
+              for (int v = 0; v < 4; ++v) acc2[hh][v][i2] += tt * t2[v][i2];
+            }
           }
         }
       }
@@ -1576,17 +1583,14 @@ void k3_chunk_out(ScanArgs a) {
 
 template <typename T, int N, int HT>
 static void launch_t(const ScanArgs &a, int phase, hipStream_t st) {
-  if (phase == PHASE_CHUNK_STATE || phase == PHASE_ADJ_STATE || phase == PHASE_TAN_STATE ||
-      phase == PHASE_ADJ_TAN) {
+  if (phase == PHASE_CHUNK_STATE || phase == PHASE_ADJ_STATE || phase == PHASE_TAN_STATE) {
     dim3 g((unsigned)(a.Z * a.nchunks * a.ndir * (a.H / HT)));
     if (phase == PHASE_CHUNK_STATE)
       launch_kernel((k1_chunk_state<T, N, HT, 0>), g, dim3(kThreads), 0, st, a);
     else if (phase == PHASE_ADJ_STATE)
       launch_kernel((k1_chunk_state<T, N, HT, 1>), g, dim3(kThreads), 0, st, a);
-    else if (phase == PHASE_TAN_STATE)
-      launch_kernel((k1_chunk_state<T, N, HT, 2>), g, dim3(kThreads), 0, st, a);
     else
-      launch_kernel((k1_chunk_state<T, N, HT, 3>), g, dim3(kThreads), 0, st, a);
+      launch_kernel((k1_chunk_state<T, N, HT, 2>), g, dim3(kThreads), 0, st, a);
   } else if (phase == PHASE_GRAM) {
     // one workgroup per (batch, chunk, slot, group, row-block / column-block
     // pair on the slot's side)

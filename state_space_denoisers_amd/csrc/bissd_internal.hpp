@@ -84,7 +84,7 @@ struct ScanArgs {
   // backward phases only
   const void *aux;  // PHASE_YDOT: dy; PHASE_DX: x (x above then holds dy)
   float *out0;      // PHASE_YDOT: dy.y_d; PHASE_DX: x.(G_t B_t); [2][Z][L][H], by direction.
-                    // PHASE_ADJ_STATE / PHASE_ADJ_TAN: <state, sin> per [2][Z][nchunks][H].
+                    // PHASE_ADJ_STATE: <state, sin> per [2][Z][nchunks][H].
                     // PHASE_ADJ_PASS: wave partials of <adjoint carry, state after the chunk>
   float *out1;      // PHASE_DX: dx [Z][L][H][P]; PHASE_TAN_STATE: chunk dt sums [2][Z][nchunks][H]
   float *out2;      // PHASE_DX: partial sums of dy.x per (b, chunk, row-block, head)
@@ -133,7 +133,6 @@ enum {
   PHASE_DX = 6,           // dx and x.(G_t B_t)
   PHASE_TAN_STATE = 7,    // chunk-local A-tangent states (dt-sum weighted)
   PHASE_TAN_PASS = 8,     // A-tangent carry-in states
-  PHASE_ADJ_TAN = 9,      // <dt-sum weighted adjoint chunk state, carry-in state>
   PHASE_GRAM = 10,        // chunk Gram tiles for the output kernel
 };
 
@@ -188,7 +187,7 @@ struct BwdArgs {
   float *dB[2], *dC[2], *ddt[2], *dA[2], *dD;
   const float *rpart;   // [2][Z][nchunks][H][P N / 256] wave partials of the chunk-boundary dalpha
   float *dAintra;       // [2][Z][nchunks][chunk/64][H] within-chunk A-tangent sums
-  const float *dAx1, *dAx2;  // [2][Z][nchunks][H] cross-chunk A-tangent inner products
+  const float *dAx1;    // [2][Z][nchunks][H] <adjoint chunk state, A-tangent carry-in>
   const float *ddpart;  // [Z][nchunks][chunk/64][H]
   const float *lamg;    // [2][Z][H][L] in-chunk log2-decay sums (scan order)
   const float *cdtg;    // [2][Z][H][L] in-chunk cumulative dt (scan order)

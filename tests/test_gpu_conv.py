@@ -13,7 +13,7 @@ import state_space_denoisers_amd as ssd
 from oracle import conv as CV
 from oracle import oracle as O
 from synth import gen
-from tests.gpu_util import TOL, f32_dev, host, maxrel, to_dev
+from tests.gpu_util import TOL, f32_dev, host, maxrel, select_rows, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -49,6 +49,24 @@ def test_forward_with_convolution(dtype, L, chunk, K, mode):
     e = maxrel(host(y), CV.forward(inp, oracle_convs(cv)))
     print(f"err={e:.2e}", flush=True)
     assert e <= TOL[dtype]
+
+
+@pytest.mark.parametrize("mode", ("full", "scan"))
+def test_layer130m_L1k_with_convolution(mode):
+    """The bench's convolution leg at its size (Z=8, L=1024, 24 heads, N=128,
+    chunk 256, bf16, width 4 on both directions); the oracle checks batch
+    rows 0 and 7."""
+    w = W["layer130m_L1k"]
+    inp = gen.make_inputs(w, mode=mode)
+    cv = gen.make_conv(w, 4)
+    T = to_dev(inp, "bf16")
+    f, r = conv_dirs(inp, T, cv)
+    print("conv layer130m_L1k", mode, flush=True)
+    y = host(ssd.bissd_forward(T["x"], f, r, T["D"], chunk=w.chunk))
+    rows = [0, 7]
+    e = maxrel(y[rows], CV.forward(select_rows(inp, rows), oracle_convs(cv)))
+    print(f"err={e:.2e}", flush=True)
+    assert e <= TOL["bf16"]
 
 
 @pytest.mark.parametrize("which", [("f",), ("r",)])
