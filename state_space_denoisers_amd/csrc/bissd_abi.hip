@@ -627,10 +627,10 @@ int bissd_backward(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, bissd
   ScanArgs a0 = a;
   a0.cum_out = (float *)(ws + wl.lamg);
   hipError_t e = bissd::launch_scan_phase(a0, bissd::PHASE_CHUNK_STATE, st);
-  if (e == hipSuccess) e = bissd::launch_scan_phase(a, bissd::PHASE_STATE_PASS, st);
 
   // A-tangent chunk states (dt-sum weighted), chunk dt sums (and every
-  // token's cumulative dt), and the A-tangent carry-ins S^A_in
+  // token's cumulative dt), and the A-tangent carry-ins S^A_in together with
+  // the primal carry-ins S_in (the tangent's recurrence carries S_in anyway)
   ScanArgs ta = a;
   ta.states = (void *)(ws + wl.tstates);
   ta.out1 = (float *)(ws + wl.dtsum);
@@ -640,6 +640,7 @@ int bissd_backward(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, bissd
   tp.states2 = (const void *)(ws + wl.tstates);
   tp.dtsum = (const float *)(ws + wl.dtsum);
   tp.sin_t = ws + wl.sa_t;
+  tp.sin_prim = a.sin_t;
   if (e == hipSuccess) e = bissd::launch_scan_phase(tp, bissd::PHASE_TAN_PASS, st);
 
   // adjoint chunk states sum_t 2^cum_t dy_t (outer) C_t (into the tangent

@@ -644,7 +644,8 @@ __global__ __launch_bounds__(kThreads) void k2_state_pass8(ScanArgs a, int PN) {
 // A-tangent of the carry-in states, four elements per thread:
 // SA_in(c+1) = 2^cdecay(c) (SA_in(c) + Tsum(c) S_in(c)) + ST_loc(c), from zero,
 // alongside the primal carry S_in (from init_state or zero), in each
-// direction's scan order; SA_in of every chunk goes to sin_t in T.  Loads run
+// direction's scan order; SA_in of every chunk goes to sin_t in T (and S_in
+// to sin_prim when set, which makes the primal state pass unnecessary).  Loads run
 // D chunks ahead as in the state pass.  Both carries of a block-segmented
 // reverse restart from zero at its block boundaries.
 template <typename T>
@@ -659,6 +660,7 @@ __global__ __launch_bounds__(kThreads) void k2_tangent_pass(ScanArgs a, int PN) 
   const T *sl = reinterpret_cast<const T *>(a.states) + base;
   const T *tl = reinterpret_cast<const T *>(a.states2) + base;
   T *dst = reinterpret_cast<T *>(a.sin_t) + base;
+  T *pdst = a.sin_prim ? reinterpret_cast<T *>(a.sin_prim) + base : nullptr;
   const float *dec = a.cdecay + ((int64_t)d * a.Z + b) * nc * H + h;
   const float *tsum = a.dtsum + ((int64_t)d * a.Z + b) * nc * H + h;
   f32x4 S = {0.0f, 0.0f, 0.0f, 0.0f}, SA = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -699,12 +701,17 @@ __global__ __launch_bounds__(kThreads) void k2_tangent_pass(ScanArgs a, int PN) 
       }
       bmod = bmod == 0 ? rsc - 1 : bmod - 1;
       if constexpr (sizeof(T) == 2) {
-        bf16x4 o;
+        bf16x4 o, op;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) o[k] = (bf16)SA[k];
+        for (int k = 0; k < 4; ++k) {
+          o[k] = (bf16)SA[k];
+          op[k] = (bf16)S[k];
+        }
         *reinterpret_cast<bf16x4 *>(dst + c * cs) = o;
+        if (pdst) *reinterpret_cast<bf16x4 *>(pdst + c * cs) = op;
       } else {
         *reinterpret_cast<f32x4 *>(dst + c * cs) = SA;
+        if (pdst) *reinterpret_cast<f32x4 *>(pdst + c * cs) = S;
       }
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -728,6 +735,7 @@ __global__ __launch_bounds__(kThreads) void k2_tangent_pass8(ScanArgs a, int PN)
   const bf16 *sl = reinterpret_cast<const bf16 *>(a.states) + base;
   const bf16 *tl = reinterpret_cast<const bf16 *>(a.states2) + base;
   bf16 *dst = reinterpret_cast<bf16 *>(a.sin_t) + base;
+  bf16 *pdst = a.sin_prim ? reinterpret_cast<bf16 *>(a.sin_prim) + base : nullptr;
   const float *dec = a.cdecay + ((int64_t)d * a.Z + b) * nc * H + h;
   const float *tsum = a.dtsum + ((int64_t)d * a.Z + b) * nc * H + h;
   f32x4 S0 = {0.0f, 0.0f, 0.0f, 0.0f}, S1 = S0, A0 = S0, A1 = S0;
@@ -775,6 +783,7 @@ __global__ __launch_bounds__(kThreads) void k2_tangent_pass8(ScanArgs a, int PN)
       }
       bmod = bmod == 0 ? rsc - 1 : bmod - 1;
       *reinterpret_cast<bf16x8 *>(dst + c * cs) = narrow8(A0, A1);
+      if (pdst) *reinterpret_cast<bf16x8 *>(pdst + c * cs) = narrow8(S0, S1);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         A0[k] = g * (A0[k] + ts * S0[k]) + t0[k];

@@ -90,6 +90,8 @@ struct ScanArgs {
   float *out2;      // PHASE_DX: partial sums of dy.x per (b, chunk, row-block, head)
   float *out3;      // PHASE_DX: x.(G_t B_t) without the t' = t term, [2][Z][L][H]
   const void *states2;   // PHASE_TAN_PASS: tangent chunk states, compute dtype
+  void *sin_prim;        // PHASE_TAN_PASS: if set, also the primal carry-in states it
+                         // carries alongside, compute dtype, laid out as sin_t
   const float *dtsum;    // PHASE_TAN_PASS: chunk dt sums
   int slot_dir[2];  // direction under which each output-kernel slot stores out0
   // divisors of the workgroup-index splits (set by launch_scan_phase): head
