@@ -90,7 +90,7 @@ template <typename T, int N> struct PanelLds {
 // multiplied; with one (used: 38 KB of LDS), three workgroups per CU overlap
 // each other's copies.  Each head costs one or two barriers.
 template <typename T, int N, int PNL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 4 : 1)))
 void k_bwd_panel(BwdArgs a) {
   using Sm = PanelLds<T, N>;
   constexpr uint32_t ES = sizeof(T);
