@@ -161,6 +161,23 @@ def phase_times_us(f: Forward, reps):
     return out
 
 
+def state_pass_line(w, ph):
+    """The carry pass (the memory-bound scan phase): its live average
+    duration and its HBM bytes per launch from the committed counter runs
+    (FETCH_SIZE + WRITE_SIZE, calibrated; null when they were taken on
+    other kernel sources), against the 8 TB/s peak."""
+    us = ph.get(PHASE_NAMES[1])
+    if us is None:
+        return None
+    traffic = stored_traffic(PHASE_NAMES[1], w.name)
+    out = {"kernel": PHASE_NAMES[1], "avg_launch_us": round(us, 2), "traffic": traffic,
+           "unit": "GB/s", "peak": HBM_PEAK_GBS}
+    if traffic:
+        gbs = traffic / (us * 1e-6) / 1e9
+        out.update({"achieved_by_counters": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)})
+    return out
+
+
 def per_token_bytes(w):
     """Algorithmic HBM bytes per token of the whole path: read x, dt and
     B/C of both directions once, write y once."""
@@ -826,7 +843,8 @@ def main():
              "trials_us_per_step": {"values": [round(t, 2) for t in trials],
                                     "median": round(float(sorted(trials)[2]), 2)},
              "path_hbm_algorithmic_GBs": round(per_token_bytes(w) * tokens / (ev_ms * 1e-3) / 1e9, 1),
-             "k3_mfma": mfma}
+             "k3_mfma": mfma,
+             "state_pass": state_pass_line(w, ph)}
     if not args.no_extra:
         try:
             extra["long_L65k"] = bench_long(max(5, args.steps // 20))
