@@ -196,3 +196,56 @@ def test_backward_rejects_a_convolution():
     f, r = conv_dirs(inp, T, cv)
     with pytest.raises(ssd.BissdError):
         ssd.bissd_backward(T["x"], f, r, T["D"], T["dy"], chunk=64)
+
+
+def full_dirs(inp, T, cv):
+    """Directions with dt post-processing and the convolution together."""
+    out = []
+    for d in ("f", "r"):
+        b = gen.as_torch(inp[f"dt_bias_{d}"], "fp32", T["x"].device)
+        out.append(ssd.Dir(T[f"dt_{d}"], T[f"A_{d}"], T[f"B_{d}"], T[f"C_{d}"], b,
+                           inp[f"dt_min_{d}"], inp[f"dt_max_{d}"],
+                           conv_w=f32_dev(cv[f"conv_w_{d}"]), conv_b=f32_dev(cv[f"conv_b_{d}"]),
+                           conv_act=True))
+    return out
+
+
+@pytest.mark.parametrize("dtype", ("fp32", "bf16"))
+def test_convolution_with_dt_post_and_reverse_blocks(dtype):
+    """Every option of the forward at once: each direction's dt through its
+    bias, softplus and clamp, its width-3 convolution, and the reverse scan
+    restarting at every 64-token block (chunks of 128, a ragged tail)."""
+    w = W["tiny_fp32"].replace(Z=2, L=500, H=6, N=128, chunk=128, dtype=dtype, seed=421)
+    inp = gen.with_dt_post(gen.make_inputs(w, mode="scan"), w)
+    cv = gen.make_conv(w, 3)
+    T = to_dev(inp, dtype)
+    f, r = full_dirs(inp, T, cv)
+    print("conv + dt post + rev_block 64", dtype, flush=True)
+    y = ssd.bissd_forward(T["x"], f, r, T["D"], chunk=128, rev_block=64)
+    torch.cuda.synchronize()
+    e = maxrel(host(y), CV.forward(inp, oracle_convs(cv), rev_block=64))
+    print(f"err={e:.2e}", flush=True)
+    assert e <= TOL[dtype]
+
+
+@pytest.mark.parametrize("Lb", (40, 100))
+def test_block_update_with_dt_post_and_conv_state(Lb):
+    """The block update with dt post-processing and the convolution together,
+    continuing a cached state and a conv state, both committed (in place)."""
+    w = W["block_update"].replace(Z=2, L=Lb, H=6, dtype="bf16", seed=433 + Lb)
+    inp = gen.with_dt_post(gen.make_inputs(w, mode="scan"), w)
+    cv = gen.make_conv(w, 4)
+    cst = gen.make_conv_state(w, 4)
+    S0 = gen.round_fp32(np.random.default_rng(9).standard_normal((2, 6, 64, 128)) * 0.05)
+    T = to_dev(inp, "bf16")
+    f, r = full_dirs(inp, T, cv)
+    state = f32_dev(S0)
+    cstate = gen.as_torch(cst, "bf16", T["x"].device)
+    print("block + dt post + conv state", Lb, flush=True)
+    y, so = ssd.bissd_block_update(state, T["x"], f, r, T["D"], chunk=128 if Lb > 64 else 64,
+                                   state_out=state, conv_state=cstate, conv_state_out=cstate)
+    torch.cuda.synchronize()
+    ry, rso, rcs = CV.block_update(inp, oracle_convs(cv), S0, cst)
+    assert maxrel(host(y), ry) <= TOL["bf16"]
+    assert maxrel(host(so), rso) <= TOL["bf16"]
+    assert np.array_equal(host(cstate), rcs)
