@@ -263,7 +263,9 @@ int bissd_block_update(const bissd_shape_t *shape, const float *state_in,
 /*
  * Diagnostics for timing and profiling single kernels: enqueue only one
  * phase of bissd_forward with the same arguments and validation.
- *   phase 0: per-chunk local states and chunk decays (written to workspace)
+ *   phase 0: per-chunk local states and chunk decays (written to workspace);
+ *            with the convolution (conv_width > 0) first the convolution
+ *            pass that writes both directions' convolved x to the workspace
  *   phase 3: per-chunk Gram tiles C.B^T of both directions (workspace);
  *            nothing to do when phase 0 forms them itself, which it does
  *            when every B/C group has at least (chunk/64)(chunk/64 + 1)/2
@@ -354,8 +356,9 @@ int bissd_last_hip_error(void);
  * library makes in this process, on any stream and from any call, which
  * records its dispatch's start and end timestamps in them; the slot is then
  * disarmed.  Arming replaces a slot armed before; slot -1 disarms.  The
- * events are created on a slot's first arming (on the current device) and
- * kept until the process ends.  bissd_timer_read(slot, &ms) waits for the
+ * events are created on a slot's first arming on the current device (again
+ * when the slot is armed on another device) and kept until the process
+ * ends.  bissd_timer_read(slot, &ms) waits for the
  * slot's end event and returns the kernel's duration in milliseconds
  * (BISSD_ERR_HIP if that slot has recorded nothing).  Process-wide state:
  * callers that launch from several threads at once get no defined pairing.

@@ -6,6 +6,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "bissd.h"
@@ -287,20 +288,25 @@ int finish(hipError_t e) {
   return BISSD_OK;
 }
 
-// Kernel timers: per slot a pair of events (created on the slot's first
-// arming), and the one armed slot (-1: none).
+// Kernel timers: per slot a pair of events and the device they were created
+// on (created on the slot's first arming on that device), and the one armed
+// slot (-1: none; read without the lock by every launch, so a launch with
+// no timer armed takes no lock).
 std::mutex g_timer_mu;
 hipEvent_t g_timer_ev[BISSD_TIMER_SLOTS][2] = {};
-int g_timer_armed = -1;
+int g_timer_dev[BISSD_TIMER_SLOTS] = {};
+std::atomic<int> g_timer_armed{-1};
 
 }  // namespace
 
 void bissd::take_timer(hipEvent_t *start, hipEvent_t *stop) {
+  if (g_timer_armed.load(std::memory_order_relaxed) < 0) return;
   std::lock_guard<std::mutex> lock(g_timer_mu);
-  if (g_timer_armed < 0) return;
-  *start = g_timer_ev[g_timer_armed][0];
-  *stop = g_timer_ev[g_timer_armed][1];
-  g_timer_armed = -1;
+  const int slot = g_timer_armed.load(std::memory_order_relaxed);
+  if (slot < 0) return;
+  *start = g_timer_ev[slot][0];
+  *stop = g_timer_ev[slot][1];
+  g_timer_armed.store(-1, std::memory_order_relaxed);
 }
 
 extern "C" {
@@ -313,17 +319,32 @@ int bissd_timer_arm(int32_t slot) {
   if (slot < -1 || slot >= BISSD_TIMER_SLOTS) return BISSD_ERR_SHAPE;
   std::lock_guard<std::mutex> lock(g_timer_mu);
   if (slot >= 0) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+      g_last_hip = (int)e;
+      return BISSD_ERR_HIP;
+    }
+    // events belong to the device they were created on: a slot armed on
+    // another device gets new ones
+    if (g_timer_ev[slot][0] && g_timer_dev[slot] != dev) {
+      for (int i = 0; i < 2; ++i) {
+        (void)hipEventDestroy(g_timer_ev[slot][i]);
+        g_timer_ev[slot][i] = nullptr;
+      }
+    }
     for (int i = 0; i < 2; ++i)
       if (!g_timer_ev[slot][i]) {
-        const hipError_t e = hipEventCreate(&g_timer_ev[slot][i]);
+        e = hipEventCreate(&g_timer_ev[slot][i]);
         if (e != hipSuccess) {
           g_timer_ev[slot][i] = nullptr;
           g_last_hip = (int)e;
           return BISSD_ERR_HIP;
         }
       }
+    g_timer_dev[slot] = dev;
   }
-  g_timer_armed = slot;
+  g_timer_armed.store(slot, std::memory_order_relaxed);
   return BISSD_OK;
 }
 
