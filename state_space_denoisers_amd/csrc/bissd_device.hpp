@@ -84,6 +84,23 @@ template <typename T> struct Frag;
 template <> struct Frag<bf16> { bf16x8 v; };
 template <> struct Frag<float> { float v[8]; };
 
+// Elements 0..3 (hi false) or 4..7 (hi true) of a fragment as floats: whole
+// registers are selected (two selections in bf16), never single elements,
+// so a lane-uniform choice costs no per-element selection chain.
+__device__ __forceinline__ void frag_half(const Frag<bf16> &f, bool hi, float (&o)[4]) {
+  typedef uint32_t w4 __attribute__((ext_vector_type(4)));
+  const w4 r = __builtin_bit_cast(w4, f.v);
+  const uint32_t a = hi ? r[2] : r[0], b = hi ? r[3] : r[1];
+  o[0] = __builtin_bit_cast(float, a << 16);
+  o[1] = __builtin_bit_cast(float, a & 0xffff0000u);
+  o[2] = __builtin_bit_cast(float, b << 16);
+  o[3] = __builtin_bit_cast(float, b & 0xffff0000u);
+}
+__device__ __forceinline__ void frag_half(const Frag<float> &f, bool hi, float (&o)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = hi ? f.v[4 + i] : f.v[i];
+}
+
 __device__ __forceinline__ void frag_zero(Frag<bf16> &f) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) f.v[e] = (bf16)0.0f;

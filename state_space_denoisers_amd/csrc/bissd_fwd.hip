@@ -1294,20 +1294,16 @@ void k3_chunk_out(ScanArgs a) {
             // the skip D x: on the diagonal s-block, fragment q = w / 2 holds
             // x at this lane's own accumulator positions (rows 16 w + 4 g4 +
             // i, column 16 v + r16), in its low (even w) or high (odd w) half
-            // (w is wave-uniform: a branch with fixed element indices, not a
-            // per-element selection among the fragment's eight values)
+            // (frag_half selects whole registers: a per-element index would
+            // compile to a selection chain over all eight values)
             if (q == (w >> 1)) {
               const float Dh = a.D[h0 + hh];
-              if (w & 1) {
 #pragma unroll
-                for (int v = 0; v < 4; ++v)
+              for (int v = 0; v < 4; ++v) {
+                float xh[4];
+                frag_half(xf[v], (w & 1) != 0, xh);
 #pragma unroll
-                  for (int i2 = 0; i2 < 4; ++i2) acc[hh][v][i2] += Dh * (float)xf[v].v[4 + i2];
-              } else {
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-#pragma unroll
-                  for (int i2 = 0; i2 < 4; ++i2) acc[hh][v][i2] += Dh * (float)xf[v].v[i2];
+                for (int i2 = 0; i2 < 4; ++i2) acc[hh][v][i2] += Dh * xh[i2];
               }
             }
           }
