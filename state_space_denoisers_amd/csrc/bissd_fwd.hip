@@ -970,7 +970,6 @@ void k3_chunk_out(ScanArgs a) {
   const int qlen = (int)((L - t0) < Q ? (L - t0) : Q);
   if (j * kRB >= qlen) return;
   const int gidx = (int)a.fd_hpg.div((uint32_t)h0);
-  const T *xg = reinterpret_cast<const T *>(a.x) + (((int64_t)b * L + t0) * H + h0) * kP;
   const int64_t xrs = (int64_t)H * kP;
   constexpr uint32_t ES = sizeof(T);
   // one buffer per batch row: tokens past L read as zero
@@ -1426,14 +1425,72 @@ void k3_chunk_out(ScanArgs a) {
     // Backward modes: each slot's accumulator is finished on its own.  Rows
     // are staged through LDS; 8 consecutive lanes hold one row of one head
     // (8 elements each) and reduce their dot products with shuffles.
-    const T *xo = xg + (int64_t)j * kRB * xrs;  // MODE 1: x, MODE 2: dy
     const T *auxo = reinterpret_cast<const T *>(a.aux) + (((int64_t)b * L + t0 + j * kRB) * H + h0) * kP;
     float ddp[HT];
 #pragma unroll
     for (int hh = 0; hh < HT; ++hh) ddp[hh] = 0.0f;
+    // The epilogue's global inputs of one head: per row pass m2 the 8
+    // elements from p0 of row r of the aux rows (MODE 1: dy, MODE 2: x), and
+    // in MODE 2 of dy and of the dx written by slot 0.  The input rows come
+    // raw through buffer loads (rows past the sequence end read as zero, no
+    // branch); each head's are issued before the previous head is finished,
+    // so their latency overlaps that work instead of following it.
+    constexpr int NRV = sizeof(T) == 2 ? 1 : 2;  // 16-byte pieces of 8 elements
+    constexpr int NM2 = (kRB * 8) / kThreads;
+    struct EpiRows {
+      u32x4 v[NM2][NRV], dy[NM2][NRV];
+      f32x4 dx[NM2][2];
+    };
+    const int64_t rowel = (int64_t)L * H * kP;  // elements of one batch row's [L][H][P]
+    const bufres rAux = make_buf(reinterpret_cast<const T *>(a.aux) + (int64_t)b * rowel, (uint32_t)(rowel * ES));
+    auto epi_off = [&](int hh, int m2) __attribute__((always_inline)) {
+      const int it = tid + m2 * kThreads;
+      const int r = it >> 3, p0 = (it & 7) * 8;
+      return (uint32_t)(((t0 + j * kRB + r) * H + h0 + hh) * kP + p0);  // element offset in the row
+    };
+    auto epi_load = [&](int hh, bool with_dx, EpiRows &e) __attribute__((always_inline)) {
+#pragma unroll
+      for (int m2 = 0; m2 < NM2; ++m2) {
+        const uint32_t eo = epi_off(hh, m2);
+#pragma unroll
+        for (int k = 0; k < NRV; ++k) e.v[m2][k] = bload16(rAux, eo * ES + 16 * k);
+        if constexpr (MODE == 2) {
+#pragma unroll
+          for (int k = 0; k < NRV; ++k) e.dy[m2][k] = bload16(rX, eo * ES + 16 * k);
+          if (with_dx) {
+            // the dx that slot 0 of this thread stored: an ordinary load
+            // through the same pointer, so it stays ordered after that store
+            // (rows past the sequence end read row 0 of the batch row and
+            // are not used)
+            const int it = tid + m2 * kThreads;
+            const bool ok = j * kRB + (it >> 3) < qlen;
+            const float *dxs = a.out1 + (int64_t)b * rowel + (ok ? eo : 0u);
+#pragma unroll
+            for (int k = 0; k < 2; ++k) e.dx[m2][k] = *reinterpret_cast<const f32x4 *>(dxs + 4 * k);
+          }
+        }
+      }
+    };
+    auto raw8 = [&](const u32x4 (&r)[NRV], float (&o)[8]) __attribute__((always_inline)) {
+      if constexpr (sizeof(T) == 2) {
+        unpack16(o, r[0], (const bf16 *)nullptr);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            // (an element of a vector type is copied out before the bit cast:
+            // a bit cast of the element itself reads the vector's first one)
+            const uint32_t u = r[k][e];
+            o[4 * k + e] = __builtin_bit_cast(float, u);
+          }
+      }
+    };
     auto slot_epilogue = [&](auto dc) __attribute__((always_inline)) {
       constexpr int d = decltype(dc)::value;
       const int sd = a.slot_dir[d];
+      EpiRows nxt;
+      epi_load(0, d == 1, nxt);
 #pragma unroll
       for (int ih = 0; ih < HT / IH; ++ih) {
         __syncthreads();
@@ -1448,20 +1505,18 @@ void k3_chunk_out(ScanArgs a) {
 #pragma unroll
         for (int q = 0; q < IH; ++q) {
           const int hh = ih * IH + q;
+          const EpiRows cur = nxt;
+          if (hh + 1 < HT) epi_load(hh + 1, d == 1, nxt);
 #pragma unroll
-          for (int m2 = 0; m2 < (kRB * 8) / kThreads; ++m2) {
+          for (int m2 = 0; m2 < NM2; ++m2) {
             const int it = tid + m2 * kThreads;
             const int r = it >> 3, p0 = (it & 7) * 8;
             const int64_t tok = t0 + j * kRB + r;
             const bool valid = j * kRB + r < qlen;
-            const int64_t off = (int64_t)r * xrs + hh * kP + p0;
             float o[8], v[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) o[e] = sm.u.Out[q][r][p0 + e];
-            if (valid) gload8(v, auxo + off);
-            else
-#pragma unroll
-              for (int e = 0; e < 8; ++e) v[e] = 0.0f;
+            raw8(cur.v[m2], v);
             float part = 0.0f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) part += o[e] * v[e];
@@ -1476,10 +1531,7 @@ void k3_chunk_out(ScanArgs a) {
               const float dtr = sm.dtd[d][hh][r], bc = sm.bcd[d][r];
               float *dxp = a.out1 + (((int64_t)b * L + tok) * H + h0 + hh) * kP + p0;
               float dyv[8], dxo[8];
-              if (valid) gload8(dyv, xo + off);
-              else
-#pragma unroll
-                for (int e = 0; e < 8; ++e) dyv[e] = 0.0f;
+              raw8(cur.dy[m2], dyv);
               float pin = 0.0f;
 #pragma unroll
               for (int e = 0; e < 8; ++e) {
@@ -1500,10 +1552,12 @@ void k3_chunk_out(ScanArgs a) {
                   dxo[e] = Dh * dyv[e] + dtr * o[e];
                   ddp[hh] += dyv[e] * v[e];
                 }
-              } else if (valid) {
-                gload8(dxo, dxp);
+              } else {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) dxo[e] += dtr * o[e];
+                for (int k = 0; k < 2; ++k)
+#pragma unroll
+                  for (int e = 0; e < 4; ++e)
+                    dxo[4 * k + e] = cur.dx[m2][k][e] + dtr * o[4 * k + e];
               }
               if (valid) gstore8(dxp, dxo);
             }
