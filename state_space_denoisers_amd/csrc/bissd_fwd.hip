@@ -970,7 +970,6 @@ void k3_chunk_out(ScanArgs a) {
   const int qlen = (int)((L - t0) < Q ? (L - t0) : Q);
   if (j * kRB >= qlen) return;
   const int gidx = (int)a.fd_hpg.div((uint32_t)h0);
-  const int64_t xrs = (int64_t)H * kP;
   constexpr uint32_t ES = sizeof(T);
   // one buffer per batch row: tokens past L read as zero
   const bufres rX = make_buf(reinterpret_cast<const T *>(a.x) + (int64_t)b * L * H * kP,
@@ -1425,7 +1424,6 @@ void k3_chunk_out(ScanArgs a) {
     // Backward modes: each slot's accumulator is finished on its own.  Rows
     // are staged through LDS; 8 consecutive lanes hold one row of one head
     // (8 elements each) and reduce their dot products with shuffles.
-    const T *auxo = reinterpret_cast<const T *>(a.aux) + (((int64_t)b * L + t0 + j * kRB) * H + h0) * kP;
     float ddp[HT];
 #pragma unroll
     for (int hh = 0; hh < HT; ++hh) ddp[hh] = 0.0f;
@@ -1489,6 +1487,11 @@ void k3_chunk_out(ScanArgs a) {
     auto slot_epilogue = [&](auto dc) __attribute__((always_inline)) {
       constexpr int d = decltype(dc)::value;
       const int sd = a.slot_dir[d];
+      // MODE 1: the within-chunk dA of this row-block per head, the sum over
+      // its rows of dy . acc2, from the same dy rows as dy . y_d
+      float dsum[HT];
+#pragma unroll
+      for (int hh = 0; hh < HT; ++hh) dsum[hh] = 0.0f;
       EpiRows nxt;
       epi_load(0, d == 1, nxt);
 #pragma unroll
@@ -1562,40 +1565,31 @@ void k3_chunk_out(ScanArgs a) {
               if (valid) gstore8(dxp, dxo);
             }
           }
-        }
-      }
-      if constexpr (DAI) {
-        // within-chunk dA of this row-block, per head: sum over its rows of
-        // dy . acc2, rows staged through LDS as above, reduced in a fixed order
-        float dsum[HT];
-#pragma unroll
-        for (int hh = 0; hh < HT; ++hh) dsum[hh] = 0.0f;
-#pragma unroll
-        for (int ih = 0; ih < HT / IH; ++ih) {
-          __syncthreads();
-#pragma unroll
-          for (int q = 0; q < IH; ++q)
+          if constexpr (DAI) {
+            // acc2 of this head through the same LDS rows, dotted with the
+            // dy rows still in registers
+            __syncthreads();
 #pragma unroll
             for (int v = 0; v < 4; ++v)
 #pragma unroll
-              for (int i2 = 0; i2 < 4; ++i2)
-                sm.u.Out[q][16 * w + 4 * g4 + i2][16 * v + r16] = acc2[ih * IH + q][v][i2];
-          __syncthreads();
+              for (int i2 = 0; i2 < 4; ++i2) sm.u.Out[q][16 * w + 4 * g4 + i2][16 * v + r16] = acc2[hh][v][i2];
+            __syncthreads();
 #pragma unroll
-          for (int q = 0; q < IH; ++q) {
-            const int hh = ih * IH + q;
-#pragma unroll
-            for (int m2 = 0; m2 < (kRB * 8) / kThreads; ++m2) {
+            for (int m2 = 0; m2 < NM2; ++m2) {
               const int it = tid + m2 * kThreads;
               const int r = it >> 3, p0 = (it & 7) * 8;
-              if (j * kRB + r >= qlen) continue;
               float v[8];
-              gload8(v, auxo + (int64_t)r * xrs + hh * kP + p0);
+              raw8(cur.v[m2], v);
+              float t = 0.0f;
 #pragma unroll
-              for (int e = 0; e < 8; ++e) dsum[hh] += sm.u.Out[q][r][p0 + e] * v[e];
+              for (int e = 0; e < 8; ++e) t += sm.u.Out[q][r][p0 + e] * v[e];
+              if (j * kRB + r < qlen) dsum[hh] += t;
             }
           }
         }
+      }
+      if constexpr (DAI) {
+        // the within-chunk dA partial sums, reduced in a fixed order
 #pragma unroll
         for (int hh = 0; hh < HT; ++hh) {
           float v = dsum[hh];
