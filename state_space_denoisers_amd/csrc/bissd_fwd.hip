@@ -314,49 +314,64 @@ void k1_chunk_state(ScanArgs a) {
   // reverse direction's first chunk (the last in its scan order).
   const bool unread = MODE == 0 && a.skip_edges &&
                       (d == 0 ? (c == a.nchunks - 1 && a.final_state == nullptr) : c == 0);
-  if constexpr (MODE <= 2) if (!unread) {
+  // MODE 1 also forms the Frobenius product of each head's state with the
+  // given state of the same (direction, batch, chunk, head), in fp32 from the
+  // accumulators: the given state is read in 16-byte pieces (issued before
+  // the head's staging) into the same LDS tile, then in the accumulators'
+  // layout; the sum is reduced in a fixed order.
+  constexpr int EPV = 16 / (int)sizeof(T);
+  constexpr int NPV = kP * N / EPV / kThreads;  // 16-byte pieces per thread of one head's state
+  static_assert(kP * N * sizeof(T) <= sizeof(sm.Bs), "state tile must fit the B tile");
+  T *stile = &sm.Bs[0][0];
+  const T *ref = MODE == 1 ? reinterpret_cast<const T *>(a.sin[d]) + (int64_t)b * a.sin_bstride[d] +
+                                 (int64_t)c * a.sin_cstride[d] + (int64_t)h0 * kP * N
+                           : nullptr;
+  if constexpr (MODE <= 2) {
     // one head at a time through LDS (the B tile, no longer read), so that
-    // every thread stores 16 contiguous bytes
-    constexpr int EPV = 16 / (int)sizeof(T);
-    static_assert(kP * N * sizeof(T) <= sizeof(sm.Bs), "state tile must fit the B tile");
-    T *stile = &sm.Bs[0][0];
+    // every thread stores (and MODE 1 loads) 16 contiguous bytes
     T *out = reinterpret_cast<T *>(a.states) + chi * (int64_t)(kP * N);
 #pragma unroll
     for (int hh = 0; hh < HT; ++hh) {
-      __syncthreads();
+      u32x4 rp[MODE == 1 ? NPV : 1];
+      if constexpr (MODE == 1) {
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt)
+        for (int m = 0; m < NPV; ++m)
+          rp[m] = *reinterpret_cast<const u32x4 *>(ref + (int64_t)hh * kP * N + (tid + m * kThreads) * EPV);
+      }
+      if (!unread) {
+        __syncthreads();
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
+        for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            stile[(16 * pt + 4 * g4 + i) * N + nb + 16 * nt + r16] = from_f<T>(acc[hh][pt][nt][i]);
-      __syncthreads();
-      for (int v = tid; v < kP * N / EPV; v += kThreads)
-        *reinterpret_cast<u32x4 *>(out + (int64_t)hh * kP * N + v * EPV) =
-            *reinterpret_cast<const u32x4 *>(stile + v * EPV);
+          for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              stile[(16 * pt + 4 * g4 + i) * N + nb + 16 * nt + r16] = from_f<T>(acc[hh][pt][nt][i]);
+        __syncthreads();
+        for (int v = tid; v < kP * N / EPV; v += kThreads)
+          *reinterpret_cast<u32x4 *>(out + (int64_t)hh * kP * N + v * EPV) =
+              *reinterpret_cast<const u32x4 *>(stile + v * EPV);
+      }
+      if constexpr (MODE == 1) {
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < NPV; ++m) *reinterpret_cast<u32x4 *>(stile + (tid + m * kThreads) * EPV) = rp[m];
+        __syncthreads();
+        float v = 0.0f;
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              v += acc[hh][pt][nt][i] * to_f(stile[(16 * pt + 4 * g4 + i) * N + nb + 16 * nt + r16]);
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+        if (lane == 0) sm.red[w][hh] = v;
+      }
     }
   }
   if constexpr (MODE == 1) {
-    // Frobenius product with the given state of the same (direction, batch,
-    // chunk, head), reduced in a fixed order
-    const T *ref = reinterpret_cast<const T *>(a.sin[d]) + (int64_t)b * a.sin_bstride[d] +
-                   (int64_t)c * a.sin_cstride[d] + (int64_t)h0 * kP * N;
-#pragma unroll
-    for (int hh = 0; hh < HT; ++hh) {
-      float v = 0.0f;
-#pragma unroll
-      for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            v += acc[hh][pt][nt][i] *
-                 to_f(ref[(int64_t)hh * kP * N + (16 * pt + 4 * g4 + i) * N + nb + 16 * nt + r16]);
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
-      if (lane == 0) sm.red[w][hh] = v;
-    }
     __syncthreads();
     if (tid < HT) a.out0[chi + tid] = (sm.red[0][tid] + sm.red[1][tid]) + (sm.red[2][tid] + sm.red[3][tid]);
   }
