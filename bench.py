@@ -784,8 +784,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(sharding is described in the design notes); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: there is no multi-GPU path (the design notes say "
+              "how the scan would shard); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
