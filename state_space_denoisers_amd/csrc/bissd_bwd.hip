@@ -536,83 +536,187 @@ __global__ __launch_bounds__(kStThreads) void k_bwd_state(BwdArgs a) {
 
 // ====================================================== decay gradients
 
-// One wavefront per (batch, direction, head, chunk); the chunks are
-// independent once their boundary values are known:
+// One workgroup per (batch, direction, chunk, group of heads); the chunks
+// are independent once their boundary values are known:
 // d_lam_t = dy.y_d,t - dt_t x_t.(G_t B_t) (both taken without their common
 // t' = t term, which cancels); dalpha_t = the in-chunk sum of d_lam over t
 // and the tokens after it in scan order, plus the chunk's boundary value
 // (the wave partials of <adjoint carry, state after the chunk>, summed in a
 // fixed order); ddt_t = x_t.(G_t B_t) + A dalpha_t.
+// Every per-token array is [token][head], so a chunk's rows for a group of
+// heads sit together in memory: the workgroup reads and writes them in
+// consecutive-element order (each wavefront instruction covers 64
+// neighbouring elements) and transposes through an LDS tile [token][head],
+// where one wavefront per head runs the sums along the tokens.
+#ifndef BISSD_DECAY_HEADS
+#define BISSD_DECAY_HEADS 32
+#endif
+#ifndef BISSD_DECAY_THREADS
+#define BISSD_DECAY_THREADS 1024
+#endif
+constexpr int kDecHeads = BISSD_DECAY_HEADS;  // at most this many heads per workgroup
+constexpr int kDecThreads = BISSD_DECAY_THREADS;
+constexpr int kDecEpt = 256 * kDecHeads / kDecThreads;  // tile elements per thread
+constexpr int kDecHpw = (kDecHeads + kDecThreads / 64 - 1) / (kDecThreads / 64);  // heads per wavefront
+
+__host__ __device__ inline int decay_groups(int H) { return (H + kDecHeads - 1) / kDecHeads; }
+
+// LDS word of (token t, head hl) for an odd row pitch S: a wavefront whose
+// lanes take K = 4 consecutive tokens each (lane stride 4 S + 1, odd) and
+// one whose lanes take consecutive elements both meet distinct banks
+__device__ __forceinline__ int dec_idx(int t, int hl, int S) { return t * S + (t >> 2) + hl; }
+
 template <typename T>
-__global__ __launch_bounds__(kThreads) void k_bwd_decay(BwdArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int64_t item = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-  const int H = a.H, nc = a.nchunks;
-  if (item >= (int64_t)a.Z * 2 * H * nc) return;
-  const int c = (int)(item % nc);
-  const int h = (int)((item / nc) % H), d = (int)((item / ((int64_t)nc * H)) % 2);
-  const int b = (int)(item / ((int64_t)nc * H * 2));
-  const int64_t L = a.L;
+__global__ __launch_bounds__(kDecThreads) void k_bwd_decay(BwdArgs a) {
+  __shared__ float sv[256 * (kDecHeads | 1) + 64];
+  __shared__ float sA[kDecHeads], sBias[kDecHeads];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int H = a.H, nc = a.nchunks, ngrp = decay_groups(H), hgs = (H + ngrp - 1) / ngrp;
+  int item = blockIdx.x;
+  const int grp = item % ngrp;
+  item /= ngrp;
+  const int c = item % nc;
+  item /= nc;
+  const int d = item & 1, b = item >> 1;
+  const int h0 = grp * hgs, hg = min(hgs, H - h0), S = hg | 1;
+  const int64_t L = a.L, t0 = (int64_t)c * a.chunk;
   const int Q = a.chunk, K = Q / 64, nwv = kP * a.N / 256;
-  const T *dt = reinterpret_cast<const T *>(a.dt[d]) + (int64_t)b * L * H + h;
-  const float *yd = a.ydot + ((int64_t)d * a.Z + b) * L * H + h;
-  const float *qx = a.qx + ((int64_t)d * a.Z + b) * L * H + h;
-  const float *qxs = a.qxs + ((int64_t)d * a.Z + b) * L * H + h;
-  float *ddt = a.ddt[d] + (int64_t)b * L * H + h;
-  const float A = a.A[d][h];
-  const DtPost post = dt_post_of(a, d, h);
-  const float *rp = a.rpart + ((((int64_t)d * a.Z + b) * nc + c) * H + h) * nwv;
-  float R = 0.0f;
-  for (int k = 0; k < nwv; ++k) R += rp[k];
-  const int64_t base = (int64_t)c * Q + lane * K;
-  float v[4], ql[4], gr[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t t = base + i;
-    const bool ok = i < K && t < L;
-    ql[i] = ok ? qx[t * H] : 0.0f;
-    const float draw = ok ? to_f(dt[t * H]) : 0.0f;
-    // d dt / d raw of a post-processed dt (1 without), for the chain rule below
-    gr[i] = ok ? dt_post_grad(draw, post) : 0.0f;
-    // dy.y_d and x.(G_t B_t) both without their common t' = t term
-    v[i] = ok ? yd[t * H] - dt_post(draw, post) * qxs[t * H] : 0.0f;
+  const int qlen = (int)min<int64_t>(Q, L - t0);
+  const int64_t row0 = (int64_t)b * L + t0;
+  const int64_t wrow = ((int64_t)d * a.Z + b) * L + t0;
+  const T *dt = reinterpret_cast<const T *>(a.dt[d]) + row0 * H + h0;
+  const float *yd = a.ydot + wrow * H + h0, *qx = a.qx + wrow * H + h0, *qxs = a.qxs + wrow * H + h0;
+  float *ddt = a.ddt[d] + row0 * H + h0;
+  const bool post_on = a.dtb[d] != nullptr;
+  if (tid < hg) {
+    sA[tid] = a.A[d][h0 + tid];
+    sBias[tid] = post_on ? a.dtb[d][h0 + tid] : 0.0f;
   }
-  float run = 0.0f, acc[4];
-  if (d == 0) {
+  // the boundary values' wave partials of this wavefront's heads (lane k
+  // holds partial k), fetched first so their latency hides behind the tile
+  const float *rp = a.rpart + ((((int64_t)d * a.Z + b) * nc + c) * H + h0) * nwv;
+  float rpv[kDecHpw];
 #pragma unroll
-    for (int i = 3; i >= 0; --i) {
-      run += v[i];
-      acc[i] = run;
-    }
-    const float excl = wave_shift_down1(wave_scan_down(run));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] += excl + R;
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      run += v[i];
-      acc[i] = run;
-    }
-    const float excl = wave_shift_up1(wave_scan_up(run));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] += excl + R;
+  for (int m = 0; m < kDecHpw; ++m) {
+    const int hl = wv + m * (kDecThreads / 64);
+    rpv[m] = hl < hg && lane < nwv ? rp[hl * nwv + lane] : 0.0f;
   }
+  // thread tid takes tile elements tid + j kDecThreads, element e = t hg + hl
+  const int dq = kDecThreads / hg, dr = kDecThreads - dq * hg;
+  const int tq0 = tid / hg, hr0 = tid - tq0 * hg;
+  float rq[kDecEpt], ry[kDecEpt], rs[kDecEpt], rd[kDecEpt];
+  {
+    int t = tq0, hl = hr0;
+#pragma unroll
+    for (int j = 0; j < kDecEpt; ++j) {
+      const int o = t < qlen ? t * H + hl : 0;
+      rq[j] = qx[o];
+      ry[j] = yd[o];
+      rs[j] = qxs[o];
+      rd[j] = to_f(dt[o]);
+      t += dq;
+      hl += dr;
+      if (hl >= hg) {
+        hl -= hg;
+        ++t;
+      }
+    }
+  }
+  __syncthreads();
+  float ql[kDecEpt], gr[kDecEpt];
+  {
+    int t = tq0, hl = hr0;
+#pragma unroll
+    for (int j = 0; j < kDecEpt; ++j) {
+      const bool ok = t < qlen;
+      DtPost p;
+      p.on = post_on;
+      p.bias = sBias[hl];
+      p.lo = a.dtlo[d];
+      p.hi = a.dthi[d];
+      // d dt / d raw of a post-processed dt (1 without), for the chain rule below
+      gr[j] = ok ? dt_post_grad(rd[j], p) : 0.0f;
+      ql[j] = ok ? rq[j] : 0.0f;
+      // dy.y_d and x.(G_t B_t) both without their common t' = t term; rows
+      // beyond the sequence end hold 0
+      if (t < Q) sv[dec_idx(t, hl, S)] = ok ? ry[j] - dt_post(rd[j], p) * rs[j] : 0.0f;
+      t += dq;
+      hl += dr;
+      if (hl >= hg) {
+        hl -= hg;
+        ++t;
+      }
+    }
+  }
+  __syncthreads();
+  // one wavefront per head: lane l holds tokens l K .. l K + K - 1; a sum
+  // inside the lane, a scan across the lanes, and the boundary value
+#pragma unroll
+  for (int m = 0; m < kDecHpw; ++m) {
+    const int hl = wv + m * (kDecThreads / 64);
+    if (hl >= hg) break;
+    // the partials' sum, in lane order, is the top lane of their scan
+    const float R = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wave_scan_up(rpv[m])), 63));
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = i < K ? sv[dec_idx(lane * K + i, hl, S)] : 0.0f;
+    float run = 0.0f;
+    if (d == 0) {
+#pragma unroll
+      for (int i = 3; i >= 0; --i) {
+        run += x[i];
+        x[i] = run;
+      }
+      const float excl = wave_shift_down1(wave_scan_down(run));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] += excl + R;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        run += x[i];
+        x[i] = run;
+      }
+      const float excl = wave_shift_up1(wave_scan_up(run));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] += excl + R;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (i < K) sv[dec_idx(lane * K + i, hl, S)] = x[i];
+  }
+  __syncthreads();
   // with dt post-processing, ddt is taken back to the pre-activation and the
   // chunk's sum of it feeds the bias gradient
-  float bsum = 0.0f;
+  {
+    int t = tq0, hl = hr0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t t = base + i;
-    const float g = (ql[i] + A * acc[i]) * gr[i];
-    if (i < K && t < L) {
-      ddt[t * H] = g;
-      bsum += g;
+    for (int j = 0; j < kDecEpt; ++j) {
+      if (t < qlen) {
+        const int k = dec_idx(t, hl, S);
+        const float g = (ql[j] + sA[hl] * sv[k]) * gr[j];
+        ddt[t * H + hl] = g;
+        sv[k] = g;
+      }
+      t += dq;
+      hl += dr;
+      if (hl >= hg) {
+        hl -= hg;
+        ++t;
+      }
     }
   }
-  if (post.on) {
+  if (!post_on) return;
+  __syncthreads();
+  for (int hl = wv; hl < hg; hl += kDecThreads / 64) {
+    float bsum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = lane * K + i;
+      if (i < K && t < qlen) bsum += sv[dec_idx(t, hl, S)];
+    }
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) bsum += __shfl_xor(bsum, o, 64);
-    if (lane == 0) a.dbpart[(((int64_t)d * a.Z + b) * nc + c) * H + h] = bsum;
+    if (lane == 0) a.dbpart[(((int64_t)d * a.Z + b) * nc + c) * H + h0 + hl] = bsum;
   }
 }
 
@@ -694,10 +798,9 @@ hipError_t launch_bwd_panels(const BwdArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_bwd_decay(const BwdArgs &a, hipStream_t st) {
-  const int64_t items = (int64_t)a.Z * 2 * a.H * a.nchunks;
-  dim3 g((unsigned)((items + 3) / 4));
-  if (a.dtype == 1) launch_kernel(k_bwd_decay<bf16>, g, dim3(kThreads), 0, st, a);
-  else launch_kernel(k_bwd_decay<float>, g, dim3(kThreads), 0, st, a);
+  dim3 g((unsigned)((int64_t)a.Z * 2 * a.nchunks * decay_groups(a.H)));
+  if (a.dtype == 1) launch_kernel(k_bwd_decay<bf16>, g, dim3(kDecThreads), 0, st, a);
+  else launch_kernel(k_bwd_decay<float>, g, dim3(kDecThreads), 0, st, a);
   launch_kernel(k_bwd_reduce, dim3((unsigned)(5 * a.H)), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }

@@ -656,7 +656,8 @@ __device__ __forceinline__ float wave_scan_up(float v) {
   const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 15));
   const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 31));
   const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 47));
-  const float below = row == 0 ? 0.0f : row == 1 ? r0 : row == 2 ? r0 + r1 : (r0 + r1) + r2;
+  // the same sums as r0, r0 + r1, (r0 + r1) + r2, formed by selects (no branches)
+  const float below = ((row >= 1 ? r0 : 0.0f) + (row >= 2 ? r1 : 0.0f)) + (row >= 3 ? r2 : 0.0f);
   return v + below;
 }
 // Inclusive sum from lane 63 downwards (row_shl inside the rows, then the
@@ -670,7 +671,7 @@ __device__ __forceinline__ float wave_scan_down(float v) {
   const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
   const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
   const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
-  const float above = row == 3 ? 0.0f : row == 2 ? r3 : row == 1 ? r3 + r2 : (r3 + r2) + r1;
+  const float above = ((row <= 2 ? r3 : 0.0f) + (row <= 1 ? r2 : 0.0f)) + (row == 0 ? r1 : 0.0f);
   return v + above;
 }
 // lane l receives lane l - 1 (lane 0: 0) / lane l + 1 (lane 63: 0)
