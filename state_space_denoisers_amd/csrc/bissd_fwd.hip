@@ -950,7 +950,7 @@ template <typename T, int N, int HT, bool SF32> struct K3Pf {
 // the epilogue.
 template <typename T, int N, int HT, bool SF32, int MODE, bool XCONV = false>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? (MODE == 1 ? (HT == 1 ? 4 : 3) : MODE == 2 ? 2 : (SF32 ? 1 : 4)) : 1)))
+__attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? (MODE == 0 ? (SF32 ? 1 : 4) : 4) : 1)))
 void k3_chunk_out(ScanArgs a) {
   using Sm = K3Lds<T, N, HT>;
   using PF = K3Pf<T, N, HT, SF32>;
@@ -1444,16 +1444,19 @@ void k3_chunk_out(ScanArgs a) {
     for (int hh = 0; hh < HT; ++hh) ddp[hh] = 0.0f;
     // The epilogue's global inputs of one head: per row pass m2 the 8
     // elements from p0 of row r of the aux rows (MODE 1: dy, MODE 2: x), and
-    // in MODE 2 of dy and of the dx written by slot 0.  The input rows come
-    // raw through buffer loads (rows past the sequence end read as zero, no
-    // branch); each head's are issued before the previous head is finished,
-    // so their latency overlaps that work instead of following it.
+    // in MODE 2 of dy.  The input rows come raw through buffer loads (rows
+    // past the sequence end read as zero, no branch); each head's are issued
+    // before the previous head is finished, so their latency overlaps that
+    // work instead of following it.
     constexpr int NRV = sizeof(T) == 2 ? 1 : 2;  // 16-byte pieces of 8 elements
     constexpr int NM2 = (kRB * 8) / kThreads;
     struct EpiRows {
       u32x4 v[NM2][NRV], dy[NM2][NRV];
-      f32x4 dx[NM2][2];
     };
+    // MODE 2: slot 0's part of dx (D dy + dt G B of its direction) for this
+    // thread's 8 elements of each row pass and head, kept in registers until
+    // slot 1 adds its own and writes dx once
+    float dxk[MODE == 2 ? HT : 1][NM2][8];
     const int64_t rowel = (int64_t)L * H * kP;  // elements of one batch row's [L][H][P]
     const bufres rAux = make_buf(reinterpret_cast<const T *>(a.aux) + (int64_t)b * rowel, (uint32_t)(rowel * ES));
     auto epi_off = [&](int hh, int m2) __attribute__((always_inline)) {
@@ -1461,7 +1464,7 @@ void k3_chunk_out(ScanArgs a) {
       const int r = it >> 3, p0 = (it & 7) * 8;
       return (uint32_t)(((t0 + j * kRB + r) * H + h0 + hh) * kP + p0);  // element offset in the row
     };
-    auto epi_load = [&](int hh, bool with_dx, EpiRows &e) __attribute__((always_inline)) {
+    auto epi_load = [&](int hh, EpiRows &e) __attribute__((always_inline)) {
 #pragma unroll
       for (int m2 = 0; m2 < NM2; ++m2) {
         const uint32_t eo = epi_off(hh, m2);
@@ -1470,17 +1473,6 @@ void k3_chunk_out(ScanArgs a) {
         if constexpr (MODE == 2) {
 #pragma unroll
           for (int k = 0; k < NRV; ++k) e.dy[m2][k] = bload16(rX, eo * ES + 16 * k);
-          if (with_dx) {
-            // the dx that slot 0 of this thread stored: an ordinary load
-            // through the same pointer, so it stays ordered after that store
-            // (rows past the sequence end read row 0 of the batch row and
-            // are not used)
-            const int it = tid + m2 * kThreads;
-            const bool ok = j * kRB + (it >> 3) < qlen;
-            const float *dxs = a.out1 + (int64_t)b * rowel + (ok ? eo : 0u);
-#pragma unroll
-            for (int k = 0; k < 2; ++k) e.dx[m2][k] = *reinterpret_cast<const f32x4 *>(dxs + 4 * k);
-          }
         }
       }
     };
@@ -1508,7 +1500,7 @@ void k3_chunk_out(ScanArgs a) {
 #pragma unroll
       for (int hh = 0; hh < HT; ++hh) dsum[hh] = 0.0f;
       EpiRows nxt;
-      epi_load(0, d == 1, nxt);
+      epi_load(0, nxt);
 #pragma unroll
       for (int ih = 0; ih < HT / IH; ++ih) {
         __syncthreads();
@@ -1524,7 +1516,7 @@ void k3_chunk_out(ScanArgs a) {
         for (int q = 0; q < IH; ++q) {
           const int hh = ih * IH + q;
           const EpiRows cur = nxt;
-          if (hh + 1 < HT) epi_load(hh + 1, d == 1, nxt);
+          if (hh + 1 < HT) epi_load(hh + 1, nxt);
 #pragma unroll
           for (int m2 = 0; m2 < NM2; ++m2) {
             const int it = tid + m2 * kThreads;
@@ -1567,17 +1559,14 @@ void k3_chunk_out(ScanArgs a) {
                 const float Dh = a.D[h0 + hh];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                  dxo[e] = Dh * dyv[e] + dtr * o[e];
+                  dxk[hh][m2][e] = Dh * dyv[e] + dtr * o[e];
                   ddp[hh] += dyv[e] * v[e];
                 }
               } else {
 #pragma unroll
-                for (int k = 0; k < 2; ++k)
-#pragma unroll
-                  for (int e = 0; e < 4; ++e)
-                    dxo[4 * k + e] = cur.dx[m2][k][e] + dtr * o[4 * k + e];
+                for (int e = 0; e < 8; ++e) dxo[e] = dxk[hh][m2][e] + dtr * o[e];
+                if (valid) gstore8(dxp, dxo);
               }
-              if (valid) gstore8(dxp, dxo);
             }
           }
           if constexpr (DAI) {
@@ -1687,11 +1676,15 @@ static void launch_t(const ScanArgs &a, int phase, hipStream_t st) {
                        phase == PHASE_ADJ_PASS ? 1 : 0);
   } else {
     dim3 g((unsigned)(a.Z * a.nchunks * (a.chunk / kRB) * (a.H / HT)));
-    if (phase == PHASE_YDOT)
-      launch_kernel((k3_chunk_out<T, N, HT, false, 1>), g, dim3(kThreads), 0, st, a);
-    else if (phase == PHASE_DX)
-      launch_kernel((k3_chunk_out<T, N, HT, false, 2>), g, dim3(kThreads), 0, st, a);
-    else if (a.xs[0] || a.xs[1]) {
+    if (phase == PHASE_YDOT || phase == PHASE_DX) {
+      // one head per tile (the caller's choice for these passes)
+      if constexpr (HT == 1) {
+        if (phase == PHASE_YDOT)
+          launch_kernel((k3_chunk_out<T, N, 1, false, 1>), g, dim3(kThreads), 0, st, a);
+        else
+          launch_kernel((k3_chunk_out<T, N, 1, false, 2>), g, dim3(kThreads), 0, st, a);
+      }
+    } else if (a.xs[0] || a.xs[1]) {
       if (a.sin_f32[0] || a.sin_f32[1])
         launch_kernel((k3_chunk_out<T, N, HT, true, 0, true>), g, dim3(kThreads), 0, st, a);
       else
@@ -1732,7 +1725,10 @@ hipError_t launch_scan_phase(const ScanArgs &args, int phase, hipStream_t st) {
   // Heads of one tile share their B/C group: 2 heads when the heads per
   // group are even, else 1.  The dy.y_d pass (two products per stage) takes
   // one head per tile: with two, its accumulators leave too few registers
-  // for four waves per SIMD without spilling.  So do the chunk-state and
+  // for four waves per SIMD without spilling.  So does the dx pass, whose
+  // first slot's part of dx waits in registers for the second: with two
+  // heads that takes 218 registers (two waves per SIMD), with one 128
+  // (four), and the pass runs faster.  So do the chunk-state and
   // output passes of a problem whose one-head workgroups still run in one
   // round (three per compute unit for the chunk states, four for the
   // output): twice the workgroups, each on a shorter path.  (Whether the
@@ -1744,7 +1740,7 @@ hipError_t launch_scan_phase(const ScanArgs &args, int phase, hipStream_t st) {
   const int64_t items1 = (int64_t)args.Z * args.nchunks * args.ndir * (args.H / 2);
   const bool small = (phase == PHASE_CHUNK_OUT && 2 * items2 <= 4 * ncu) ||
                      (phase == PHASE_CHUNK_STATE && 2 * items1 <= 3 * ncu);
-  const int HT = (hpg % 2 == 0 && phase != PHASE_YDOT && !small) ? 2 : 1;
+  const int HT = (hpg % 2 == 0 && phase != PHASE_YDOT && phase != PHASE_DX && !small) ? 2 : 1;
   ScanArgs a = args;
   const int nrb = a.chunk / kRB;
   a.fd_tiles = FastDiv((uint32_t)(a.H / HT));
