@@ -22,7 +22,7 @@ the fp64 CPU oracle on a bounded sample of the same workload.  One JSON line
 is printed.
 
 Profiling helpers (for rocprofv3 runs):
-    python bench.py --profile-phase {0,1,2,3,all,conv,backward,block,attention} [--workload W]
+    python bench.py --profile-phase {0,1,2,3,all,conv,train,backward,block,attention} [--workload W]
         [--iters R] [--settle S]   (S seconds of a bf16 matrix product first)
     python bench.py --copy-calibrate
 """
@@ -408,8 +408,11 @@ def bench_block(reps):
 
 
 class Train:
-    """Preallocated forward + backward call on one workload (a training
-    step of the scan: y, then every gradient of sum(dy * y))."""
+    """Preallocated training step of the scan on one workload: the forward
+    that keeps its chunk states, carry-ins, decays and Gram tiles for the
+    backward (BISSD_SAVE), then the backward that reads them -- y, then every
+    gradient of sum(dy * y).  ``backward_recompute`` is the backward that
+    forms everything itself (no saving forward needed)."""
 
     def __init__(self, w, rev_block=0):
         import torch
@@ -428,13 +431,24 @@ class Train:
                                         self.dy, chunk=w.chunk, rev_block=rev_block,
                                         workspace=self.ws)
 
+    def forward(self):
+        self.ssd.bissd_forward(self.f.T["x"], self.f.fwd, self.f.rev, self.f.T["D"],
+                               chunk=self.w.chunk, rev_block=self.rb, y=self.f.y,
+                               workspace=self.ws, save=True)
+
     def backward(self):
+        """The saved backward: valid right after forward()."""
+        self.ssd.bissd_backward(self.f.T["x"], self.f.fwd, self.f.rev, self.f.T["D"], self.dy,
+                                chunk=self.w.chunk, rev_block=self.rb, grads=self.grads,
+                                saved=self.ws)
+
+    def backward_recompute(self):
         self.ssd.bissd_backward(self.f.T["x"], self.f.fwd, self.f.rev, self.f.T["D"], self.dy,
                                 chunk=self.w.chunk, rev_block=self.rb, grads=self.grads,
                                 workspace=self.ws)
 
     def __call__(self):
-        self.f()
+        self.forward()
         self.backward()
 
 
@@ -460,13 +474,16 @@ def bench_train(steps, rev_block=0):
         t()
     torch.cuda.synchronize()
     settle(t, LEG_SETTLE_S)
-    ms_f = event_time_ms(t.f, steps)
-    ms_b = event_time_ms(t.backward, steps)
+    # the saved backward needs the saving forward before it, so its time is
+    # the step's less the forward's
+    ms_f = event_time_ms(t.forward, steps)
     ms = event_time_ms(t, steps)
+    ms_r = event_time_ms(t.backward_recompute, steps)
     name = w.name + (f"_rev{rev_block}" if rev_block else "")
     return {"workload": name, "batch": w.Z, "seq_len": w.L, "rev_block": rev_block,
             "tokens_per_s": w.tokens / (ms * 1e-3),
-            "ms_per_step": ms, "ms_forward": ms_f, "ms_backward": ms_b,
+            "ms_per_step": ms, "ms_forward": ms_f, "ms_backward": ms - ms_f,
+            "ms_backward_recompute": ms_r, "ms_forward_plain": event_time_ms(t.f, steps),
             "hbm_algorithmic_GBs": train_bytes_per_token(w) * w.tokens / (ms * 1e-3) / 1e9}
 
 
@@ -725,13 +742,16 @@ def profile_phase(args):
         torch.cuda.synchronize()
         print("done", flush=True)
         return
-    if args.profile_phase == "backward":
+    if args.profile_phase in ("train", "backward"):
+        # train: the training step (saving forward, saved backward);
+        # backward: the backward that forms everything itself
         t = Train(w)
-        settle(t.backward, args.settle)
+        fn = t if args.profile_phase == "train" else t.backward_recompute
+        settle(fn, args.settle)
         torch.cuda.synchronize()
-        print(f"profiling backward on {w.name} x{args.iters}", flush=True)
+        print(f"profiling {args.profile_phase} on {w.name} x{args.iters}", flush=True)
         for _ in range(args.iters):
-            t.backward()
+            fn()
         torch.cuda.synchronize()
         print("done", flush=True)
         return
@@ -769,8 +789,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--profile-phase", choices=["0", "1", "2", "3", "all", "conv", "backward", "block",
-                                                "attention"])
+    ap.add_argument("--profile-phase", choices=["0", "1", "2", "3", "all", "conv", "train", "backward",
+                                                "block", "attention"])
     ap.add_argument("--workload", default="layer130m_L1k")
     ap.add_argument("--iters", type=int, default=20)
     ap.add_argument("--copy-calibrate", action="store_true")

@@ -140,8 +140,17 @@ typedef struct {
   int32_t conv_width; /* 0: no convolution; 1..4: the width K of the directions'
                          convolutions (each direction with conv_w set uses it;
                          the workspace has room for their outputs) */
-  int32_t reserved;   /* must be 0 */
+  int32_t flags;      /* 0, or BISSD_SAVE for bissd_forward / bissd_backward
+                         (and bissd_workspace_size): the forward leaves in its
+                         workspace what the backward would otherwise recompute */
 } bissd_shape_t;
+
+/* shape->flags: a training step's forward keeps, in its workspace, the chunk
+ * states, carry-in states, chunk decays, per-token decay sums and Gram tiles
+ * that the backward of the same inputs needs; the backward, given the same
+ * workspace with the same flag, takes them from there instead of forming
+ * them again.  Only for shapes without a convolution (conv_width 0). */
+#define BISSD_SAVE 1
 
 /* One scan direction's parameters.  Without dt_bias, dt is the step itself
  * (already positive).  With dt_bias, dt holds the mixer's pre-activation and
@@ -179,7 +188,9 @@ typedef struct {
  * The workspace holds the per-chunk states and carries (compute dtype), the
  * chunk decays and the chunk Gram tiles C.B^T (compute dtype), plus the backward
  * pass's adjoint and reduction buffers; it is overwritten by every call and
- * its contents between calls mean nothing.
+ * its contents between calls mean nothing -- except with BISSD_SAVE in
+ * shape->flags, where BISSD_OP_FORWARD gives the backward's size and a
+ * forward call leaves in it what a following bissd_backward reads.
  */
 size_t bissd_workspace_size(const bissd_shape_t *shape, int op);
 
@@ -191,6 +202,12 @@ size_t bissd_workspace_size(const bissd_shape_t *shape, int op);
  *               May equal init_state.
  *   fwd.* and rev.* may point to the same buffers (weight-tied directions).
  *   y must not overlap any input.
+ * With BISSD_SAVE in shape->flags (forward of a training step) the
+ * workspace must hold bissd_workspace_size(shape, BISSD_OP_FORWARD) bytes
+ * (the backward's size) and keeps, after the call, the chunk states, carry-in
+ * states (forward direction from init_state), chunk decays, per-token decay
+ * sums and Gram tiles for bissd_backward; a convolution is then not supported
+ * (BISSD_ERR_UNSUPPORTED).
  */
 int bissd_forward(const bissd_shape_t *shape, const void *x, bissd_dir_t fwd,
                   bissd_dir_t rev, const float *D, const float *init_state, void *y,
@@ -213,6 +230,8 @@ int bissd_forward(const bissd_shape_t *shape, const void *x, bissd_dir_t fwd,
  * streams, other host threads) race on it and must be serialised by the
  * caller; calls on one stream are ordered.
  */
+/* (shape->flags must be 0 here: the static array is no place to keep values
+ * for a backward; BISSD_ERR_UNSUPPORTED otherwise.) */
 int bissd_forward_noalloc(const bissd_shape_t *shape, const void *x, bissd_dir_t fwd,
                           bissd_dir_t rev, const float *D, const float *init_state, void *y,
                           float *final_state, void *stream);
@@ -233,6 +252,12 @@ int bissd_forward_noalloc(const bissd_shape_t *shape, const void *x, bissd_dir_t
  *   dx [Z][L][H][P] fp32; gfwd / grev: per-direction ddt, dA, dB, dC (fp32);
  *   dD [H] fp32.  All outputs are overwritten; dA, dB, dC and dD are
  *   reduced deterministically (no floating-point atomics).
+ * With BISSD_SAVE in shape->flags the workspace must be the one a
+ * bissd_forward call with the same shape (flag included), x, fwd, rev, D
+ * and init_state filled, untouched since: its chunk states, carry-ins, decays
+ * and Gram tiles are read instead of formed again, with the same results
+ * bit for bit.  The library cannot check that contract.  The backward
+ * overwrites them (one backward per saving forward).
  */
 int bissd_backward(const bissd_shape_t *shape, const void *x, bissd_dir_t fwd,
                    bissd_dir_t rev, const float *D, const float *init_state,
@@ -368,7 +393,8 @@ int bissd_last_hip_error(void);
 int bissd_timer_arm(int32_t slot);
 int bissd_timer_read(int32_t slot, float *ms);
 
-/* ABI version: 3 (2 had no convolution fields, 1 no dt post-processing fields). */
+/* ABI version: 4 (3 had a reserved field in place of bissd_shape_t.flags, 2 no
+ * convolution fields, 1 no dt post-processing fields). */
 int bissd_version(void);
 
 #ifdef __cplusplus

@@ -62,16 +62,16 @@ _SHAPES: dict = {}
 
 
 def shape_of(x: torch.Tensor, B: torch.Tensor, chunk: int, rev_block: int = 0,
-             conv_width: int = 0) -> _abi.Shape:
+             conv_width: int = 0, flags: int = 0) -> _abi.Shape:
     """The ABI shape struct for x / B (memoised: block updates call this in
     tight loops, and the C side only reads it)."""
-    key = (x.shape, B.shape, x.dtype, chunk, rev_block, conv_width)
+    key = (x.shape, B.shape, x.dtype, chunk, rev_block, conv_width, flags)
     s = _SHAPES.get(key)
     if s is None:
         Z, L, H, P = x.shape
         G, N = B.shape[2], B.shape[3]
         s = _abi.Shape(Z, L, H, P, N, G, int(chunk), _dtype_code(x), int(rev_block),
-                       int(conv_width), 0)
+                       int(conv_width), int(flags))
         if len(_SHAPES) > 1024:
             _SHAPES.clear()
         _SHAPES[key] = s
@@ -238,15 +238,18 @@ def _on_stream(device: torch.device, stream):
 def bissd_forward(x: torch.Tensor, fwd, rev, D: torch.Tensor, *, chunk: int = 256,
                   rev_block: int = 0, init_state: Optional[torch.Tensor] = None,
                   y: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
-                  workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                  workspace: Optional[torch.Tensor] = None, save: bool = False, stream=None):
     """y = yf + yr + D x (see include/bissd.h, bissd_forward).  ``rev_block``
     > 0 restarts the reverse scan at the end of every block of that many
-    tokens (the block-segmented reverse of full-block training)."""
+    tokens (the block-segmented reverse of full-block training).  With
+    ``save`` (the forward of a training step) it returns ``(y, saved)``:
+    ``saved`` is the workspace holding what ``bissd_backward(..., saved=saved)``
+    of the same inputs reads instead of recomputing (BISSD_SAVE)."""
     lib = _abi.load()
     fwd, rev = Dir(*fwd), Dir(*rev)
     _check_scan(x, fwd, rev, D, states=(("init_state", init_state), ("final_state", final_state)),
                 acts=(("y", y),))
-    shape = shape_of(x, fwd.B, chunk, rev_block, _conv_width(fwd, rev))
+    shape = shape_of(x, fwd.B, chunk, rev_block, _conv_width(fwd, rev), _abi.SAVE if save else 0)
     with _on_stream(x.device, stream):
         if y is None:
             y = torch.empty_like(x)
@@ -255,7 +258,7 @@ def bissd_forward(x: torch.Tensor, fwd, rev, D: torch.Tensor, *, chunk: int = 25
                            _ptr(init_state), _ptr(y), _ptr(final_state), _ptr(ws),
                            C.c_size_t(nws), _stream(x.device, stream))
     _abi.check("bissd_forward", st)
-    return y
+    return (y, ws) if save else y
 
 
 def bissd_forward_noalloc(x: torch.Tensor, fwd, rev, D: torch.Tensor, *, y: torch.Tensor,
@@ -348,11 +351,14 @@ GRAD_KEYS = ("dx", "ddt_f", "dA_f", "dB_f", "dC_f", "ddt_r", "dA_r", "dB_r", "dC
 def bissd_backward(x: torch.Tensor, fwd, rev, D: torch.Tensor, dy: torch.Tensor, *,
                    chunk: int = 256, rev_block: int = 0,
                    init_state: Optional[torch.Tensor] = None, grads: Optional[dict] = None,
-                   workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+                   workspace: Optional[torch.Tensor] = None,
+                   saved: Optional[torch.Tensor] = None, stream=None) -> dict:
     """Gradients of sum(dy * y) (include/bissd.h, bissd_backward).  Returns a
     dict with dx, ddt_f, dA_f, dB_f, dC_f, ddt_r, dA_r, dB_r, dC_r, dD (fp32),
     plus ddt_bias_<d> for a direction with a dt bias; ``grads`` may hold
-    preallocated tensors under those keys.  ``rev_block`` as in bissd_forward."""
+    preallocated tensors under those keys.  ``rev_block`` as in bissd_forward.
+    ``saved``: the second result of ``bissd_forward(..., save=True)`` with the
+    same inputs, used as the workspace (BISSD_SAVE); it is consumed."""
     lib = _abi.load()
     fwd, rev = Dir(*fwd), Dir(*rev)
     g = dict(grads) if grads is not None else {}
@@ -370,7 +376,12 @@ def bissd_backward(x: torch.Tensor, fwd, rev, D: torch.Tensor, dy: torch.Tensor,
                 outs=tuple((k, g.get(k), shp, torch.float32) for k, shp in gshape.items()))
     if dy is None:
         raise ValueError("dy is required")
-    shape = shape_of(x, fwd.B, chunk, rev_block, _conv_width(fwd, rev))
+    if saved is not None and workspace is not None:
+        raise ValueError("pass saved or workspace, not both")
+    shape = shape_of(x, fwd.B, chunk, rev_block, _conv_width(fwd, rev),
+                     _abi.SAVE if saved is not None else 0)
+    if saved is not None:
+        workspace = saved
     with _on_stream(x.device, stream):
         for k, shp in gshape.items():
             if k not in g:

@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(HERE, "libbissd.so")
 BISSD_F32 = 0
 BISSD_BF16 = 1
 OP_FORWARD, OP_BACKWARD, OP_BLOCK = 0, 1, 2
+SAVE = 1  # shape flag: the forward keeps what the backward reads
 
 STATUS = {
     0: "BISSD_OK", -1: "BISSD_ERR_NULL", -2: "BISSD_ERR_SHAPE", -3: "BISSD_ERR_UNSUPPORTED",
@@ -36,7 +37,7 @@ class Shape(C.Structure):
     _fields_ = [("batch", C.c_int64), ("seqlen", C.c_int64), ("nheads", C.c_int64),
                 ("headdim", C.c_int64), ("dstate", C.c_int64), ("ngroups", C.c_int64),
                 ("chunk", C.c_int64), ("dtype", C.c_int32), ("rev_block", C.c_int32),
-                ("conv_width", C.c_int32), ("reserved", C.c_int32)]
+                ("conv_width", C.c_int32), ("flags", C.c_int32)]
 
 
 class AttnShape(C.Structure):

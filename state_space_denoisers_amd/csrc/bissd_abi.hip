@@ -65,9 +65,12 @@ int check_shape(const bissd_shape_t *s, int op) {
       s->ngroups <= 0 || s->chunk <= 0)
     return BISSD_ERR_SHAPE;
   if (s->nheads % s->ngroups != 0) return BISSD_ERR_SHAPE;
-  if (s->rev_block < 0 || s->conv_width < 0 || s->reserved != 0) return BISSD_ERR_SHAPE;
+  if (s->rev_block < 0 || s->conv_width < 0 || (s->flags & ~BISSD_SAVE) != 0) return BISSD_ERR_SHAPE;
   if (s->conv_width > 4) return BISSD_ERR_UNSUPPORTED;
   if (op != BISSD_OP_FORWARD && op != BISSD_OP_BACKWARD && op != BISSD_OP_BLOCK)
+    return BISSD_ERR_UNSUPPORTED;
+  // values kept for a backward: forward and backward only, no convolution
+  if ((s->flags & BISSD_SAVE) && (op == BISSD_OP_BLOCK || s->conv_width > 0))
     return BISSD_ERR_UNSUPPORTED;
   // the reverse blocks are whole 64-token tiles and either split a chunk
   // evenly or span whole chunks
@@ -114,6 +117,9 @@ struct WsLayout {
 
 WsLayout ws_layout(const bissd_shape_t *s, int op) {
   WsLayout w;
+  // a forward that keeps values for the backward writes them where the
+  // backward reads them: it takes the backward's layout
+  if (op == BISSD_OP_FORWARD && (s->flags & BISSD_SAVE)) op = BISSD_OP_BACKWARD;
   const int64_t nc = op == BISSD_OP_BLOCK ? 1 : ceil_div(s->seqlen, s->chunk);
   const int64_t ndir = op == BISSD_OP_BLOCK ? 1 : 2;
   const size_t nst = (size_t)(ndir * s->batch * nc * s->nheads * s->headdim * s->dstate);
@@ -311,7 +317,7 @@ void bissd::take_timer(hipEvent_t *start, hipEvent_t *stop) {
 
 extern "C" {
 
-int bissd_version(void) { return 3; }
+int bissd_version(void) { return 4; }
 
 int bissd_last_hip_error(void) { return g_last_hip; }
 
@@ -422,7 +428,11 @@ static int forward_impl(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, 
   a.ndir = 2;
   a.init_state = init_state;
   a.final_state = final_state;
-  a.skip_edges = 1;
+  const bool save = (s->flags & BISSD_SAVE) != 0;
+  // kept for the backward: every chunk state and carry-in (no edge skipped)
+  // and every token's decay sum
+  a.skip_edges = save ? 0 : 1;
+  if (save) a.cum_out = (float *)(ws + wl.lamg);
   const int64_t PN = s->headdim * s->dstate;
   a.sin_t = ws + wl.sin_t;
   const size_t esz = s->dtype == BISSD_BF16 ? 2 : 4;
@@ -464,6 +474,7 @@ int bissd_forward_noalloc(const bissd_shape_t *s, const void *x, bissd_dir_t fwd
                           void *stream) {
   int rc = check_shape(s, BISSD_OP_FORWARD);
   if (rc) return rc;
+  if (s->flags & BISSD_SAVE) return BISSD_ERR_UNSUPPORTED;
   // the forward's workspace needs no zeroing: every kernel writes what a
   // later one reads before it is read, in this call
   const size_t need = ws_layout(s, BISSD_OP_FORWARD).total;
@@ -644,10 +655,13 @@ int bissd_backward(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, bissd
     a.sin_bstride[d] = (int64_t)nc * a.H * PN;
     a.sin_cstride[d] = (int64_t)a.H * PN;
   }
-  // the primal chunk states also keep every token's decay sum for the panels
+  // the primal chunk states also keep every token's decay sum for the
+  // panels; a saving forward has left them (and the chunk decays, the Gram
+  // tiles and the carry-ins) in the workspace
+  const bool saved = (s->flags & BISSD_SAVE) != 0;
   ScanArgs a0 = a;
   a0.cum_out = (float *)(ws + wl.lamg);
-  hipError_t e = bissd::launch_scan_phase(a0, bissd::PHASE_CHUNK_STATE, st);
+  hipError_t e = saved ? hipSuccess : bissd::launch_scan_phase(a0, bissd::PHASE_CHUNK_STATE, st);
 
   // A-tangent chunk states (dt-sum weighted), chunk dt sums (and every
   // token's cumulative dt), and the A-tangent carry-ins S^A_in together with
@@ -661,7 +675,7 @@ int bissd_backward(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, bissd
   tp.states2 = (const void *)(ws + wl.tstates);
   tp.dtsum = (const float *)(ws + wl.dtsum);
   tp.sin_t = ws + wl.sa_t;
-  tp.sin_prim = a.sin_t;
+  tp.sin_prim = saved ? nullptr : a.sin_t;
   if (e == hipSuccess) e = bissd::launch_scan_phase(tp, bissd::PHASE_TAN_PASS, st);
 
   // adjoint chunk states sum_t 2^cum_t dy_t (outer) C_t (into the tangent
@@ -692,7 +706,7 @@ int bissd_backward(const bissd_shape_t *s, const void *x, bissd_dir_t fwd, bissd
   yd.slot_dir[0] = 0;
   yd.slot_dir[1] = 1;
   // the primal Gram tiles: from the chunk-state launch above, or here
-  if (e == hipSuccess && !a.gram_k1) e = bissd::launch_scan_phase(yd, bissd::PHASE_GRAM, st);
+  if (e == hipSuccess && !a.gram_k1 && !saved) e = bissd::launch_scan_phase(yd, bissd::PHASE_GRAM, st);
   if (e == hipSuccess) e = bissd::launch_scan_phase(yd, bissd::PHASE_YDOT, st);
 
   // dx and x.(G_t B_t): slot 0 (causal) takes the reverse direction's

@@ -35,7 +35,7 @@ def test_header_and_binding_agree():
 def test_every_declared_symbol_is_exported(lib):
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert lib.bissd_version() == 3
+    assert lib.bissd_version() == 4
     assert lib.bissd_last_hip_error() == 0
 
 
@@ -313,7 +313,7 @@ def test_convolution_validation(lib):
     assert call_forward(lib, shape(conv_width=0), fwd=conv_dir(1, ok_w)) == -2
     assert call_forward(lib, shape(conv_width=5)) == -3
     assert call_forward(lib, shape(conv_width=-1)) == -2
-    assert call_forward(lib, shape(reserved=1)) == -2
+    assert call_forward(lib, shape(flags=2)) == -2
     assert call_forward(lib, shape(conv_width=4), rev=conv_dir(5, None, addr(31))) == -2
     assert call_forward(lib, shape(conv_width=4), rev=conv_dir(5, None, None, act=1)) == -2
     assert call_forward(lib, shape(conv_width=4), rev=conv_dir(5, ok_w, act=2)) == -2
@@ -357,3 +357,29 @@ def test_timer_validation(lib):
     assert lib.bissd_timer_read(4096, C.byref(ms)) == -2
     assert lib.bissd_timer_read(4095, None) == -1
     assert lib.bissd_timer_read(4095, C.byref(ms)) == -1
+
+
+def test_save_flag_validation(lib):
+    """BISSD_SAVE: the saving forward's workspace is the backward's (so one
+    buffer serves both calls), and the flag is refused where there is no
+    backward to keep values for (a convolution, a block update, the static
+    scratch array) or next to an unknown flag bit."""
+    plain, saving = shape(), shape(flags=_abi.SAVE)
+    nf = lib.bissd_workspace_size(C.byref(plain), _abi.OP_FORWARD)
+    nb = lib.bissd_workspace_size(C.byref(plain), _abi.OP_BACKWARD)
+    assert nb > nf > 0
+    assert lib.bissd_workspace_size(C.byref(saving), _abi.OP_FORWARD) == nb
+    assert lib.bissd_workspace_size(C.byref(saving), _abi.OP_BACKWARD) == nb
+    # a forward-sized workspace is too small for a saving forward
+    assert call_forward(lib, saving, nws=nf) == -5
+    assert call_forward(lib, shape(flags=_abi.SAVE | 2)) == -2
+    assert call_forward(lib, shape(flags=_abi.SAVE, conv_width=4)) == -3
+    assert lib.bissd_workspace_size(C.byref(shape(flags=_abi.SAVE, conv_width=4)), _abi.OP_FORWARD) == 0
+    blk = shape(seqlen=64, chunk=64, flags=_abi.SAVE)
+    rc = lib.bissd_block_update(C.byref(blk), addr(20), addr(0), dirs(1), dirs(5), addr(9),
+                                addr(10), None, None, None, addr(12), C.c_size_t(1 << 40), None)
+    assert rc == -3
+    args = (addr(0), dirs(1), dirs(5), addr(9), None, addr(10), None, None)
+    assert lib.bissd_forward_noalloc(C.byref(shape(seqlen=64, chunk=64, flags=_abi.SAVE)), *args) == -3
+    # the backward takes the flag like the forward
+    assert call_backward(lib, shape(flags=_abi.SAVE), nws=16) == -5
