@@ -400,6 +400,9 @@ __global__ __launch_bounds__(kStThreads) void k_bwd_state(BwdArgs a) {
   Frag<T> rf[NS][2][2];
   f32x4 lm[NS][2];
   uint32_t dtr[NS][2][4];
+  // dB: the head's decay sum at the chunk's end and its dt bias (uniform
+  // scalars, fetched with the head's other loads)
+  float lendv[NS], biasv[NS];
   // Issue order, pinned by compiler fences (no memory access moves across
   // them, in the IR or in the machine scheduler): head after head, and in
   // each head the state copy before the register loads.  The waits below
@@ -431,6 +434,10 @@ __global__ __launch_bounds__(kStThreads) void k_bwd_state(BwdArgs a) {
                              __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, lo + 8u, 0, 0)),
                              __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, lo + 12u, 0, 0))};
         if constexpr (PNL == 1) {
+          if (rt == 0) {
+            lendv[slot] = a.lamg[(cbase + h) * L + t0 + (d == 0 ? qlen - 1 : 0)];
+            biasv[slot] = post.on ? a.dtb[d][h] : 0.0f;
+          }
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const uint32_t doff = (uint32_t)((t0 + r + 4 * g4 + i) * H + h) * ES;
@@ -480,12 +487,11 @@ __global__ __launch_bounds__(kStThreads) void k_bwd_state(BwdArgs a) {
       __syncthreads();
       if (hi + NS - 1 < hpg) issue(hi + NS - 1, (u + NS - 1) % NS);
       if (!rows) continue;
-      const int h = g * hpg + hi;
       const char *tile = tiles + u * STB;
       float lend = 0.0f, bias = 0.0f;
       if constexpr (PNL == 1) {
-        lend = a.lamg[(cbase + h) * L + t0 + (d == 0 ? qlen - 1 : 0)];
-        bias = post.on ? a.dtb[d][h] : 0.0f;
+        lend = lendv[u];
+        bias = biasv[u];
       }
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {

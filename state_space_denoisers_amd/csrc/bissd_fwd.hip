@@ -963,6 +963,13 @@ void k3_chunk_out(ScanArgs a) {
   __shared__ Sm sm;
   // MODE 1: in-chunk cumulative dt of every token, per (direction, head)
   __shared__ __attribute__((aligned(16))) float smcdt[DAI ? 2 : 1][HT][DAI ? kQmax : 4];
+  // MODE 1 (one head per workgroup): the row-block's dy rows, staged once
+  // and read by both slots' epilogues in the accumulators' layout.  Row
+  // pitch 68 elements: the reads (lane rows 4 apart, 16 consecutive
+  // columns) meet distinct banks, and the rows stay 8-byte aligned for the
+  // staging writes.
+  constexpr int kDyP = 68;
+  __shared__ __attribute__((aligned(16))) T sdy[MODE == 1 ? kRB : 1][MODE == 1 ? kDyP : 4];
   constexpr int NK = N / 32;
   const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
   const int Q = a.chunk, NRB = Q / kRB, H = a.H, G = a.G;
@@ -1047,6 +1054,21 @@ void k3_chunk_out(ScanArgs a) {
   // out first, raw and unconditional (tokens past L read as zero), then the
   // first stage's loads, so neither waits for the other.
   static_assert(2 * HT <= kThreads / 64, "one decay scan per wave");
+  // MODE 1: the row-block's dy rows (aux), in 16-byte pieces (rows past the
+  // end read as zero), go out before everything else and reach LDS at the
+  // end of the prologue, where the epilogues find them.  (MODE 2 reads its
+  // epilogue rows from global memory there, x from aux and dy from x.)
+  constexpr int kDyV = (kRB * kP * (int)ES / 16) / kThreads;  // pieces per thread
+  const int64_t rowel = (int64_t)L * H * kP;  // elements of one batch row's [L][H][P]
+  const bufres rXa = make_buf(reinterpret_cast<const T *>(a.aux) + (int64_t)b * rowel, (uint32_t)(rowel * ES));
+  u32x4 dyraw[MODE == 1 ? kDyV : 1];
+  if constexpr (MODE == 1) {
+#pragma unroll
+    for (int m = 0; m < kDyV; ++m) {
+      const int it = tid + m * kThreads, r = it / (kP * (int)ES / 16), pc = it % (kP * (int)ES / 16);
+      dyraw[m] = bload16(rXa, (uint32_t)(((t0 + j * kRB + r) * H + h0) * kP) * ES + 16u * pc);
+    }
+  }
   const int pd = w / HT, ph = w % HT;
   uint32_t dtraw[4], cdraw[kQmax / kRB];
   float Ah = 0.0f;
@@ -1116,6 +1138,15 @@ void k3_chunk_out(ScanArgs a) {
     for (int ks = 0; ks < NK; ++ks)
       frag_bload(cfd[ks], rC[d], (uint32_t)((t0 + trow) * G + gidx) * N * ES + (32 * ks + 8 * g4) * ES);
   };
+  if constexpr (MODE == 1) {
+#pragma unroll
+    for (int m = 0; m < kDyV; ++m) {
+      const int it = tid + m * kThreads, r = it / (kP * (int)ES / 16), pc = it % (kP * (int)ES / 16);
+      uint2 *dst = reinterpret_cast<uint2 *>(reinterpret_cast<char *>(&sdy[r][0]) + 16 * pc);
+      dst[0] = uint2{dyraw[m][0], dyraw[m][1]};
+      dst[1] = uint2{dyraw[m][2], dyraw[m][3]};
+    }
+  }
   __syncthreads();
 
   // The factored diagonal slab multiplies by 2^(lam_t - lam_end) <= 2^(15 max|a|)
@@ -1436,18 +1467,70 @@ void k3_chunk_out(ScanArgs a) {
       }
     }
   } else {
-    // Backward modes: each slot's accumulator is finished on its own.  Rows
-    // are staged through LDS; 8 consecutive lanes hold one row of one head
-    // (8 elements each) and reduce their dot products with shuffles.
+    // Backward modes: each slot's accumulator is finished on its own.
+    // MODE 1 (one head per workgroup): dy . y_d per row and the within-chunk
+    // dA partial straight from the accumulators, whose lane (r16, g4) of
+    // wave w holds rows 16 w + 4 g4 + i2, columns 16 v + r16: dy is read
+    // from LDS in that layout, each row's dot product is summed over its 16
+    // lanes by DPP, and the dA partial needs no per-row sum at all.
+    auto ydot_epilogue = [&](auto dc) __attribute__((always_inline)) {
+      constexpr int d = decltype(dc)::value;
+      static_assert(HT == 1, "one head per workgroup");
+      float part[4], dsum = 0.0f;
+#pragma unroll
+      for (int i2 = 0; i2 < 4; ++i2) {
+        const int r = 16 * w + 4 * g4 + i2;
+        float pa = 0.0f, pb = 0.0f;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float dv = to_f(sdy[r][16 * v + r16]);
+          pa += acc[0][v][i2] * dv;
+          if constexpr (DAI) pb += acc2[0][v][i2] * dv;
+        }
+        part[i2] = pa;
+        if (j * kRB + r < qlen) dsum += pb;
+      }
+      // row sums: inclusive sums over the 16 lanes of each lane row
+#pragma unroll
+      for (int i2 = 0; i2 < 4; ++i2) {
+        float v = part[i2];
+        v += dpp_f<0x111>(v);
+        v += dpp_f<0x112>(v);
+        v += dpp_f<0x114>(v);
+        v += dpp_f<0x118>(v);
+        part[i2] = v;
+      }
+      const int sd = a.slot_dir[d];
+      if (r16 == 15) {
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2) {
+          const int r = j * kRB + 16 * w + 4 * g4 + i2;
+          if (r < qlen) a.out0[(((int64_t)sd * a.Z + b) * L + t0 + r) * H + h0] = part[i2];
+        }
+      }
+      // the within-chunk dA partial of this row-block, reduced in a fixed order
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) dsum += __shfl_xor(dsum, o, 64);
+      if (lane == 0) sm.red[w][0] = dsum;
+      __syncthreads();
+      if (tid == 0)
+        a.dai_out[((((int64_t)sd * a.Z + b) * a.nchunks + c) * NRB + j) * H + h0] =
+            (sm.red[0][0] + sm.red[1][0]) + (sm.red[2][0] + sm.red[3][0]);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) zero4(acc2[0][v]);
+    };
+    // MODE 2: each head's accumulator is staged through LDS; 8 consecutive
+    // lanes hold one row (8 elements each) and reduce their dot products
+    // with shuffles.
     float ddp[HT];
 #pragma unroll
     for (int hh = 0; hh < HT; ++hh) ddp[hh] = 0.0f;
     // The epilogue's global inputs of one head: per row pass m2 the 8
-    // elements from p0 of row r of the aux rows (MODE 1: dy, MODE 2: x), and
-    // in MODE 2 of dy.  The input rows come raw through buffer loads (rows
-    // past the sequence end read as zero, no branch); each head's are issued
-    // before the previous head is finished, so their latency overlaps that
-    // work instead of following it.
+    // elements from p0 of row r of the x rows (aux) and of the dy rows.  The
+    // input rows come raw through buffer loads (rows past the sequence end
+    // read as zero, no branch); each head's are issued before the previous
+    // head is finished, so their latency overlaps that work instead of
+    // following it.
     constexpr int NRV = sizeof(T) == 2 ? 1 : 2;  // 16-byte pieces of 8 elements
     constexpr int NM2 = (kRB * 8) / kThreads;
     struct EpiRows {
@@ -1457,8 +1540,7 @@ void k3_chunk_out(ScanArgs a) {
     // thread's 8 elements of each row pass and head, kept in registers until
     // slot 1 adds its own and writes dx once
     float dxk[MODE == 2 ? HT : 1][NM2][8];
-    const int64_t rowel = (int64_t)L * H * kP;  // elements of one batch row's [L][H][P]
-    const bufres rAux = make_buf(reinterpret_cast<const T *>(a.aux) + (int64_t)b * rowel, (uint32_t)(rowel * ES));
+    const bufres rAux = rXa;
     auto epi_off = [&](int hh, int m2) __attribute__((always_inline)) {
       const int it = tid + m2 * kThreads;
       const int r = it >> 3, p0 = (it & 7) * 8;
@@ -1470,10 +1552,8 @@ void k3_chunk_out(ScanArgs a) {
         const uint32_t eo = epi_off(hh, m2);
 #pragma unroll
         for (int k = 0; k < NRV; ++k) e.v[m2][k] = bload16(rAux, eo * ES + 16 * k);
-        if constexpr (MODE == 2) {
 #pragma unroll
-          for (int k = 0; k < NRV; ++k) e.dy[m2][k] = bload16(rX, eo * ES + 16 * k);
-        }
+        for (int k = 0; k < NRV; ++k) e.dy[m2][k] = bload16(rX, eo * ES + 16 * k);
       }
     };
     auto raw8 = [&](const u32x4 (&r)[NRV], float (&o)[8]) __attribute__((always_inline)) {
@@ -1491,14 +1571,9 @@ void k3_chunk_out(ScanArgs a) {
           }
       }
     };
-    auto slot_epilogue = [&](auto dc) __attribute__((always_inline)) {
+    auto dx_epilogue = [&](auto dc) __attribute__((always_inline)) {
       constexpr int d = decltype(dc)::value;
       const int sd = a.slot_dir[d];
-      // MODE 1: the within-chunk dA of this row-block per head, the sum over
-      // its rows of dy . acc2, from the same dy rows as dy . y_d
-      float dsum[HT];
-#pragma unroll
-      for (int hh = 0; hh < HT; ++hh) dsum[hh] = 0.0f;
       EpiRows nxt;
       epi_load(0, nxt);
 #pragma unroll
@@ -1534,9 +1609,7 @@ void k3_chunk_out(ScanArgs a) {
             part += __shfl_xor(part, 2, 64);
             part += __shfl_xor(part, 4, 64);
             const int64_t oix = (((int64_t)sd * a.Z + b) * L + tok) * H + h0 + hh;
-            if constexpr (MODE == 1) {
-              if ((tid & 7) == 0 && valid) a.out0[oix] = part;
-            } else {
+            {
               // part = x.(G_t B_t) without t' = t; add dy_t (B_t.C_t)
               const float dtr = sm.dtd[d][hh][r], bc = sm.bcd[d][r];
               float *dxp = a.out1 + (((int64_t)b * L + tok) * H + h0 + hh) * kP + p0;
@@ -1569,48 +1642,9 @@ void k3_chunk_out(ScanArgs a) {
               }
             }
           }
-          if constexpr (DAI) {
-            // acc2 of this head through the same LDS rows, dotted with the
-            // dy rows still in registers
-            __syncthreads();
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-#pragma unroll
-              for (int i2 = 0; i2 < 4; ++i2) sm.u.Out[q][16 * w + 4 * g4 + i2][16 * v + r16] = acc2[hh][v][i2];
-            __syncthreads();
-#pragma unroll
-            for (int m2 = 0; m2 < NM2; ++m2) {
-              const int it = tid + m2 * kThreads;
-              const int r = it >> 3, p0 = (it & 7) * 8;
-              float v[8];
-              raw8(cur.v[m2], v);
-              float t = 0.0f;
-#pragma unroll
-              for (int e = 0; e < 8; ++e) t += sm.u.Out[q][r][p0 + e] * v[e];
-              if (j * kRB + r < qlen) dsum[hh] += t;
-            }
-          }
         }
       }
-      if constexpr (DAI) {
-        // the within-chunk dA partial sums, reduced in a fixed order
-#pragma unroll
-        for (int hh = 0; hh < HT; ++hh) {
-          float v = dsum[hh];
-#pragma unroll
-          for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
-          if (lane == 0) sm.red[w][hh] = v;
-        }
-        __syncthreads();
-        if (tid < HT)
-          a.dai_out[((((int64_t)sd * a.Z + b) * a.nchunks + c) * NRB + j) * H + h0 + tid] =
-              (sm.red[0][tid] + sm.red[1][tid]) + (sm.red[2][tid] + sm.red[3][tid]);
-#pragma unroll
-        for (int hh = 0; hh < HT; ++hh)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) zero4(acc2[hh][v]);
-      }
-      if constexpr (MODE == 2 && d == 0) {
+      if constexpr (d == 0) {
         // dy.x of this row-block, per head, in a fixed order
 #pragma unroll
         for (int hh = 0; hh < HT; ++hh) {
@@ -1626,13 +1660,15 @@ void k3_chunk_out(ScanArgs a) {
       }
     };
     run_direction(std::integral_constant<int, 0>{});
-    slot_epilogue(std::integral_constant<int, 0>{});
+    if constexpr (MODE == 1) ydot_epilogue(std::integral_constant<int, 0>{});
+    else dx_epilogue(std::integral_constant<int, 0>{});
 #pragma unroll
     for (int hh = 0; hh < HT; ++hh)
 #pragma unroll
       for (int v = 0; v < 4; ++v) zero4(acc[hh][v]);
     run_direction(std::integral_constant<int, 1>{});
-    slot_epilogue(std::integral_constant<int, 1>{});
+    if constexpr (MODE == 1) ydot_epilogue(std::integral_constant<int, 1>{});
+    else dx_epilogue(std::integral_constant<int, 1>{});
   }
 }
 
