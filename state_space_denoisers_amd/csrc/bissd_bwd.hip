@@ -60,6 +60,9 @@ __device__ __forceinline__ DtPost dt_post_of(const BwdArgs &a, int d, int h) {
 
 // ============================================================ dB / dC panel
 
+// compute units per XCD (256 in 8 XCDs)
+constexpr int kCusPerXcd = 32;
+
 template <typename T, int N> struct PanelLds {
   float lam[2][kQmax];
   float dtv[2][kQmax];
@@ -107,9 +110,15 @@ void k_bwd_panel(BwdArgs a) {
   const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
   const int Q = a.chunk, NRB = Q / kRB, H = a.H, G = a.G, hpg = H / G;
   const int64_t L = a.L;
-  // work item = (((b * nchunks + c) * 2 + d) * G + g) * NRB + j
+  // work item = (((b * nchunks + c) * 2 + d) * G + g) * NRB + j', where an
+  // XCD hands its consecutive workgroups to its 32 compute units in turn
+  // (items 32 apart share one): the row-block j, whose causal column range
+  // sets the workgroup's work (1 to NRB column blocks), is j' rotated by the
+  // item's group of 32, so that a compute unit holds every row-block instead
+  // of four workgroups of one (a bijection: the NRB items of one (b, c, d,
+  // g) share their group)
   int bx = xcd_linear_id(blockIdx.x, gridDim.x);
-  const int j = bx % NRB;
+  const int j = (bx + bx / kCusPerXcd) % NRB;
   bx /= NRB;
   const int g = bx % G;
   bx /= G;
