@@ -151,3 +151,14 @@ def test_chunk_invariance_fp32():
     b = gpu_backward(inp, "fp32", 256)
     for k in KEYS:
         assert maxrel(a[k], b[k]) <= 1e-5, k
+
+
+@pytest.mark.parametrize("H,G", [(40, 2), (33, 1)])
+def test_many_heads_fp32(H, G):
+    """More heads than one decay-gradient workgroup takes (32): the heads
+    split into equal groups (40 -> 2 x 20; 33 -> 17 + 16, an odd and an even
+    LDS pitch); every gradient against the oracle."""
+    w = W["tiny_fp32"].replace(L=300, Z=1, H=H, G=G, chunk=128)
+    inp = gen.make_inputs(w, mode="scan", with_dy=True)
+    print("bwd many heads", H, G, flush=True)
+    check(inp, "fp32", w.chunk)
