@@ -193,11 +193,12 @@ __global__ __launch_bounds__(kBlkThreads) void k_block_update(ScanArgs a) {
       for (int v = 0; v < 4; ++v) {
         Frag<T> xf;
         frag_rows_swz<DX>(xf, tXd[d], 32 * q + 4 * g4, 32 * q + 16 + 4 * g4, 16 * v);
-        mma(acc[v], mf, xf);
+        mma(acc[v], xf, mf);
       }
     }
     if constexpr (d == 0) {
-      // carried state: 2^lam_t C_t S_in^T (rows t = 16w + 4 g4 + i)
+      // carried state: 2^lam_t (S_in C_t^T) for this lane's token t = 16w + r16
+      const float et = exp2_fast(sm.lam[0][trow]);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         f32x4 t2;
@@ -206,10 +207,10 @@ __global__ __launch_bounds__(kBlkThreads) void k_block_update(ScanArgs a) {
         for (int ks = 0; ks < NK; ++ks) {
           Frag<T> sf;
           frag_ld8_swz_f32<DS>(sf, tS, 16 * v + r16, 32 * ks + 8 * g4);
-          mma(t2, cf[ks], sf);
+          mma(t2, sf, cf[ks]);
         }
 #pragma unroll
-        for (int i2 = 0; i2 < 4; ++i2) acc[v][i2] += exp2_fast(sm.lam[0][16 * w + 4 * g4 + i2]) * t2[i2];
+        for (int i2 = 0; i2 < 4; ++i2) acc[v][i2] += et * t2[i2];
       }
     }
   };
@@ -229,9 +230,9 @@ __global__ __launch_bounds__(kBlkThreads) void k_block_update(ScanArgs a) {
   __syncthreads();
 
   if (grp == 0) {
-    // ---- y = forward + reverse + D x (forward group; rows 16w + 4 g4 + i,
-    // columns 16 v + r16; 16 lanes store one contiguous row segment), x from
-    // its tile
+    // ---- y = forward + reverse + D x (forward group), x from its tile.  The
+    // products are transposed (x^T W^T): the lane holds token t = 16w + r16
+    // and four consecutive columns p = 16 v + 4 g4 + i per v, stored at once
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const f32x4 r = xchg[w][v][lane];
@@ -239,16 +240,25 @@ __global__ __launch_bounds__(kBlkThreads) void k_block_update(ScanArgs a) {
       for (int i2 = 0; i2 < 4; ++i2) acc[v][i2] += r[i2];
     }
     const float Dh = a.D[h];
-    T *yg = reinterpret_cast<T *>(a.y) + ((int64_t)b * L * H + h) * kP;
-#pragma unroll
-    for (int i2 = 0; i2 < 4; ++i2) {
-      const int t = 16 * w + 4 * g4 + i2;
-      if (t >= L) continue;
+    if (trow < L) {
+      T *yg = reinterpret_cast<T *>(a.y) + (((int64_t)b * L + trow) * H + h) * kP;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int p = 16 * v + r16;
-        const float xv = to_f(*reinterpret_cast<const T *>(tX + DX::at(t, (int)ES * p)));
-        yg[(int64_t)t * H * kP + p] = from_f<T>(acc[v][i2] + Dh * xv);
+        const int p = 16 * v + 4 * g4;
+        const T *xp = reinterpret_cast<const T *>(tX + DX::at(trow, (int)ES * p));
+        if constexpr (sizeof(T) == 2) {
+          const bf16x4 xv = *reinterpret_cast<const bf16x4 *>(xp);
+          bf16x4 o;
+#pragma unroll
+          for (int i2 = 0; i2 < 4; ++i2) o[i2] = (bf16)(acc[v][i2] + Dh * (float)xv[i2]);
+          *reinterpret_cast<bf16x4 *>(yg + p) = o;
+        } else {
+          const f32x4 xv = *reinterpret_cast<const f32x4 *>(xp);
+          f32x4 o;
+#pragma unroll
+          for (int i2 = 0; i2 < 4; ++i2) o[i2] = acc[v][i2] + Dh * xv[i2];
+          *reinterpret_cast<f32x4 *>(yg + p) = o;
+        }
       }
     }
   }
@@ -256,7 +266,9 @@ __global__ __launch_bounds__(kBlkThreads) void k_block_update(ScanArgs a) {
   // ---- committed state: S_out = 2^lam_last S_in + sum_s w_s x_s (outer)
   // B_s, w_s = 2^(lam_last - lam_s) dt_s.  Group g forms columns n of its
   // half (16-column tiles g NT / 2 .. g NT / 2 + NT / 2 - 1); wave w owns
-  // state rows p = 16w..16w+15.
+  // state rows p = 16w..16w+15.  Formed transposed (B^T x), so the lane
+  // holds row p = 16w + r16 and four consecutive columns n per tile, read
+  // from S_in and written as one 16-byte piece each.
   if (a.final_state) {
     constexpr int NH = NT / 2;
     const int nt0 = grp * NH;
@@ -281,19 +293,20 @@ __global__ __launch_bounds__(kBlkThreads) void k_block_update(ScanArgs a) {
       for (int nt = 0; nt < NH; ++nt) {
         Frag<T> bfr;
         frag_rows_swz<DB>(bfr, tBf, 32 * ks + 8 * g4, 32 * ks + 8 * g4 + 4, 16 * (nt0 + nt));
-        mma(sacc[nt], xa, bfr);
+        mma(sacc[nt], bfr, xa);
       }
     }
     const float gam = exp2_fast(lend);
     float *so = a.final_state + ((int64_t)b * H + h) * kP * N;
 #pragma unroll
-    for (int nt = 0; nt < NH; ++nt)
+    for (int nt = 0; nt < NH; ++nt) {
+      const int p = 16 * w + r16, n = 16 * (nt0 + nt) + 4 * g4;
+      const f32x4 s0 = *reinterpret_cast<const f32x4 *>(tS + DS::at(p, 4 * n));
+      f32x4 o;
 #pragma unroll
-      for (int i2 = 0; i2 < 4; ++i2) {
-        const int p = 16 * w + 4 * g4 + i2, n = 16 * (nt0 + nt) + r16;
-        const float s0 = *reinterpret_cast<const float *>(tS + DS::at(p, 4 * n));
-        so[p * N + n] = gam * s0 + sacc[nt][i2];
-      }
+      for (int i2 = 0; i2 < 4; ++i2) o[i2] = gam * s0[i2] + sacc[nt][i2];
+      *reinterpret_cast<f32x4 *>(so + p * N + n) = o;
+    }
   }
 
   // ---- the next conv state: row j of [conv state | x_blk] at j + L (the old
