@@ -349,8 +349,12 @@ void k_bwd_panel(BwdArgs a) {
 //   dC_t += sum_h 2^cum_t (dy_t . S_in)            (PNL 0, S_in the carry-in)
 //   dB_s += sum_h dt_s 2^(cum_end - cum_s) (x_s . Gc)  (PNL 1, Gc the adjoint carry)
 // with the head-dim product dy_t . S (a 64-vector times a 64 x N state).
-// Workgroup = (batch b, chunk c, direction d, group g), eight waves; wave w
-// owns chunk rows 32 w .. 32 w + 31.  Every head's state goes buffer -> LDS
+// Workgroup = (batch b, chunk c, direction d, group g, half of the chunk's
+// rows), four waves; wave w owns chunk rows 128 half + 32 w .. + 31.  Two
+// such workgroups per compute unit keep twice the state copies in flight
+// that one eight-wave workgroup over the whole chunk did (train L=2K
+// backward 1.073 -> 1.063 ms); each half copies every head's state (the
+// second read of a state is an L2 hit: the halves run side by side).  Every head's state goes buffer -> LDS
 // (transposed swizzle, as in the panels) into one of NS tiles, so the copies
 // of the next NS - 1 heads are in flight while one is multiplied; each state
 // tile serves all rows of the chunk.  Added to the panel's output (launched
@@ -362,9 +366,10 @@ __device__ __forceinline__ void hold(Frag<float> &f) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(f.v[e]) : : "memory");
 }
-constexpr int kStThreads = 512;
+constexpr int kStThreads = 256;
 template <typename T, int N, int PNL>
-__global__ __launch_bounds__(kStThreads) void k_bwd_state(BwdArgs a) {
+__global__ __launch_bounds__(kStThreads) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1)))
+void k_bwd_state(BwdArgs a) {
   constexpr uint32_t ES = sizeof(T);
   constexpr int SRB = N * (int)ES, STB = kP * SRB;
   constexpr int NS = sizeof(T) == 2 ? 3 : 2;  // state tiles (heads) in flight
@@ -381,9 +386,12 @@ __global__ __launch_bounds__(kStThreads) void k_bwd_state(BwdArgs a) {
   const int tid = threadIdx.x, wv = wave_id(), lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
   const int Q = a.chunk, H = a.H, G = a.G, hpg = H / G;
   const int64_t L = a.L;
-  // work item = ((b * nchunks + c) * 2 + d) * G + g; consecutive items on one
-  // XCD, so both directions of a chunk read its rows through the same L2
+  // work item = (((b * nchunks + c) * 2 + d) * G + g) * 2 + half; consecutive
+  // items on one XCD, so both halves and both directions of a chunk read its
+  // rows and states through the same L2
   int bx = xcd_linear_id(blockIdx.x, gridDim.x);
+  const int rb = (bx & 1) * NWV * 32;  // first chunk row of this half
+  bx >>= 1;
   const int g = bx % G;
   bx /= G;
   const int d = bx % 2;
@@ -391,7 +399,8 @@ __global__ __launch_bounds__(kStThreads) void k_bwd_state(BwdArgs a) {
   const int c = bx % a.nchunks, b = bx / a.nchunks;
   const int64_t t0 = (int64_t)c * Q;
   const int qlen = (int)((L - t0) < Q ? (L - t0) : Q);
-  const bool rows = 32 * wv < qlen;  // this wave has rows of the chunk
+  if (rb >= qlen) return;  // the whole workgroup: no barrier is reached
+  const bool rows = rb + 32 * wv < qlen;  // this wave has rows of the chunk
 
   const T *rowsrc = reinterpret_cast<const T *>(PNL == 0 ? a.dy : a.x);
   const T *stsrc = reinterpret_cast<const T *>(PNL == 0 ? a.sin[d] : a.gin[d]);
@@ -404,7 +413,7 @@ __global__ __launch_bounds__(kStThreads) void k_bwd_state(BwdArgs a) {
   post.hi = a.dthi[d];
 
   // per head in flight: row-source fragments of the wave's two 16-row tiles,
-  // the decay sums of the lane's 8 rows (rows 32 w + 16 rt + 4 g4 + i), and
+  // the decay sums of the lane's 8 rows (rows rb + 32 w + 16 rt + 4 g4 + i), and
   // for dB their raw dt
   Frag<T> rf[NS][2][2];
   f32x4 lm[NS][2];
@@ -432,7 +441,7 @@ __global__ __launch_bounds__(kStThreads) void k_bwd_state(BwdArgs a) {
       const bufres rl = make_buf(a.lamg + (cbase + h) * L, (uint32_t)(L * 4));
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
-        const int r = 32 * wv + 16 * rt;
+        const int r = rb + 32 * wv + 16 * rt;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
           frag_bload(rf[slot][rt][ks], rRow, (uint32_t)((t0 + r + r16) * H + h) * kP * ES + (32 * ks + 8 * g4) * ES);
@@ -512,7 +521,7 @@ __global__ __launch_bounds__(kStThreads) void k_bwd_state(BwdArgs a) {
           } else {
             DtPost ph = post;
             ph.bias = bias;
-            const int64_t tok = t0 + 32 * wv + 16 * rt + 4 * g4 + i;
+            const int64_t tok = t0 + rb + 32 * wv + 16 * rt + 4 * g4 + i;
             const float draw = __builtin_bit_cast(float, sizeof(T) == 2 ? dtr[u][rt][i] << 16 : dtr[u][rt][i]);
             const float dtv = tok < L ? dt_post(draw, ph) : 0.0f;
             fr[i] = dtv * exp2_fast(fminf(lend - lm[u][rt][i], 0.0f));
@@ -541,7 +550,7 @@ __global__ __launch_bounds__(kStThreads) void k_bwd_state(BwdArgs a) {
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = 32 * wv + 16 * rt + 4 * g4 + i;
+      const int r = rb + 32 * wv + 16 * rt + 4 * g4 + i;
       if (r >= qlen) continue;
       float *o = out + ((((int64_t)b * L + t0 + r) * G + g) * N);
 #pragma unroll
@@ -794,7 +803,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_reduce(BwdArgs a) {
 template <typename T, int N>
 static void launch_panels_t(const BwdArgs &a, hipStream_t st) {
   dim3 g((unsigned)(a.Z * a.nchunks * 2 * a.G * (a.chunk / kRB)));
-  dim3 gs((unsigned)(a.Z * a.nchunks * 2 * a.G));
+  dim3 gs((unsigned)(a.Z * a.nchunks * 2 * a.G * 2));
   launch_kernel((k_bwd_panel<T, N, 0>), g, dim3(kThreads), 0, st, a);
   launch_kernel((k_bwd_state<T, N, 0>), gs, dim3(kStThreads), 0, st, a);
   launch_kernel((k_bwd_panel<T, N, 1>), g, dim3(kThreads), 0, st, a);
