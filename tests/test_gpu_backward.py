@@ -65,6 +65,18 @@ def test_chunks_and_ragged_lengths_fp32(chunk, L):
     check(inp, "fp32", chunk)
 
 
+@pytest.mark.parametrize("L", (356, 456))
+def test_ragged_last_chunk_bf16(L):
+    """bf16 at chunk 256 with a last chunk of 100 or 200 tokens: the
+    carried-state kernels split a chunk's rows in halves of 128, so the
+    second half is empty in one case and partly filled in the other."""
+    w = W["tiny_fp32"].replace(L=L, chunk=256, Z=2, H=4, N=128, dtype="bf16")
+    for mode in ("full", "scan"):
+        inp = gen.make_inputs(w, mode=mode, with_dy=True)
+        print("bwd ragged bf16", L, mode, flush=True)
+        check(inp, "bf16", 256)
+
+
 @pytest.mark.parametrize("dtype", ("fp32", "bf16"))
 def test_groups_and_dstate(dtype):
     w = W["tiny_fp32"].replace(L=300, H=8, G=2, N=128, chunk=128, Z=2, dtype=dtype)
