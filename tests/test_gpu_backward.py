@@ -77,6 +77,17 @@ def test_ragged_last_chunk_bf16(L):
         check(inp, "bf16", 256)
 
 
+@pytest.mark.parametrize("chunk,L", [(256, 520), (128, 300)])
+def test_dstate64_bf16(chunk, L):
+    """bf16 with d_state 64 (the model card's width) and a ragged last chunk:
+    the N = 64 instantiations of every backward kernel."""
+    w = W["tiny_fp32"].replace(L=L, chunk=chunk, Z=2, H=4, N=64, dtype="bf16", seed=64 + L)
+    for mode in ("full", "scan"):
+        inp = gen.make_inputs(w, mode=mode, with_dy=True)
+        print("bwd dstate64 bf16", chunk, L, mode, flush=True)
+        check(inp, "bf16", chunk)
+
+
 @pytest.mark.parametrize("dtype", ("fp32", "bf16"))
 def test_groups_and_dstate(dtype):
     w = W["tiny_fp32"].replace(L=300, H=8, G=2, N=128, chunk=128, Z=2, dtype=dtype)
