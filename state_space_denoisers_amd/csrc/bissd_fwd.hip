@@ -829,44 +829,57 @@ __global__ __launch_bounds__(kThreads) void k2_tangent_pass8(ScanArgs a, int PN)
 // run on one XCD and share its L2 copy of the B and C rows.
 template <typename T, int N>
 __global__ __launch_bounds__(kThreads) void k_gram(ScanArgs a) {
+  // workgroup = (batch, chunk, slot, group, column block kb); wave w forms
+  // rows 16 w .. 16 w + 15 of every row-block j on the slot's side of kb
+  // (j >= kb for slot 0, j <= kb for slot 1), holding kb's B rows in
+  // registers across them; the heaviest column blocks come first
   constexpr int NK = N / 32;
   constexpr uint32_t ES = sizeof(T);
   const int w = wave_id(), lane = threadIdx.x & 63, r16 = lane & 15, g4 = lane >> 4;
   const int Q = a.chunk, NRB = Q / kRB, G = a.G;
   uint32_t item = (uint32_t)xcd_linear_id(blockIdx.x, gridDim.x), rem;
-  item = a.fd_pairs.divmod(item, rem);
-  const int pr = (int)rem;
+  const int kr = (int)(item % (uint32_t)NRB);
+  item /= (uint32_t)NRB;
   item = a.fd_g.divmod(item, rem);
   const int g = (int)rem;
   const int d = (int)(item & 1);
   item = a.fd_nc.divmod(item >> 1, rem);
   const int c = (int)rem, b = (int)item;
-  int j, kb;
-  gram_pair(pr, d, NRB, j, kb);
+  const int kb = d == 0 ? kr : NRB - 1 - kr;
+  const int j0 = d == 0 ? kb : 0, j1 = d == 0 ? NRB - 1 : kb;
   const int64_t L = a.L, t0 = (int64_t)c * Q;
   const bufres rC = make_buf(reinterpret_cast<const T *>(a.C[d]) + (int64_t)b * L * G * N, (uint32_t)(L * G * N * ES));
   const bufres rB = make_buf(reinterpret_cast<const T *>(a.B[d]) + (int64_t)b * L * G * N, (uint32_t)(L * G * N * ES));
   Frag<T> cf[NK], bf[4][NK];
+  auto load_c = [&](int j, Frag<T> (&f)[NK]) __attribute__((always_inline)) {
 #pragma unroll
-  for (int ks = 0; ks < NK; ++ks)
-    frag_bload(cf[ks], rC, (uint32_t)((t0 + j * kRB + 16 * w + r16) * G + g) * N * ES + (32 * ks + 8 * g4) * ES);
+    for (int ks = 0; ks < NK; ++ks)
+      frag_bload(f[ks], rC, (uint32_t)((t0 + j * kRB + 16 * w + r16) * G + g) * N * ES + (32 * ks + 8 * g4) * ES);
+  };
+  load_c(j0, cf);
 #pragma unroll
   for (int u = 0; u < 4; ++u)
 #pragma unroll
     for (int ks = 0; ks < NK; ++ks)
       frag_bload(bf[u][ks], rB, (uint32_t)((t0 + kb * kRB + 16 * u + r16) * G + g) * N * ES + (32 * ks + 8 * g4) * ES);
-  f32x4 cb[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) zero4(cb[u]);
-#pragma unroll
-  for (int ks = 0; ks < NK; ++ks)
-#pragma unroll
-    for (int u = 0; u < 4; ++u) mma(cb[u], bf[u][ks], cf[ks]);
   constexpr int GV = GramIO<T>::GV;
-  u32x4 *out = reinterpret_cast<u32x4 *>(a.gram) +
-               ((((int64_t)d * a.Z + b) * a.nchunks + c) * G + g) * (int64_t)Q * Q * GV / 16 +
-               (int64_t)((4 * j + w) * NRB + kb) * 64 * GV + lane;
-  GramIO<T>::put(out, cb);
+  u32x4 *base = reinterpret_cast<u32x4 *>(a.gram) +
+                ((((int64_t)d * a.Z + b) * a.nchunks + c) * G + g) * (int64_t)Q * Q * GV / 16 + lane;
+  for (int j = j0; j <= j1; ++j) {
+    Frag<T> cn[NK];
+    if (j < j1) load_c(j + 1, cn);
+    f32x4 cb[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) zero4(cb[u]);
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) mma(cb[u], bf[u][ks], cf[ks]);
+    GramIO<T>::put(base + (int64_t)((4 * j + w) * NRB + kb) * 64 * GV, cb);
+    if (j < j1)
+#pragma unroll
+      for (int ks = 0; ks < NK; ++ks) cf[ks] = cn[ks];
+  }
 }
 
 // =================================================================== K3
@@ -1685,10 +1698,10 @@ static void launch_t(const ScanArgs &a, int phase, hipStream_t st) {
     else
       launch_kernel((k1_chunk_state<T, N, HT, 2>), g, dim3(kThreads), 0, st, a);
   } else if (phase == PHASE_GRAM) {
-    // one workgroup per (batch, chunk, slot, group, row-block / column-block
-    // pair on the slot's side)
+    // one workgroup per (batch, chunk, slot, group, column block), covering
+    // the block's row-blocks on the slot's side
     const int nrb = a.chunk / kRB;
-    dim3 g((unsigned)((int64_t)a.Z * a.nchunks * 2 * a.G * (nrb * (nrb + 1) / 2)));
+    dim3 g((unsigned)((int64_t)a.Z * a.nchunks * 2 * a.G * nrb));
     launch_kernel((k_gram<T, N>), g, dim3(kThreads), 0, st, a);
   } else if (phase == PHASE_TAN_PASS && sizeof(T) == 2) {
     const int PN = kP * N;
